@@ -1,0 +1,288 @@
+/*
+ * ccl_oracle.c -- plain, sequential CPU oracle for connected-component labelling.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with the
+ * HIP library.
+ *
+ * What it computes (per image of a batch, each image on its own):
+ *   leader(p) = the smallest reading-order index q (q = row*W + col inside the
+ *               image) such that p and q are joined by a chain of neighbours of
+ *               identical colour value.  Neighbours are the 8 (or 4) pixels
+ *               around p inside the H x W rectangle; rows do not wrap and images
+ *               never touch each other.
+ *   label(p)  = 1 + the number of leaders r with r < leader(p).
+ *   count     = the number of leaders.
+ *
+ * Sources (titles of the pages the method is taken from):
+ *   "Accountable AI starts at the pixel" (every-colour blog), ch.01-02: a region
+ *     is touching pixels of exactly one colour, corners count (8 neighbours).
+ *   same page, ch.04 "Point at a leader": one parent per pixel; joining two
+ *     groups re-points the leader with the larger position at the smaller, so a
+ *     region's leader is its first pixel in reading order; the pixel scan looks
+ *     at up-left, up, up-right, then left.
+ *   same page, ch.05 "Start, Connect, Collapse, Number": the four stages.
+ *   same page, ch.08 idea 3 "Shorten arrows while walking": path halving; it
+ *     only moves arrows closer to the leader and never changes which pixel is
+ *     the leader, so it is used here for speed only.
+ *   same page, ch.08 idea 5: a leader's number is 1 + the leaders before it.
+ *   "About Connected Components Labeling on GPU" (TorchCC blog), "The basic
+ *     approach: Union-Find" and "Application in CCL": Find / Union / Compress,
+ *     the raster two-pass scan over already-visited neighbours, 4- and
+ *     8-connectivity.
+ *
+ * The BFS labeller below is an independent second algorithm (graph traversal,
+ * the alternative that page names in "The basic approach") used to pin the
+ * union-find oracle; it is not used by the union-find code.
+ *
+ * dtype: 1 = one byte per pixel, 4 = one 32-bit word per pixel; colours are
+ * compared as whole stored values.
+ *
+ * Building with -DORACLE_MUTANT=k plants a deliberate mistake (k = 1..8) so the
+ * pin tests can show that they catch it.  The default build plants nothing.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+enum { ORACLE_OK = 0, ORACLE_ERR_ARG = -1, ORACLE_ERR_NOMEM = -2 };
+
+/* Colour of pixel i of one image (whole stored value). */
+static inline uint32_t colour_at(const void *img, int dtype, int64_t i)
+{
+    if (dtype == 1)
+        return ((const uint8_t *)img)[i];
+#if ORACLE_MUTANT == 7
+    return ((const uint32_t *)img)[i] & 0xFFu; /* mutant: low byte only */
+#else
+    return ((const uint32_t *)img)[i];
+#endif
+}
+
+/* Find: walk parent arrows to the pixel that points at itself, halving the
+ * path on the way (each visited pixel is pointed at its grandparent). */
+static int32_t find_leader(int32_t *P, int32_t x)
+{
+    while (P[x] != x) {
+        P[x] = P[P[x]];
+        x = P[x];
+    }
+    return x;
+}
+
+/* Union: find both leaders and re-point the larger at the smaller. */
+static void join(int32_t *P, int32_t p, int32_t q)
+{
+    int32_t a = find_leader(P, p);
+    int32_t b = find_leader(P, q);
+    if (a == b)
+        return;
+#if ORACLE_MUTANT == 3
+    if (a < b) P[q] = a; else P[p] = b;   /* mutant: re-point the node, not its leader */
+#elif ORACLE_MUTANT == 4
+    if (a < b) P[a] = b; else P[b] = a;   /* mutant: larger leader wins */
+#else
+    if (a < b) P[b] = a; else P[a] = b;
+#endif
+}
+
+/* Stages Start and Connect for one image: P[i] = i, then the reading-order
+ * scan joining each pixel with its earlier same-colour neighbours in the
+ * order up-left, up, up-right, left (4-connectivity: up, left). */
+static void start_connect(const void *img, int dtype, int64_t H, int64_t W,
+                          int conn, int32_t *P)
+{
+    const int64_t n = H * W;
+    for (int64_t i = 0; i < n; ++i)
+        P[i] = (int32_t)i;                                   /* Start */
+
+    for (int64_t r = 0; r < H; ++r) {
+        for (int64_t c = 0; c < W; ++c) {
+            const int64_t p = r * W + c;
+            const uint32_t v = colour_at(img, dtype, p);
+            /* candidate earlier neighbours as (row offset, col offset) */
+            int64_t dr[4], dc[4];
+            int k = 0;
+            if (conn == 8) {
+#if ORACLE_MUTANT != 6
+                dr[k] = -1; dc[k] = -1; ++k;                 /* up-left  */
+#endif
+                dr[k] = -1; dc[k] = 0; ++k;                  /* up       */
+#if ORACLE_MUTANT != 1
+                dr[k] = -1; dc[k] = +1; ++k;                 /* up-right */
+#endif
+                dr[k] = 0; dc[k] = -1; ++k;                  /* left     */
+            } else {
+                dr[k] = -1; dc[k] = 0; ++k;                  /* up       */
+#if ORACLE_MUTANT == 8
+                dr[k] = -1; dc[k] = +1; ++k;   /* mutant: a diagonal in 4-connectivity */
+#endif
+                dr[k] = 0; dc[k] = -1; ++k;                  /* left     */
+            }
+            for (int j = 0; j < k; ++j) {
+                const int64_t rr = r + dr[j], cc = c + dc[j];
+#if ORACLE_MUTANT == 2
+                /* mutant: neighbours taken in the flat index, so row ends wrap */
+                const int64_t q = p + dr[j] * W + dc[j];
+                if (q < 0 || q >= n) continue;
+#else
+                if (rr < 0 || cc < 0 || cc >= W) continue;   /* inside H x W only */
+                const int64_t q = rr * W + cc;
+#endif
+                if (colour_at(img, dtype, q) == v)
+                    join(P, (int32_t)p, (int32_t)q);
+            }
+        }
+    }
+}
+
+/* Stage Collapse: every pixel points straight at its leader.  P[i] <= i holds
+ * for every pixel, so an ascending pass sees each parent's leader first. */
+static void collapse(int32_t *P, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        P[i] = (P[i] == i) ? (int32_t)i : P[P[i]];
+}
+
+static int check_args(const void *img, int dtype, int64_t B, int64_t H,
+                      int64_t W, int conn, const void *out)
+{
+    if (B < 0 || H < 0 || W < 0) return ORACLE_ERR_ARG;
+    if (dtype != 1 && dtype != 4) return ORACLE_ERR_ARG;
+    if (conn != 4 && conn != 8) return ORACLE_ERR_ARG;
+    if (H * W > 2147483647LL) return ORACLE_ERR_ARG;
+    if (B * H * W > 0 && (img == NULL || out == NULL)) return ORACLE_ERR_ARG;
+    return ORACLE_OK;
+}
+
+/* Parent array after the Connect stage (no Collapse) -- exposed so tests can
+ * check the stage semantics against the worked examples on the pages. */
+int oracle_connect(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
+                   int conn, int32_t *parents)
+{
+    int rc = check_args(img, dtype, B, H, W, conn, parents);
+    if (rc) return rc;
+    const int64_t n = H * W;
+    for (int64_t b = 0; b < B; ++b)
+        start_connect((const char *)img + b * n * dtype, dtype, H, W, conn,
+                      parents + b * n);
+    return ORACLE_OK;
+}
+
+/* Leaders: Start, Connect, Collapse, per image.  Indices are per image. */
+int oracle_label(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
+                 int conn, int32_t *leaders)
+{
+    int rc = check_args(img, dtype, B, H, W, conn, leaders);
+    if (rc) return rc;
+    const int64_t n = H * W;
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t *P = leaders + b * n;
+        start_connect((const char *)img + b * n * dtype, dtype, H, W, conn, P);
+        collapse(P, n);
+    }
+    return ORACLE_OK;
+}
+
+/* Stage Number: leaders become 1, 2, 3, ... in reading order and every pixel
+ * takes its leader's number.  Requires a valid leader image (leader[p] <= p,
+ * leader[leader[p]] == leader[p]).  counts may be NULL. */
+int oracle_number(const int32_t *leaders, int64_t B, int64_t H, int64_t W,
+                  int32_t *labels, int32_t *counts)
+{
+    if (B < 0 || H < 0 || W < 0) return ORACLE_ERR_ARG;
+    const int64_t n = H * W;
+    if (B * n > 0 && (leaders == NULL || labels == NULL)) return ORACLE_ERR_ARG;
+    int32_t *num = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    if (!num) return ORACLE_ERR_NOMEM;
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t *L = leaders + b * n;
+        int32_t *out = labels + b * n;
+        int32_t k = 0;
+        for (int64_t i = 0; i < n; ++i) {
+            if (L[i] == i) {
+#if ORACLE_MUTANT == 5
+                num[i] = k;                       /* mutant: numbers start at 0 */
+                k += 1;
+#else
+                k += 1;
+                num[i] = k;
+#endif
+            }
+            out[i] = num[L[i]];
+        }
+        if (counts) counts[b] = k;
+    }
+    free(num);
+    return ORACLE_OK;
+}
+
+/* Count: number of leaders (pixels with leader[p] == p) per image. */
+int oracle_count(const int32_t *leaders, int64_t B, int64_t H, int64_t W,
+                 int32_t *counts)
+{
+    if (B < 0 || H < 0 || W < 0 || counts == NULL) return ORACLE_ERR_ARG;
+    const int64_t n = H * W;
+    if (B * n > 0 && leaders == NULL) return ORACLE_ERR_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t *L = leaders + b * n;
+        int32_t k = 0;
+        for (int64_t i = 0; i < n; ++i)
+            k += (L[i] == i);
+        counts[b] = k;
+    }
+    return ORACLE_OK;
+}
+
+/* Independent second labeller: breadth-first flood fill.  Seeds are taken in
+ * reading order, so each seed is the smallest index of its region (every
+ * smaller pixel was reached from an earlier seed), and every pixel of the
+ * region gets the seed's index.  Used only to pin the union-find above. */
+int oracle_bfs_label(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
+                     int conn, int32_t *leaders)
+{
+    int rc = check_args(img, dtype, B, H, W, conn, leaders);
+    if (rc) return rc;
+    const int64_t n = H * W;
+    int32_t *queue = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    if (!queue) return ORACLE_ERR_NOMEM;
+    static const int dr8[8] = {-1, -1, -1, 0, 0, 1, 1, 1};
+    static const int dc8[8] = {-1, 0, 1, -1, 1, -1, 0, 1};
+    static const int dr4[4] = {-1, 0, 0, 1};
+    static const int dc4[4] = {0, -1, 1, 0};
+    const int *dr = conn == 8 ? dr8 : dr4;
+    const int *dc = conn == 8 ? dc8 : dc4;
+    const int nn = conn;
+    for (int64_t b = 0; b < B; ++b) {
+        const void *im = (const char *)img + b * n * dtype;
+        int32_t *L = leaders + b * n;
+        for (int64_t i = 0; i < n; ++i) L[i] = -1;
+        for (int64_t s = 0; s < n; ++s) {
+            if (L[s] >= 0) continue;
+            const uint32_t v = colour_at(im, dtype, s);
+            int64_t head = 0, tail = 0;
+            queue[tail++] = (int32_t)s;
+            L[s] = (int32_t)s;
+            while (head < tail) {
+                const int64_t p = queue[head++];
+                const int64_t r = p / W, c = p % W;
+                for (int j = 0; j < nn; ++j) {
+                    const int64_t rr = r + dr[j], cc = c + dc[j];
+                    if (rr < 0 || rr >= H || cc < 0 || cc >= W) continue;
+                    const int64_t q = rr * W + cc;
+                    if (L[q] < 0 && colour_at(im, dtype, q) == v) {
+                        L[q] = (int32_t)s;
+                        queue[tail++] = (int32_t)q;
+                    }
+                }
+            }
+        }
+    }
+    free(queue);
+    return ORACLE_OK;
+}

@@ -1,0 +1,288 @@
+"""Checks that pin the CPU oracle to things other than itself.
+
+Each ``pin_*`` function raises ``AssertionError`` when the oracle library it is
+given disagrees with:
+  * values printed for the pages' worked examples (``tests/golden/``),
+  * an independent labeller (breadth-first flood fill -- in pure Python, and the
+    C one built from the unmodified oracle source),
+  * scipy's binary labelling run once per colour (the "one colour at a time"
+    approach of "Accountable AI starts at the pixel", ch.03), compared as a
+    partition,
+  * closed forms (uniform, checkerboard, stripes, single rows, no row wrap),
+  * invariants of the definition (leader = region minimum, equal-colour
+    neighbours share a leader, numbers are 1..n in reading order).
+
+``tests/test_oracle_pins.py`` runs them on the oracle; ``tests/test_oracle_mutants.py``
+runs them on builds with planted mistakes and requires each to be caught.
+"""
+from __future__ import annotations
+
+import itertools
+from collections import deque
+
+import numpy as np
+import scipy.ndimage as ndi
+
+import oracle
+from tests.golden import fixtures
+
+NB8 = [(-1, -1), (-1, 0), (-1, 1), (0, -1), (0, 1), (1, -1), (1, 0), (1, 1)]
+NB4 = [(-1, 0), (0, -1), (0, 1), (1, 0)]
+
+
+def py_bfs(img: np.ndarray, conn: int) -> np.ndarray:
+    """Pure-Python flood fill, seeds in reading order (independent of the C file)."""
+    H, W = img.shape
+    nb = NB8 if conn == 8 else NB4
+    lab = np.full((H, W), -1, dtype=np.int64)
+    for s in range(H * W):
+        r0, c0 = divmod(s, W)
+        if lab[r0, c0] >= 0:
+            continue
+        v = img[r0, c0]
+        lab[r0, c0] = s
+        q = deque([(r0, c0)])
+        while q:
+            r, c = q.popleft()
+            for dr, dc in nb:
+                rr, cc = r + dr, c + dc
+                if 0 <= rr < H and 0 <= cc < W and lab[rr, cc] < 0 and img[rr, cc] == v:
+                    lab[rr, cc] = s
+                    q.append((rr, cc))
+    return lab.astype(np.int32)
+
+
+def random_images(rng, B, H, W, ncol, dtype=np.uint32):
+    """Small random images with ``ncol`` distinct values; u32 values use all bytes."""
+    idx = rng.integers(0, ncol, size=(B, H, W))
+    if dtype == np.uint8:
+        return idx.astype(np.uint8)
+    palette = rng.integers(0, 2**32, size=ncol, dtype=np.uint64).astype(np.uint32)
+    return palette[idx]
+
+
+def check_invariants(img: np.ndarray, leaders: np.ndarray, conn: int):
+    """Definition-level properties of a leader image, checked with numpy only."""
+    H, W = img.shape
+    n = H * W
+    L = leaders.reshape(-1).astype(np.int64)
+    flat = img.reshape(-1)
+    idx = np.arange(n)
+    assert np.all(L >= 0) and np.all(L <= idx), "leader must be an earlier-or-same pixel"
+    assert np.all(L[L] == L), "a leader must lead itself"
+    assert np.all(flat[L] == flat), "a pixel and its leader must have the same colour"
+    # equal-colour neighbours share a leader (no row wrap: 2-D offsets only)
+    offs = [(0, 1), (1, 0)] + ([(1, 1), (1, -1)] if conn == 8 else [])
+    Li = leaders.reshape(H, W)
+    for dr, dc in offs:
+        r0, r1 = 0, H - dr
+        c0, c1 = max(0, -dc), W - max(0, dc)
+        if r1 <= r0 or c1 <= c0:
+            continue
+        a = img[r0:r1, c0:c1]
+        b = img[r0 + dr:r1 + dr, c0 + dc:c1 + dc]
+        la = Li[r0:r1, c0:c1]
+        lb = Li[r0 + dr:r1 + dr, c0 + dc:c1 + dc]
+        same = a == b
+        assert np.all(la[same] == lb[same]), f"equal-colour neighbours at offset {(dr, dc)} split"
+
+
+def check_numbering(leaders: np.ndarray, labels: np.ndarray, count: int):
+    """Numbers are 1..n, in reading order of the leaders (sort-based check)."""
+    L = leaders.reshape(-1)
+    uniq = np.unique(L)                       # sorted leaders
+    expect = np.searchsorted(uniq, L) + 1     # rank among leaders, from 1
+    assert count == uniq.size, "count must be the number of distinct leaders"
+    assert np.array_equal(labels.reshape(-1), expect), "numbering is not 1 + leaders before"
+    if labels.size:
+        lab = labels.reshape(-1)
+        first = np.full(count + 1, lab.size)
+        np.minimum.at(first, lab, np.arange(lab.size))   # first occurrence of each number
+        assert np.all(np.diff(first[1:]) > 0), "first occurrences not in reading order"
+
+
+# ---------------------------------------------------------------------------
+# worked examples from the pages
+
+def pin_torchcc_4x4(lib):
+    fx = fixtures.load("torchcc_4x4_binary.txt")
+    img = fx["input"].astype(np.uint8)
+    P = oracle.connect(img, 8, lib=lib).reshape(-1)
+    for item in fx["scan_parent_foreground"].split():
+        i, p = (int(v) for v in item.split(":"))
+        assert P[i] == p, f"parent of {i} after the scan: {P[i]} != {p} (page)"
+    L = oracle.label(img, 8, lib=lib).reshape(-1)
+    fg = np.flatnonzero(img.reshape(-1) == 1)
+    roots = sorted(set(int(v) for v in L[fg]))
+    assert roots == [int(v) for v in fx["roots_foreground"].split()]
+    assert [r + 1 for r in roots] == [int(v) for v in fx["labels_foreground_root_plus_one"].split()]
+
+
+def pin_every_colour_3x3(lib):
+    fx = fixtures.load("every_colour_3x3_reconstruction.txt")
+    img = fx["input"]
+    P = oracle.connect(img, 8, lib=lib).reshape(-1)
+    assert P[5] == int(fx["after_connect_parent_5"]), "pixel 5 must point at 2 after Connect"
+    assert P[2] == int(fx["after_connect_parent_2"]), "leader 2 must be re-pointed at 0"
+    L = oracle.label(img, 8, lib=lib).reshape(-1)
+    # both arms of colour X form one region led by 0; pixel 2 is not left behind
+    assert set(L[[0, 2, 3, 5, 7]]) == {0}
+    assert set(L[[1, 4, 6, 8]]) == {1}
+
+
+def pin_torchcc_6x6(lib):
+    fx = fixtures.load("torchcc_6x6_binary.txt")
+    img = fx["input"].astype(np.uint8)
+    for conn in (8, 4):
+        L = oracle.label(img, conn, lib=lib)
+        assert np.array_equal(L, py_bfs(img, conn))
+    # the page's block init labels are the raster index of each 2x2 block's top-left pixel
+    blocks = [int(v) for v in fx["block_init_labels"].split()]
+    assert blocks == [r * 6 + c for r in range(0, 6, 2) for c in range(0, 6, 2)]
+
+
+# ---------------------------------------------------------------------------
+# independent labellers
+
+def pin_random_vs_python_bfs(lib, n_images=300, seed=11):
+    rng = np.random.default_rng(seed)
+    for k in range(n_images):
+        H, W = int(rng.integers(1, 13)), int(rng.integers(1, 13))
+        ncol = int(rng.integers(1, 5))
+        dt = np.uint8 if k % 2 else np.uint32
+        img = random_images(rng, 1, H, W, ncol, dt)[0]
+        conn = 8 if k % 3 else 4
+        L = oracle.label(img, conn, lib=lib)
+        assert np.array_equal(L, py_bfs(img, conn)), f"case {k}: {H}x{W} conn {conn}"
+
+
+def pin_random_vs_c_bfs(lib, ref_lib=None, seed=12, per_shape=200):
+    """Many random images against the C flood fill of ``ref_lib``."""
+    ref_lib = ref_lib or lib
+    rng = np.random.default_rng(seed)
+    shapes = [(1, 1), (1, 24), (24, 1), (2, 2), (3, 7), (7, 3), (5, 5), (8, 13),
+              (16, 16), (24, 24), (17, 23), (23, 17)]
+    for H, W in shapes:
+        for ncol in (1, 2, 3, 4):
+            for dt in (np.uint8, np.uint32):
+                imgs = random_images(rng, per_shape, H, W, ncol, dt)
+                for conn in (8, 4):
+                    a = oracle.label(imgs, conn, lib=lib)
+                    b = oracle.bfs_label(imgs, conn, lib=ref_lib)
+                    assert np.array_equal(a, b), f"{H}x{W} ncol={ncol} {dt.__name__} conn={conn}"
+
+
+def pin_exhaustive(lib, ref_lib=None):
+    """Every 3-colour 3x3 image and every 2-colour 4x4 image, both connectivities."""
+    ref_lib = ref_lib or lib
+    for H, W, ncol in ((3, 3, 3), (4, 4, 2)):
+        imgs = np.array(list(itertools.product(range(ncol), repeat=H * W)),
+                        dtype=np.uint8).reshape(-1, H, W)
+        for conn in (8, 4):
+            a = oracle.label(imgs, conn, lib=lib)
+            b = oracle.bfs_label(imgs, conn, lib=ref_lib)
+            assert np.array_equal(a, b), f"exhaustive {H}x{W} conn={conn}"
+
+
+def pin_scipy_partition(lib, seed=13, n_images=60):
+    """Per-colour binary labelling (scipy) must give the same partition."""
+    rng = np.random.default_rng(seed)
+    for k in range(n_images):
+        H, W = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        img = random_images(rng, 1, H, W, int(rng.integers(1, 6)))[0]
+        for conn in (8, 4):
+            L = oracle.label(img, conn, lib=lib)
+            structure = np.ones((3, 3)) if conn == 8 else ndi.generate_binary_structure(2, 1)
+            region = np.full((H, W), -1, dtype=np.int64)
+            base = 0
+            for v in np.unique(img):
+                lab, n = ndi.label(img == v, structure=structure)
+                m = lab > 0
+                region[m] = lab[m] - 1 + base
+                base += n
+            # same partition: the maps region -> leader and leader -> region are functions
+            pairs = np.unique(np.stack([region.reshape(-1), L.reshape(-1)]), axis=1)
+            assert pairs.shape[1] == base == np.unique(L).size, f"case {k} conn {conn}"
+            # and each region's leader is its smallest index
+            flat = np.arange(H * W)
+            mins = np.full(base, H * W)
+            np.minimum.at(mins, region.reshape(-1), flat)
+            assert np.array_equal(L.reshape(-1), mins[region.reshape(-1)])
+
+
+# ---------------------------------------------------------------------------
+# closed forms and special cases
+
+def pin_closed_forms(lib):
+    for conn in (8, 4):
+        # uniform image: one region led by pixel 0
+        for H, W in ((1, 1), (1, 9), (9, 1), (7, 11)):
+            L = oracle.label(np.full((H, W), 0xABCDEF12, np.uint32), conn, lib=lib)
+            assert np.all(L == 0)
+            _, c = oracle.number(L, lib=lib)
+            assert c[0] == 1
+        # vertical stripes of alternating colours: W regions, leader = column index
+        H, W = 6, 9
+        img = np.tile((np.arange(W) % 2).astype(np.uint8), (H, 1))
+        L = oracle.label(img, conn, lib=lib)
+        assert np.array_equal(L, np.tile(np.arange(W, dtype=np.int32), (H, 1)))
+        labels, c = oracle.number(L, lib=lib)           # numbers 1..W left to right
+        assert c[0] == W and np.array_equal(labels, L + 1)
+        # single row: regions = colour changes + 1
+        row = np.array([[3, 3, 1, 1, 1, 3, 2, 2, 3, 3]], np.uint8)
+        L = oracle.label(row, conn, lib=lib)
+        assert np.array_equal(L[0], [0, 0, 2, 2, 2, 5, 6, 6, 8, 8])
+        # no join across a row end: (r, W-1) and (r+1, 0) only touch in the flat index
+        img = np.zeros((3, 4), np.uint8)
+        img[0, 3] = 1
+        img[1, 0] = 1
+        L = oracle.label(img, conn, lib=lib)
+        assert L[0, 3] == 3 and L[1, 0] == 4
+    # checkerboard: 8-connectivity joins the diagonals (2 regions), 4 does not
+    for H, W in ((2, 2), (5, 6), (8, 8)):
+        cb = ((np.add.outer(np.arange(H), np.arange(W))) % 2).astype(np.uint8)
+        L8 = oracle.label(cb, 8, lib=lib)
+        assert np.unique(L8).tolist() == [0, 1]
+        L4 = oracle.label(cb, 4, lib=lib)
+        assert np.array_equal(L4.reshape(-1), np.arange(H * W))
+    # colours differing only in their high bytes are different colours
+    img = np.array([[0x00000001, 0x01000001], [0x00010001, 0x00000001]], np.uint32)
+    L = oracle.label(img, 8, lib=lib)
+    assert L.reshape(-1).tolist() == [0, 1, 2, 0]
+    # empty inputs
+    assert oracle.label(np.zeros((0, 5, 5), np.uint8), 8, lib=lib).shape == (0, 5, 5)
+    assert oracle.label(np.zeros((2, 0, 5), np.uint8), 8, lib=lib).shape == (2, 0, 5)
+    _, c = oracle.number(np.zeros((2, 0, 5), np.int32), lib=lib)
+    assert c.tolist() == [0, 0]
+
+
+def pin_invariants_and_numbering(lib, seed=14, n_images=200):
+    rng = np.random.default_rng(seed)
+    for k in range(n_images):
+        H, W = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        img = random_images(rng, 1, H, W, int(rng.integers(1, 5)),
+                            np.uint32 if k % 2 else np.uint8)[0]
+        conn = 8 if k % 2 else 4
+        L = oracle.label(img, conn, lib=lib)
+        check_invariants(img, L, conn)
+        labels, counts = oracle.number(L, lib=lib)
+        check_numbering(L, labels, int(counts[0]))
+        assert oracle.count(L, lib=lib)[0] == counts[0]
+    # batches: each image is labelled on its own, indices per image
+    imgs = random_images(rng, 5, 9, 7, 3)
+    L = oracle.label(imgs, 8, lib=lib)
+    for b in range(5):
+        assert np.array_equal(L[b], oracle.label(imgs[b], 8, lib=lib))
+
+
+ALL_PINS = [
+    pin_torchcc_4x4,
+    pin_every_colour_3x3,
+    pin_torchcc_6x6,
+    pin_closed_forms,
+    pin_random_vs_python_bfs,
+    pin_random_vs_c_bfs,
+    pin_exhaustive,
+    pin_scipy_partition,
+    pin_invariants_and_numbering,
+]
