@@ -191,15 +191,15 @@ int oracle_label(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
 
 /* Stage Number: leaders become 1, 2, 3, ... in reading order and every pixel
  * takes its leader's number.  Requires a valid leader image (leader[p] <= p,
- * leader[leader[p]] == leader[p]).  counts may be NULL. */
+ * leader[leader[p]] == leader[p]): a leader comes no later than its pixels, so
+ * its number is already written when a later pixel copies it.  counts may be
+ * NULL. */
 int oracle_number(const int32_t *leaders, int64_t B, int64_t H, int64_t W,
                   int32_t *labels, int32_t *counts)
 {
     if (B < 0 || H < 0 || W < 0) return ORACLE_ERR_ARG;
     const int64_t n = H * W;
     if (B * n > 0 && (leaders == NULL || labels == NULL)) return ORACLE_ERR_ARG;
-    int32_t *num = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
-    if (!num) return ORACLE_ERR_NOMEM;
     for (int64_t b = 0; b < B; ++b) {
         const int32_t *L = leaders + b * n;
         int32_t *out = labels + b * n;
@@ -207,18 +207,18 @@ int oracle_number(const int32_t *leaders, int64_t B, int64_t H, int64_t W,
         for (int64_t i = 0; i < n; ++i) {
             if (L[i] == i) {
 #if ORACLE_MUTANT == 5
-                num[i] = k;                       /* mutant: numbers start at 0 */
+                out[i] = k;                       /* mutant: numbers start at 0 */
                 k += 1;
 #else
                 k += 1;
-                num[i] = k;
+                out[i] = k;
 #endif
+            } else {
+                out[i] = out[L[i]];
             }
-            out[i] = num[L[i]];
         }
         if (counts) counts[b] = k;
     }
-    free(num);
     return ORACLE_OK;
 }
 
