@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Throughput of the labelled+numbered path on one MI355X.
+
+One step = one ccl_label call with CCL_NUMBER and counts (tile pass, seam
+merge, seam collapse, numbering scan, final write) over the 806.4-Mpx
+synthetic construction sheet (33600 x 24000, uint32 colours, 8-connected),
+with the picture already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5]
+
+Per-stage kernel durations come from HIP events that the library records
+between its launches on the benchmark's stream (ccl_label_profiled).  The CPU
+baseline runs the sequential oracle (single thread) on a band of the same
+sheet; the GPU labels that band too and must match it bit for bit.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Gpixels/s labelled+numbered (8-conn, multi-colour), 806-Mpix sheet; % HBM peak"
+HBM_PEAK_GBS = 8000.0
+STAGES = ["tile_label", "seam_merge", "seam_collapse", "number_scan", "final_write"]
+KERNEL_SOURCES = [os.path.join(ROOT, "connected_component_labelling_amd", "csrc", f)
+                  for f in ("ccl_kernels.hip", "ccl_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def load_traffic(kernel: str, launch_pixels: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    if rec.get("pixels") != launch_pixels:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(img_np, rows: int, ccl, torch):
+    """Oracle (one thread) on the first `rows` rows of the sheet, and the GPU on
+    the same band for a bit-exact check."""
+    import numpy as np
+
+    import oracle
+    band = np.ascontiguousarray(img_np[:, :rows, :])
+    B, H, W = band.shape
+    lib = oracle.load()
+    t0 = time.perf_counter()
+    leaders = oracle.label(band, 8, lib=lib)
+    labels, counts = oracle.number(leaders, lib=lib)
+    dt = time.perf_counter() - t0
+    dev = torch.from_numpy(band.view(np.int32)).cuda()
+    got, gc = ccl.label(dev, 8, number=True)
+    torch.cuda.synchronize()
+    exact = bool(np.array_equal(got.cpu().numpy(), labels) and
+                 np.array_equal(gc.cpu().numpy(), counts))
+    del dev, got
+    return {
+        "value": round(B * H * W / dt / 1e9, 4),
+        "unit": "Gpixels/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"rows 0..{H - 1} of the sheet ({B * H * W / 1e6:.1f} Mpx, full width), "
+                  f"label + number, sequential C oracle on one host thread, {dt:.1f} s",
+    }, exact
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--cpu-rows", type=int, default=6000,
+                    help="rows of the sheet the CPU baseline labels (0 = skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this labeller runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import connected_component_labelling_amd as ccl
+    import synth
+
+    desc, (B, H, W), np_dtype, seed = synth.CONFIGS[args.config]
+    t0 = time.perf_counter()
+    img_np = synth.generate(args.config)
+    gen_s = time.perf_counter() - t0
+    print(f"[bench] generated {desc} in {gen_s:.1f} s", file=sys.stderr, flush=True)
+    bpp = np.dtype(np_dtype).itemsize
+    npx = B * H * W
+    dev = torch.from_numpy(img_np.view(np.int32) if bpp == 4 else img_np).cuda()
+    lab = ccl.Labeller((B, H, W), device="cuda", connectivity=8)
+    stream = torch.cuda.current_stream()
+    hip = HipEvents()
+
+    for _ in range(args.warmup):
+        lab(dev, number=True, stream=stream)
+    torch.cuda.synchronize()
+    print(f"[bench] warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    events = [hip.create(6) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        lab(dev, number=True, stream=stream, events=events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    stage_ms = {s: 0.0 for s in STAGES}
+    step_ms = []
+    for ev in events:
+        for i, s in enumerate(STAGES):
+            stage_ms[s] += hip.elapsed_ms(ev[i], ev[i + 1]) / args.steps
+        step_ms.append(hip.elapsed_ms(ev[0], ev[5]))
+    for ev in events:
+        hip.destroy(ev)
+    counts = lab.counts.cpu().tolist()
+    err = ccl.error_word(lab.workspace)
+
+    algo_bytes = {"tile_label": npx * bpp, "final_write": npx * 4}
+    dominant = max(algo_bytes, key=lambda s: stage_ms[s])
+    dom_ms = stage_ms[dominant]
+    achieved = algo_bytes[dominant] / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(dominant, npx)
+    value = npx / (ms_per_step * 1e-3) / 1e9
+    path_gbs = npx * (bpp + 4) / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    exact = None
+    if args.cpu_rows > 0:
+        print("[bench] CPU baseline (oracle) ...", file=sys.stderr, flush=True)
+        del lab
+        torch.cuda.empty_cache()
+        cpu, exact = cpu_baseline(img_np, min(args.cpu_rows, H), ccl, torch)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Gpixels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32" if bpp == 4 else "u8",
+        "data": "synthetic",
+        "config": {"workload": desc, "batch": B, "height": H, "width": W, "connectivity": 8,
+                   "numbered": True, "counts": True, "seed": seed},
+        "hbm_frac_path": round(path_gbs / HBM_PEAK_GBS, 4),
+        "path_algorithmic_GBps": round(path_gbs, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dominant,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "event_ms_per_step": round(float(np.median(step_ms)), 4),
+        "regions": counts[:4],
+        "error_word": err,
+        "cpu_baseline": cpu,
+        "band_parity_bit_exact": exact,
+        "kernel_source": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+"""MI355X (gfx950) connected-component labeller: a thin Python binding over the
+C ABI of ``include/ccl.h`` (``libccl.so``, built from ``csrc/``).
+
+This module only marshals arguments: PyTorch supplies device memory and the
+stream, every step of the labelling runs in the HIP kernels of ``libccl.so``.
+If the library is missing or cannot be loaded, importing the binding's
+functions raises -- there is no CPU fallback.
+
+    out, counts = label(img, connectivity=8, number=True)   # 1..n per image
+    leaders, _  = label(img)                                # region minima
+    labels, counts = number(leaders)
+    counts = count(leaders)
+
+``img`` is a CUDA (HIP) tensor of shape [H, W] or [B, H, W], dtype uint8, or
+uint32 / int32 (the 32 bits are compared as they are); results are int32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+__all__ = ["label", "number", "count", "workspace_bytes", "Labeller", "error_word",
+           "CclError", "library_path"]
+
+CCL_U8, CCL_U32 = 1, 4
+CCL_NUMBER = 1
+
+_lib = None
+
+
+class CclError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _build.LIB_PATH
+    if not os.path.exists(path):
+        _build.build()
+    lib = ctypes.CDLL(path)
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    lib.ccl_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.ccl_workspace_bytes.restype = sz
+    lib.ccl_label.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp,
+                              vp, sz, vp]
+    lib.ccl_label.restype = ctypes.c_int
+    lib.ccl_label_profiled.argtypes = lib.ccl_label.argtypes + [ctypes.POINTER(vp), ctypes.c_int]
+    lib.ccl_label_profiled.restype = ctypes.c_int
+    lib.ccl_number.argtypes = [vp, i64, i64, i64, vp, vp, vp, sz, vp]
+    lib.ccl_number.restype = ctypes.c_int
+    lib.ccl_count.argtypes = [vp, i64, i64, i64, vp, vp, sz, vp]
+    lib.ccl_count.restype = ctypes.c_int
+    lib.ccl_status_string.argtypes = [ctypes.c_int]
+    lib.ccl_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise CclError(f"ccl status {rc}: {_load().ccl_status_string(rc).decode()}")
+
+
+def workspace_bytes(batch: int, height: int, width: int) -> int:
+    return int(_load().ccl_workspace_bytes(batch, height, width))
+
+
+def _batch_view(t: torch.Tensor):
+    if t.dim() == 2:
+        return t.unsqueeze(0), True
+    if t.dim() != 3:
+        raise ValueError("expected a [H, W] or [B, H, W] tensor")
+    return t, False
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.uint8:
+        return CCL_U8
+    if t.dtype in (torch.int32, torch.uint32):
+        return CCL_U32
+    raise TypeError(f"colour dtype must be uint8, uint32 or int32, not {t.dtype}")
+
+
+def _require_device(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+
+
+def _new_workspace(B, H, W, device):
+    n = workspace_bytes(B, H, W)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def error_word(workspace: torch.Tensor) -> int:
+    """The workspace's error word (nonzero only if a kernel hit a safety bound)."""
+    return int(workspace[:4].view(torch.int32).item())
+
+
+def label(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream=None,
+          workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+          with_counts: bool = True):
+    """Label ``img``: leaders (per-image reading-order index of each region's first
+    pixel) or, with ``number=True``, numbers 1..n per image.  Returns (out, counts)."""
+    _require_device(img, "img")
+    x, squeeze = _batch_view(img)
+    B, H, W = x.shape
+    if out is None:
+        out = torch.empty((B, H, W), dtype=torch.int32, device=img.device)
+    counts = torch.empty(B, dtype=torch.int32, device=img.device) if with_counts else None
+    if workspace is None:
+        workspace = _new_workspace(B, H, W, img.device)
+    _check(_load().ccl_label(_ptr(x), _dtype_code(x), B, H, W, int(connectivity),
+                             CCL_NUMBER if number else 0, _ptr(out), _ptr(counts),
+                             _ptr(workspace), workspace.numel(),
+                             ctypes.c_void_p(_stream_handle(stream))))
+    return (out[0] if squeeze else out), counts
+
+
+def number(leaders: torch.Tensor, stream=None, inplace: bool = False,
+           workspace: torch.Tensor | None = None):
+    """Numbers 1..n per image from a leader image.  Returns (labels, counts)."""
+    _require_device(leaders, "leaders")
+    if leaders.dtype != torch.int32:
+        raise TypeError("leaders must be int32")
+    x, squeeze = _batch_view(leaders)
+    B, H, W = x.shape
+    labels = x if inplace else torch.empty_like(x)
+    counts = torch.empty(B, dtype=torch.int32, device=leaders.device)
+    if workspace is None:
+        workspace = _new_workspace(B, H, W, leaders.device)
+    _check(_load().ccl_number(_ptr(x), B, H, W, _ptr(labels), _ptr(counts), _ptr(workspace),
+                              workspace.numel(), ctypes.c_void_p(_stream_handle(stream))))
+    return (labels[0] if squeeze else labels), counts
+
+
+def count(leaders: torch.Tensor, stream=None, workspace: torch.Tensor | None = None):
+    """Regions per image of a leader image (pixels with leaders[p] == p)."""
+    _require_device(leaders, "leaders")
+    if leaders.dtype != torch.int32:
+        raise TypeError("leaders must be int32")
+    x, _ = _batch_view(leaders)
+    B, H, W = x.shape
+    counts = torch.empty(B, dtype=torch.int32, device=leaders.device)
+    if workspace is None:
+        workspace = _new_workspace(B, H, W, leaders.device)
+    _check(_load().ccl_count(_ptr(x), B, H, W, _ptr(counts), _ptr(workspace), workspace.numel(),
+                             ctypes.c_void_p(_stream_handle(stream))))
+    return counts
+
+
+class Labeller:
+    """Holds output, counts and workspace for one batch shape, so repeated calls
+    allocate nothing (as a benchmark or a serving loop wants)."""
+
+    def __init__(self, shape, device="cuda", connectivity: int = 8):
+        if len(shape) == 2:
+            shape = (1, *shape)
+        self.B, self.H, self.W = (int(v) for v in shape)
+        self.connectivity = connectivity
+        self.out = torch.empty((self.B, self.H, self.W), dtype=torch.int32, device=device)
+        self.counts = torch.empty(self.B, dtype=torch.int32, device=device)
+        self.workspace = _new_workspace(self.B, self.H, self.W, device)
+
+    def __call__(self, img: torch.Tensor, number: bool = True, stream=None, events=None):
+        x, _ = _batch_view(img)
+        if tuple(x.shape) != (self.B, self.H, self.W):
+            raise ValueError("image shape does not match the Labeller")
+        lib = _load()
+        args = [_ptr(x), _dtype_code(x), self.B, self.H, self.W, self.connectivity,
+                CCL_NUMBER if number else 0, _ptr(self.out), _ptr(self.counts),
+                _ptr(self.workspace), self.workspace.numel(),
+                ctypes.c_void_p(_stream_handle(stream))]
+        if events is None:
+            _check(lib.ccl_label(*args))
+        else:
+            arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e) for e in events])
+            _check(lib.ccl_label_profiled(*args, arr, len(events)))
+        return self.out, self.counts

@@ -1,0 +1,248 @@
+// ccl_api.hip -- the C ABI declared in include/ccl.h: argument checks, the
+// workspace layout, and the launch sequence on the caller's stream.
+#include "ccl.h"
+#include "ccl_internal.h"
+
+#include <limits.h>
+
+namespace ccl {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static FastDiv make_fastdiv(uint32_t d)
+{
+    // exact for every n < 2^31: with s = 32 + ceil(log2 d) and m = ceil(2^s / d),
+    // n*m < 2^64 and the rounding error n*(m*d - 2^s) < n*d < 2^s.
+    FastDiv f;
+    uint32_t l = 0;
+    while (l < 32 && (1ull << l) < d) ++l;
+    f.s = 32 + l;
+    f.m = ((1ull << f.s) + d - 1) / d;
+    f.d = d;
+    return f;
+}
+
+bool make_layout(int64_t B, int64_t H, int64_t W, Layout *L)
+{
+    Geom &g = L->g;
+    g.B = B;
+    g.H = H;
+    g.W = W;
+    g.HW = H * W;
+    g.ntx = (int32_t)((W + TW - 1) / TW);
+    g.nty = (int32_t)((H + TH - 1) / TH);
+    g.tpi = (int64_t)g.ntx * g.nty;
+    g.ntiles = B * g.tpi;
+    if (g.ntiles > (int64_t)(UINT32_MAX / KMAX)) return false;  // seam node ids are 32-bit
+    g.nseg = B * H * g.ntx;
+    g.cpi = (H * g.ntx + SCAN_CHUNK - 1) / SCAN_CHUNK;
+    g.nchunk = B * g.cpi;
+    if (g.nchunk > INT32_MAX || B > INT32_MAX) return false;
+    g.divW = make_fastdiv(W > 0 ? (uint32_t)W : 1u);
+
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const size_t nt = (size_t)g.ntiles;
+    L->off_err = take(256);
+    L->off_hdr = take(nt * sizeof(TileHdr));
+    size_t mask_words = nt * TH;
+    if ((size_t)g.nseg > mask_words) mask_words = (size_t)g.nseg;
+    L->off_runmask = take(mask_words * sizeof(uint64_t));
+    L->off_runinfo = take(nt * TPX * sizeof(uint32_t));
+    L->off_gp = take(nt * KMAX * sizeof(uint64_t));
+    L->off_aux = take(nt * KMAX * sizeof(uint32_t));
+    L->off_bslot = take(nt * TW);
+    L->off_rslot = take(nt * TH);
+    L->off_req = take(nt * REQMAX * sizeof(uint16_t));
+    L->off_seg = take((size_t)g.nseg * sizeof(uint32_t));
+    L->off_chunk = take((size_t)g.nchunk * sizeof(uint32_t));
+    L->total = off;
+    return true;
+}
+
+Work bind_work(const Layout &L, void *workspace)
+{
+    char *base = (char *)workspace;
+    Work w;
+    w.err = (uint32_t *)(base + L.off_err);
+    w.hdr = (TileHdr *)(base + L.off_hdr);
+    w.runmask = (uint64_t *)(base + L.off_runmask);
+    w.runinfo = (uint32_t *)(base + L.off_runinfo);
+    w.gp = (uint64_t *)(base + L.off_gp);
+    w.aux = (uint32_t *)(base + L.off_aux);
+    w.bslot = (uint8_t *)(base + L.off_bslot);
+    w.rslot = (uint8_t *)(base + L.off_rslot);
+    w.req = (uint16_t *)(base + L.off_req);
+    w.seg = (uint32_t *)(base + L.off_seg);
+    w.chunk = (uint32_t *)(base + L.off_chunk);
+    return w;
+}
+
+// Shape checks shared by every call.  On success `empty` tells whether the
+// batch has no pixels.
+static int check_shape(int64_t B, int64_t H, int64_t W, bool *empty)
+{
+    if (B < 0 || H < 0 || W < 0) return CCL_ERR_SHAPE;
+    *empty = (B == 0 || H == 0 || W == 0);
+    if (*empty) return CCL_OK;
+    if (H > INT32_MAX / W) return CCL_ERR_TOO_LARGE;  // per-image indices are int32
+    if (B > INT64_MAX / (H * W)) return CCL_ERR_TOO_LARGE;
+    return CCL_OK;
+}
+
+static int finish_launches()
+{
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CCL_OK : CCL_ERR_HIP;
+}
+
+static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int64_t W, int conn,
+                      int flags, int32_t *out, int32_t *counts, void *workspace,
+                      size_t workspace_bytes, void *stream, void **events, int n_events)
+{
+    if (flags & ~CCL_NUMBER) return CCL_ERR_FLAGS;
+    bool empty;
+    int rc = check_shape(B, H, W, &empty);
+    if (rc != CCL_OK) return rc;
+    if (dtype != CCL_U8 && dtype != CCL_U32) return CCL_ERR_DTYPE;
+    if (conn != 4 && conn != 8) return CCL_ERR_CONNECTIVITY;
+    if (events != nullptr && n_events < 6) return CCL_ERR_NULL;
+    hipStream_t s = (hipStream_t)stream;
+    if (empty) {
+        if (counts && B > 0) {
+            launch_zero_i32(counts, B, s);
+            return finish_launches();
+        }
+        return CCL_OK;
+    }
+    if (!colours || !out || !workspace) return CCL_ERR_NULL;
+    Layout L;
+    if (!make_layout(B, H, W, &L)) return CCL_ERR_TOO_LARGE;
+    if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
+    const Work w = bind_work(L, workspace);
+    const int number = (flags & CCL_NUMBER) != 0;
+    const bool need_scan = number || counts != nullptr;
+
+    auto mark = [&](int i) {
+        if (events) (void)hipEventRecord((hipEvent_t)events[i], s);
+    };
+    mark(0);
+    launch_tile(colours, dtype, conn, L.g, w, s);
+    mark(1);
+    launch_seam(L.g, w, s);
+    mark(2);
+    launch_seam_collapse(L.g, w, need_scan ? 1 : 0, s);
+    mark(3);
+    if (need_scan) launch_scan(L.g, w, counts, number, s);
+    mark(4);
+    launch_final(L.g, w, out, number, s);
+    mark(5);
+    return finish_launches();
+}
+
+}  // namespace ccl
+
+using namespace ccl;
+
+extern "C" {
+
+size_t ccl_workspace_bytes(int64_t batch, int64_t height, int64_t width)
+{
+    bool empty;
+    if (check_shape(batch, height, width, &empty) != CCL_OK) return SIZE_MAX;
+    if (empty) return 0;
+    Layout L;
+    if (!make_layout(batch, height, width, &L)) return SIZE_MAX;
+    return L.total;
+}
+
+int ccl_label(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
+              int connectivity, int flags, int32_t *out, int32_t *counts, void *workspace,
+              size_t workspace_bytes, void *stream)
+{
+    return label_impl(colours, dtype, batch, height, width, connectivity, flags, out, counts,
+                      workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+int ccl_label_profiled(const void *colours, int dtype, int64_t batch, int64_t height,
+                       int64_t width, int connectivity, int flags, int32_t *out, int32_t *counts,
+                       void *workspace, size_t workspace_bytes, void *stream, void **events,
+                       int n_events)
+{
+    if (events == nullptr) return CCL_ERR_NULL;
+    return label_impl(colours, dtype, batch, height, width, connectivity, flags, out, counts,
+                      workspace, workspace_bytes, stream, events, n_events);
+}
+
+int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t width,
+               int32_t *labels, int32_t *counts, void *workspace, size_t workspace_bytes,
+               void *stream)
+{
+    bool empty;
+    int rc = check_shape(batch, height, width, &empty);
+    if (rc != CCL_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (empty) {
+        if (counts && batch > 0) {
+            launch_zero_i32(counts, batch, s);
+            return finish_launches();
+        }
+        return CCL_OK;
+    }
+    if (!leaders || !labels || !workspace) return CCL_ERR_NULL;
+    Layout L;
+    if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+    if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
+    const Work w = bind_work(L, workspace);
+    launch_leader_flags(leaders, L.g, w, 1, s);
+    launch_scan(L.g, w, counts, 1, s);
+    launch_leader_assign(leaders, labels, L.g, w, s);
+    return finish_launches();
+}
+
+int ccl_count(const int32_t *leaders, int64_t batch, int64_t height, int64_t width,
+              int32_t *counts, void *workspace, size_t workspace_bytes, void *stream)
+{
+    bool empty;
+    int rc = check_shape(batch, height, width, &empty);
+    if (rc != CCL_OK) return rc;
+    if (!counts) return CCL_ERR_NULL;
+    hipStream_t s = (hipStream_t)stream;
+    if (empty) {
+        if (batch > 0) {
+            launch_zero_i32(counts, batch, s);
+            return finish_launches();
+        }
+        return CCL_OK;
+    }
+    if (!leaders || !workspace) return CCL_ERR_NULL;
+    Layout L;
+    if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+    if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
+    const Work w = bind_work(L, workspace);
+    launch_leader_flags(leaders, L.g, w, 0, s);
+    launch_scan(L.g, w, counts, 0, s);
+    return finish_launches();
+}
+
+const char *ccl_status_string(int status)
+{
+    switch (status) {
+    case CCL_OK: return "ok";
+    case CCL_ERR_NULL: return "a required pointer is NULL";
+    case CCL_ERR_SHAPE: return "batch, height or width is negative";
+    case CCL_ERR_TOO_LARGE: return "image or batch too large to index";
+    case CCL_ERR_CONNECTIVITY: return "connectivity must be 4 or 8";
+    case CCL_ERR_DTYPE: return "dtype must be CCL_U8 or CCL_U32";
+    case CCL_ERR_WORKSPACE: return "workspace smaller than ccl_workspace_bytes()";
+    case CCL_ERR_HIP: return "HIP rejected a kernel launch";
+    case CCL_ERR_FLAGS: return "unknown flag bits";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

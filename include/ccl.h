@@ -1,0 +1,137 @@
+/*
+ * ccl.h -- C ABI of the MI355X (gfx950) connected-component labeller.
+ *
+ * What is computed (per image of a batch, each image on its own):
+ *   Two pixels belong to one region exactly when a chain of neighbours of
+ *   identical colour value joins them.  Neighbours are the 8 pixels around a
+ *   pixel (or the 4 sharing an edge) inside the H x W rectangle: rows do not
+ *   wrap and images never touch ("Accountable AI starts at the pixel",
+ *   ch.01 "The job" and ch.02 "Regions"; "About Connected Components Labeling
+ *   on GPU", section "Connected Components Labeling" for 4 vs 8 neighbours).
+ *   A region's leader is its smallest reading-order index (row * W + col,
+ *   counted inside its image): joins always re-point the larger leader at the
+ *   smaller ("Accountable AI starts at the pixel", ch.04 "Point at a leader").
+ *   Its number is 1 + the count of leaders before it in reading order (same
+ *   page, ch.08 idea 5 "Number without a giant list").  Colours are compared
+ *   as whole stored values: all 32 bits of a CCL_U32 pixel, the byte of a
+ *   CCL_U8 pixel.  Every value, 0 included, forms regions.
+ *
+ * Memory.  Every pointer argument except the host-side ones named below is a
+ * DEVICE pointer on the current HIP device.  Images are contiguous row-major
+ * [batch, height, width]; labels are int32 [batch, height, width]; counts are
+ * int32 [batch].  The caller owns every buffer, including the workspace; the
+ * library allocates nothing and keeps no state between calls, so calls are
+ * reentrant.  Two calls that run at the same time need distinct workspaces.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Calls only enqueue work on it and never synchronise; results are
+ * ready when the stream reaches that point.
+ *
+ * Errors.  Each call returns a ccl_status.  Arguments are checked on the host
+ * before anything is enqueued; on a validation error nothing is enqueued and
+ * the output buffers are untouched.  CCL_ERR_HIP reports a launch that HIP
+ * rejected.  Faults inside kernels are asynchronous and surface at the
+ * caller's next synchronisation, as for any HIP kernel.  A batch, height or
+ * width of 0 is valid and does nothing except writing zeros to `counts`.
+ */
+#ifndef CCL_H
+#define CCL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CCL_OK = 0,
+    CCL_ERR_NULL = -1,          /* a required pointer is NULL                        */
+    CCL_ERR_SHAPE = -2,         /* batch, height or width is negative                */
+    CCL_ERR_TOO_LARGE = -3,     /* height*width > 2^31-1, or the batch needs more
+                                   than 2^32 seam nodes (about 47 Gpx in all)        */
+    CCL_ERR_CONNECTIVITY = -4,  /* connectivity is not 4 or 8                        */
+    CCL_ERR_DTYPE = -5,         /* dtype is not CCL_U8 or CCL_U32                    */
+    CCL_ERR_WORKSPACE = -6,     /* workspace smaller than ccl_workspace_bytes()      */
+    CCL_ERR_HIP = -7,           /* HIP rejected a kernel launch                      */
+    CCL_ERR_FLAGS = -8          /* unknown bits in flags                             */
+} ccl_status;
+
+/* Colour element types; the value is the size of one pixel in bytes. */
+enum { CCL_U8 = 1, CCL_U32 = 4 };
+
+/* ccl_label flag: write numbers 1..n instead of leaders. */
+enum { CCL_NUMBER = 1 };
+
+/*
+ * Bytes of device workspace any call below needs for a batch of this shape.
+ * Pure host arithmetic (no HIP call).  Returns 0 for an empty batch and
+ * SIZE_MAX for a negative shape.  The workspace must be 256-byte aligned (any
+ * HIP allocation is).  Its first 4 bytes are an error word that kernels set
+ * to a nonzero value if an internal safety bound is ever hit; callers that
+ * want to check it zero the workspace once after allocating it.
+ */
+size_t ccl_workspace_bytes(int64_t batch, int64_t height, int64_t width);
+
+/*
+ * Label a batch of colour images: Start, Connect, Collapse and (with
+ * CCL_NUMBER) Number, the four stages of "Accountable AI starts at the pixel",
+ * ch.05.
+ *   colours       device, [batch, height, width] of uint8 (dtype CCL_U8) or
+ *                 uint32 (CCL_U32)
+ *   connectivity  8 (edges and corners) or 4 (edges only)
+ *   flags         0: out[p] = leader of p (per-image reading-order index);
+ *                 CCL_NUMBER: out[p] = number of p's region, 1..n per image
+ *   out           device int32 [batch, height, width]; must not overlap colours
+ *   counts        device int32 [batch] or NULL: number of regions per image
+ *   workspace     device, at least ccl_workspace_bytes(batch, height, width)
+ */
+int ccl_label(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
+              int connectivity, int flags, int32_t *out, int32_t *counts,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ccl_label with stage timing: records `events[0]` before the first kernel
+ * and `events[i]` after stage i, for the stages tile labelling, seam merge,
+ * seam collapse, numbering scan and final write (n_events >= 6; the scan
+ * event is recorded even when no scan runs).  `events` is a host array of
+ * hipEvent_t created by the caller.  Same results as ccl_label.
+ */
+int ccl_label_profiled(const void *colours, int dtype, int64_t batch, int64_t height,
+                       int64_t width, int connectivity, int flags, int32_t *out,
+                       int32_t *counts, void *workspace, size_t workspace_bytes,
+                       void *stream, void **events, int n_events);
+
+/*
+ * Number a leader image: labels[p] = 1 + (number of leaders r < leaders[p]) in
+ * p's image ("Accountable AI starts at the pixel", ch.05 stage Number and
+ * ch.08 idea 5).
+ *   leaders  device int32 [batch, height, width]: a valid leader image, i.e.
+ *            leaders[p] <= p and leaders[leaders[p]] == leaders[p] (as written
+ *            by ccl_label).  Not checked; a value outside [0, height*width)
+ *            yields label 0 and is never dereferenced.
+ *   labels   device int32 [batch, height, width]; may be the same buffer as
+ *            leaders (in-place), must not otherwise overlap it
+ *   counts   device int32 [batch] or NULL
+ */
+int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t width,
+               int32_t *labels, int32_t *counts, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/*
+ * Count the regions of a leader image: counts[b] = number of pixels p of image
+ * b with leaders[p] == p.
+ *   leaders  device int32 [batch, height, width] (any int32 values)
+ *   counts   device int32 [batch], required
+ */
+int ccl_count(const int32_t *leaders, int64_t batch, int64_t height, int64_t width,
+              int32_t *counts, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *ccl_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCL_H */

@@ -1,0 +1,105 @@
+"""The C-ABI library: it loads, exports every function include/ccl.h declares,
+and rejects bad arguments on the host before touching HIP (so these run
+without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ccl.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ccl_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from connected_component_labelling_amd import _load
+    return _load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("ccl_label", "ccl_number", "ccl_count", "ccl_workspace_bytes",
+                     "ccl_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_function(lib):
+    from connected_component_labelling_amd import library_path
+    out = subprocess.run(["nm", "-D", "--defined-only", library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ccl_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in ccl.h but not exported"
+        assert getattr(lib, name) is not None
+
+
+def test_library_is_built_for_gfx950():
+    from connected_component_labelling_amd import library_path
+    blob = open(library_path(), "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_workspace_bytes(lib):
+    assert lib.ccl_workspace_bytes(0, 10, 10) == 0
+    assert lib.ccl_workspace_bytes(1, 0, 10) == 0
+    assert lib.ccl_workspace_bytes(-1, 10, 10) == 2**64 - 1
+    a = lib.ccl_workspace_bytes(1, 256, 256)
+    b = lib.ccl_workspace_bytes(2, 256, 256)
+    assert 0 < a < b
+    assert a % 256 == 0
+    # 806-Mpx sheet: a few bytes per pixel of workspace
+    big = lib.ccl_workspace_bytes(1, 24000, 33600)
+    assert 0 < big < 8 * 24000 * 33600
+    # per-image indices must fit in int32
+    assert lib.ccl_workspace_bytes(1, 65536, 65536) == 2**64 - 1
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("args,status", [
+    # (dtype, B, H, W, conn, flags, workspace_bytes), expected status
+    ((4, 1, 8, 8, 6, 0, 1 << 30), -4),          # connectivity
+    ((2, 1, 8, 8, 8, 0, 1 << 30), -5),          # dtype
+    ((4, -1, 8, 8, 8, 0, 1 << 30), -2),         # shape
+    ((4, 1, 8, -3, 8, 0, 1 << 30), -2),
+    ((4, 1, 65536, 65536, 8, 0, 1 << 30), -3),  # H*W > 2^31-1
+    ((4, 1, 8, 8, 8, 2, 1 << 30), -8),          # flags
+    ((4, 1, 8, 8, 8, 0, 16), -6),               # workspace too small
+])
+def test_label_validation(lib, args, status):
+    dtype, B, H, W, conn, flags, wsb = args
+    rc = lib.ccl_label(FAKE, dtype, B, H, W, conn, flags, FAKE, None, FAKE, wsb, None)
+    assert rc == status
+    assert lib.ccl_status_string(rc)
+
+
+def test_null_pointers(lib):
+    assert lib.ccl_label(None, 4, 1, 8, 8, 8, 0, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert lib.ccl_label(FAKE, 4, 1, 8, 8, 8, 0, None, None, FAKE, 1 << 30, None) == -1
+    assert lib.ccl_label(FAKE, 4, 1, 8, 8, 8, 0, FAKE, None, None, 1 << 30, None) == -1
+    assert lib.ccl_number(None, 1, 8, 8, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert lib.ccl_count(FAKE, 1, 8, 8, None, FAKE, 1 << 30, None) == -1
+    assert lib.ccl_number(FAKE, 1, 8, 8, FAKE, None, FAKE, 16, None) == -6
+    assert lib.ccl_count(FAKE, -1, 8, 8, FAKE, FAKE, 1 << 30, None) == -2
+
+
+def test_empty_batches_are_noops(lib):
+    # nothing to do and no counts to write: returns before any HIP call
+    assert lib.ccl_label(None, 4, 0, 8, 8, 8, 1, None, None, None, 0, None) == 0
+    assert lib.ccl_label(None, 1, 3, 0, 8, 8, 0, None, None, None, 0, None) == 0
+    assert lib.ccl_number(None, 2, 5, 0, None, None, None, 0, None) == 0
+
+
+def test_status_strings(lib):
+    for s in range(-8, 1):
+        assert lib.ccl_status_string(s).decode()
+    assert lib.ccl_status_string(-99) == b"unknown status"

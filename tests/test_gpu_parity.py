@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit for
+bit -- leaders, numbers and counts -- on seeded inputs: ragged small shapes that
+span several tiles, structured adversaries, every workload at its full size,
+and the standalone number / count calls."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ccl():
+    import connected_component_labelling_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m._load()
+    return m
+
+
+def to_device(img: np.ndarray) -> torch.Tensor:
+    if img.dtype == np.uint32:
+        img = img.view(np.int32)
+    return torch.from_numpy(np.ascontiguousarray(img)).cuda()
+
+
+def announce(name, img, conn):
+    print(f"[gpu case] {name} shape={tuple(img.shape)} dtype={img.dtype} conn={conn}", flush=True)
+
+
+def check_case(ccl, name, img, conn=8, workspace=None):
+    """Leaders, numbers and counts of the HIP path equal the oracle's."""
+    announce(name, img, conn)
+    exp_leaders = oracle.label(img, conn)
+    exp_labels, exp_counts = oracle.number(exp_leaders)
+    t = to_device(img)
+    batch = img if img.ndim == 3 else img[None]
+    B, H, W = batch.shape
+    if workspace is None:
+        workspace = torch.zeros(max(ccl.workspace_bytes(B, H, W), 1), dtype=torch.uint8,
+                                device="cuda")
+    leaders, c0 = ccl.label(t, conn, number=False, workspace=workspace)
+    labels, c1 = ccl.label(t, conn, number=True, workspace=workspace)
+    torch.cuda.synchronize()
+    got_leaders = leaders.cpu().numpy()
+    got_labels = labels.cpu().numpy()
+    assert ccl.error_word(workspace) == 0, f"{name}: kernel safety bound hit"
+    if not np.array_equal(got_leaders, exp_leaders):
+        bad = np.argwhere(got_leaders != exp_leaders)
+        raise AssertionError(f"{name}: leaders differ at {len(bad)} pixels, first {bad[:5].tolist()}")
+    assert np.array_equal(got_labels, exp_labels), f"{name}: numbers differ"
+    assert np.array_equal(c0.cpu().numpy(), exp_counts), f"{name}: counts (leader mode) differ"
+    assert np.array_equal(c1.cpu().numpy(), exp_counts), f"{name}: counts differ"
+    return exp_counts
+
+
+# ---------------------------------------------------------------- small shapes
+
+HS = [1, 2, 31, 32, 33, 64, 65, 100]
+WS = [1, 2, 63, 64, 65, 127, 128, 129, 200]
+
+
+@pytest.mark.parametrize("conn", [8, 4])
+@pytest.mark.parametrize("dtype", [np.uint32, np.uint8])
+def test_ragged_shapes_random(ccl, conn, dtype):
+    rng = np.random.default_rng(100 + conn)
+    for H in HS:
+        for W in WS:
+            ncol = int(rng.integers(1, 4))
+            idx = rng.integers(0, ncol, size=(H, W))
+            if dtype == np.uint8:
+                img = idx.astype(np.uint8)
+            else:
+                img = rng.integers(0, 2**32, size=ncol, dtype=np.uint64).astype(np.uint32)[idx]
+            check_case(ccl, f"random {H}x{W} ncol={ncol}", img, conn)
+
+
+@pytest.mark.parametrize("conn", [8, 4])
+def test_ragged_shapes_blobs(ccl, conn):
+    """Smooth multi-colour blobs: long runs and regions that cross many seams."""
+    rng = np.random.default_rng(7)
+    for H, W in [(97, 131), (64, 64), (200, 190), (33, 257), (300, 65)]:
+        base = rng.random((H // 8 + 2, W // 8 + 2))
+        up = np.kron(base, np.ones((8, 8)))[:H, :W]
+        img = (up * 3).astype(np.uint32) + 5
+        check_case(ccl, f"blobs {H}x{W}", img, conn)
+
+
+# ------------------------------------------------------ structured adversaries
+
+def structured_images():
+    out = {}
+    H, W = 130, 200
+    yy, xx = np.mgrid[0:H, 0:W]
+    out["uniform"] = np.full((H, W), 0xFFFFFF, np.uint32)
+    out["checkerboard"] = ((yy + xx) % 2).astype(np.uint32)
+    out["vertical stripes"] = (xx % 2).astype(np.uint8)
+    out["horizontal stripes"] = (yy % 2).astype(np.uint8)
+    out["wide stripes across seams"] = ((xx // 3) % 2).astype(np.uint32)
+    diag = np.zeros((H, W), np.uint32)
+    for d in range(-H, W, 7):                      # 1-px diagonals crossing tile corners
+        idx = np.arange(H)
+        c = idx + d
+        ok = (c >= 0) & (c < W)
+        diag[idx[ok], c[ok]] = 1
+    out["diagonals"] = diag
+    anti = np.zeros((H, W), np.uint32)
+    for d in range(0, H + W, 5):
+        idx = np.arange(H)
+        c = d - idx
+        ok = (c >= 0) & (c < W)
+        anti[idx[ok], c[ok]] = 2
+    out["anti-diagonals"] = anti
+    comb = np.zeros((H, W), np.uint8)
+    comb[:, ::2] = 1
+    comb[H - 1, :] = 1                              # teeth joined at the very bottom
+    out["comb joined at the bottom"] = comb
+    stair = np.zeros((H, W), np.uint32)
+    for i in range(W):                              # staircase: later teeth start higher
+        stair[max(0, H - 1 - i):, i] = 3 if i % 2 == 0 else 0
+    stair[H - 1, :] = 3
+    out["staircase"] = stair
+    out["spiral 200x300"] = synth.spiral_image(200, 300, seed=4)
+    out["sheet 640x960"] = synth.sheet_image(640, 960, seed=6, density=30.0)
+    out["lines 256x256"] = synth.lines_image(256, 256, seed=1)
+    return out
+
+
+@pytest.mark.parametrize("conn", [8, 4])
+def test_structured(ccl, conn):
+    for name, img in structured_images().items():
+        check_case(ccl, name, img, conn)
+
+
+def test_batch_ragged(ccl):
+    rng = np.random.default_rng(3)
+    img = rng.integers(0, 3, size=(3, 70, 130)).astype(np.uint8)
+    check_case(ccl, "batch 3x70x130", img, 8)
+    img = synth.bernoulli_batch(5, 100, 90, seed=9)
+    check_case(ccl, "bernoulli batch 5x100x90", img, 8)
+
+
+# -------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+def test_workload_full_size(ccl, config):
+    img = synth.generate(config)
+    counts = check_case(ccl, f"workload {config}: {synth.CONFIGS[config][0]}", img, 8)
+    print(f"[gpu case] workload {config} regions per image: {counts[:4].tolist()}", flush=True)
+
+
+# ----------------------------------------------------- standalone number/count
+
+def test_number_and_count_standalone(ccl):
+    for name, img in [("sheet", synth.sheet_image(480, 700, seed=2)),
+                      ("bernoulli", synth.bernoulli_batch(4, 130, 77, seed=5))]:
+        announce(f"number/count {name}", img, 8)
+        L = oracle.label(img, 8)
+        exp_labels, exp_counts = oracle.number(L)
+        Ld = torch.from_numpy(np.ascontiguousarray(L)).cuda()
+        labels, counts = ccl.number(Ld)
+        c2 = ccl.count(Ld)
+        torch.cuda.synchronize()
+        assert np.array_equal(labels.cpu().numpy(), exp_labels)
+        assert np.array_equal(np.atleast_1d(counts.cpu().numpy()), np.atleast_1d(exp_counts))
+        assert np.array_equal(np.atleast_1d(c2.cpu().numpy()), np.atleast_1d(oracle.count(L)))
+        # in place
+        labels2, _ = ccl.number(Ld, inplace=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(Ld.cpu().numpy(), exp_labels)
+
+
+def test_number_rejects_out_of_range_leaders_safely(ccl):
+    L = np.arange(64 * 70, dtype=np.int32).reshape(64, 70)
+    L[3, 4] = -5
+    L[5, 6] = 64 * 70 + 100
+    announce("number out-of-range leaders", L, 8)
+    labels, counts = ccl.number(torch.from_numpy(L).cuda())
+    got = labels.cpu().numpy()
+    assert got[3, 4] == 0 and got[5, 6] == 0
+    ok = np.ones_like(L, bool)
+    ok[3, 4] = ok[5, 6] = False
+    # the remaining pixels lead themselves except the two bad ones
+    assert np.array_equal(np.sort(got[ok]), np.arange(1, 64 * 70 - 1))
+
+
+# ----------------------------------------------- determinism, streams, sizes
+
+def test_repeat_calls_are_identical(ccl):
+    img = synth.spiral_image(1024, 1024, seed=3)
+    announce("determinism spiral 1024", img, 8)
+    t = to_device(img)
+    ref, _ = ccl.label(t, 8, number=True)
+    ref = ref.clone()
+    ws = torch.zeros(ccl.workspace_bytes(1, 1024, 1024), dtype=torch.uint8, device="cuda")
+    for _ in range(20):
+        out, _ = ccl.label(t, 8, number=True, workspace=ws)
+        assert torch.equal(out, ref)
+    assert ccl.error_word(ws) == 0
+
+
+def test_side_stream_and_reused_workspace(ccl):
+    imgs = [synth.lines_image(256, 256, seed=s) for s in (1, 2)]
+    announce("side stream", imgs[0], 8)
+    s = torch.cuda.Stream()
+    ws = torch.zeros(ccl.workspace_bytes(1, 256, 256), dtype=torch.uint8, device="cuda")
+    with torch.cuda.stream(s):
+        outs = [ccl.label(to_device(im), 8, number=True, stream=s, workspace=ws)[0].clone()
+                for im in imgs]
+    s.synchronize()
+    for im, o in zip(imgs, outs):
+        exp, _ = oracle.number(oracle.label(im, 8))
+        assert np.array_equal(o.cpu().numpy(), exp)
+
+
+def test_empty_inputs(ccl):
+    for shape in [(0, 5, 5), (2, 0, 7), (3, 4, 0)]:
+        img = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+        out, counts = ccl.label(img, 8, number=True)
+        torch.cuda.synchronize()
+        assert out.shape == shape
+        assert counts.cpu().tolist() == [0] * shape[0]
