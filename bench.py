@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=6000,
                     help="rows of the sheet the CPU baseline labels (0 = skip)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -168,6 +171,14 @@ def main():
         step_ms.append(hip.elapsed_ms(ev[0], ev[5]))
     for ev in events:
         hip.destroy(ev)
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.add(src, 0, out=dst)   # an elementwise kernel: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        del src, dst
     counts = lab.counts.cpu().tolist()
     err = ccl.error_word(lab.workspace)
 

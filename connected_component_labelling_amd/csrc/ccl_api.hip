@@ -34,11 +34,11 @@ bool make_layout(int64_t B, int64_t H, int64_t W, Layout *L)
     g.tpi = (int64_t)g.ntx * g.nty;
     g.ntiles = B * g.tpi;
     if (g.ntiles > (int64_t)(UINT32_MAX / KMAX)) return false;  // seam node ids are 32-bit
-    g.nseg = B * H * g.ntx;
-    g.cpi = (H * g.ntx + SCAN_CHUNK - 1) / SCAN_CHUNK;
-    g.nchunk = B * g.cpi;
-    if (g.nchunk > INT32_MAX || B > INT32_MAX) return false;
+    g.nbands = B * g.nty;
     g.divW = make_fastdiv(W > 0 ? (uint32_t)W : 1u);
+    g.divTpi = make_fastdiv(g.tpi > 0 ? (uint32_t)g.tpi : 1u);
+    g.divNtx = make_fastdiv(g.ntx > 0 ? (uint32_t)g.ntx : 1u);
+    g.divNty = make_fastdiv(g.nty > 0 ? (uint32_t)g.nty : 1u);
 
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -49,17 +49,15 @@ bool make_layout(int64_t B, int64_t H, int64_t W, Layout *L)
     const size_t nt = (size_t)g.ntiles;
     L->off_err = take(256);
     L->off_hdr = take(nt * sizeof(TileHdr));
-    size_t mask_words = nt * TH;
-    if ((size_t)g.nseg > mask_words) mask_words = (size_t)g.nseg;
-    L->off_runmask = take(mask_words * sizeof(uint64_t));
+    L->off_runmask = take(nt * TH * sizeof(uint64_t));
+    L->off_leadmask = take(nt * TH * sizeof(uint64_t));
     L->off_runinfo = take(nt * TPX * sizeof(uint32_t));
     L->off_gp = take(nt * KMAX * sizeof(uint64_t));
-    L->off_aux = take(nt * KMAX * sizeof(uint32_t));
     L->off_bslot = take(nt * TW);
     L->off_rslot = take(nt * TH);
     L->off_req = take(nt * REQMAX * sizeof(uint16_t));
-    L->off_seg = take((size_t)g.nseg * sizeof(uint32_t));
-    L->off_chunk = take((size_t)g.nchunk * sizeof(uint32_t));
+    L->off_seg = take(nt * TH * sizeof(uint32_t));
+    L->off_rowoff = take((size_t)(B * H) * sizeof(uint32_t));
     L->total = off;
     return true;
 }
@@ -71,14 +69,14 @@ Work bind_work(const Layout &L, void *workspace)
     w.err = (uint32_t *)(base + L.off_err);
     w.hdr = (TileHdr *)(base + L.off_hdr);
     w.runmask = (uint64_t *)(base + L.off_runmask);
+    w.leadmask = (uint64_t *)(base + L.off_leadmask);
     w.runinfo = (uint32_t *)(base + L.off_runinfo);
     w.gp = (uint64_t *)(base + L.off_gp);
-    w.aux = (uint32_t *)(base + L.off_aux);
     w.bslot = (uint8_t *)(base + L.off_bslot);
     w.rslot = (uint8_t *)(base + L.off_rslot);
     w.req = (uint16_t *)(base + L.off_req);
     w.seg = (uint32_t *)(base + L.off_seg);
-    w.chunk = (uint32_t *)(base + L.off_chunk);
+    w.rowoff = (uint32_t *)(base + L.off_rowoff);
     return w;
 }
 
@@ -138,6 +136,7 @@ static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int6
     launch_seam_collapse(L.g, w, need_scan ? 1 : 0, s);
     mark(3);
     if (need_scan) launch_scan(L.g, w, counts, number, s);
+    launch_resolve(L.g, w, number, s);
     mark(4);
     launch_final(L.g, w, out, number, s);
     mark(5);

@@ -8,39 +8,44 @@
 
 namespace ccl {
 
-// A tile is 64 columns (one wave64 lane per column) by 32 rows, handled by one
-// 256-thread workgroup: wave w owns rows 8w..8w+7 of the tile.
+// A tile is 64 columns (one wave64 lane per column) by 32 rows.  The tile pass
+// runs one 256-thread workgroup per tile (wave w loads rows 8w..8w+7); the
+// final write runs one wave per tile; the seam passes run one lane per tile.
 constexpr int TW = 64;
 constexpr int TH = 32;
 constexpr int NWAVES = 4;
 constexpr int BLOCK = 64 * NWAVES;
 constexpr int RPW = TH / NWAVES;            // rows per wave
 constexpr int TPX = TW * TH;                // pixels (and at most runs) per tile
-constexpr int KMAX = 2 * TW + 2 * TH - 4;   // distinct border roots <= border pixels
+// Seam-node slots of a tile, one per position a region can touch an open edge
+// through: top-row run k (k), bottom-row run k (64+k), first run of row y
+// (128+y), last run of row y (160+y).  A region's slot is the smallest of its.
+constexpr int KMAX = 2 * TW + 2 * TH;
 constexpr int REQ_TOP = 2 * TW;             // seam requests along the top edge
 constexpr int REQ_LEFT = 3 * TH;            // seam requests along the left edge
 constexpr int REQMAX = REQ_TOP + REQ_LEFT;
-constexpr int SCAN_PT = 16;                 // scan entries per thread
-constexpr int SCAN_CHUNK = BLOCK * SCAN_PT; // scan entries per workgroup
+constexpr int DLAB = 512;                   // run labels a final-write wave stages in LDS
+constexpr int SCAN_PT = 16;                 // row-scan entries per thread
 
-static_assert(KMAX < 255, "border slots are stored in one byte, 0xFF = none");
-static_assert(TH <= 64 && TW == 64, "row masks are one wave64 ballot");
+static_assert(KMAX <= 255, "seam slots are stored in one byte");
+static_assert(TH == 32 && TW == 64, "row masks are one wave64 ballot, tile rows are lanes");
 
 // Bit layout of a per-run record written by the tile pass.
-//   bit 31 set:  the run's tile-local root has seam node <slot> = bits 0..7
-//   bit 31 clear: the root is final inside the tile: bits 0..10 = row*64+col of
-//                 the root, bits 11..16 = number of earlier final roots in that row
+//   bit 31 set:   the run's region has seam node <slot> = bits 0..7
+//   bit 31 clear: the region lies inside the tile; bits 0..10 = row*64+col of
+//                 its first pixel (its tile-local root)
 constexpr uint32_t INFO_BORDER = 0x80000000u;
 
 // error word bits (first word of the workspace)
 constexpr uint32_t ERR_LOOP = 1u;      // a find/union loop hit its safety bound
-constexpr uint32_t ERR_SLOTS = 2u;     // more border roots than KMAX (impossible)
 
 struct TileHdr {
-    uint32_t nruns;   // runs in the tile
-    uint32_t nnodes;  // seam nodes (border roots)
-    uint32_t ntop;    // seam requests along the top edge
-    uint32_t nleft;   // seam requests along the left edge
+    uint32_t nruns;     // runs in the tile
+    uint32_t ntop;      // seam requests along the top edge
+    uint32_t nleft;     // seam requests along the left edge
+    uint32_t pad;
+    uint64_t used[3];   // seam slots in use (bit s of word s/64)
+    uint64_t pad2;
 };
 
 // exact unsigned division of n < 2^31 by a fixed d >= 1: q = (n*m) >> s
@@ -56,30 +61,35 @@ struct Geom {
     int32_t ntx, nty;           // tiles per row / per column of one image
     int64_t tpi;                // tiles per image
     int64_t ntiles;             // tiles in the batch
-    int64_t nseg;               // 64-px row segments in the batch = B*H*ntx
-    int64_t cpi;                // scan chunks per image
-    int64_t nchunk;             // scan chunks in the batch
-    FastDiv divW;
+    int64_t nbands;             // B * nty
+    FastDiv divW;               // by W
+    FastDiv divTpi;             // by tiles per image
+    FastDiv divNtx;             // by tiles per image row
+    FastDiv divNty;             // by tile rows per image
 };
 
+// Per tile row ("row segment": 64 pixels of one image row), tile-major:
+// entry t*TH + y is row y of tile t.
 struct Work {
     uint32_t *err;      // [1]
     TileHdr *hdr;       // [ntiles]
-    uint64_t *runmask;  // [ntiles][TH] run starts per tile row; [nseg] root masks for ccl_number
-    uint32_t *runinfo;  // [ntiles][TPX]
-    uint64_t *gp;       // [ntiles][KMAX] seam nodes: (key of parent << 32) | parent node
-    uint32_t *aux;      // [ntiles][KMAX] (row << 8 | rank) -> rank within the row segment
-    uint8_t *bslot;     // [ntiles][TW] seam slot of each bottom-row pixel
-    uint8_t *rslot;     // [ntiles][TH] seam slot of each right-column pixel
-    uint16_t *req;      // [ntiles][REQMAX] seam requests
-    uint32_t *seg;      // [nseg] leaders per row segment, then their exclusive prefix
-    uint32_t *chunk;    // [nchunk] scan partial sums
+    uint64_t *runmask;  // [ntiles*TH] run starts of each row segment
+    uint64_t *leadmask; // [ntiles*TH] leaders of the image in each row segment
+    uint32_t *runinfo;  // [ntiles*TPX] per-run records
+    uint64_t *gp;       // [ntiles*KMAX] seam nodes: (key of parent << 32) | parent node;
+                        //   after the resolve pass: the value of the node's pixels
+    uint8_t *bslot;     // [ntiles*TW] seam slot of each bottom-row pixel
+    uint8_t *rslot;     // [ntiles*TH] seam slot of each right-column pixel
+    uint16_t *req;      // [ntiles*REQMAX] seam requests
+    uint32_t *seg;      // [ntiles*TH] leaders per row segment, then their exclusive
+                        //   prefix in reading order (per image)
+    uint32_t *rowoff;   // [B*H] leaders per image row, then their exclusive prefix
 };
 
 struct Layout {
     Geom g;
-    size_t off_err, off_hdr, off_runmask, off_runinfo, off_gp, off_aux, off_bslot, off_rslot,
-        off_req, off_seg, off_chunk, total;
+    size_t off_err, off_hdr, off_runmask, off_leadmask, off_runinfo, off_gp, off_bslot,
+        off_rslot, off_req, off_seg, off_rowoff, total;
 };
 
 // Fills `L` for a batch shape; returns false if the shape is too large to
@@ -93,6 +103,7 @@ void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, cons
 void launch_seam(const Geom &g, const Work &w, hipStream_t s);
 void launch_seam_collapse(const Geom &g, const Work &w, int count_survivors, hipStream_t s);
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, hipStream_t s);
+void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s);
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, hipStream_t s);
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
                          hipStream_t s);

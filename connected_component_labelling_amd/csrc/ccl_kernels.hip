@@ -1,32 +1,34 @@
 // ccl_kernels.hip -- gfx950 kernels of the tiled union-find labeller.
 //
 // The four stages of "Accountable AI starts at the pixel" (ch.05 "Start,
-// Connect, Collapse, Number"), mapped onto 64x32 tiles:
+// Connect, Collapse, Number") mapped onto 64x32 tiles:
 //
 //   tile_label_kernel     Start + Connect + Collapse inside one tile, in LDS.
 //                         Start groups each tile row into runs of one colour by
 //                         a wave64 ballot (ch.08 idea 1, "Let the warp find the
-//                         runs"); Connect joins each run to the runs of the row
-//                         above only where no other join already covers the
-//                         pair (ch.08 idea 2, "Skip joins someone else makes"),
-//                         row above first (ch.08 "the order of the joins"),
-//                         with an atomic minimum that re-points the larger
-//                         leader at the smaller and retries when it lost a race
-//                         (ch.06 "Two workers, one leader"; the Union routine of
-//                         "About Connected Components Labeling on GPU", section
+//                         runs").  Connect joins each run once to every run of
+//                         the row above that touches it and has its colour, so
+//                         no join is made twice (ch.08 idea 2, "Skip joins
+//                         someone else makes"), always against the row above
+//                         (ch.08 "the order of the joins"), with an atomic
+//                         minimum that re-points the larger leader at the
+//                         smaller and retries when it lost a race (ch.06 "Two
+//                         workers, one leader"; the Union routine of "About
+//                         Connected Components Labeling on GPU", section
 //                         "Block-based Union-Find") and path halving (ch.08
-//                         idea 3).  Regions that touch a tile edge get a seam
-//                         node; the joins across the tile's top and left edges
-//                         are written as requests.
+//                         idea 3).  Regions that touch an edge shared with
+//                         another tile get a seam node; the joins across the
+//                         tile's top and left edges are written as requests.
 //   seam_merge_kernel     the requests: global atomic-min unions of seam nodes,
-//                         keyed by the reading-order index of each node's pixel.
+//                         ordered by the reading-order index of each node's pixel.
 //   seam_collapse_kernel  every seam node points straight at its leader (ch.05
-//                         Collapse); surviving leaders are counted per row
-//                         segment for Number.
-//   scan_*_kernel         exclusive prefix of leaders per 64-px row segment in
-//                         reading order, per image (the prefix sum in the
-//                         middle of Number, ch.12 "The call").
-//   final_write_kernel    each pixel gets its leader or 1 + the leaders before
+//                         Collapse); leaders of the whole image are added to
+//                         their row segment's leader mask and count.
+//   scan kernels          exclusive prefix of leaders per 64-px row segment in
+//                         reading order, per image (the prefix sum in the middle
+//                         of Number, ch.12 "The call").
+//   resolve_kernel        each seam node gets the value of its pixels.
+//   final_write_kernel    every pixel gets its leader or 1 + the leaders before
 //                         it (ch.08 idea 5), written once, coalesced.
 //
 // Standalone ccl_number / ccl_count use leader_flag_kernel (one wave64 ballot
@@ -41,15 +43,17 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ uint64_t mask_lt(int lane) { return (1ull << lane) - 1ull; }
 
+__device__ __forceinline__ uint64_t mask_le(int x) { return x >= 63 ? ~0ull : ((2ull << x) - 1ull); }
+
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
-// Map workgroup ids to tiles so that each XCD (workgroups are dealt to the 8
-// XCDs round-robin) works on one contiguous range of tiles: neighbouring
-// tiles then share that XCD's L2.
-__device__ __forceinline__ int64_t remap_tile(int64_t bid, int64_t n)
+// Map workgroup ids to work items so that each XCD (workgroups are dealt to the
+// 8 XCDs round-robin) gets one contiguous range: neighbouring tiles then share
+// that XCD's L2.
+__device__ __forceinline__ uint32_t remap_tile(uint32_t bid, uint32_t n)
 {
-    const int64_t q = n >> 3, r = n & 7;
-    const int64_t j = bid & 7, i = bid >> 3;
+    const uint32_t q = n >> 3, r = n & 7u;
+    const uint32_t j = bid & 7u, i = bid >> 3;
     return j * q + (j < r ? j : r) + i;
 }
 
@@ -63,32 +67,48 @@ __device__ __forceinline__ void set_err(uint32_t *err, uint32_t bit)
     __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// exclusive prefix over the workgroup; `total` receives the sum of all values
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *sWave, uint32_t &total)
+struct TilePos {
+    uint32_t b, ty, tx;
+    int64_t y0, x0;
+    int vh, vw;
+};
+
+__device__ __forceinline__ TilePos tile_pos(uint32_t t, const Geom &g)
 {
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
-    if (lane == 63) sWave[wave] = x;
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NWAVES; ++i) {
-        const uint32_t s = sWave[i];
-        off += (i < wave) ? s : 0u;
-        tot += s;
-    }
-    __syncthreads();
-    total = tot;
-    return off + x - v;
+    TilePos p;
+    p.b = fast_div(t, g.divTpi);
+    const uint32_t tt = t - p.b * (uint32_t)g.tpi;
+    p.ty = fast_div(tt, g.divNtx);
+    p.tx = tt - p.ty * (uint32_t)g.ntx;
+    p.y0 = (int64_t)p.ty * TH;
+    p.x0 = (int64_t)p.tx * TW;
+    p.vh = (int)(g.H - p.y0 < TH ? g.H - p.y0 : TH);
+    p.vw = (int)(g.W - p.x0 < TW ? g.W - p.x0 : TW);
+    return p;
+}
+
+// tile, row and column (inside the tile) of pixel `key` of image b
+__device__ __forceinline__ void pixel_tile(uint32_t key, uint32_t b, const Geom &g, uint32_t &t,
+                                           uint32_t &row, uint32_t &col)
+{
+    const uint32_t Y = fast_div(key, g.divW);
+    const uint32_t X = key - Y * (uint32_t)g.W;
+    t = b * (uint32_t)g.tpi + (Y / TH) * (uint32_t)g.ntx + X / TW;
+    row = Y % TH;
+    col = X % TW;
 }
 
 // ------------------------------------------------------- union-find in LDS
-// Parents point only at smaller run ids; a root points at itself.
+// Run slots are numbered y*64+k (k-th run of tile row y): reading order, so a
+// smaller slot is an earlier run.  Parents only point at smaller slots; a root
+// points at itself.  A root's word may also carry its seam slot in bits 16..23
+// (stored as 255 - slot, so the smallest slot wins an atomic maximum).  The
+// arrays are stored with column bits 3..5 XOR-ed with row bits 0..2 so that
+// eight rows accessed together fall on different LDS banks.
+
+constexpr uint32_t PMASK = 0xFFFFu;
+
+__device__ __forceinline__ uint32_t sw(uint32_t slot) { return slot ^ (((slot >> 6) & 7u) << 3); }
 
 // Every find/union carries a step budget: a correct forest never comes near
 // it (tile chains are shorter than a tile's runs, and halving keeps seam chains
@@ -97,19 +117,19 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *sWave, uint32_t &
 constexpr int LDS_BUDGET = 1 << 16;
 constexpr int GLOBAL_BUDGET = 1 << 22;
 
-__device__ __forceinline__ uint32_t lds_load(const uint32_t *p)
+__device__ __forceinline__ uint32_t lds_parent(const uint32_t *P, uint32_t x)
 {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __hip_atomic_load(&P[sw(x)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & PMASK;
 }
 
 __device__ uint32_t lds_find(uint32_t *P, uint32_t x, int &budget)
 {
     while (budget-- > 0) {
-        const uint32_t p = lds_load(&P[x]);
+        const uint32_t p = lds_parent(P, x);
         if (p == x) return x;
-        const uint32_t g = lds_load(&P[p]);
+        const uint32_t g = lds_parent(P, p);
         if (g == p) return p;
-        atomicMin(&P[x], g);  // path halving: an arrow only moves closer to the root
+        atomicMin(&P[sw(x)], g);  // path halving: an arrow only moves closer to the root
         x = g;
     }
     return x;
@@ -128,20 +148,12 @@ __device__ void lds_unite(uint32_t *P, uint32_t a, uint32_t b, uint32_t *err)
             a = b;
             b = t;
         }
-        const uint32_t old = atomicMin(&P[b], a);  // re-point the larger root at the smaller
-        if (old == b) return;                      // b was still a root: joined
-        b = old;                                   // someone re-pointed b first: retry
+        const uint32_t old = atomicMin(&P[sw(b)], a);  // re-point the larger root at the smaller
+        if (old == b) return;                          // b was still a root: joined
+        b = old;                                       // someone re-pointed b first: retry
         --budget;
     }
     set_err(err, ERR_LOOP);
-}
-
-__device__ uint32_t lds_root(uint32_t *P, uint32_t x, uint32_t *err)
-{
-    int budget = LDS_BUDGET;
-    const uint32_t r = lds_find(P, x, budget);
-    if (budget <= 0) set_err(err, ERR_LOOP);
-    return r;
 }
 
 // --------------------------------------------------- union-find in global
@@ -191,8 +203,10 @@ __device__ void g_unite(uint64_t *gp, uint32_t a, uint32_t b, uint32_t *err)
         uint32_t lo = ra, hi = rb;
         uint64_t lo_rec = ra_rec, hi_rec = rb_rec;
         if (ra_rec > rb_rec) {
-            lo = rb; hi = ra;
-            lo_rec = rb_rec; hi_rec = ra_rec;
+            lo = rb;
+            hi = ra;
+            lo_rec = rb_rec;
+            hi_rec = ra_rec;
         }
         const uint64_t old = g_min(&gp[hi], lo_rec);
         if (old == hi_rec) return;  // hi was still a root: joined
@@ -214,39 +228,45 @@ __device__ uint32_t g_root(uint64_t *gp, uint32_t x, uint64_t &root_rec, uint32_
 }
 
 // ------------------------------------------------------------- tile pass
+// One workgroup per 64x32 tile.
+//   1 Start    each wave loads 8 rows; a ballot per row marks run starts and
+//              the start lanes record their run (colour, start column, parent).
+//   2 Connect  one thread per run joins it to every run of the row above that
+//              touches its span (widened by one pixel each side for 8
+//              neighbours) and has its colour.
+//   3 Collapse every run points at its tile root; a run on an edge shared with
+//              another tile offers its edge position as the region's seam slot.
+//   4 Write    per-run records, the leader mask and count of each row
+//              segment, seam nodes, the slots of the bottom row and right
+//              column, and the seam requests for the top and left edges (joins
+//              with pixels of the tiles above and to the left, found from a
+//              one-pixel halo).
 
 template <typename T, int CONN>
 __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__ img, Geom g,
                                                            Work w)
 {
-    __shared__ uint32_t sP[TPX];          // run parents
-    __shared__ uint32_t sStart[TPX];      // run start: row << 6 | col
-    __shared__ uint16_t sNb[TPX + 1];     // final (non-border) roots before each run
-    __shared__ uint8_t sFs[TPX];          // border flag, then seam slot (0xFF: none)
-    __shared__ uint32_t sRowBase[TH + 1];
-    __shared__ uint32_t sRowCnt[TH];
-    __shared__ uint32_t sXcol[NWAVES][TW];   // colours of each wave's last row
-    __shared__ uint32_t sXrid[NWAVES][TW];   // run ids of each wave's last row
-    __shared__ uint32_t sColC[TH];           // colour at column 0 of each row
-    __shared__ uint32_t sHalo[TH];           // colour left of column 0 of each row
-    __shared__ uint32_t sWave[NWAVES];
+    __shared__ uint64_t sMask[TH];   // run starts of each tile row
+    __shared__ uint32_t sP[TPX];     // parent of run slot (swizzled); roots: + seam slot
+    __shared__ uint32_t sRC[TPX];    // colour of run slot (swizzled)
+    __shared__ uint8_t sRX[TPX];     // start column of run slot (swizzled)
+    __shared__ uint32_t sColC[TH];   // colour at column 0 of each row
+    __shared__ uint32_t sHalo[TH];   // colour left of column 0 of each row
+    __shared__ uint64_t sUsed[KMAX / 64];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int64_t t = remap_tile(blockIdx.x, g.ntiles);
-    const int64_t b = t / g.tpi;
-    const int64_t tt = t - b * g.tpi;
-    const int ty = (int)(tt / g.ntx), tx = (int)(tt - (int64_t)ty * g.ntx);
-    const int64_t y0 = (int64_t)ty * TH, x0 = (int64_t)tx * TW;
-    const int vh = (int)(g.H - y0 < TH ? g.H - y0 : TH);
-    const int vw = (int)(g.W - x0 < TW ? g.W - x0 : TW);
-    const bool has_top = ty > 0, has_left = tx > 0;
+    const uint32_t t = remap_tile(blockIdx.x, (uint32_t)g.ntiles);
+    const TilePos tp = tile_pos(t, g);
+    const int64_t y0 = tp.y0, x0 = tp.x0;
+    const int vh = tp.vh, vw = tp.vw;
+    const bool has_top = tp.ty > 0, has_left = tp.tx > 0;
     const bool has_bottom = y0 + TH < g.H, has_right = x0 + TW < g.W;
     const int64_t W = g.W;
-    const T *im = img + b * g.HW;
+    const T *im = img + (int64_t)tp.b * g.HW;
     const bool lane_ok = lane < vw;
     const uint64_t lt = mask_lt(lane);
 
-    // ---- load the tile (one coalesced row per wave instruction) and halos
+    // ---- 1 Start
     uint32_t c[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
@@ -261,181 +281,133 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
         if (lane == TW - 1 && has_right) hp1 = up[TW];
     }
     if (wave == 1 && has_left && lane < vh) sHalo[lane] = im[(y0 + lane) * W + x0 - 1];
+    if (tid < KMAX / 64) sUsed[tid] = 0;
 
-    // ---- Start: runs of one colour along each tile row, by ballot
     uint64_t m[RPW];
-    uint32_t k[RPW];
-    bool st[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int y = wave * RPW + i;
         const bool valid = lane_ok && y < vh;
         const uint32_t left = __shfl_up(c[i], 1);
-        st[i] = valid && (lane == 0 || left != c[i]);
-        m[i] = __ballot(st[i]);
-        k[i] = popc64(m[i] & lt) + (st[i] ? 0u : 0xFFFFFFFFu);  // run index within the row
+        const bool st = valid && (lane == 0 || left != c[i]);
+        m[i] = __ballot(st);
+        if (st) {
+            const uint32_t slot = (uint32_t)(y * 64) + popc64(m[i] & lt);
+            sRC[sw(slot)] = c[i];
+            sRX[sw(slot)] = (uint8_t)lane;
+            sP[sw(slot)] = slot;
+        }
         if (lane == 0) {
-            sRowCnt[y] = popc64(m[i]);
+            sMask[y] = m[i];
             sColC[y] = c[i];
-            w.runmask[t * TH + y] = m[i];  // rows past the image edge store 0
+            w.runmask[(size_t)t * TH + y] = m[i];  // rows past the image edge store 0
         }
     }
-    sXcol[wave][lane] = c[RPW - 1];
     __syncthreads();
 
-    // row bases: exclusive prefix of the run counts (every wave computes it)
-    uint32_t rc = lane < TH ? sRowCnt[lane] : 0u;
-    const uint32_t own = rc;
+    // ---- 2 Connect: thread (row ry, rm) handles runs rm, rm+8, ... of row ry
+    const int ry = tid >> 3, rm = tid & 7;
+    if (ry >= 1 && ry < vh) {
+        const uint64_t mr = sMask[ry], ma = sMask[ry - 1];
+        const int cnt = (int)popc64(mr);
+        for (int k = rm; k < cnt; k += 8) {
+            const uint32_t slot = (uint32_t)(ry * 64 + k);
+            const int s0 = sRX[sw(slot)];
+            const int e0 = (k + 1 < cnt) ? (int)sRX[sw(slot + 1)] - 1 : vw - 1;
+            const uint32_t cc = sRC[sw(slot)];
+            const int xa = (CONN == 8 && s0 > 0) ? s0 - 1 : s0;
+            const int xb = (CONN == 8 && e0 + 1 < vw) ? e0 + 1 : e0;
+            const int ka = (int)popc64(ma & mask_le(xa)) - 1;
+            const int kb = (int)popc64(ma & mask_le(xb)) - 1;
+            for (int j = ka; j <= kb; ++j) {
+                const uint32_t above = (uint32_t)((ry - 1) * 64 + j);
+                if (sRC[sw(above)] == cc) lds_unite(sP, slot, above, w.err);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 3 Collapse; runs on an edge shared with another tile offer their
+    //      edge position as the region's seam slot (the smallest wins)
+    if (ry < vh) {
+        const int cnt = (int)popc64(sMask[ry]);
+        for (int k = rm; k < cnt; k += 8) {
+            const uint32_t slot = (uint32_t)(ry * 64 + k);
+            int budget = LDS_BUDGET;
+            const uint32_t root = lds_find(sP, slot, budget);
+            if (budget <= 0) set_err(w.err, ERR_LOOP);
+            if (root != slot) atomicMin(&sP[sw(slot)], root);
+            uint32_t es = 255;
+            if (has_right && k == cnt - 1) es = 2 * TW + TH + ry;
+            if (has_left && k == 0) es = 2 * TW + ry;
+            if (has_bottom && ry == TH - 1) es = TW + k;
+            if (has_top && ry == 0) es = k;
+            if (es != 255) atomicMax(&sP[sw(root)], ((255u - es) << 16) | root);
+        }
+    }
+    __syncthreads();
+
+    // ---- 4 Write: the same thread-per-run mapping as Connect
+    // run base of each row (lane y < TH): runs in the rows above it
+    uint32_t rc = lane < TH ? popc64(sMask[lane]) : 0u;
+    const uint32_t rown = rc;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
         const uint32_t v = __shfl_up(rc, d);
         if (lane >= d) rc += v;
     }
     const uint32_t R = __shfl(rc, TH - 1);
-    const uint32_t rex = rc - own;
-    if (wave == 0 && lane < TH) sRowBase[lane] = rex;
-    if (wave == 0 && lane == 0) sRowBase[TH] = R;
-
-    uint32_t rid[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        rid[i] = __shfl(rex, wave * RPW + i) + k[i];
-        if (st[i]) {
-            sP[rid[i]] = rid[i];
-            sStart[rid[i]] = (uint32_t)((wave * RPW + i) << 6 | lane);
-            sFs[rid[i]] = 0;
-        }
-    }
-    sXrid[wave][lane] = rid[RPW - 1];
-    __syncthreads();
-
-    // ---- Connect inside the tile, row above first
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int y = wave * RPW + i;
-        uint32_t ac = 0, ar = 0;
-        if (i > 0) {
-            ac = c[i - 1];
-            ar = rid[i - 1];
-        } else if (wave > 0) {
-            ac = sXcol[wave - 1][lane];
-            ar = sXrid[wave - 1][lane];
-        }
-        const uint32_t acm = __shfl_up(ac, 1), acp = __shfl_down(ac, 1);
-        const uint32_t arm = __shfl_up(ar, 1), arp = __shfl_down(ar, 1);
-        if (y >= 1 && y < vh && lane_ok) {
-            const uint32_t cur = c[i];
-            const bool um1 = lane >= 1 && acm == cur;
-            const bool u0 = ac == cur;
-            const bool up1 = lane + 1 < vw && acp == cur;
-            if (CONN == 8) {
-                if (up1 && !u0) lds_unite(sP, rid[i], arp, w.err);
-                if (st[i]) {
-                    if (um1) lds_unite(sP, rid[i], arm, w.err);
-                    else if (u0) lds_unite(sP, rid[i], ar, w.err);
-                }
-            } else {
-                if (u0 && (st[i] || !um1)) lds_unite(sP, rid[i], ar, w.err);
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- Collapse inside the tile
-    for (uint32_t r = tid; r < R; r += BLOCK) {
-        const uint32_t root = lds_root(sP, r, w.err);
-        atomicMin(&sP[r], root);
-    }
-    __syncthreads();
-
-    // ---- roots of regions touching an edge that has a neighbour tile
-    if (tid < TW) {
-        const uint32_t r = sRowBase[0] + tid;
-        if (has_top && r < sRowBase[1]) sFs[sP[r]] = 1;
-    } else if (tid < 2 * TW) {
-        const uint32_t r = sRowBase[TH - 1] + (tid - TW);
-        if (has_bottom && r < sRowBase[TH]) sFs[sP[r]] = 1;
-    } else if (tid < 2 * TW + TH) {
-        const int y = tid - 2 * TW;
-        if (has_left && y < vh) sFs[sP[sRowBase[y]]] = 1;
-    } else if (tid < 2 * TW + 2 * TH) {
-        const int y = tid - 2 * TW - TH;
-        if (has_right && y < vh) sFs[sP[sRowBase[y + 1] - 1]] = 1;
-    }
-    __syncthreads();
-
-    // ---- seam slots of border roots, ranks of the other roots (run order)
-    {
-        const uint32_t r0 = (uint32_t)tid * 8;
-        uint32_t nb = 0, bd = 0, kinds = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t r = r0 + j;
-            if (r < R && sP[r] == r) {
-                if (sFs[r]) {
-                    ++bd;
-                    kinds |= 2u << (2 * j);
+    const uint32_t rb_row = __shfl(rc - rown, ry);
+    uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
+    uint64_t leadbits = 0;  // start columns of this thread's runs that are final roots
+    if (ry < vh) {
+        const int cnt = (int)popc64(sMask[ry]);
+        for (int k = rm; k < cnt; k += 8) {
+            const uint32_t slot = (uint32_t)(ry * 64 + k);
+            const uint32_t pv = sP[sw(slot)];
+            const uint32_t root = pv & PMASK;
+            const uint32_t rv = root == slot ? pv : sP[sw(root)];
+            const uint32_t es = 255u - (rv >> 16);
+            const uint32_t rcol = sRX[sw(root)];
+            rinfo[rb_row + k] = es != 255u ? (INFO_BORDER | es) : ((root & ~63u) | rcol);
+            if (root == slot) {
+                if (es == 255u) {
+                    leadbits |= 1ull << rcol;
                 } else {
-                    ++nb;
-                    kinds |= 1u << (2 * j);
+                    const uint32_t node = t * KMAX + es;
+                    const uint32_t key = (uint32_t)(y0 + ry) * (uint32_t)W + (uint32_t)x0 + rcol;
+                    w.gp[node] = ((uint64_t)key << 32) | node;
+                    atomicOr((unsigned long long *)&sUsed[es >> 6], 1ull << (es & 63u));
                 }
             }
         }
-        uint32_t total;
-        const uint32_t base = block_exclusive_scan((nb << 16) | bd, sWave, total);
-        uint32_t run_nb = base >> 16, run_bd = base & 0xFFFFu;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t r = r0 + j;
-            if (r < R) {
-                sNb[r] = (uint16_t)run_nb;
-                const uint32_t kd = (kinds >> (2 * j)) & 3u;
-                if (kd == 2) {
-                    sFs[r] = (uint8_t)(run_bd < KMAX ? run_bd : KMAX - 1);
-                    ++run_bd;
-                } else if (kd == 1) {
-                    sFs[r] = 0xFF;
-                    ++run_nb;
-                }
-            }
-        }
-        if (tid == 0) {
-            sNb[R] = (uint16_t)(total >> 16);
-            const uint32_t nnodes = total & 0xFFFFu;
-            if (nnodes > KMAX) set_err(w.err, ERR_SLOTS);
-            w.hdr[t].nruns = R;
-            w.hdr[t].nnodes = nnodes < KMAX ? nnodes : KMAX;
-        }
     }
-    __syncthreads();
-
-    // ---- per-run records, seam nodes, segment counts, edge slots
-    uint32_t *rinfo = w.runinfo + t * TPX;
-    for (uint32_t r = tid; r < R; r += BLOCK) {
-        const uint32_t root = sP[r];
-        const uint32_t s0 = sStart[root];
-        const uint32_t fs = sFs[root];
-        const uint32_t rank = (uint32_t)sNb[root] - (uint32_t)sNb[sRowBase[s0 >> 6]];
-        rinfo[r] = fs != 0xFF ? (INFO_BORDER | fs) : ((rank << 11) | s0);
-        if (root == r && fs != 0xFF) {
-            const uint32_t node = (uint32_t)(t * KMAX) + fs;
-            const uint64_t key = (uint64_t)((y0 + (s0 >> 6)) * W + x0 + (s0 & 63));
-            w.gp[node] = (key << 32) | node;
-            w.aux[node] = ((s0 >> 6) << 8) | rank;
-        }
+    // the 8 threads of a row sit in adjacent lanes: OR their leader columns
+    leadbits |= __shfl_xor(leadbits, 1);
+    leadbits |= __shfl_xor(leadbits, 2);
+    leadbits |= __shfl_xor(leadbits, 4);
+    if (rm == 0) {
+        w.leadmask[(size_t)t * TH + ry] = leadbits;   // rows past the image edge store 0
+        w.seg[(size_t)t * TH + ry] = popc64(leadbits);
     }
-    if (tid < vh)
-        w.seg[(b * g.H + y0 + tid) * g.ntx + tx] =
-            (uint32_t)sNb[sRowBase[tid + 1]] - (uint32_t)sNb[sRowBase[tid]];
+    // seam slot of the region of the run containing (row y, column x)
+    auto slot_of = [&](int y, int x, bool ok) -> uint32_t {
+        if (!ok) return 0u;
+        const uint32_t run = (uint32_t)(y * 64) + popc64(sMask[y] & mask_le(x)) - 1u;
+        const uint32_t root = sP[sw(run)] & PMASK;
+        return 255u - (sP[sw(root)] >> 16);
+    };
     if (has_bottom && wave == NWAVES - 1 && lane_ok)
-        w.bslot[t * TW + lane] = sFs[sP[rid[RPW - 1]]];
-    if (has_right && tid >= TW && tid < TW + TH && tid - TW < vh)
-        w.rslot[t * TH + (tid - TW)] = sFs[sP[sRowBase[tid - TW + 1] - 1]];
+        w.bslot[(size_t)t * TW + lane] = (uint8_t)slot_of(TH - 1, lane, true);
+    if (has_right && wave == 2 && lane < vh)
+        w.rslot[(size_t)t * TH + lane] = (uint8_t)slot_of(lane, TW - 1, true);
 
-    // ---- seam requests across the top edge (wave 0: tile row 0 against the row above)
+    // seam requests across the top edge: tile row 0 against the row above
     if (wave == 0) {
         uint32_t ntop = 0;
         if (has_top) {
+            const uint32_t me = slot_of(0, lane, lane_ok);
+            const bool st0 = (m[0] >> lane) & 1ull;
             const uint32_t cur = c[0];
             const uint32_t hl = __shfl_up(hrow, 1), hr = __shfl_down(hrow, 1);
             const bool vm1 = lane >= 1 || has_left;
@@ -448,8 +420,8 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
             bool ra = false, rb = false;
             int xb = lane;
             if (CONN == 8) {
-                ra = up1 && !u0;
-                if (st[0]) {
+                ra = up1 && !u0;  // up-right starts a stretch of the run's colour
+                if (st0) {        // a run's first pixel also takes up-left or up
                     if (um1) {
                         rb = true;
                         xb = lane - 1;
@@ -458,27 +430,25 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
                     }
                 }
             } else {
-                rb = u0 && (st[0] || !um1);
+                rb = u0 && (st0 || !um1);
             }
             const uint64_t ba = __ballot(ra), bb = __ballot(rb);
             const uint32_t pos = popc64(ba & lt) + popc64(bb & lt);
-            if (ra || rb) {
-                const uint32_t me = sFs[sP[rid[0]]];
-                uint16_t *q = w.req + t * REQMAX;
-                if (rb) q[pos] = (uint16_t)(me | ((uint32_t)(xb + 1) << 8));
-                if (ra) q[pos + (rb ? 1 : 0)] = (uint16_t)(me | ((uint32_t)(lane + 2) << 8));
-            }
+            uint16_t *q = w.req + (size_t)t * REQMAX;
+            if (rb) q[pos] = (uint16_t)(me | ((uint32_t)(xb + 1) << 8));
+            if (ra) q[pos + (rb ? 1 : 0)] = (uint16_t)(me | ((uint32_t)(lane + 2) << 8));
             ntop = popc64(ba) + popc64(bb);
         }
         if (lane == 0) w.hdr[t].ntop = ntop;
     }
 
-    // ---- seam requests across the left edge (wave 1: one lane per tile row)
+    // seam requests across the left edge: one lane per tile row
     if (wave == 1) {
         uint32_t nleft = 0;
         if (has_left) {
             const int y = lane;
             const bool valid = y < vh;
+            const uint32_t me = slot_of(y, 0, valid);
             const uint32_t cur = valid ? sColC[y] : 0u;
             const uint32_t h = valid ? sHalo[y] : 0u;
             const bool ml = valid && h == cur;
@@ -487,6 +457,7 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
             const uint32_t cu = up_ok ? sColC[y - 1] : 0u, hu = up_ok ? sHalo[y - 1] : 0u;
             const uint32_t cd = dn_ok ? sColC[y + 1] : 0u, hd = dn_ok ? sHalo[y + 1] : 0u;
             const bool up_same = up_ok && cu == cur;
+            // skip a join that the row above (or this row's left join) already makes
             const bool rl = ml && !(up_same && hu == cur);
             bool rul = false, rdl = false;
             if (CONN == 8) {
@@ -495,209 +466,323 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
             }
             const uint64_t bu = __ballot(rul), bl = __ballot(rl), bdl = __ballot(rdl);
             uint32_t pos = popc64(bu & lt) + popc64(bl & lt) + popc64(bdl & lt);
-            if (rul || rl || rdl) {
-                const uint32_t me = sFs[sP[sRowBase[y]]];
-                uint16_t *q = w.req + t * REQMAX + REQ_TOP;
-                if (rul) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y - 1)) << 8));
-                if (rl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)y) << 8));
-                if (rdl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y + 1)) << 8));
-            }
+            uint16_t *q = w.req + (size_t)t * REQMAX + REQ_TOP;
+            if (rul) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y - 1)) << 8));
+            if (rl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)y) << 8));
+            if (rdl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y + 1)) << 8));
             nleft = popc64(bu) + popc64(bl) + popc64(bdl);
         }
         if (lane == 0) w.hdr[t].nleft = nleft;
     }
+    __syncthreads();
+    if (tid == 0) w.hdr[t].nruns = R;
+    if (tid < KMAX / 64) w.hdr[t].used[tid] = sUsed[tid];
 }
 
 // ------------------------------------------------------------ seam merge
-// One wave per tile resolves its requests to seam nodes of the neighbour
-// tiles and joins them; a request equal to the previous lane's is skipped.
+// One lane per tile walks its requests, resolves each to the seam node of the
+// neighbour tile's pixel and joins the two nodes; a request equal to the one
+// before it is skipped.
 
 __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w)
 {
-    const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * NWAVES + (threadIdx.x >> 6);
-    if (t >= g.ntiles) return;
-    const TileHdr h = w.hdr[t];
-    const uint16_t *q = w.req + t * REQMAX;
-    const uint32_t mine = (uint32_t)(t * KMAX);
-    for (uint32_t base = 0; base < h.ntop; base += 64) {
-        const uint32_t i = base + lane;
-        const bool active = i < h.ntop;
-        uint32_t a = 0xFFFFFFFFu, bn = 0xFFFFFFFFu;
-        if (active) {
-            const uint32_t rq = q[i];
-            const int xp = (int)(rq >> 8) - 1;
-            int64_t tn;
-            int col;
-            if (xp < 0) {
-                tn = t - g.ntx - 1;
-                col = TW - 1;
-            } else if (xp >= TW) {
-                tn = t - g.ntx + 1;
-                col = 0;
-            } else {
-                tn = t - g.ntx;
-                col = xp;
-            }
-            a = mine + (rq & 0xFFu);
-            bn = (uint32_t)(tn * KMAX) + w.bslot[tn * TW + col];
+    const uint32_t t = blockIdx.x * BLOCK + threadIdx.x;
+    if (t >= (uint32_t)g.ntiles) return;
+    const uint32_t ntop = w.hdr[t].ntop, nleft = w.hdr[t].nleft;
+    const uint16_t *q = w.req + (size_t)t * REQMAX;
+    const uint32_t mine = t * KMAX, ntx = (uint32_t)g.ntx;
+    uint32_t pa = 0xFFFFFFFFu, pb = 0xFFFFFFFFu;
+    for (uint32_t i = 0; i < ntop; ++i) {
+        const uint32_t rq = q[i];
+        const int xp = (int)(rq >> 8) - 1;
+        uint32_t tn;
+        int col;
+        if (xp < 0) {
+            tn = t - ntx - 1;
+            col = TW - 1;
+        } else if (xp >= TW) {
+            tn = t - ntx + 1;
+            col = 0;
+        } else {
+            tn = t - ntx;
+            col = xp;
         }
-        const uint32_t pa = __shfl_up(a, 1), pb = __shfl_up(bn, 1);
-        const bool dup = lane > 0 && pa == a && pb == bn;
-        if (active && !dup) g_unite(w.gp, a, bn, w.err);
+        const uint32_t a = mine + (rq & 0xFFu);
+        const uint32_t bn = tn * KMAX + w.bslot[(size_t)tn * TW + col];
+        if (a != pa || bn != pb) g_unite(w.gp, a, bn, w.err);
+        pa = a;
+        pb = bn;
     }
-    for (uint32_t base = 0; base < h.nleft; base += 64) {
-        const uint32_t i = base + lane;
-        const bool active = i < h.nleft;
-        uint32_t a = 0xFFFFFFFFu, bn = 0xFFFFFFFFu;
-        if (active) {
-            const uint32_t rq = q[REQ_TOP + i];
-            const int64_t tn = t - 1;
-            a = mine + (rq & 0xFFu);
-            bn = (uint32_t)(tn * KMAX) + w.rslot[tn * TH + ((rq >> 8) & 0x7Fu)];
-        }
-        const uint32_t pa = __shfl_up(a, 1), pb = __shfl_up(bn, 1);
-        const bool dup = lane > 0 && pa == a && pb == bn;
-        if (active && !dup) g_unite(w.gp, a, bn, w.err);
+    for (uint32_t i = 0; i < nleft; ++i) {
+        const uint32_t rq = q[REQ_TOP + i];
+        const uint32_t tn = t - 1;
+        const uint32_t a = mine + (rq & 0xFFu);
+        const uint32_t bn = tn * KMAX + w.rslot[(size_t)tn * TH + ((rq >> 8) & 0x7Fu)];
+        if (a != pa || bn != pb) g_unite(w.gp, a, bn, w.err);
+        pa = a;
+        pb = bn;
     }
 }
 
 // ---------------------------------------------------------- seam collapse
-// One wave per tile: each seam node points straight at its leader; a node that
-// is its own leader is a leader of the whole image: it is counted in its row
-// segment and gets its rank among that segment's leaders.
+// One lane per tile: each seam node points straight at its leader (Collapse).
+// A node that is its own leader leads a region of the whole image: it joins
+// its row segment's leader mask and count.
 
-__global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, int count_survivors)
+__global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, int count_leaders)
 {
-    const int lane = lane_id();
-    const int64_t t = (int64_t)blockIdx.x * NWAVES + (threadIdx.x >> 6);
-    if (t >= g.ntiles) return;
-    const uint32_t k = w.hdr[t].nnodes;
-    if (k == 0) return;
-    const int64_t b = t / g.tpi;
-    const int64_t tt = t - b * g.tpi;
-    const int ty = (int)(tt / g.ntx), tx = (int)(tt - (int64_t)ty * g.ntx);
-    const int64_t y0 = (int64_t)ty * TH;
-    const uint64_t lt = mask_lt(lane);
-    uint32_t carry_row = 0xFFFFFFFFu, carry_cnt = 0;
-    for (uint32_t base = 0; base < k; base += 64) {
-        const uint32_t s = base + lane;
-        const bool active = s < k;
-        const uint32_t n = (uint32_t)(t * KMAX) + s;
-        bool surv = false;
-        uint32_t row = 0xFFFFFFFEu, a = 0;
-        if (active) {
+    const uint32_t t = blockIdx.x * BLOCK + threadIdx.x;
+    if (t >= (uint32_t)g.ntiles) return;
+    const TilePos tp = tile_pos(t, g);
+    const uint32_t y0 = (uint32_t)tp.y0, x0 = (uint32_t)tp.x0;
+    for (int word = 0; word < KMAX / 64; ++word) {
+        uint64_t used = w.hdr[t].used[word];
+        while (used) {
+            const uint32_t s = (uint32_t)(word * 64 + __ffsll((unsigned long long)used) - 1);
+            used &= used - 1;
+            const uint32_t n = t * KMAX + s;
             uint64_t rrec;
             const uint32_t root = g_root(w.gp, n, rrec, w.err);
-            g_min(&w.gp[n], rrec);
-            surv = root == n;
-            a = w.aux[n];
-            row = a >> 8;
+            if (root != n) {
+                g_min(&w.gp[n], rrec);
+            } else if (count_leaders) {
+                const uint32_t key = (uint32_t)(rrec >> 32);
+                const uint32_t Y = fast_div(key, g.divW);
+                const uint32_t row = Y - y0, col = key - Y * (uint32_t)g.W - x0;
+                w.leadmask[(size_t)t * TH + row] |= 1ull << col;
+                w.seg[(size_t)t * TH + row] += 1u;
+            }
         }
-        if (!count_survivors) continue;
-        // survivors before this lane in the same tile row (slots are in row order)
-        const uint64_t sb = __ballot(active && surv);
-        const uint32_t prow = __shfl_up(row, 1);
-        const uint64_t nb = __ballot(active && (lane == 0 || prow != row));
-        const uint64_t le = nb & (lt | (1ull << lane));
-        const int rs = 63 - __clzll(le | 1ull);  // first lane of my row in this chunk
-        uint32_t cnt = popc64(sb & lt & ~mask_lt(rs));
-        if (rs == 0 && row == carry_row) cnt += carry_cnt;
-        if (active && surv) {
-            w.aux[n] = (a & 0xFFu) + cnt;
-            atomicAdd(&w.seg[(b * g.H + y0 + row) * g.ntx + tx], 1u);
-        }
-        const int last = (int)(k - 1 - base < 63 ? k - 1 - base : 63);
-        const uint32_t lrow = __shfl(row, last);
-        const uint32_t lcnt = __shfl(cnt, last) + (__shfl(surv ? 1u : 0u, last));
-        carry_row = lrow;
-        carry_cnt = lcnt;
     }
 }
 
 // ------------------------------------------------------------------ scan
-// seg[] holds, per image, the leaders of each 64-px row segment in reading
-// order; it is replaced in place by the exclusive prefix, per image.
+// seg[] holds the leaders of each row segment (tile-major).  Per tile row of
+// tiles ("band"): sum each image row across the band's tiles; scan the row
+// sums of each image; then give every segment the leaders of all earlier rows
+// plus those of the earlier segments of its row.
 
-__global__ __launch_bounds__(BLOCK) void scan_reduce_kernel(Geom g, Work w)
+// exclusive prefix over the workgroup of 32 values per thread (one per tile
+// row): vals[y] is replaced by its prefix; tot[y] receives the row's total
+__device__ void block_scan_rows(uint32_t (&vals)[TH], uint32_t (&tot)[TH], uint32_t *sW)
 {
-    __shared__ uint32_t sWave[NWAVES];
-    const int64_t c = blockIdx.x;
-    const int64_t b = c / g.cpi, cc = c - b * g.cpi;
-    const int64_t img_end = (b + 1) * g.H * g.ntx;
-    const int64_t base = b * g.H * g.ntx + cc * SCAN_CHUNK + (int64_t)threadIdx.x * SCAN_PT;
-    uint32_t sum = 0;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < SCAN_PT; ++j)
-        if (base + j < img_end) sum += w.seg[base + j];
-    uint32_t total;
-    block_exclusive_scan(sum, sWave, total);
-    if (threadIdx.x == 0) w.chunk[c] = total;
+    for (int y = 0; y < TH; ++y) {
+        uint32_t x = vals[y];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t v = __shfl_up(x, d);
+            if (lane >= d) x += v;
+        }
+        if (lane == 63) sW[wave * TH + y] = x;
+        vals[y] = x - vals[y];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int y = 0; y < TH; ++y) {
+        uint32_t off = 0, sum = 0;
+#pragma unroll
+        for (int i = 0; i < NWAVES; ++i) {
+            const uint32_t s = sW[i * TH + y];
+            off += i < wave ? s : 0u;
+            sum += s;
+        }
+        vals[y] += off;
+        tot[y] = sum;
+    }
+    __syncthreads();
 }
 
-__global__ __launch_bounds__(BLOCK) void scan_chunks_kernel(Geom g, Work w, int32_t *counts)
+__global__ __launch_bounds__(BLOCK) void scan_band_sum_kernel(Geom g, Work w)
+{
+    __shared__ uint32_t sW[NWAVES * TH];
+    const uint32_t band = blockIdx.x;  // b * nty + ty
+    const uint32_t b = fast_div(band, g.divNty), ty = band - b * (uint32_t)g.nty;
+    const size_t t0 = (size_t)b * g.tpi + (size_t)ty * g.ntx;
+    uint32_t acc[TH], tot[TH];
+#pragma unroll
+    for (int y = 0; y < TH; ++y) acc[y] = 0;
+    for (uint32_t tx = threadIdx.x; tx < (uint32_t)g.ntx; tx += BLOCK) {
+        const uint4 *p = (const uint4 *)(w.seg + (t0 + tx) * TH);
+#pragma unroll
+        for (int q = 0; q < TH / 4; ++q) {
+            const uint4 v = p[q];
+            acc[4 * q] += v.x;
+            acc[4 * q + 1] += v.y;
+            acc[4 * q + 2] += v.z;
+            acc[4 * q + 3] += v.w;
+        }
+    }
+    block_scan_rows(acc, tot, sW);
+    const int64_t Y0 = (int64_t)ty * TH;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int y = 0; y < TH; ++y)
+            if (Y0 + y < g.H) w.rowoff[(int64_t)b * g.H + Y0 + y] = tot[y];
+    }
+}
+
+__global__ __launch_bounds__(BLOCK) void scan_rows_kernel(Geom g, Work w, int32_t *counts)
 {
     __shared__ uint32_t sWave[NWAVES];
     const int64_t b = blockIdx.x;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    uint32_t *ro = w.rowoff + b * g.H;
     uint32_t carry = 0;
-    for (int64_t base = 0; base < g.cpi; base += BLOCK) {
-        const int64_t i = base + threadIdx.x;
-        const uint32_t v = i < g.cpi ? w.chunk[b * g.cpi + i] : 0u;
-        uint32_t total;
-        const uint32_t ex = block_exclusive_scan(v, sWave, total);
-        if (i < g.cpi) w.chunk[b * g.cpi + i] = carry + ex;
-        carry += total;
+    for (int64_t base = 0; base < g.H; base += (int64_t)BLOCK * SCAN_PT) {
+        uint32_t v[SCAN_PT], sum = 0;
+        const int64_t i0 = base + (int64_t)threadIdx.x * SCAN_PT;
+#pragma unroll
+        for (int j = 0; j < SCAN_PT; ++j) {
+            v[j] = i0 + j < g.H ? ro[i0 + j] : 0u;
+            sum += v[j];
+        }
+        uint32_t x = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) sWave[wave] = x;
+        __syncthreads();
+        uint32_t off = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < NWAVES; ++i) {
+            off += i < wave ? sWave[i] : 0u;
+            tot += sWave[i];
+        }
+        __syncthreads();
+        uint32_t run = carry + off + x - sum;
+#pragma unroll
+        for (int j = 0; j < SCAN_PT; ++j) {
+            if (i0 + j < g.H) ro[i0 + j] = run;
+            run += v[j];
+        }
+        carry += tot;
     }
     if (threadIdx.x == 0 && counts) counts[b] = (int32_t)carry;
 }
 
-__global__ __launch_bounds__(BLOCK) void scan_apply_kernel(Geom g, Work w)
+__global__ __launch_bounds__(BLOCK) void scan_band_apply_kernel(Geom g, Work w)
 {
-    __shared__ uint32_t sWave[NWAVES];
-    const int64_t c = blockIdx.x;
-    const int64_t b = c / g.cpi, cc = c - b * g.cpi;
-    const int64_t img_end = (b + 1) * g.H * g.ntx;
-    const int64_t base = b * g.H * g.ntx + cc * SCAN_CHUNK + (int64_t)threadIdx.x * SCAN_PT;
-    uint32_t v[SCAN_PT];
-    uint32_t sum = 0;
+    __shared__ uint32_t sW[NWAVES * TH];
+    const uint32_t band = blockIdx.x;
+    const uint32_t b = fast_div(band, g.divNty), ty = band - b * (uint32_t)g.nty;
+    const size_t t0 = (size_t)b * g.tpi + (size_t)ty * g.ntx;
+    const uint32_t ntx = (uint32_t)g.ntx;
+    // thread i handles the contiguous tiles [i*G, i*G + G) of the band
+    const uint32_t G = (ntx + BLOCK - 1) / BLOCK;
+    const uint32_t tx0 = threadIdx.x * G;
+    uint32_t acc[TH], tot[TH];
 #pragma unroll
-    for (int j = 0; j < SCAN_PT; ++j) {
-        v[j] = base + j < img_end ? w.seg[base + j] : 0u;
-        sum += v[j];
+    for (int y = 0; y < TH; ++y) acc[y] = 0;
+    for (uint32_t j = 0; j < G && tx0 + j < ntx; ++j) {
+        const uint4 *p = (const uint4 *)(w.seg + (t0 + tx0 + j) * TH);
+#pragma unroll
+        for (int q = 0; q < TH / 4; ++q) {
+            const uint4 v = p[q];
+            acc[4 * q] += v.x;
+            acc[4 * q + 1] += v.y;
+            acc[4 * q + 2] += v.z;
+            acc[4 * q + 3] += v.w;
+        }
     }
-    uint32_t total;
-    uint32_t run = block_exclusive_scan(sum, sWave, total) + w.chunk[c];
+    block_scan_rows(acc, tot, sW);
+    const int64_t Y0 = (int64_t)ty * TH;
 #pragma unroll
-    for (int j = 0; j < SCAN_PT; ++j) {
-        if (base + j < img_end) w.seg[base + j] = run;
-        run += v[j];
+    for (int y = 0; y < TH; ++y)
+        acc[y] += Y0 + y < g.H ? w.rowoff[(int64_t)b * g.H + Y0 + y] : 0u;
+    for (uint32_t j = 0; j < G && tx0 + j < ntx; ++j) {
+        uint4 *p = (uint4 *)(w.seg + (t0 + tx0 + j) * TH);
+#pragma unroll
+        for (int q = 0; q < TH / 4; ++q) {
+            const uint4 v = p[q];
+            const uint4 o = make_uint4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+            acc[4 * q] += v.x;
+            acc[4 * q + 1] += v.y;
+            acc[4 * q + 2] += v.z;
+            acc[4 * q + 3] += v.w;
+            p[q] = o;
+        }
     }
 }
 
-// ----------------------------------------------------------- final write
+// ---------------------------------------------------------------- resolve
+// One lane per tile, after the scan: each seam node gets the value its pixels
+// will carry: its leader's index, or 1 + the leaders before it.
+
+__global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int number)
+{
+    const uint32_t t = blockIdx.x * BLOCK + threadIdx.x;
+    if (t >= (uint32_t)g.ntiles) return;
+    const uint32_t b = fast_div(t, g.divTpi);
+    for (int word = 0; word < KMAX / 64; ++word) {
+        uint64_t used = w.hdr[t].used[word];
+        while (used) {
+            const uint32_t s = (uint32_t)(word * 64 + __ffsll((unsigned long long)used) - 1);
+            used &= used - 1;
+            const uint32_t n = t * KMAX + s;
+            const uint32_t key = (uint32_t)(w.gp[n] >> 32);
+            uint32_t val = key;
+            if (number) {
+                uint32_t tl, row, col;
+                pixel_tile(key, b, g, tl, row, col);
+                const size_t sg = (size_t)tl * TH + row;
+                val = 1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)col));
+            }
+            w.gp[n] = val;
+        }
+    }
+}
+
+// ------------------------------------------------------------ final write
+// One wave per tile: stage the tile's run labels in LDS (runs beyond DLAB are
+// labelled from their records on the fly), then write each tile row once,
+// coalesced.
 
 __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int32_t *out,
                                                             int number)
 {
-    __shared__ uint32_t sLab[TPX];
-    __shared__ uint32_t sSlotLab[KMAX];
-    __shared__ uint64_t sSurv[TH];
-    __shared__ uint32_t sPrefix[TH];
+    __shared__ uint32_t sLab[NWAVES][DLAB];
+    __shared__ uint32_t sNode[NWAVES][KMAX];
+    __shared__ uint64_t sLead[NWAVES][TH];
+    __shared__ uint32_t sPre[NWAVES][TH];
 
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int64_t t = remap_tile(blockIdx.x, g.ntiles);
-    const int64_t b = t / g.tpi;
-    const int64_t tt = t - b * g.tpi;
-    const int ty = (int)(tt / g.ntx), tx = (int)(tt - (int64_t)ty * g.ntx);
-    const int64_t y0 = (int64_t)ty * TH, x0 = (int64_t)tx * TW;
-    const int vh = (int)(g.H - y0 < TH ? g.H - y0 : TH);
-    const int vw = (int)(g.W - x0 < TW ? g.W - x0 : TW);
-    const int64_t W = g.W;
-    const TileHdr h = w.hdr[t];
-    const uint32_t R = h.nruns, k = h.nnodes;
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t t = remap_tile(blockIdx.x, gridDim.x) * NWAVES + wave;
+    if (t >= (uint32_t)g.ntiles) return;
+    const TilePos tp = tile_pos(t, g);
+    const int64_t y0 = tp.y0, x0 = tp.x0, W = g.W;
+    const uint32_t R = w.hdr[t].nruns;
+    uint32_t *lab = sLab[wave];
+    uint32_t *nodev = sNode[wave];
+    uint64_t *lead = sLead[wave];
+    uint32_t *pre = sPre[wave];
+    const size_t t32 = (size_t)t * TH;
 
-    // run starts of this wave's rows and their run bases
-    const uint64_t mk = lane < TH ? w.runmask[t * TH + lane] : 0ull;
+    const uint64_t mk = lane < TH ? w.runmask[t32 + lane] : 0ull;
+    if (number && lane < TH) {
+        lead[lane] = w.leadmask[t32 + lane];
+        pre[lane] = w.seg[t32 + lane];
+    }
+#pragma unroll
+    for (int word = 0; word < KMAX / 64; ++word) {
+        const uint64_t used = w.hdr[t].used[word];
+        if ((used >> lane) & 1ull) nodev[word * 64 + lane] = (uint32_t)w.gp[(size_t)t * KMAX + word * 64 + lane];
+    }
+    __syncwarp();
+    const uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
+    auto run_label = [&](uint32_t info) -> uint32_t {
+        if (info & INFO_BORDER) return nodev[info & 0xFFu];
+        const uint32_t row = info >> 6, col = info & 63u;
+        if (number) return 1u + pre[row] + popc64(lead[row] & mask_lt((int)col));
+        return (uint32_t)((y0 + row) * W + x0 + col);
+    };
+    const uint32_t nl = R < DLAB ? R : DLAB;
+    for (uint32_t r = lane; r < nl; r += 64) lab[r] = run_label(rinfo[r]);
+    __syncwarp();
+
     const uint32_t cnt = popc64(mk);
     uint32_t inc = cnt;
 #pragma unroll
@@ -705,83 +790,42 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         const uint32_t v = __shfl_up(inc, d);
         if (lane >= d) inc += v;
     }
-    const uint32_t ex = inc - cnt;
-    uint64_t rm[RPW];
-    uint32_t rb[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        rm[i] = __shfl(mk, wave * RPW + i);
-        rb[i] = __shfl(ex, wave * RPW + i);
-    }
-    if (tid < TH) {
-        sSurv[tid] = 0;
-        sPrefix[tid] = (number && tid < vh) ? w.seg[(b * g.H + y0 + tid) * g.ntx + tx] : 0u;
-    }
-    __syncthreads();
-    if ((uint32_t)tid < k) {
-        const uint32_t n = (uint32_t)(t * KMAX) + tid;
-        const uint64_t rec = w.gp[n];
-        const uint32_t L = (uint32_t)rec;
-        const uint32_t key = (uint32_t)(rec >> 32);
-        const uint32_t Y = fast_div(key, g.divW);
-        const uint32_t X = key - Y * (uint32_t)W;
-        if (L == n)
-            atomicOr((unsigned long long *)&sSurv[Y - y0], 1ull << (X - x0));
-        uint32_t lab = key;
-        if (number)
-            lab = 1u + w.seg[(b * g.H + Y) * g.ntx + (X >> 6)] + w.aux[L];
-        sSlotLab[tid] = lab;
-    }
-    __syncthreads();
-    const uint32_t *rinfo = w.runinfo + t * TPX;
-    for (uint32_t r = tid; r < R; r += BLOCK) {
-        const uint32_t info = rinfo[r];
-        uint32_t lab;
-        if (info & INFO_BORDER) {
-            lab = sSlotLab[info & 0xFFu];
-        } else {
-            const uint32_t row = (info >> 6) & 31u, col = info & 63u;
-            if (number)
-                lab = 1u + sPrefix[row] + ((info >> 11) & 63u) +
-                      popc64(sSurv[row] & mask_lt((int)col));
-            else
-                lab = (uint32_t)((y0 + row) * W + x0 + col);
-        }
-        sLab[r] = lab;
-    }
-    __syncthreads();
-    int32_t *o = out + b * g.HW;
+    const uint32_t rex = inc - cnt;
     const uint64_t lt = mask_lt(lane);
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int y = wave * RPW + i;
-        if (y < vh && lane < vw) {
-            const uint32_t s = (uint32_t)(rm[i] >> lane) & 1u;
-            const uint32_t run = rb[i] + popc64(rm[i] & lt) + s - 1u;
-            o[(y0 + y) * W + x0 + lane] = (int32_t)sLab[run];
+    int32_t *o = out + (int64_t)tp.b * g.HW + y0 * W + x0 + lane;
+    for (int y = 0; y < tp.vh; ++y) {
+        const uint64_t m = __shfl(mk, y);
+        const uint32_t rb = __shfl(rex, y);
+        if (lane < tp.vw) {
+            const uint32_t run = rb + popc64(m & lt) + (uint32_t)((m >> lane) & 1ull) - 1u;
+            o[y * W] = (int32_t)(run < DLAB ? lab[run] : run_label(rinfo[run]));
         }
     }
 }
 
 // ------------------------------------------------ standalone number/count
-// Row segments of 64 pixels: one wave64 ballot of "leaders[p] == p" each.
+// A leader image has no tiles of its own; its row segments use the same
+// tile-major layout so that the same scan numbers them.  One wave per row
+// segment: a ballot of "leaders[p] == p".
 
 __global__ __launch_bounds__(BLOCK) void leader_flag_kernel(const int32_t *leaders, Geom g,
                                                             Work w, int write_mask)
 {
     const int lane = lane_id();
-    const int64_t nw = (int64_t)gridDim.x * NWAVES;
-    for (int64_t sgi = (int64_t)blockIdx.x * NWAVES + (threadIdx.x >> 6); sgi < g.nseg; sgi += nw) {
-        const int64_t row = sgi / g.ntx;          // b*H + Y
-        const int64_t sx = sgi - row * g.ntx;
-        const int64_t Y = row % g.H;
-        const int64_t x = sx * 64 + lane;
+    const uint64_t nsegs = (uint64_t)g.ntiles * TH;
+    const uint64_t nw = (uint64_t)gridDim.x * NWAVES;
+    for (uint64_t sgi = (uint64_t)blockIdx.x * NWAVES + (threadIdx.x >> 6); sgi < nsegs; sgi += nw) {
+        const uint32_t t = (uint32_t)(sgi / TH), y = (uint32_t)(sgi % TH);
+        const TilePos tp = tile_pos(t, g);
         bool root = false;
-        if (x < g.W) root = (int64_t)leaders[row * g.W + x] == Y * g.W + x;
+        if ((int)y < tp.vh && lane < tp.vw) {
+            const int64_t Y = tp.y0 + y, X = tp.x0 + lane;
+            root = (int64_t)leaders[(int64_t)tp.b * g.HW + Y * g.W + X] == Y * g.W + X;
+        }
         const uint64_t m = __ballot(root);
         if (lane == 0) {
             w.seg[sgi] = popc64(m);
-            if (write_mask) w.runmask[sgi] = m;
+            if (write_mask) w.leadmask[sgi] = m;
         }
     }
 }
@@ -791,19 +835,18 @@ __global__ __launch_bounds__(BLOCK) void leader_assign_kernel(const int32_t *lea
 {
     const int64_t nrows = g.B * g.H;
     for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
-        const int64_t b = row / g.H;
-        const int64_t segbase = b * g.H * g.ntx;
+        const uint32_t b = (uint32_t)(row / g.H);
         for (int64_t x = threadIdx.x; x < g.W; x += BLOCK) {
             const int64_t i = row * g.W + x;
             const int32_t v = leaders[i];
-            int32_t lab = 0;
+            int32_t out = 0;
             if (v >= 0 && (int64_t)v < g.HW) {
-                const uint32_t Y = fast_div((uint32_t)v, g.divW);
-                const uint32_t X = (uint32_t)v - Y * (uint32_t)g.W;
-                const int64_t sg = segbase + (int64_t)Y * g.ntx + (X >> 6);
-                lab = (int32_t)(1u + w.seg[sg] + popc64(w.runmask[sg] & mask_lt((int)(X & 63u))));
+                uint32_t tl, r, c;
+                pixel_tile((uint32_t)v, b, g, tl, r, c);
+                const size_t sg = (size_t)tl * TH + r;
+                out = (int32_t)(1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)c)));
             }
-            labels[i] = lab;
+            labels[i] = out;
         }
     }
 }
@@ -845,33 +888,40 @@ void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, cons
 
 void launch_seam(const Geom &g, const Work &w, hipStream_t s)
 {
-    hipLaunchKernelGGL(seam_merge_kernel, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0, s, g, w);
+    hipLaunchKernelGGL(seam_merge_kernel, dim3(grid_of(g.ntiles, BLOCK)), dim3(BLOCK), 0, s, g, w);
 }
 
-void launch_seam_collapse(const Geom &g, const Work &w, int count_survivors, hipStream_t s)
+void launch_seam_collapse(const Geom &g, const Work &w, int count_leaders, hipStream_t s)
 {
-    hipLaunchKernelGGL(seam_collapse_kernel, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0, s,
-                       g, w, count_survivors);
+    hipLaunchKernelGGL(seam_collapse_kernel, dim3(grid_of(g.ntiles, BLOCK)), dim3(BLOCK), 0, s,
+                       g, w, count_leaders);
 }
 
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, hipStream_t s)
 {
-    hipLaunchKernelGGL(scan_reduce_kernel, dim3((unsigned)g.nchunk), dim3(BLOCK), 0, s, g, w);
-    hipLaunchKernelGGL(scan_chunks_kernel, dim3((unsigned)g.B), dim3(BLOCK), 0, s, g, w, counts);
+    hipLaunchKernelGGL(scan_band_sum_kernel, dim3((unsigned)g.nbands), dim3(BLOCK), 0, s, g, w);
+    hipLaunchKernelGGL(scan_rows_kernel, dim3((unsigned)g.B), dim3(BLOCK), 0, s, g, w, counts);
     if (apply)
-        hipLaunchKernelGGL(scan_apply_kernel, dim3((unsigned)g.nchunk), dim3(BLOCK), 0, s, g, w);
+        hipLaunchKernelGGL(scan_band_apply_kernel, dim3((unsigned)g.nbands), dim3(BLOCK), 0, s, g,
+                           w);
+}
+
+void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s)
+{
+    hipLaunchKernelGGL(resolve_kernel, dim3(grid_of(g.ntiles, BLOCK)), dim3(BLOCK), 0, s, g, w,
+                       number);
 }
 
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, hipStream_t s)
 {
-    hipLaunchKernelGGL(final_write_kernel, dim3((unsigned)g.ntiles), dim3(BLOCK), 0, s, g, w, out,
-                       number);
+    hipLaunchKernelGGL(final_write_kernel, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0, s, g,
+                       w, out, number);
 }
 
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
                          hipStream_t s)
 {
-    int64_t blocks = grid_of(g.nseg, NWAVES);
+    int64_t blocks = grid_of(g.ntiles * TH, NWAVES);
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(leader_flag_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, leaders, g,
                        w, write_mask);
