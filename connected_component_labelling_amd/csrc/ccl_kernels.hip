@@ -47,6 +47,12 @@ __device__ __forceinline__ uint64_t mask_le(int x) { return x >= 63 ? ~0ull : ((
 
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
+// value of lane-1 (lane 0 gets 0): one DPP move across the whole wave64
+__device__ __forceinline__ uint32_t from_left_lane(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138 /* wave_shr:1 */, 0xF, 0xF, false);
+}
+
 // Map workgroup ids to work items so that each XCD (workgroups are dealt to the
 // 8 XCDs round-robin) gets one contiguous range: neighbouring tiles then share
 // that XCD's L2.
@@ -103,12 +109,13 @@ __device__ __forceinline__ void pixel_tile(uint32_t key, uint32_t b, const Geom 
 // smaller slot is an earlier run.  Parents only point at smaller slots; a root
 // points at itself.  A root's word may also carry its seam slot in bits 16..23
 // (stored as 255 - slot, so the smallest slot wins an atomic maximum).  The
-// arrays are stored with column bits 3..5 XOR-ed with row bits 0..2 so that
-// eight rows accessed together fall on different LDS banks.
+// arrays are stored with the run index XOR-ed with the row so that the same
+// run index of all 32 rows (how the run phases access them) falls on
+// different LDS banks.
 
 constexpr uint32_t PMASK = 0xFFFFu;
 
-__device__ __forceinline__ uint32_t sw(uint32_t slot) { return slot ^ (((slot >> 6) & 7u) << 3); }
+__device__ __forceinline__ uint32_t sw(uint32_t slot) { return slot ^ ((slot >> 6) & 31u); }
 
 // Every find/union carries a step budget: a correct forest never comes near
 // it (tile chains are shorter than a tile's runs, and halving keeps seam chains
@@ -242,6 +249,35 @@ __device__ uint32_t g_root(uint64_t *gp, uint32_t x, uint64_t &root_rec, uint32_
 //              with pixels of the tiles above and to the left, found from a
 //              one-pixel halo).
 
+// barrier for LDS traffic only: global loads in flight (the next tile's rows)
+// are not waited for
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct TileRows {
+    uint32_t c[RPW];
+};
+
+// this wave's 8 rows of tile t (lane = column), 0 outside the image
+template <typename T>
+__device__ __forceinline__ TileRows load_rows(const T *__restrict__ img, const Geom &g, uint32_t t,
+                                              int wave, int lane)
+{
+    TileRows r;
+    const TilePos tp = tile_pos(t, g);
+    const T *rows = img + (int64_t)tp.b * g.HW + (tp.y0 + wave * RPW) * g.W + tp.x0;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+        r.c[i] = (lane < tp.vw && wave * RPW + i < tp.vh) ? (uint32_t)rows[i * g.W + lane] : 0u;
+    return r;
+}
+
+// One workgroup per tile: workgroup v labels tile remap_tile(v), so that each
+// XCD works through one contiguous range of tiles.
 template <typename T, int CONN>
 __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__ img, Geom g,
                                                            Work w)
@@ -250,29 +286,30 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
     __shared__ uint32_t sP[TPX];     // parent of run slot (swizzled); roots: + seam slot
     __shared__ uint32_t sRC[TPX];    // colour of run slot (swizzled)
     __shared__ uint8_t sRX[TPX];     // start column of run slot (swizzled)
+    __shared__ uint16_t sRun[TPX];   // run slot of each run in reading order
     __shared__ uint32_t sColC[TH];   // colour at column 0 of each row
     __shared__ uint32_t sHalo[TH];   // colour left of column 0 of each row
     __shared__ uint64_t sUsed[KMAX / 64];
+    __shared__ uint64_t sLead[TH];   // start columns of the final roots of each row
+    __shared__ uint32_t sUni[NWAVES], sUniC[NWAVES];
 
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const uint32_t t = remap_tile(blockIdx.x, (uint32_t)g.ntiles);
+    const uint64_t lt = mask_lt(lane);
+    const int64_t W = g.W;
+    const uint32_t t = remap_tile(blockIdx.x, gridDim.x);
+    const TileRows rows = load_rows(img, g, t, wave, lane);
+    uint32_t c[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) c[i] = rows.c[i];
     const TilePos tp = tile_pos(t, g);
     const int64_t y0 = tp.y0, x0 = tp.x0;
     const int vh = tp.vh, vw = tp.vw;
     const bool has_top = tp.ty > 0, has_left = tp.tx > 0;
     const bool has_bottom = y0 + TH < g.H, has_right = x0 + TW < g.W;
-    const int64_t W = g.W;
     const T *im = img + (int64_t)tp.b * g.HW;
     const bool lane_ok = lane < vw;
-    const uint64_t lt = mask_lt(lane);
 
     // ---- 1 Start
-    uint32_t c[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int y = wave * RPW + i;
-        c[i] = (lane_ok && y < vh) ? (uint32_t)im[(y0 + y) * W + x0 + lane] : 0u;
-    }
     uint32_t hrow = 0, hm1 = 0, hp1 = 0;  // row above: (y0-1, x0+lane), (y0-1, x0-1), (y0-1, x0+TW)
     if (wave == 0 && has_top) {
         const T *up = im + (y0 - 1) * W + x0;
@@ -282,15 +319,20 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
     }
     if (wave == 1 && has_left && lane < vh) sHalo[lane] = im[(y0 + lane) * W + x0 - 1];
     if (tid < KMAX / 64) sUsed[tid] = 0;
+    if (tid < TH) sLead[tid] = 0;
 
     uint64_t m[RPW];
+    bool wave_uniform = true;  // every valid row of this wave: one run, same colour
+    const uint32_t c00 = __builtin_amdgcn_readfirstlane(c[0]);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int y = wave * RPW + i;
-        const bool valid = lane_ok && y < vh;
-        const uint32_t left = __shfl_up(c[i], 1);
-        const bool st = valid && (lane == 0 || left != c[i]);
+        const bool valid = lane_ok & (y < vh);
+        const uint32_t left = from_left_lane(c[i]);
+        const bool st = valid & ((lane == 0) | (left != c[i]));
         m[i] = __ballot(st);
+        if (y < vh)
+            wave_uniform &= (m[i] == 1ull) & (__builtin_amdgcn_readfirstlane(c[i]) == c00);
         if (st) {
             const uint32_t slot = (uint32_t)(y * 64) + popc64(m[i] & lt);
             sRC[sw(slot)] = c[i];
@@ -303,15 +345,45 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
             w.runmask[(size_t)t * TH + y] = m[i];  // rows past the image edge store 0
         }
     }
-    __syncthreads();
+    const uint32_t cur0 = c[0];  // tile row 0 (wave 0), for the top-edge requests
+    // a tile of one colour needs none of the run phases
+    if (lane == 0) {
+        sUni[wave] = wave * RPW >= vh ? 2u : (wave_uniform ? 1u : 0u);
+        sUniC[wave] = c00;
+    }
+    lds_barrier();
+    bool uniform = true;
+#pragma unroll
+    for (int q = 0; q < NWAVES; ++q)
+        uniform &= sUni[q] == 2u || (sUni[q] == 1u && sUniC[q] == sUniC[0]);
 
-    // ---- 2 Connect: thread (row ry, rm) handles runs rm, rm+8, ... of row ry
-    const int ry = tid >> 3, rm = tid & 7;
-    if (ry >= 1 && ry < vh) {
-        const uint64_t mr = sMask[ry], ma = sMask[ry - 1];
-        const int cnt = (int)popc64(mr);
-        for (int k = rm; k < cnt; k += 8) {
-            const uint32_t slot = (uint32_t)(ry * 64 + k);
+    uint32_t R;
+    if (!uniform) {
+        // reading-order run index r -> run slot: rows hold cnt runs each, and
+        // the runs of row y follow those of the rows above it
+        uint32_t rc = lane < TH ? popc64(sMask[lane]) : 0u;
+        const uint32_t rown = rc;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t q = __shfl_up(rc, d);
+            if (lane >= d) rc += q;
+        }
+        R = __shfl(rc, TH - 1);
+        {
+            const int ry = tid & 31, rm = tid >> 5;
+            const uint32_t rb = __shfl(rc - rown, ry);
+            const int cnt = (int)popc64(sMask[ry]);
+            for (int k = rm; k < cnt; k += 8) sRun[rb + k] = (uint16_t)(ry * 64 + k);
+        }
+        lds_barrier();
+
+        // ---- 2 Connect: one thread per run (reading order)
+        for (uint32_t r = tid; r < R; r += BLOCK) {
+            const uint32_t slot = sRun[r];
+            const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
+            if (ry == 0) continue;
+            const uint64_t ma = sMask[ry - 1];
+            const int cnt = (int)popc64(sMask[ry]);
             const int s0 = sRX[sw(slot)];
             const int e0 = (k + 1 < cnt) ? (int)sRX[sw(slot + 1)] - 1 : vw - 1;
             const uint32_t cc = sRC[sw(slot)];
@@ -324,15 +396,14 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
                 if (sRC[sw(above)] == cc) lds_unite(sP, slot, above, w.err);
             }
         }
-    }
-    __syncthreads();
+        lds_barrier();
 
-    // ---- 3 Collapse; runs on an edge shared with another tile offer their
-    //      edge position as the region's seam slot (the smallest wins)
-    if (ry < vh) {
-        const int cnt = (int)popc64(sMask[ry]);
-        for (int k = rm; k < cnt; k += 8) {
-            const uint32_t slot = (uint32_t)(ry * 64 + k);
+        // ---- 3 Collapse; runs on an edge shared with another tile offer their
+        //      edge position as the region's seam slot (the smallest wins)
+        for (uint32_t r = tid; r < R; r += BLOCK) {
+            const uint32_t slot = sRun[r];
+            const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
+            const int cnt = (int)popc64(sMask[ry]);
             int budget = LDS_BUDGET;
             const uint32_t root = lds_find(sP, slot, budget);
             if (budget <= 0) set_err(w.err, ERR_LOOP);
@@ -344,52 +415,53 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
             if (has_top && ry == 0) es = k;
             if (es != 255) atomicMax(&sP[sw(root)], ((255u - es) << 16) | root);
         }
-    }
-    __syncthreads();
+        lds_barrier();
 
-    // ---- 4 Write: the same thread-per-run mapping as Connect
-    // run base of each row (lane y < TH): runs in the rows above it
-    uint32_t rc = lane < TH ? popc64(sMask[lane]) : 0u;
-    const uint32_t rown = rc;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t v = __shfl_up(rc, d);
-        if (lane >= d) rc += v;
-    }
-    const uint32_t R = __shfl(rc, TH - 1);
-    const uint32_t rb_row = __shfl(rc - rown, ry);
-    uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
-    uint64_t leadbits = 0;  // start columns of this thread's runs that are final roots
-    if (ry < vh) {
-        const int cnt = (int)popc64(sMask[ry]);
-        for (int k = rm; k < cnt; k += 8) {
-            const uint32_t slot = (uint32_t)(ry * 64 + k);
+        // ---- 4 Write: one thread per run; records in reading order
+        uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
+        for (uint32_t r = tid; r < R; r += BLOCK) {
+            const uint32_t slot = sRun[r];
             const uint32_t pv = sP[sw(slot)];
             const uint32_t root = pv & PMASK;
             const uint32_t rv = root == slot ? pv : sP[sw(root)];
             const uint32_t es = 255u - (rv >> 16);
             const uint32_t rcol = sRX[sw(root)];
-            rinfo[rb_row + k] = es != 255u ? (INFO_BORDER | es) : ((root & ~63u) | rcol);
+            rinfo[r] = es != 255u ? (INFO_BORDER | es) : ((root & ~63u) | rcol);
             if (root == slot) {
                 if (es == 255u) {
-                    leadbits |= 1ull << rcol;
+                    atomicOr((unsigned long long *)&sLead[slot >> 6], 1ull << rcol);
                 } else {
                     const uint32_t node = t * KMAX + es;
-                    const uint32_t key = (uint32_t)(y0 + ry) * (uint32_t)W + (uint32_t)x0 + rcol;
+                    const uint32_t key = (uint32_t)(y0 + (slot >> 6)) * (uint32_t)W + (uint32_t)x0 + rcol;
                     w.gp[node] = ((uint64_t)key << 32) | node;
                     atomicOr((unsigned long long *)&sUsed[es >> 6], 1ull << (es & 63u));
                 }
             }
         }
+    } else {
+        // ---- one colour: a single region led by the tile's first pixel, with
+        //      the seam slot of its first open edge (top row, bottom row, left
+        //      column, right column), one run per row
+        R = (uint32_t)vh;
+        const uint32_t es = has_top ? 0u : has_bottom ? (uint32_t)TW
+                          : has_left ? (uint32_t)(2 * TW) : has_right ? (uint32_t)(2 * TW + TH) : 255u;
+        if (tid < vh) w.runinfo[(size_t)t * TPX + tid] = es != 255u ? (INFO_BORDER | es) : 0u;
+        if (tid == 0) {
+            if (es != 255u) {
+                const uint32_t node = t * KMAX + es;
+                const uint32_t key = (uint32_t)y0 * (uint32_t)W + (uint32_t)x0;
+                w.gp[node] = ((uint64_t)key << 32) | node;
+                sUsed[es >> 6] = 1ull << (es & 63u);
+            } else {
+                sLead[0] = 1ull;
+            }
+            // the run-slot tables describe the same region to the edge lookups below
+            sP[sw(0)] = (es != 255u ? ((255u - es) << 16) : 0u);
+        }
+        if (tid >= 1 && tid < vh) sP[sw((uint32_t)tid * 64)] = 0u;
     }
-    // the 8 threads of a row sit in adjacent lanes: OR their leader columns
-    leadbits |= __shfl_xor(leadbits, 1);
-    leadbits |= __shfl_xor(leadbits, 2);
-    leadbits |= __shfl_xor(leadbits, 4);
-    if (rm == 0) {
-        w.leadmask[(size_t)t * TH + ry] = leadbits;   // rows past the image edge store 0
-        w.seg[(size_t)t * TH + ry] = popc64(leadbits);
-    }
+    lds_barrier();
+
     // seam slot of the region of the run containing (row y, column x)
     auto slot_of = [&](int y, int x, bool ok) -> uint32_t {
         if (!ok) return 0u;
@@ -408,7 +480,7 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
         if (has_top) {
             const uint32_t me = slot_of(0, lane, lane_ok);
             const bool st0 = (m[0] >> lane) & 1ull;
-            const uint32_t cur = c[0];
+            const uint32_t cur = cur0;
             const uint32_t hl = __shfl_up(hrow, 1), hr = __shfl_down(hrow, 1);
             const bool vm1 = lane >= 1 || has_left;
             const uint32_t cm1 = lane >= 1 ? hl : hm1;
@@ -474,84 +546,189 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
         }
         if (lane == 0) w.hdr[t].nleft = nleft;
     }
-    __syncthreads();
     if (tid == 0) w.hdr[t].nruns = R;
     if (tid < KMAX / 64) w.hdr[t].used[tid] = sUsed[tid];
+    if (tid >= 64 && tid < 64 + TH) {  // rows past the image edge store 0
+        const uint64_t lead = sLead[tid - 64];
+        w.leadmask[(size_t)t * TH + tid - 64] = lead;
+        w.seg[(size_t)t * TH + tid - 64] = popc64(lead);
+    }
 }
 
 // ------------------------------------------------------------ seam merge
-// One lane per tile walks its requests, resolves each to the seam node of the
-// neighbour tile's pixel and joins the two nodes; a request equal to the one
-// before it is skipped.
+// Each workgroup covers 256 consecutive tiles.  Their requests are counted,
+// prefix-summed and dealt round-robin to the 256 threads, so a tile with many
+// requests does not serialise on one lane.  Each request is resolved to the
+// seam node of the neighbour tile's pixel and the two nodes are joined; a
+// request equal to the one before it (held by the previous lane) is skipped.
+
+// exclusive prefix over the workgroup; `total` receives the sum of all values
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *sWave, uint32_t &total)
+{
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) sWave[wave] = x;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVES; ++i) {
+        const uint32_t sv = sWave[i];
+        off += i < wave ? sv : 0u;
+        tot += sv;
+    }
+    __syncthreads();
+    total = tot;
+    return off + x - v;
+}
+
+// index j of the tile holding item i: the largest j with off[j] <= i
+// (off[BLOCK] is the total, so a tile found this way has items)
+__device__ __forceinline__ uint32_t item_tile(const uint32_t *off, uint32_t i)
+{
+    uint32_t lo = 0, hi = BLOCK - 1;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= i) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
 
 __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w)
 {
-    const uint32_t t = blockIdx.x * BLOCK + threadIdx.x;
-    if (t >= (uint32_t)g.ntiles) return;
-    const uint32_t ntop = w.hdr[t].ntop, nleft = w.hdr[t].nleft;
-    const uint16_t *q = w.req + (size_t)t * REQMAX;
-    const uint32_t mine = t * KMAX, ntx = (uint32_t)g.ntx;
-    uint32_t pa = 0xFFFFFFFFu, pb = 0xFFFFFFFFu;
-    for (uint32_t i = 0; i < ntop; ++i) {
-        const uint32_t rq = q[i];
-        const int xp = (int)(rq >> 8) - 1;
-        uint32_t tn;
-        int col;
-        if (xp < 0) {
-            tn = t - ntx - 1;
-            col = TW - 1;
-        } else if (xp >= TW) {
-            tn = t - ntx + 1;
-            col = 0;
-        } else {
-            tn = t - ntx;
-            col = xp;
-        }
-        const uint32_t a = mine + (rq & 0xFFu);
-        const uint32_t bn = tn * KMAX + w.bslot[(size_t)tn * TW + col];
-        if (a != pa || bn != pb) g_unite(w.gp, a, bn, w.err);
-        pa = a;
-        pb = bn;
+    __shared__ uint32_t sOff[BLOCK + 1];
+    __shared__ uint32_t sTop[BLOCK];
+    __shared__ uint32_t sWave[NWAVES];
+    const uint32_t t0 = blockIdx.x * BLOCK;
+    const uint32_t tme = t0 + threadIdx.x;
+    uint32_t ntop = 0, n = 0;
+    if (tme < (uint32_t)g.ntiles) {
+        ntop = w.hdr[tme].ntop;
+        n = ntop + w.hdr[tme].nleft;
     }
-    for (uint32_t i = 0; i < nleft; ++i) {
-        const uint32_t rq = q[REQ_TOP + i];
-        const uint32_t tn = t - 1;
-        const uint32_t a = mine + (rq & 0xFFu);
-        const uint32_t bn = tn * KMAX + w.rslot[(size_t)tn * TH + ((rq >> 8) & 0x7Fu)];
-        if (a != pa || bn != pb) g_unite(w.gp, a, bn, w.err);
-        pa = a;
-        pb = bn;
+    uint32_t total;
+    const uint32_t off = block_exclusive_scan(n, sWave, total);
+    sOff[threadIdx.x] = off;
+    sTop[threadIdx.x] = ntop;
+    if (threadIdx.x == 0) sOff[BLOCK] = total;
+    __syncthreads();
+    const uint32_t ntx = (uint32_t)g.ntx;
+    const int lane = lane_id();
+    const uint32_t rounds = (total + BLOCK - 1) / BLOCK;
+    for (uint32_t k = 0; k < rounds; ++k) {
+        const uint32_t i = k * BLOCK + threadIdx.x;
+        uint32_t a = 0xFFFFFFFFu, bn = 0xFFFFFFFFu;
+        if (i < total) {
+            const uint32_t j = item_tile(sOff, i);
+            const uint32_t t = t0 + j, r = i - sOff[j];
+            const uint16_t *q = w.req + (size_t)t * REQMAX;
+            if (r < sTop[j]) {
+                const uint32_t rq = q[r];
+                const int xp = (int)(rq >> 8) - 1;
+                uint32_t tn;
+                int col;
+                if (xp < 0) {
+                    tn = t - ntx - 1;
+                    col = TW - 1;
+                } else if (xp >= TW) {
+                    tn = t - ntx + 1;
+                    col = 0;
+                } else {
+                    tn = t - ntx;
+                    col = xp;
+                }
+                a = t * KMAX + (rq & 0xFFu);
+                bn = tn * KMAX + w.bslot[(size_t)tn * TW + col];
+            } else {
+                const uint32_t rq = q[REQ_TOP + r - sTop[j]];
+                const uint32_t tn = t - 1;
+                a = t * KMAX + (rq & 0xFFu);
+                bn = tn * KMAX + w.rslot[(size_t)tn * TH + ((rq >> 8) & 0x7Fu)];
+            }
+        }
+        const uint32_t pa = __shfl_up(a, 1), pb = __shfl_up(bn, 1);
+        if (i < total && !(lane > 0 && pa == a && pb == bn)) g_unite(w.gp, a, bn, w.err);
     }
 }
 
+// the r-th set bit (from 0) of the 192-bit mask u[0..2]
+__device__ __forceinline__ uint32_t select_bit(const uint64_t (&u)[KMAX / 64], uint32_t r)
+{
+    uint32_t base = 0;
+#pragma unroll
+    for (int word = 0; word < KMAX / 64; ++word) {
+        const uint32_t c = popc64(u[word]);
+        if (r < c) {
+            uint64_t m = u[word];
+            uint32_t pos = 0;
+#pragma unroll
+            for (int half = 32; half >= 1; half >>= 1) {  // binary search on popcounts
+                const uint64_t lowm = m & ((1ull << half) - 1ull);
+                const uint32_t lc = popc64(lowm);
+                if (r >= lc) {
+                    r -= lc;
+                    m >>= half;
+                    pos += half;
+                } else {
+                    m = lowm;
+                }
+            }
+            return base + pos;
+        }
+        r -= c;
+        base += 64;
+    }
+    return 0;
+}
+
 // ---------------------------------------------------------- seam collapse
-// One lane per tile: each seam node points straight at its leader (Collapse).
-// A node that is its own leader leads a region of the whole image: it joins
-// its row segment's leader mask and count.
+// Seam nodes of 256 consecutive tiles, dealt round-robin to the workgroup's
+// threads.  Each node points straight at its leader (Collapse); a node that is
+// its own leader leads a region of the whole image and joins its row
+// segment's leader mask and count.
 
 __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, int count_leaders)
 {
-    const uint32_t t = blockIdx.x * BLOCK + threadIdx.x;
-    if (t >= (uint32_t)g.ntiles) return;
-    const TilePos tp = tile_pos(t, g);
-    const uint32_t y0 = (uint32_t)tp.y0, x0 = (uint32_t)tp.x0;
+    __shared__ uint32_t sOff[BLOCK + 1];
+    __shared__ uint64_t sUsed[BLOCK][KMAX / 64];
+    __shared__ uint32_t sWave[NWAVES];
+    const uint32_t t0 = blockIdx.x * BLOCK;
+    const uint32_t tme = t0 + threadIdx.x;
+    uint32_t n = 0;
+#pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) {
-        uint64_t used = w.hdr[t].used[word];
-        while (used) {
-            const uint32_t s = (uint32_t)(word * 64 + __ffsll((unsigned long long)used) - 1);
-            used &= used - 1;
-            const uint32_t n = t * KMAX + s;
-            uint64_t rrec;
-            const uint32_t root = g_root(w.gp, n, rrec, w.err);
-            if (root != n) {
-                g_min(&w.gp[n], rrec);
-            } else if (count_leaders) {
-                const uint32_t key = (uint32_t)(rrec >> 32);
-                const uint32_t Y = fast_div(key, g.divW);
-                const uint32_t row = Y - y0, col = key - Y * (uint32_t)g.W - x0;
-                w.leadmask[(size_t)t * TH + row] |= 1ull << col;
-                w.seg[(size_t)t * TH + row] += 1u;
-            }
+        const uint64_t u = tme < (uint32_t)g.ntiles ? w.hdr[tme].used[word] : 0ull;
+        sUsed[threadIdx.x][word] = u;
+        n += popc64(u);
+    }
+    uint32_t total;
+    const uint32_t off = block_exclusive_scan(n, sWave, total);
+    sOff[threadIdx.x] = off;
+    if (threadIdx.x == 0) sOff[BLOCK] = total;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < total; i += BLOCK) {
+        const uint32_t j = item_tile(sOff, i);
+        const uint32_t t = t0 + j;
+        uint64_t u[KMAX / 64];
+#pragma unroll
+        for (int word = 0; word < KMAX / 64; ++word) u[word] = sUsed[j][word];
+        const uint32_t node = t * KMAX + select_bit(u, i - sOff[j]);
+        uint64_t rrec;
+        const uint32_t root = g_root(w.gp, node, rrec, w.err);
+        if (root != node) {
+            g_min(&w.gp[node], rrec);
+        } else if (count_leaders) {
+            const TilePos tp = tile_pos(t, g);
+            const uint32_t key = (uint32_t)(rrec >> 32);
+            const uint32_t Y = fast_div(key, g.divW);
+            const uint32_t row = Y - (uint32_t)tp.y0, col = key - Y * (uint32_t)g.W - (uint32_t)tp.x0;
+            atomicOr((unsigned long long *)&w.leadmask[(size_t)t * TH + row], 1ull << col);
+            atomicAdd(&w.seg[(size_t)t * TH + row], 1u);
         }
     }
 }
@@ -709,30 +886,45 @@ __global__ __launch_bounds__(BLOCK) void scan_band_apply_kernel(Geom g, Work w)
 }
 
 // ---------------------------------------------------------------- resolve
-// One lane per tile, after the scan: each seam node gets the value its pixels
-// will carry: its leader's index, or 1 + the leaders before it.
+// After the scan, each seam node gets the value its pixels will carry: its
+// leader's index, or 1 + the leaders before it.  Nodes of 256 consecutive
+// tiles are dealt round-robin to the workgroup's threads.
 
 __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int number)
 {
-    const uint32_t t = blockIdx.x * BLOCK + threadIdx.x;
-    if (t >= (uint32_t)g.ntiles) return;
-    const uint32_t b = fast_div(t, g.divTpi);
+    __shared__ uint32_t sOff[BLOCK + 1];
+    __shared__ uint64_t sUsed[BLOCK][KMAX / 64];
+    __shared__ uint32_t sWave[NWAVES];
+    const uint32_t t0 = blockIdx.x * BLOCK;
+    const uint32_t tme = t0 + threadIdx.x;
+    uint32_t n = 0;
+#pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) {
-        uint64_t used = w.hdr[t].used[word];
-        while (used) {
-            const uint32_t s = (uint32_t)(word * 64 + __ffsll((unsigned long long)used) - 1);
-            used &= used - 1;
-            const uint32_t n = t * KMAX + s;
-            const uint32_t key = (uint32_t)(w.gp[n] >> 32);
-            uint32_t val = key;
-            if (number) {
-                uint32_t tl, row, col;
-                pixel_tile(key, b, g, tl, row, col);
-                const size_t sg = (size_t)tl * TH + row;
-                val = 1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)col));
-            }
-            w.gp[n] = val;
+        const uint64_t u = tme < (uint32_t)g.ntiles ? w.hdr[tme].used[word] : 0ull;
+        sUsed[threadIdx.x][word] = u;
+        n += popc64(u);
+    }
+    uint32_t total;
+    const uint32_t off = block_exclusive_scan(n, sWave, total);
+    sOff[threadIdx.x] = off;
+    if (threadIdx.x == 0) sOff[BLOCK] = total;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < total; i += BLOCK) {
+        const uint32_t j = item_tile(sOff, i);
+        const uint32_t t = t0 + j;
+        uint64_t u[KMAX / 64];
+#pragma unroll
+        for (int word = 0; word < KMAX / 64; ++word) u[word] = sUsed[j][word];
+        const uint32_t node = t * KMAX + select_bit(u, i - sOff[j]);
+        const uint32_t key = (uint32_t)(w.gp[node] >> 32);
+        uint32_t val = key;
+        if (number) {
+            uint32_t tl, row, col;
+            pixel_tile(key, fast_div(t, g.divTpi), g, tl, row, col);
+            const size_t sg = (size_t)tl * TH + row;
+            val = 1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)col));
         }
+        w.gp[node] = val;
     }
 }
 
