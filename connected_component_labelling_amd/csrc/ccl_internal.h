@@ -43,7 +43,7 @@ struct TileHdr {
     uint32_t nruns;     // runs in the tile
     uint32_t ntop;      // seam requests along the top edge
     uint32_t nleft;     // seam requests along the left edge
-    uint32_t pad;
+    uint32_t uniform;   // 1: every valid pixel of the tile has one colour
     uint64_t used[3];   // seam slots in use (bit s of word s/64)
     uint64_t pad2;
 };

@@ -47,7 +47,9 @@ __device__ __forceinline__ uint64_t mask_le(int x) { return x >= 63 ? ~0ull : ((
 
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
-// value of lane-1 (lane 0 gets 0): one DPP move across the whole wave64
+// value of lane-1 (lane 0 gets 0): one DPP move across the whole wave64.  A
+// lane that is switched off at the call also reads as 0, so lane shifts are
+// taken where every lane is active.
 __device__ __forceinline__ uint32_t from_left_lane(uint32_t v)
 {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138 /* wave_shr:1 */, 0xF, 0xF, false);
@@ -235,12 +237,16 @@ __device__ uint32_t g_root(uint64_t *gp, uint32_t x, uint64_t &root_rec, uint32_
 }
 
 // ------------------------------------------------------------- tile pass
-// One workgroup per 64x32 tile.
-//   1 Start    each wave loads 8 rows; a ballot per row marks run starts and
-//              the start lanes record their run (colour, start column, parent).
-//   2 Connect  one thread per run joins it to every run of the row above that
-//              touches its span (widened by one pixel each side for 8
-//              neighbours) and has its colour.
+// One workgroup per 64x32 tile; wave w holds tile rows 8w..8w+7, lane = column.
+//   1 Start    a ballot per row marks run starts ("left neighbour differs");
+//              start lanes initialise their run's parent and start column.  A
+//              tile whose valid pixels all have one colour is finished on a
+//              short path (one region, no run tables).
+//   2 Connect  each run is joined once to every run of the row above that
+//              touches it and has its colour.  The joins are found per pixel
+//              from the row above (shifted one lane each way), so that exactly
+//              one pixel of the run stands for each such pair; they are queued
+//              per wave and united in LDS with every lane busy.
 //   3 Collapse every run points at its tile root; a run on an edge shared with
 //              another tile offers its edge position as the region's seam slot.
 //   4 Write    per-run records, the leader mask and count of each row
@@ -249,8 +255,7 @@ __device__ uint32_t g_root(uint64_t *gp, uint32_t x, uint64_t &root_rec, uint32_
 //              with pixels of the tiles above and to the left, found from a
 //              one-pixel halo).
 
-// barrier for LDS traffic only: global loads in flight (the next tile's rows)
-// are not waited for
+// barrier for LDS traffic only (outstanding global stores are not waited for)
 __device__ __forceinline__ void lds_barrier()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -258,110 +263,243 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-struct TileRows {
-    uint32_t c[RPW];
-};
-
-// this wave's 8 rows of tile t (lane = column), 0 outside the image
-template <typename T>
-__device__ __forceinline__ TileRows load_rows(const T *__restrict__ img, const Geom &g, uint32_t t,
-                                              int wave, int lane)
+// value of lane+1 (lane 63 gets 0)
+__device__ __forceinline__ uint32_t from_right_lane(uint32_t v)
 {
-    TileRows r;
-    const TilePos tp = tile_pos(t, g);
-    const T *rows = img + (int64_t)tp.b * g.HW + (tp.y0 + wave * RPW) * g.W + tp.x0;
-#pragma unroll
-    for (int i = 0; i < RPW; ++i)
-        r.c[i] = (lane < tp.vw && wave * RPW + i < tp.vh) ? (uint32_t)rows[i * g.W + lane] : 0u;
-    return r;
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130 /* wave_shl:1 */, 0xF, 0xF, false);
 }
 
-// One workgroup per tile: workgroup v labels tile remap_tile(v), so that each
-// XCD works through one contiguous range of tiles.
-template <typename T, int CONN>
-__global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__ img, Geom g,
-                                                           Work w)
+// number of set bits of m below this lane
+__device__ __forceinline__ uint32_t mbcnt(uint64_t m)
 {
-    __shared__ uint64_t sMask[TH];   // run starts of each tile row
-    __shared__ uint32_t sP[TPX];     // parent of run slot (swizzled); roots: + seam slot
-    __shared__ uint32_t sRC[TPX];    // colour of run slot (swizzled)
-    __shared__ uint8_t sRX[TPX];     // start column of run slot (swizzled)
-    __shared__ uint16_t sRun[TPX];   // run slot of each run in reading order
-    __shared__ uint32_t sColC[TH];   // colour at column 0 of each row
-    __shared__ uint32_t sHalo[TH];   // colour left of column 0 of each row
-    __shared__ uint64_t sUsed[KMAX / 64];
-    __shared__ uint64_t sLead[TH];   // start columns of the final roots of each row
-    __shared__ uint32_t sUni[NWAVES], sUniC[NWAVES];
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+constexpr int QCAP = 256;  // join queue of one wave (a ring; at most 63 + 128 pending)
+
+struct TileLds {
+    uint32_t P[TPX];               // parent of run slot (swizzled); roots: + seam slot
+    uint16_t Run[TPX];             // run slot of each run in reading order
+    uint8_t RX[TPX];               // start column of run slot (swizzled)
+    uint32_t Q[NWAVES][QCAP];      // queued joins: slot | other slot << 16
+    uint64_t Mask[TH];             // run starts of each tile row
+    uint64_t Lead[TH];             // start columns of the final roots of each row
+    uint32_t LastC[NWAVES - 1][TW]; // last row of waves 0..2 (the next wave's row above)
+    uint32_t ColC[TH];             // colour at column 0 of each row
+    uint64_t Used[KMAX / 64];
+    uint32_t Uni[NWAVES], UniC[NWAVES];
+};
+
+// Seam requests across the top edge (wave 0, lane = column): tile row 0
+// (colour cur, run start flag st0, seam slot me of its region) against the row
+// above (hrow; hm1 / hp1 = the pixels diagonally beyond columns 0 and 63).
+// Returns the number written.
+template <int CONN>
+__device__ __forceinline__ uint32_t top_requests(uint16_t *q, int lane, bool lane_ok, int vw,
+                                                 bool has_left, bool has_right, uint32_t cur,
+                                                 bool st0, uint32_t me, uint32_t hrow,
+                                                 uint32_t hm1, uint32_t hp1)
+{
     const uint64_t lt = mask_lt(lane);
+    const uint32_t hl = from_left_lane(hrow), hr = from_right_lane(hrow);
+    const bool vm1 = lane >= 1 || has_left;
+    const uint32_t cm1 = lane >= 1 ? hl : hm1;
+    const bool vp1 = lane < TW - 1 ? lane + 1 < vw : has_right;
+    const uint32_t cp1 = lane < TW - 1 ? hr : hp1;
+    const bool um1 = lane_ok && vm1 && cm1 == cur;
+    const bool u0 = lane_ok && hrow == cur;
+    const bool up1 = lane_ok && vp1 && cp1 == cur;
+    bool ra = false, rb = false;
+    int xb = lane;
+    if (CONN == 8) {
+        ra = up1 && !u0;  // up-right starts a stretch of the run's colour
+        if (st0) {        // a run's first pixel also takes up-left or up
+            if (um1) {
+                rb = true;
+                xb = lane - 1;
+            } else if (u0) {
+                rb = true;
+            }
+        }
+    } else {
+        rb = u0 && (st0 || !um1);
+    }
+    const uint64_t ba = __ballot(ra), bb = __ballot(rb);
+    const uint32_t pos = popc64(ba & lt) + popc64(bb & lt);
+    if (rb) q[pos] = (uint16_t)(me | ((uint32_t)(xb + 1) << 8));
+    if (ra) q[pos + (rb ? 1 : 0)] = (uint16_t)(me | ((uint32_t)(lane + 2) << 8));
+    return popc64(ba) + popc64(bb);
+}
+
+// Seam requests across the left edge (wave 1, lane = tile row y): the pixel at
+// column 0 (colour cur, seam slot me) against the halo column h; cu/hu and
+// cd/hd are the same two values for rows y-1 and y+1.
+template <int CONN>
+__device__ __forceinline__ uint32_t left_requests(uint16_t *q, int y, bool valid, bool up_ok,
+                                                  bool dn_ok, uint32_t me, uint32_t cur,
+                                                  uint32_t h, uint32_t cu, uint32_t hu,
+                                                  uint32_t cd, uint32_t hd)
+{
+    const uint64_t lt = mask_lt(y);
+    const bool ml = valid && h == cur;
+    const bool up_same = up_ok && cu == cur;
+    // skip a join that the row above (or this row's left join) already makes
+    const bool rl = ml && !(up_same && hu == cur);
+    bool rul = false, rdl = false;
+    if (CONN == 8) {
+        rul = up_ok && hu == cur && !up_same && !(ml && h == hu);
+        rdl = dn_ok && hd == cur && cd != cur && !(ml && h == hd);
+    }
+    const uint64_t bu = __ballot(rul), bl = __ballot(rl), bdl = __ballot(rdl);
+    uint32_t pos = popc64(bu & lt) + popc64(bl & lt) + popc64(bdl & lt);
+    if (rul) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y - 1)) << 8));
+    if (rl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)y) << 8));
+    if (rdl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y + 1)) << 8));
+    return popc64(bu) + popc64(bl) + popc64(bdl);
+}
+
+// unite the queued joins q[head .. tail) (indices modulo QCAP), 64 at a time
+__device__ __forceinline__ void drain_joins(uint32_t *P, const uint32_t *q, uint32_t &head,
+                                            uint32_t tail, bool all, int lane, uint32_t *err)
+{
+    while (tail - head >= 64u || (all && tail != head)) {
+        const uint32_t n = tail - head;
+        __syncwarp();
+        if ((uint32_t)lane < n) {
+            const uint32_t e = q[(head + (uint32_t)lane) & (QCAP - 1)];
+            lds_unite(P, e & 0xFFFFu, e >> 16, err);
+        }
+        head += n < 64u ? n : 64u;
+    }
+}
+
+template <typename T, int CONN, bool FULL>
+__device__ __forceinline__ void label_tile(const T *__restrict__ img, const Geom &g, const Work &w,
+                                           TileLds &s, uint32_t t, const TilePos &tp)
+{
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int64_t W = g.W;
-    const uint32_t t = remap_tile(blockIdx.x, gridDim.x);
-    const TileRows rows = load_rows(img, g, t, wave, lane);
-    uint32_t c[RPW];
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) c[i] = rows.c[i];
-    const TilePos tp = tile_pos(t, g);
     const int64_t y0 = tp.y0, x0 = tp.x0;
-    const int vh = tp.vh, vw = tp.vw;
+    const int vh = FULL ? TH : tp.vh, vw = FULL ? TW : tp.vw;
     const bool has_top = tp.ty > 0, has_left = tp.tx > 0;
     const bool has_bottom = y0 + TH < g.H, has_right = x0 + TW < g.W;
     const T *im = img + (int64_t)tp.b * g.HW;
-    const bool lane_ok = lane < vw;
+    const bool lane_ok = FULL || lane < vw;
 
-    // ---- 1 Start
-    uint32_t hrow = 0, hm1 = 0, hp1 = 0;  // row above: (y0-1, x0+lane), (y0-1, x0-1), (y0-1, x0+TW)
+    // ---- loads: this wave's rows, and the halo (row above, column to the left)
+    uint32_t c[RPW];
+    {
+        const T *rows = im + (y0 + wave * RPW) * W + x0;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            if (FULL)
+                c[i] = (uint32_t)rows[i * W + lane];
+            else
+                c[i] = (lane_ok && wave * RPW + i < vh) ? (uint32_t)rows[i * W + lane] : 0u;
+        }
+    }
+    uint32_t hrow = 0, hm1 = 0, hp1 = 0;  // (y0-1, x0+lane), (y0-1, x0-1), (y0-1, x0+TW)
+    uint32_t hleft = 0;                   // wave 1: (y0+lane, x0-1)
     if (wave == 0 && has_top) {
         const T *up = im + (y0 - 1) * W + x0;
         if (lane_ok) hrow = up[lane];
         if (lane == 0 && has_left) hm1 = up[-1];
         if (lane == TW - 1 && has_right) hp1 = up[TW];
     }
-    if (wave == 1 && has_left && lane < vh) sHalo[lane] = im[(y0 + lane) * W + x0 - 1];
-    if (tid < KMAX / 64) sUsed[tid] = 0;
-    if (tid < TH) sLead[tid] = 0;
+    if (wave == 1 && has_left && lane < vh) hleft = im[(y0 + lane) * W + x0 - 1];
 
+    // ---- 1 Start
     uint64_t m[RPW];
-    bool wave_uniform = true;  // every valid row of this wave: one run, same colour
+    uint64_t bad = 0;  // lanes holding a colour other than the wave's first pixel's
     const uint32_t c00 = __builtin_amdgcn_readfirstlane(c[0]);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int y = wave * RPW + i;
-        const bool valid = lane_ok & (y < vh);
+        const bool valid = FULL || (lane_ok && y < vh);
         const uint32_t left = from_left_lane(c[i]);
-        const bool st = valid & ((lane == 0) | (left != c[i]));
+        const bool st = valid && (lane == 0 || left != c[i]);
         m[i] = __ballot(st);
-        if (y < vh)
-            wave_uniform &= (m[i] == 1ull) & (__builtin_amdgcn_readfirstlane(c[i]) == c00);
+        bad |= __ballot(valid && c[i] != c00);
         if (st) {
-            const uint32_t slot = (uint32_t)(y * 64) + popc64(m[i] & lt);
-            sRC[sw(slot)] = c[i];
-            sRX[sw(slot)] = (uint8_t)lane;
-            sP[sw(slot)] = slot;
+            const uint32_t slot = (uint32_t)(y * 64) + mbcnt(m[i]);
+            s.RX[sw(slot)] = (uint8_t)lane;
+            s.P[sw(slot)] = slot;
         }
         if (lane == 0) {
-            sMask[y] = m[i];
-            sColC[y] = c[i];
-            w.runmask[(size_t)t * TH + y] = m[i];  // rows past the image edge store 0
+            s.Mask[y] = m[i];
+            s.ColC[y] = c[i];
         }
     }
-    const uint32_t cur0 = c[0];  // tile row 0 (wave 0), for the top-edge requests
-    // a tile of one colour needs none of the run phases
+    if (wave < NWAVES - 1) s.LastC[wave][lane] = c[RPW - 1];
+    if (tid < KMAX / 64) s.Used[tid] = 0;
+    if (tid < TH) s.Lead[tid] = 0;
     if (lane == 0) {
-        sUni[wave] = wave * RPW >= vh ? 2u : (wave_uniform ? 1u : 0u);
-        sUniC[wave] = c00;
+        s.Uni[wave] = (!FULL && wave * RPW >= vh) ? 2u : (bad == 0 ? 1u : 0u);
+        s.UniC[wave] = c00;
     }
     lds_barrier();
     bool uniform = true;
 #pragma unroll
     for (int q = 0; q < NWAVES; ++q)
-        uniform &= sUni[q] == 2u || (sUni[q] == 1u && sUniC[q] == sUniC[0]);
+        uniform &= s.Uni[q] == 2u || (s.Uni[q] == 1u && s.UniC[q] == s.UniC[0]);
 
+    TileHdr &hdr = w.hdr[t];
+    const size_t t32 = (size_t)t * TH;
+    if (tid < TH) w.runmask[t32 + tid] = s.Mask[tid];  // rows past the image edge store 0
+
+    if (uniform) {
+        // ---- one colour: a single region led by the tile's first pixel, with
+        //      the seam slot of its first open edge (top row, bottom row, left
+        //      column, right column), one run per row
+        const uint32_t C = s.UniC[0];
+        const uint32_t es = has_top ? 0u : has_bottom ? (uint32_t)TW
+                          : has_left ? (uint32_t)(2 * TW) : has_right ? (uint32_t)(2 * TW + TH) : 255u;
+        if (tid < vh) w.runinfo[(size_t)t * TPX + tid] = es != 255u ? (INFO_BORDER | es) : 0u;
+        if (tid < TH) {
+            const uint64_t lead = (tid == 0 && es == 255u) ? 1ull : 0ull;
+            w.leadmask[t32 + tid] = lead;
+            w.seg[t32 + tid] = (uint32_t)lead;
+        }
+        if (tid < KMAX / 64)
+            hdr.used[tid] = (es != 255u && (es >> 6) == (uint32_t)tid) ? 1ull << (es & 63u) : 0ull;
+        if (tid == 0) {
+            hdr.nruns = (uint32_t)vh;
+            hdr.uniform = 1u;
+            if (es != 255u) {
+                const uint32_t node = t * KMAX + es;
+                const uint32_t key = (uint32_t)y0 * (uint32_t)W + (uint32_t)x0;
+                w.gp[node] = ((uint64_t)key << 32) | node;
+            }
+        }
+        if (has_bottom && wave == NWAVES - 1 && lane_ok) w.bslot[(size_t)t * TW + lane] = (uint8_t)es;
+        if (has_right && wave == 2 && lane < vh) w.rslot[t32 + lane] = (uint8_t)es;
+        if (wave == 0) {
+            const uint32_t n = has_top ? top_requests<CONN>(w.req + (size_t)t * REQMAX, lane, lane_ok, vw,
+                                                            has_left, has_right, C, lane == 0, es,
+                                                            hrow, hm1, hp1)
+                                       : 0u;
+            if (lane == 0) hdr.ntop = n;
+        }
+        if (wave == 1) {
+            uint32_t n = 0;
+            if (has_left) {
+                const int y = lane;
+                const bool valid = y < vh;
+                const uint32_t hu = from_left_lane(hleft), hd = from_right_lane(hleft);
+                n = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, y, valid,
+                                        valid && y >= 1, valid && y + 1 < vh, es, C, hleft, C, hu,
+                                        C, hd);
+            }
+            if (lane == 0) hdr.nleft = n;
+        }
+        return;
+    }
+
+    // reading-order run index r -> run slot: rows hold cnt runs each, and the
+    // runs of row y follow those of the rows above it
     uint32_t R;
-    if (!uniform) {
-        // reading-order run index r -> run slot: rows hold cnt runs each, and
-        // the runs of row y follow those of the rows above it
-        uint32_t rc = lane < TH ? popc64(sMask[lane]) : 0u;
+    {
+        uint32_t rc = lane < TH ? popc64(s.Mask[lane]) : 0u;
         const uint32_t rown = rc;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -369,190 +507,165 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
             if (lane >= d) rc += q;
         }
         R = __shfl(rc, TH - 1);
-        {
-            const int ry = tid & 31, rm = tid >> 5;
-            const uint32_t rb = __shfl(rc - rown, ry);
-            const int cnt = (int)popc64(sMask[ry]);
-            for (int k = rm; k < cnt; k += 8) sRun[rb + k] = (uint16_t)(ry * 64 + k);
-        }
-        lds_barrier();
+        const int ry = tid & 31, rm = tid >> 5;
+        const uint32_t rb = __shfl(rc - rown, ry);
+        const int cnt = (int)popc64(s.Mask[ry]);
+        for (int k = rm; k < cnt; k += 8) s.Run[rb + k] = (uint16_t)(ry * 64 + k);
+    }
 
-        // ---- 2 Connect: one thread per run (reading order)
-        for (uint32_t r = tid; r < R; r += BLOCK) {
-            const uint32_t slot = sRun[r];
-            const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
-            if (ry == 0) continue;
-            const uint64_t ma = sMask[ry - 1];
-            const int cnt = (int)popc64(sMask[ry]);
-            const int s0 = sRX[sw(slot)];
-            const int e0 = (k + 1 < cnt) ? (int)sRX[sw(slot + 1)] - 1 : vw - 1;
-            const uint32_t cc = sRC[sw(slot)];
-            const int xa = (CONN == 8 && s0 > 0) ? s0 - 1 : s0;
-            const int xb = (CONN == 8 && e0 + 1 < vw) ? e0 + 1 : e0;
-            const int ka = (int)popc64(ma & mask_le(xa)) - 1;
-            const int kb = (int)popc64(ma & mask_le(xb)) - 1;
-            for (int j = ka; j <= kb; ++j) {
-                const uint32_t above = (uint32_t)((ry - 1) * 64 + j);
-                if (sRC[sw(above)] == cc) lds_unite(sP, slot, above, w.err);
-            }
-        }
-        lds_barrier();
-
-        // ---- 3 Collapse; runs on an edge shared with another tile offer their
-        //      edge position as the region's seam slot (the smallest wins)
-        for (uint32_t r = tid; r < R; r += BLOCK) {
-            const uint32_t slot = sRun[r];
-            const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
-            const int cnt = (int)popc64(sMask[ry]);
-            int budget = LDS_BUDGET;
-            const uint32_t root = lds_find(sP, slot, budget);
-            if (budget <= 0) set_err(w.err, ERR_LOOP);
-            if (root != slot) atomicMin(&sP[sw(slot)], root);
-            uint32_t es = 255;
-            if (has_right && k == cnt - 1) es = 2 * TW + TH + ry;
-            if (has_left && k == 0) es = 2 * TW + ry;
-            if (has_bottom && ry == TH - 1) es = TW + k;
-            if (has_top && ry == 0) es = k;
-            if (es != 255) atomicMax(&sP[sw(root)], ((255u - es) << 16) | root);
-        }
-        lds_barrier();
-
-        // ---- 4 Write: one thread per run; records in reading order
-        uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
-        for (uint32_t r = tid; r < R; r += BLOCK) {
-            const uint32_t slot = sRun[r];
-            const uint32_t pv = sP[sw(slot)];
-            const uint32_t root = pv & PMASK;
-            const uint32_t rv = root == slot ? pv : sP[sw(root)];
-            const uint32_t es = 255u - (rv >> 16);
-            const uint32_t rcol = sRX[sw(root)];
-            rinfo[r] = es != 255u ? (INFO_BORDER | es) : ((root & ~63u) | rcol);
-            if (root == slot) {
-                if (es == 255u) {
-                    atomicOr((unsigned long long *)&sLead[slot >> 6], 1ull << rcol);
-                } else {
-                    const uint32_t node = t * KMAX + es;
-                    const uint32_t key = (uint32_t)(y0 + (slot >> 6)) * (uint32_t)W + (uint32_t)x0 + rcol;
-                    w.gp[node] = ((uint64_t)key << 32) | node;
-                    atomicOr((unsigned long long *)&sUsed[es >> 6], 1ull << (es & 63u));
-                }
-            }
-        }
-    } else {
-        // ---- one colour: a single region led by the tile's first pixel, with
-        //      the seam slot of its first open edge (top row, bottom row, left
-        //      column, right column), one run per row
-        R = (uint32_t)vh;
-        const uint32_t es = has_top ? 0u : has_bottom ? (uint32_t)TW
-                          : has_left ? (uint32_t)(2 * TW) : has_right ? (uint32_t)(2 * TW + TH) : 255u;
-        if (tid < vh) w.runinfo[(size_t)t * TPX + tid] = es != 255u ? (INFO_BORDER | es) : 0u;
-        if (tid == 0) {
-            if (es != 255u) {
-                const uint32_t node = t * KMAX + es;
-                const uint32_t key = (uint32_t)y0 * (uint32_t)W + (uint32_t)x0;
-                w.gp[node] = ((uint64_t)key << 32) | node;
-                sUsed[es >> 6] = 1ull << (es & 63u);
+    // ---- 2 Connect: per pixel against the row above; one queued join per
+    //      pair of touching runs of one colour
+    {
+        uint32_t *q = s.Q[wave];
+        uint32_t head = 0, tail = 0;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int y = wave * RPW + i;
+            if (y == 0 || (!FULL && y >= vh)) continue;
+            const uint32_t ca = i > 0 ? c[i - 1] : s.LastC[wave - 1][lane];
+            const uint64_t ma = i > 0 ? m[i - 1] : s.Mask[y - 1];
+            const bool valid = FULL || lane_ok;
+            const bool st = (m[i] >> lane) & 1ull;
+            const uint32_t cc = c[i];
+            // lane shifts read other lanes, so they run with every lane active
+            const uint32_t cl = from_left_lane(ca), cr = from_right_lane(ca);
+            const bool u0 = valid && ca == cc;
+            const bool um1 = valid && lane > 0 && cl == cc;
+            bool ra = false, rb;
+            uint32_t xb;  // 0: up-left, 1: up, 2: up-right run of the join
+            if (CONN == 8) {
+                const bool up1 = valid && lane + 1 < vw && cr == cc;
+                ra = up1 && !u0;         // a run of the colour starts up-right
+                rb = st && (um1 || u0);  // the run's first pixel takes up-left or up
+                xb = um1 ? 0u : 1u;
             } else {
-                sLead[0] = 1ull;
+                rb = u0 && (st || !um1);
+                xb = 1u;
             }
-            // the run-slot tables describe the same region to the edge lookups below
-            sP[sw(0)] = (es != 255u ? ((255u - es) << 16) : 0u);
+            const uint32_t me = (uint32_t)(y * 64) + mbcnt(m[i]) + (st ? 1u : 0u) - 1u;  // run of this pixel
+            // run of the row above at column lane-1+xb: runs started at or before it
+            const uint32_t plt = mbcnt(ma);
+            const uint32_t bx = (uint32_t)(ma >> lane) & 1u;
+            const uint32_t bx1 = lane < 63 ? (uint32_t)(ma >> (lane + 1)) & 1u : 0u;
+            const uint32_t above = (uint32_t)((y - 1) * 64) + plt - 1u;
+            const uint32_t ab = above + (xb >= 1u ? bx : 0u);
+            const uint32_t ar = above + bx + bx1;
+            const uint64_t bbm = __ballot(rb), bam = __ballot(ra);
+            if (rb) q[(tail + mbcnt(bbm)) & (QCAP - 1)] = me | (ab << 16);
+            tail += popc64(bbm);
+            if (ra) q[(tail + mbcnt(bam)) & (QCAP - 1)] = me | (ar << 16);
+            tail += popc64(bam);
+            drain_joins(s.P, q, head, tail, false, lane, w.err);
         }
-        if (tid >= 1 && tid < vh) sP[sw((uint32_t)tid * 64)] = 0u;
+        drain_joins(s.P, q, head, tail, true, lane, w.err);
     }
     lds_barrier();
 
-    // seam slot of the region of the run containing (row y, column x)
-    auto slot_of = [&](int y, int x, bool ok) -> uint32_t {
-        if (!ok) return 0u;
-        const uint32_t run = (uint32_t)(y * 64) + popc64(sMask[y] & mask_le(x)) - 1u;
-        const uint32_t root = sP[sw(run)] & PMASK;
-        return 255u - (sP[sw(root)] >> 16);
-    };
-    if (has_bottom && wave == NWAVES - 1 && lane_ok)
-        w.bslot[(size_t)t * TW + lane] = (uint8_t)slot_of(TH - 1, lane, true);
-    if (has_right && wave == 2 && lane < vh)
-        w.rslot[(size_t)t * TH + lane] = (uint8_t)slot_of(lane, TW - 1, true);
-
-    // seam requests across the top edge: tile row 0 against the row above
-    if (wave == 0) {
-        uint32_t ntop = 0;
-        if (has_top) {
-            const uint32_t me = slot_of(0, lane, lane_ok);
-            const bool st0 = (m[0] >> lane) & 1ull;
-            const uint32_t cur = cur0;
-            const uint32_t hl = __shfl_up(hrow, 1), hr = __shfl_down(hrow, 1);
-            const bool vm1 = lane >= 1 || has_left;
-            const uint32_t cm1 = lane >= 1 ? hl : hm1;
-            const bool vp1 = lane < TW - 1 ? lane + 1 < vw : has_right;
-            const uint32_t cp1 = lane < TW - 1 ? hr : hp1;
-            const bool um1 = lane_ok && vm1 && cm1 == cur;
-            const bool u0 = lane_ok && hrow == cur;
-            const bool up1 = lane_ok && vp1 && cp1 == cur;
-            bool ra = false, rb = false;
-            int xb = lane;
-            if (CONN == 8) {
-                ra = up1 && !u0;  // up-right starts a stretch of the run's colour
-                if (st0) {        // a run's first pixel also takes up-left or up
-                    if (um1) {
-                        rb = true;
-                        xb = lane - 1;
-                    } else if (u0) {
-                        rb = true;
-                    }
-                }
-            } else {
-                rb = u0 && (st0 || !um1);
-            }
-            const uint64_t ba = __ballot(ra), bb = __ballot(rb);
-            const uint32_t pos = popc64(ba & lt) + popc64(bb & lt);
-            uint16_t *q = w.req + (size_t)t * REQMAX;
-            if (rb) q[pos] = (uint16_t)(me | ((uint32_t)(xb + 1) << 8));
-            if (ra) q[pos + (rb ? 1 : 0)] = (uint16_t)(me | ((uint32_t)(lane + 2) << 8));
-            ntop = popc64(ba) + popc64(bb);
-        }
-        if (lane == 0) w.hdr[t].ntop = ntop;
+    // ---- 3 Collapse; runs on an edge shared with another tile offer their
+    //      edge position as the region's seam slot (the smallest wins)
+    for (uint32_t r = tid; r < R; r += BLOCK) {
+        const uint32_t slot = s.Run[r];
+        const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
+        const int cnt = (int)popc64(s.Mask[ry]);
+        int budget = LDS_BUDGET;
+        const uint32_t root = lds_find(s.P, slot, budget);
+        if (budget <= 0) set_err(w.err, ERR_LOOP);
+        if (root != slot) atomicMin(&s.P[sw(slot)], root);
+        uint32_t es = 255;
+        if (has_right && k == cnt - 1) es = 2 * TW + TH + ry;
+        if (has_left && k == 0) es = 2 * TW + ry;
+        if (has_bottom && ry == TH - 1) es = TW + k;
+        if (has_top && ry == 0) es = k;
+        if (es != 255) atomicMax(&s.P[sw(root)], ((255u - es) << 16) | root);
     }
+    lds_barrier();
 
-    // seam requests across the left edge: one lane per tile row
+    // ---- 4 Write: one thread per run; records in reading order
+    uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
+    for (uint32_t r = tid; r < R; r += BLOCK) {
+        const uint32_t slot = s.Run[r];
+        const uint32_t pv = s.P[sw(slot)];
+        const uint32_t root = pv & PMASK;
+        const uint32_t rv = root == slot ? pv : s.P[sw(root)];
+        const uint32_t es = 255u - (rv >> 16);
+        const uint32_t rcol = s.RX[sw(root)];
+        rinfo[r] = es != 255u ? (INFO_BORDER | es) : ((root & ~63u) | rcol);
+        if (root == slot) {
+            if (es == 255u) {
+                atomicOr((unsigned long long *)&s.Lead[slot >> 6], 1ull << rcol);
+            } else {
+                const uint32_t node = t * KMAX + es;
+                const uint32_t key = (uint32_t)(y0 + (slot >> 6)) * (uint32_t)W + (uint32_t)x0 + rcol;
+                w.gp[node] = ((uint64_t)key << 32) | node;
+                atomicOr((unsigned long long *)&s.Used[es >> 6], 1ull << (es & 63u));
+            }
+        }
+    }
+    lds_barrier();
+
+    // seam slot of the region of run slot `run`
+    auto seam_of = [&](uint32_t run) -> uint32_t {
+        const uint32_t root = s.P[sw(run)] & PMASK;
+        return 255u - (s.P[sw(root)] >> 16);
+    };
+    if (has_bottom && wave == NWAVES - 1 && lane_ok) {
+        const bool st = (m[RPW - 1] >> lane) & 1ull;
+        w.bslot[(size_t)t * TW + lane] =
+            (uint8_t)seam_of((uint32_t)((TH - 1) * 64) + mbcnt(m[RPW - 1]) + (st ? 1u : 0u) - 1u);
+    }
+    if (has_right && wave == 2 && lane < vh)
+        w.rslot[t32 + lane] = (uint8_t)seam_of((uint32_t)(lane * 64) + popc64(s.Mask[lane]) - 1u);
+    if (wave == 0) {
+        uint32_t n = 0;
+        if (has_top) {
+            const bool st0 = (m[0] >> lane) & 1ull;
+            const uint32_t me = lane_ok ? seam_of(mbcnt(m[0]) + (st0 ? 1u : 0u) - 1u) : 0u;
+            n = top_requests<CONN>(w.req + (size_t)t * REQMAX, lane, lane_ok, vw, has_left, has_right,
+                                   c[0], st0, me, hrow, hm1, hp1);
+        }
+        if (lane == 0) hdr.ntop = n;
+    }
     if (wave == 1) {
-        uint32_t nleft = 0;
+        uint32_t n = 0;
         if (has_left) {
             const int y = lane;
             const bool valid = y < vh;
-            const uint32_t me = slot_of(y, 0, valid);
-            const uint32_t cur = valid ? sColC[y] : 0u;
-            const uint32_t h = valid ? sHalo[y] : 0u;
-            const bool ml = valid && h == cur;
-            const bool up_ok = valid && y >= 1;
-            const bool dn_ok = valid && y + 1 < vh;
-            const uint32_t cu = up_ok ? sColC[y - 1] : 0u, hu = up_ok ? sHalo[y - 1] : 0u;
-            const uint32_t cd = dn_ok ? sColC[y + 1] : 0u, hd = dn_ok ? sHalo[y + 1] : 0u;
-            const bool up_same = up_ok && cu == cur;
-            // skip a join that the row above (or this row's left join) already makes
-            const bool rl = ml && !(up_same && hu == cur);
-            bool rul = false, rdl = false;
-            if (CONN == 8) {
-                rul = up_ok && hu == cur && !up_same && !(ml && h == hu);
-                rdl = dn_ok && hd == cur && cd != cur && !(ml && h == hd);
-            }
-            const uint64_t bu = __ballot(rul), bl = __ballot(rl), bdl = __ballot(rdl);
-            uint32_t pos = popc64(bu & lt) + popc64(bl & lt) + popc64(bdl & lt);
-            uint16_t *q = w.req + (size_t)t * REQMAX + REQ_TOP;
-            if (rul) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y - 1)) << 8));
-            if (rl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)y) << 8));
-            if (rdl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y + 1)) << 8));
-            nleft = popc64(bu) + popc64(bl) + popc64(bdl);
+            const bool up_ok = valid && y >= 1, dn_ok = valid && y + 1 < vh;
+            const uint32_t me = valid ? seam_of((uint32_t)(y * 64)) : 0u;
+            const uint32_t cur = valid ? s.ColC[y] : 0u;
+            const uint32_t cu = up_ok ? s.ColC[y - 1] : 0u, cd = dn_ok ? s.ColC[y + 1] : 0u;
+            const uint32_t hu = from_left_lane(hleft), hd = from_right_lane(hleft);
+            n = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, y, valid, up_ok, dn_ok, me,
+                                    cur, hleft, cu, hu, cd, hd);
         }
-        if (lane == 0) w.hdr[t].nleft = nleft;
+        if (lane == 0) hdr.nleft = n;
     }
-    if (tid == 0) w.hdr[t].nruns = R;
-    if (tid < KMAX / 64) w.hdr[t].used[tid] = sUsed[tid];
+    if (tid == 0) {
+        hdr.nruns = R;
+        hdr.uniform = 0u;
+    }
+    if (tid < KMAX / 64) hdr.used[tid] = s.Used[tid];
     if (tid >= 64 && tid < 64 + TH) {  // rows past the image edge store 0
-        const uint64_t lead = sLead[tid - 64];
-        w.leadmask[(size_t)t * TH + tid - 64] = lead;
-        w.seg[(size_t)t * TH + tid - 64] = popc64(lead);
+        const uint64_t lead = s.Lead[tid - 64];
+        w.leadmask[t32 + tid - 64] = lead;
+        w.seg[t32 + tid - 64] = popc64(lead);
     }
+}
+
+// One workgroup per tile: workgroup v labels tile remap_tile(v), so that each
+// XCD works through one contiguous range of tiles.  Tiles wholly inside the
+// image take a path without edge checks.
+template <typename T, int CONN>
+__global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__ img, Geom g,
+                                                           Work w)
+{
+    __shared__ TileLds s;
+    const uint32_t t = remap_tile(blockIdx.x, gridDim.x);
+    const TilePos tp = tile_pos(t, g);
+    if (tp.vh == TH && tp.vw == TW)
+        label_tile<T, CONN, true>(img, g, w, s, t, tp);
+    else
+        label_tile<T, CONN, false>(img, g, w, s, t, tp);
 }
 
 // ------------------------------------------------------------ seam merge
@@ -946,13 +1059,33 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     if (t >= (uint32_t)g.ntiles) return;
     const TilePos tp = tile_pos(t, g);
     const int64_t y0 = tp.y0, x0 = tp.x0, W = g.W;
+    const size_t t32 = (size_t)t * TH;
+    const uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
+    int32_t *o = out + (int64_t)tp.b * g.HW + y0 * W + x0 + lane;
+    const bool lane_ok = lane < tp.vw;
+
+    if (w.hdr[t].uniform != 0u) {
+        // one colour: every pixel carries the value of run 0
+        const uint32_t info = rinfo[0];
+        uint32_t v;
+        if (info & INFO_BORDER)
+            v = (uint32_t)w.gp[(size_t)t * KMAX + (info & 0xFFu)];
+        else
+            v = number ? 1u + w.seg[t32] : (uint32_t)(y0 * W + x0);
+        if (tp.vh == TH && lane_ok) {
+#pragma unroll
+            for (int y = 0; y < TH; ++y) o[y * W] = (int32_t)v;
+        } else if (lane_ok) {
+            for (int y = 0; y < tp.vh; ++y) o[y * W] = (int32_t)v;
+        }
+        return;
+    }
+
     const uint32_t R = w.hdr[t].nruns;
     uint32_t *lab = sLab[wave];
     uint32_t *nodev = sNode[wave];
     uint64_t *lead = sLead[wave];
     uint32_t *pre = sPre[wave];
-    const size_t t32 = (size_t)t * TH;
-
     const uint64_t mk = lane < TH ? w.runmask[t32 + lane] : 0ull;
     if (number && lane < TH) {
         lead[lane] = w.leadmask[t32 + lane];
@@ -964,7 +1097,6 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         if ((used >> lane) & 1ull) nodev[word * 64 + lane] = (uint32_t)w.gp[(size_t)t * KMAX + word * 64 + lane];
     }
     __syncwarp();
-    const uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
     auto run_label = [&](uint32_t info) -> uint32_t {
         if (info & INFO_BORDER) return nodev[info & 0xFFu];
         const uint32_t row = info >> 6, col = info & 63u;
@@ -975,6 +1107,7 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     for (uint32_t r = lane; r < nl; r += 64) lab[r] = run_label(rinfo[r]);
     __syncwarp();
 
+    // runs before each row (lane y holds row y's)
     const uint32_t cnt = popc64(mk);
     uint32_t inc = cnt;
 #pragma unroll
@@ -983,13 +1116,13 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         if (lane >= d) inc += v;
     }
     const uint32_t rex = inc - cnt;
-    const uint64_t lt = mask_lt(lane);
-    int32_t *o = out + (int64_t)tp.b * g.HW + y0 * W + x0 + lane;
+    const uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
     for (int y = 0; y < tp.vh; ++y) {
-        const uint64_t m = __shfl(mk, y);
-        const uint32_t rb = __shfl(rex, y);
-        if (lane < tp.vw) {
-            const uint32_t run = rb + popc64(m & lt) + (uint32_t)((m >> lane) & 1ull) - 1u;
+        const uint64_t m = ((uint64_t)__builtin_amdgcn_readlane(mhi, y) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane(mlo, y);
+        const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
+        if (lane_ok) {
+            const uint32_t run = rb + mbcnt(m) + (uint32_t)((m >> lane) & 1ull) - 1u;
             o[y * W] = (int32_t)(run < DLAB ? lab[run] : run_label(rinfo[run]));
         }
     }
