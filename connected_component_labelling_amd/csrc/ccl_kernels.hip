@@ -287,7 +287,7 @@ struct TileLds {
     uint32_t LastC[NWAVES - 1][TW]; // last row of waves 0..2 (the next wave's row above)
     uint32_t ColC[TH];             // colour at column 0 of each row
     uint64_t Used[KMAX / 64];
-    uint32_t Uni[NWAVES], UniC[NWAVES];
+    uint64_t Uni[NWAVES];          // per wave: (one colour? << 32) | first colour
 };
 
 // Seam requests across the top edge (wave 0, lane = column): tile row 0
@@ -358,104 +358,97 @@ __device__ __forceinline__ uint32_t left_requests(uint16_t *q, int y, bool valid
     return popc64(bu) + popc64(bl) + popc64(bdl);
 }
 
-// unite the queued joins q[head .. tail) (indices modulo QCAP), 64 at a time
-__device__ __forceinline__ void drain_joins(uint32_t *P, const uint32_t *q, uint32_t &head,
-                                            uint32_t tail, bool all, int lane, uint32_t *err)
-{
-    while (tail - head >= 64u || (all && tail != head)) {
-        const uint32_t n = tail - head;
-        __syncwarp();
-        if ((uint32_t)lane < n) {
-            const uint32_t e = q[(head + (uint32_t)lane) & (QCAP - 1)];
-            lds_unite(P, e & 0xFFFFu, e >> 16, err);
-        }
-        head += n < 64u ? n : 64u;
-    }
-}
-
-template <typename T, int CONN, bool FULL>
-__device__ __forceinline__ void label_tile(const T *__restrict__ img, const Geom &g, const Work &w,
-                                           TileLds &s, uint32_t t, const TilePos &tp)
-{
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int64_t W = g.W;
-    const int64_t y0 = tp.y0, x0 = tp.x0;
-    const int vh = FULL ? TH : tp.vh, vw = FULL ? TW : tp.vw;
-    const bool has_top = tp.ty > 0, has_left = tp.tx > 0;
-    const bool has_bottom = y0 + TH < g.H, has_right = x0 + TW < g.W;
-    const T *im = img + (int64_t)tp.b * g.HW;
-    const bool lane_ok = FULL || lane < vw;
-
-    // ---- loads: this wave's rows, and the halo (row above, column to the left)
+// The pixels one wave reads for a tile: its 8 rows (lane = column) and the
+// halo, the row above the tile (wave 0) and the column to its left (wave 1).
+struct TileIn {
     uint32_t c[RPW];
-    {
-        const T *rows = im + (y0 + wave * RPW) * W + x0;
-#pragma unroll
-        for (int i = 0; i < RPW; ++i) {
-            if (FULL)
-                c[i] = (uint32_t)rows[i * W + lane];
-            else
-                c[i] = (lane_ok && wave * RPW + i < vh) ? (uint32_t)rows[i * W + lane] : 0u;
-        }
-    }
-    uint32_t hrow = 0, hm1 = 0, hp1 = 0;  // (y0-1, x0+lane), (y0-1, x0-1), (y0-1, x0+TW)
-    uint32_t hleft = 0;                   // wave 1: (y0+lane, x0-1)
-    if (wave == 0 && has_top) {
-        const T *up = im + (y0 - 1) * W + x0;
-        if (lane_ok) hrow = up[lane];
-        if (lane == 0 && has_left) hm1 = up[-1];
-        if (lane == TW - 1 && has_right) hp1 = up[TW];
-    }
-    if (wave == 1 && has_left && lane < vh) hleft = im[(y0 + lane) * W + x0 - 1];
+    uint32_t hrow, hm1, hp1;  // (y0-1, x0+lane), (y0-1, x0-1), (y0-1, x0+TW)
+    uint32_t hleft;           // wave 1: (y0+lane, x0-1)
+};
 
-    // ---- 1 Start
-    uint64_t m[RPW];
-    uint64_t bad = 0;  // lanes holding a colour other than the wave's first pixel's
-    const uint32_t c00 = __builtin_amdgcn_readfirstlane(c[0]);
+template <typename T, bool FULL>
+__device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geom &g,
+                                            const TilePos &tp, int wave, int lane)
+{
+    TileIn in;
+    const int64_t W = g.W, y0 = tp.y0, x0 = tp.x0;
+    const int vh = FULL ? TH : tp.vh, vw = FULL ? TW : tp.vw;
+    const bool lane_ok = FULL || lane < vw;
+    const T *im = img + (int64_t)tp.b * g.HW;
+    const T *rows = im + (y0 + wave * RPW) * W + x0;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        const int y = wave * RPW + i;
-        const bool valid = FULL || (lane_ok && y < vh);
-        const uint32_t left = from_left_lane(c[i]);
-        const bool st = valid && (lane == 0 || left != c[i]);
-        m[i] = __ballot(st);
-        bad |= __ballot(valid && c[i] != c00);
-        if (st) {
-            const uint32_t slot = (uint32_t)(y * 64) + mbcnt(m[i]);
-            s.RX[sw(slot)] = (uint8_t)lane;
-            s.P[sw(slot)] = slot;
-        }
-        if (lane == 0) {
-            s.Mask[y] = m[i];
-            s.ColC[y] = c[i];
-        }
+        if (FULL)
+            in.c[i] = (uint32_t)rows[i * W + lane];
+        else
+            in.c[i] = (lane_ok && wave * RPW + i < vh) ? (uint32_t)rows[i * W + lane] : 0u;
     }
-    if (wave < NWAVES - 1) s.LastC[wave][lane] = c[RPW - 1];
-    if (tid < KMAX / 64) s.Used[tid] = 0;
-    if (tid < TH) s.Lead[tid] = 0;
-    if (lane == 0) {
-        s.Uni[wave] = (!FULL && wave * RPW >= vh) ? 2u : (bad == 0 ? 1u : 0u);
-        s.UniC[wave] = c00;
+    in.hrow = in.hm1 = in.hp1 = in.hleft = 0;
+    if (wave == 0 && tp.ty > 0) {
+        const T *up = im + (y0 - 1) * W + x0;
+        if (lane_ok) in.hrow = up[lane];
+        if (lane == 0 && tp.tx > 0) in.hm1 = up[-1];
+        if (lane == TW - 1 && x0 + TW < W) in.hp1 = up[TW];
+    }
+    if (wave == 1 && tp.tx > 0 && lane < vh) in.hleft = im[(y0 + lane) * W + x0 - 1];
+    return in;
+}
+
+template <int CONN>
+__device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds &s, uint32_t t,
+                                           const TilePos &tp, const TileIn &in)
+{
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // the same in the whole wave
+    const int64_t W = g.W;
+    const int64_t y0 = tp.y0, x0 = tp.x0;
+    const int vh = tp.vh, vw = tp.vw;
+    const bool has_top = tp.ty > 0, has_left = tp.tx > 0;
+    const bool has_bottom = y0 + TH < g.H, has_right = x0 + TW < g.W;
+    const bool lane_ok = lane < vw;
+    uint32_t c[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) c[i] = in.c[i];
+    const uint32_t hrow = in.hrow, hm1 = in.hm1, hp1 = in.hp1, hleft = in.hleft;
+
+    // ---- a tile of one colour needs none of the run phases: is every valid
+    //      pixel equal to the tile's first?
+    const uint32_t c00 = __builtin_amdgcn_readfirstlane(c[0]);
+    {
+        uint64_t bad = 0;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const uint64_t diff = __ballot(c[i] != c00);
+            if (wave * RPW + i < vh) bad |= diff;
+        }
+        bad &= __ballot(lane_ok);
+        if (lane == 0)
+            s.Uni[wave] = ((uint64_t)(wave * RPW >= vh ? 2u : (bad == 0 ? 1u : 0u)) << 32) | c00;
     }
     lds_barrier();
-    bool uniform = true;
+    // every wave reads the same words, so every wave takes the same branch
+    const uint32_t C = (uint32_t)s.Uni[0];  // the tile's first pixel (wave 0 always has rows)
+    bool uni = true;
 #pragma unroll
-    for (int q = 0; q < NWAVES; ++q)
-        uniform &= s.Uni[q] == 2u || (s.Uni[q] == 1u && s.UniC[q] == s.UniC[0]);
+    for (int q = 0; q < NWAVES; ++q) {
+        const uint32_t state = (uint32_t)(s.Uni[q] >> 32), cq = (uint32_t)s.Uni[q];
+        uni &= state == 2u || (state == 1u && cq == C);
+    }
+    // the same for every thread: said so, the branch below stays uniform
+    const bool uniform = __builtin_amdgcn_readfirstlane((int)uni) != 0;
 
     TileHdr &hdr = w.hdr[t];
     const size_t t32 = (size_t)t * TH;
-    if (tid < TH) w.runmask[t32 + tid] = s.Mask[tid];  // rows past the image edge store 0
 
     if (uniform) {
         // ---- one colour: a single region led by the tile's first pixel, with
         //      the seam slot of its first open edge (top row, bottom row, left
         //      column, right column), one run per row
-        const uint32_t C = s.UniC[0];
         const uint32_t es = has_top ? 0u : has_bottom ? (uint32_t)TW
                           : has_left ? (uint32_t)(2 * TW) : has_right ? (uint32_t)(2 * TW + TH) : 255u;
         if (tid < vh) w.runinfo[(size_t)t * TPX + tid] = es != 255u ? (INFO_BORDER | es) : 0u;
         if (tid < TH) {
+            w.runmask[t32 + tid] = tid < vh ? 1ull : 0ull;  // rows past the image edge store 0
             const uint64_t lead = (tid == 0 && es == 255u) ? 1ull : 0ull;
             w.leadmask[t32 + tid] = lead;
             w.seg[t32 + tid] = (uint32_t)lead;
@@ -495,6 +488,30 @@ __device__ __forceinline__ void label_tile(const T *__restrict__ img, const Geom
         return;
     }
 
+    // ---- 1 Start: run starts of each row ("left neighbour differs")
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int y = wave * RPW + i;
+        const bool valid = lane_ok && y < vh;
+        const uint32_t left = from_left_lane(c[i]);
+        const bool st = valid && (lane == 0 || left != c[i]);
+        const uint64_t mi = __ballot(st);
+        if (st) {
+            const uint32_t slot = (uint32_t)(y * 64) + mbcnt(mi);
+            s.RX[sw(slot)] = (uint8_t)lane;
+            s.P[sw(slot)] = slot;
+        }
+        if (lane == 0) {
+            s.Mask[y] = mi;
+            s.ColC[y] = c[i];
+        }
+    }
+    if (wave < NWAVES - 1) s.LastC[wave][lane] = c[RPW - 1];
+    if (tid < KMAX / 64) s.Used[tid] = 0;
+    if (tid < TH) s.Lead[tid] = 0;
+    lds_barrier();
+    if (tid < TH) w.runmask[t32 + tid] = s.Mask[tid];  // rows past the image edge store 0
+
     // reading-order run index r -> run slot: rows hold cnt runs each, and the
     // runs of row y follow those of the rows above it
     uint32_t R;
@@ -514,27 +531,38 @@ __device__ __forceinline__ void label_tile(const T *__restrict__ img, const Geom
     }
 
     // ---- 2 Connect: per pixel against the row above; one queued join per
-    //      pair of touching runs of one colour
+    //      pair of touching runs of one colour.  The rows are walked in a loop
+    //      (not unrolled) so that the union code exists once.
     {
         uint32_t *q = s.Q[wave];
         uint32_t head = 0, tail = 0;
+        const int i0 = wave == 0 ? 1 : 0;
+        const int i1 = vh - wave * RPW < RPW ? vh - wave * RPW : RPW;
+        // rows move down the register array so that row i is always in r[0]
+        // and the row above it in ca
+        uint32_t r[RPW];
 #pragma unroll
-        for (int i = 0; i < RPW; ++i) {
+        for (int k = 0; k < RPW; ++k) r[k] = c[k];
+        uint32_t ca = wave > 0 ? s.LastC[wave > 0 ? wave - 1 : 0][lane] : 0u;
+        if (i0 == 1) {
+            ca = r[0];
+#pragma unroll
+            for (int k = 0; k + 1 < RPW; ++k) r[k] = r[k + 1];
+        }
+#pragma nounroll
+        for (int i = i0; i < i1; ++i) {
             const int y = wave * RPW + i;
-            if (y == 0 || (!FULL && y >= vh)) continue;
-            const uint32_t ca = i > 0 ? c[i - 1] : s.LastC[wave - 1][lane];
-            const uint64_t ma = i > 0 ? m[i - 1] : s.Mask[y - 1];
-            const bool valid = FULL || lane_ok;
-            const bool st = (m[i] >> lane) & 1ull;
-            const uint32_t cc = c[i];
+            const uint32_t cc = r[0];
+            const uint64_t mi = s.Mask[y], ma = s.Mask[y - 1];
             // lane shifts read other lanes, so they run with every lane active
             const uint32_t cl = from_left_lane(ca), cr = from_right_lane(ca);
-            const bool u0 = valid && ca == cc;
-            const bool um1 = valid && lane > 0 && cl == cc;
+            const bool st = (mi >> lane) & 1ull;
+            const bool u0 = lane_ok && ca == cc;
+            const bool um1 = lane_ok && lane > 0 && cl == cc;
             bool ra = false, rb;
             uint32_t xb;  // 0: up-left, 1: up, 2: up-right run of the join
             if (CONN == 8) {
-                const bool up1 = valid && lane + 1 < vw && cr == cc;
+                const bool up1 = lane_ok && lane + 1 < vw && cr == cc;
                 ra = up1 && !u0;         // a run of the colour starts up-right
                 rb = st && (um1 || u0);  // the run's first pixel takes up-left or up
                 xb = um1 ? 0u : 1u;
@@ -542,7 +570,7 @@ __device__ __forceinline__ void label_tile(const T *__restrict__ img, const Geom
                 rb = u0 && (st || !um1);
                 xb = 1u;
             }
-            const uint32_t me = (uint32_t)(y * 64) + mbcnt(m[i]) + (st ? 1u : 0u) - 1u;  // run of this pixel
+            const uint32_t me = (uint32_t)(y * 64) + mbcnt(mi) + (st ? 1u : 0u) - 1u;  // run of this pixel
             // run of the row above at column lane-1+xb: runs started at or before it
             const uint32_t plt = mbcnt(ma);
             const uint32_t bx = (uint32_t)(ma >> lane) & 1u;
@@ -555,9 +583,21 @@ __device__ __forceinline__ void label_tile(const T *__restrict__ img, const Geom
             tail += popc64(bbm);
             if (ra) q[(tail + mbcnt(bam)) & (QCAP - 1)] = me | (ar << 16);
             tail += popc64(bam);
-            drain_joins(s.P, q, head, tail, false, lane, w.err);
+            // unite once 64 joins are waiting, and after the last row
+            const bool last = i + 1 == i1;
+            while (tail - head >= 64u || (last && tail != head)) {
+                const uint32_t n = tail - head;
+                __syncwarp();
+                if ((uint32_t)lane < n) {
+                    const uint32_t e = q[(head + (uint32_t)lane) & (QCAP - 1)];
+                    lds_unite(s.P, e & 0xFFFFu, e >> 16, w.err);
+                }
+                head += n < 64u ? n : 64u;
+            }
+            ca = cc;
+#pragma unroll
+            for (int k = 0; k + 1 < RPW; ++k) r[k] = r[k + 1];
         }
-        drain_joins(s.P, q, head, tail, true, lane, w.err);
     }
     lds_barrier();
 
@@ -609,17 +649,19 @@ __device__ __forceinline__ void label_tile(const T *__restrict__ img, const Geom
         return 255u - (s.P[sw(root)] >> 16);
     };
     if (has_bottom && wave == NWAVES - 1 && lane_ok) {
-        const bool st = (m[RPW - 1] >> lane) & 1ull;
+        const uint64_t mb = s.Mask[TH - 1];
+        const bool st = (mb >> lane) & 1ull;
         w.bslot[(size_t)t * TW + lane] =
-            (uint8_t)seam_of((uint32_t)((TH - 1) * 64) + mbcnt(m[RPW - 1]) + (st ? 1u : 0u) - 1u);
+            (uint8_t)seam_of((uint32_t)((TH - 1) * 64) + mbcnt(mb) + (st ? 1u : 0u) - 1u);
     }
     if (has_right && wave == 2 && lane < vh)
         w.rslot[t32 + lane] = (uint8_t)seam_of((uint32_t)(lane * 64) + popc64(s.Mask[lane]) - 1u);
     if (wave == 0) {
         uint32_t n = 0;
         if (has_top) {
-            const bool st0 = (m[0] >> lane) & 1ull;
-            const uint32_t me = lane_ok ? seam_of(mbcnt(m[0]) + (st0 ? 1u : 0u) - 1u) : 0u;
+            const uint64_t m0 = s.Mask[0];
+            const bool st0 = (m0 >> lane) & 1ull;
+            const uint32_t me = lane_ok ? seam_of(mbcnt(m0) + (st0 ? 1u : 0u) - 1u) : 0u;
             n = top_requests<CONN>(w.req + (size_t)t * REQMAX, lane, lane_ok, vw, has_left, has_right,
                                    c[0], st0, me, hrow, hm1, hp1);
         }
@@ -654,18 +696,18 @@ __device__ __forceinline__ void label_tile(const T *__restrict__ img, const Geom
 
 // One workgroup per tile: workgroup v labels tile remap_tile(v), so that each
 // XCD works through one contiguous range of tiles.  Tiles wholly inside the
-// image take a path without edge checks.
+// image are loaded without edge checks.
 template <typename T, int CONN>
 __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__ img, Geom g,
                                                            Work w)
 {
     __shared__ TileLds s;
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t t = remap_tile(blockIdx.x, gridDim.x);
     const TilePos tp = tile_pos(t, g);
-    if (tp.vh == TH && tp.vw == TW)
-        label_tile<T, CONN, true>(img, g, w, s, t, tp);
-    else
-        label_tile<T, CONN, false>(img, g, w, s, t, tp);
+    const TileIn in = (tp.vh == TH && tp.vw == TW) ? load_tile<T, true>(img, g, tp, wave, lane)
+                                                   : load_tile<T, false>(img, g, tp, wave, lane);
+    label_tile<CONN>(g, w, s, t, tp, in);
 }
 
 // ------------------------------------------------------------ seam merge
