@@ -119,53 +119,52 @@ constexpr uint32_t PMASK = 0xFFFFu;
 
 __device__ __forceinline__ uint32_t sw(uint32_t slot) { return slot ^ ((slot >> 6) & 31u); }
 
-// Every find/union carries a step budget: a correct forest never comes near
-// it (tile chains are shorter than a tile's runs, and halving keeps seam chains
-// short); if it is ever exhausted the call stops early and flags ERR_LOOP in
-// the workspace error word instead of spinning.
-constexpr int LDS_BUDGET = 1 << 16;
-constexpr int GLOBAL_BUDGET = 1 << 22;
+// Loops here need no step budget: every arrow points at a smaller slot, and
+// each loop below only moves to strictly smaller slots (a word that does not
+// point lower counts as a root), so it ends after at most TPX steps even on a
+// corrupted forest.
 
 __device__ __forceinline__ uint32_t lds_parent(const uint32_t *P, uint32_t x)
 {
     return __hip_atomic_load(&P[sw(x)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & PMASK;
 }
 
-__device__ uint32_t lds_find(uint32_t *P, uint32_t x, int &budget)
+// root of x, halving the path on the way (an arrow only moves closer to the root)
+__device__ __forceinline__ uint32_t lds_find(uint32_t *P, uint32_t x)
 {
-    while (budget-- > 0) {
-        const uint32_t p = lds_parent(P, x);
-        if (p == x) return x;
+    uint32_t p = lds_parent(P, x);
+    while (p < x) {
         const uint32_t g = lds_parent(P, p);
-        if (g == p) return p;
-        atomicMin(&P[sw(x)], g);  // path halving: an arrow only moves closer to the root
-        x = g;
+        if (g < p) atomicMin(&P[sw(x)], g);
+        x = p;
+        p = g;
     }
     return x;
 }
 
-__device__ void lds_unite(uint32_t *P, uint32_t a, uint32_t b, uint32_t *err)
+// join the trees of a and b: the larger root is re-pointed at the smaller; if
+// it stopped being a root meanwhile, join again from where it points now (the
+// larger of the two roots strictly decreases each time)
+__device__ __forceinline__ void lds_unite(uint32_t *P, uint32_t a, uint32_t b)
 {
-    int budget = LDS_BUDGET;
-    while (budget > 0) {
-        a = lds_find(P, a, budget);
-        b = lds_find(P, b, budget);
-        if (budget <= 0) break;
+    for (;;) {
+        a = lds_find(P, a);
+        b = lds_find(P, b);
         if (a == b) return;
-        if (a > b) {
-            const uint32_t t = a;
-            a = b;
-            b = t;
-        }
-        const uint32_t old = atomicMin(&P[sw(b)], a);  // re-point the larger root at the smaller
-        if (old == b) return;                          // b was still a root: joined
-        b = old;                                       // someone re-pointed b first: retry
-        --budget;
+        const uint32_t lo = a < b ? a : b, hi = a ^ b ^ lo;
+        const uint32_t old = atomicMin(&P[sw(hi)], lo) & PMASK;
+        if (old >= hi) return;  // hi was still a root: joined
+        a = lo;
+        b = old;
     }
-    set_err(err, ERR_LOOP);
 }
 
 // --------------------------------------------------- union-find in global
+// These loops carry a step budget: a correct forest never comes near it
+// (halving keeps seam chains short); if it is ever exhausted the call stops
+// early and flags ERR_LOOP in the workspace error word instead of spinning.
+constexpr int GLOBAL_BUDGET = 1 << 22;
+
 // Seam node record: (reading-order key of the parent's pixel << 32) | parent
 // node id.  A root's record holds its own key and id, and the 64-bit minimum
 // orders records by key, so joins always keep the earlier pixel as leader.
@@ -590,7 +589,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
                 __syncwarp();
                 if ((uint32_t)lane < n) {
                     const uint32_t e = q[(head + (uint32_t)lane) & (QCAP - 1)];
-                    lds_unite(s.P, e & 0xFFFFu, e >> 16, w.err);
+                    lds_unite(s.P, e & 0xFFFFu, e >> 16);
                 }
                 head += n < 64u ? n : 64u;
             }
@@ -607,9 +606,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         const uint32_t slot = s.Run[r];
         const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
         const int cnt = (int)popc64(s.Mask[ry]);
-        int budget = LDS_BUDGET;
-        const uint32_t root = lds_find(s.P, slot, budget);
-        if (budget <= 0) set_err(w.err, ERR_LOOP);
+        const uint32_t root = lds_find(s.P, slot);
         if (root != slot) atomicMin(&s.P[sw(slot)], root);
         uint32_t es = 255;
         if (has_right && k == cnt - 1) es = 2 * TW + TH + ry;
