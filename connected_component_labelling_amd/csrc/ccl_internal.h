@@ -40,12 +40,14 @@ constexpr uint32_t INFO_BORDER = 0x80000000u;
 constexpr uint32_t ERR_LOOP = 1u;      // a find/union loop hit its safety bound
 
 struct TileHdr {
+    uint32_t uniform;   // 1: every valid pixel of the tile has one colour
+    uint32_t value;     // one-colour tile with a seam node: its pixels' value
+                        //   (written by the resolve pass)
     uint32_t nruns;     // runs in the tile
     uint32_t ntop;      // seam requests along the top edge
     uint32_t nleft;     // seam requests along the left edge
-    uint32_t uniform;   // 1: every valid pixel of the tile has one colour
+    uint32_t pad;
     uint64_t used[3];   // seam slots in use (bit s of word s/64)
-    uint64_t pad2;
 };
 
 // exact unsigned division of n < 2^31 by a fixed d >= 1: q = (n*m) >> s

@@ -848,6 +848,7 @@ __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, in
 {
     __shared__ uint32_t sOff[BLOCK + 1];
     __shared__ uint64_t sUsed[BLOCK][KMAX / 64];
+    __shared__ uint8_t sUni[BLOCK];
     __shared__ uint32_t sWave[NWAVES];
     const uint32_t t0 = blockIdx.x * BLOCK;
     const uint32_t tme = t0 + threadIdx.x;
@@ -858,6 +859,7 @@ __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, in
         sUsed[threadIdx.x][word] = u;
         n += popc64(u);
     }
+    sUni[threadIdx.x] = tme < (uint32_t)g.ntiles ? (uint8_t)w.hdr[tme].uniform : (uint8_t)0;
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
     sOff[threadIdx.x] = off;
@@ -1046,6 +1048,7 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
 {
     __shared__ uint32_t sOff[BLOCK + 1];
     __shared__ uint64_t sUsed[BLOCK][KMAX / 64];
+    __shared__ uint8_t sUni[BLOCK];
     __shared__ uint32_t sWave[NWAVES];
     const uint32_t t0 = blockIdx.x * BLOCK;
     const uint32_t tme = t0 + threadIdx.x;
@@ -1056,6 +1059,7 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
         sUsed[threadIdx.x][word] = u;
         n += popc64(u);
     }
+    sUni[threadIdx.x] = tme < (uint32_t)g.ntiles ? (uint8_t)w.hdr[tme].uniform : (uint8_t)0;
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
     sOff[threadIdx.x] = off;
@@ -1077,13 +1081,45 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
             val = 1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)col));
         }
         w.gp[node] = val;
+        if (sUni[j]) w.hdr[t].value = val;  // a one-colour tile's only node
     }
 }
 
 // ------------------------------------------------------------ final write
 // One wave per tile: stage the tile's run labels in LDS (runs beyond DLAB are
-// labelled from their records on the fly), then write each tile row once,
-// coalesced.
+// labelled from their records on the fly), then write the tile's rows, four
+// pixels (16 bytes) per lane where rows are whole and 16-byte aligned.
+
+// labels of the tile's rows y = lane/16, +4, ...: lane covers columns
+// 4*(lane%16) .. +3.  rowmask/rowex: lane y holds row y's run starts and the
+// runs before row y.
+template <bool ALL_STAGED, typename L>
+__device__ __forceinline__ void write_rows_x4(int32_t *o0, int64_t W, int vh, int lane,
+                                              uint32_t mlo, uint32_t mhi, uint32_t rex,
+                                              const uint32_t *lab, L run_label_slow)
+{
+    const int c4 = 4 * (lane & 15);
+    for (int yb = 0; yb < vh; yb += 4) {  // the same trip count for every lane
+        const int y = yb + (lane >> 4);
+        const int ys = y < vh ? y : vh - 1;
+        const uint64_t m = ((uint64_t)(uint32_t)__shfl((int)mhi, ys) << 32) | (uint32_t)__shfl((int)mlo, ys);
+        const uint32_t rb = (uint32_t)__shfl((int)rex, ys);
+        if (y >= vh) continue;
+        const uint32_t bits = (uint32_t)(m >> c4) & 15u;
+        const uint32_t r0 = rb + popc64(m & mask_le(c4)) - 1u;
+        const uint32_t r1 = r0 + ((bits >> 1) & 1u), r2 = r1 + ((bits >> 2) & 1u), r3 = r2 + (bits >> 3);
+        int4 v;
+        if (ALL_STAGED) {
+            v = make_int4((int)lab[r0], (int)lab[r1], (int)lab[r2], (int)lab[r3]);
+        } else {
+            v = make_int4((int)(r0 < DLAB ? lab[r0] : run_label_slow(r0)),
+                          (int)(r1 < DLAB ? lab[r1] : run_label_slow(r1)),
+                          (int)(r2 < DLAB ? lab[r2] : run_label_slow(r2)),
+                          (int)(r3 < DLAB ? lab[r3] : run_label_slow(r3)));
+        }
+        *(int4 *)(o0 + y * W + c4) = v;
+    }
+}
 
 __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int32_t *out,
                                                             int number)
@@ -1093,34 +1129,36 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     __shared__ uint64_t sLead[NWAVES][TH];
     __shared__ uint32_t sPre[NWAVES][TH];
 
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t t = remap_tile(blockIdx.x, gridDim.x) * NWAVES + wave;
     if (t >= (uint32_t)g.ntiles) return;
     const TilePos tp = tile_pos(t, g);
     const int64_t y0 = tp.y0, x0 = tp.x0, W = g.W;
     const size_t t32 = (size_t)t * TH;
     const uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
-    int32_t *o = out + (int64_t)tp.b * g.HW + y0 * W + x0 + lane;
+    int32_t *o0 = out + (int64_t)tp.b * g.HW + y0 * W + x0;
     const bool lane_ok = lane < tp.vw;
+    // 16-byte stores: whole tile rows whose starts are 16-byte aligned
+    const bool x4 = tp.vw == TW && (W & 3) == 0 && ((uintptr_t)out & 15u) == 0;
+    const TileHdr &h = w.hdr[t];
+    const uint2 uv = *(const uint2 *)&h;  // one colour?, value
 
-    if (w.hdr[t].uniform != 0u) {
-        // one colour: every pixel carries the value of run 0
-        const uint32_t info = rinfo[0];
-        uint32_t v;
-        if (info & INFO_BORDER)
-            v = (uint32_t)w.gp[(size_t)t * KMAX + (info & 0xFFu)];
-        else
-            v = number ? 1u + w.seg[t32] : (uint32_t)(y0 * W + x0);
-        if (tp.vh == TH && lane_ok) {
-#pragma unroll
-            for (int y = 0; y < TH; ++y) o[y * W] = (int32_t)v;
+    if (uv.x != 0u) {
+        // one colour: every pixel carries the region's value (its seam
+        // node's, unless the tile is the whole image)
+        const bool seam = tp.ty > 0 || tp.tx > 0 || y0 + TH < g.H || x0 + TW < W;
+        uint32_t v = uv.y;
+        if (!seam) v = number ? 1u + w.seg[t32] : (uint32_t)(y0 * W + x0);
+        if (x4) {
+            const int4 v4 = make_int4((int)v, (int)v, (int)v, (int)v);
+            for (int y = lane >> 4; y < tp.vh; y += 4) *(int4 *)(o0 + y * W + 4 * (lane & 15)) = v4;
         } else if (lane_ok) {
-            for (int y = 0; y < tp.vh; ++y) o[y * W] = (int32_t)v;
+            for (int y = 0; y < tp.vh; ++y) o0[y * W + lane] = (int32_t)v;
         }
         return;
     }
 
-    const uint32_t R = w.hdr[t].nruns;
+    const uint32_t R = h.nruns;
     uint32_t *lab = sLab[wave];
     uint32_t *nodev = sNode[wave];
     uint64_t *lead = sLead[wave];
@@ -1132,7 +1170,7 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     }
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) {
-        const uint64_t used = w.hdr[t].used[word];
+        const uint64_t used = h.used[word];
         if ((used >> lane) & 1ull) nodev[word * 64 + lane] = (uint32_t)w.gp[(size_t)t * KMAX + word * 64 + lane];
     }
     __syncwarp();
@@ -1156,13 +1194,21 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     }
     const uint32_t rex = inc - cnt;
     const uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
+    auto slow = [&](uint32_t run) -> uint32_t { return run_label(rinfo[run]); };
+    if (x4) {
+        if (R <= DLAB)
+            write_rows_x4<true>(o0, W, tp.vh, lane, mlo, mhi, rex, lab, slow);
+        else
+            write_rows_x4<false>(o0, W, tp.vh, lane, mlo, mhi, rex, lab, slow);
+        return;
+    }
     for (int y = 0; y < tp.vh; ++y) {
         const uint64_t m = ((uint64_t)__builtin_amdgcn_readlane(mhi, y) << 32) |
                            (uint32_t)__builtin_amdgcn_readlane(mlo, y);
         const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
         if (lane_ok) {
             const uint32_t run = rb + mbcnt(m) + (uint32_t)((m >> lane) & 1ull) - 1u;
-            o[y * W] = (int32_t)(run < DLAB ? lab[run] : run_label(rinfo[run]));
+            o0[y * W + lane] = (int32_t)(run < DLAB ? lab[run] : run_label(rinfo[run]));
         }
     }
 }
