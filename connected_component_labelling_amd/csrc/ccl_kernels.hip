@@ -708,6 +708,14 @@ __global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__
 }
 
 // ------------------------------------------------------------ seam merge
+// The seam passes give each workgroup NT consecutive tiles and deal their
+// items (requests or seam nodes) to its threads.  Collapse and resolve use few
+// tiles per workgroup (most threads hold one item, so that many find chains
+// are in flight at once); the merge uses more, since its unions of one large
+// region contend on the same roots when too many run at once.
+constexpr int SEAM_TILES = 64;
+constexpr int MERGE_TILES = 256;
+
 // Each workgroup covers 256 consecutive tiles.  Their requests are counted,
 // prefix-summed and dealt round-robin to the 256 threads, so a tile with many
 // requests does not serialise on one lane.  Each request is resolved to the
@@ -739,10 +747,11 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *sWave, uint32_t &
 }
 
 // index j of the tile holding item i: the largest j with off[j] <= i
-// (off[BLOCK] is the total, so a tile found this way has items)
+// (off[NT] is the total, so a tile found this way has items)
+template <int NT>
 __device__ __forceinline__ uint32_t item_tile(const uint32_t *off, uint32_t i)
 {
-    uint32_t lo = 0, hi = BLOCK - 1;
+    uint32_t lo = 0, hi = NT - 1;
     while (lo < hi) {
         const uint32_t mid = (lo + hi + 1) >> 1;
         if (off[mid] <= i) lo = mid;
@@ -753,21 +762,21 @@ __device__ __forceinline__ uint32_t item_tile(const uint32_t *off, uint32_t i)
 
 __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w)
 {
-    __shared__ uint32_t sOff[BLOCK + 1];
-    __shared__ uint32_t sTop[BLOCK];
+    __shared__ uint32_t sOff[MERGE_TILES + 1];
+    __shared__ uint32_t sTop[MERGE_TILES];
     __shared__ uint32_t sWave[NWAVES];
-    const uint32_t t0 = blockIdx.x * BLOCK;
+    const uint32_t t0 = blockIdx.x * MERGE_TILES;
     const uint32_t tme = t0 + threadIdx.x;
+    const bool mine = threadIdx.x < MERGE_TILES && tme < (uint32_t)g.ntiles;
     uint32_t ntop = 0, n = 0;
-    if (tme < (uint32_t)g.ntiles) {
+    if (mine) {
         ntop = w.hdr[tme].ntop;
         n = ntop + w.hdr[tme].nleft;
     }
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
-    sOff[threadIdx.x] = off;
-    sTop[threadIdx.x] = ntop;
-    if (threadIdx.x == 0) sOff[BLOCK] = total;
+    if (threadIdx.x <= MERGE_TILES) sOff[threadIdx.x] = off;  // sOff[MERGE_TILES] = total
+    if (threadIdx.x < MERGE_TILES) sTop[threadIdx.x] = ntop;
     __syncthreads();
     const uint32_t ntx = (uint32_t)g.ntx;
     const int lane = lane_id();
@@ -776,7 +785,7 @@ __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w)
         const uint32_t i = k * BLOCK + threadIdx.x;
         uint32_t a = 0xFFFFFFFFu, bn = 0xFFFFFFFFu;
         if (i < total) {
-            const uint32_t j = item_tile(sOff, i);
+            const uint32_t j = item_tile<MERGE_TILES>(sOff, i);
             const uint32_t t = t0 + j, r = i - sOff[j];
             const uint16_t *q = w.req + (size_t)t * REQMAX;
             if (r < sTop[j]) {
@@ -846,27 +855,25 @@ __device__ __forceinline__ uint32_t select_bit(const uint64_t (&u)[KMAX / 64], u
 
 __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, int count_leaders)
 {
-    __shared__ uint32_t sOff[BLOCK + 1];
-    __shared__ uint64_t sUsed[BLOCK][KMAX / 64];
-    __shared__ uint8_t sUni[BLOCK];
+    __shared__ uint32_t sOff[SEAM_TILES + 1];
+    __shared__ uint64_t sUsed[SEAM_TILES][KMAX / 64];
     __shared__ uint32_t sWave[NWAVES];
-    const uint32_t t0 = blockIdx.x * BLOCK;
+    const uint32_t t0 = blockIdx.x * SEAM_TILES;
     const uint32_t tme = t0 + threadIdx.x;
+    const bool mine = threadIdx.x < SEAM_TILES && tme < (uint32_t)g.ntiles;
     uint32_t n = 0;
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) {
-        const uint64_t u = tme < (uint32_t)g.ntiles ? w.hdr[tme].used[word] : 0ull;
-        sUsed[threadIdx.x][word] = u;
+        const uint64_t u = mine ? w.hdr[tme].used[word] : 0ull;
+        if (threadIdx.x < SEAM_TILES) sUsed[threadIdx.x][word] = u;
         n += popc64(u);
     }
-    sUni[threadIdx.x] = tme < (uint32_t)g.ntiles ? (uint8_t)w.hdr[tme].uniform : (uint8_t)0;
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
-    sOff[threadIdx.x] = off;
-    if (threadIdx.x == 0) sOff[BLOCK] = total;
+    if (threadIdx.x <= SEAM_TILES) sOff[threadIdx.x] = off;  // sOff[SEAM_TILES] = total
     __syncthreads();
     for (uint32_t i = threadIdx.x; i < total; i += BLOCK) {
-        const uint32_t j = item_tile(sOff, i);
+        const uint32_t j = item_tile<SEAM_TILES>(sOff, i);
         const uint32_t t = t0 + j;
         uint64_t u[KMAX / 64];
 #pragma unroll
@@ -1046,27 +1053,27 @@ __global__ __launch_bounds__(BLOCK) void scan_band_apply_kernel(Geom g, Work w)
 
 __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int number)
 {
-    __shared__ uint32_t sOff[BLOCK + 1];
-    __shared__ uint64_t sUsed[BLOCK][KMAX / 64];
-    __shared__ uint8_t sUni[BLOCK];
+    __shared__ uint32_t sOff[SEAM_TILES + 1];
+    __shared__ uint64_t sUsed[SEAM_TILES][KMAX / 64];
+    __shared__ uint8_t sUni[SEAM_TILES];
     __shared__ uint32_t sWave[NWAVES];
-    const uint32_t t0 = blockIdx.x * BLOCK;
+    const uint32_t t0 = blockIdx.x * SEAM_TILES;
     const uint32_t tme = t0 + threadIdx.x;
+    const bool mine = threadIdx.x < SEAM_TILES && tme < (uint32_t)g.ntiles;
     uint32_t n = 0;
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) {
-        const uint64_t u = tme < (uint32_t)g.ntiles ? w.hdr[tme].used[word] : 0ull;
-        sUsed[threadIdx.x][word] = u;
+        const uint64_t u = mine ? w.hdr[tme].used[word] : 0ull;
+        if (threadIdx.x < SEAM_TILES) sUsed[threadIdx.x][word] = u;
         n += popc64(u);
     }
-    sUni[threadIdx.x] = tme < (uint32_t)g.ntiles ? (uint8_t)w.hdr[tme].uniform : (uint8_t)0;
+    if (threadIdx.x < SEAM_TILES) sUni[threadIdx.x] = mine ? (uint8_t)w.hdr[tme].uniform : (uint8_t)0;
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
-    sOff[threadIdx.x] = off;
-    if (threadIdx.x == 0) sOff[BLOCK] = total;
+    if (threadIdx.x <= SEAM_TILES) sOff[threadIdx.x] = off;  // sOff[SEAM_TILES] = total
     __syncthreads();
     for (uint32_t i = threadIdx.x; i < total; i += BLOCK) {
-        const uint32_t j = item_tile(sOff, i);
+        const uint32_t j = item_tile<SEAM_TILES>(sOff, i);
         const uint32_t t = t0 + j;
         uint64_t u[KMAX / 64];
 #pragma unroll
@@ -1298,12 +1305,12 @@ void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, cons
 
 void launch_seam(const Geom &g, const Work &w, hipStream_t s)
 {
-    hipLaunchKernelGGL(seam_merge_kernel, dim3(grid_of(g.ntiles, BLOCK)), dim3(BLOCK), 0, s, g, w);
+    hipLaunchKernelGGL(seam_merge_kernel, dim3(grid_of(g.ntiles, MERGE_TILES)), dim3(BLOCK), 0, s, g, w);
 }
 
 void launch_seam_collapse(const Geom &g, const Work &w, int count_leaders, hipStream_t s)
 {
-    hipLaunchKernelGGL(seam_collapse_kernel, dim3(grid_of(g.ntiles, BLOCK)), dim3(BLOCK), 0, s,
+    hipLaunchKernelGGL(seam_collapse_kernel, dim3(grid_of(g.ntiles, SEAM_TILES)), dim3(BLOCK), 0, s,
                        g, w, count_leaders);
 }
 
@@ -1318,7 +1325,7 @@ void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, hipSt
 
 void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s)
 {
-    hipLaunchKernelGGL(resolve_kernel, dim3(grid_of(g.ntiles, BLOCK)), dim3(BLOCK), 0, s, g, w,
+    hipLaunchKernelGGL(resolve_kernel, dim3(grid_of(g.ntiles, SEAM_TILES)), dim3(BLOCK), 0, s, g, w,
                        number);
 }
 
