@@ -84,6 +84,55 @@ def load_traffic(kernel: str, launch_pixels: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def read_counter_csv(path: str, counter: str):
+    """rocprofv3 counter CSV -> list of (kernel name, value in KiB) per dispatch."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    return [(name, v) for (_, name), v in sorted(per.items())]
+
+
+def write_traffic(fetch_csv: str, write_csv: str, copy_mb: int, launch_pixels: int):
+    """HBM bytes per launch of each path kernel from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled by
+    what it reads for the plain device copy of copy_mb MiB that the same bench
+    command ran (an elementwise add: copy_mb MiB read, copy_mb MiB written)."""
+    fetch = read_counter_csv(fetch_csv, "FETCH_SIZE")
+    write = read_counter_csv(write_csv, "WRITE_SIZE")
+    nbytes = copy_mb << 20
+
+    def copy_value(rows):
+        vals = [v for name, v in rows if "elementwise" in name and "Functor" in name
+                and "Fill" not in name]
+        if not vals:
+            raise SystemExit("no copy-calibration kernel in the counter file")
+        return vals[-1]
+
+    f_fetch = nbytes / (copy_value(fetch) * 1024.0)
+    f_write = nbytes / (copy_value(write) * 1024.0)
+    out = {"_calibration": {"copy_bytes": nbytes, "fetch_factor": round(f_fetch, 4),
+                            "write_factor": round(f_write, 4)}}
+    for kernel, short in [("tile_label_kernel", "tile_label"), ("final_write_kernel", "final_write"),
+                          ("seam_merge_kernel", "seam_merge"), ("seam_collapse_kernel", "seam_collapse"),
+                          ("resolve_kernel", "resolve")]:
+        fv = [v for name, v in fetch if kernel in name]
+        wv = [v for name, v in write if kernel in name]
+        if not fv or not wv:
+            continue
+        fb = sum(fv) / len(fv) * 1024.0 * f_fetch
+        wb = sum(wv) / len(wv) * 1024.0 * f_write
+        out[short] = {"fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                      "hbm_bytes_per_launch": round(fb + wb), "pixels": launch_pixels,
+                      "source_hash": kernel_source_hash()}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(img_np, rows: int, ccl, torch):
     """Oracle (one thread) on the first `rows` rows of the sheet, and the GPU on
     the same band for a bit-exact check."""
@@ -124,7 +173,17 @@ def main():
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE, both with --copy-calibration-mb) into profiles/traffic.json "
+                         "and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        import synth
+        _, (B, H, W), _, _ = synth.CONFIGS[args.config]
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.copy_calibration_mb or 1024,
+                      B * H * W)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this labeller runs on a single MI355X and has no "
