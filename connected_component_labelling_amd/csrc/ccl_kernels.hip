@@ -487,29 +487,112 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         return;
     }
 
-    // ---- 1 Start: run starts of each row ("left neighbour differs")
+    // ---- 1 Start and 2 Connect, fused per row: a ballot marks the row's run
+    //      starts ("left neighbour differs"), start lanes initialise their run,
+    //      and the row is joined to the row above it.  The joins are found per
+    //      pixel against the row above (shifted one lane each way), so that
+    //      exactly one pixel stands for each pair of touching runs of one
+    //      colour; they are queued per wave and united in LDS with every lane
+    //      busy.  A wave's first row is joined to the last row of the wave
+    //      above only after the barrier: until then every arrow stays inside
+    //      the wave's own rows, which it has initialised itself.
+    uint32_t *q = s.Q[wave];
+    uint32_t head = 0, tail = 0;
+    // queue the joins of row y (colours cc, run starts st, starts before the
+    // lane kx) with the row above it (ca, sta, kxa)
+    auto join_rows = [&](int y, uint32_t cc, bool st, uint32_t kx, uint32_t ca, bool sta,
+                         uint32_t kxa) {
+        // lane shifts read other lanes, so they run with every lane active
+        const uint32_t cl = from_left_lane(ca), cr = from_right_lane(ca);
+        const uint32_t sta1 = from_right_lane(sta ? 1u : 0u);
+        const bool u0 = lane_ok && ca == cc;
+        const bool um1 = lane_ok && lane > 0 && cl == cc;
+        bool ra = false, rb;
+        bool left_up;  // the join of rb goes to the up-left pixel's run
+        if (CONN == 8) {
+            const bool up1 = lane_ok && lane + 1 < vw && cr == cc;
+            ra = up1 && !u0;         // a run of the colour starts up-right
+            rb = st && (um1 || u0);  // the run's first pixel takes up-left or up
+            left_up = um1;
+        } else {
+            rb = u0 && (st || !um1);
+            left_up = false;
+        }
+        const uint32_t me = (uint32_t)(y * 64) + kx + (st ? 1u : 0u) - 1u;  // run of this pixel
+        // run of the row above at column lane-1 (runs started before the lane),
+        // at the lane (plus its own start), at lane+1 (plus that start too)
+        const uint32_t above = (uint32_t)((y - 1) * 64) + kxa - 1u;
+        const uint32_t ab = above + (left_up ? 0u : (sta ? 1u : 0u));
+        const uint32_t ar = above + (sta ? 1u : 0u) + sta1;
+        const uint64_t bbm = __ballot(rb), bam = __ballot(ra);
+        if (rb) q[(tail + mbcnt(bbm)) & (QCAP - 1)] = me | (ab << 16);
+        tail += popc64(bbm);
+        if (ra) q[(tail + mbcnt(bam)) & (QCAP - 1)] = me | (ar << 16);
+        tail += popc64(bam);
+    };
+    // unite queued joins, 64 at a time while 64 wait (all: until none wait)
+    auto drain = [&](bool all) {
+        while (tail - head >= 64u || (all && tail != head)) {
+            const uint32_t n = tail - head;
+            __syncwarp();
+            if ((uint32_t)lane < n) {
+                const uint32_t e = q[(head + (uint32_t)lane) & (QCAP - 1)];
+                lds_unite(s.P, e & 0xFFFFu, e >> 16);
+            }
+            head += n < 64u ? n : 64u;
+        }
+    };
+    const int nrows = vh - wave * RPW < 0 ? 0 : (vh - wave * RPW < RPW ? vh - wave * RPW : RPW);
+    const uint32_t c0 = c[0];
+    {
+        // rows move down the register array so that row i is always in r[0]
+        uint32_t r[RPW];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-        const int y = wave * RPW + i;
-        const bool valid = lane_ok && y < vh;
-        const uint32_t left = from_left_lane(c[i]);
-        const bool st = valid && (lane == 0 || left != c[i]);
-        const uint64_t mi = __ballot(st);
-        if (st) {
-            const uint32_t slot = (uint32_t)(y * 64) + mbcnt(mi);
-            s.RX[sw(slot)] = (uint8_t)lane;
-            s.P[sw(slot)] = slot;
+        for (int k = 0; k < RPW; ++k) r[k] = c[k];
+        uint32_t ca = 0, kxa = 0;
+        bool sta = false;
+        uint32_t mlo = 0, mhi = 0, col0 = 0;  // lane i collects row i's run starts, first colour
+#pragma nounroll
+        for (int i = 0; i < nrows; ++i) {
+            const int y = wave * RPW + i;
+            const uint32_t cc = r[0];
+            const uint32_t left = from_left_lane(cc);
+            const bool st = lane_ok && (lane == 0 || left != cc);
+            const uint64_t mi = __ballot(st);
+            const uint32_t kx = mbcnt(mi);
+            if (st) {
+                const uint32_t slot = (uint32_t)(y * 64) + kx;
+                s.RX[sw(slot)] = (uint8_t)lane;
+                s.P[sw(slot)] = slot;
+            }
+            // (the colour at column 0 is read with every lane active)
+            const uint32_t cfirst = (uint32_t)__builtin_amdgcn_readfirstlane((int)cc);
+            if (lane == i) {
+                mlo = (uint32_t)mi;
+                mhi = (uint32_t)(mi >> 32);
+                col0 = cfirst;
+            }
+            if (i > 0) {
+                join_rows(y, cc, st, kx, ca, sta, kxa);
+                drain(false);
+            }
+            ca = cc;
+            sta = st;
+            kxa = kx;
+#pragma unroll
+            for (int k = 0; k + 1 < RPW; ++k) r[k] = r[k + 1];
         }
-        if (lane == 0) {
-            s.Mask[y] = mi;
-            s.ColC[y] = c[i];
+        drain(true);
+        if (lane < RPW) {  // rows past the image edge store 0
+            s.Mask[wave * RPW + lane] = lane < nrows ? ((uint64_t)mhi << 32) | mlo : 0ull;
+            s.ColC[wave * RPW + lane] = col0;
         }
+        if (wave < NWAVES - 1) s.LastC[wave][lane] = ca;  // this wave's last row
     }
-    if (wave < NWAVES - 1) s.LastC[wave][lane] = c[RPW - 1];
     if (tid < KMAX / 64) s.Used[tid] = 0;
     if (tid < TH) s.Lead[tid] = 0;
     lds_barrier();
-    if (tid < TH) w.runmask[t32 + tid] = s.Mask[tid];  // rows past the image edge store 0
+    if (tid < TH) w.runmask[t32 + tid] = s.Mask[tid];
 
     // reading-order run index r -> run slot: rows hold cnt runs each, and the
     // runs of row y follow those of the rows above it
@@ -519,8 +602,8 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         const uint32_t rown = rc;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t q = __shfl_up(rc, d);
-            if (lane >= d) rc += q;
+            const uint32_t qv = __shfl_up(rc, d);
+            if (lane >= d) rc += qv;
         }
         R = __shfl(rc, TH - 1);
         const int ry = tid & 31, rm = tid >> 5;
@@ -529,74 +612,13 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         for (int k = rm; k < cnt; k += 8) s.Run[rb + k] = (uint16_t)(ry * 64 + k);
     }
 
-    // ---- 2 Connect: per pixel against the row above; one queued join per
-    //      pair of touching runs of one colour.  The rows are walked in a loop
-    //      (not unrolled) so that the union code exists once.
-    {
-        uint32_t *q = s.Q[wave];
-        uint32_t head = 0, tail = 0;
-        const int i0 = wave == 0 ? 1 : 0;
-        const int i1 = vh - wave * RPW < RPW ? vh - wave * RPW : RPW;
-        // rows move down the register array so that row i is always in r[0]
-        // and the row above it in ca
-        uint32_t r[RPW];
-#pragma unroll
-        for (int k = 0; k < RPW; ++k) r[k] = c[k];
-        uint32_t ca = wave > 0 ? s.LastC[wave > 0 ? wave - 1 : 0][lane] : 0u;
-        if (i0 == 1) {
-            ca = r[0];
-#pragma unroll
-            for (int k = 0; k + 1 < RPW; ++k) r[k] = r[k + 1];
-        }
-#pragma nounroll
-        for (int i = i0; i < i1; ++i) {
-            const int y = wave * RPW + i;
-            const uint32_t cc = r[0];
-            const uint64_t mi = s.Mask[y], ma = s.Mask[y - 1];
-            // lane shifts read other lanes, so they run with every lane active
-            const uint32_t cl = from_left_lane(ca), cr = from_right_lane(ca);
-            const bool st = (mi >> lane) & 1ull;
-            const bool u0 = lane_ok && ca == cc;
-            const bool um1 = lane_ok && lane > 0 && cl == cc;
-            bool ra = false, rb;
-            uint32_t xb;  // 0: up-left, 1: up, 2: up-right run of the join
-            if (CONN == 8) {
-                const bool up1 = lane_ok && lane + 1 < vw && cr == cc;
-                ra = up1 && !u0;         // a run of the colour starts up-right
-                rb = st && (um1 || u0);  // the run's first pixel takes up-left or up
-                xb = um1 ? 0u : 1u;
-            } else {
-                rb = u0 && (st || !um1);
-                xb = 1u;
-            }
-            const uint32_t me = (uint32_t)(y * 64) + mbcnt(mi) + (st ? 1u : 0u) - 1u;  // run of this pixel
-            // run of the row above at column lane-1+xb: runs started at or before it
-            const uint32_t plt = mbcnt(ma);
-            const uint32_t bx = (uint32_t)(ma >> lane) & 1u;
-            const uint32_t bx1 = lane < 63 ? (uint32_t)(ma >> (lane + 1)) & 1u : 0u;
-            const uint32_t above = (uint32_t)((y - 1) * 64) + plt - 1u;
-            const uint32_t ab = above + (xb >= 1u ? bx : 0u);
-            const uint32_t ar = above + bx + bx1;
-            const uint64_t bbm = __ballot(rb), bam = __ballot(ra);
-            if (rb) q[(tail + mbcnt(bbm)) & (QCAP - 1)] = me | (ab << 16);
-            tail += popc64(bbm);
-            if (ra) q[(tail + mbcnt(bam)) & (QCAP - 1)] = me | (ar << 16);
-            tail += popc64(bam);
-            // unite once 64 joins are waiting, and after the last row
-            const bool last = i + 1 == i1;
-            while (tail - head >= 64u || (last && tail != head)) {
-                const uint32_t n = tail - head;
-                __syncwarp();
-                if ((uint32_t)lane < n) {
-                    const uint32_t e = q[(head + (uint32_t)lane) & (QCAP - 1)];
-                    lds_unite(s.P, e & 0xFFFFu, e >> 16);
-                }
-                head += n < 64u ? n : 64u;
-            }
-            ca = cc;
-#pragma unroll
-            for (int k = 0; k + 1 < RPW; ++k) r[k] = r[k + 1];
-        }
+    // the wave's first row against the last row of the wave above
+    if (wave > 0 && nrows > 0) {
+        const int y = wave * RPW;
+        const uint64_t mi = s.Mask[y], ma = s.Mask[y - 1];
+        join_rows(y, c0, (mi >> lane) & 1ull, mbcnt(mi), s.LastC[wave - 1][lane],
+                  (ma >> lane) & 1ull, mbcnt(ma));
+        drain(true);
     }
     lds_barrier();
 
