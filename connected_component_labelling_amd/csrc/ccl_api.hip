@@ -131,11 +131,11 @@ static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int6
     mark(0);
     launch_tile(colours, dtype, conn, L.g, w, s);
     mark(1);
-    launch_seam(L.g, w, s);
+    launch_seam(L.g, w, conn, s);
     mark(2);
     launch_seam_collapse(L.g, w, need_scan ? 1 : 0, s);
     mark(3);
-    if (need_scan) launch_scan(L.g, w, counts, number, s);
+    if (need_scan) launch_scan(L.g, w, counts, number, 1, s);
     launch_resolve(L.g, w, number, s);
     mark(4);
     launch_final(L.g, w, out, number, s);
@@ -198,7 +198,7 @@ int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t wi
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
     const Work w = bind_work(L, workspace);
     launch_leader_flags(leaders, L.g, w, 1, s);
-    launch_scan(L.g, w, counts, 1, s);
+    launch_scan(L.g, w, counts, 1, 0, s);
     launch_leader_assign(leaders, labels, L.g, w, s);
     return finish_launches();
 }
@@ -224,7 +224,7 @@ int ccl_count(const int32_t *leaders, int64_t batch, int64_t height, int64_t wid
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
     const Work w = bind_work(L, workspace);
     launch_leader_flags(leaders, L.g, w, 0, s);
-    launch_scan(L.g, w, counts, 0, s);
+    launch_scan(L.g, w, counts, 0, 0, s);
     return finish_launches();
 }
 

@@ -39,16 +39,32 @@ constexpr uint32_t INFO_BORDER = 0x80000000u;
 // error word bits (first word of the workspace)
 constexpr uint32_t ERR_LOOP = 1u;      // a find/union loop hit its safety bound
 
+// Per-tile header, 64 bytes, written by the tile pass in one store.  A tile
+// whose valid pixels all have one colour ("one-colour tile") writes nothing
+// else: its runs, masks, edge slots and seam requests follow from the fields
+// marked "one-colour" below.
 struct TileHdr {
-    uint32_t uniform;   // 1: every valid pixel of the tile has one colour
+    uint32_t kind;      // bit 0: one-colour tile.  One-colour: bits 8..15 its seam
+                        //   slot (255: none); bit 1: a top-edge request at column 0
+                        //   (8 neighbours), bit 2: that request goes up-left
     uint32_t value;     // one-colour tile with a seam node: its pixels' value
                         //   (written by the resolve pass)
     uint32_t nruns;     // runs in the tile
     uint32_t ntop;      // seam requests along the top edge
     uint32_t nleft;     // seam requests along the left edge
-    uint32_t pad;
+    uint32_t leftmask;  // one-colour: rows with a left-edge request
     uint64_t used[3];   // seam slots in use (bit s of word s/64)
+    uint64_t topmask;   // one-colour: columns with a top-edge request to the pixel
+                        //   up-right (8 neighbours) or up (4 neighbours)
+    uint32_t lead;      // one-colour: 1 if its first pixel leads a region (collapse pass)
+    uint32_t pre;       // one-colour: leaders before its first pixel in its image
+                        //   (scan pass)
 };
+static_assert(sizeof(TileHdr) == 64, "one 64-byte store per tile");
+
+constexpr uint32_t KIND_UNIFORM = 1u;
+constexpr uint32_t KIND_TOP0 = 2u;      // one-colour: top request at column 0
+constexpr uint32_t KIND_TOP0_UL = 4u;   // ... to the pixel up-left of column 0
 
 // exact unsigned division of n < 2^31 by a fixed d >= 1: q = (n*m) >> s
 struct FastDiv {
@@ -102,9 +118,10 @@ Work bind_work(const Layout &L, void *workspace);
 // Launchers (enqueue only).  dtype_bytes is 1 or 4, conn is 4 or 8.
 void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, const Work &w,
                  hipStream_t s);
-void launch_seam(const Geom &g, const Work &w, hipStream_t s);
+void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s);
 void launch_seam_collapse(const Geom &g, const Work &w, int count_survivors, hipStream_t s);
-void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, hipStream_t s);
+void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
+                 hipStream_t s);
 void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s);
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, hipStream_t s);
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,

@@ -357,12 +357,12 @@ __device__ __forceinline__ uint32_t left_requests(uint16_t *q, int y, bool valid
     return popc64(bu) + popc64(bl) + popc64(bdl);
 }
 
-// The pixels one wave reads for a tile: its 8 rows (lane = column) and the
-// halo, the row above the tile (wave 0) and the column to its left (wave 1).
+// The pixels one wave reads for a tile: its 8 rows (lane = column) and, for
+// wave 0, the halo: the row above the tile and the column to its left.
 struct TileIn {
     uint32_t c[RPW];
-    uint32_t hrow, hm1, hp1;  // (y0-1, x0+lane), (y0-1, x0-1), (y0-1, x0+TW)
-    uint32_t hleft;           // wave 1: (y0+lane, x0-1)
+    uint32_t hrow, hm1, hp1;  // wave 0: (y0-1, x0+lane), (y0-1, x0-1), (y0-1, x0+TW)
+    uint32_t hleft;           // wave 0: (y0+lane, x0-1)
 };
 
 template <typename T, bool FULL>
@@ -389,7 +389,7 @@ __device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geo
         if (lane == 0 && tp.tx > 0) in.hm1 = up[-1];
         if (lane == TW - 1 && x0 + TW < W) in.hp1 = up[TW];
     }
-    if (wave == 1 && tp.tx > 0 && lane < vh) in.hleft = im[(y0 + lane) * W + x0 - 1];
+    if (wave == 0 && tp.tx > 0 && lane < vh) in.hleft = im[(y0 + lane) * W + x0 - 1];
     return in;
 }
 
@@ -442,47 +442,57 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     if (uniform) {
         // ---- one colour: a single region led by the tile's first pixel, with
         //      the seam slot of its first open edge (top row, bottom row, left
-        //      column, right column), one run per row
+        //      column, right column), one run per row.  Wave 0 writes the
+        //      header, which holds everything the later passes need, and the
+        //      region's seam node; the other waves are done.
+        if (wave != 0) return;
         const uint32_t es = has_top ? 0u : has_bottom ? (uint32_t)TW
                           : has_left ? (uint32_t)(2 * TW) : has_right ? (uint32_t)(2 * TW + TH) : 255u;
-        if (tid < vh) w.runinfo[(size_t)t * TPX + tid] = es != 255u ? (INFO_BORDER | es) : 0u;
-        if (tid < TH) {
-            w.runmask[t32 + tid] = tid < vh ? 1ull : 0ull;  // rows past the image edge store 0
-            const uint64_t lead = (tid == 0 && es == 255u) ? 1ull : 0ull;
-            w.leadmask[t32 + tid] = lead;
-            w.seg[t32 + tid] = (uint32_t)lead;
-        }
-        if (tid < KMAX / 64)
-            hdr.used[tid] = (es != 255u && (es >> 6) == (uint32_t)tid) ? 1ull << (es & 63u) : 0ull;
-        if (tid == 0) {
-            hdr.nruns = (uint32_t)vh;
-            hdr.uniform = 1u;
-            if (es != 255u) {
-                const uint32_t node = t * KMAX + es;
-                const uint32_t key = (uint32_t)y0 * (uint32_t)W + (uint32_t)x0;
-                w.gp[node] = ((uint64_t)key << 32) | node;
+        uint32_t kind = KIND_UNIFORM | (es << 8);
+        uint64_t topmask = 0;
+        uint32_t ntop = 0, nleft = 0, leftmask = 0;
+        if (has_top) {
+            // tile row 0 is one run of colour C against the row above
+            const uint32_t hl = from_left_lane(hrow), hr = from_right_lane(hrow);
+            const bool u0 = lane_ok && hrow == C;
+            const bool um1 = lane_ok && (lane >= 1 ? hl == C : (has_left && hm1 == C));
+            const bool up1 = lane_ok && (lane < TW - 1 ? (lane + 1 < vw && hr == C) : (has_right && hp1 == C));
+            if (CONN == 8) {
+                topmask = __ballot(up1 && !u0);  // a stretch of the colour starts up-right
+                const uint64_t l0 = __ballot(lane == 0 && (um1 || u0));
+                const uint64_t l0ul = __ballot(lane == 0 && um1);
+                if (l0) kind |= KIND_TOP0 | (l0ul ? KIND_TOP0_UL : 0u);
+                ntop = popc64(topmask) + (l0 ? 1u : 0u);
+            } else {
+                topmask = __ballot(u0 && (lane == 0 || !um1));  // a stretch starts up
+                ntop = popc64(topmask);
             }
         }
-        if (has_bottom && wave == NWAVES - 1 && lane_ok) w.bslot[(size_t)t * TW + lane] = (uint8_t)es;
-        if (has_right && wave == 2 && lane < vh) w.rslot[t32 + lane] = (uint8_t)es;
-        if (wave == 0) {
-            const uint32_t n = has_top ? top_requests<CONN>(w.req + (size_t)t * REQMAX, lane, lane_ok, vw,
-                                                            has_left, has_right, C, lane == 0, es,
-                                                            hrow, hm1, hp1)
-                                       : 0u;
-            if (lane == 0) hdr.ntop = n;
+        if (has_left) {
+            // lane y: column 0 of row y (colour C) against the halo column;
+            // the row above already joins unless its halo pixel differs
+            const bool ml = lane < vh && hleft == C;
+            const uint32_t hu = from_left_lane(hleft);
+            leftmask = (uint32_t)__ballot(ml && (lane == 0 || hu != C));
+            nleft = (uint32_t)__popc(leftmask);
         }
-        if (wave == 1) {
-            uint32_t n = 0;
-            if (has_left) {
-                const int y = lane;
-                const bool valid = y < vh;
-                const uint32_t hu = from_left_lane(hleft), hd = from_right_lane(hleft);
-                n = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, y, valid,
-                                        valid && y >= 1, valid && y + 1 < vh, es, C, hleft, C, hu,
-                                        C, hd);
-            }
-            if (lane == 0) hdr.nleft = n;
+        if (lane < (int)(sizeof(TileHdr) / 4)) {
+            uint32_t v = 0;
+            if (lane == 0) v = kind;
+            if (lane == 2) v = (uint32_t)vh;
+            if (lane == 3) v = ntop;
+            if (lane == 4) v = nleft;
+            if (lane == 5) v = leftmask;
+            if (es != 255u && lane == 6 + (int)(es >> 5)) v = 1u << (es & 31u);
+            if (lane == 12) v = (uint32_t)topmask;
+            if (lane == 13) v = (uint32_t)(topmask >> 32);
+            if (lane == 14 && es == 255u) v = 1u;  // the whole image: its first pixel leads
+            ((uint32_t *)&hdr)[lane] = v;
+        }
+        if (lane == 0 && es != 255u) {
+            const uint32_t node = t * KMAX + es;
+            const uint32_t key = (uint32_t)y0 * (uint32_t)W + (uint32_t)x0;
+            w.gp[node] = ((uint64_t)key << 32) | node;
         }
         return;
     }
@@ -676,36 +686,38 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     if (has_right && wave == 2 && lane < vh)
         w.rslot[t32 + lane] = (uint8_t)seam_of((uint32_t)(lane * 64) + popc64(s.Mask[lane]) - 1u);
     if (wave == 0) {
-        uint32_t n = 0;
+        uint32_t ntop = 0, nleft = 0;
         if (has_top) {
             const uint64_t m0 = s.Mask[0];
             const bool st0 = (m0 >> lane) & 1ull;
             const uint32_t me = lane_ok ? seam_of(mbcnt(m0) + (st0 ? 1u : 0u) - 1u) : 0u;
-            n = top_requests<CONN>(w.req + (size_t)t * REQMAX, lane, lane_ok, vw, has_left, has_right,
-                                   c[0], st0, me, hrow, hm1, hp1);
+            ntop = top_requests<CONN>(w.req + (size_t)t * REQMAX, lane, lane_ok, vw, has_left,
+                                      has_right, c[0], st0, me, hrow, hm1, hp1);
         }
-        if (lane == 0) hdr.ntop = n;
-    }
-    if (wave == 1) {
-        uint32_t n = 0;
         if (has_left) {
             const int y = lane;
             const bool valid = y < vh;
             const bool up_ok = valid && y >= 1, dn_ok = valid && y + 1 < vh;
+            const uint32_t hu = from_left_lane(hleft), hd = from_right_lane(hleft);
             const uint32_t me = valid ? seam_of((uint32_t)(y * 64)) : 0u;
             const uint32_t cur = valid ? s.ColC[y] : 0u;
             const uint32_t cu = up_ok ? s.ColC[y - 1] : 0u, cd = dn_ok ? s.ColC[y + 1] : 0u;
-            const uint32_t hu = from_left_lane(hleft), hd = from_right_lane(hleft);
-            n = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, y, valid, up_ok, dn_ok, me,
-                                    cur, hleft, cu, hu, cd, hd);
+            nleft = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, y, valid, up_ok, dn_ok,
+                                        me, cur, hleft, cu, hu, cd, hd);
         }
-        if (lane == 0) hdr.nleft = n;
+        // the header in one store (the one-colour fields stay 0)
+        if (lane < (int)(sizeof(TileHdr) / 4)) {
+            uint32_t v = 0;
+            if (lane == 2) v = R;
+            if (lane == 3) v = ntop;
+            if (lane == 4) v = nleft;
+            if (lane >= 6 && lane < 12) {
+                const uint64_t u = s.Used[(lane - 6) >> 1];
+                v = (lane & 1) ? (uint32_t)(u >> 32) : (uint32_t)u;
+            }
+            ((uint32_t *)&hdr)[lane] = v;
+        }
     }
-    if (tid == 0) {
-        hdr.nruns = R;
-        hdr.uniform = 0u;
-    }
-    if (tid < KMAX / 64) hdr.used[tid] = s.Used[tid];
     if (tid >= 64 && tid < 64 + TH) {  // rows past the image edge store 0
         const uint64_t lead = s.Lead[tid - 64];
         w.leadmask[t32 + tid - 64] = lead;
@@ -782,18 +794,50 @@ __device__ __forceinline__ uint32_t item_tile(const uint32_t *off, uint32_t i)
     return lo;
 }
 
-__global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w)
+// the r-th set bit (from 0) of a 64-bit mask
+__device__ __forceinline__ uint32_t select_bit64(uint64_t m, uint32_t r)
+{
+    uint32_t base = 0;
+    const uint32_t lo = popc64(m & 0xFFFFFFFFull);
+    if (r >= lo) {
+        r -= lo;
+        m >>= 32;
+        base = 32;
+    }
+    uint32_t x = (uint32_t)m;
+    for (; r > 0; --r) x &= x - 1u;  // drop the r lowest set bits
+    return base + (uint32_t)__builtin_ctz(x);
+}
+
+// seam slot of the pixel at (row, col) of tile tn on its bottom row or right
+// column: a one-colour tile has a single slot, kept in its header
+__device__ __forceinline__ uint32_t edge_slot(const Work &w, uint32_t tn, const uint8_t *slots,
+                                              uint32_t idx)
+{
+    const uint32_t kind = w.hdr[tn].kind;
+    const uint32_t s8 = slots[idx];
+    return (kind & KIND_UNIFORM) ? (kind >> 8) & 0xFFu : s8;
+}
+
+__global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w, int conn)
 {
     __shared__ uint32_t sOff[MERGE_TILES + 1];
     __shared__ uint32_t sTop[MERGE_TILES];
+    __shared__ uint32_t sKind[MERGE_TILES];
+    __shared__ uint32_t sLeftMask[MERGE_TILES];
+    __shared__ uint64_t sTopMask[MERGE_TILES];
     __shared__ uint32_t sWave[NWAVES];
     const uint32_t t0 = blockIdx.x * MERGE_TILES;
     const uint32_t tme = t0 + threadIdx.x;
     const bool mine = threadIdx.x < MERGE_TILES && tme < (uint32_t)g.ntiles;
     uint32_t ntop = 0, n = 0;
     if (mine) {
-        ntop = w.hdr[tme].ntop;
-        n = ntop + w.hdr[tme].nleft;
+        const TileHdr &h = w.hdr[tme];
+        ntop = h.ntop;
+        n = ntop + h.nleft;
+        sKind[threadIdx.x] = h.kind;
+        sLeftMask[threadIdx.x] = h.leftmask;
+        sTopMask[threadIdx.x] = h.topmask;
     }
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
@@ -809,10 +853,28 @@ __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w)
         if (i < total) {
             const uint32_t j = item_tile<MERGE_TILES>(sOff, i);
             const uint32_t t = t0 + j, r = i - sOff[j];
+            const uint32_t kind = sKind[j];
+            const bool uni = kind & KIND_UNIFORM;
             const uint16_t *q = w.req + (size_t)t * REQMAX;
             if (r < sTop[j]) {
-                const uint32_t rq = q[r];
-                const int xp = (int)(rq >> 8) - 1;
+                // across the top edge: this tile's slot, and the column of the
+                // pixel above (-1 and TW: the tiles up-left and up-right)
+                uint32_t me;
+                int xp;
+                if (uni) {
+                    me = (kind >> 8) & 0xFFu;
+                    const uint32_t r0 = (kind & KIND_TOP0) ? 1u : 0u;
+                    if (r < r0) {
+                        xp = (kind & KIND_TOP0_UL) ? -1 : 0;
+                    } else {
+                        const int x = (int)select_bit64(sTopMask[j], r - r0);
+                        xp = conn == 8 ? x + 1 : x;
+                    }
+                } else {
+                    const uint32_t rq = q[r];
+                    me = rq & 0xFFu;
+                    xp = (int)(rq >> 8) - 1;
+                }
                 uint32_t tn;
                 int col;
                 if (xp < 0) {
@@ -825,13 +887,23 @@ __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w)
                     tn = t - ntx;
                     col = xp;
                 }
-                a = t * KMAX + (rq & 0xFFu);
-                bn = tn * KMAX + w.bslot[(size_t)tn * TW + col];
+                a = t * KMAX + me;
+                bn = tn * KMAX + edge_slot(w, tn, w.bslot, (uint32_t)tn * TW + (uint32_t)col);
             } else {
-                const uint32_t rq = q[REQ_TOP + r - sTop[j]];
+                // across the left edge: this tile's slot and the tile row
+                uint32_t me, row;
+                if (uni) {
+                    me = (kind >> 8) & 0xFFu;
+                    uint64_t lm = sLeftMask[j];
+                    row = select_bit64(lm, r - sTop[j]);
+                } else {
+                    const uint32_t rq = q[REQ_TOP + r - sTop[j]];
+                    me = rq & 0xFFu;
+                    row = (rq >> 8) & 0x7Fu;
+                }
                 const uint32_t tn = t - 1;
-                a = t * KMAX + (rq & 0xFFu);
-                bn = tn * KMAX + w.rslot[(size_t)tn * TH + ((rq >> 8) & 0x7Fu)];
+                a = t * KMAX + me;
+                bn = tn * KMAX + edge_slot(w, tn, w.rslot, (uint32_t)tn * TH + row);
             }
         }
         const uint32_t pa = __shfl_up(a, 1), pb = __shfl_up(bn, 1);
@@ -879,6 +951,7 @@ __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, in
 {
     __shared__ uint32_t sOff[SEAM_TILES + 1];
     __shared__ uint64_t sUsed[SEAM_TILES][KMAX / 64];
+    __shared__ uint8_t sUni[SEAM_TILES];
     __shared__ uint32_t sWave[NWAVES];
     const uint32_t t0 = blockIdx.x * SEAM_TILES;
     const uint32_t tme = t0 + threadIdx.x;
@@ -890,6 +963,7 @@ __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, in
         if (threadIdx.x < SEAM_TILES) sUsed[threadIdx.x][word] = u;
         n += popc64(u);
     }
+    if (threadIdx.x < SEAM_TILES) sUni[threadIdx.x] = mine ? (uint8_t)(w.hdr[tme].kind & KIND_UNIFORM) : (uint8_t)0;
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
     if (threadIdx.x <= SEAM_TILES) sOff[threadIdx.x] = off;  // sOff[SEAM_TILES] = total
@@ -905,6 +979,8 @@ __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, in
         const uint32_t root = g_root(w.gp, node, rrec, w.err);
         if (root != node) {
             g_min(&w.gp[node], rrec);
+        } else if (count_leaders && sUni[j]) {
+            w.hdr[t].lead = 1u;  // a one-colour tile's only node: its first pixel leads
         } else if (count_leaders) {
             const TilePos tp = tile_pos(t, g);
             const uint32_t key = (uint32_t)(rrec >> 32);
@@ -954,7 +1030,10 @@ __device__ void block_scan_rows(uint32_t (&vals)[TH], uint32_t (&tot)[TH], uint3
     __syncthreads();
 }
 
-__global__ __launch_bounds__(BLOCK) void scan_band_sum_kernel(Geom g, Work w)
+// With headers (the labelling path), a one-colour tile counts the leader bit
+// of its header in row 0 instead of its row-segment counts, which it never
+// wrote; ccl_number / ccl_count have no headers.
+__global__ __launch_bounds__(BLOCK) void scan_band_sum_kernel(Geom g, Work w, int use_hdr)
 {
     __shared__ uint32_t sW[NWAVES * TH];
     const uint32_t band = blockIdx.x;  // b * nty + ty
@@ -964,6 +1043,10 @@ __global__ __launch_bounds__(BLOCK) void scan_band_sum_kernel(Geom g, Work w)
 #pragma unroll
     for (int y = 0; y < TH; ++y) acc[y] = 0;
     for (uint32_t tx = threadIdx.x; tx < (uint32_t)g.ntx; tx += BLOCK) {
+        if (use_hdr && (w.hdr[t0 + tx].kind & KIND_UNIFORM)) {
+            acc[0] += w.hdr[t0 + tx].lead;
+            continue;
+        }
         const uint4 *p = (const uint4 *)(w.seg + (t0 + tx) * TH);
 #pragma unroll
         for (int q = 0; q < TH / 4; ++q) {
@@ -1024,7 +1107,7 @@ __global__ __launch_bounds__(BLOCK) void scan_rows_kernel(Geom g, Work w, int32_
     if (threadIdx.x == 0 && counts) counts[b] = (int32_t)carry;
 }
 
-__global__ __launch_bounds__(BLOCK) void scan_band_apply_kernel(Geom g, Work w)
+__global__ __launch_bounds__(BLOCK) void scan_band_apply_kernel(Geom g, Work w, int use_hdr)
 {
     __shared__ uint32_t sW[NWAVES * TH];
     const uint32_t band = blockIdx.x;
@@ -1038,6 +1121,10 @@ __global__ __launch_bounds__(BLOCK) void scan_band_apply_kernel(Geom g, Work w)
 #pragma unroll
     for (int y = 0; y < TH; ++y) acc[y] = 0;
     for (uint32_t j = 0; j < G && tx0 + j < ntx; ++j) {
+        if (use_hdr && (w.hdr[t0 + tx0 + j].kind & KIND_UNIFORM)) {
+            acc[0] += w.hdr[t0 + tx0 + j].lead;
+            continue;
+        }
         const uint4 *p = (const uint4 *)(w.seg + (t0 + tx0 + j) * TH);
 #pragma unroll
         for (int q = 0; q < TH / 4; ++q) {
@@ -1054,6 +1141,12 @@ __global__ __launch_bounds__(BLOCK) void scan_band_apply_kernel(Geom g, Work w)
     for (int y = 0; y < TH; ++y)
         acc[y] += Y0 + y < g.H ? w.rowoff[(int64_t)b * g.H + Y0 + y] : 0u;
     for (uint32_t j = 0; j < G && tx0 + j < ntx; ++j) {
+        if (use_hdr && (w.hdr[t0 + tx0 + j].kind & KIND_UNIFORM)) {
+            TileHdr &h = w.hdr[t0 + tx0 + j];
+            h.pre = acc[0];  // leaders before the tile's first pixel
+            acc[0] += h.lead;
+            continue;
+        }
         uint4 *p = (uint4 *)(w.seg + (t0 + tx0 + j) * TH);
 #pragma unroll
         for (int q = 0; q < TH / 4; ++q) {
@@ -1089,7 +1182,7 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
         if (threadIdx.x < SEAM_TILES) sUsed[threadIdx.x][word] = u;
         n += popc64(u);
     }
-    if (threadIdx.x < SEAM_TILES) sUni[threadIdx.x] = mine ? (uint8_t)w.hdr[tme].uniform : (uint8_t)0;
+    if (threadIdx.x < SEAM_TILES) sUni[threadIdx.x] = mine ? (uint8_t)(w.hdr[tme].kind & KIND_UNIFORM) : (uint8_t)0;
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
     if (threadIdx.x <= SEAM_TILES) sOff[threadIdx.x] = off;  // sOff[SEAM_TILES] = total
@@ -1106,8 +1199,13 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
         if (number) {
             uint32_t tl, row, col;
             pixel_tile(key, fast_div(t, g.divTpi), g, tl, row, col);
-            const size_t sg = (size_t)tl * TH + row;
-            val = 1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)col));
+            const uint32_t lkind = w.hdr[tl].kind;
+            if (lkind & KIND_UNIFORM) {
+                val = 1u + w.hdr[tl].pre;  // the leader is a one-colour tile's first pixel
+            } else {
+                const size_t sg = (size_t)tl * TH + row;
+                val = 1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)col));
+            }
         }
         w.gp[node] = val;
         if (sUni[j]) w.hdr[t].value = val;  // a one-colour tile's only node
@@ -1170,14 +1268,14 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     // 16-byte stores: whole tile rows whose starts are 16-byte aligned
     const bool x4 = tp.vw == TW && (W & 3) == 0 && ((uintptr_t)out & 15u) == 0;
     const TileHdr &h = w.hdr[t];
-    const uint2 uv = *(const uint2 *)&h;  // one colour?, value
+    const uint2 uv = *(const uint2 *)&h;  // kind, value
 
-    if (uv.x != 0u) {
+    if (uv.x & KIND_UNIFORM) {
         // one colour: every pixel carries the region's value (its seam
         // node's, unless the tile is the whole image)
         const bool seam = tp.ty > 0 || tp.tx > 0 || y0 + TH < g.H || x0 + TW < W;
         uint32_t v = uv.y;
-        if (!seam) v = number ? 1u + w.seg[t32] : (uint32_t)(y0 * W + x0);
+        if (!seam) v = number ? 1u + h.pre : (uint32_t)(y0 * W + x0);
         if (x4) {
             const int4 v4 = make_int4((int)v, (int)v, (int)v, (int)v);
             for (int y = lane >> 4; y < tp.vh; y += 4) *(int4 *)(o0 + y * W + 4 * (lane & 15)) = v4;
@@ -1325,9 +1423,10 @@ void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, cons
     }
 }
 
-void launch_seam(const Geom &g, const Work &w, hipStream_t s)
+void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s)
 {
-    hipLaunchKernelGGL(seam_merge_kernel, dim3(grid_of(g.ntiles, MERGE_TILES)), dim3(BLOCK), 0, s, g, w);
+    hipLaunchKernelGGL(seam_merge_kernel, dim3(grid_of(g.ntiles, MERGE_TILES)), dim3(BLOCK), 0, s, g, w,
+                       conn);
 }
 
 void launch_seam_collapse(const Geom &g, const Work &w, int count_leaders, hipStream_t s)
@@ -1336,13 +1435,15 @@ void launch_seam_collapse(const Geom &g, const Work &w, int count_leaders, hipSt
                        g, w, count_leaders);
 }
 
-void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, hipStream_t s)
+void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
+                 hipStream_t s)
 {
-    hipLaunchKernelGGL(scan_band_sum_kernel, dim3((unsigned)g.nbands), dim3(BLOCK), 0, s, g, w);
+    hipLaunchKernelGGL(scan_band_sum_kernel, dim3((unsigned)g.nbands), dim3(BLOCK), 0, s, g, w,
+                       use_hdr);
     hipLaunchKernelGGL(scan_rows_kernel, dim3((unsigned)g.B), dim3(BLOCK), 0, s, g, w, counts);
     if (apply)
         hipLaunchKernelGGL(scan_band_apply_kernel, dim3((unsigned)g.nbands), dim3(BLOCK), 0, s, g,
-                           w);
+                           w, use_hdr);
 }
 
 void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s)
