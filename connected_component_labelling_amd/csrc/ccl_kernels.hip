@@ -1290,16 +1290,28 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     uint32_t *nodev = sNode[wave];
     uint64_t *lead = sLead[wave];
     uint32_t *pre = sPre[wave];
+    // every record of the tile is requested before any is used, so that their
+    // latencies overlap (the node and run-record areas of a tile always exist,
+    // so those are read unconditionally)
     const uint64_t mk = lane < TH ? w.runmask[t32 + lane] : 0ull;
+    const uint64_t ld = (number && lane < TH) ? w.leadmask[t32 + lane] : 0ull;
+    const uint32_t pr = (number && lane < TH) ? w.seg[t32 + lane] : 0u;
+    uint64_t used[KMAX / 64];
+#pragma unroll
+    for (int word = 0; word < KMAX / 64; ++word) used[word] = h.used[word];
+    uint32_t nv[KMAX / 64];
+#pragma unroll
+    for (int word = 0; word < KMAX / 64; ++word) nv[word] = (uint32_t)w.gp[(size_t)t * KMAX + word * 64 + lane];
+    uint32_t info[DLAB / 64];
+#pragma unroll
+    for (int j = 0; j < DLAB / 64; ++j) info[j] = rinfo[(uint32_t)lane + 64u * (uint32_t)j];
     if (number && lane < TH) {
-        lead[lane] = w.leadmask[t32 + lane];
-        pre[lane] = w.seg[t32 + lane];
+        lead[lane] = ld;
+        pre[lane] = pr;
     }
 #pragma unroll
-    for (int word = 0; word < KMAX / 64; ++word) {
-        const uint64_t used = h.used[word];
-        if ((used >> lane) & 1ull) nodev[word * 64 + lane] = (uint32_t)w.gp[(size_t)t * KMAX + word * 64 + lane];
-    }
+    for (int word = 0; word < KMAX / 64; ++word)
+        if ((used[word] >> lane) & 1ull) nodev[word * 64 + lane] = nv[word];
     __syncwarp();
     auto run_label = [&](uint32_t info) -> uint32_t {
         if (info & INFO_BORDER) return nodev[info & 0xFFu];
@@ -1308,7 +1320,11 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         return (uint32_t)((y0 + row) * W + x0 + col);
     };
     const uint32_t nl = R < DLAB ? R : DLAB;
-    for (uint32_t r = lane; r < nl; r += 64) lab[r] = run_label(rinfo[r]);
+#pragma unroll
+    for (int j = 0; j < DLAB / 64; ++j) {
+        const uint32_t r = (uint32_t)lane + 64u * (uint32_t)j;
+        if (r < nl) lab[r] = run_label(info[j]);
+    }
     __syncwarp();
 
     // runs before each row (lane y holds row y's)
