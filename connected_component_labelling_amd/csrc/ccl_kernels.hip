@@ -1217,6 +1217,19 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
 // labelled from their records on the fly), then write the tile's rows, four
 // pixels (16 bytes) per lane where rows are whole and 16-byte aligned.
 
+// Label stores are streaming (non-temporal): the labels are not read again by
+// this pass, so they should not take L2 space from the run records.
+typedef int int4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_label4(int32_t *p, int4 v)
+{
+    const int4v vv = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(vv, (int4v *)p);
+}
+__device__ __forceinline__ void store_label(int32_t *p, int32_t v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
 // labels of the tile's rows y = lane/16, +4, ...: lane covers columns
 // 4*(lane%16) .. +3.  rowmask/rowex: lane y holds row y's run starts and the
 // runs before row y.
@@ -1244,7 +1257,7 @@ __device__ __forceinline__ void write_rows_x4(int32_t *o0, int64_t W, int vh, in
                           (int)(r2 < DLAB ? lab[r2] : run_label_slow(r2)),
                           (int)(r3 < DLAB ? lab[r3] : run_label_slow(r3)));
         }
-        *(int4 *)(o0 + y * W + c4) = v;
+        store_label4(o0 + y * W + c4, v);
     }
 }
 
@@ -1278,9 +1291,9 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         if (!seam) v = number ? 1u + h.pre : (uint32_t)(y0 * W + x0);
         if (x4) {
             const int4 v4 = make_int4((int)v, (int)v, (int)v, (int)v);
-            for (int y = lane >> 4; y < tp.vh; y += 4) *(int4 *)(o0 + y * W + 4 * (lane & 15)) = v4;
+            for (int y = lane >> 4; y < tp.vh; y += 4) store_label4(o0 + y * W + 4 * (lane & 15), v4);
         } else if (lane_ok) {
-            for (int y = 0; y < tp.vh; ++y) o0[y * W + lane] = (int32_t)v;
+            for (int y = 0; y < tp.vh; ++y) store_label(o0 + y * W + lane, (int32_t)v);
         }
         return;
     }
@@ -1351,7 +1364,7 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
         if (lane_ok) {
             const uint32_t run = rb + mbcnt(m) + (uint32_t)((m >> lane) & 1ull) - 1u;
-            o0[y * W + lane] = (int32_t)(run < DLAB ? lab[run] : run_label(rinfo[run]));
+            store_label(o0 + y * W + lane, (int32_t)(run < DLAB ? lab[run] : run_label(rinfo[run])));
         }
     }
 }
