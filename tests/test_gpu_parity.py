@@ -134,6 +134,42 @@ def test_structured(ccl, conn):
         check_case(ccl, name, img, conn)
 
 
+def mosaic_images():
+    """Solid areas (tiles of one colour) beside noisy ones: aligned and shifted
+    against the 64x32 tile grid, solid areas that meet across tile edges only
+    through a few pixels or a diagonal, and single tiles."""
+    out = {}
+    rng = np.random.default_rng(21)
+    for H, W, bh, bw, off in [(96, 192, 32, 64, (0, 0)), (130, 260, 40, 70, (5, 17)),
+                              (64, 256, 32, 64, (0, 0)), (200, 333, 50, 90, (13, 40))]:
+        yy, xx = np.mgrid[0:H, 0:W]
+        cell = ((yy + off[0]) // bh) * 1000 + (xx + off[1]) // bw
+        solid_colour = (cell % 3).astype(np.uint32) + 7          # neighbouring cells may match
+        noisy = rng.random((H // 8 + 1, W // 8 + 1)) < 0.3
+        noise_cell = np.kron(noisy, np.ones((8, 8), bool))[:H, :W]
+        img = np.where(noise_cell, rng.integers(0, 3, size=(H, W)).astype(np.uint32) + 7, solid_colour)
+        out[f"mosaic {H}x{W} cells {bh}x{bw}"] = img
+    # one-colour tiles joined to each other only through one pixel or a diagonal
+    img = np.zeros((96, 192), np.uint32)
+    img[0:32, 0:64] = 5
+    img[32:64, 64:128] = 5                                         # diagonal corner contact
+    img[31, 64] = 9                                                 # keeps tile (0,1) mixed
+    img[64:96, 0:64] = 5
+    img[63, 10] = 5                                                 # one-pixel bridge upward
+    out["one-colour tiles meeting at corners"] = img
+    out["single tile, one colour"] = np.full((32, 64), 3, np.uint32)
+    out["single partial tile, one colour"] = np.full((17, 40), 3, np.uint32)
+    out["two tiles, one colour"] = np.full((32, 128), 3, np.uint32)
+    return out
+
+
+@pytest.mark.parametrize("conn", [8, 4])
+@pytest.mark.parametrize("dtype", [np.uint32, np.uint8])
+def test_one_colour_tiles(ccl, conn, dtype):
+    for name, img in mosaic_images().items():
+        check_case(ccl, name, img.astype(dtype), conn)
+
+
 def test_batch_ragged(ccl):
     rng = np.random.default_rng(3)
     img = rng.integers(0, 3, size=(3, 70, 130)).astype(np.uint8)
