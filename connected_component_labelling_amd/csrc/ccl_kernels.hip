@@ -555,17 +555,14 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     const int nrows = vh - wave * RPW < 0 ? 0 : (vh - wave * RPW < RPW ? vh - wave * RPW : RPW);
     const uint32_t c0 = c[0];
     {
-        // rows move down the register array so that row i is always in r[0]
-        uint32_t r[RPW];
-#pragma unroll
-        for (int k = 0; k < RPW; ++k) r[k] = c[k];
         uint32_t ca = 0, kxa = 0;
         bool sta = false;
         uint32_t mlo = 0, mhi = 0, col0 = 0;  // lane i collects row i's run starts, first colour
-#pragma nounroll
-        for (int i = 0; i < nrows; ++i) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            if (i >= nrows) break;
             const int y = wave * RPW + i;
-            const uint32_t cc = r[0];
+            const uint32_t cc = c[i];
             const uint32_t left = from_left_lane(cc);
             const bool st = lane_ok && (lane == 0 || left != cc);
             const uint64_t mi = __ballot(st);
@@ -589,8 +586,6 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             ca = cc;
             sta = st;
             kxa = kx;
-#pragma unroll
-            for (int k = 0; k + 1 < RPW; ++k) r[k] = r[k + 1];
         }
         drain(true);
         if (lane < RPW) {  // rows past the image edge store 0
