@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popc
 // taken where every lane is active.
 __device__ __forceinline__ uint32_t from_left_lane(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138 /* wave_shr:1 */, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138 /* wave_shr:1 */, 0xF, 0xF, true);
 }
 
 // Map workgroup ids to work items so that each XCD (workgroups are dealt to the
@@ -265,7 +265,7 @@ __device__ __forceinline__ void lds_barrier()
 // value of lane+1 (lane 63 gets 0)
 __device__ __forceinline__ uint32_t from_right_lane(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130 /* wave_shl:1 */, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130 /* wave_shl:1 */, 0xF, 0xF, true);
 }
 
 // number of set bits of m below this lane
@@ -587,7 +587,6 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             sta = st;
             kxa = kx;
         }
-        drain(true);
         if (lane < RPW) {  // rows past the image edge store 0
             s.Mask[wave * RPW + lane] = lane < nrows ? ((uint64_t)mhi << 32) | mlo : 0ull;
             s.ColC[wave * RPW + lane] = col0;
@@ -617,14 +616,16 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         for (int k = rm; k < cnt; k += 8) s.Run[rb + k] = (uint16_t)(ry * 64 + k);
     }
 
-    // the wave's first row against the last row of the wave above
+    // the wave's first row against the last row of the wave above; then every
+    // join still queued (fewer than 64 from the wave's rows, and these) is
+    // united
     if (wave > 0 && nrows > 0) {
         const int y = wave * RPW;
         const uint64_t mi = s.Mask[y], ma = s.Mask[y - 1];
         join_rows(y, c0, (mi >> lane) & 1ull, mbcnt(mi), s.LastC[wave - 1][lane],
                   (ma >> lane) & 1ull, mbcnt(ma));
-        drain(true);
     }
+    drain(true);
     lds_barrier();
 
     // ---- 3 Collapse; runs on an edge shared with another tile offer their
