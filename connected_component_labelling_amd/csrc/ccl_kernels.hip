@@ -179,13 +179,19 @@ __device__ __forceinline__ uint64_t g_min(uint64_t *p, uint64_t v)
     return __hip_atomic_fetch_min(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// PLAIN: cacheable loads, for passes that run after every union is done.  A
+// stale cached record then only shows an earlier parent on the path to the
+// same root (path halving only moves arrows closer to the root), and roots no
+// longer change, so the walk still ends at the root.
+template <bool PLAIN = false>
 __device__ uint32_t g_find(uint64_t *gp, uint32_t x, uint64_t &root_rec, int &budget)
 {
-    uint64_t rec = g_load(&gp[x]);
+    auto load = [&](uint32_t i) -> uint64_t { return PLAIN ? gp[i] : g_load(&gp[i]); };
+    uint64_t rec = load(x);
     while (budget-- > 0) {
         const uint32_t p = (uint32_t)rec;
         if (p == x) break;
-        const uint64_t prec = g_load(&gp[p]);
+        const uint64_t prec = load(p);
         if ((uint32_t)prec == p) {
             x = p;
             rec = prec;
@@ -193,7 +199,7 @@ __device__ uint32_t g_find(uint64_t *gp, uint32_t x, uint64_t &root_rec, int &bu
         }
         g_min(&gp[x], prec);  // path halving
         x = (uint32_t)prec;
-        rec = g_load(&gp[x]);
+        rec = load(x);
     }
     root_rec = rec;
     return x;
@@ -227,10 +233,11 @@ __device__ void g_unite(uint64_t *gp, uint32_t a, uint32_t b, uint32_t *err)
     set_err(err, ERR_LOOP);
 }
 
+// the root of x once every union is done
 __device__ uint32_t g_root(uint64_t *gp, uint32_t x, uint64_t &root_rec, uint32_t *err)
 {
     int budget = GLOBAL_BUDGET;
-    const uint32_t r = g_find(gp, x, root_rec, budget);
+    const uint32_t r = g_find<true>(gp, x, root_rec, budget);
     if (budget <= 0) set_err(err, ERR_LOOP);
     return r;
 }
