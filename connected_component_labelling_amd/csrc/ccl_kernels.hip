@@ -1307,20 +1307,31 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     uint64_t *lead = sLead[wave];
     uint32_t *pre = sPre[wave];
     // every record of the tile is requested before any is used, so that their
-    // latencies overlap (the node and run-record areas of a tile always exist,
-    // so those are read unconditionally)
+    // latencies overlap
     const uint64_t mk = lane < TH ? w.runmask[t32 + lane] : 0ull;
     const uint64_t ld = (number && lane < TH) ? w.leadmask[t32 + lane] : 0ull;
     const uint32_t pr = (number && lane < TH) ? w.seg[t32 + lane] : 0u;
     uint64_t used[KMAX / 64];
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) used[word] = h.used[word];
+    // buffer loads bounded by the used seam slots and the run count: lanes past
+    // them read 0 without touching memory, and no branch splits the loads
+    const uint32_t nslots = used[2] ? 128u + 64u - (uint32_t)__builtin_clzll(used[2])
+                          : used[1] ? 64u + 64u - (uint32_t)__builtin_clzll(used[1])
+                          : used[0] ? 64u - (uint32_t)__builtin_clzll(used[0]) : 0u;
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(w.gp + (size_t)t * KMAX), (short)0, (int)(nslots * 8u), 0x00020000);
     uint32_t nv[KMAX / 64];
 #pragma unroll
-    for (int word = 0; word < KMAX / 64; ++word) nv[word] = (uint32_t)w.gp[(size_t)t * KMAX + word * 64 + lane];
+    for (int word = 0; word < KMAX / 64; ++word)
+        nv[word] = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(word * 64 + lane) * 8u, 0, 0);
+    const uint32_t nl = R < DLAB ? R : DLAB;
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void *)rinfo, (short)0,
+                                                                        (int)(nl * 4u), 0x00020000);
     uint32_t info[DLAB / 64];
 #pragma unroll
-    for (int j = 0; j < DLAB / 64; ++j) info[j] = rinfo[(uint32_t)lane + 64u * (uint32_t)j];
+    for (int j = 0; j < DLAB / 64; ++j)
+        info[j] = __builtin_amdgcn_raw_buffer_load_b32(rr, ((uint32_t)lane + 64u * (uint32_t)j) * 4u, 0, 0);
     if (number && lane < TH) {
         lead[lane] = ld;
         pre[lane] = pr;
@@ -1335,7 +1346,6 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         if (number) return 1u + pre[row] + popc64(lead[row] & mask_lt((int)col));
         return (uint32_t)((y0 + row) * W + x0 + col);
     };
-    const uint32_t nl = R < DLAB ? R : DLAB;
 #pragma unroll
     for (int j = 0; j < DLAB / 64; ++j) {
         const uint32_t r = (uint32_t)lane + 64u * (uint32_t)j;
