@@ -46,9 +46,11 @@ constexpr uint32_t ERR_LOOP = 1u;      // a find/union loop hit its safety bound
 struct TileHdr {
     uint32_t kind;      // bit 0: one-colour tile.  One-colour: bits 8..15 its seam
                         //   slot (255: none); bit 1: a top-edge request at column 0
-                        //   (8 neighbours), bit 2: that request goes up-left
+                        //   (8 neighbours), bit 2: that request goes up-left.
+                        //   Otherwise bits 8..15: 1 + the highest seam slot in use
+                        //   (0: none)
     uint32_t value;     // one-colour tile with a seam node: its pixels' value
-                        //   (written by the resolve pass)
+                        //   (written by the resolve pass); otherwise its runs
     uint32_t nruns;     // runs in the tile
     uint32_t ntop;      // seam requests along the top edge
     uint32_t nleft;     // seam requests along the left edge

@@ -708,9 +708,15 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             nleft = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, y, valid, up_ok, dn_ok,
                                         me, cur, hleft, cu, hu, cd, hd);
         }
-        // the header in one store (the one-colour fields stay 0)
+        // the header in one store (the one-colour fields stay 0); the first
+        // eight bytes also give the final write the bounds of its reads
+        const uint32_t nslots = s.Used[2] ? 128u + 64u - (uint32_t)__builtin_clzll(s.Used[2])
+                              : s.Used[1] ? 64u + 64u - (uint32_t)__builtin_clzll(s.Used[1])
+                              : s.Used[0] ? 64u - (uint32_t)__builtin_clzll(s.Used[0]) : 0u;
         if (lane < (int)(sizeof(TileHdr) / 4)) {
             uint32_t v = 0;
+            if (lane == 0) v = nslots << 8;
+            if (lane == 1) v = R;
             if (lane == 2) v = R;
             if (lane == 3) v = ntop;
             if (lane == 4) v = nleft;
@@ -1301,7 +1307,8 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         return;
     }
 
-    const uint32_t R = h.nruns;
+    const uint32_t R = uv.y;                 // a tile of several colours: its runs
+    const uint32_t nslots = (uv.x >> 8) & 0xFFu;  // 1 + its highest seam slot in use
     uint32_t *lab = sLab[wave];
     uint32_t *nodev = sNode[wave];
     uint64_t *lead = sLead[wave];
@@ -1314,11 +1321,9 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     uint64_t used[KMAX / 64];
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) used[word] = h.used[word];
-    // buffer loads bounded by the used seam slots and the run count: lanes past
-    // them read 0 without touching memory, and no branch splits the loads
-    const uint32_t nslots = used[2] ? 128u + 64u - (uint32_t)__builtin_clzll(used[2])
-                          : used[1] ? 64u + 64u - (uint32_t)__builtin_clzll(used[1])
-                          : used[0] ? 64u - (uint32_t)__builtin_clzll(used[0]) : 0u;
+    // buffer loads bounded by the used seam slots and the run count (from the
+    // header's first eight bytes): lanes past them read 0 without touching
+    // memory, and no branch splits the loads
     const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(w.gp + (size_t)t * KMAX), (short)0, (int)(nslots * 8u), 0x00020000);
     uint32_t nv[KMAX / 64];
