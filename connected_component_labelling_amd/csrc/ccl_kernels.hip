@@ -110,14 +110,9 @@ __device__ __forceinline__ void pixel_tile(uint32_t key, uint32_t b, const Geom 
 // Run slots are numbered y*64+k (k-th run of tile row y): reading order, so a
 // smaller slot is an earlier run.  Parents only point at smaller slots; a root
 // points at itself.  A root's word may also carry its seam slot in bits 16..23
-// (stored as 255 - slot, so the smallest slot wins an atomic maximum).  The
-// arrays are stored with the run index XOR-ed with the row so that the same
-// run index of all 32 rows (how the run phases access them) falls on
-// different LDS banks.
+// (stored as 255 - slot, so the smallest slot wins an atomic maximum).
 
 constexpr uint32_t PMASK = 0xFFFFu;
-
-__device__ __forceinline__ uint32_t sw(uint32_t slot) { return slot ^ ((slot >> 6) & 31u); }
 
 // Loops here need no step budget: every arrow points at a smaller slot, and
 // each loop below only moves to strictly smaller slots (a word that does not
@@ -126,7 +121,7 @@ __device__ __forceinline__ uint32_t sw(uint32_t slot) { return slot ^ ((slot >> 
 
 __device__ __forceinline__ uint32_t lds_parent(const uint32_t *P, uint32_t x)
 {
-    return __hip_atomic_load(&P[sw(x)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & PMASK;
+    return __hip_atomic_load(&P[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & PMASK;
 }
 
 // root of x, halving the path on the way (an arrow only moves closer to the root)
@@ -135,7 +130,7 @@ __device__ __forceinline__ uint32_t lds_find(uint32_t *P, uint32_t x)
     uint32_t p = lds_parent(P, x);
     while (p < x) {
         const uint32_t g = lds_parent(P, p);
-        if (g < p) atomicMin(&P[sw(x)], g);
+        if (g < p) atomicMin(&P[x], g);
         x = p;
         p = g;
     }
@@ -152,7 +147,7 @@ __device__ __forceinline__ void lds_unite(uint32_t *P, uint32_t a, uint32_t b)
         b = lds_find(P, b);
         if (a == b) return;
         const uint32_t lo = a < b ? a : b, hi = a ^ b ^ lo;
-        const uint32_t old = atomicMin(&P[sw(hi)], lo) & PMASK;
+        const uint32_t old = atomicMin(&P[hi], lo) & PMASK;
         if (old >= hi) return;  // hi was still a root: joined
         a = lo;
         b = old;
@@ -284,9 +279,9 @@ __device__ __forceinline__ uint32_t mbcnt(uint64_t m)
 constexpr int QCAP = 256;  // join queue of one wave (a ring; at most 63 + 128 pending)
 
 struct TileLds {
-    uint32_t P[TPX];               // parent of run slot (swizzled); roots: + seam slot
+    uint32_t P[TPX];               // parent of run slot; roots: + seam slot
     uint16_t Run[TPX];             // run slot of each run in reading order
-    uint8_t RX[TPX];               // start column of run slot (swizzled)
+    uint8_t RX[TPX];               // start column of run slot
     uint32_t Q[NWAVES][QCAP];      // queued joins: slot | other slot << 16
     uint64_t Mask[TH];             // run starts of each tile row
     uint64_t Lead[TH];             // start columns of the final roots of each row
@@ -576,8 +571,8 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             const uint32_t kx = mbcnt(mi);
             if (st) {
                 const uint32_t slot = (uint32_t)(y * 64) + kx;
-                s.RX[sw(slot)] = (uint8_t)lane;
-                s.P[sw(slot)] = slot;
+                s.RX[slot] = (uint8_t)lane;
+                s.P[slot] = slot;
             }
             // (the colour at column 0 is read with every lane active)
             const uint32_t cfirst = (uint32_t)__builtin_amdgcn_readfirstlane((int)cc);
@@ -642,13 +637,13 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
         const int cnt = (int)popc64(s.Mask[ry]);
         const uint32_t root = lds_find(s.P, slot);
-        if (root != slot) atomicMin(&s.P[sw(slot)], root);
+        if (root != slot) atomicMin(&s.P[slot], root);
         uint32_t es = 255;
         if (has_right && k == cnt - 1) es = 2 * TW + TH + ry;
         if (has_left && k == 0) es = 2 * TW + ry;
         if (has_bottom && ry == TH - 1) es = TW + k;
         if (has_top && ry == 0) es = k;
-        if (es != 255) atomicMax(&s.P[sw(root)], ((255u - es) << 16) | root);
+        if (es != 255) atomicMax(&s.P[root], ((255u - es) << 16) | root);
     }
     lds_barrier();
 
@@ -656,11 +651,11 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
     for (uint32_t r = tid; r < R; r += BLOCK) {
         const uint32_t slot = s.Run[r];
-        const uint32_t pv = s.P[sw(slot)];
+        const uint32_t pv = s.P[slot];
         const uint32_t root = pv & PMASK;
-        const uint32_t rv = root == slot ? pv : s.P[sw(root)];
+        const uint32_t rv = root == slot ? pv : s.P[root];
         const uint32_t es = 255u - (rv >> 16);
-        const uint32_t rcol = s.RX[sw(root)];
+        const uint32_t rcol = s.RX[root];
         rinfo[r] = es != 255u ? (INFO_BORDER | es) : ((root & ~63u) | rcol);
         if (root == slot) {
             if (es == 255u) {
@@ -677,8 +672,8 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
 
     // seam slot of the region of run slot `run`
     auto seam_of = [&](uint32_t run) -> uint32_t {
-        const uint32_t root = s.P[sw(run)] & PMASK;
-        return 255u - (s.P[sw(root)] >> 16);
+        const uint32_t root = s.P[run] & PMASK;
+        return 255u - (s.P[root] >> 16);
     };
     if (has_bottom && wave == NWAVES - 1 && lane_ok) {
         const uint64_t mb = s.Mask[TH - 1];
