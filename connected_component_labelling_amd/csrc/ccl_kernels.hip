@@ -119,17 +119,21 @@ constexpr uint32_t PMASK = 0xFFFFu;
 // point lower counts as a root), so it ends after at most TPX steps even on a
 // corrupted forest.
 
+// SEAM: roots may carry seam bits (after Connect), so they are masked off
+template <bool SEAM>
 __device__ __forceinline__ uint32_t lds_parent(const uint32_t *P, uint32_t x)
 {
-    return __hip_atomic_load(&P[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) & PMASK;
+    const uint32_t v = __hip_atomic_load(&P[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return SEAM ? v & PMASK : v;
 }
 
 // root of x, halving the path on the way (an arrow only moves closer to the root)
+template <bool SEAM>
 __device__ __forceinline__ uint32_t lds_find(uint32_t *P, uint32_t x)
 {
-    uint32_t p = lds_parent(P, x);
+    uint32_t p = lds_parent<SEAM>(P, x);
     while (p < x) {
-        const uint32_t g = lds_parent(P, p);
+        const uint32_t g = lds_parent<SEAM>(P, p);
         if (g < p) atomicMin(&P[x], g);
         x = p;
         p = g;
@@ -137,17 +141,18 @@ __device__ __forceinline__ uint32_t lds_find(uint32_t *P, uint32_t x)
     return x;
 }
 
-// join the trees of a and b: the larger root is re-pointed at the smaller; if
-// it stopped being a root meanwhile, join again from where it points now (the
-// larger of the two roots strictly decreases each time)
+// join the trees of a and b (during Connect: no seam bits yet): the larger
+// root is re-pointed at the smaller; if it stopped being a root meanwhile, join
+// again from where it points now (the larger of the two roots strictly
+// decreases each time)
 __device__ __forceinline__ void lds_unite(uint32_t *P, uint32_t a, uint32_t b)
 {
     for (;;) {
-        a = lds_find(P, a);
-        b = lds_find(P, b);
+        a = lds_find<false>(P, a);
+        b = lds_find<false>(P, b);
         if (a == b) return;
         const uint32_t lo = a < b ? a : b, hi = a ^ b ^ lo;
-        const uint32_t old = atomicMin(&P[hi], lo) & PMASK;
+        const uint32_t old = atomicMin(&P[hi], lo);
         if (old >= hi) return;  // hi was still a root: joined
         a = lo;
         b = old;
@@ -636,7 +641,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         const uint32_t slot = s.Run[r];
         const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
         const int cnt = (int)popc64(s.Mask[ry]);
-        const uint32_t root = lds_find(s.P, slot);
+        const uint32_t root = lds_find<true>(s.P, slot);
         if (root != slot) atomicMin(&s.P[slot], root);
         uint32_t es = 255;
         if (has_right && k == cnt - 1) es = 2 * TW + TH + ry;
