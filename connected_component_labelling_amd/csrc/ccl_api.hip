@@ -33,7 +33,7 @@ bool make_layout(int64_t B, int64_t H, int64_t W, Layout *L)
     g.nty = (int32_t)((H + TH - 1) / TH);
     g.tpi = (int64_t)g.ntx * g.nty;
     g.ntiles = B * g.tpi;
-    if (g.ntiles > (int64_t)(UINT32_MAX / KMAX)) return false;  // seam node ids are 32-bit
+    if (g.ntiles > MAX_TILES) return false;  // seam node ids are 32-bit
     g.nbands = B * g.nty;
     g.divW = make_fastdiv(W > 0 ? (uint32_t)W : 1u);
     g.divTpi = make_fastdiv(g.tpi > 0 ? (uint32_t)g.tpi : 1u);

@@ -28,6 +28,12 @@ constexpr int DLAB = 512;                   // run labels a final-write wave sta
 constexpr int SCAN_PT = 16;                 // row-scan entries per thread
 
 static_assert(KMAX <= 255, "seam slots are stored in one byte");
+
+// Seam node ids are (tile << 8) | slot.  Slots below KMAX are the regions of a
+// tile of several colours, whose records are gp[tile*KMAX + slot]; a one-colour
+// tile has one node, slot UNI_SLOT, whose record sits in its header.
+constexpr uint32_t UNI_SLOT = 255;
+constexpr int64_t MAX_TILES = int64_t(1) << 24;  // node ids are 32-bit
 static_assert(TH == 32 && TW == 64, "row masks are one wave64 ballot, tile rows are lanes");
 
 // Bit layout of a per-run record written by the tile pass.
@@ -44,8 +50,9 @@ constexpr uint32_t ERR_LOOP = 1u;      // a find/union loop hit its safety bound
 // else: its runs, masks, edge slots and seam requests follow from the fields
 // marked "one-colour" below.
 struct TileHdr {
-    uint32_t kind;      // bit 0: one-colour tile.  One-colour: bits 8..15 its seam
-                        //   slot (255: none); bit 1: a top-edge request at column 0
+    uint32_t kind;      // bit 0: one-colour tile.  One-colour: bits 8..15 the slot of
+                        //   its first open edge (255: none, so no seam node; its node
+                        //   is slot UNI_SLOT); bit 1: a top-edge request at column 0
                         //   (8 neighbours), bit 2: that request goes up-left.
                         //   Otherwise bits 8..15: 1 + the highest seam slot in use
                         //   (0: none)
@@ -55,7 +62,10 @@ struct TileHdr {
     uint32_t ntop;      // seam requests along the top edge
     uint32_t nleft;     // seam requests along the left edge
     uint32_t leftmask;  // one-colour: rows with a left-edge request
-    uint64_t used[3];   // seam slots in use (bit s of word s/64)
+    union {
+        uint64_t used[3];   // seam slots in use (bit s of word s/64)
+        uint64_t rec;       // one-colour: the record of its seam node
+    };
     uint64_t topmask;   // one-colour: columns with a top-edge request to the pixel
                         //   up-right (8 neighbours) or up (4 neighbours)
     uint32_t lead;      // one-colour: 1 if its first pixel leads a region (collapse pass)
@@ -96,8 +106,9 @@ struct Work {
     uint64_t *runmask;  // [ntiles*TH] run starts of each row segment
     uint64_t *leadmask; // [ntiles*TH] leaders of the image in each row segment
     uint32_t *runinfo;  // [ntiles*TPX] per-run records
-    uint64_t *gp;       // [ntiles*KMAX] seam nodes: (key of parent << 32) | parent node;
-                        //   after the resolve pass: the value of the node's pixels
+    uint64_t *gp;       // [ntiles*KMAX] seam node records of tiles of several colours:
+                        //   (key of parent << 32) | parent node; after the resolve
+                        //   pass: the value of the node's pixels
     uint8_t *bslot;     // [ntiles*TW] seam slot of each bottom-row pixel
     uint8_t *rslot;     // [ntiles*TH] seam slot of each right-column pixel
     uint16_t *req;      // [ntiles*REQMAX] seam requests

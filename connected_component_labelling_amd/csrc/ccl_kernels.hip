@@ -169,6 +169,12 @@ constexpr int GLOBAL_BUDGET = 1 << 22;
 // node id.  A root's record holds its own key and id, and the 64-bit minimum
 // orders records by key, so joins always keep the earlier pixel as leader.
 
+__device__ __forceinline__ uint64_t *node_rec(const Work &w, uint32_t node)
+{
+    const uint32_t t = node >> 8, slot = node & 0xFFu;
+    return slot == UNI_SLOT ? &w.hdr[t].rec : w.gp + (size_t)t * KMAX + slot;
+}
+
 __device__ __forceinline__ uint64_t g_load(const uint64_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -184,9 +190,12 @@ __device__ __forceinline__ uint64_t g_min(uint64_t *p, uint64_t v)
 // same root (path halving only moves arrows closer to the root), and roots no
 // longer change, so the walk still ends at the root.
 template <bool PLAIN = false>
-__device__ uint32_t g_find(uint64_t *gp, uint32_t x, uint64_t &root_rec, int &budget)
+__device__ uint32_t g_find(const Work &w, uint32_t x, uint64_t &root_rec, int &budget)
 {
-    auto load = [&](uint32_t i) -> uint64_t { return PLAIN ? gp[i] : g_load(&gp[i]); };
+    auto load = [&](uint32_t i) -> uint64_t {
+        const uint64_t *r = node_rec(w, i);
+        return PLAIN ? *r : g_load(r);
+    };
     uint64_t rec = load(x);
     while (budget-- > 0) {
         const uint32_t p = (uint32_t)rec;
@@ -197,7 +206,7 @@ __device__ uint32_t g_find(uint64_t *gp, uint32_t x, uint64_t &root_rec, int &bu
             rec = prec;
             break;
         }
-        g_min(&gp[x], prec);  // path halving
+        g_min(node_rec(w, x), prec);  // path halving
         x = (uint32_t)prec;
         rec = load(x);
     }
@@ -205,13 +214,13 @@ __device__ uint32_t g_find(uint64_t *gp, uint32_t x, uint64_t &root_rec, int &bu
     return x;
 }
 
-__device__ void g_unite(uint64_t *gp, uint32_t a, uint32_t b, uint32_t *err)
+__device__ void g_unite(const Work &w, uint32_t a, uint32_t b)
 {
     int budget = GLOBAL_BUDGET;
     while (budget > 0) {
         uint64_t ra_rec, rb_rec;
-        const uint32_t ra = g_find(gp, a, ra_rec, budget);
-        const uint32_t rb = g_find(gp, b, rb_rec, budget);
+        const uint32_t ra = g_find(w, a, ra_rec, budget);
+        const uint32_t rb = g_find(w, b, rb_rec, budget);
         if (budget <= 0) break;
         if (ra == rb) return;
         uint32_t lo = ra, hi = rb;
@@ -222,7 +231,7 @@ __device__ void g_unite(uint64_t *gp, uint32_t a, uint32_t b, uint32_t *err)
             lo_rec = rb_rec;
             hi_rec = ra_rec;
         }
-        const uint64_t old = g_min(&gp[hi], lo_rec);
+        const uint64_t old = g_min(node_rec(w, hi), lo_rec);
         if (old == hi_rec) return;  // hi was still a root: joined
         // hi had just been joined elsewhere (to old's node), and the minimum may
         // have moved it under lo: join lo with that node so neither join is lost
@@ -230,15 +239,15 @@ __device__ void g_unite(uint64_t *gp, uint32_t a, uint32_t b, uint32_t *err)
         b = (uint32_t)old;
         --budget;
     }
-    set_err(err, ERR_LOOP);
+    set_err(w.err, ERR_LOOP);
 }
 
 // the root of x once every union is done
-__device__ uint32_t g_root(uint64_t *gp, uint32_t x, uint64_t &root_rec, uint32_t *err)
+__device__ uint32_t g_root(const Work &w, uint32_t x, uint64_t &root_rec)
 {
     int budget = GLOBAL_BUDGET;
-    const uint32_t r = g_find<true>(gp, x, root_rec, budget);
-    if (budget <= 0) set_err(err, ERR_LOOP);
+    const uint32_t r = g_find<true>(w, x, root_rec, budget);
+    if (budget <= 0) set_err(w.err, ERR_LOOP);
     return r;
 }
 
@@ -490,16 +499,13 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             if (lane == 3) v = ntop;
             if (lane == 4) v = nleft;
             if (lane == 5) v = leftmask;
-            if (es != 255u && lane == 6 + (int)(es >> 5)) v = 1u << (es & 31u);
+            // its seam node's record: (key of its first pixel << 32) | node
+            if (es != 255u && lane == 6) v = (t << 8) | UNI_SLOT;
+            if (es != 255u && lane == 7) v = (uint32_t)y0 * (uint32_t)W + (uint32_t)x0;
             if (lane == 12) v = (uint32_t)topmask;
             if (lane == 13) v = (uint32_t)(topmask >> 32);
             if (lane == 14 && es == 255u) v = 1u;  // the whole image: its first pixel leads
             ((uint32_t *)&hdr)[lane] = v;
-        }
-        if (lane == 0 && es != 255u) {
-            const uint32_t node = t * KMAX + es;
-            const uint32_t key = (uint32_t)y0 * (uint32_t)W + (uint32_t)x0;
-            w.gp[node] = ((uint64_t)key << 32) | node;
         }
         return;
     }
@@ -666,9 +672,9 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             if (es == 255u) {
                 atomicOr((unsigned long long *)&s.Lead[slot >> 6], 1ull << rcol);
             } else {
-                const uint32_t node = t * KMAX + es;
+                const uint32_t node = (t << 8) | es;
                 const uint32_t key = (uint32_t)(y0 + (slot >> 6)) * (uint32_t)W + (uint32_t)x0 + rcol;
-                w.gp[node] = ((uint64_t)key << 32) | node;
+                w.gp[(size_t)t * KMAX + es] = ((uint64_t)key << 32) | node;
                 atomicOr((unsigned long long *)&s.Used[es >> 6], 1ull << (es & 63u));
             }
         }
@@ -818,14 +824,14 @@ __device__ __forceinline__ uint32_t select_bit64(uint64_t m, uint32_t r)
     return base + (uint32_t)__builtin_ctz(x);
 }
 
-// seam slot of the pixel at (row, col) of tile tn on its bottom row or right
-// column: a one-colour tile has a single slot, kept in its header
-__device__ __forceinline__ uint32_t edge_slot(const Work &w, uint32_t tn, const uint8_t *slots,
+// seam node of the pixel at (row, col) of tile tn on its bottom row or right
+// column: a one-colour tile has a single node
+__device__ __forceinline__ uint32_t edge_node(const Work &w, uint32_t tn, const uint8_t *slots,
                                               uint32_t idx)
 {
     const uint32_t kind = w.hdr[tn].kind;
     const uint32_t s8 = slots[idx];
-    return (kind & KIND_UNIFORM) ? (kind >> 8) & 0xFFu : s8;
+    return (tn << 8) | ((kind & KIND_UNIFORM) ? UNI_SLOT : s8);
 }
 
 __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w, int conn)
@@ -871,7 +877,7 @@ __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w, int c
                 uint32_t me;
                 int xp;
                 if (uni) {
-                    me = (kind >> 8) & 0xFFu;
+                    me = UNI_SLOT;
                     const uint32_t r0 = (kind & KIND_TOP0) ? 1u : 0u;
                     if (r < r0) {
                         xp = (kind & KIND_TOP0_UL) ? -1 : 0;
@@ -896,13 +902,13 @@ __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w, int c
                     tn = t - ntx;
                     col = xp;
                 }
-                a = t * KMAX + me;
-                bn = tn * KMAX + edge_slot(w, tn, w.bslot, (uint32_t)tn * TW + (uint32_t)col);
+                a = (t << 8) | me;
+                bn = edge_node(w, tn, w.bslot, (uint32_t)tn * TW + (uint32_t)col);
             } else {
                 // across the left edge: this tile's slot and the tile row
                 uint32_t me, row;
                 if (uni) {
-                    me = (kind >> 8) & 0xFFu;
+                    me = UNI_SLOT;
                     uint64_t lm = sLeftMask[j];
                     row = select_bit64(lm, r - sTop[j]);
                 } else {
@@ -911,12 +917,12 @@ __global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w, int c
                     row = (rq >> 8) & 0x7Fu;
                 }
                 const uint32_t tn = t - 1;
-                a = t * KMAX + me;
-                bn = tn * KMAX + edge_slot(w, tn, w.rslot, (uint32_t)tn * TH + row);
+                a = (t << 8) | me;
+                bn = edge_node(w, tn, w.rslot, (uint32_t)tn * TH + row);
             }
         }
         const uint32_t pa = __shfl_up(a, 1), pb = __shfl_up(bn, 1);
-        if (i < total && !(lane > 0 && pa == a && pb == bn)) g_unite(w.gp, a, bn, w.err);
+        if (i < total && !(lane > 0 && pa == a && pb == bn)) g_unite(w, a, bn);
     }
 }
 
@@ -966,13 +972,19 @@ __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, in
     const uint32_t tme = t0 + threadIdx.x;
     const bool mine = threadIdx.x < SEAM_TILES && tme < (uint32_t)g.ntiles;
     uint32_t n = 0;
+    bool uni = false;
+    if (mine) {
+        const uint32_t kind = w.hdr[tme].kind;
+        uni = (kind & KIND_UNIFORM) != 0;
+        if (uni) n = ((kind >> 8) & 0xFFu) != 255u ? 1u : 0u;  // its node, if it has an open edge
+    }
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) {
-        const uint64_t u = mine ? w.hdr[tme].used[word] : 0ull;
+        const uint64_t u = (mine && !uni) ? w.hdr[tme].used[word] : 0ull;
         if (threadIdx.x < SEAM_TILES) sUsed[threadIdx.x][word] = u;
         n += popc64(u);
     }
-    if (threadIdx.x < SEAM_TILES) sUni[threadIdx.x] = mine ? (uint8_t)(w.hdr[tme].kind & KIND_UNIFORM) : (uint8_t)0;
+    if (threadIdx.x < SEAM_TILES) sUni[threadIdx.x] = uni ? 1 : 0;
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
     if (threadIdx.x <= SEAM_TILES) sOff[threadIdx.x] = off;  // sOff[SEAM_TILES] = total
@@ -983,11 +995,11 @@ __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, in
         uint64_t u[KMAX / 64];
 #pragma unroll
         for (int word = 0; word < KMAX / 64; ++word) u[word] = sUsed[j][word];
-        const uint32_t node = t * KMAX + select_bit(u, i - sOff[j]);
+        const uint32_t node = (t << 8) | (sUni[j] ? UNI_SLOT : select_bit(u, i - sOff[j]));
         uint64_t rrec;
-        const uint32_t root = g_root(w.gp, node, rrec, w.err);
+        const uint32_t root = g_root(w, node, rrec);
         if (root != node) {
-            g_min(&w.gp[node], rrec);
+            g_min(node_rec(w, node), rrec);
         } else if (count_leaders && sUni[j]) {
             w.hdr[t].lead = 1u;  // a one-colour tile's only node: its first pixel leads
         } else if (count_leaders) {
@@ -1185,13 +1197,19 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
     const uint32_t tme = t0 + threadIdx.x;
     const bool mine = threadIdx.x < SEAM_TILES && tme < (uint32_t)g.ntiles;
     uint32_t n = 0;
+    bool uni = false;
+    if (mine) {
+        const uint32_t kind = w.hdr[tme].kind;
+        uni = (kind & KIND_UNIFORM) != 0;
+        if (uni) n = ((kind >> 8) & 0xFFu) != 255u ? 1u : 0u;  // its node, if it has an open edge
+    }
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) {
-        const uint64_t u = mine ? w.hdr[tme].used[word] : 0ull;
+        const uint64_t u = (mine && !uni) ? w.hdr[tme].used[word] : 0ull;
         if (threadIdx.x < SEAM_TILES) sUsed[threadIdx.x][word] = u;
         n += popc64(u);
     }
-    if (threadIdx.x < SEAM_TILES) sUni[threadIdx.x] = mine ? (uint8_t)(w.hdr[tme].kind & KIND_UNIFORM) : (uint8_t)0;
+    if (threadIdx.x < SEAM_TILES) sUni[threadIdx.x] = uni ? 1 : 0;
     uint32_t total;
     const uint32_t off = block_exclusive_scan(n, sWave, total);
     if (threadIdx.x <= SEAM_TILES) sOff[threadIdx.x] = off;  // sOff[SEAM_TILES] = total
@@ -1202,8 +1220,9 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
         uint64_t u[KMAX / 64];
 #pragma unroll
         for (int word = 0; word < KMAX / 64; ++word) u[word] = sUsed[j][word];
-        const uint32_t node = t * KMAX + select_bit(u, i - sOff[j]);
-        const uint32_t key = (uint32_t)(w.gp[node] >> 32);
+        const uint32_t node = (t << 8) | (sUni[j] ? UNI_SLOT : select_bit(u, i - sOff[j]));
+        uint64_t *rec = node_rec(w, node);
+        const uint32_t key = (uint32_t)(*rec >> 32);
         uint32_t val = key;
         if (number) {
             uint32_t tl, row, col;
@@ -1216,7 +1235,7 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
                 val = 1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)col));
             }
         }
-        w.gp[node] = val;
+        *rec = val;
         if (sUni[j]) w.hdr[t].value = val;  // a one-colour tile's only node
     }
 }
