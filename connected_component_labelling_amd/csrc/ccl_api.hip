@@ -57,7 +57,7 @@ bool make_layout(int64_t B, int64_t H, int64_t W, Layout *L)
     L->off_rslot = take(nt * TH);
     L->off_req = take(nt * REQMAX * sizeof(uint16_t));
     L->off_seg = take(nt * TH * sizeof(uint32_t));
-    L->off_rowoff = take((size_t)(B * H) * sizeof(uint32_t));
+    L->off_bandst = take((size_t)g.nbands * sizeof(uint64_t));
     L->total = off;
     return true;
 }
@@ -76,7 +76,7 @@ Work bind_work(const Layout &L, void *workspace)
     w.rslot = (uint8_t *)(base + L.off_rslot);
     w.req = (uint16_t *)(base + L.off_req);
     w.seg = (uint32_t *)(base + L.off_seg);
-    w.rowoff = (uint32_t *)(base + L.off_rowoff);
+    w.bandst = (uint64_t *)(base + L.off_bandst);
     return w;
 }
 

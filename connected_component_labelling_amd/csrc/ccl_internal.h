@@ -25,7 +25,6 @@ constexpr int REQ_TOP = 2 * TW;             // seam requests along the top edge
 constexpr int REQ_LEFT = 3 * TH;            // seam requests along the left edge
 constexpr int REQMAX = REQ_TOP + REQ_LEFT;
 constexpr int DLAB = 512;                   // run labels a final-write wave stages in LDS
-constexpr int SCAN_PT = 16;                 // row-scan entries per thread
 
 static_assert(KMAX <= 255, "seam slots are stored in one byte");
 
@@ -114,13 +113,13 @@ struct Work {
     uint16_t *req;      // [ntiles*REQMAX] seam requests
     uint32_t *seg;      // [ntiles*TH] leaders per row segment, then their exclusive
                         //   prefix in reading order (per image)
-    uint32_t *rowoff;   // [B*H] leaders per image row, then their exclusive prefix
+    uint64_t *bandst;   // [B*nty] scan status of each band of tiles: (value << 32) | state
 };
 
 struct Layout {
     Geom g;
     size_t off_err, off_hdr, off_runmask, off_leadmask, off_runinfo, off_gp, off_bslot,
-        off_rslot, off_req, off_seg, off_rowoff, total;
+        off_rslot, off_req, off_seg, off_bandst, total;
 };
 
 // Fills `L` for a batch shape; returns false if the shape is too large to

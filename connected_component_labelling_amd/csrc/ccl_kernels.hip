@@ -75,6 +75,16 @@ __device__ __forceinline__ void set_err(uint32_t *err, uint32_t bit)
     __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// clears the band status words before a scan (grid-stride over the threads
+// of the calling kernel)
+__device__ __forceinline__ void clear_bands(const Geom &g, const Work &w)
+{
+    const uint64_t n = (uint64_t)g.nbands;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (uint64_t)gridDim.x * blockDim.x)
+        w.bandst[i] = 0ull;
+}
+
 struct TilePos {
     uint32_t b, ty, tx;
     int64_t y0, x0;
@@ -185,11 +195,15 @@ __device__ __forceinline__ uint64_t g_min(uint64_t *p, uint64_t v)
     return __hip_atomic_fetch_min(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// PLAIN: cacheable loads, for passes that run after every union is done.  A
-// stale cached record then only shows an earlier parent on the path to the
-// same root (path halving only moves arrows closer to the root), and roots no
-// longer change, so the walk still ends at the root.
-template <bool PLAIN = false>
+// Finds read records with cacheable loads, which may be stale: a record only
+// ever moves to a parent with a smaller key in the same region, so a stale
+// record still names an ancestor, and a walk still ends (keys fall at every
+// step) at a node of the same region.  During the merge such a node may have
+// stopped being a root; the atomic minimum that links it returns its true
+// record, and the union goes on from there (g_unite).  Once every union is
+// done, roots no longer change and the walk ends at the root.
+// PLAIN = false reads with agent-scope atomic loads instead.
+template <bool PLAIN = true>
 __device__ uint32_t g_find(const Work &w, uint32_t x, uint64_t &root_rec, int &budget)
 {
     auto load = [&](uint32_t i) -> uint64_t {
@@ -964,6 +978,7 @@ __device__ __forceinline__ uint32_t select_bit(const uint64_t (&u)[KMAX / 64], u
 
 __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, int count_leaders)
 {
+    clear_bands(g, w);
     __shared__ uint32_t sOff[SEAM_TILES + 1];
     __shared__ uint64_t sUsed[SEAM_TILES][KMAX / 64];
     __shared__ uint8_t sUni[SEAM_TILES];
@@ -1014,10 +1029,13 @@ __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, in
 }
 
 // ------------------------------------------------------------------ scan
-// seg[] holds the leaders of each row segment (tile-major).  Per tile row of
-// tiles ("band"): sum each image row across the band's tiles; scan the row
-// sums of each image; then give every segment the leaders of all earlier rows
-// plus those of the earlier segments of its row.
+// seg[] holds the leaders of each row segment (tile-major).  One workgroup per
+// tile row of tiles ("band"), in one pass: sum each tile row across the
+// band's tiles, take the leaders of all earlier bands of the image from the
+// bands before it (decoupled look-back: each band publishes its own total at
+// once, and its inclusive prefix as soon as it knows it), then give every
+// segment the leaders of all earlier rows plus those of the earlier segments
+// of its row.
 
 // exclusive prefix over the workgroup of 32 values per thread (one per tile
 // row): vals[y] is replaced by its prefix; tot[y] receives the row's total
@@ -1051,87 +1069,27 @@ __device__ void block_scan_rows(uint32_t (&vals)[TH], uint32_t (&tot)[TH], uint3
     __syncthreads();
 }
 
+// Band status word: (value << 32) | state; state 1: value = the band's own
+// leaders, state 2: value = the leaders of the band and all earlier bands of
+// its image.  Cleared by the pass before the scan.
+constexpr uint32_t BAND_TOTAL = 1u, BAND_PREFIX = 2u;
+constexpr int LOOKBACK_BUDGET = 1 << 22;
+
+__device__ __forceinline__ void band_publish(uint64_t *p, uint32_t state, uint32_t value)
+{
+    __hip_atomic_store(p, ((uint64_t)value << 32) | state, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // With headers (the labelling path), a one-colour tile counts the leader bit
 // of its header in row 0 instead of its row-segment counts, which it never
-// wrote; ccl_number / ccl_count have no headers.
-__global__ __launch_bounds__(BLOCK) void scan_band_sum_kernel(Geom g, Work w, int use_hdr)
+// wrote; ccl_number / ccl_count have no headers.  apply = 0 only counts.
+__global__ __launch_bounds__(BLOCK) void scan_kernel(Geom g, Work w, int32_t *counts, int apply,
+                                                     int use_hdr)
 {
     __shared__ uint32_t sW[NWAVES * TH];
+    __shared__ uint32_t sPre;
     const uint32_t band = blockIdx.x;  // b * nty + ty
-    const uint32_t b = fast_div(band, g.divNty), ty = band - b * (uint32_t)g.nty;
-    const size_t t0 = (size_t)b * g.tpi + (size_t)ty * g.ntx;
-    uint32_t acc[TH], tot[TH];
-#pragma unroll
-    for (int y = 0; y < TH; ++y) acc[y] = 0;
-    for (uint32_t tx = threadIdx.x; tx < (uint32_t)g.ntx; tx += BLOCK) {
-        if (use_hdr && (w.hdr[t0 + tx].kind & KIND_UNIFORM)) {
-            acc[0] += w.hdr[t0 + tx].lead;
-            continue;
-        }
-        const uint4 *p = (const uint4 *)(w.seg + (t0 + tx) * TH);
-#pragma unroll
-        for (int q = 0; q < TH / 4; ++q) {
-            const uint4 v = p[q];
-            acc[4 * q] += v.x;
-            acc[4 * q + 1] += v.y;
-            acc[4 * q + 2] += v.z;
-            acc[4 * q + 3] += v.w;
-        }
-    }
-    block_scan_rows(acc, tot, sW);
-    const int64_t Y0 = (int64_t)ty * TH;
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int y = 0; y < TH; ++y)
-            if (Y0 + y < g.H) w.rowoff[(int64_t)b * g.H + Y0 + y] = tot[y];
-    }
-}
-
-__global__ __launch_bounds__(BLOCK) void scan_rows_kernel(Geom g, Work w, int32_t *counts)
-{
-    __shared__ uint32_t sWave[NWAVES];
-    const int64_t b = blockIdx.x;
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    uint32_t *ro = w.rowoff + b * g.H;
-    uint32_t carry = 0;
-    for (int64_t base = 0; base < g.H; base += (int64_t)BLOCK * SCAN_PT) {
-        uint32_t v[SCAN_PT], sum = 0;
-        const int64_t i0 = base + (int64_t)threadIdx.x * SCAN_PT;
-#pragma unroll
-        for (int j = 0; j < SCAN_PT; ++j) {
-            v[j] = i0 + j < g.H ? ro[i0 + j] : 0u;
-            sum += v[j];
-        }
-        uint32_t x = sum;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t y = __shfl_up(x, d);
-            if (lane >= d) x += y;
-        }
-        if (lane == 63) sWave[wave] = x;
-        __syncthreads();
-        uint32_t off = 0, tot = 0;
-#pragma unroll
-        for (int i = 0; i < NWAVES; ++i) {
-            off += i < wave ? sWave[i] : 0u;
-            tot += sWave[i];
-        }
-        __syncthreads();
-        uint32_t run = carry + off + x - sum;
-#pragma unroll
-        for (int j = 0; j < SCAN_PT; ++j) {
-            if (i0 + j < g.H) ro[i0 + j] = run;
-            run += v[j];
-        }
-        carry += tot;
-    }
-    if (threadIdx.x == 0 && counts) counts[b] = (int32_t)carry;
-}
-
-__global__ __launch_bounds__(BLOCK) void scan_band_apply_kernel(Geom g, Work w, int use_hdr)
-{
-    __shared__ uint32_t sW[NWAVES * TH];
-    const uint32_t band = blockIdx.x;
     const uint32_t b = fast_div(band, g.divNty), ty = band - b * (uint32_t)g.nty;
     const size_t t0 = (size_t)b * g.tpi + (size_t)ty * g.ntx;
     const uint32_t ntx = (uint32_t)g.ntx;
@@ -1157,10 +1115,45 @@ __global__ __launch_bounds__(BLOCK) void scan_band_apply_kernel(Geom g, Work w, 
         }
     }
     block_scan_rows(acc, tot, sW);
-    const int64_t Y0 = (int64_t)ty * TH;
+    uint32_t total = 0;
 #pragma unroll
-    for (int y = 0; y < TH; ++y)
-        acc[y] += Y0 + y < g.H ? w.rowoff[(int64_t)b * g.H + Y0 + y] : 0u;
+    for (int y = 0; y < TH; ++y) total += tot[y];
+
+    if (threadIdx.x == 0) {
+        uint64_t *st = w.bandst;
+        uint32_t pre = 0;
+        if (ty == 0) {
+            band_publish(&st[band], BAND_PREFIX, total);
+        } else {
+            band_publish(&st[band], BAND_TOTAL, total);
+            // earlier bands of this image, nearest first, until one has its prefix
+            int budget = LOOKBACK_BUDGET;
+            for (uint32_t k = band - 1;; --k) {
+                uint64_t v;
+                while (((v = __hip_atomic_load(&st[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) &
+                        0xFFFFFFFFull) == 0 && --budget > 0)
+                    __builtin_amdgcn_s_sleep(1);
+                if (budget <= 0) {  // an earlier band never reported: flag it, do not wait
+                    set_err(w.err, ERR_LOOP);
+                    break;
+                }
+                pre += (uint32_t)(v >> 32);
+                if ((uint32_t)v == BAND_PREFIX || k == band - ty) break;
+            }
+            band_publish(&st[band], BAND_PREFIX, pre + total);
+        }
+        sPre = pre;
+        if (counts && ty == (uint32_t)g.nty - 1) counts[b] = (int32_t)(pre + total);
+    }
+    __syncthreads();
+    if (!apply) return;
+    // leaders before each row of the band, then before this thread's tiles
+    uint32_t before = sPre;
+#pragma unroll
+    for (int y = 0; y < TH; ++y) {
+        acc[y] += before;
+        before += tot[y];
+    }
     for (uint32_t j = 0; j < G && tx0 + j < ntx; ++j) {
         if (use_hdr && (w.hdr[t0 + tx0 + j].kind & KIND_UNIFORM)) {
             TileHdr &h = w.hdr[t0 + tx0 + j];
@@ -1414,6 +1407,7 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
 __global__ __launch_bounds__(BLOCK) void leader_flag_kernel(const int32_t *leaders, Geom g,
                                                             Work w, int write_mask)
 {
+    clear_bands(g, w);
     const int lane = lane_id();
     const uint64_t nsegs = (uint64_t)g.ntiles * TH;
     const uint64_t nw = (uint64_t)gridDim.x * NWAVES;
@@ -1504,12 +1498,8 @@ void launch_seam_collapse(const Geom &g, const Work &w, int count_leaders, hipSt
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
                  hipStream_t s)
 {
-    hipLaunchKernelGGL(scan_band_sum_kernel, dim3((unsigned)g.nbands), dim3(BLOCK), 0, s, g, w,
-                       use_hdr);
-    hipLaunchKernelGGL(scan_rows_kernel, dim3((unsigned)g.B), dim3(BLOCK), 0, s, g, w, counts);
-    if (apply)
-        hipLaunchKernelGGL(scan_band_apply_kernel, dim3((unsigned)g.nbands), dim3(BLOCK), 0, s, g,
-                           w, use_hdr);
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)g.nbands), dim3(BLOCK), 0, s, g, w, counts,
+                       apply, use_hdr);
 }
 
 void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s)
