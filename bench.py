@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gpixels/s labelled+numbered (8-conn, multi-colour), 806-Mpix sheet; % HBM peak"
 HBM_PEAK_GBS = 8000.0
-STAGES = ["tile_label", "seam_merge", "seam_collapse", "number_scan", "final_write"]
+STAGES = ["tile_label", "seam_merge", "seam_roots", "number_scan", "final_write"]
 KERNEL_SOURCES = [os.path.join(ROOT, "connected_component_labelling_amd", "csrc", f)
                   for f in ("ccl_kernels.hip", "ccl_internal.h")]
 
@@ -117,7 +117,7 @@ def write_traffic(fetch_csv: str, write_csv: str, copy_mb: int, launch_pixels: i
     out = {"_calibration": {"copy_bytes": nbytes, "fetch_factor": round(f_fetch, 4),
                             "write_factor": round(f_write, 4)}}
     for kernel, short in [("tile_label_kernel", "tile_label"), ("final_write_kernel", "final_write"),
-                          ("seam_merge_kernel", "seam_merge"), ("seam_collapse_kernel", "seam_collapse"),
+                          ("seam_merge_kernel", "seam_merge"), ("seam_roots_kernel", "seam_roots"), ("scan_kernel", "scan"),
                           ("resolve_kernel", "resolve")]:
         fv = [v for name, v in fetch if kernel in name]
         wv = [v for name, v in write if kernel in name]

@@ -53,6 +53,7 @@ bool make_layout(int64_t B, int64_t H, int64_t W, Layout *L)
     L->off_leadmask = take(nt * TH * sizeof(uint64_t));
     L->off_runinfo = take(nt * TPX * sizeof(uint32_t));
     L->off_gp = take(nt * KMAX * sizeof(uint64_t));
+    L->off_nval = take(nt * KMAX * sizeof(uint32_t));
     L->off_bslot = take(nt * TW);
     L->off_rslot = take(nt * TH);
     L->off_req = take(nt * REQMAX * sizeof(uint16_t));
@@ -72,6 +73,7 @@ Work bind_work(const Layout &L, void *workspace)
     w.leadmask = (uint64_t *)(base + L.off_leadmask);
     w.runinfo = (uint32_t *)(base + L.off_runinfo);
     w.gp = (uint64_t *)(base + L.off_gp);
+    w.nval = (uint32_t *)(base + L.off_nval);
     w.bslot = (uint8_t *)(base + L.off_bslot);
     w.rslot = (uint8_t *)(base + L.off_rslot);
     w.req = (uint16_t *)(base + L.off_req);
@@ -133,7 +135,7 @@ static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int6
     mark(1);
     launch_seam(L.g, w, conn, s);
     mark(2);
-    launch_seam_collapse(L.g, w, need_scan ? 1 : 0, s);
+    if (need_scan) launch_seam_roots(L.g, w, s);
     mark(3);
     if (need_scan) launch_scan(L.g, w, counts, number, 1, s);
     launch_resolve(L.g, w, number, s);

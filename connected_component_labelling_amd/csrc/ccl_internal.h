@@ -106,8 +106,8 @@ struct Work {
     uint64_t *leadmask; // [ntiles*TH] leaders of the image in each row segment
     uint32_t *runinfo;  // [ntiles*TPX] per-run records
     uint64_t *gp;       // [ntiles*KMAX] seam node records of tiles of several colours:
-                        //   (key of parent << 32) | parent node; after the resolve
-                        //   pass: the value of the node's pixels
+                        //   (key of parent << 32) | parent node
+    uint32_t *nval;     // [ntiles*KMAX] the value of each such node's pixels (resolve)
     uint8_t *bslot;     // [ntiles*TW] seam slot of each bottom-row pixel
     uint8_t *rslot;     // [ntiles*TH] seam slot of each right-column pixel
     uint16_t *req;      // [ntiles*REQMAX] seam requests
@@ -118,7 +118,7 @@ struct Work {
 
 struct Layout {
     Geom g;
-    size_t off_err, off_hdr, off_runmask, off_leadmask, off_runinfo, off_gp, off_bslot,
+    size_t off_err, off_hdr, off_runmask, off_leadmask, off_runinfo, off_gp, off_nval, off_bslot,
         off_rslot, off_req, off_seg, off_bandst, total;
 };
 
@@ -131,7 +131,7 @@ Work bind_work(const Layout &L, void *workspace);
 void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, const Work &w,
                  hipStream_t s);
 void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s);
-void launch_seam_collapse(const Geom &g, const Work &w, int count_survivors, hipStream_t s);
+void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s);
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
                  hipStream_t s);
 void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s);

@@ -21,13 +21,15 @@
 //                         tile's top and left edges are written as requests.
 //   seam_merge_kernel     the requests: global atomic-min unions of seam nodes,
 //                         ordered by the reading-order index of each node's pixel.
-//   seam_collapse_kernel  every seam node points straight at its leader (ch.05
-//                         Collapse); leaders of the whole image are added to
-//                         their row segment's leader mask and count.
-//   scan kernels          exclusive prefix of leaders per 64-px row segment in
+//   seam_roots_kernel     seam nodes that are still roots lead regions of the
+//                         whole image: they are added to their row segment's
+//                         leader mask and count.
+//   scan_kernel           exclusive prefix of leaders per 64-px row segment in
 //                         reading order, per image (the prefix sum in the middle
-//                         of Number, ch.12 "The call").
-//   resolve_kernel        each seam node gets the value of its pixels.
+//                         of Number, ch.12 "The call"), one decoupled look-back
+//                         pass over bands of tiles.
+//   resolve_kernel        each seam node finds its leader (ch.05 Collapse) and
+//                         gets the value of its pixels.
 //   final_write_kernel    every pixel gets its leader or 1 + the leaders before
 //                         it (ch.08 idea 5), written once, coalesced.
 //
@@ -970,13 +972,14 @@ __device__ __forceinline__ uint32_t select_bit(const uint64_t (&u)[KMAX / 64], u
     return 0;
 }
 
-// ---------------------------------------------------------- seam collapse
-// Seam nodes of 256 consecutive tiles, dealt round-robin to the workgroup's
-// threads.  Each node points straight at its leader (Collapse); a node that is
-// its own leader leads a region of the whole image and joins its row
-// segment's leader mask and count.
+// ------------------------------------------------------------- seam roots
+// Seam nodes of SEAM_TILES consecutive tiles, dealt round-robin to the
+// workgroup's threads.  A node that is still a root after the merge leads a
+// region of the whole image: it joins its row segment's leader mask and count
+// (a one-colour tile's node sets the tile's leader bit).  This pass also
+// clears the band status words of the scan that follows.
 
-__global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, int count_leaders)
+__global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
 {
     clear_bands(g, w);
     __shared__ uint32_t sOff[SEAM_TILES + 1];
@@ -1011,15 +1014,15 @@ __global__ __launch_bounds__(BLOCK) void seam_collapse_kernel(Geom g, Work w, in
 #pragma unroll
         for (int word = 0; word < KMAX / 64; ++word) u[word] = sUsed[j][word];
         const uint32_t node = (t << 8) | (sUni[j] ? UNI_SLOT : select_bit(u, i - sOff[j]));
-        uint64_t rrec;
-        const uint32_t root = g_root(w, node, rrec);
-        if (root != node) {
-            g_min(node_rec(w, node), rrec);
-        } else if (count_leaders && sUni[j]) {
+        // every union is done: a node leads its region exactly when its record
+        // still names itself
+        const uint64_t rec = *node_rec(w, node);
+        if ((uint32_t)rec != node) continue;
+        if (sUni[j]) {
             w.hdr[t].lead = 1u;  // a one-colour tile's only node: its first pixel leads
-        } else if (count_leaders) {
+        } else {
             const TilePos tp = tile_pos(t, g);
-            const uint32_t key = (uint32_t)(rrec >> 32);
+            const uint32_t key = (uint32_t)(rec >> 32);
             const uint32_t Y = fast_div(key, g.divW);
             const uint32_t row = Y - (uint32_t)tp.y0, col = key - Y * (uint32_t)g.W - (uint32_t)tp.x0;
             atomicOr((unsigned long long *)&w.leadmask[(size_t)t * TH + row], 1ull << col);
@@ -1176,9 +1179,11 @@ __global__ __launch_bounds__(BLOCK) void scan_kernel(Geom g, Work w, int32_t *co
 }
 
 // ---------------------------------------------------------------- resolve
-// After the scan, each seam node gets the value its pixels will carry: its
-// leader's index, or 1 + the leaders before it.  Nodes of 256 consecutive
-// tiles are dealt round-robin to the workgroup's threads.
+// After the scan, each seam node finds its leader (Collapse) and gets the value
+// its pixels will carry: the leader's index, or 1 + the leaders before it.
+// Nodes of SEAM_TILES consecutive tiles are dealt round-robin to the
+// workgroup's threads.  The records are only read here, so the walks may run
+// side by side; the values go to nval (a one-colour tile: its header).
 
 __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int number)
 {
@@ -1214,8 +1219,9 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
 #pragma unroll
         for (int word = 0; word < KMAX / 64; ++word) u[word] = sUsed[j][word];
         const uint32_t node = (t << 8) | (sUni[j] ? UNI_SLOT : select_bit(u, i - sOff[j]));
-        uint64_t *rec = node_rec(w, node);
-        const uint32_t key = (uint32_t)(*rec >> 32);
+        uint64_t rrec;
+        g_root(w, node, rrec);
+        const uint32_t key = (uint32_t)(rrec >> 32);
         uint32_t val = key;
         if (number) {
             uint32_t tl, row, col;
@@ -1228,8 +1234,10 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
                 val = 1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)col));
             }
         }
-        *rec = val;
-        if (sUni[j]) w.hdr[t].value = val;  // a one-colour tile's only node
+        if (sUni[j])
+            w.hdr[t].value = val;  // a one-colour tile's only node
+        else
+            w.nval[(size_t)t * KMAX + (node & 0xFFu)] = val;
     }
 }
 
@@ -1337,11 +1345,11 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     // header's first eight bytes): lanes past them read 0 without touching
     // memory, and no branch splits the loads
     const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(w.gp + (size_t)t * KMAX), (short)0, (int)(nslots * 8u), 0x00020000);
+        (void *)(w.nval + (size_t)t * KMAX), (short)0, (int)(nslots * 4u), 0x00020000);
     uint32_t nv[KMAX / 64];
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word)
-        nv[word] = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(word * 64 + lane) * 8u, 0, 0);
+        nv[word] = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(word * 64 + lane) * 4u, 0, 0);
     const uint32_t nl = R < DLAB ? R : DLAB;
     const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void *)rinfo, (short)0,
                                                                         (int)(nl * 4u), 0x00020000);
@@ -1489,10 +1497,10 @@ void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s)
                        conn);
 }
 
-void launch_seam_collapse(const Geom &g, const Work &w, int count_leaders, hipStream_t s)
+void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s)
 {
-    hipLaunchKernelGGL(seam_collapse_kernel, dim3(grid_of(g.ntiles, SEAM_TILES)), dim3(BLOCK), 0, s,
-                       g, w, count_leaders);
+    hipLaunchKernelGGL(seam_roots_kernel, dim3(grid_of(g.ntiles, SEAM_TILES)), dim3(BLOCK), 0, s, g,
+                       w);
 }
 
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
