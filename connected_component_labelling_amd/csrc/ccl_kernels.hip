@@ -409,8 +409,9 @@ __device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geo
     const T *rows = im + (y0 + wave * RPW) * W + x0;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        if (FULL)
-            in.c[i] = (uint32_t)rows[i * W + lane];
+        if (FULL)  // a uniform base and a 32-bit offset per lane (rows of one image)
+            in.c[i] = (uint32_t)*(const T *)((const char *)rows +
+                                             (uint32_t)((i * (uint32_t)W + lane) * sizeof(T)));
         else
             in.c[i] = (lane_ok && wave * RPW + i < vh) ? (uint32_t)rows[i * W + lane] : 0u;
     }
@@ -425,7 +426,8 @@ __device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geo
     return in;
 }
 
-template <int CONN>
+// FULL: the tile lies wholly inside the image (every edge check folds away)
+template <int CONN, bool FULL>
 __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds &s, uint32_t t,
                                            const TilePos &tp, const TileIn &in)
 {
@@ -433,7 +435,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // the same in the whole wave
     const int64_t W = g.W;
     const int64_t y0 = tp.y0, x0 = tp.x0;
-    const int vh = tp.vh, vw = tp.vw;
+    const int vh = FULL ? TH : tp.vh, vw = FULL ? TW : tp.vw;
     const bool has_top = tp.ty > 0, has_left = tp.tx > 0;
     const bool has_bottom = y0 + TH < g.H, has_right = x0 + TW < g.W;
     const bool lane_ok = lane < vw;
@@ -445,7 +447,15 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     // ---- a tile of one colour needs none of the run phases: is every valid
     //      pixel equal to the tile's first?
     const uint32_t c00 = __builtin_amdgcn_readfirstlane(c[0]);
-    {
+    const bool full = FULL;
+    if (full) {
+        // every row is valid: fold the differences from c00 in each lane
+        uint32_t d = 0;
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) d |= c[i] ^ c00;
+        const bool bad = __ballot(d != 0) != 0;
+        if (lane == 0) s.Uni[wave] = bad ? 0ull : ((uint64_t)1u << 32) | c00;
+    } else {
         uint64_t bad = 0;
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
@@ -457,13 +467,17 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             s.Uni[wave] = ((uint64_t)(wave * RPW >= vh ? 2u : (bad == 0 ? 1u : 0u)) << 32) | c00;
     }
     lds_barrier();
-    // every wave reads the same words, so every wave takes the same branch
-    const uint32_t C = (uint32_t)s.Uni[0];  // the tile's first pixel (wave 0 always has rows)
-    bool uni = true;
-#pragma unroll
-    for (int q = 0; q < NWAVES; ++q) {
-        const uint32_t state = (uint32_t)(s.Uni[q] >> 32), cq = (uint32_t)s.Uni[q];
-        uni &= state == 2u || (state == 1u && cq == C);
+    // every wave reads the same words, so every wave takes the same branch:
+    // one colour if every wave with rows saw only the colour of the first pixel
+    bool uni;
+    {
+        const uint64_t u0 = s.Uni[0], u1 = s.Uni[1], u2 = s.Uni[2], u3 = s.Uni[3];
+        if (full) {
+            uni = (((u1 ^ u0) | (u2 ^ u0) | (u3 ^ u0)) == 0) && (u0 >> 32) == 1u;
+        } else {
+            auto same = [&](uint64_t u) { return u == u0 || (u >> 32) == 2u; };
+            uni = (u0 >> 32) == 1u && same(u1) && same(u2) && same(u3);
+        }
     }
     // the same for every thread: said so, the branch below stays uniform
     const bool uniform = __builtin_amdgcn_readfirstlane((int)uni) != 0;
@@ -478,6 +492,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         //      header, which holds everything the later passes need, and the
         //      region's seam node; the other waves are done.
         if (wave != 0) return;
+        const uint32_t C = c00;  // (wave 0) the colour of the tile's first pixel
         const uint32_t es = has_top ? 0u : has_bottom ? (uint32_t)TW
                           : has_left ? (uint32_t)(2 * TW) : has_right ? (uint32_t)(2 * TW + TH) : 255u;
         uint32_t kind = KIND_UNIFORM | (es << 8);
@@ -760,16 +775,17 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
 // XCD works through one contiguous range of tiles.  Tiles wholly inside the
 // image are loaded without edge checks.
 template <typename T, int CONN>
-__global__ __launch_bounds__(BLOCK) void tile_label_kernel(const T *__restrict__ img, Geom g,
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void tile_label_kernel(const T *__restrict__ img, Geom g,
                                                            Work w)
 {
     __shared__ TileLds s;
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t t = remap_tile(blockIdx.x, gridDim.x);
     const TilePos tp = tile_pos(t, g);
-    const TileIn in = (tp.vh == TH && tp.vw == TW) ? load_tile<T, true>(img, g, tp, wave, lane)
-                                                   : load_tile<T, false>(img, g, tp, wave, lane);
-    label_tile<CONN>(g, w, s, t, tp, in);
+    if (tp.vh == TH && tp.vw == TW)
+        label_tile<CONN, true>(g, w, s, t, tp, load_tile<T, true>(img, g, tp, wave, lane));
+    else
+        label_tile<CONN, false>(g, w, s, t, tp, load_tile<T, false>(img, g, tp, wave, lane));
 }
 
 // ------------------------------------------------------------ seam merge
