@@ -1002,6 +1002,14 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
     __shared__ uint64_t sUsed[SEAM_TILES][KMAX / 64];
     __shared__ uint8_t sUni[SEAM_TILES];
     __shared__ uint32_t sWave[NWAVES];
+    // the workgroup's leaders, gathered per tile row before they join the row
+    // segments' masks and counts (each tile belongs to this workgroup alone)
+    __shared__ uint64_t sLead[SEAM_TILES * TH];
+    __shared__ uint32_t sCnt[SEAM_TILES * TH];
+    for (int i = threadIdx.x; i < SEAM_TILES * TH; i += BLOCK) {
+        sLead[i] = 0ull;
+        sCnt[i] = 0u;
+    }
     const uint32_t t0 = blockIdx.x * SEAM_TILES;
     const uint32_t tme = t0 + threadIdx.x;
     const bool mine = threadIdx.x < SEAM_TILES && tme < (uint32_t)g.ntiles;
@@ -1041,9 +1049,18 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
             const uint32_t key = (uint32_t)(rec >> 32);
             const uint32_t Y = fast_div(key, g.divW);
             const uint32_t row = Y - (uint32_t)tp.y0, col = key - Y * (uint32_t)g.W - (uint32_t)tp.x0;
-            atomicOr((unsigned long long *)&w.leadmask[(size_t)t * TH + row], 1ull << col);
-            atomicAdd(&w.seg[(size_t)t * TH + row], 1u);
+            atomicOr((unsigned long long *)&sLead[j * TH + row], 1ull << col);
+            atomicAdd(&sCnt[j * TH + row], 1u);
         }
+    }
+    __syncthreads();
+    // the tile pass wrote these words (its own leaders); add the seam leaders
+    for (int i = threadIdx.x; i < SEAM_TILES * TH; i += BLOCK) {
+        const uint32_t cnt = sCnt[i];
+        if (cnt == 0) continue;
+        const size_t sg = (size_t)t0 * TH + i;
+        w.leadmask[sg] |= sLead[i];
+        w.seg[sg] += cnt;
     }
 }
 
