@@ -788,20 +788,14 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void
         label_tile<CONN, false>(g, w, s, t, tp, load_tile<T, false>(img, g, tp, wave, lane));
 }
 
-// ------------------------------------------------------------ seam merge
-// The seam passes give each workgroup NT consecutive tiles and deal their
-// items (requests or seam nodes) to its threads.  Collapse and resolve use few
-// tiles per workgroup (most threads hold one item, so that many find chains
-// are in flight at once); the merge uses more, since its unions of one large
-// region contend on the same roots when too many run at once.
+// ------------------------------------------------------------- seam passes
+// The seam passes give each workgroup a group of tiles and deal their items
+// (requests or seam nodes) to its threads: the per-tile counts are
+// prefix-summed and each thread takes every BLOCK-th item, so a tile with
+// many items does not serialise on one lane.  The roots and resolve passes use
+// few tiles per workgroup (most threads hold one item, so that many find
+// chains are in flight at once).
 constexpr int SEAM_TILES = 64;
-constexpr int MERGE_TILES = 256;
-
-// Each workgroup covers 256 consecutive tiles.  Their requests are counted,
-// prefix-summed and dealt round-robin to the 256 threads, so a tile with many
-// requests does not serialise on one lane.  Each request is resolved to the
-// seam node of the neighbour tile's pixel and the two nodes are joined; a
-// request equal to the one before it (held by the previous lane) is skipped.
 
 // exclusive prefix over the workgroup; `total` receives the sum of all values
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *sWave, uint32_t &total)
@@ -856,108 +850,6 @@ __device__ __forceinline__ uint32_t select_bit64(uint64_t m, uint32_t r)
     return base + (uint32_t)__builtin_ctz(x);
 }
 
-// seam node of the pixel at (row, col) of tile tn on its bottom row or right
-// column: a one-colour tile has a single node
-__device__ __forceinline__ uint32_t edge_node(const Work &w, uint32_t tn, const uint8_t *slots,
-                                              uint32_t idx)
-{
-    const uint32_t kind = w.hdr[tn].kind;
-    const uint32_t s8 = slots[idx];
-    return (tn << 8) | ((kind & KIND_UNIFORM) ? UNI_SLOT : s8);
-}
-
-__global__ __launch_bounds__(BLOCK) void seam_merge_kernel(Geom g, Work w, int conn)
-{
-    __shared__ uint32_t sOff[MERGE_TILES + 1];
-    __shared__ uint32_t sTop[MERGE_TILES];
-    __shared__ uint32_t sKind[MERGE_TILES];
-    __shared__ uint32_t sLeftMask[MERGE_TILES];
-    __shared__ uint64_t sTopMask[MERGE_TILES];
-    __shared__ uint32_t sWave[NWAVES];
-    const uint32_t t0 = blockIdx.x * MERGE_TILES;
-    const uint32_t tme = t0 + threadIdx.x;
-    const bool mine = threadIdx.x < MERGE_TILES && tme < (uint32_t)g.ntiles;
-    uint32_t ntop = 0, n = 0;
-    if (mine) {
-        const TileHdr &h = w.hdr[tme];
-        ntop = h.ntop;
-        n = ntop + h.nleft;
-        sKind[threadIdx.x] = h.kind;
-        sLeftMask[threadIdx.x] = h.leftmask;
-        sTopMask[threadIdx.x] = h.topmask;
-    }
-    uint32_t total;
-    const uint32_t off = block_exclusive_scan(n, sWave, total);
-    if (threadIdx.x <= MERGE_TILES) sOff[threadIdx.x] = off;  // sOff[MERGE_TILES] = total
-    if (threadIdx.x < MERGE_TILES) sTop[threadIdx.x] = ntop;
-    __syncthreads();
-    const uint32_t ntx = (uint32_t)g.ntx;
-    const int lane = lane_id();
-    const uint32_t rounds = (total + BLOCK - 1) / BLOCK;
-    for (uint32_t k = 0; k < rounds; ++k) {
-        const uint32_t i = k * BLOCK + threadIdx.x;
-        uint32_t a = 0xFFFFFFFFu, bn = 0xFFFFFFFFu;
-        if (i < total) {
-            const uint32_t j = item_tile<MERGE_TILES>(sOff, i);
-            const uint32_t t = t0 + j, r = i - sOff[j];
-            const uint32_t kind = sKind[j];
-            const bool uni = kind & KIND_UNIFORM;
-            const uint16_t *q = w.req + (size_t)t * REQMAX;
-            if (r < sTop[j]) {
-                // across the top edge: this tile's slot, and the column of the
-                // pixel above (-1 and TW: the tiles up-left and up-right)
-                uint32_t me;
-                int xp;
-                if (uni) {
-                    me = UNI_SLOT;
-                    const uint32_t r0 = (kind & KIND_TOP0) ? 1u : 0u;
-                    if (r < r0) {
-                        xp = (kind & KIND_TOP0_UL) ? -1 : 0;
-                    } else {
-                        const int x = (int)select_bit64(sTopMask[j], r - r0);
-                        xp = conn == 8 ? x + 1 : x;
-                    }
-                } else {
-                    const uint32_t rq = q[r];
-                    me = rq & 0xFFu;
-                    xp = (int)(rq >> 8) - 1;
-                }
-                uint32_t tn;
-                int col;
-                if (xp < 0) {
-                    tn = t - ntx - 1;
-                    col = TW - 1;
-                } else if (xp >= TW) {
-                    tn = t - ntx + 1;
-                    col = 0;
-                } else {
-                    tn = t - ntx;
-                    col = xp;
-                }
-                a = (t << 8) | me;
-                bn = edge_node(w, tn, w.bslot, (uint32_t)tn * TW + (uint32_t)col);
-            } else {
-                // across the left edge: this tile's slot and the tile row
-                uint32_t me, row;
-                if (uni) {
-                    me = UNI_SLOT;
-                    uint64_t lm = sLeftMask[j];
-                    row = select_bit64(lm, r - sTop[j]);
-                } else {
-                    const uint32_t rq = q[REQ_TOP + r - sTop[j]];
-                    me = rq & 0xFFu;
-                    row = (rq >> 8) & 0x7Fu;
-                }
-                const uint32_t tn = t - 1;
-                a = (t << 8) | me;
-                bn = edge_node(w, tn, w.rslot, (uint32_t)tn * TH + row);
-            }
-        }
-        const uint32_t pa = __shfl_up(a, 1), pb = __shfl_up(bn, 1);
-        if (i < total && !(lane > 0 && pa == a && pb == bn)) g_unite(w, a, bn);
-    }
-}
-
 // the r-th set bit (from 0) of the 192-bit mask u[0..2]
 __device__ __forceinline__ uint32_t select_bit(const uint64_t (&u)[KMAX / 64], uint32_t r)
 {
@@ -986,6 +878,349 @@ __device__ __forceinline__ uint32_t select_bit(const uint64_t (&u)[KMAX / 64], u
         base += 64;
     }
     return 0;
+}
+
+// ------------------------------------------------------------ seam merge
+// Two passes over blocks of MB x MB tiles of one image (thread j < BT of a
+// workgroup holds tile (j / MB, j % MB) of its block; all threads share the
+// block's nodes and requests).
+//   block_merge_kernel  joins the seam requests whose two tiles both lie in the
+//       block, with a union-find over the block's seam nodes in LDS (records
+//       ordered by key as in global memory, so the smallest key leads), then
+//       points every node's global record straight at its block root.  A block
+//       with more than NODE_CAP nodes joins those requests with global unions
+//       instead (one with more than REQ_CAP requests finds each request's tile
+//       by a search over the tiles' offsets rather than from a list).
+//   border_merge_kernel joins the requests that cross a block border, with
+//       global unions, which now start from nearly flat trees.
+// Within a block a long chain of joins (a row of blank tiles, each joined to
+// the one before it) costs LDS steps, not global round trips.
+constexpr int MB = 8;             // block side in tiles
+constexpr int BT = MB * MB;       // tiles per block
+constexpr int NODE_CAP = 3072;    // seam nodes of a block merged in LDS
+constexpr int REQ_CAP = 3072;     // seam requests of a block joined in LDS
+static_assert(BT <= BLOCK, "one thread per tile of a block");
+
+// the workgroup's block: the tile number of its first tile, and how many of
+// its tile rows / columns lie in the image
+struct BlockBase {
+    uint32_t t0;
+    int rows, cols;
+};
+
+__device__ __forceinline__ BlockBase block_base(const Geom &g)
+{
+    const uint32_t nbx = ((uint32_t)g.ntx + MB - 1) / MB, nby = ((uint32_t)g.nty + MB - 1) / MB;
+    const uint32_t per = nbx * nby, blk = blockIdx.x;
+    const uint32_t b = blk / per, r = blk - b * per, by = r / nbx, bx = r - by * nbx;
+    BlockBase bb;
+    bb.t0 = b * (uint32_t)g.tpi + by * MB * (uint32_t)g.ntx + bx * MB;
+    bb.rows = min(MB, g.nty - (int)(by * MB));
+    bb.cols = min(MB, g.ntx - (int)(bx * MB));
+    return bb;
+}
+
+struct BlockTile {
+    int ly, lx;   // place in the block
+    bool valid;   // inside the image
+    uint32_t t;   // tile number
+};
+
+__device__ __forceinline__ BlockTile block_tile(const Geom &g, const BlockBase &bb, int j)
+{
+    BlockTile p;
+    p.ly = j / MB;
+    p.lx = j % MB;
+    p.valid = j < BT && p.ly < bb.rows && p.lx < bb.cols;
+    p.t = bb.t0 + (uint32_t)p.ly * (uint32_t)g.ntx + (uint32_t)p.lx;
+    return p;
+}
+
+// One seam request of a tile: its own seam slot, the neighbour tile's offset
+// (dy = -1: a tile above; dx = -1, 0, +1) and the neighbour's pixel on its
+// bottom row (column) or right column (row).
+struct SeamReq {
+    uint32_t me;
+    int dy, dx;
+    uint32_t pos;
+};
+
+// request r of tile t (the first ntop cross its top edge, the rest its left
+// edge); a one-colour tile's requests come from its header masks
+__device__ __forceinline__ SeamReq decode_req(const Work &w, uint32_t t, uint32_t r, uint32_t kind,
+                                              uint32_t ntop, uint32_t leftmask, uint64_t topmask,
+                                              int conn)
+{
+    SeamReq q;
+    const bool uni = kind & KIND_UNIFORM;
+    const uint16_t *rq = w.req + (size_t)t * REQMAX;
+    if (r < ntop) {
+        // across the top edge: the column of the pixel above (-1 and TW: the
+        // tiles up-left and up-right)
+        int xp;
+        if (uni) {
+            q.me = UNI_SLOT;
+            const uint32_t r0 = (kind & KIND_TOP0) ? 1u : 0u;
+            if (r < r0) {
+                xp = (kind & KIND_TOP0_UL) ? -1 : 0;
+            } else {
+                const int x = (int)select_bit64(topmask, r - r0);
+                xp = conn == 8 ? x + 1 : x;
+            }
+        } else {
+            const uint32_t e = rq[r];
+            q.me = e & 0xFFu;
+            xp = (int)(e >> 8) - 1;
+        }
+        q.dy = -1;
+        q.dx = xp < 0 ? -1 : (xp >= TW ? 1 : 0);
+        q.pos = xp < 0 ? (uint32_t)(TW - 1) : (xp >= TW ? 0u : (uint32_t)xp);
+    } else {
+        // across the left edge: the tile row
+        if (uni) {
+            q.me = UNI_SLOT;
+            q.pos = select_bit64((uint64_t)leftmask, r - ntop);
+        } else {
+            const uint32_t e = rq[REQ_TOP + r - ntop];
+            q.me = e & 0xFFu;
+            q.pos = (e >> 8) & 0x7Fu;
+        }
+        q.dy = 0;
+        q.dx = -1;
+    }
+    return q;
+}
+
+// the neighbour's seam slot at the request's pixel (a one-colour tile has one)
+__device__ __forceinline__ uint32_t nb_slot(const Work &w, uint32_t tn, uint32_t nkind,
+                                            const SeamReq &q)
+{
+    if (nkind & KIND_UNIFORM) return UNI_SLOT;
+    return q.dy < 0 ? w.bslot[(size_t)tn * TW + q.pos] : w.rslot[(size_t)tn * TH + q.pos];
+}
+
+// LDS union-find over block nodes: record = (key << 32) | parent index; the
+// same rules as g_find / g_unite (every arrow points at a smaller key, so each
+// loop ends)
+__device__ __forceinline__ uint32_t l_find(uint64_t *R, uint32_t x, uint64_t &root_rec)
+{
+    auto load = [&](uint32_t i) {
+        return __hip_atomic_load(&R[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    uint64_t rec = load(x);
+    for (;;) {
+        const uint32_t p = (uint32_t)rec;
+        if (p == x) break;
+        const uint64_t prec = load(p);
+        if ((uint32_t)prec == p) {
+            x = p;
+            rec = prec;
+            break;
+        }
+        atomicMin((unsigned long long *)&R[x], prec);  // path halving
+        x = (uint32_t)prec;
+        rec = load(x);
+    }
+    root_rec = rec;
+    return x;
+}
+
+__device__ __forceinline__ void l_unite(uint64_t *R, uint32_t a, uint32_t b)
+{
+    for (;;) {
+        uint64_t ra_rec, rb_rec;
+        const uint32_t ra = l_find(R, a, ra_rec), rb = l_find(R, b, rb_rec);
+        if (ra == rb) return;
+        const bool a_lo = ra_rec < rb_rec;
+        const uint32_t lo = a_lo ? ra : rb, hi = a_lo ? rb : ra;
+        const uint64_t lo_rec = a_lo ? ra_rec : rb_rec, hi_rec = a_lo ? rb_rec : ra_rec;
+        const uint64_t old = atomicMin((unsigned long long *)&R[hi], lo_rec);
+        if (old == hi_rec) return;
+        a = lo;
+        b = (uint32_t)old;
+    }
+}
+
+__global__ __launch_bounds__(BLOCK) void block_merge_kernel(Geom g, Work w, int conn)
+{
+    __shared__ uint64_t sRec[NODE_CAP];      // node records: (key << 32) | parent
+    __shared__ uint16_t sNode[NODE_CAP];     // node -> (local tile << 8) | seam slot
+    __shared__ uint16_t sReq[REQ_CAP];       // request -> (local tile << 8) | its index
+    __shared__ uint64_t sUsed[BT][KMAX / 64];
+    __shared__ uint64_t sTop[BT];
+    __shared__ uint32_t sBase[BT], sOff[BT + 1];
+    __shared__ uint32_t sKind[BT], sNtop[BT], sLeft[BT];
+    __shared__ uint32_t sWave[NWAVES];
+    const int j = threadIdx.x;
+    const BlockBase bb = block_base(g);
+    const BlockTile me = block_tile(g, bb, j);
+    uint32_t nnodes = 0, nreq = 0, kind = 0;
+    uint64_t u[KMAX / 64] = {0ull, 0ull, 0ull};
+    {
+        uint64_t topmask = 0;
+        uint32_t ntop = 0, leftmask = 0;
+        if (me.valid) {
+            const TileHdr &h = w.hdr[me.t];
+            kind = h.kind;
+            ntop = h.ntop;
+            nreq = ntop + h.nleft;
+            if (kind & KIND_UNIFORM) {
+                nnodes = ((kind >> 8) & 0xFFu) != 255u ? 1u : 0u;  // if it has an open edge
+                topmask = h.topmask;
+                leftmask = h.leftmask;
+            } else {
+#pragma unroll
+                for (int word = 0; word < KMAX / 64; ++word) {
+                    u[word] = h.used[word];
+                    nnodes += popc64(u[word]);
+                }
+            }
+        }
+        if (j < BT) {
+#pragma unroll
+            for (int word = 0; word < KMAX / 64; ++word) sUsed[j][word] = u[word];
+            sTop[j] = topmask;
+            sKind[j] = kind;
+            sNtop[j] = ntop;
+            sLeft[j] = leftmask;
+        }
+    }
+    uint32_t total_nodes, total_req;
+    const uint32_t noff = block_exclusive_scan(nnodes, sWave, total_nodes);
+    const uint32_t roff = block_exclusive_scan(nreq, sWave, total_req);
+    const bool in_lds = total_nodes <= (uint32_t)NODE_CAP;  // the union-find fits in LDS
+    const bool listed = total_req <= (uint32_t)REQ_CAP;     // so does the request list
+    if (j <= BT) sOff[j] = roff;  // entry BT: the total
+    if (in_lds && j < BT) {
+        // each tile lists its nodes (slots in order)
+        sBase[j] = noff;
+        if (kind & KIND_UNIFORM) {
+            if (nnodes) sNode[noff] = (uint16_t)((j << 8) | UNI_SLOT);
+        } else {
+            uint32_t k = noff;
+#pragma unroll
+            for (int word = 0; word < KMAX / 64; ++word)
+                for (uint64_t m = u[word]; m; m &= m - 1ull)
+                    sNode[k++] = (uint16_t)((j << 8) | (uint32_t)(word * 64 + __builtin_ctzll(m)));
+        }
+    }
+    if (listed && j < BT)  // ... and its requests
+        for (uint32_t r = 0; r < nreq; ++r) sReq[roff + r] = (uint16_t)((j << 8) | r);
+    __syncthreads();
+    // local index of seam slot `slot` of local tile jj
+    auto local_node = [&](int jj, uint32_t slot) -> uint32_t {
+        if (slot == UNI_SLOT) return sBase[jj];
+        const uint32_t word = slot >> 6;
+        uint32_t below = popc64(sUsed[jj][word] & mask_lt((int)(slot & 63u)));
+        if (word > 0) below += popc64(sUsed[jj][0]);
+        if (word > 1) below += popc64(sUsed[jj][1]);
+        // (a slot in use always lands inside the tile's nodes; the bound only
+        // keeps a malformed request inside the table)
+        return min(sBase[jj] + below, total_nodes - 1u);
+    };
+    if (in_lds) {
+        // the nodes' own records, two per thread at a time (their loads overlap)
+        for (uint32_t i0 = j; i0 < total_nodes; i0 += 2 * BLOCK) {
+            const uint32_t i1 = i0 + BLOCK;
+            const uint32_t n0 = sNode[i0], n1 = i1 < total_nodes ? sNode[i1] : n0;
+            const uint64_t r0 = *node_rec(w, (block_tile(g, bb, (int)(n0 >> 8)).t << 8) | (n0 & 0xFFu));
+            const uint64_t r1 = *node_rec(w, (block_tile(g, bb, (int)(n1 >> 8)).t << 8) | (n1 & 0xFFu));
+            // before the merge every record is its node's own: (key << 32) | node
+            sRec[i0] = (r0 & 0xFFFFFFFF00000000ull) | i0;
+            if (i1 < total_nodes) sRec[i1] = (r1 & 0xFFFFFFFF00000000ull) | i1;
+        }
+        __syncthreads();
+    }
+    // the requests whose two tiles lie in the block
+    for (uint32_t i = j; i < total_req; i += BLOCK) {
+        uint32_t jj, r;
+        if (listed) {
+            const uint32_t e = sReq[i];
+            jj = e >> 8;
+            r = e & 0xFFu;
+        } else {  // without the lists: the tile holding item i, by its offsets
+            jj = item_tile<BT>(sOff, i);
+            r = i - sOff[jj];
+        }
+        const BlockTile tt = block_tile(g, bb, (int)jj);
+        const SeamReq q = decode_req(w, tt.t, r, sKind[jj], sNtop[jj], sLeft[jj], sTop[jj], conn);
+        const int nly = tt.ly + q.dy, nlx = tt.lx + q.dx;
+        if (nly < 0 || nlx < 0 || nlx >= MB) continue;  // crosses the block border
+        const int jn = nly * MB + nlx;
+        const uint32_t tn = block_tile(g, bb, jn).t;
+        const uint32_t ns = nb_slot(w, tn, sKind[jn], q);
+        if (in_lds)
+            l_unite(sRec, local_node((int)jj, q.me), local_node(jn, ns));
+        else
+            g_unite(w, (tt.t << 8) | q.me, (tn << 8) | ns);
+    }
+    if (!in_lds) return;
+    __syncthreads();
+    // every node's record names its block root (roots keep their own)
+    for (uint32_t i = j; i < total_nodes; i += BLOCK) {
+        uint64_t rrec;
+        const uint32_t r = l_find(sRec, i, rrec);
+        if (r == i) continue;
+        const uint32_t ni = sNode[i], nr = sNode[r];
+        const uint32_t gi = (block_tile(g, bb, (int)(ni >> 8)).t << 8) | (ni & 0xFFu);
+        const uint32_t gr = (block_tile(g, bb, (int)(nr >> 8)).t << 8) | (nr & 0xFFu);
+        *node_rec(w, gi) = (rrec & 0xFFFFFFFF00000000ull) | gr;
+    }
+}
+
+// The requests that cross a block border, from the tiles on the block's top
+// row and its left and right columns.
+__global__ __launch_bounds__(BLOCK) void border_merge_kernel(Geom g, Work w, int conn)
+{
+    __shared__ uint64_t sTop[BT];
+    __shared__ uint32_t sOff[BT + 1];
+    __shared__ uint32_t sKind[BT], sNtop[BT], sLeft[BT];
+    __shared__ uint32_t sWave[NWAVES];
+    const int j = threadIdx.x;
+    const BlockBase bb = block_base(g);
+    const BlockTile me = block_tile(g, bb, j);
+    const bool border = me.ly == 0 || me.lx == 0 || me.lx == MB - 1;
+    uint32_t nreq = 0, kind = 0, ntop = 0, leftmask = 0;
+    uint64_t topmask = 0;
+    if (me.valid && border) {
+        const TileHdr &h = w.hdr[me.t];
+        kind = h.kind;
+        ntop = h.ntop;
+        nreq = ntop + h.nleft;
+        topmask = h.topmask;
+        leftmask = h.leftmask;
+    }
+    if (j < BT) {
+        sTop[j] = topmask;
+        sKind[j] = kind;
+        sNtop[j] = ntop;
+        sLeft[j] = leftmask;
+    }
+    uint32_t total;
+    const uint32_t off = block_exclusive_scan(nreq, sWave, total);
+    if (j <= BT) sOff[j] = off;  // entry BT: the total
+    __syncthreads();
+    const int lane = lane_id();
+    const uint32_t rounds = (total + BLOCK - 1) / BLOCK;
+    for (uint32_t k = 0; k < rounds; ++k) {
+        const uint32_t i = k * BLOCK + (uint32_t)j;
+        uint32_t a = 0xFFFFFFFFu, bn = 0xFFFFFFFFu;
+        if (i < total) {
+            const uint32_t jj = item_tile<BT>(sOff, i);
+            const BlockTile tt = block_tile(g, bb, (int)jj);
+            const SeamReq q = decode_req(w, tt.t, i - sOff[jj], sKind[jj], sNtop[jj], sLeft[jj],
+                                         sTop[jj], conn);
+            const int nly = tt.ly + q.dy, nlx = tt.lx + q.dx;
+            if (nly < 0 || nlx < 0 || nlx >= MB) {
+                const uint32_t tn = tt.t - (q.dy < 0 ? (uint32_t)g.ntx : 0u) + (uint32_t)q.dx;
+                a = (tt.t << 8) | q.me;
+                bn = (tn << 8) | nb_slot(w, tn, w.hdr[tn].kind, q);
+            }
+        }
+        // a request equal to the one before it (held by the previous lane) is skipped
+        const uint32_t pa = __shfl_up(a, 1), pb = __shfl_up(bn, 1);
+        if (a != 0xFFFFFFFFu && !(lane > 0 && pa == a && pb == bn)) g_unite(w, a, bn);
+    }
 }
 
 // ------------------------------------------------------------- seam roots
@@ -1526,8 +1761,9 @@ void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, cons
 
 void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s)
 {
-    hipLaunchKernelGGL(seam_merge_kernel, dim3(grid_of(g.ntiles, MERGE_TILES)), dim3(BLOCK), 0, s, g, w,
-                       conn);
+    const int64_t blocks = g.B * ((g.nty + MB - 1) / MB) * ((g.ntx + MB - 1) / MB);
+    hipLaunchKernelGGL(block_merge_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, g, w, conn);
+    hipLaunchKernelGGL(border_merge_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, g, w, conn);
 }
 
 void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s)
