@@ -117,7 +117,8 @@ def write_traffic(fetch_csv: str, write_csv: str, copy_mb: int, launch_pixels: i
     out = {"_calibration": {"copy_bytes": nbytes, "fetch_factor": round(f_fetch, 4),
                             "write_factor": round(f_write, 4)}}
     for kernel, short in [("tile_label_kernel", "tile_label"), ("final_write_kernel", "final_write"),
-                          ("seam_merge_kernel", "seam_merge"), ("seam_roots_kernel", "seam_roots"), ("scan_kernel", "scan"),
+                          ("block_merge_kernel", "block_merge"), ("border_merge_kernel", "border_merge"),
+                          ("seam_roots_kernel", "seam_roots"), ("scan_kernel", "scan"),
                           ("resolve_kernel", "resolve")]:
         fv = [v for name, v in fetch if kernel in name]
         wv = [v for name, v in write if kernel in name]
