@@ -51,7 +51,7 @@ bool make_layout(int64_t B, int64_t H, int64_t W, Layout *L)
     L->off_hdr = take(nt * sizeof(TileHdr));
     L->off_runmask = take(nt * TH * sizeof(uint64_t));
     L->off_leadmask = take(nt * TH * sizeof(uint64_t));
-    L->off_runinfo = take(nt * TPX * sizeof(uint32_t));
+    L->off_runinfo = take(nt * TPX * sizeof(uint16_t));
     L->off_gp = take(nt * KMAX * sizeof(uint64_t));
     L->off_nval = take(nt * KMAX * sizeof(uint32_t));
     L->off_bslot = take(nt * TW);
@@ -71,7 +71,7 @@ Work bind_work(const Layout &L, void *workspace)
     w.hdr = (TileHdr *)(base + L.off_hdr);
     w.runmask = (uint64_t *)(base + L.off_runmask);
     w.leadmask = (uint64_t *)(base + L.off_leadmask);
-    w.runinfo = (uint32_t *)(base + L.off_runinfo);
+    w.runinfo = (uint16_t *)(base + L.off_runinfo);
     w.gp = (uint64_t *)(base + L.off_gp);
     w.nval = (uint32_t *)(base + L.off_nval);
     w.bslot = (uint8_t *)(base + L.off_bslot);

@@ -35,11 +35,11 @@ constexpr uint32_t UNI_SLOT = 255;
 constexpr int64_t MAX_TILES = int64_t(1) << 24;  // node ids are 32-bit
 static_assert(TH == 32 && TW == 64, "row masks are one wave64 ballot, tile rows are lanes");
 
-// Bit layout of a per-run record written by the tile pass.
-//   bit 31 set:   the run's region has seam node <slot> = bits 0..7
-//   bit 31 clear: the region lies inside the tile; bits 0..10 = row*64+col of
+// Bit layout of a per-run record (16 bits) written by the tile pass.
+//   bit 15 set:   the run's region has seam node <slot> = bits 0..7
+//   bit 15 clear: the region lies inside the tile; bits 0..10 = row*64+col of
 //                 its first pixel (its tile-local root)
-constexpr uint32_t INFO_BORDER = 0x80000000u;
+constexpr uint32_t INFO_BORDER = 0x8000u;
 
 // error word bits (first word of the workspace)
 constexpr uint32_t ERR_LOOP = 1u;      // a find/union loop hit its safety bound
@@ -104,7 +104,7 @@ struct Work {
     TileHdr *hdr;       // [ntiles]
     uint64_t *runmask;  // [ntiles*TH] run starts of each row segment
     uint64_t *leadmask; // [ntiles*TH] leaders of the image in each row segment
-    uint32_t *runinfo;  // [ntiles*TPX] per-run records
+    uint16_t *runinfo;  // [ntiles*TPX] per-run records
     uint64_t *gp;       // [ntiles*KMAX] seam node records of tiles of several colours:
                         //   (key of parent << 32) | parent node
     uint32_t *nval;     // [ntiles*KMAX] the value of each such node's pixels (resolve)

@@ -690,7 +690,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     lds_barrier();
 
     // ---- 4 Write: one thread per run; records in reading order
-    uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
+    uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
     for (uint32_t r = tid; r < R; r += BLOCK) {
         const uint32_t slot = s.Run[r];
         const uint32_t pv = s.P[slot];
@@ -698,7 +698,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         const uint32_t rv = root == slot ? pv : s.P[root];
         const uint32_t es = 255u - (rv >> 16);
         const uint32_t rcol = s.RX[root];
-        rinfo[r] = es != 255u ? (INFO_BORDER | es) : ((root & ~63u) | rcol);
+        rinfo[r] = (uint16_t)(es != 255u ? (INFO_BORDER | es) : ((root & ~63u) | rcol));
         if (root == slot) {
             if (es == 255u) {
                 atomicOr((unsigned long long *)&s.Lead[slot >> 6], 1ull << rcol);
@@ -1572,7 +1572,7 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     const TilePos tp = tile_pos(t, g);
     const int64_t y0 = tp.y0, x0 = tp.x0, W = g.W;
     const size_t t32 = (size_t)t * TH;
-    const uint32_t *rinfo = w.runinfo + (size_t)t * TPX;
+    const uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
     int32_t *o0 = out + (int64_t)tp.b * g.HW + y0 * W + x0;
     const bool lane_ok = lane < tp.vw;
     // 16-byte stores: whole tile rows whose starts are 16-byte aligned
@@ -1619,11 +1619,14 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     for (int word = 0; word < KMAX / 64; ++word)
         nv[word] = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(word * 64 + lane) * 4u, 0, 0);
     const uint32_t nl = R < DLAB ? R : DLAB;
-    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void *)rinfo, (short)0,
-                                                                        (int)(nl * 4u), 0x00020000);
-    uint32_t info[DLAB / 64];
+    // two 16-bit records per dword: lane l of load j holds runs 2(l + 64j) and
+    // 2(l + 64j) + 1 (the bound is rounded up to whole dwords; a run past nl is
+    // never used)
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)rinfo, (short)0, (int)((nl * 2u + 3u) & ~3u), 0x00020000);
+    uint32_t info[DLAB / 128];
 #pragma unroll
-    for (int j = 0; j < DLAB / 64; ++j)
+    for (int j = 0; j < DLAB / 128; ++j)
         info[j] = __builtin_amdgcn_raw_buffer_load_b32(rr, ((uint32_t)lane + 64u * (uint32_t)j) * 4u, 0, 0);
     if (number && lane < TH) {
         lead[lane] = ld;
@@ -1640,9 +1643,10 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         return (uint32_t)((y0 + row) * W + x0 + col);
     };
 #pragma unroll
-    for (int j = 0; j < DLAB / 64; ++j) {
-        const uint32_t r = (uint32_t)lane + 64u * (uint32_t)j;
-        if (r < nl) lab[r] = run_label(info[j]);
+    for (int j = 0; j < DLAB / 128; ++j) {
+        const uint32_t r = 2u * ((uint32_t)lane + 64u * (uint32_t)j);
+        if (r < nl) lab[r] = run_label(info[j] & 0xFFFFu);
+        if (r + 1u < nl) lab[r + 1u] = run_label(info[j] >> 16);
     }
     __syncwarp();
 
