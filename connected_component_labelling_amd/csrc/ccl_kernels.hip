@@ -774,10 +774,27 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
 // One workgroup per tile: workgroup v labels tile remap_tile(v), so that each
 // XCD works through one contiguous range of tiles.  Tiles wholly inside the
 // image are loaded without edge checks.
+//
+// The arguments come as one struct, read through the kernel-argument segment
+// pointer at each use.  Arguments named as parameters are all loaded into scalar
+// registers at kernel entry and stay live; this pass needs more scalar registers
+// than are left after that, and the spills (to vector lanes) cost vector
+// instructions in every tile, one-colour tiles included.
+template <typename T>
+struct TileArgs {
+    const T *img;
+    Geom g;
+    Work w;
+};
+
 template <typename T, int CONN>
-__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void tile_label_kernel(const T *__restrict__ img, Geom g,
-                                                           Work w)
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void tile_label_kernel(TileArgs<T> args)
 {
+    (void)args;  // read below through the segment pointer
+    const TileArgs<T> &a = *(const TileArgs<T> *)__builtin_amdgcn_kernarg_segment_ptr();
+    const T *__restrict__ img = a.img;
+    const Geom &g = a.g;
+    const Work &w = a.w;
     __shared__ TileLds s;
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t t = remap_tile(blockIdx.x, gridDim.x);
@@ -1749,17 +1766,17 @@ void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, cons
     if (dtype_bytes == 1) {
         if (conn == 8)
             hipLaunchKernelGGL((tile_label_kernel<uint8_t, 8>), grid, block, 0, s,
-                               (const uint8_t *)img, g, w);
+                               TileArgs<uint8_t>{(const uint8_t *)img, g, w});
         else
             hipLaunchKernelGGL((tile_label_kernel<uint8_t, 4>), grid, block, 0, s,
-                               (const uint8_t *)img, g, w);
+                               TileArgs<uint8_t>{(const uint8_t *)img, g, w});
     } else {
         if (conn == 8)
             hipLaunchKernelGGL((tile_label_kernel<uint32_t, 8>), grid, block, 0, s,
-                               (const uint32_t *)img, g, w);
+                               TileArgs<uint32_t>{(const uint32_t *)img, g, w});
         else
             hipLaunchKernelGGL((tile_label_kernel<uint32_t, 4>), grid, block, 0, s,
-                               (const uint32_t *)img, g, w);
+                               TileArgs<uint32_t>{(const uint32_t *)img, g, w});
     }
 }
 
