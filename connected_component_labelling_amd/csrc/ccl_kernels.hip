@@ -306,6 +306,39 @@ __device__ __forceinline__ uint32_t mbcnt(uint64_t m)
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// number of set bits of m below this lane, plus acc
+__device__ __forceinline__ uint32_t mbcnt_acc(uint64_t m, uint32_t acc)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, acc));
+}
+
+// this lane's bit of the wave-uniform mask m (no vector instruction: the mask
+// itself becomes the lane condition)
+__device__ __forceinline__ bool lane_bit(uint64_t m) { return __builtin_amdgcn_inverse_ballot_w64(m); }
+
+// a value that is the same in every lane, in scalar registers
+__device__ __forceinline__ uint64_t uniform64(uint64_t v)
+{
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+}
+
+// v with lane i < 8 replaced by the wave-uniform value x: one v_writelane
+// (the lane is an inline constant, as the scalar data already takes the one
+// scalar operand an instruction may read; i is a constant once unrolled)
+static_assert(RPW <= 8, "write_lane covers lanes 0..7");
+__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t x, int i)
+{
+#define CCL_WRITELANE(L) \
+    case L: asm("v_writelane_b32 %0, %1, " #L : "+v"(v) : "s"(x)); break;
+    switch (i) {
+        CCL_WRITELANE(0) CCL_WRITELANE(1) CCL_WRITELANE(2) CCL_WRITELANE(3)
+        CCL_WRITELANE(4) CCL_WRITELANE(5) CCL_WRITELANE(6) CCL_WRITELANE(7)
+    }
+#undef CCL_WRITELANE
+    return v;
+}
+
 constexpr int QCAP = 256;  // join queue of one wave (a ring; at most 63 + 128 pending)
 
 struct TileLds {
@@ -552,37 +585,36 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     //      the wave's own rows, which it has initialised itself.
     uint32_t *q = s.Q[wave];
     uint32_t head = 0, tail = 0;
-    // queue the joins of row y (colours cc, run starts st, starts before the
-    // lane kx) with the row above it (ca, sta, kxa)
-    auto join_rows = [&](int y, uint32_t cc, bool st, uint32_t kx, uint32_t ca, bool sta,
-                         uint32_t kxa) {
+    // lanes of the tile's columns
+    const uint64_t ok_m = FULL || vw >= TW ? ~0ull : (1ull << vw) - 1ull;
+    // Rows are handled as lane masks: a ballot per comparison, the logic on
+    // the masks in scalar registers.  me / mea: run slot of the lane's pixel in
+    // row y / in the row above (bit 0 of a row's start mask is always set, so
+    // the run of lane L is y*64 + the starts in lanes 1..L).
+    // queue the joins of row y (colours cc, run starts st_m) with the row above
+    // it (ca, sta_m)
+    auto join_rows = [&](uint32_t cc, uint64_t st_m, uint32_t me, uint32_t ca, uint64_t sta_m,
+                         uint32_t mea) {
         // lane shifts read other lanes, so they run with every lane active
         const uint32_t cl = from_left_lane(ca), cr = from_right_lane(ca);
-        const uint32_t sta1 = from_right_lane(sta ? 1u : 0u);
-        const bool u0 = lane_ok && ca == cc;
-        const bool um1 = lane_ok && lane > 0 && cl == cc;
-        bool ra = false, rb;
-        bool left_up;  // the join of rb goes to the up-left pixel's run
+        const uint64_t u0 = __ballot(ca == cc) & ok_m;
+        const uint64_t um1 = __ballot(cl == cc) & ok_m & ~1ull;
+        uint64_t ra = 0, rb, lu = 0;
         if (CONN == 8) {
-            const bool up1 = lane_ok && lane + 1 < vw && cr == cc;
-            ra = up1 && !u0;         // a run of the colour starts up-right
-            rb = st && (um1 || u0);  // the run's first pixel takes up-left or up
-            left_up = um1;
+            const uint64_t up1 = __ballot(cr == cc) & ok_m & (ok_m >> 1);
+            ra = up1 & ~u0;          // a run of the colour starts up-right
+            rb = st_m & (um1 | u0);  // the run's first pixel takes up-left or up
+            lu = um1 & sta_m;        // ... up-left, where the run above starts at the lane
         } else {
-            rb = u0 && (st || !um1);
-            left_up = false;
+            rb = u0 & (st_m | ~um1);
         }
-        const uint32_t me = (uint32_t)(y * 64) + kx + (st ? 1u : 0u) - 1u;  // run of this pixel
-        // run of the row above at column lane-1 (runs started before the lane),
-        // at the lane (plus its own start), at lane+1 (plus that start too)
-        const uint32_t above = (uint32_t)((y - 1) * 64) + kxa - 1u;
-        const uint32_t ab = above + (left_up ? 0u : (sta ? 1u : 0u));
-        const uint32_t ar = above + (sta ? 1u : 0u) + sta1;
-        const uint64_t bbm = __ballot(rb), bam = __ballot(ra);
-        if (rb) q[(tail + mbcnt(bbm)) & (QCAP - 1)] = me | (ab << 16);
-        tail += popc64(bbm);
-        if (ra) q[(tail + mbcnt(bam)) & (QCAP - 1)] = me | (ar << 16);
-        tail += popc64(bam);
+        // run of the row above at column lane-1 (if taken) or lane; at lane+1
+        const uint32_t ab = mea - (lane_bit(lu) ? 1u : 0u);
+        const uint32_t ar = mea + (lane_bit(sta_m >> 1) ? 1u : 0u);
+        if (lane_bit(rb)) q[mbcnt_acc(rb, tail) & (QCAP - 1)] = me | (ab << 16);
+        tail += popc64(rb);
+        if (lane_bit(ra)) q[mbcnt_acc(ra, tail) & (QCAP - 1)] = me | (ar << 16);
+        tail += popc64(ra);
     };
     // unite queued joins, 64 at a time while 64 wait (all: until none wait)
     auto drain = [&](bool all) {
@@ -599,41 +631,34 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     const int nrows = vh - wave * RPW < 0 ? 0 : (vh - wave * RPW < RPW ? vh - wave * RPW : RPW);
     const uint32_t c0 = c[0];
     {
-        uint32_t ca = 0, kxa = 0;
-        bool sta = false;
-        uint32_t mlo = 0, mhi = 0, col0 = 0;  // lane i collects row i's run starts, first colour
+        uint32_t ca = 0, mea = 0;
+        uint64_t sta = 0;
+        uint32_t mlo = 0, mhi = 0;  // lane i collects row i's run starts
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             if (i >= nrows) break;
             const int y = wave * RPW + i;
             const uint32_t cc = c[i];
-            const uint32_t left = from_left_lane(cc);
-            const bool st = lane_ok && (lane == 0 || left != cc);
-            const uint64_t mi = __ballot(st);
-            const uint32_t kx = mbcnt(mi);
-            if (st) {
-                const uint32_t slot = (uint32_t)(y * 64) + kx;
-                s.RX[slot] = (uint8_t)lane;
-                s.P[slot] = slot;
+            const uint64_t st_m = (__ballot(from_left_lane(cc) != cc) | 1ull) & ok_m;
+            const uint32_t me = mbcnt_acc(st_m >> 1, (uint32_t)(y * 64));
+            if (lane_bit(st_m)) {
+                s.RX[me] = (uint8_t)lane;
+                s.P[me] = me;
             }
-            // (the colour at column 0 is read with every lane active)
-            const uint32_t cfirst = (uint32_t)__builtin_amdgcn_readfirstlane((int)cc);
-            if (lane == i) {
-                mlo = (uint32_t)mi;
-                mhi = (uint32_t)(mi >> 32);
-                col0 = cfirst;
-            }
+            mlo = write_lane(mlo, (uint32_t)st_m, i);
+            mhi = write_lane(mhi, (uint32_t)(st_m >> 32), i);
             if (i > 0) {
-                join_rows(y, cc, st, kx, ca, sta, kxa);
+                join_rows(cc, st_m, me, ca, sta, mea);
                 drain(false);
             }
             ca = cc;
-            sta = st;
-            kxa = kx;
+            sta = st_m;
+            mea = me;
         }
-        if (lane < RPW) {  // rows past the image edge store 0
-            s.Mask[wave * RPW + lane] = lane < nrows ? ((uint64_t)mhi << 32) | mlo : 0ull;
-            s.ColC[wave * RPW + lane] = col0;
+        if (lane < RPW) s.Mask[wave * RPW + lane] = ((uint64_t)mhi << 32) | mlo;  // 0 past the image edge
+        if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < RPW; ++i) s.ColC[wave * RPW + i] = c[i];  // (0 past the image edge)
         }
         if (wave < NWAVES - 1) s.LastC[wave][lane] = ca;  // this wave's last row
     }
@@ -665,9 +690,9 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     // united
     if (wave > 0 && nrows > 0) {
         const int y = wave * RPW;
-        const uint64_t mi = s.Mask[y], ma = s.Mask[y - 1];
-        join_rows(y, c0, (mi >> lane) & 1ull, mbcnt(mi), s.LastC[wave - 1][lane],
-                  (ma >> lane) & 1ull, mbcnt(ma));
+        const uint64_t mi = uniform64(s.Mask[y]), ma = uniform64(s.Mask[y - 1]);
+        join_rows(c0, mi, mbcnt_acc(mi >> 1, (uint32_t)(y * 64)), s.LastC[wave - 1][lane], ma,
+                  mbcnt_acc(ma >> 1, (uint32_t)((y - 1) * 64)));
     }
     drain(true);
     lds_barrier();
