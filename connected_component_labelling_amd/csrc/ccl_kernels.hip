@@ -343,7 +343,9 @@ constexpr int QCAP = 256;  // join queue of one wave (a ring; at most 63 + 128 p
 
 struct TileLds {
     uint32_t P[TPX];               // parent of run slot; roots: + seam slot
-    uint16_t Run[TPX];             // run slot of each run in reading order
+    uint16_t Run[TPX];             // run slots in reading order, wave w's rows from
+                                   // entry w*RPW*TW on
+    uint32_t WaveRuns[NWAVES];     // runs in each wave's rows
     uint8_t RX[TPX];               // start column of run slot
     uint32_t Q[NWAVES][QCAP];      // queued joins: slot | other slot << 16
     uint64_t Mask[TH];             // run starts of each tile row
@@ -634,6 +636,8 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         uint32_t ca = 0, mea = 0;
         uint64_t sta = 0;
         uint32_t mlo = 0, mhi = 0;  // lane i collects row i's run starts
+        uint32_t nw = 0;            // runs in the wave's rows so far
+        uint16_t *run = s.Run + wave * (RPW * TW);
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             if (i >= nrows) break;
@@ -644,7 +648,9 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             if (lane_bit(st_m)) {
                 s.RX[me] = (uint8_t)lane;
                 s.P[me] = me;
+                run[nw + me - (uint32_t)(y * 64)] = (uint16_t)me;
             }
+            nw += popc64(st_m);
             mlo = write_lane(mlo, (uint32_t)st_m, i);
             mhi = write_lane(mhi, (uint32_t)(st_m >> 32), i);
             if (i > 0) {
@@ -661,29 +667,26 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             for (int i = 0; i < RPW; ++i) s.ColC[wave * RPW + i] = c[i];  // (0 past the image edge)
         }
         if (wave < NWAVES - 1) s.LastC[wave][lane] = ca;  // this wave's last row
+        if (lane == 0) s.WaveRuns[wave] = nw;
     }
     if (tid < KMAX / 64) s.Used[tid] = 0;
     if (tid < TH) s.Lead[tid] = 0;
     lds_barrier();
     if (tid < TH) w.runmask[t32 + tid] = s.Mask[tid];
 
-    // reading-order run index r -> run slot: rows hold cnt runs each, and the
-    // runs of row y follow those of the rows above it
-    uint32_t R;
-    {
-        uint32_t rc = lane < TH ? popc64(s.Mask[lane]) : 0u;
-        const uint32_t rown = rc;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t qv = __shfl_up(rc, d);
-            if (lane >= d) rc += qv;
-        }
-        R = __shfl(rc, TH - 1);
-        const int ry = tid & 31, rm = tid >> 5;
-        const uint32_t rb = __shfl(rc - rown, ry);
-        const int cnt = (int)popc64(s.Mask[ry]);
-        for (int k = rm; k < cnt; k += 8) s.Run[rb + k] = (uint16_t)(ry * 64 + k);
-    }
+    // runs of the tile; reading-order run r sits in wave w's part of Run when
+    // off[w] <= r < off[w+1] (the waves' rows follow each other)
+    const uint32_t n0 = __builtin_amdgcn_readfirstlane(s.WaveRuns[0]),
+                   n1 = __builtin_amdgcn_readfirstlane(s.WaveRuns[1]),
+                   n2 = __builtin_amdgcn_readfirstlane(s.WaveRuns[2]),
+                   n3 = __builtin_amdgcn_readfirstlane(s.WaveRuns[3]);
+    const uint32_t off1 = n0, off2 = off1 + n1, off3 = off2 + n2, R = off3 + n3;
+    auto run_slot = [&](uint32_t r) -> uint32_t {
+        const uint32_t i = r >= off3 ? r + (3u * RPW * TW - off3)
+                         : r >= off2 ? r + (2u * RPW * TW - off2)
+                         : r >= off1 ? r + (1u * RPW * TW - off1) : r;
+        return s.Run[i];
+    };
 
     // the wave's first row against the last row of the wave above; then every
     // join still queued (fewer than 64 from the wave's rows, and these) is
@@ -700,7 +703,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     // ---- 3 Collapse; runs on an edge shared with another tile offer their
     //      edge position as the region's seam slot (the smallest wins)
     for (uint32_t r = tid; r < R; r += BLOCK) {
-        const uint32_t slot = s.Run[r];
+        const uint32_t slot = run_slot(r);
         const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
         const int cnt = (int)popc64(s.Mask[ry]);
         const uint32_t root = lds_find<true>(s.P, slot);
@@ -717,7 +720,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     // ---- 4 Write: one thread per run; records in reading order
     uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
     for (uint32_t r = tid; r < R; r += BLOCK) {
-        const uint32_t slot = s.Run[r];
+        const uint32_t slot = run_slot(r);
         const uint32_t pv = s.P[slot];
         const uint32_t root = pv & PMASK;
         const uint32_t rv = root == slot ? pv : s.P[root];
