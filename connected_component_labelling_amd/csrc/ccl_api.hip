@@ -11,14 +11,17 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static FastDiv make_fastdiv(uint32_t d)
 {
-    // exact for every n < 2^31: with s = 32 + ceil(log2 d) and m = ceil(2^s / d),
-    // n*m < 2^64 and the rounding error n*(m*d - 2^s) < n*d < 2^s.
+    // exact for every n < 2^31: with l = ceil(log2 d), s = 31 + l and
+    // m = ceil(2^s / d), the error e = m*d - 2^s < d gives n*e < 2^31 * 2^l = 2^s,
+    // so floor(n*m / 2^s) = floor(n / d); and 2^(l-1) < d (or d = 1) keeps
+    // m < 2^32.
     FastDiv f;
     uint32_t l = 0;
     while (l < 32 && (1ull << l) < d) ++l;
-    f.s = 32 + l;
-    f.m = ((1ull << f.s) + d - 1) / d;
+    f.s = 31 + l;
+    f.m = (uint32_t)(((1ull << f.s) + d - 1) / d);
     f.d = d;
+    f.pad = 0;
     return f;
 }
 

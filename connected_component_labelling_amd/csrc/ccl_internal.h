@@ -77,11 +77,13 @@ constexpr uint32_t KIND_UNIFORM = 1u;
 constexpr uint32_t KIND_TOP0 = 2u;      // one-colour: top request at column 0
 constexpr uint32_t KIND_TOP0_UL = 4u;   // ... to the pixel up-left of column 0
 
-// exact unsigned division of n < 2^31 by a fixed d >= 1: q = (n*m) >> s
+// exact unsigned division of n < 2^31 by a fixed d >= 1: q = (n*m) >> s, with
+// a 32-bit m (one 32x32 multiply and a shift)
 struct FastDiv {
-    uint64_t m;
+    uint32_t m;
     uint32_t s;
     uint32_t d;
+    uint32_t pad;
 };
 
 struct Geom {

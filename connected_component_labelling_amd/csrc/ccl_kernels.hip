@@ -87,10 +87,11 @@ __device__ __forceinline__ void clear_bands(const Geom &g, const Work &w)
         w.bandst[i] = 0ull;
 }
 
+// Positions inside one image are 32-bit: an image holds fewer than 2^31 pixels.
 struct TilePos {
     uint32_t b, ty, tx;
-    int64_t y0, x0;
-    int vh, vw;
+    uint32_t y0, x0;  // first row and column
+    int vh, vw;       // rows and columns inside the image
 };
 
 __device__ __forceinline__ TilePos tile_pos(uint32_t t, const Geom &g)
@@ -100,10 +101,11 @@ __device__ __forceinline__ TilePos tile_pos(uint32_t t, const Geom &g)
     const uint32_t tt = t - p.b * (uint32_t)g.tpi;
     p.ty = fast_div(tt, g.divNtx);
     p.tx = tt - p.ty * (uint32_t)g.ntx;
-    p.y0 = (int64_t)p.ty * TH;
-    p.x0 = (int64_t)p.tx * TW;
-    p.vh = (int)(g.H - p.y0 < TH ? g.H - p.y0 : TH);
-    p.vw = (int)(g.W - p.x0 < TW ? g.W - p.x0 : TW);
+    p.y0 = p.ty * TH;
+    p.x0 = p.tx * TW;
+    const uint32_t rh = (uint32_t)g.H - p.y0, rw = (uint32_t)g.W - p.x0;
+    p.vh = (int)(rh < (uint32_t)TH ? rh : (uint32_t)TH);
+    p.vw = (int)(rw < (uint32_t)TW ? rw : (uint32_t)TW);
     return p;
 }
 
@@ -437,27 +439,27 @@ __device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geo
                                             const TilePos &tp, int wave, int lane)
 {
     TileIn in;
-    const int64_t W = g.W, y0 = tp.y0, x0 = tp.x0;
+    const uint32_t W = (uint32_t)g.W, y0 = tp.y0, x0 = tp.x0;
     const int vh = FULL ? TH : tp.vh, vw = FULL ? TW : tp.vw;
     const bool lane_ok = FULL || lane < vw;
-    const T *im = img + (int64_t)tp.b * g.HW;
-    const T *rows = im + (y0 + wave * RPW) * W + x0;
+    const T *im = img + (size_t)tp.b * (size_t)g.HW;
+    const T *rows = im + ((y0 + (uint32_t)(wave * RPW)) * W + x0);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        if (FULL)  // a uniform base and a 32-bit offset per lane (rows of one image)
+        if (FULL)  // a uniform base and a 32-bit byte offset per lane
             in.c[i] = (uint32_t)*(const T *)((const char *)rows +
-                                             (uint32_t)((i * (uint32_t)W + lane) * sizeof(T)));
+                                             (uint32_t)(((uint32_t)i * W + lane) * sizeof(T)));
         else
-            in.c[i] = (lane_ok && wave * RPW + i < vh) ? (uint32_t)rows[i * W + lane] : 0u;
+            in.c[i] = (lane_ok && wave * RPW + i < vh) ? (uint32_t)rows[(uint32_t)i * W + lane] : 0u;
     }
     in.hrow = in.hm1 = in.hp1 = in.hleft = 0;
     if (wave == 0 && tp.ty > 0) {
-        const T *up = im + (y0 - 1) * W + x0;
+        const T *up = im + ((y0 - 1u) * W + x0);
         if (lane_ok) in.hrow = up[lane];
         if (lane == 0 && tp.tx > 0) in.hm1 = up[-1];
         if (lane == TW - 1 && x0 + TW < W) in.hp1 = up[TW];
     }
-    if (wave == 0 && tp.tx > 0 && lane < vh) in.hleft = im[(y0 + lane) * W + x0 - 1];
+    if (wave == 0 && tp.tx > 0 && lane < vh) in.hleft = im[(y0 + (uint32_t)lane) * W + x0 - 1u];
     return in;
 }
 
@@ -468,11 +470,11 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
 {
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // the same in the whole wave
-    const int64_t W = g.W;
-    const int64_t y0 = tp.y0, x0 = tp.x0;
+    const uint32_t W = (uint32_t)g.W;
+    const uint32_t y0 = tp.y0, x0 = tp.x0;
     const int vh = FULL ? TH : tp.vh, vw = FULL ? TW : tp.vw;
     const bool has_top = tp.ty > 0, has_left = tp.tx > 0;
-    const bool has_bottom = y0 + TH < g.H, has_right = x0 + TW < g.W;
+    const bool has_bottom = y0 + TH < (uint32_t)g.H, has_right = x0 + TW < W;
     const bool lane_ok = lane < vw;
     uint32_t c[RPW];
 #pragma unroll
@@ -567,7 +569,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             if (lane == 5) v = leftmask;
             // its seam node's record: (key of its first pixel << 32) | node
             if (es != 255u && lane == 6) v = (t << 8) | UNI_SLOT;
-            if (es != 255u && lane == 7) v = (uint32_t)y0 * (uint32_t)W + (uint32_t)x0;
+            if (es != 255u && lane == 7) v = y0 * W + x0;
             if (lane == 12) v = (uint32_t)topmask;
             if (lane == 13) v = (uint32_t)(topmask >> 32);
             if (lane == 14 && es == 255u) v = 1u;  // the whole image: its first pixel leads
@@ -732,7 +734,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
                 atomicOr((unsigned long long *)&s.Lead[slot >> 6], 1ull << rcol);
             } else {
                 const uint32_t node = (t << 8) | es;
-                const uint32_t key = (uint32_t)(y0 + (slot >> 6)) * (uint32_t)W + (uint32_t)x0 + rcol;
+                const uint32_t key = (y0 + (slot >> 6)) * W + x0 + rcol;
                 w.gp[(size_t)t * KMAX + es] = ((uint64_t)key << 32) | node;
                 atomicOr((unsigned long long *)&s.Used[es >> 6], 1ull << (es & 63u));
             }
@@ -1328,7 +1330,7 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
             const TilePos tp = tile_pos(t, g);
             const uint32_t key = (uint32_t)(rec >> 32);
             const uint32_t Y = fast_div(key, g.divW);
-            const uint32_t row = Y - (uint32_t)tp.y0, col = key - Y * (uint32_t)g.W - (uint32_t)tp.x0;
+            const uint32_t row = Y - tp.y0, col = key - Y * (uint32_t)g.W - tp.x0;
             atomicOr((unsigned long long *)&sLead[j * TH + row], 1ull << col);
             atomicAdd(&sCnt[j * TH + row], 1u);
         }
