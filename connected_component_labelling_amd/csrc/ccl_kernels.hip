@@ -325,17 +325,20 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v)
            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
 }
 
-// v with lane i < 8 replaced by the wave-uniform value x: one v_writelane
+// v with lane i < 16 replaced by the wave-uniform value x: one v_writelane
 // (the lane is an inline constant, as the scalar data already takes the one
-// scalar operand an instruction may read; i is a constant once unrolled)
-static_assert(RPW <= 8, "write_lane covers lanes 0..7");
+// scalar operand an instruction may read; i is a constant once inlined)
+static_assert(RPW <= 16 && sizeof(TileHdr) / 4 <= 16, "write_lane covers lanes 0..15");
 __device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t x, int i)
 {
+    x = (uint32_t)__builtin_amdgcn_readfirstlane((int)x);  // into a scalar register
 #define CCL_WRITELANE(L) \
     case L: asm("v_writelane_b32 %0, %1, " #L : "+v"(v) : "s"(x)); break;
     switch (i) {
         CCL_WRITELANE(0) CCL_WRITELANE(1) CCL_WRITELANE(2) CCL_WRITELANE(3)
         CCL_WRITELANE(4) CCL_WRITELANE(5) CCL_WRITELANE(6) CCL_WRITELANE(7)
+        CCL_WRITELANE(8) CCL_WRITELANE(9) CCL_WRITELANE(10) CCL_WRITELANE(11)
+        CCL_WRITELANE(12) CCL_WRITELANE(13) CCL_WRITELANE(14) CCL_WRITELANE(15)
     }
 #undef CCL_WRITELANE
     return v;
@@ -359,71 +362,64 @@ struct TileLds {
 };
 
 // Seam requests across the top edge (wave 0, lane = column): tile row 0
-// (colour cur, run start flag st0, seam slot me of its region) against the row
-// above (hrow; hm1 / hp1 = the pixels diagonally beyond columns 0 and 63).
-// Returns the number written.
+// (colours cur, run starts st0, seam slot me of the lane's region) against the
+// row above (hrow; hm1 / hp1 = the pixels diagonally beyond columns 0 and 63,
+// held by lanes 0 and 63).  ok_m: lanes of the tile's columns.  The joins are
+// found as in Connect, one request per pair of touching stretches.  Returns
+// the number written.
 template <int CONN>
-__device__ __forceinline__ uint32_t top_requests(uint16_t *q, int lane, bool lane_ok, int vw,
-                                                 bool has_left, bool has_right, uint32_t cur,
-                                                 bool st0, uint32_t me, uint32_t hrow,
-                                                 uint32_t hm1, uint32_t hp1)
+__device__ __forceinline__ uint32_t top_requests(uint16_t *q, int lane, uint64_t ok_m, bool has_left,
+                                                 bool has_right, uint32_t cur, uint64_t st0,
+                                                 uint32_t me, uint32_t hrow, uint32_t hm1,
+                                                 uint32_t hp1)
 {
-    const uint64_t lt = mask_lt(lane);
-    const uint32_t hl = from_left_lane(hrow), hr = from_right_lane(hrow);
-    const bool vm1 = lane >= 1 || has_left;
-    const uint32_t cm1 = lane >= 1 ? hl : hm1;
-    const bool vp1 = lane < TW - 1 ? lane + 1 < vw : has_right;
-    const uint32_t cp1 = lane < TW - 1 ? hr : hp1;
-    const bool um1 = lane_ok && vm1 && cm1 == cur;
-    const bool u0 = lane_ok && hrow == cur;
-    const bool up1 = lane_ok && vp1 && cp1 == cur;
-    bool ra = false, rb = false;
-    int xb = lane;
+    const uint64_t u0 = __ballot(hrow == cur) & ok_m;
+    uint64_t um1 = __ballot(from_left_lane(hrow) == cur) & ok_m & ~1ull;
+    if (has_left) um1 |= __ballot(hm1 == cur) & 1ull;
+    uint64_t ra = 0, rb, lu = 0;
     if (CONN == 8) {
-        ra = up1 && !u0;  // up-right starts a stretch of the run's colour
-        if (st0) {        // a run's first pixel also takes up-left or up
-            if (um1) {
-                rb = true;
-                xb = lane - 1;
-            } else if (u0) {
-                rb = true;
-            }
-        }
+        uint64_t up1 = __ballot(from_right_lane(hrow) == cur) & ok_m & (ok_m >> 1);
+        if (has_right) up1 |= __ballot(hp1 == cur) & (1ull << 63);
+        ra = up1 & ~u0;         // up-right starts a stretch of the run's colour
+        rb = st0 & (um1 | u0);  // a run's first pixel also takes up-left or up
+        lu = um1;
     } else {
-        rb = u0 && (st0 || !um1);
+        rb = u0 & (st0 | ~um1);
     }
-    const uint64_t ba = __ballot(ra), bb = __ballot(rb);
-    const uint32_t pos = popc64(ba & lt) + popc64(bb & lt);
-    if (rb) q[pos] = (uint16_t)(me | ((uint32_t)(xb + 1) << 8));
-    if (ra) q[pos + (rb ? 1 : 0)] = (uint16_t)(me | ((uint32_t)(lane + 2) << 8));
-    return popc64(ba) + popc64(bb);
+    // requests in lane order, a lane's up-left/up one before its up-right one;
+    // the byte above the slot is 1 + the column of the pixel above
+    const uint32_t pos = mbcnt(ra) + mbcnt(rb);
+    if (lane_bit(rb)) q[pos] = (uint16_t)(me | ((uint32_t)(lane + (lane_bit(lu) ? 0 : 1)) << 8));
+    if (lane_bit(ra)) q[pos + (lane_bit(rb) ? 1u : 0u)] = (uint16_t)(me | ((uint32_t)(lane + 2) << 8));
+    return popc64(ra) + popc64(rb);
 }
 
-// Seam requests across the left edge (wave 1, lane = tile row y): the pixel at
-// column 0 (colour cur, seam slot me) against the halo column h; cu/hu and
-// cd/hd are the same two values for rows y-1 and y+1.
+// Seam requests across the left edge (wave 0, lane = tile row y): the pixel at
+// column 0 (colour cur, seam slot me) against the halo column h (the pixel left
+// of it); rows y-1 and y+1 are read from the neighbouring lanes.  vh_m: lanes
+// of the tile's rows.
 template <int CONN>
-__device__ __forceinline__ uint32_t left_requests(uint16_t *q, int y, bool valid, bool up_ok,
-                                                  bool dn_ok, uint32_t me, uint32_t cur,
-                                                  uint32_t h, uint32_t cu, uint32_t hu,
-                                                  uint32_t cd, uint32_t hd)
+__device__ __forceinline__ uint32_t left_requests(uint16_t *q, int y, uint64_t vh_m, uint32_t me,
+                                                  uint32_t cur, uint32_t h)
 {
-    const uint64_t lt = mask_lt(y);
-    const bool ml = valid && h == cur;
-    const bool up_same = up_ok && cu == cur;
+    const uint32_t hu = from_left_lane(h), hd = from_right_lane(h);
+    const uint32_t cu = from_left_lane(cur), cd = from_right_lane(cur);
+    const uint64_t up_ok = vh_m & ~1ull, dn_ok = vh_m & (vh_m >> 1);
+    const uint64_t ml = __ballot(h == cur) & vh_m;
+    const uint64_t up_same = __ballot(cu == cur) & up_ok;
+    const uint64_t hu_cur = __ballot(hu == cur);
     // skip a join that the row above (or this row's left join) already makes
-    const bool rl = ml && !(up_same && hu == cur);
-    bool rul = false, rdl = false;
+    const uint64_t rl = ml & ~(up_same & hu_cur);
+    uint64_t rul = 0, rdl = 0;
     if (CONN == 8) {
-        rul = up_ok && hu == cur && !up_same && !(ml && h == hu);
-        rdl = dn_ok && hd == cur && cd != cur && !(ml && h == hd);
+        rul = up_ok & hu_cur & ~up_same & ~(ml & __ballot(h == hu));
+        rdl = dn_ok & __ballot(hd == cur) & ~__ballot(cd == cur) & ~(ml & __ballot(h == hd));
     }
-    const uint64_t bu = __ballot(rul), bl = __ballot(rl), bdl = __ballot(rdl);
-    uint32_t pos = popc64(bu & lt) + popc64(bl & lt) + popc64(bdl & lt);
-    if (rul) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y - 1)) << 8));
-    if (rl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)y) << 8));
-    if (rdl) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y + 1)) << 8));
-    return popc64(bu) + popc64(bl) + popc64(bdl);
+    uint32_t pos = mbcnt(rul) + mbcnt(rl) + mbcnt(rdl);
+    if (lane_bit(rul)) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y - 1)) << 8));
+    if (lane_bit(rl)) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)y) << 8));
+    if (lane_bit(rdl)) q[pos] = (uint16_t)(me | ((0x80u | (uint32_t)(y + 1)) << 8));
+    return popc64(rul) + popc64(rl) + popc64(rdl);
 }
 
 // The pixels one wave reads for a tile: its 8 rows (lane = column) and, for
@@ -535,46 +531,53 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         uint32_t kind = KIND_UNIFORM | (es << 8);
         uint64_t topmask = 0;
         uint32_t ntop = 0, nleft = 0, leftmask = 0;
+        const uint64_t ok_m = FULL || vw >= TW ? ~0ull : (1ull << vw) - 1ull;
         if (has_top) {
-            // tile row 0 is one run of colour C against the row above
-            const uint32_t hl = from_left_lane(hrow), hr = from_right_lane(hrow);
-            const bool u0 = lane_ok && hrow == C;
-            const bool um1 = lane_ok && (lane >= 1 ? hl == C : (has_left && hm1 == C));
-            const bool up1 = lane_ok && (lane < TW - 1 ? (lane + 1 < vw && hr == C) : (has_right && hp1 == C));
+            // tile row 0 is one run of colour C against the row above: lane
+            // masks of the pixels up, up-left and up-right that have colour C
+            // (lanes 0 and 63 look at the halo corners hm1 and hp1)
+            const uint64_t u0 = __ballot(hrow == C) & ok_m;
+            uint64_t um1 = __ballot(from_left_lane(hrow) == C) & ok_m & ~1ull;
+            if (has_left) um1 |= __ballot(hm1 == C) & 1ull;
             if (CONN == 8) {
-                topmask = __ballot(up1 && !u0);  // a stretch of the colour starts up-right
-                const uint64_t l0 = __ballot(lane == 0 && (um1 || u0));
-                const uint64_t l0ul = __ballot(lane == 0 && um1);
-                if (l0) kind |= KIND_TOP0 | (l0ul ? KIND_TOP0_UL : 0u);
-                ntop = popc64(topmask) + (l0 ? 1u : 0u);
+                uint64_t up1 = __ballot(from_right_lane(hrow) == C) & ok_m & (ok_m >> 1);
+                if (has_right) up1 |= __ballot(hp1 == C) & (1ull << 63);
+                topmask = up1 & ~u0;  // a stretch of the colour starts up-right
+                if ((um1 | u0) & 1ull) {
+                    kind |= KIND_TOP0 | ((um1 & 1ull) ? KIND_TOP0_UL : 0u);
+                    ntop = 1;
+                }
+                ntop += popc64(topmask);
             } else {
-                topmask = __ballot(u0 && (lane == 0 || !um1));  // a stretch starts up
+                topmask = u0 & (~um1 | 1ull);  // a stretch starts up
                 ntop = popc64(topmask);
             }
         }
         if (has_left) {
             // lane y: column 0 of row y (colour C) against the halo column;
             // the row above already joins unless its halo pixel differs
-            const bool ml = lane < vh && hleft == C;
-            const uint32_t hu = from_left_lane(hleft);
-            leftmask = (uint32_t)__ballot(ml && (lane == 0 || hu != C));
+            const uint64_t ml = __ballot(hleft == C) & ((1ull << vh) - 1ull);
+            const uint64_t hu = __ballot(from_left_lane(hleft) == C);
+            leftmask = (uint32_t)(ml & (~hu | 1ull));
             nleft = (uint32_t)__popc(leftmask);
         }
-        if (lane < (int)(sizeof(TileHdr) / 4)) {
-            uint32_t v = 0;
-            if (lane == 0) v = kind;
-            if (lane == 2) v = (uint32_t)vh;
-            if (lane == 3) v = ntop;
-            if (lane == 4) v = nleft;
-            if (lane == 5) v = leftmask;
+        // the header: lane i holds word i
+        uint32_t v = 0;
+        v = write_lane(v, kind, 0);
+        v = write_lane(v, (uint32_t)vh, 2);
+        v = write_lane(v, ntop, 3);
+        v = write_lane(v, nleft, 4);
+        v = write_lane(v, leftmask, 5);
+        if (es != 255u) {
             // its seam node's record: (key of its first pixel << 32) | node
-            if (es != 255u && lane == 6) v = (t << 8) | UNI_SLOT;
-            if (es != 255u && lane == 7) v = y0 * W + x0;
-            if (lane == 12) v = (uint32_t)topmask;
-            if (lane == 13) v = (uint32_t)(topmask >> 32);
-            if (lane == 14 && es == 255u) v = 1u;  // the whole image: its first pixel leads
-            ((uint32_t *)&hdr)[lane] = v;
+            v = write_lane(v, (t << 8) | UNI_SLOT, 6);
+            v = write_lane(v, y0 * W + x0, 7);
+        } else {
+            v = write_lane(v, 1u, 14);  // the whole image: its first pixel leads
         }
+        v = write_lane(v, (uint32_t)topmask, 12);
+        v = write_lane(v, (uint32_t)(topmask >> 32), 13);
+        if (lane < (int)(sizeof(TileHdr) / 4)) ((uint32_t *)&hdr)[lane] = v;
         return;
     }
 
@@ -748,51 +751,38 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         return 255u - (s.P[root] >> 16);
     };
     if (has_bottom && wave == NWAVES - 1 && lane_ok) {
-        const uint64_t mb = s.Mask[TH - 1];
-        const bool st = (mb >> lane) & 1ull;
-        w.bslot[(size_t)t * TW + lane] =
-            (uint8_t)seam_of((uint32_t)((TH - 1) * 64) + mbcnt(mb) + (st ? 1u : 0u) - 1u);
+        const uint64_t mb = uniform64(s.Mask[TH - 1]);
+        w.bslot[(size_t)t * TW + lane] = (uint8_t)seam_of(mbcnt_acc(mb >> 1, (uint32_t)((TH - 1) * 64)));
     }
     if (has_right && wave == 2 && lane < vh)
         w.rslot[t32 + lane] = (uint8_t)seam_of((uint32_t)(lane * 64) + popc64(s.Mask[lane]) - 1u);
     if (wave == 0) {
         uint32_t ntop = 0, nleft = 0;
         if (has_top) {
-            const uint64_t m0 = s.Mask[0];
-            const bool st0 = (m0 >> lane) & 1ull;
-            const uint32_t me = lane_ok ? seam_of(mbcnt(m0) + (st0 ? 1u : 0u) - 1u) : 0u;
-            ntop = top_requests<CONN>(w.req + (size_t)t * REQMAX, lane, lane_ok, vw, has_left,
-                                      has_right, c[0], st0, me, hrow, hm1, hp1);
+            const uint64_t m0 = uniform64(s.Mask[0]);
+            const uint32_t me = seam_of(mbcnt_acc(m0 >> 1, 0u));  // region of the lane's run
+            ntop = top_requests<CONN>(w.req + (size_t)t * REQMAX, lane, ok_m, has_left, has_right,
+                                      c[0], m0, me, hrow, hm1, hp1);
         }
         if (has_left) {
-            const int y = lane;
-            const bool valid = y < vh;
-            const bool up_ok = valid && y >= 1, dn_ok = valid && y + 1 < vh;
-            const uint32_t hu = from_left_lane(hleft), hd = from_right_lane(hleft);
-            const uint32_t me = valid ? seam_of((uint32_t)(y * 64)) : 0u;
-            const uint32_t cur = valid ? s.ColC[y] : 0u;
-            const uint32_t cu = up_ok ? s.ColC[y - 1] : 0u, cd = dn_ok ? s.ColC[y + 1] : 0u;
-            nleft = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, y, valid, up_ok, dn_ok,
-                                        me, cur, hleft, cu, hu, cd, hd);
+            const bool valid = lane < vh;
+            const uint32_t me = valid ? seam_of((uint32_t)(lane * 64)) : 0u;
+            const uint32_t cur = valid ? s.ColC[lane] : 0u;
+            nleft = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, lane,
+                                        (1ull << vh) - 1ull, me, cur, hleft);
         }
         // the header in one store (the one-colour fields stay 0); the first
         // eight bytes also give the final write the bounds of its reads
         const uint32_t nslots = s.Used[2] ? 128u + 64u - (uint32_t)__builtin_clzll(s.Used[2])
                               : s.Used[1] ? 64u + 64u - (uint32_t)__builtin_clzll(s.Used[1])
                               : s.Used[0] ? 64u - (uint32_t)__builtin_clzll(s.Used[0]) : 0u;
-        if (lane < (int)(sizeof(TileHdr) / 4)) {
-            uint32_t v = 0;
-            if (lane == 0) v = nslots << 8;
-            if (lane == 1) v = R;
-            if (lane == 2) v = R;
-            if (lane == 3) v = ntop;
-            if (lane == 4) v = nleft;
-            if (lane >= 6 && lane < 12) {
-                const uint64_t u = s.Used[(lane - 6) >> 1];
-                v = (lane & 1) ? (uint32_t)(u >> 32) : (uint32_t)u;
-            }
-            ((uint32_t *)&hdr)[lane] = v;
-        }
+        uint32_t v = lane >= 6 && lane < 12 ? ((const uint32_t *)s.Used)[lane - 6] : 0u;
+        v = write_lane(v, nslots << 8, 0);
+        v = write_lane(v, R, 1);
+        v = write_lane(v, R, 2);
+        v = write_lane(v, ntop, 3);
+        v = write_lane(v, nleft, 4);
+        if (lane < (int)(sizeof(TileHdr) / 4)) ((uint32_t *)&hdr)[lane] = v;
     }
     if (tid >= 64 && tid < 64 + TH) {  // rows past the image edge store 0
         const uint64_t lead = s.Lead[tid - 64];
