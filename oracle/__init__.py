@@ -50,6 +50,9 @@ def _bind(lib):
         f = getattr(lib, name)
         f.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, i32p]
         f.restype = ctypes.c_int
+    lib.oracle_label_ignore.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int,
+                                        ctypes.c_uint32, i32p]
+    lib.oracle_label_ignore.restype = ctypes.c_int
     lib.oracle_number.argtypes = [i32p, i64, i64, i64, i32p, i32p]
     lib.oracle_number.restype = ctypes.c_int
     lib.oracle_count.argtypes = [i32p, i64, i64, i64, i32p]
@@ -89,20 +92,24 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def _run_labeller(fname: str, img, connectivity: int, lib):
+def _run_labeller(fname: str, img, connectivity: int, lib, *extra):
     img, dtype, squeeze = _as_batch(img)
     B, H, W = img.shape
     out = np.empty((B, H, W), dtype=np.int32)
     rc = getattr(lib, fname)(img.ctypes.data_as(ctypes.c_void_p), dtype, B, H, W,
-                             int(connectivity), _ptr(out))
+                             int(connectivity), *extra, _ptr(out))
     if rc != 0:
         raise ValueError(f"{fname} failed with status {rc}")
     return out[0] if squeeze else out
 
 
-def label(img, connectivity: int = 8, lib=None) -> np.ndarray:
-    """Leader image: each pixel's region minimum reading-order index (per image)."""
-    return _run_labeller("oracle_label", img, connectivity, lib or load())
+def label(img, connectivity: int = 8, lib=None, ignore=None) -> np.ndarray:
+    """Leader image: each pixel's region minimum reading-order index (per image).
+    With ``ignore`` set, pixels of that colour get -1 and join nothing."""
+    if ignore is None:
+        return _run_labeller("oracle_label", img, connectivity, lib or load())
+    return _run_labeller("oracle_label_ignore", img, connectivity, lib or load(),
+                         ctypes.c_uint32(int(ignore) & 0xFFFFFFFF))
 
 
 def connect(img, connectivity: int = 8, lib=None) -> np.ndarray:
@@ -116,7 +123,8 @@ def bfs_label(img, connectivity: int = 8, lib=None) -> np.ndarray:
 
 
 def number(leaders, lib=None):
-    """(labels 1..n in reading order, counts per image) from a leader image."""
+    """(labels 1..n in reading order, counts per image) from a leader image;
+    pixels with a negative leader (ignored) get 0 and are not counted."""
     lib = lib or load()
     L = np.ascontiguousarray(np.asarray(leaders, dtype=np.int32))
     squeeze = L.ndim == 2
@@ -145,9 +153,9 @@ def count(leaders, lib=None) -> np.ndarray:
     return counts
 
 
-def label_and_number(img, connectivity: int = 8, lib=None):
+def label_and_number(img, connectivity: int = 8, lib=None, ignore=None):
     """(leaders, labels, counts): the whole path as the oracle computes it."""
     lib = lib or load()
-    leaders = label(img, connectivity, lib)
+    leaders = label(img, connectivity, lib, ignore=ignore)
     labels, counts = number(leaders, lib)
     return leaders, labels, counts

@@ -27,6 +27,11 @@
  *     only moves arrows closer to the leader and never changes which pixel is
  *     the leader, so it is used here for speed only.
  *   same page, ch.08 idea 5: a leader's number is 1 + the leaders before it.
+ *   same page, ch.08 idea 4 "Ignore the paper": a caller may name one colour
+ *     to ignore; its pixels get label 0 in Start and take part in nothing
+ *     after (no joins, not counted, not numbered).  Leader images mark them
+ *     with -1 (label 0 in the "leader + 1" form that the TorchCC page uses,
+ *     where 0 is kept for background); numbers give them 0.
  *   "About Connected Components Labeling on GPU" (TorchCC blog), "The basic
  *     approach: Union-Find" and "Application in CCL": Find / Union / Compress,
  *     the raster two-pass scan over already-visited neighbours, 4- and
@@ -39,7 +44,7 @@
  * dtype: 1 = one byte per pixel, 4 = one 32-bit word per pixel; colours are
  * compared as whole stored values.
  *
- * Building with -DORACLE_MUTANT=k plants a deliberate mistake (k = 1..8) so the
+ * Building with -DORACLE_MUTANT=k plants a deliberate mistake (k = 1..10) so the
  * pin tests can show that they catch it.  The default build plants nothing.
  */
 #include <stdint.h>
@@ -93,17 +98,26 @@ static void join(int32_t *P, int32_t p, int32_t q)
 
 /* Stages Start and Connect for one image: P[i] = i, then the reading-order
  * scan joining each pixel with its earlier same-colour neighbours in the
- * order up-left, up, up-right, left (4-connectivity: up, left). */
+ * order up-left, up, up-right, left (4-connectivity: up, left).  With
+ * ign != 0, pixels of colour `ignv` are marked -1 in Start and skipped by
+ * Connect, as the pixel itself and as a neighbour. */
 static void start_connect(const void *img, int dtype, int64_t H, int64_t W,
-                          int conn, int32_t *P)
+                          int conn, int ign, uint32_t ignv, int32_t *P)
 {
     const int64_t n = H * W;
-    for (int64_t i = 0; i < n; ++i)
-        P[i] = (int32_t)i;                                   /* Start */
+    for (int64_t i = 0; i < n; ++i)                          /* Start */
+#if ORACLE_MUTANT == 10
+        P[i] = (int32_t)i;              /* mutant: the ignored colour is labelled */
+#else
+        P[i] = (ign && colour_at(img, dtype, i) == ignv) ? -1 : (int32_t)i;
+#endif
 
     for (int64_t r = 0; r < H; ++r) {
         for (int64_t c = 0; c < W; ++c) {
             const int64_t p = r * W + c;
+#if ORACLE_MUTANT != 10
+            if (P[p] < 0) continue;                          /* ignored: no joins */
+#endif
             const uint32_t v = colour_at(img, dtype, p);
             /* candidate earlier neighbours as (row offset, col offset) */
             int64_t dr[4], dc[4];
@@ -134,7 +148,7 @@ static void start_connect(const void *img, int dtype, int64_t H, int64_t W,
                 if (rr < 0 || cc < 0 || cc >= W) continue;   /* inside H x W only */
                 const int64_t q = rr * W + cc;
 #endif
-                if (colour_at(img, dtype, q) == v)
+                if (P[q] >= 0 && colour_at(img, dtype, q) == v)
                     join(P, (int32_t)p, (int32_t)q);
             }
         }
@@ -142,11 +156,13 @@ static void start_connect(const void *img, int dtype, int64_t H, int64_t W,
 }
 
 /* Stage Collapse: every pixel points straight at its leader.  P[i] <= i holds
- * for every pixel, so an ascending pass sees each parent's leader first. */
+ * for every pixel, so an ascending pass sees each parent's leader first.
+ * Ignored pixels (-1) stay -1. */
 static void collapse(int32_t *P, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
-        P[i] = (P[i] == i) ? (int32_t)i : P[P[i]];
+        if (P[i] >= 0)
+            P[i] = (P[i] == i) ? (int32_t)i : P[P[i]];
 }
 
 static int check_args(const void *img, int dtype, int64_t B, int64_t H,
@@ -169,8 +185,22 @@ int oracle_connect(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
     if (rc) return rc;
     const int64_t n = H * W;
     for (int64_t b = 0; b < B; ++b)
-        start_connect((const char *)img + b * n * dtype, dtype, H, W, conn,
+        start_connect((const char *)img + b * n * dtype, dtype, H, W, conn, 0, 0u,
                       parents + b * n);
+    return ORACLE_OK;
+}
+
+static int label_images(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
+                        int conn, int ign, uint32_t ignv, int32_t *leaders)
+{
+    int rc = check_args(img, dtype, B, H, W, conn, leaders);
+    if (rc) return rc;
+    const int64_t n = H * W;
+    for (int64_t b = 0; b < B; ++b) {
+        int32_t *P = leaders + b * n;
+        start_connect((const char *)img + b * n * dtype, dtype, H, W, conn, ign, ignv, P);
+        collapse(P, n);
+    }
     return ORACLE_OK;
 }
 
@@ -178,22 +208,26 @@ int oracle_connect(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
 int oracle_label(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
                  int conn, int32_t *leaders)
 {
-    int rc = check_args(img, dtype, B, H, W, conn, leaders);
-    if (rc) return rc;
-    const int64_t n = H * W;
-    for (int64_t b = 0; b < B; ++b) {
-        int32_t *P = leaders + b * n;
-        start_connect((const char *)img + b * n * dtype, dtype, H, W, conn, P);
-        collapse(P, n);
-    }
-    return ORACLE_OK;
+    return label_images(img, dtype, B, H, W, conn, 0, 0u, leaders);
+}
+
+/* Leaders with one colour ignored ("Accountable AI starts at the pixel",
+ * ch.08 idea 4): pixels of colour `ignore` (compared as the whole stored
+ * value; a CCL_U8-style byte image has no colour above 255, so such a value
+ * ignores nothing) get -1 and join nothing; every other pixel gets its
+ * region's leader. */
+int oracle_label_ignore(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
+                        int conn, uint32_t ignore, int32_t *leaders)
+{
+    return label_images(img, dtype, B, H, W, conn, 1, ignore, leaders);
 }
 
 /* Stage Number: leaders become 1, 2, 3, ... in reading order and every pixel
  * takes its leader's number.  Requires a valid leader image (leader[p] <= p,
  * leader[leader[p]] == leader[p]): a leader comes no later than its pixels, so
- * its number is already written when a later pixel copies it.  counts may be
- * NULL. */
+ * its number is already written when a later pixel copies it.  A pixel whose
+ * leader is negative (an ignored pixel) gets 0 and is not counted.  counts
+ * may be NULL. */
 int oracle_number(const int32_t *leaders, int64_t B, int64_t H, int64_t W,
                   int32_t *labels, int32_t *counts)
 {
@@ -205,7 +239,12 @@ int oracle_number(const int32_t *leaders, int64_t B, int64_t H, int64_t W,
         int32_t *out = labels + b * n;
         int32_t k = 0;
         for (int64_t i = 0; i < n; ++i) {
-            if (L[i] == i) {
+            if (L[i] < 0) {
+#if ORACLE_MUTANT == 9
+                k += 1;                           /* mutant: ignored pixels counted */
+#endif
+                out[i] = 0;
+            } else if (L[i] == i) {
 #if ORACLE_MUTANT == 5
                 out[i] = k;                       /* mutant: numbers start at 0 */
                 k += 1;

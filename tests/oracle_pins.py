@@ -9,6 +9,10 @@ given disagrees with:
     approach of "Accountable AI starts at the pixel", ch.03), compared as a
     partition,
   * closed forms (uniform, checkerboard, stripes, single rows, no row wrap),
+  * for one ignored colour ("Accountable AI starts at the pixel", ch.08 idea 4):
+    the TorchCC page's "Find(i) + 1, 0 for background" labels, a flood fill
+    that skips the ignored colour, and scipy's binary labelling (whose numbers
+    are 1..n in reading order, 0 for background) value for value,
   * invariants of the definition (leader = region minimum, equal-colour
     neighbours share a leader, numbers are 1..n in reading order).
 
@@ -40,6 +44,29 @@ def py_bfs(img: np.ndarray, conn: int) -> np.ndarray:
         if lab[r0, c0] >= 0:
             continue
         v = img[r0, c0]
+        lab[r0, c0] = s
+        q = deque([(r0, c0)])
+        while q:
+            r, c = q.popleft()
+            for dr, dc in nb:
+                rr, cc = r + dr, c + dc
+                if 0 <= rr < H and 0 <= cc < W and lab[rr, cc] < 0 and img[rr, cc] == v:
+                    lab[rr, cc] = s
+                    q.append((rr, cc))
+    return lab.astype(np.int32)
+
+
+def py_bfs_ignore(img: np.ndarray, conn: int, ignore) -> np.ndarray:
+    """Pure-Python flood fill in which pixels of colour ``ignore`` are -1 and are
+    neither seeds nor reached (independent of the C file)."""
+    H, W = img.shape
+    nb = NB8 if conn == 8 else NB4
+    lab = np.full((H, W), -1, dtype=np.int64)
+    for s in range(H * W):
+        r0, c0 = divmod(s, W)
+        v = img[r0, c0]
+        if lab[r0, c0] >= 0 or v == ignore:
+            continue
         lab[r0, c0] = s
         q = deque([(r0, c0)])
         while q:
@@ -141,6 +168,22 @@ def pin_torchcc_6x6(lib):
     assert blocks == [r * 6 + c for r in range(0, 6, 2) for c in range(0, 6, 2)]
 
 
+def pin_ignore_torchcc_4x4(lib):
+    """The page's labels with background ignored are leader + 1, 0 for background."""
+    fx = fixtures.load("torchcc_4x4_binary.txt")
+    img = fx["input"].astype(np.uint8)
+    L = oracle.label(img, 8, lib=lib, ignore=0)
+    expect = np.array([int(v) for v in fx["labels_find_plus_one_raster"].split()])
+    assert np.array_equal(L.reshape(-1) + 1, expect), "leader + 1 must be the page's labels"
+    labels, counts = oracle.number(L, lib=lib)
+    assert counts[0] == 3, "three components besides the background"
+    # numbers keep 0 for background and count the components 1, 2, 3 in reading order
+    assert np.array_equal(labels.reshape(-1), [1, 1, 0, 1, 0, 0, 1, 0, 0, 0, 0, 0, 2, 0, 0, 3])
+    # u32 view of the same picture: the whole stored value is compared
+    L32 = oracle.label(img.astype(np.uint32) * 0x01010101, 8, lib=lib, ignore=0)
+    assert np.array_equal(L32, L)
+
+
 # ---------------------------------------------------------------------------
 # independent labellers
 
@@ -208,6 +251,81 @@ def pin_scipy_partition(lib, seed=13, n_images=60):
             mins = np.full(base, H * W)
             np.minimum.at(mins, region.reshape(-1), flat)
             assert np.array_equal(L.reshape(-1), mins[region.reshape(-1)])
+
+
+def pin_ignore_vs_python_bfs(lib, n_images=300, seed=15):
+    """One ignored colour: leaders against a flood fill that skips it; numbers
+    and counts over the other regions only."""
+    rng = np.random.default_rng(seed)
+    for k in range(n_images):
+        H, W = int(rng.integers(1, 14)), int(rng.integers(1, 14))
+        ncol = int(rng.integers(1, 5))
+        dt = np.uint8 if k % 2 else np.uint32
+        img = random_images(rng, 1, H, W, ncol, dt)[0]
+        conn = 8 if k % 3 else 4
+        # usually a colour of the picture; now and then one it does not contain
+        ign = img.reshape(-1)[int(rng.integers(0, H * W))] if k % 5 else int(img.max()) + 1
+        L = oracle.label(img, conn, lib=lib, ignore=ign)
+        E = py_bfs_ignore(img, conn, ign)
+        assert np.array_equal(L, E), f"case {k}: {H}x{W} conn {conn} ignore {ign}"
+        labels, counts = oracle.number(L, lib=lib)
+        kept = E.reshape(-1) >= 0
+        uniq = np.unique(E.reshape(-1)[kept])
+        exp_num = np.zeros(H * W, np.int64)
+        exp_num[kept] = np.searchsorted(uniq, E.reshape(-1)[kept]) + 1
+        assert np.array_equal(labels.reshape(-1), exp_num), f"case {k}: numbers"
+        assert counts[0] == uniq.size and oracle.count(L, lib=lib)[0] == uniq.size
+
+
+def pin_ignore_scipy_binary(lib, seed=16, n_images=150):
+    """Binary pictures with 0 ignored: numbers equal scipy's labelling value for
+    value (scipy numbers components 1..n in reading order of their first pixel,
+    background 0), at every foreground density."""
+    rng = np.random.default_rng(seed)
+    for k in range(n_images):
+        H, W = int(rng.integers(1, 48)), int(rng.integers(1, 48))
+        p = 0.05 + 0.9 * (k % 19) / 18
+        img = (rng.random((H, W)) < p).astype(np.uint8)
+        for conn in (8, 4):
+            structure = np.ones((3, 3)) if conn == 8 else ndi.generate_binary_structure(2, 1)
+            lab, n = ndi.label(img, structure=structure)
+            L = oracle.label(img, conn, lib=lib, ignore=0)
+            labels, counts = oracle.number(L, lib=lib)
+            assert np.array_equal(labels, lab), f"case {k} conn {conn}: numbers differ from scipy"
+            assert counts[0] == n, f"case {k} conn {conn}: count differs from scipy"
+    # a batch: every image numbered on its own from 1
+    imgs = (rng.random((4, 20, 30)) < 0.4).astype(np.uint8)
+    labels, counts = oracle.number(oracle.label(imgs, 8, lib=lib, ignore=0), lib=lib)
+    for b in range(4):
+        lab, n = ndi.label(imgs[b], structure=np.ones((3, 3)))
+        assert np.array_equal(labels[b], lab) and counts[b] == n
+
+
+def pin_ignore_leaves_other_regions(lib, seed=17, n_images=100):
+    """Regions never mix colours, so ignoring one colour changes no other
+    pixel's leader; ignoring a colour the picture lacks changes nothing; an
+    all-ignored picture has no regions."""
+    rng = np.random.default_rng(seed)
+    for k in range(n_images):
+        H, W = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        img = random_images(rng, 1, H, W, int(rng.integers(1, 5)),
+                            np.uint32 if k % 2 else np.uint8)[0]
+        conn = 8 if k % 2 else 4
+        full = oracle.label(img, conn, lib=lib)
+        ign = img.reshape(-1)[int(rng.integers(0, H * W))]
+        L = oracle.label(img, conn, lib=lib, ignore=ign)
+        keep = img != ign
+        assert np.array_equal(L[keep], full[keep]) and np.all(L[~keep] == -1)
+        # regions of the ignored colour, counted by scipy, are exactly the ones lost
+        structure = np.ones((3, 3)) if conn == 8 else ndi.generate_binary_structure(2, 1)
+        _, n_ign = ndi.label(~keep, structure=structure)
+        assert oracle.count(L, lib=lib)[0] == oracle.count(full, lib=lib)[0] - n_ign
+    img = np.full((5, 7), 9, np.uint8)
+    L = oracle.label(img, 8, lib=lib, ignore=9)
+    labels, counts = oracle.number(L, lib=lib)
+    assert np.all(L == -1) and np.all(labels == 0) and counts[0] == 0
+    L = oracle.label(img, 8, lib=lib, ignore=8)
+    assert np.all(L == 0)
 
 
 # ---------------------------------------------------------------------------
@@ -285,4 +403,8 @@ ALL_PINS = [
     pin_exhaustive,
     pin_scipy_partition,
     pin_invariants_and_numbering,
+    pin_ignore_torchcc_4x4,
+    pin_ignore_vs_python_bfs,
+    pin_ignore_scipy_binary,
+    pin_ignore_leaves_other_regions,
 ]

@@ -14,6 +14,8 @@ MUTANTS = {
     6: "up-left neighbour dropped",
     7: "32-bit colours compared on the low byte",
     8: "a diagonal joined in 4-connectivity",
+    9: "ignored pixels counted as regions",
+    10: "the ignored colour still labelled",
 }
 
 
