@@ -8,6 +8,7 @@ functions raises -- there is no CPU fallback.
 
     out, counts = label(img, connectivity=8, number=True)   # 1..n per image
     leaders, _  = label(img)                                # region minima
+    out, counts = label(img, number=True, ignore=0xFFFFFF)  # white ignored: 0
     labels, counts = number(leaders)
     counts = count(leaders)
 
@@ -27,7 +28,7 @@ __all__ = ["label", "number", "count", "workspace_bytes", "Labeller", "error_wor
            "CclError", "library_path"]
 
 CCL_U8, CCL_U32 = 1, 4
-CCL_NUMBER = 1
+CCL_NUMBER, CCL_IGNORE = 1, 2
 
 _lib = None
 
@@ -51,8 +52,8 @@ def _load():
     i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     lib.ccl_workspace_bytes.argtypes = [i64, i64, i64]
     lib.ccl_workspace_bytes.restype = sz
-    lib.ccl_label.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp,
-                              vp, sz, vp]
+    lib.ccl_label.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                              ctypes.c_uint32, vp, vp, vp, sz, vp]
     lib.ccl_label.restype = ctypes.c_int
     lib.ccl_label_profiled.argtypes = lib.ccl_label.argtypes + [ctypes.POINTER(vp), ctypes.c_int]
     lib.ccl_label_profiled.restype = ctypes.c_int
@@ -117,11 +118,21 @@ def error_word(workspace: torch.Tensor) -> int:
     return int(workspace[:4].view(torch.int32).item())
 
 
+def _flags(number: bool, ignore) -> tuple[int, int]:
+    """(flags, ignore value) for ccl_label; ``ignore`` None ignores nothing."""
+    flags = CCL_NUMBER if number else 0
+    if ignore is None:
+        return flags, 0
+    return flags | CCL_IGNORE, int(ignore) & 0xFFFFFFFF
+
+
 def label(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream=None,
           workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-          with_counts: bool = True):
+          with_counts: bool = True, ignore: int | None = None):
     """Label ``img``: leaders (per-image reading-order index of each region's first
-    pixel) or, with ``number=True``, numbers 1..n per image.  Returns (out, counts)."""
+    pixel) or, with ``number=True``, numbers 1..n per image.  With ``ignore`` set,
+    pixels of that colour belong to no region: -1 as leaders, 0 as numbers, never
+    counted.  Returns (out, counts)."""
     _require_device(img, "img")
     x, squeeze = _batch_view(img)
     B, H, W = x.shape
@@ -130,9 +141,9 @@ def label(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream
     counts = torch.empty(B, dtype=torch.int32, device=img.device) if with_counts else None
     if workspace is None:
         workspace = _new_workspace(B, H, W, img.device)
-    _check(_load().ccl_label(_ptr(x), _dtype_code(x), B, H, W, int(connectivity),
-                             CCL_NUMBER if number else 0, _ptr(out), _ptr(counts),
-                             _ptr(workspace), workspace.numel(),
+    flags, ign = _flags(number, ignore)
+    _check(_load().ccl_label(_ptr(x), _dtype_code(x), B, H, W, int(connectivity), flags, ign,
+                             _ptr(out), _ptr(counts), _ptr(workspace), workspace.numel(),
                              ctypes.c_void_p(_stream_handle(stream))))
     return (out[0] if squeeze else out), counts
 
@@ -182,13 +193,15 @@ class Labeller:
         self.counts = torch.empty(self.B, dtype=torch.int32, device=device)
         self.workspace = _new_workspace(self.B, self.H, self.W, device)
 
-    def __call__(self, img: torch.Tensor, number: bool = True, stream=None, events=None):
+    def __call__(self, img: torch.Tensor, number: bool = True, stream=None, events=None,
+                 ignore: int | None = None):
         x, _ = _batch_view(img)
         if tuple(x.shape) != (self.B, self.H, self.W):
             raise ValueError("image shape does not match the Labeller")
         lib = _load()
+        flags, ign = _flags(number, ignore)
         args = [_ptr(x), _dtype_code(x), self.B, self.H, self.W, self.connectivity,
-                CCL_NUMBER if number else 0, _ptr(self.out), _ptr(self.counts),
+                flags, ign, _ptr(self.out), _ptr(self.counts),
                 _ptr(self.workspace), self.workspace.numel(),
                 ctypes.c_void_p(_stream_handle(stream))]
         if events is None:

@@ -104,15 +104,17 @@ static int finish_launches()
 }
 
 static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int64_t W, int conn,
-                      int flags, int32_t *out, int32_t *counts, void *workspace,
+                      int flags, uint32_t ignore, int32_t *out, int32_t *counts, void *workspace,
                       size_t workspace_bytes, void *stream, void **events, int n_events)
 {
-    if (flags & ~CCL_NUMBER) return CCL_ERR_FLAGS;
+    if (flags & ~(CCL_NUMBER | CCL_IGNORE)) return CCL_ERR_FLAGS;
     bool empty;
     int rc = check_shape(B, H, W, &empty);
     if (rc != CCL_OK) return rc;
     if (dtype != CCL_U8 && dtype != CCL_U32) return CCL_ERR_DTYPE;
     if (conn != 4 && conn != 8) return CCL_ERR_CONNECTIVITY;
+    const int ign = (flags & CCL_IGNORE) != 0;
+    if (ign && dtype == CCL_U8 && ignore > 0xFFu) return CCL_ERR_IGNORE;
     if (events != nullptr && n_events < 6) return CCL_ERR_NULL;
     hipStream_t s = (hipStream_t)stream;
     if (empty) {
@@ -134,7 +136,7 @@ static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int6
         if (events) (void)hipEventRecord((hipEvent_t)events[i], s);
     };
     mark(0);
-    launch_tile(colours, dtype, conn, L.g, w, s);
+    launch_tile(colours, dtype, conn, ign, ignore, L.g, w, s);
     mark(1);
     launch_seam(L.g, w, conn, s);
     mark(2);
@@ -143,7 +145,8 @@ static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int6
     if (need_scan) launch_scan(L.g, w, counts, number, 1, s);
     launch_resolve(L.g, w, number, s);
     mark(4);
-    launch_final(L.g, w, out, number, s);
+    // ignored pixels: number 0, or leader -1 (label 0 in the leader + 1 form)
+    launch_final(L.g, w, out, number, number ? 0u : 0xFFFFFFFFu, s);
     mark(5);
     return finish_launches();
 }
@@ -165,21 +168,21 @@ size_t ccl_workspace_bytes(int64_t batch, int64_t height, int64_t width)
 }
 
 int ccl_label(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
-              int connectivity, int flags, int32_t *out, int32_t *counts, void *workspace,
-              size_t workspace_bytes, void *stream)
+              int connectivity, int flags, uint32_t ignore, int32_t *out, int32_t *counts,
+              void *workspace, size_t workspace_bytes, void *stream)
 {
-    return label_impl(colours, dtype, batch, height, width, connectivity, flags, out, counts,
-                      workspace, workspace_bytes, stream, nullptr, 0);
+    return label_impl(colours, dtype, batch, height, width, connectivity, flags, ignore, out,
+                      counts, workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 int ccl_label_profiled(const void *colours, int dtype, int64_t batch, int64_t height,
-                       int64_t width, int connectivity, int flags, int32_t *out, int32_t *counts,
-                       void *workspace, size_t workspace_bytes, void *stream, void **events,
-                       int n_events)
+                       int64_t width, int connectivity, int flags, uint32_t ignore, int32_t *out,
+                       int32_t *counts, void *workspace, size_t workspace_bytes, void *stream,
+                       void **events, int n_events)
 {
     if (events == nullptr) return CCL_ERR_NULL;
-    return label_impl(colours, dtype, batch, height, width, connectivity, flags, out, counts,
-                      workspace, workspace_bytes, stream, events, n_events);
+    return label_impl(colours, dtype, batch, height, width, connectivity, flags, ignore, out,
+                      counts, workspace, workspace_bytes, stream, events, n_events);
 }
 
 int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t width,
@@ -245,6 +248,7 @@ const char *ccl_status_string(int status)
     case CCL_ERR_WORKSPACE: return "workspace smaller than ccl_workspace_bytes()";
     case CCL_ERR_HIP: return "HIP rejected a kernel launch";
     case CCL_ERR_FLAGS: return "unknown flag bits";
+    case CCL_ERR_IGNORE: return "ignored colour does not fit the dtype";
     default: return "unknown status";
     }
 }

@@ -40,6 +40,11 @@ static_assert(TH == 32 && TW == 64, "row masks are one wave64 ballot, tile rows 
 //   bit 15 clear: the region lies inside the tile; bits 0..10 = row*64+col of
 //                 its first pixel (its tile-local root)
 constexpr uint32_t INFO_BORDER = 0x8000u;
+// A run of an ignored colour: a border record whose slot is IGN_SLOT, one past
+// the last seam slot, where the final write keeps the ignored pixels' value.
+constexpr uint32_t IGN_SLOT = KMAX;
+constexpr uint32_t INFO_IGNORED = INFO_BORDER | IGN_SLOT;
+static_assert(IGN_SLOT < UNI_SLOT, "the ignored slot is no seam slot");
 
 // error word bits (first word of the workspace)
 constexpr uint32_t ERR_LOOP = 1u;      // a find/union loop hit its safety bound
@@ -52,7 +57,8 @@ struct TileHdr {
     uint32_t kind;      // bit 0: one-colour tile.  One-colour: bits 8..15 the slot of
                         //   its first open edge (255: none, so no seam node; its node
                         //   is slot UNI_SLOT); bit 1: a top-edge request at column 0
-                        //   (8 neighbours), bit 2: that request goes up-left.
+                        //   (8 neighbours), bit 2: that request goes up-left, bit 3:
+                        //   the ignored colour (no node, no requests, no leader).
                         //   Otherwise bits 8..15: 1 + the highest seam slot in use
                         //   (0: none)
     uint32_t value;     // one-colour tile with a seam node: its pixels' value
@@ -76,6 +82,7 @@ static_assert(sizeof(TileHdr) == 64, "one 64-byte store per tile");
 constexpr uint32_t KIND_UNIFORM = 1u;
 constexpr uint32_t KIND_TOP0 = 2u;      // one-colour: top request at column 0
 constexpr uint32_t KIND_TOP0_UL = 4u;   // ... to the pixel up-left of column 0
+constexpr uint32_t KIND_IGNORED = 8u;   // one-colour: the tile is of the ignored colour
 
 // exact unsigned division of n < 2^31 by a fixed d >= 1: q = (n*m) >> s, with
 // a 32-bit m (one 32x32 multiply and a shift)
@@ -130,14 +137,18 @@ bool make_layout(int64_t B, int64_t H, int64_t W, Layout *L);
 Work bind_work(const Layout &L, void *workspace);
 
 // Launchers (enqueue only).  dtype_bytes is 1 or 4, conn is 4 or 8.
-void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, const Work &w,
-                 hipStream_t s);
+// ignore: pixels of colour ign take part in nothing (their regions are neither
+// labelled nor counted)
+void launch_tile(const void *img, int dtype_bytes, int conn, int ignore, uint32_t ign,
+                 const Geom &g, const Work &w, hipStream_t s);
 void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s);
 void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s);
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
                  hipStream_t s);
 void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s);
-void launch_final(const Geom &g, const Work &w, int32_t *out, int number, hipStream_t s);
+// ignv: the value written for pixels of an ignored colour
+void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,
+                  hipStream_t s);
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
                          hipStream_t s);
 void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g, const Work &w,

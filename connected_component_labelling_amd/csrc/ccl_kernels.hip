@@ -346,6 +346,7 @@ __device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t x, int i)
 
 constexpr int QCAP = 256;  // join queue of one wave (a ring; at most 63 + 128 pending)
 
+template <bool IGN>
 struct TileLds {
     uint32_t P[TPX];               // parent of run slot; roots: + seam slot
     uint16_t Run[TPX];             // run slots in reading order, wave w's rows from
@@ -359,6 +360,7 @@ struct TileLds {
     uint32_t ColC[TH];             // colour at column 0 of each row
     uint64_t Used[KMAX / 64];
     uint64_t Uni[NWAVES];          // per wave: (one colour? << 32) | first colour
+    uint64_t Ign[IGN ? TH : 1];    // with an ignored colour: its pixels in each tile row
 };
 
 // Seam requests across the top edge (wave 0, lane = column): tile row 0
@@ -366,12 +368,13 @@ struct TileLds {
 // row above (hrow; hm1 / hp1 = the pixels diagonally beyond columns 0 and 63,
 // held by lanes 0 and 63).  ok_m: lanes of the tile's columns.  The joins are
 // found as in Connect, one request per pair of touching stretches.  Returns
-// the number written.
+// the number written.  Lanes outside keep_m (pixels of an ignored colour)
+// make none.
 template <int CONN>
 __device__ __forceinline__ uint32_t top_requests(uint16_t *q, int lane, uint64_t ok_m, bool has_left,
                                                  bool has_right, uint32_t cur, uint64_t st0,
                                                  uint32_t me, uint32_t hrow, uint32_t hm1,
-                                                 uint32_t hp1)
+                                                 uint32_t hp1, uint64_t keep_m)
 {
     const uint64_t u0 = __ballot(hrow == cur) & ok_m;
     uint64_t um1 = __ballot(from_left_lane(hrow) == cur) & ok_m & ~1ull;
@@ -386,6 +389,8 @@ __device__ __forceinline__ uint32_t top_requests(uint16_t *q, int lane, uint64_t
     } else {
         rb = u0 & (st0 | ~um1);
     }
+    ra &= keep_m;  // lanes of an ignored colour make no requests
+    rb &= keep_m;
     // requests in lane order, a lane's up-left/up one before its up-right one;
     // the byte above the slot is 1 + the column of the pixel above
     const uint32_t pos = mbcnt(ra) + mbcnt(rb);
@@ -397,10 +402,10 @@ __device__ __forceinline__ uint32_t top_requests(uint16_t *q, int lane, uint64_t
 // Seam requests across the left edge (wave 0, lane = tile row y): the pixel at
 // column 0 (colour cur, seam slot me) against the halo column h (the pixel left
 // of it); rows y-1 and y+1 are read from the neighbouring lanes.  vh_m: lanes
-// of the tile's rows.
+// of the tile's rows; lanes outside keep_m (an ignored colour) make none.
 template <int CONN>
 __device__ __forceinline__ uint32_t left_requests(uint16_t *q, int y, uint64_t vh_m, uint32_t me,
-                                                  uint32_t cur, uint32_t h)
+                                                  uint32_t cur, uint32_t h, uint64_t keep_m)
 {
     const uint32_t hu = from_left_lane(h), hd = from_right_lane(h);
     const uint32_t cu = from_left_lane(cur), cd = from_right_lane(cur);
@@ -409,11 +414,11 @@ __device__ __forceinline__ uint32_t left_requests(uint16_t *q, int y, uint64_t v
     const uint64_t up_same = __ballot(cu == cur) & up_ok;
     const uint64_t hu_cur = __ballot(hu == cur);
     // skip a join that the row above (or this row's left join) already makes
-    const uint64_t rl = ml & ~(up_same & hu_cur);
+    const uint64_t rl = ml & ~(up_same & hu_cur) & keep_m;
     uint64_t rul = 0, rdl = 0;
     if (CONN == 8) {
-        rul = up_ok & hu_cur & ~up_same & ~(ml & __ballot(h == hu));
-        rdl = dn_ok & __ballot(hd == cur) & ~__ballot(cd == cur) & ~(ml & __ballot(h == hd));
+        rul = up_ok & hu_cur & ~up_same & ~(ml & __ballot(h == hu)) & keep_m;
+        rdl = dn_ok & __ballot(hd == cur) & ~__ballot(cd == cur) & ~(ml & __ballot(h == hd)) & keep_m;
     }
     uint32_t pos = mbcnt(rul) + mbcnt(rl) + mbcnt(rdl);
     if (lane_bit(rul)) q[pos++] = (uint16_t)(me | ((0x80u | (uint32_t)(y - 1)) << 8));
@@ -459,10 +464,14 @@ __device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geo
     return in;
 }
 
-// FULL: the tile lies wholly inside the image (every edge check folds away)
-template <int CONN, bool FULL>
-__device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds &s, uint32_t t,
-                                           const TilePos &tp, const TileIn &in)
+// FULL: the tile lies wholly inside the image (every edge check folds away).
+// IGN: pixels of colour ign take part in nothing: their runs join no run,
+// reach no seam slot, lead no region and make no seam request; their run
+// records say so (INFO_IGNORED), and a tile of that one colour only writes a
+// header that says so (KIND_IGNORED).
+template <int CONN, bool FULL, bool IGN>
+__device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds<IGN> &s, uint32_t t,
+                                           const TilePos &tp, const TileIn &in, uint32_t ign)
 {
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // the same in the whole wave
@@ -526,6 +535,14 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         //      region's seam node; the other waves are done.
         if (wave != 0) return;
         const uint32_t C = c00;  // (wave 0) the colour of the tile's first pixel
+        if (IGN && C == ign) {
+            // the ignored colour: no region, no seam node, no requests
+            uint32_t v = 0;
+            v = write_lane(v, KIND_UNIFORM | KIND_IGNORED | (255u << 8), 0);
+            v = write_lane(v, (uint32_t)vh, 2);
+            if (lane < (int)(sizeof(TileHdr) / 4)) ((uint32_t *)&hdr)[lane] = v;
+            return;
+        }
         const uint32_t es = has_top ? 0u : has_bottom ? (uint32_t)TW
                           : has_left ? (uint32_t)(2 * TW) : has_right ? (uint32_t)(2 * TW + TH) : 255u;
         uint32_t kind = KIND_UNIFORM | (es << 8);
@@ -601,7 +618,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     // queue the joins of row y (colours cc, run starts st_m) with the row above
     // it (ca, sta_m)
     auto join_rows = [&](uint32_t cc, uint64_t st_m, uint32_t me, uint32_t ca, uint64_t sta_m,
-                         uint32_t mea) {
+                         uint32_t mea, uint64_t ig_m) {
         // lane shifts read other lanes, so they run with every lane active
         const uint32_t cl = from_left_lane(ca), cr = from_right_lane(ca);
         const uint64_t u0 = __ballot(ca == cc) & ok_m;
@@ -614,6 +631,10 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             lu = um1 & sta_m;        // ... up-left, where the run above starts at the lane
         } else {
             rb = u0 & (st_m | ~um1);
+        }
+        if (IGN) {  // a pixel of the ignored colour joins nothing
+            ra &= ~ig_m;
+            rb &= ~ig_m;
         }
         // run of the row above at column lane-1 (if taken) or lane; at lane+1
         const uint32_t ab = mea - (lane_bit(lu) ? 1u : 0u);
@@ -650,23 +671,36 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             const uint32_t cc = c[i];
             const uint64_t st_m = (__ballot(from_left_lane(cc) != cc) | 1ull) & ok_m;
             const uint32_t me = mbcnt_acc(st_m >> 1, (uint32_t)(y * 64));
+            uint64_t ig_m = 0;
+            if (IGN) ig_m = __ballot(cc == ign) & ok_m;
             if (lane_bit(st_m)) {
                 s.RX[me] = (uint8_t)lane;
                 s.P[me] = me;
                 run[nw + me - (uint32_t)(y * 64)] = (uint16_t)me;
             }
             nw += popc64(st_m);
-            mlo = write_lane(mlo, (uint32_t)st_m, i);
-            mhi = write_lane(mhi, (uint32_t)(st_m >> 32), i);
+            if (IGN) {
+                // plain stores by lane 0 (gathering these masks into lanes with
+                // write_lane, as the other instance does, gave wrong masks in
+                // this instance on MI355X; the cause was not found)
+                if (lane == 0) {
+                    s.Mask[y] = st_m;
+                    s.Ign[y] = ig_m;
+                }
+            } else {
+                mlo = write_lane(mlo, (uint32_t)st_m, i);
+                mhi = write_lane(mhi, (uint32_t)(st_m >> 32), i);
+            }
             if (i > 0) {
-                join_rows(cc, st_m, me, ca, sta, mea);
+                join_rows(cc, st_m, me, ca, sta, mea, ig_m);
                 drain(false);
             }
             ca = cc;
             sta = st_m;
             mea = me;
         }
-        if (lane < RPW) s.Mask[wave * RPW + lane] = ((uint64_t)mhi << 32) | mlo;  // 0 past the image edge
+        if (!IGN && lane < RPW) s.Mask[wave * RPW + lane] = ((uint64_t)mhi << 32) | mlo;  // 0 past the image edge
+        if (IGN && lane < RPW && lane >= nrows) s.Mask[wave * RPW + lane] = 0ull;
         if (lane == 0) {
 #pragma unroll
             for (int i = 0; i < RPW; ++i) s.ColC[wave * RPW + i] = c[i];  // (0 past the image edge)
@@ -700,7 +734,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         const int y = wave * RPW;
         const uint64_t mi = uniform64(s.Mask[y]), ma = uniform64(s.Mask[y - 1]);
         join_rows(c0, mi, mbcnt_acc(mi >> 1, (uint32_t)(y * 64)), s.LastC[wave - 1][lane], ma,
-                  mbcnt_acc(ma >> 1, (uint32_t)((y - 1) * 64)));
+                  mbcnt_acc(ma >> 1, (uint32_t)((y - 1) * 64)), IGN ? uniform64(s.Ign[y]) : 0ull);
     }
     drain(true);
     lds_barrier();
@@ -713,6 +747,8 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         const int cnt = (int)popc64(s.Mask[ry]);
         const uint32_t root = lds_find<true>(s.P, slot);
         if (root != slot) atomicMin(&s.P[slot], root);
+        // a run of the ignored colour joined nothing: it is its own root
+        if (IGN && ((s.Ign[ry] >> s.RX[slot]) & 1ull)) continue;
         uint32_t es = 255;
         if (has_right && k == cnt - 1) es = 2 * TW + TH + ry;
         if (has_left && k == 0) es = 2 * TW + ry;
@@ -726,6 +762,10 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
     for (uint32_t r = tid; r < R; r += BLOCK) {
         const uint32_t slot = run_slot(r);
+        if (IGN && ((s.Ign[slot >> 6] >> s.RX[slot]) & 1ull)) {
+            rinfo[r] = (uint16_t)INFO_IGNORED;
+            continue;
+        }
         const uint32_t pv = s.P[slot];
         const uint32_t root = pv & PMASK;
         const uint32_t rv = root == slot ? pv : s.P[root];
@@ -762,14 +802,16 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             const uint64_t m0 = uniform64(s.Mask[0]);
             const uint32_t me = seam_of(mbcnt_acc(m0 >> 1, 0u));  // region of the lane's run
             ntop = top_requests<CONN>(w.req + (size_t)t * REQMAX, lane, ok_m, has_left, has_right,
-                                      c[0], m0, me, hrow, hm1, hp1);
+                                      c[0], m0, me, hrow, hm1, hp1,
+                                      IGN ? ~uniform64(s.Ign[0]) : ~0ull);
         }
         if (has_left) {
             const bool valid = lane < vh;
             const uint32_t me = valid ? seam_of((uint32_t)(lane * 64)) : 0u;
             const uint32_t cur = valid ? s.ColC[lane] : 0u;
             nleft = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, lane,
-                                        (1ull << vh) - 1ull, me, cur, hleft);
+                                        (1ull << vh) - 1ull, me, cur, hleft,
+                                        IGN ? ~__ballot(valid && cur == ign) : ~0ull);
         }
         // the header in one store (the one-colour fields stay 0); the first
         // eight bytes also give the final write the bounds of its reads
@@ -805,9 +847,10 @@ struct TileArgs {
     const T *img;
     Geom g;
     Work w;
+    uint32_t ign;  // the ignored colour (IGN instances only)
 };
 
-template <typename T, int CONN>
+template <typename T, int CONN, bool IGN>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void tile_label_kernel(TileArgs<T> args)
 {
     (void)args;  // read below through the segment pointer
@@ -815,14 +858,14 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void
     const T *__restrict__ img = a.img;
     const Geom &g = a.g;
     const Work &w = a.w;
-    __shared__ TileLds s;
+    __shared__ TileLds<IGN> s;
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t t = remap_tile(blockIdx.x, gridDim.x);
     const TilePos tp = tile_pos(t, g);
     if (tp.vh == TH && tp.vw == TW)
-        label_tile<CONN, true>(g, w, s, t, tp, load_tile<T, true>(img, g, tp, wave, lane));
+        label_tile<CONN, true, IGN>(g, w, s, t, tp, load_tile<T, true>(img, g, tp, wave, lane), a.ign);
     else
-        label_tile<CONN, false>(g, w, s, t, tp, load_tile<T, false>(img, g, tp, wave, lane));
+        label_tile<CONN, false, IGN>(g, w, s, t, tp, load_tile<T, false>(img, g, tp, wave, lane), a.ign);
 }
 
 // ------------------------------------------------------------- seam passes
@@ -1596,10 +1639,10 @@ __device__ __forceinline__ void write_rows_x4(int32_t *o0, int64_t W, int vh, in
 }
 
 __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int32_t *out,
-                                                            int number)
+                                                            int number, uint32_t ignv)
 {
     __shared__ uint32_t sLab[NWAVES][DLAB];
-    __shared__ uint32_t sNode[NWAVES][KMAX];
+    __shared__ uint32_t sNode[NWAVES][KMAX + 1];  // + IGN_SLOT: the ignored pixels' value
     __shared__ uint64_t sLead[NWAVES][TH];
     __shared__ uint32_t sPre[NWAVES][TH];
 
@@ -1623,6 +1666,7 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         const bool seam = tp.ty > 0 || tp.tx > 0 || y0 + TH < g.H || x0 + TW < W;
         uint32_t v = uv.y;
         if (!seam) v = number ? 1u + h.pre : (uint32_t)(y0 * W + x0);
+        if (uv.x & KIND_IGNORED) v = ignv;
         if (x4) {
             const int4 v4 = make_int4((int)v, (int)v, (int)v, (int)v);
             for (int y = lane >> 4; y < tp.vh; y += 4) store_label4(o0 + y * W + 4 * (lane & 15), v4);
@@ -1672,6 +1716,7 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word)
         if ((used[word] >> lane) & 1ull) nodev[word * 64 + lane] = nv[word];
+    if (lane == 0) nodev[IGN_SLOT] = ignv;  // runs of an ignored colour read it
     __syncwarp();
     auto run_label = [&](uint32_t info) -> uint32_t {
         if (info & INFO_BORDER) return nodev[info & 0xFFu];
@@ -1779,24 +1824,27 @@ static inline unsigned grid_of(int64_t n, int64_t per)
     return (unsigned)((n + per - 1) / per);
 }
 
-void launch_tile(const void *img, int dtype_bytes, int conn, const Geom &g, const Work &w,
-                 hipStream_t s)
+template <typename T, int CONN>
+static void launch_tile_t(const void *img, int ignore, uint32_t ign, const Geom &g, const Work &w,
+                          hipStream_t s)
 {
     const dim3 grid((unsigned)g.ntiles), block(BLOCK);
+    const TileArgs<T> a{(const T *)img, g, w, ign};
+    if (ignore)
+        hipLaunchKernelGGL((tile_label_kernel<T, CONN, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((tile_label_kernel<T, CONN, false>), grid, block, 0, s, a);
+}
+
+void launch_tile(const void *img, int dtype_bytes, int conn, int ignore, uint32_t ign,
+                 const Geom &g, const Work &w, hipStream_t s)
+{
     if (dtype_bytes == 1) {
-        if (conn == 8)
-            hipLaunchKernelGGL((tile_label_kernel<uint8_t, 8>), grid, block, 0, s,
-                               TileArgs<uint8_t>{(const uint8_t *)img, g, w});
-        else
-            hipLaunchKernelGGL((tile_label_kernel<uint8_t, 4>), grid, block, 0, s,
-                               TileArgs<uint8_t>{(const uint8_t *)img, g, w});
+        if (conn == 8) launch_tile_t<uint8_t, 8>(img, ignore, ign, g, w, s);
+        else launch_tile_t<uint8_t, 4>(img, ignore, ign, g, w, s);
     } else {
-        if (conn == 8)
-            hipLaunchKernelGGL((tile_label_kernel<uint32_t, 8>), grid, block, 0, s,
-                               TileArgs<uint32_t>{(const uint32_t *)img, g, w});
-        else
-            hipLaunchKernelGGL((tile_label_kernel<uint32_t, 4>), grid, block, 0, s,
-                               TileArgs<uint32_t>{(const uint32_t *)img, g, w});
+        if (conn == 8) launch_tile_t<uint32_t, 8>(img, ignore, ign, g, w, s);
+        else launch_tile_t<uint32_t, 4>(img, ignore, ign, g, w, s);
     }
 }
 
@@ -1826,10 +1874,11 @@ void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s)
                        number);
 }
 
-void launch_final(const Geom &g, const Work &w, int32_t *out, int number, hipStream_t s)
+void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,
+                  hipStream_t s)
 {
     hipLaunchKernelGGL(final_write_kernel, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0, s, g,
-                       w, out, number);
+                       w, out, number, ignv);
 }
 
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,

@@ -14,7 +14,10 @@
  *   Its number is 1 + the count of leaders before it in reading order (same
  *   page, ch.08 idea 5 "Number without a giant list").  Colours are compared
  *   as whole stored values: all 32 bits of a CCL_U32 pixel, the byte of a
- *   CCL_U8 pixel.  Every value, 0 included, forms regions.
+ *   CCL_U8 pixel.  Every value, 0 included, forms regions, unless the caller
+ *   names one colour to ignore (CCL_IGNORE, same page, ch.08 idea 4 "Ignore the
+ *   paper"): its pixels then belong to no region and are neither numbered nor
+ *   counted.
  *
  * Memory.  Every pointer argument except the host-side ones named below is a
  * DEVICE pointer on the current HIP device.  Images are contiguous row-major
@@ -54,14 +57,24 @@ typedef enum {
     CCL_ERR_DTYPE = -5,         /* dtype is not CCL_U8 or CCL_U32                    */
     CCL_ERR_WORKSPACE = -6,     /* workspace smaller than ccl_workspace_bytes()      */
     CCL_ERR_HIP = -7,           /* HIP rejected a kernel launch                      */
-    CCL_ERR_FLAGS = -8          /* unknown bits in flags                             */
+    CCL_ERR_FLAGS = -8,         /* unknown bits in flags                             */
+    CCL_ERR_IGNORE = -9         /* CCL_IGNORE with a value above 255 for CCL_U8      */
 } ccl_status;
 
 /* Colour element types; the value is the size of one pixel in bytes. */
 enum { CCL_U8 = 1, CCL_U32 = 4 };
 
-/* ccl_label flag: write numbers 1..n instead of leaders. */
-enum { CCL_NUMBER = 1 };
+/* ccl_label flags.
+ *   CCL_NUMBER  write numbers 1..n instead of leaders.
+ *   CCL_IGNORE  pixels whose colour equals `ignore` take part in nothing
+ *               ("Accountable AI starts at the pixel", ch.08 idea 4): they join
+ *               no neighbour, lead no region and are not counted.  They are
+ *               written as 0 with CCL_NUMBER and as -1 without it (the label 0
+ *               of the "leader + 1, 0 for background" form of "About Connected
+ *               Components Labeling on GPU", "Application in CCL").  Every
+ *               other pixel gets the leader it gets without the flag (regions
+ *               never mix colours), and numbers count only such leaders. */
+enum { CCL_NUMBER = 1, CCL_IGNORE = 2 };
 
 /*
  * Bytes of device workspace any call below needs for a batch of this shape.
@@ -81,13 +94,16 @@ size_t ccl_workspace_bytes(int64_t batch, int64_t height, int64_t width);
  *                 uint32 (CCL_U32)
  *   connectivity  8 (edges and corners) or 4 (edges only)
  *   flags         0: out[p] = leader of p (per-image reading-order index);
- *                 CCL_NUMBER: out[p] = number of p's region, 1..n per image
+ *                 CCL_NUMBER: out[p] = number of p's region, 1..n per image;
+ *                 | CCL_IGNORE: the colour `ignore` is ignored (see above)
+ *   ignore        the ignored colour, used only with CCL_IGNORE (a whole stored
+ *                 value; at most 255 for CCL_U8, else CCL_ERR_IGNORE)
  *   out           device int32 [batch, height, width]; must not overlap colours
  *   counts        device int32 [batch] or NULL: number of regions per image
  *   workspace     device, at least ccl_workspace_bytes(batch, height, width)
  */
 int ccl_label(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
-              int connectivity, int flags, int32_t *out, int32_t *counts,
+              int connectivity, int flags, uint32_t ignore, int32_t *out, int32_t *counts,
               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -98,8 +114,8 @@ int ccl_label(const void *colours, int dtype, int64_t batch, int64_t height, int
  * hipEvent_t created by the caller.  Same results as ccl_label.
  */
 int ccl_label_profiled(const void *colours, int dtype, int64_t batch, int64_t height,
-                       int64_t width, int connectivity, int flags, int32_t *out,
-                       int32_t *counts, void *workspace, size_t workspace_bytes,
+                       int64_t width, int connectivity, int flags, uint32_t ignore,
+                       int32_t *out, int32_t *counts, void *workspace, size_t workspace_bytes,
                        void *stream, void **events, int n_events);
 
 /*
@@ -108,8 +124,9 @@ int ccl_label_profiled(const void *colours, int dtype, int64_t batch, int64_t he
  * ch.08 idea 5).
  *   leaders  device int32 [batch, height, width]: a valid leader image, i.e.
  *            leaders[p] <= p and leaders[leaders[p]] == leaders[p] (as written
- *            by ccl_label).  Not checked; a value outside [0, height*width)
- *            yields label 0 and is never dereferenced.
+ *            by ccl_label).  Not checked; a value outside [0, height*width),
+ *            such as the -1 of an ignored pixel, yields label 0 and is never
+ *            dereferenced.
  *   labels   device int32 [batch, height, width]; may be the same buffer as
  *            leaders (in-place), must not otherwise overlap it
  *   counts   device int32 [batch] or NULL

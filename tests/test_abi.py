@@ -66,26 +66,29 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
 
 
 @pytest.mark.parametrize("args,status", [
-    # (dtype, B, H, W, conn, flags, workspace_bytes), expected status
-    ((4, 1, 8, 8, 6, 0, 1 << 30), -4),          # connectivity
-    ((2, 1, 8, 8, 8, 0, 1 << 30), -5),          # dtype
-    ((4, -1, 8, 8, 8, 0, 1 << 30), -2),         # shape
-    ((4, 1, 8, -3, 8, 0, 1 << 30), -2),
-    ((4, 1, 65536, 65536, 8, 0, 1 << 30), -3),  # H*W > 2^31-1
-    ((4, 1, 8, 8, 8, 2, 1 << 30), -8),          # flags
-    ((4, 1, 8, 8, 8, 0, 16), -6),               # workspace too small
+    # (dtype, B, H, W, conn, flags, ignore, workspace_bytes), expected status
+    ((4, 1, 8, 8, 6, 0, 0, 1 << 30), -4),          # connectivity
+    ((2, 1, 8, 8, 8, 0, 0, 1 << 30), -5),          # dtype
+    ((4, -1, 8, 8, 8, 0, 0, 1 << 30), -2),         # shape
+    ((4, 1, 8, -3, 8, 0, 0, 1 << 30), -2),
+    ((4, 1, 65536, 65536, 8, 0, 0, 1 << 30), -3),  # H*W > 2^31-1
+    ((4, 1, 8, 8, 8, 4, 0, 1 << 30), -8),          # flags
+    ((4, 1, 8, 8, 8, 0, 0, 16), -6),               # workspace too small
+    ((4, 1, 8, 8, 8, 3, 0, 16), -6),               # ... with an ignored colour too
+    ((1, 1, 8, 8, 8, 2, 256, 1 << 30), -9),        # ignored colour wider than a byte
+    ((1, 1, 8, 8, 8, 3, 0xFFFFFFFF, 1 << 30), -9),
 ])
 def test_label_validation(lib, args, status):
-    dtype, B, H, W, conn, flags, wsb = args
-    rc = lib.ccl_label(FAKE, dtype, B, H, W, conn, flags, FAKE, None, FAKE, wsb, None)
+    dtype, B, H, W, conn, flags, ign, wsb = args
+    rc = lib.ccl_label(FAKE, dtype, B, H, W, conn, flags, ign, FAKE, None, FAKE, wsb, None)
     assert rc == status
     assert lib.ccl_status_string(rc)
 
 
 def test_null_pointers(lib):
-    assert lib.ccl_label(None, 4, 1, 8, 8, 8, 0, FAKE, None, FAKE, 1 << 30, None) == -1
-    assert lib.ccl_label(FAKE, 4, 1, 8, 8, 8, 0, None, None, FAKE, 1 << 30, None) == -1
-    assert lib.ccl_label(FAKE, 4, 1, 8, 8, 8, 0, FAKE, None, None, 1 << 30, None) == -1
+    assert lib.ccl_label(None, 4, 1, 8, 8, 8, 0, 0, FAKE, None, FAKE, 1 << 30, None) == -1
+    assert lib.ccl_label(FAKE, 4, 1, 8, 8, 8, 0, 0, None, None, FAKE, 1 << 30, None) == -1
+    assert lib.ccl_label(FAKE, 4, 1, 8, 8, 8, 2, 7, FAKE, None, None, 1 << 30, None) == -1
     assert lib.ccl_number(None, 1, 8, 8, FAKE, None, FAKE, 1 << 30, None) == -1
     assert lib.ccl_count(FAKE, 1, 8, 8, None, FAKE, 1 << 30, None) == -1
     assert lib.ccl_number(FAKE, 1, 8, 8, FAKE, None, FAKE, 16, None) == -6
@@ -94,12 +97,13 @@ def test_null_pointers(lib):
 
 def test_empty_batches_are_noops(lib):
     # nothing to do and no counts to write: returns before any HIP call
-    assert lib.ccl_label(None, 4, 0, 8, 8, 8, 1, None, None, None, 0, None) == 0
-    assert lib.ccl_label(None, 1, 3, 0, 8, 8, 0, None, None, None, 0, None) == 0
+    assert lib.ccl_label(None, 4, 0, 8, 8, 8, 1, 0, None, None, None, 0, None) == 0
+    assert lib.ccl_label(None, 1, 3, 0, 8, 8, 0, 0, None, None, None, 0, None) == 0
+    assert lib.ccl_label(None, 1, 3, 0, 8, 8, 3, 255, None, None, None, 0, None) == 0
     assert lib.ccl_number(None, 2, 5, 0, None, None, None, 0, None) == 0
 
 
 def test_status_strings(lib):
-    for s in range(-8, 1):
+    for s in range(-9, 1):
         assert lib.ccl_status_string(s).decode()
     assert lib.ccl_status_string(-99) == b"unknown status"

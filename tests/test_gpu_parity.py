@@ -26,14 +26,17 @@ def to_device(img: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(img)).cuda()
 
 
-def announce(name, img, conn):
-    print(f"[gpu case] {name} shape={tuple(img.shape)} dtype={img.dtype} conn={conn}", flush=True)
+def announce(name, img, conn, ignore=None):
+    ign = "" if ignore is None else f" ignore=0x{int(ignore):x}"
+    print(f"[gpu case] {name} shape={tuple(img.shape)} dtype={img.dtype} conn={conn}{ign}",
+          flush=True)
 
 
-def check_case(ccl, name, img, conn=8, workspace=None):
-    """Leaders, numbers and counts of the HIP path equal the oracle's."""
-    announce(name, img, conn)
-    exp_leaders = oracle.label(img, conn)
+def check_case(ccl, name, img, conn=8, workspace=None, ignore=None):
+    """Leaders, numbers and counts of the HIP path equal the oracle's (with
+    ``ignore``: pixels of that colour are -1 / 0 and not counted)."""
+    announce(name, img, conn, ignore)
+    exp_leaders = oracle.label(img, conn, ignore=ignore)
     exp_labels, exp_counts = oracle.number(exp_leaders)
     t = to_device(img)
     batch = img if img.ndim == 3 else img[None]
@@ -41,8 +44,8 @@ def check_case(ccl, name, img, conn=8, workspace=None):
     if workspace is None:
         workspace = torch.zeros(max(ccl.workspace_bytes(B, H, W), 1), dtype=torch.uint8,
                                 device="cuda")
-    leaders, c0 = ccl.label(t, conn, number=False, workspace=workspace)
-    labels, c1 = ccl.label(t, conn, number=True, workspace=workspace)
+    leaders, c0 = ccl.label(t, conn, number=False, workspace=workspace, ignore=ignore)
+    labels, c1 = ccl.label(t, conn, number=True, workspace=workspace, ignore=ignore)
     torch.cuda.synchronize()
     got_leaders = leaders.cpu().numpy()
     got_labels = labels.cpu().numpy()
@@ -176,6 +179,78 @@ def test_batch_ragged(ccl):
     check_case(ccl, "batch 3x70x130", img, 8)
     img = synth.bernoulli_batch(5, 100, 90, seed=9)
     check_case(ccl, "bernoulli batch 5x100x90", img, 8)
+
+
+# ------------------------------------------------------- one ignored colour
+
+def most_common_colour(img: np.ndarray) -> int:
+    """The colour of most pixels (of a strided sample): the paper of a drawing."""
+    v, c = np.unique(img.reshape(-1)[::97], return_counts=True)
+    return int(v[np.argmax(c)])
+
+
+@pytest.mark.parametrize("conn", [8, 4])
+@pytest.mark.parametrize("dtype", [np.uint32, np.uint8])
+def test_ignore_ragged_random(ccl, conn, dtype):
+    rng = np.random.default_rng(200 + conn)
+    for H in HS:
+        for W in WS:
+            ncol = int(rng.integers(1, 4))
+            idx = rng.integers(0, ncol, size=(H, W))
+            if dtype == np.uint8:
+                img = idx.astype(np.uint8)
+            else:
+                img = rng.integers(0, 2**32, size=ncol, dtype=np.uint64).astype(np.uint32)[idx]
+            ign = int(img.reshape(-1)[int(rng.integers(0, H * W))])
+            check_case(ccl, f"ignore random {H}x{W} ncol={ncol}", img, conn, ignore=ign)
+    # a colour the picture lacks changes nothing; a one-colour picture vanishes
+    img = rng.integers(0, 3, size=(70, 130)).astype(dtype)
+    check_case(ccl, "ignore an absent colour", img, conn, ignore=7)
+    check_case(ccl, "ignore the only colour", np.full((70, 130), 2, dtype), conn, ignore=2)
+
+
+@pytest.mark.parametrize("conn", [8, 4])
+@pytest.mark.parametrize("dtype", [np.uint32, np.uint8])
+def test_ignore_one_colour_tiles(ccl, conn, dtype):
+    """Ignored one-colour tiles beside mixed tiles and one-colour tiles of other
+    colours (the mosaics' solid colours are 7, 8 and 9)."""
+    for name, img in mosaic_images().items():
+        for ign in (7, 5, 3):
+            check_case(ccl, f"ignore {ign}: {name}", img.astype(dtype), conn, ignore=ign)
+
+
+@pytest.mark.parametrize("conn", [8, 4])
+def test_ignore_structured(ccl, conn):
+    for name, img in structured_images().items():
+        check_case(ccl, f"ignore paper: {name}", img, conn, ignore=most_common_colour(img))
+
+
+def test_ignore_batch_and_standalone_number(ccl):
+    img = synth.bernoulli_batch(5, 100, 90, seed=9)
+    check_case(ccl, "ignore 0: bernoulli batch 5x100x90", img, 8, ignore=0)
+    img = synth.sheet_image(480, 700, seed=2)
+    ign = most_common_colour(img)
+    announce("number/count of an ignore leader image", img, 8, ign)
+    L = oracle.label(img, 8, ignore=ign)
+    exp_labels, exp_counts = oracle.number(L)
+    Ld = torch.from_numpy(np.ascontiguousarray(L)).cuda()
+    labels, counts = ccl.number(Ld)
+    c2 = ccl.count(Ld)
+    torch.cuda.synchronize()
+    assert np.array_equal(labels.cpu().numpy(), exp_labels)
+    assert int(counts.cpu()[0]) == int(exp_counts[0]) == int(c2.cpu()[0])
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+def test_ignore_workload_full_size(ccl, config):
+    """Every workload at full size with its most common colour ignored (the
+    paper of the drawings, the background of the binary pictures)."""
+    img = synth.generate(config)
+    ign = most_common_colour(img)
+    counts = check_case(ccl, f"ignore 0x{ign:x}, workload {config}: {synth.CONFIGS[config][0]}",
+                        img, 8, ignore=ign)
+    print(f"[gpu case] workload {config} regions per image, 0x{ign:x} ignored: "
+          f"{counts[:4].tolist()}", flush=True)
 
 
 # -------------------------------------------------------- full-size workloads
