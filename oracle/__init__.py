@@ -72,8 +72,18 @@ def load(path: str | None = None):
     return _lib
 
 
-def _as_batch(img: np.ndarray):
+def _as_batch(img: np.ndarray, rgb: bool = False):
+    """(contiguous [B, H, W] or [B, H, W, 3] array, dtype code, squeezed?)."""
     img = np.asarray(img)
+    if rgb:
+        if img.dtype != np.uint8 or img.shape[-1:] != (3,):
+            raise TypeError("an RGB picture is uint8 with a last dimension of 3")
+        squeeze = img.ndim == 3
+        if squeeze:
+            img = img[None]
+        if img.ndim != 4:
+            raise ValueError("RGB picture must be [H, W, 3] or [B, H, W, 3]")
+        return np.ascontiguousarray(img), 3, squeeze
     squeeze = img.ndim == 2
     if squeeze:
         img = img[None]
@@ -92,9 +102,9 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def _run_labeller(fname: str, img, connectivity: int, lib, *extra):
-    img, dtype, squeeze = _as_batch(img)
-    B, H, W = img.shape
+def _run_labeller(fname: str, img, connectivity: int, lib, *extra, rgb: bool = False):
+    img, dtype, squeeze = _as_batch(img, rgb)
+    B, H, W = img.shape[:3]
     out = np.empty((B, H, W), dtype=np.int32)
     rc = getattr(lib, fname)(img.ctypes.data_as(ctypes.c_void_p), dtype, B, H, W,
                              int(connectivity), *extra, _ptr(out))
@@ -103,23 +113,24 @@ def _run_labeller(fname: str, img, connectivity: int, lib, *extra):
     return out[0] if squeeze else out
 
 
-def label(img, connectivity: int = 8, lib=None, ignore=None) -> np.ndarray:
+def label(img, connectivity: int = 8, lib=None, ignore=None, rgb: bool = False) -> np.ndarray:
     """Leader image: each pixel's region minimum reading-order index (per image).
-    With ``ignore`` set, pixels of that colour get -1 and join nothing."""
+    With ``ignore`` set, pixels of that colour get -1 and join nothing.  With
+    ``rgb``, ``img`` is uint8 [.., H, W, 3] and all three bytes are compared."""
     if ignore is None:
-        return _run_labeller("oracle_label", img, connectivity, lib or load())
+        return _run_labeller("oracle_label", img, connectivity, lib or load(), rgb=rgb)
     return _run_labeller("oracle_label_ignore", img, connectivity, lib or load(),
-                         ctypes.c_uint32(int(ignore) & 0xFFFFFFFF))
+                         ctypes.c_uint32(int(ignore) & 0xFFFFFFFF), rgb=rgb)
 
 
-def connect(img, connectivity: int = 8, lib=None) -> np.ndarray:
+def connect(img, connectivity: int = 8, lib=None, rgb: bool = False) -> np.ndarray:
     """Parent array after the Start and Connect stages (before Collapse)."""
-    return _run_labeller("oracle_connect", img, connectivity, lib or load())
+    return _run_labeller("oracle_connect", img, connectivity, lib or load(), rgb=rgb)
 
 
-def bfs_label(img, connectivity: int = 8, lib=None) -> np.ndarray:
+def bfs_label(img, connectivity: int = 8, lib=None, rgb: bool = False) -> np.ndarray:
     """Independent breadth-first flood-fill labeller (leader = seed index)."""
-    return _run_labeller("oracle_bfs_label", img, connectivity, lib or load())
+    return _run_labeller("oracle_bfs_label", img, connectivity, lib or load(), rgb=rgb)
 
 
 def number(leaders, lib=None):
@@ -153,9 +164,9 @@ def count(leaders, lib=None) -> np.ndarray:
     return counts
 
 
-def label_and_number(img, connectivity: int = 8, lib=None, ignore=None):
+def label_and_number(img, connectivity: int = 8, lib=None, ignore=None, rgb: bool = False):
     """(leaders, labels, counts): the whole path as the oracle computes it."""
     lib = lib or load()
-    leaders = label(img, connectivity, lib, ignore=ignore)
+    leaders = label(img, connectivity, lib, ignore=ignore, rgb=rgb)
     labels, counts = number(leaders, lib)
     return leaders, labels, counts

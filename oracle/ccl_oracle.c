@@ -41,10 +41,14 @@
  * the alternative that page names in "The basic approach") used to pin the
  * union-find oracle; it is not used by the union-find code.
  *
- * dtype: 1 = one byte per pixel, 4 = one 32-bit word per pixel; colours are
- * compared as whole stored values.
+ * dtype: 1 = one byte per pixel, 4 = one 32-bit word per pixel, 3 = three
+ * bytes per pixel (an RGB picture as it is stored, "Accountable AI starts at
+ * the pixel", ch.08 "Tried and dropped" and ch.09: the labeller reads the RGB
+ * picture without packing it); colours are compared as whole stored values,
+ * all three bytes of an RGB pixel.  An RGB pixel's colour value, as an ignored
+ * colour is named, is b0 | b1 << 8 | b2 << 16 with b0 its first byte.
  *
- * Building with -DORACLE_MUTANT=k plants a deliberate mistake (k = 1..10) so the
+ * Building with -DORACLE_MUTANT=k plants a deliberate mistake (k = 1..11) so the
  * pin tests can show that they catch it.  The default build plants nothing.
  */
 #include <stdint.h>
@@ -62,6 +66,14 @@ static inline uint32_t colour_at(const void *img, int dtype, int64_t i)
 {
     if (dtype == 1)
         return ((const uint8_t *)img)[i];
+    if (dtype == 3) {
+        const uint8_t *p = (const uint8_t *)img + 3 * i;
+#if ORACLE_MUTANT == 11
+        return (uint32_t)p[0] | ((uint32_t)p[1] << 8);   /* mutant: third byte not compared */
+#else
+        return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
+#endif
+    }
 #if ORACLE_MUTANT == 7
     return ((const uint32_t *)img)[i] & 0xFFu; /* mutant: low byte only */
 #else
@@ -169,7 +181,7 @@ static int check_args(const void *img, int dtype, int64_t B, int64_t H,
                       int64_t W, int conn, const void *out)
 {
     if (B < 0 || H < 0 || W < 0) return ORACLE_ERR_ARG;
-    if (dtype != 1 && dtype != 4) return ORACLE_ERR_ARG;
+    if (dtype != 1 && dtype != 3 && dtype != 4) return ORACLE_ERR_ARG;
     if (conn != 4 && conn != 8) return ORACLE_ERR_ARG;
     if (H * W > 2147483647LL) return ORACLE_ERR_ARG;
     if (B * H * W > 0 && (img == NULL || out == NULL)) return ORACLE_ERR_ARG;

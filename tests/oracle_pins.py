@@ -13,6 +13,8 @@ given disagrees with:
     the TorchCC page's "Find(i) + 1, 0 for background" labels, a flood fill
     that skips the ignored colour, and scipy's binary labelling (whose numbers
     are 1..n in reading order, 0 for background) value for value,
+  * for RGB pictures stored as three bytes per pixel (same page, ch.08-09): a
+    flood fill comparing the three bytes as a tuple,
   * invariants of the definition (leader = region minimum, equal-colour
     neighbours share a leader, numbers are 1..n in reading order).
 
@@ -328,6 +330,50 @@ def pin_ignore_leaves_other_regions(lib, seed=17, n_images=100):
     assert np.all(L == 0)
 
 
+def rgb_tuples(img: np.ndarray) -> np.ndarray:
+    """[H, W] object array of (b0, b1, b2) tuples: colours compared as tuples,
+    with no packing into one number."""
+    H, W, _ = img.shape
+    out = np.empty((H, W), dtype=object)
+    for r in range(H):
+        for c in range(W):
+            out[r, c] = tuple(int(v) for v in img[r, c])
+    return out
+
+
+def random_rgb(rng, B, H, W, ncol):
+    """Random RGB pictures whose ``ncol`` colours differ from one another in one
+    byte only (which byte varies per colour), so every byte decides."""
+    base = rng.integers(0, 256, size=3)
+    pal = np.tile(base, (ncol, 1))
+    for k in range(1, ncol):
+        pal[k, k % 3] = (base[k % 3] + k) % 256
+    return pal[rng.integers(0, ncol, size=(B, H, W))].astype(np.uint8)
+
+
+def pin_rgb_vs_python_bfs(lib, n_images=240, seed=18):
+    """Three-byte pixels: leaders against a flood fill over byte tuples, both
+    connectivities, with and without an ignored colour; a batch is labelled
+    image by image."""
+    rng = np.random.default_rng(seed)
+    for k in range(n_images):
+        H, W = int(rng.integers(1, 13)), int(rng.integers(1, 13))
+        img = random_rgb(rng, 1, H, W, int(rng.integers(1, 5)))[0]
+        conn = 8 if k % 3 else 4
+        T = rgb_tuples(img)
+        L = oracle.label(img, conn, lib=lib, rgb=True)
+        assert np.array_equal(L, py_bfs(T, conn)), f"case {k}: {H}x{W} conn {conn}"
+        if k % 2:
+            r, c = int(rng.integers(0, H)), int(rng.integers(0, W))
+            ign = int(img[r, c, 0]) | (int(img[r, c, 1]) << 8) | (int(img[r, c, 2]) << 16)
+            L = oracle.label(img, conn, lib=lib, rgb=True, ignore=ign)
+            assert np.array_equal(L, py_bfs_ignore(T, conn, T[r, c])), f"case {k}: ignore"
+    imgs = random_rgb(rng, 3, 9, 11, 3)
+    L = oracle.label(imgs, 8, lib=lib, rgb=True)
+    for b in range(3):
+        assert np.array_equal(L[b], py_bfs(rgb_tuples(imgs[b]), 8))
+
+
 # ---------------------------------------------------------------------------
 # closed forms and special cases
 
@@ -407,4 +453,5 @@ ALL_PINS = [
     pin_ignore_vs_python_bfs,
     pin_ignore_scipy_binary,
     pin_ignore_leaves_other_regions,
+    pin_rgb_vs_python_bfs,
 ]

@@ -16,6 +16,7 @@ MUTANTS = {
     8: "a diagonal joined in 4-connectivity",
     9: "ignored pixels counted as regions",
     10: "the ignored colour still labelled",
+    11: "RGB pixels compared on two of their three bytes",
 }
 
 
