@@ -13,7 +13,10 @@ functions raises -- there is no CPU fallback.
     counts = count(leaders)
 
 ``img`` is a CUDA (HIP) tensor of shape [H, W] or [B, H, W], dtype uint8, or
-uint32 / int32 (the 32 bits are compared as they are); results are int32.
+uint32 / int32 (the 32 bits are compared as they are), or with ``rgb=True`` an
+RGB picture as stored, uint8 [H, W, 3] or [B, H, W, 3] (all three bytes are
+compared; an ignored RGB colour is named b0 | b1 << 8 | b2 << 16, b0 the
+pixel's first byte); results are int32.
 """
 from __future__ import annotations
 
@@ -27,7 +30,7 @@ from . import build as _build
 __all__ = ["label", "number", "count", "workspace_bytes", "Labeller", "error_word",
            "CclError", "library_path"]
 
-CCL_U8, CCL_U32 = 1, 4
+CCL_U8, CCL_RGB24, CCL_U32 = 1, 3, 4
 CCL_NUMBER, CCL_IGNORE = 1, 2
 
 _lib = None
@@ -76,7 +79,15 @@ def workspace_bytes(batch: int, height: int, width: int) -> int:
     return int(_load().ccl_workspace_bytes(batch, height, width))
 
 
-def _batch_view(t: torch.Tensor):
+def _batch_view(t: torch.Tensor, rgb: bool = False):
+    if rgb:
+        if t.dtype != torch.uint8 or t.shape[-1:] != (3,):
+            raise TypeError("an RGB picture is a uint8 tensor with a last dimension of 3")
+        if t.dim() == 3:
+            return t.unsqueeze(0), True
+        if t.dim() != 4:
+            raise ValueError("expected an [H, W, 3] or [B, H, W, 3] RGB tensor")
+        return t, False
     if t.dim() == 2:
         return t.unsqueeze(0), True
     if t.dim() != 3:
@@ -84,7 +95,9 @@ def _batch_view(t: torch.Tensor):
     return t, False
 
 
-def _dtype_code(t: torch.Tensor) -> int:
+def _dtype_code(t: torch.Tensor, rgb: bool = False) -> int:
+    if rgb:
+        return CCL_RGB24
     if t.dtype == torch.uint8:
         return CCL_U8
     if t.dtype in (torch.int32, torch.uint32):
@@ -128,21 +141,22 @@ def _flags(number: bool, ignore) -> tuple[int, int]:
 
 def label(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream=None,
           workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-          with_counts: bool = True, ignore: int | None = None):
+          with_counts: bool = True, ignore: int | None = None, rgb: bool = False):
     """Label ``img``: leaders (per-image reading-order index of each region's first
     pixel) or, with ``number=True``, numbers 1..n per image.  With ``ignore`` set,
     pixels of that colour belong to no region: -1 as leaders, 0 as numbers, never
-    counted.  Returns (out, counts)."""
+    counted.  With ``rgb``, ``img`` is an RGB picture of three bytes per pixel.
+    Returns (out, counts)."""
     _require_device(img, "img")
-    x, squeeze = _batch_view(img)
-    B, H, W = x.shape
+    x, squeeze = _batch_view(img, rgb)
+    B, H, W = x.shape[:3]
     if out is None:
         out = torch.empty((B, H, W), dtype=torch.int32, device=img.device)
     counts = torch.empty(B, dtype=torch.int32, device=img.device) if with_counts else None
     if workspace is None:
         workspace = _new_workspace(B, H, W, img.device)
     flags, ign = _flags(number, ignore)
-    _check(_load().ccl_label(_ptr(x), _dtype_code(x), B, H, W, int(connectivity), flags, ign,
+    _check(_load().ccl_label(_ptr(x), _dtype_code(x, rgb), B, H, W, int(connectivity), flags, ign,
                              _ptr(out), _ptr(counts), _ptr(workspace), workspace.numel(),
                              ctypes.c_void_p(_stream_handle(stream))))
     return (out[0] if squeeze else out), counts
@@ -185,6 +199,8 @@ class Labeller:
     allocate nothing (as a benchmark or a serving loop wants)."""
 
     def __init__(self, shape, device="cuda", connectivity: int = 8):
+        """``shape`` is the label shape, [H, W] or [B, H, W] (for an RGB picture,
+        its shape without the last dimension)."""
         if len(shape) == 2:
             shape = (1, *shape)
         self.B, self.H, self.W = (int(v) for v in shape)
@@ -194,13 +210,13 @@ class Labeller:
         self.workspace = _new_workspace(self.B, self.H, self.W, device)
 
     def __call__(self, img: torch.Tensor, number: bool = True, stream=None, events=None,
-                 ignore: int | None = None):
-        x, _ = _batch_view(img)
-        if tuple(x.shape) != (self.B, self.H, self.W):
+                 ignore: int | None = None, rgb: bool = False):
+        x, _ = _batch_view(img, rgb)
+        if tuple(x.shape[:3]) != (self.B, self.H, self.W):
             raise ValueError("image shape does not match the Labeller")
         lib = _load()
         flags, ign = _flags(number, ignore)
-        args = [_ptr(x), _dtype_code(x), self.B, self.H, self.W, self.connectivity,
+        args = [_ptr(x), _dtype_code(x, rgb), self.B, self.H, self.W, self.connectivity,
                 flags, ign, _ptr(self.out), _ptr(self.counts),
                 _ptr(self.workspace), self.workspace.numel(),
                 ctypes.c_void_p(_stream_handle(stream))]

@@ -111,10 +111,10 @@ static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int6
     bool empty;
     int rc = check_shape(B, H, W, &empty);
     if (rc != CCL_OK) return rc;
-    if (dtype != CCL_U8 && dtype != CCL_U32) return CCL_ERR_DTYPE;
+    if (dtype != CCL_U8 && dtype != CCL_RGB24 && dtype != CCL_U32) return CCL_ERR_DTYPE;
     if (conn != 4 && conn != 8) return CCL_ERR_CONNECTIVITY;
     const int ign = (flags & CCL_IGNORE) != 0;
-    if (ign && dtype == CCL_U8 && ignore > 0xFFu) return CCL_ERR_IGNORE;
+    if (ign && dtype != CCL_U32 && ignore >= (1u << (8 * dtype))) return CCL_ERR_IGNORE;
     if (events != nullptr && n_events < 6) return CCL_ERR_NULL;
     hipStream_t s = (hipStream_t)stream;
     if (empty) {
@@ -244,7 +244,7 @@ const char *ccl_status_string(int status)
     case CCL_ERR_SHAPE: return "batch, height or width is negative";
     case CCL_ERR_TOO_LARGE: return "image or batch too large to index";
     case CCL_ERR_CONNECTIVITY: return "connectivity must be 4 or 8";
-    case CCL_ERR_DTYPE: return "dtype must be CCL_U8 or CCL_U32";
+    case CCL_ERR_DTYPE: return "dtype must be CCL_U8, CCL_RGB24 or CCL_U32";
     case CCL_ERR_WORKSPACE: return "workspace smaller than ccl_workspace_bytes()";
     case CCL_ERR_HIP: return "HIP rejected a kernel launch";
     case CCL_ERR_FLAGS: return "unknown flag bits";

@@ -136,7 +136,7 @@ struct Layout {
 bool make_layout(int64_t B, int64_t H, int64_t W, Layout *L);
 Work bind_work(const Layout &L, void *workspace);
 
-// Launchers (enqueue only).  dtype_bytes is 1 or 4, conn is 4 or 8.
+// Launchers (enqueue only).  dtype_bytes is 1, 3 (RGB) or 4, conn is 4 or 8.
 // ignore: pixels of colour ign take part in nothing (their regions are neither
 // labelled nor counted)
 void launch_tile(const void *img, int dtype_bytes, int conn, int ignore, uint32_t ign,

@@ -427,6 +427,22 @@ __device__ __forceinline__ uint32_t left_requests(uint16_t *q, int y, uint64_t v
     return popc64(rul) + popc64(rl) + popc64(rdl);
 }
 
+// A pixel of an RGB picture as it is stored: three bytes, any alignment.  Its
+// colour value is b0 | b1 << 8 | b2 << 16 (b0 the first byte), so that pixels
+// are equal exactly when all three bytes are.
+struct Rgb24 {
+    uint8_t b[3];
+};
+static_assert(sizeof(Rgb24) == 3, "three bytes per RGB pixel");
+
+// colour value of a stored pixel
+__device__ __forceinline__ uint32_t px(uint8_t v) { return v; }
+__device__ __forceinline__ uint32_t px(uint32_t v) { return v; }
+__device__ __forceinline__ uint32_t px(const Rgb24 &v)
+{
+    return (uint32_t)v.b[0] | ((uint32_t)v.b[1] << 8) | ((uint32_t)v.b[2] << 16);
+}
+
 // The pixels one wave reads for a tile: its 8 rows (lane = column) and, for
 // wave 0, the halo: the row above the tile and the column to its left.
 struct TileIn {
@@ -448,19 +464,19 @@ __device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geo
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         if (FULL)  // a uniform base and a 32-bit byte offset per lane
-            in.c[i] = (uint32_t)*(const T *)((const char *)rows +
-                                             (uint32_t)(((uint32_t)i * W + lane) * sizeof(T)));
+            in.c[i] = px(*(const T *)((const char *)rows +
+                                      (uint32_t)(((uint32_t)i * W + lane) * sizeof(T))));
         else
-            in.c[i] = (lane_ok && wave * RPW + i < vh) ? (uint32_t)rows[(uint32_t)i * W + lane] : 0u;
+            in.c[i] = (lane_ok && wave * RPW + i < vh) ? px(rows[(uint32_t)i * W + lane]) : 0u;
     }
     in.hrow = in.hm1 = in.hp1 = in.hleft = 0;
     if (wave == 0 && tp.ty > 0) {
         const T *up = im + ((y0 - 1u) * W + x0);
-        if (lane_ok) in.hrow = up[lane];
-        if (lane == 0 && tp.tx > 0) in.hm1 = up[-1];
-        if (lane == TW - 1 && x0 + TW < W) in.hp1 = up[TW];
+        if (lane_ok) in.hrow = px(up[lane]);
+        if (lane == 0 && tp.tx > 0) in.hm1 = px(up[-1]);
+        if (lane == TW - 1 && x0 + TW < W) in.hp1 = px(up[TW]);
     }
-    if (wave == 0 && tp.tx > 0 && lane < vh) in.hleft = im[(y0 + (uint32_t)lane) * W + x0 - 1u];
+    if (wave == 0 && tp.tx > 0 && lane < vh) in.hleft = px(im[(y0 + (uint32_t)lane) * W + x0 - 1u]);
     return in;
 }
 
@@ -1842,6 +1858,9 @@ void launch_tile(const void *img, int dtype_bytes, int conn, int ignore, uint32_
     if (dtype_bytes == 1) {
         if (conn == 8) launch_tile_t<uint8_t, 8>(img, ignore, ign, g, w, s);
         else launch_tile_t<uint8_t, 4>(img, ignore, ign, g, w, s);
+    } else if (dtype_bytes == 3) {
+        if (conn == 8) launch_tile_t<Rgb24, 8>(img, ignore, ign, g, w, s);
+        else launch_tile_t<Rgb24, 4>(img, ignore, ign, g, w, s);
     } else {
         if (conn == 8) launch_tile_t<uint32_t, 8>(img, ignore, ign, g, w, s);
         else launch_tile_t<uint32_t, 4>(img, ignore, ign, g, w, s);

@@ -54,15 +54,24 @@ typedef enum {
     CCL_ERR_TOO_LARGE = -3,     /* height*width > 2^31-1, or the batch needs more
                                    than 2^32 seam nodes (about 47 Gpx in all)        */
     CCL_ERR_CONNECTIVITY = -4,  /* connectivity is not 4 or 8                        */
-    CCL_ERR_DTYPE = -5,         /* dtype is not CCL_U8 or CCL_U32                    */
+    CCL_ERR_DTYPE = -5,         /* dtype is not CCL_U8, CCL_RGB24 or CCL_U32         */
     CCL_ERR_WORKSPACE = -6,     /* workspace smaller than ccl_workspace_bytes()      */
     CCL_ERR_HIP = -7,           /* HIP rejected a kernel launch                      */
     CCL_ERR_FLAGS = -8,         /* unknown bits in flags                             */
-    CCL_ERR_IGNORE = -9         /* CCL_IGNORE with a value above 255 for CCL_U8      */
+    CCL_ERR_IGNORE = -9         /* CCL_IGNORE with a value wider than the pixel:
+                                   above 255 (CCL_U8) or 0xFFFFFF (CCL_RGB24)        */
 } ccl_status;
 
-/* Colour element types; the value is the size of one pixel in bytes. */
-enum { CCL_U8 = 1, CCL_U32 = 4 };
+/* Colour element types; the value is the size of one pixel in bytes.
+ *   CCL_U8     one byte per pixel
+ *   CCL_RGB24  three bytes per pixel, an RGB picture as it is stored: all three
+ *              bytes are compared, in place, with no packed copy ("Accountable
+ *              AI starts at the pixel", ch.08 "Tried and dropped" and ch.09
+ *              "Against NVIDIA's libraries").  Its colour value, where an
+ *              ignored colour is named, is b0 | b1 << 8 | b2 << 16, b0 the
+ *              pixel's first byte.
+ *   CCL_U32    one 32-bit word per pixel */
+enum { CCL_U8 = 1, CCL_RGB24 = 3, CCL_U32 = 4 };
 
 /* ccl_label flags.
  *   CCL_NUMBER  write numbers 1..n instead of leaders.
@@ -90,14 +99,15 @@ size_t ccl_workspace_bytes(int64_t batch, int64_t height, int64_t width);
  * Label a batch of colour images: Start, Connect, Collapse and (with
  * CCL_NUMBER) Number, the four stages of "Accountable AI starts at the pixel",
  * ch.05.
- *   colours       device, [batch, height, width] of uint8 (dtype CCL_U8) or
- *                 uint32 (CCL_U32)
+ *   colours       device, [batch, height, width] of uint8 (dtype CCL_U8),
+ *                 uint32 (CCL_U32) or three bytes (CCL_RGB24, any alignment)
  *   connectivity  8 (edges and corners) or 4 (edges only)
  *   flags         0: out[p] = leader of p (per-image reading-order index);
  *                 CCL_NUMBER: out[p] = number of p's region, 1..n per image;
  *                 | CCL_IGNORE: the colour `ignore` is ignored (see above)
  *   ignore        the ignored colour, used only with CCL_IGNORE (a whole stored
- *                 value; at most 255 for CCL_U8, else CCL_ERR_IGNORE)
+ *                 value; at most 255 for CCL_U8 and 0xFFFFFF for CCL_RGB24,
+ *                 else CCL_ERR_IGNORE)
  *   out           device int32 [batch, height, width]; must not overlap colours
  *   counts        device int32 [batch] or NULL: number of regions per image
  *   workspace     device, at least ccl_workspace_bytes(batch, height, width)

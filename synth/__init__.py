@@ -125,5 +125,16 @@ def generate(config: int) -> np.ndarray:
     return img[None]
 
 
+def rgb24(img: np.ndarray) -> np.ndarray:
+    """An 0x00RRGGBB picture (u32 [.., H, W]) stored as RGB bytes, uint8
+    [.., H, W, 3] in the order R, G, B: the same picture, three bytes a pixel."""
+    img = np.asarray(img, dtype=np.uint32)
+    out = np.empty(img.shape + (3,), dtype=np.uint8)
+    out[..., 0] = (img >> 16) & 0xFF
+    out[..., 1] = (img >> 8) & 0xFF
+    out[..., 2] = img & 0xFF
+    return out
+
+
 def sha256(a: np.ndarray) -> str:
     return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()

@@ -77,6 +77,9 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
     ((4, 1, 8, 8, 8, 3, 0, 16), -6),               # ... with an ignored colour too
     ((1, 1, 8, 8, 8, 2, 256, 1 << 30), -9),        # ignored colour wider than a byte
     ((1, 1, 8, 8, 8, 3, 0xFFFFFFFF, 1 << 30), -9),
+    ((3, 1, 8, 8, 8, 2, 0x1000000, 1 << 30), -9),  # ... wider than three bytes
+    ((3, 1, 8, 8, 5, 2, 0xFFFFFF, 1 << 30), -4),
+    ((3, 1, 8, 8, 8, 2, 0xFFFFFF, 16), -6),        # an RGB picture passes the dtype check
 ])
 def test_label_validation(lib, args, status):
     dtype, B, H, W, conn, flags, ign, wsb = args

@@ -253,6 +253,75 @@ def test_ignore_workload_full_size(ccl, config):
           f"{counts[:4].tolist()}", flush=True)
 
 
+# ------------------------------------------------- RGB pictures, three bytes
+
+def check_rgb(ccl, name, img, conn=8, ignore=None):
+    """An RGB picture ([.., H, W, 3] uint8) labelled in place against the oracle."""
+    announce(f"rgb {name}", img, conn, ignore)
+    exp_leaders = oracle.label(img, conn, ignore=ignore, rgb=True)
+    exp_labels, exp_counts = oracle.number(exp_leaders)
+    t = torch.from_numpy(np.ascontiguousarray(img)).cuda()
+    leaders, c0 = ccl.label(t, conn, number=False, ignore=ignore, rgb=True)
+    labels, c1 = ccl.label(t, conn, number=True, ignore=ignore, rgb=True)
+    torch.cuda.synchronize()
+    got = leaders.cpu().numpy()
+    if not np.array_equal(got, exp_leaders):
+        bad = np.argwhere(got != exp_leaders)
+        raise AssertionError(f"rgb {name}: leaders differ at {len(bad)} pixels, first {bad[:5].tolist()}")
+    assert np.array_equal(labels.cpu().numpy(), exp_labels), f"rgb {name}: numbers differ"
+    assert np.array_equal(c0.cpu().numpy(), exp_counts) and np.array_equal(c1.cpu().numpy(), exp_counts)
+    return exp_counts
+
+
+def rgb_palette_image(rng, shape, ncol):
+    """Colours that differ from one another in one byte only (each byte decides)."""
+    base = rng.integers(0, 256, size=3)
+    pal = np.tile(base, (ncol, 1))
+    for k in range(1, ncol):
+        pal[k, k % 3] = (base[k % 3] + 37 * k) % 256
+    return pal[rng.integers(0, ncol, size=shape)].astype(np.uint8)
+
+
+@pytest.mark.parametrize("conn", [8, 4])
+def test_rgb_ragged_random(ccl, conn):
+    """Ragged shapes, rows of every alignment (3*W mod 4), with and without an
+    ignored colour."""
+    rng = np.random.default_rng(300 + conn)
+    for H in HS:
+        for W in WS:
+            img = rgb_palette_image(rng, (H, W), int(rng.integers(1, 5)))
+            check_rgb(ccl, f"random {H}x{W}", img, conn)
+            px = img[int(rng.integers(0, H)), int(rng.integers(0, W))]
+            ign = int(px[0]) | (int(px[1]) << 8) | (int(px[2]) << 16)
+            check_rgb(ccl, f"random {H}x{W}", img, conn, ignore=ign)
+
+
+def test_rgb_structured_and_batch(ccl):
+    for name, img in list(structured_images().items()) + list(mosaic_images().items()):
+        if img.dtype != np.uint32:
+            continue
+        rgb = synth.rgb24(img)
+        check_rgb(ccl, name, rgb, 8)
+        # the same picture packed into 32 bits has the same regions
+        assert np.array_equal(oracle.label(rgb, 8, rgb=True), oracle.label(img, 8))
+    rng = np.random.default_rng(31)
+    check_rgb(ccl, "batch 3x70x131", rgb_palette_image(rng, (3, 70, 131), 3), 8)
+
+
+@pytest.mark.parametrize("config", [1, 3, 5])
+def test_rgb_workload_full_size(ccl, config):
+    """The colour workloads stored as RGB bytes at full size, with and without
+    the paper (most common colour) ignored."""
+    img = synth.generate(config)
+    p = most_common_colour(img)                     # 0x00RRGGBB
+    rgb = synth.rgb24(img)
+    del img
+    counts = check_rgb(ccl, f"workload {config}", rgb, 8)
+    paper = ((p >> 16) & 0xFF) | (((p >> 8) & 0xFF) << 8) | ((p & 0xFF) << 16)  # bytes R, G, B
+    check_rgb(ccl, f"workload {config}", rgb, 8, ignore=paper)
+    print(f"[gpu case] rgb workload {config} regions: {counts[:4].tolist()}", flush=True)
+
+
 # -------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
