@@ -13,10 +13,11 @@ between its launches on the benchmark's stream (ccl_label_profiled).  The CPU
 baseline runs the sequential oracle (single thread) on a band of the same
 sheet; the GPU labels that band too and must match it bit for bit.
 
-A second leg ("ignore_leg") times the same call with the paper colour (the
-sheet's most common value) ignored (CCL_IGNORE), as "Accountable AI starts at
-the pixel" ch.08 idea 4 runs it; it is reported beside the headline value,
-never as it.
+More legs are timed the same way and reported beside the headline value,
+never as it: "ignore_leg", the same call with the paper colour (the sheet's
+most common value) ignored (CCL_IGNORE, "Accountable AI starts at the pixel"
+ch.08 idea 4); "rgb24_leg", the same sheet stored as RGB bytes (3 B/px, read
+in place, same page ch.09), labelled whole and with the paper ignored.
 """
 from __future__ import annotations
 
@@ -101,6 +102,32 @@ def read_counter_csv(path: str, counter: str):
     return [(name, v) for (_, name), v in sorted(per.items())]
 
 
+def summarize_counters(csv_path: str):
+    """Per path kernel, the mean per dispatch of every counter in one rocprofv3
+    --pmc CSV (counter values summed over the dispatch's instances), as a
+    markdown table."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        k = (int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"])
+        per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    names = sorted({c for (_, _, c) in per})
+    acc = {}
+    for (_, kname, c), v in per.items():
+        short = kname.split("(")[0].replace("void ", "").replace("ccl::", "")
+        if "ccl::" not in kname:
+            continue
+        a = acc.setdefault(short, {}).setdefault(c, [])
+        a.append(v)
+    print("| kernel | dispatches | " + " | ".join(names) + " |")
+    print("|---|---|" + "---|" * len(names))
+    for short in sorted(acc):
+        n = max(len(v) for v in acc[short].values())
+        cells = [f"{sum(acc[short][c]) / len(acc[short][c]):.4g}" if c in acc[short] else "-"
+                 for c in names]
+        print(f"| `{short}` | {n} | " + " | ".join(cells) + " |")
+
+
 def write_traffic(fetch_csv: str, write_csv: str, copy_mb: int, launch_pixels: int):
     """HBM bytes per launch of each path kernel from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled by
@@ -160,14 +187,14 @@ def band_parity_ignore(img_np, rows: int, ignore: int, ccl, torch) -> bool:
                 np.array_equal(gc.cpu().numpy(), counts))
 
 
-def timed_steps(lab, dev, steps: int, stream, hip, torch, ignore=None):
+def timed_steps(lab, dev, steps: int, stream, hip, torch, ignore=None, rgb=False):
     """(ms per step by wall clock, mean stage ms from HIP events, median event ms)."""
     import numpy as np
     events = [hip.create(6) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(steps):
-        lab(dev, number=True, stream=stream, events=events[k], ignore=ignore)
+        lab(dev, number=True, stream=stream, events=events[k], ignore=ignore, rgb=rgb)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage_ms = {s: 0.0 for s in STAGES}
@@ -179,6 +206,26 @@ def timed_steps(lab, dev, steps: int, stream, hip, torch, ignore=None):
     for ev in events:
         hip.destroy(ev)
     return wall / steps * 1e3, stage_ms, float(np.median(step_ms))
+
+
+def extra_leg(lab, dev, npx, bpp, args, stream, hip, torch, ignore=None, rgb=False):
+    """One more timed leg of the labelled+numbered call (warm-up, then K steps)."""
+    for _ in range(args.warmup):
+        lab(dev, number=True, stream=stream, ignore=ignore, rgb=rgb)
+    ms, stage, event = timed_steps(lab, dev, args.steps, stream, hip, torch, ignore=ignore, rgb=rgb)
+    tile_gbs = npx * bpp / (stage["tile_label"] * 1e-3) / 1e9
+    return {
+        "ignore": None if ignore is None else f"0x{ignore:06x}",
+        "bytes_per_pixel": bpp,
+        "value": round(npx / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gpixels/s",
+        "ms_per_step": round(ms, 4),
+        "event_ms_per_step": round(event, 4),
+        "hbm_frac_path": round(npx * (bpp + 4) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "tile_label_GBps": round(tile_gbs, 1),
+        "stage_ms": {s: round(v, 4) for s, v in stage.items()},
+        "regions": lab.counts.cpu().tolist()[:4],
+    }
 
 
 def cpu_baseline(img_np, rows: int, ccl, torch):
@@ -218,8 +265,8 @@ def main():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=6000,
                     help="rows of the sheet the CPU baseline labels (0 = skip)")
-    ap.add_argument("--no-ignore-leg", action="store_true",
-                    help="skip the second leg (paper colour ignored)")
+    ap.add_argument("--no-extra-legs", action="store_true",
+                    help="time the headline call only (no paper-ignored or RGB legs)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -227,7 +274,13 @@ def main():
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
                          "WRITE_SIZE, both with --copy-calibration-mb) into profiles/traffic.json "
                          "and exit")
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="print the per-kernel mean per dispatch of every counter in a rocprofv3 "
+                         "--pmc CSV of this script and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.write_traffic:
         import synth
         _, (B, H, W), _, _ = synth.CONFIGS[args.config]
@@ -267,23 +320,22 @@ def main():
     counts = lab.counts.cpu().tolist()
 
     ignore_leg = None
+    rgb24_leg = None
     paper = None
-    if not args.no_ignore_leg:
+    if not args.no_extra_legs:
         paper = most_common_colour(img_np)
-        for _ in range(args.warmup):
-            lab(dev, number=True, stream=stream, ignore=paper)
-        ig_ms, ig_stage, ig_event = timed_steps(lab, dev, args.steps, stream, hip, torch,
-                                                ignore=paper)
+        ignore_leg = extra_leg(lab, dev, npx, bpp, args, stream, hip, torch, ignore=paper)
         print(f"[bench] ignore leg done ({args.steps} steps)", file=sys.stderr, flush=True)
-        ignore_leg = {
-            "ignore": f"0x{paper:06x}",
-            "value": round(npx / (ig_ms * 1e-3) / 1e9, 3),
-            "unit": "Gpixels/s",
-            "ms_per_step": round(ig_ms, 4),
-            "event_ms_per_step": round(ig_event, 4),
-            "stage_ms": {s: round(v, 4) for s, v in ig_stage.items()},
-            "regions": lab.counts.cpu().tolist()[:4],
-        }
+        if bpp == 4:
+            rgb_dev = torch.from_numpy(synth.rgb24(img_np)).cuda()
+            rgb_paper = ((paper >> 16) & 0xFF) | (((paper >> 8) & 0xFF) << 8) | ((paper & 0xFF) << 16)
+            rgb24_leg = {
+                "all_labelled": extra_leg(lab, rgb_dev, npx, 3, args, stream, hip, torch, rgb=True),
+                "paper_ignored": extra_leg(lab, rgb_dev, npx, 3, args, stream, hip, torch,
+                                           ignore=rgb_paper, rgb=True),
+            }
+            del rgb_dev
+            print(f"[bench] rgb24 legs done ({args.steps} steps each)", file=sys.stderr, flush=True)
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
         src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
@@ -346,6 +398,7 @@ def main():
         "cpu_baseline": cpu,
         "band_parity_bit_exact": exact,
         "ignore_leg": ignore_leg,
+        "rgb24_leg": rgb24_leg,
         "kernel_source": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
