@@ -451,6 +451,23 @@ struct TileIn {
     uint32_t hleft;           // wave 0: (y0+lane, x0-1)
 };
 
+// Lane p's pixel of a whole tile row of an RGB picture (64 pixels, 192 bytes
+// from `row`, any alignment): the lane loads the aligned dword holding its
+// pixel's first byte and, when the three bytes cross into the next dword,
+// that one too (else the same dword again), and takes its bytes from the pair.
+// Every dword read holds a byte of the lane's pixel.
+__device__ __forceinline__ uint32_t load_row_rgb(const Rgb24 *row, int lane)
+{
+    const uint32_t m = (uint32_t)(uintptr_t)row & 3u;
+    // (pointer arithmetic, not integers, so the loads stay global ones)
+    const uint32_t *base = (const uint32_t *)((const char *)row - m);
+    const uint32_t o = m + 3u * (uint32_t)lane;  // byte of the lane's pixel from base
+    const uint32_t d = o >> 2, k = o & 3u;
+    const uint32_t lo = base[d];
+    const uint32_t hi = base[k >= 2u ? d + 1u : d];
+    return __builtin_amdgcn_alignbyte(hi, lo, k) & 0xFFFFFFu;
+}
+
 template <typename T, bool FULL>
 __device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geom &g,
                                             const TilePos &tp, int wave, int lane)
@@ -461,9 +478,12 @@ __device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geo
     const bool lane_ok = FULL || lane < vw;
     const T *im = img + (size_t)tp.b * (size_t)g.HW;
     const T *rows = im + ((y0 + (uint32_t)(wave * RPW)) * W + x0);
+    constexpr bool RGB_ROWS = FULL && std::is_same<T, Rgb24>::value;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
-        if (FULL)  // a uniform base and a 32-bit byte offset per lane
+        if constexpr (RGB_ROWS)
+            in.c[i] = load_row_rgb(rows + (uint32_t)i * W, lane);
+        else if constexpr (FULL)  // a uniform base and a 32-bit byte offset per lane
             in.c[i] = px(*(const T *)((const char *)rows +
                                       (uint32_t)(((uint32_t)i * W + lane) * sizeof(T))));
         else
@@ -472,7 +492,8 @@ __device__ __forceinline__ TileIn load_tile(const T *__restrict__ img, const Geo
     in.hrow = in.hm1 = in.hp1 = in.hleft = 0;
     if (wave == 0 && tp.ty > 0) {
         const T *up = im + ((y0 - 1u) * W + x0);
-        if (lane_ok) in.hrow = px(up[lane]);
+        if constexpr (RGB_ROWS) in.hrow = load_row_rgb(up, lane);
+        else if (lane_ok) in.hrow = px(up[lane]);
         if (lane == 0 && tp.tx > 0) in.hm1 = px(up[-1]);
         if (lane == TW - 1 && x0 + TW < W) in.hp1 = px(up[TW]);
     }
