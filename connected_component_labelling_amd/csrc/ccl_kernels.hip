@@ -1418,44 +1418,17 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
 
 // ------------------------------------------------------------------ scan
 // seg[] holds the leaders of each row segment (tile-major).  One workgroup per
-// tile row of tiles ("band"), in one pass: sum each tile row across the
-// band's tiles, take the leaders of all earlier bands of the image from the
-// bands before it (decoupled look-back: each band publishes its own total at
-// once, and its inclusive prefix as soon as it knows it), then give every
-// segment the leaders of all earlier rows plus those of the earlier segments
-// of its row.
+// tile row of tiles ("band"), in one pass.  Thread (y, g) owns tile row y of
+// a contiguous group g of the band's tiles (32 rows x 8 groups = 256 threads;
+// the 32 threads of a group read one tile's 32 counts, 128 contiguous bytes).
+// It sums its counts; the sums give, for each row, the leaders of the earlier
+// groups and of all earlier rows of the band; the leaders of all earlier
+// bands of the image come from a decoupled look-back (each band publishes its
+// own total at once and its inclusive prefix as soon as it knows it; one wave
+// inspects 64 earlier bands per step).  Then every segment gets its
+// exclusive prefix in reading order.
 
-// exclusive prefix over the workgroup of 32 values per thread (one per tile
-// row): vals[y] is replaced by its prefix; tot[y] receives the row's total
-__device__ void block_scan_rows(uint32_t (&vals)[TH], uint32_t (&tot)[TH], uint32_t *sW)
-{
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int y = 0; y < TH; ++y) {
-        uint32_t x = vals[y];
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t v = __shfl_up(x, d);
-            if (lane >= d) x += v;
-        }
-        if (lane == 63) sW[wave * TH + y] = x;
-        vals[y] = x - vals[y];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int y = 0; y < TH; ++y) {
-        uint32_t off = 0, sum = 0;
-#pragma unroll
-        for (int i = 0; i < NWAVES; ++i) {
-            const uint32_t s = sW[i * TH + y];
-            off += i < wave ? s : 0u;
-            sum += s;
-        }
-        vals[y] += off;
-        tot[y] = sum;
-    }
-    __syncthreads();
-}
+constexpr int SCAN_GROUPS = BLOCK / TH;  // tile groups per band
 
 // Band status word: (value << 32) | state; state 1: value = the band's own
 // leaders, state 2: value = the leaders of the band and all earlier bands of
@@ -1469,96 +1442,144 @@ __device__ __forceinline__ void band_publish(uint64_t *p, uint32_t state, uint32
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// With headers (the labelling path), a one-colour tile counts the leader bit
-// of its header in row 0 instead of its row-segment counts, which it never
-// wrote; ccl_number / ccl_count have no headers.  apply = 0 only counts.
+// Leaders of SCAN_U consecutive segments of tile row y (tiles t .. t+n-1, n <=
+// SCAN_U), all loads issued before any is used: with headers (the labelling
+// path), a one-colour tile counts the leader bit of its header in its row 0
+// and 0 in its other rows (it never wrote row-segment counts, so the count
+// read for it is not used); ccl_number / ccl_count have no headers.  uni[u]
+// tells whether tile t+u is a one-colour tile.
+constexpr int SCAN_U = 8;
+__device__ __forceinline__ void scan_counts(const Work &w, size_t t, uint32_t n, int y, int use_hdr,
+                                            uint32_t (&c)[SCAN_U], bool (&uni)[SCAN_U])
+{
+    uint32_t kind[SCAN_U], lead[SCAN_U];
+#pragma unroll
+    for (int u = 0; u < SCAN_U; ++u) {
+        kind[u] = lead[u] = c[u] = 0;
+        if ((uint32_t)u < n) {
+            if (use_hdr) {
+                kind[u] = w.hdr[t + u].kind;
+                lead[u] = w.hdr[t + u].lead;
+            }
+            c[u] = w.seg[(t + u) * TH + (size_t)y];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < SCAN_U; ++u) {
+        uni[u] = (kind[u] & KIND_UNIFORM) != 0;
+        if (uni[u]) c[u] = y == 0 ? lead[u] : 0u;
+    }
+}
+
+// apply = 0 only counts.
 __global__ __launch_bounds__(BLOCK) void scan_kernel(Geom g, Work w, int32_t *counts, int apply,
                                                      int use_hdr)
 {
-    __shared__ uint32_t sW[NWAVES * TH];
-    __shared__ uint32_t sPre;
+    __shared__ uint32_t sPart[TH][SCAN_GROUPS + 1];  // per row: each group's sum, then its prefix
+    __shared__ uint32_t sRowPre[TH + 1];             // leaders of the earlier rows; [TH]: the band's
+    __shared__ uint32_t sPre;                        // leaders of the earlier bands of the image
     const uint32_t band = blockIdx.x;  // b * nty + ty
     const uint32_t b = fast_div(band, g.divNty), ty = band - b * (uint32_t)g.nty;
     const size_t t0 = (size_t)b * g.tpi + (size_t)ty * g.ntx;
     const uint32_t ntx = (uint32_t)g.ntx;
-    // thread i handles the contiguous tiles [i*G, i*G + G) of the band
-    const uint32_t G = (ntx + BLOCK - 1) / BLOCK;
-    const uint32_t tx0 = threadIdx.x * G;
-    uint32_t acc[TH], tot[TH];
-#pragma unroll
-    for (int y = 0; y < TH; ++y) acc[y] = 0;
-    for (uint32_t j = 0; j < G && tx0 + j < ntx; ++j) {
-        if (use_hdr && (w.hdr[t0 + tx0 + j].kind & KIND_UNIFORM)) {
-            acc[0] += w.hdr[t0 + tx0 + j].lead;
-            continue;
-        }
-        const uint4 *p = (const uint4 *)(w.seg + (t0 + tx0 + j) * TH);
-#pragma unroll
-        for (int q = 0; q < TH / 4; ++q) {
-            const uint4 v = p[q];
-            acc[4 * q] += v.x;
-            acc[4 * q + 1] += v.y;
-            acc[4 * q + 2] += v.z;
-            acc[4 * q + 3] += v.w;
-        }
-    }
-    block_scan_rows(acc, tot, sW);
-    uint32_t total = 0;
-#pragma unroll
-    for (int y = 0; y < TH; ++y) total += tot[y];
+    const int y = threadIdx.x & (TH - 1), grp = threadIdx.x / TH;
+    const int lane = lane_id();
+    const uint32_t G = (ntx + SCAN_GROUPS - 1) / SCAN_GROUPS;
+    const uint32_t tx0 = min(ntx, (uint32_t)grp * G), tx1 = min(ntx, tx0 + G);
 
-    if (threadIdx.x == 0) {
-        uint64_t *st = w.bandst;
+    uint32_t sum = 0;
+    for (uint32_t tx = tx0; tx < tx1; tx += SCAN_U) {
+        uint32_t c[SCAN_U];
+        bool uni[SCAN_U];
+        scan_counts(w, t0 + tx, tx1 - tx, y, use_hdr, c, uni);
+#pragma unroll
+        for (int u = 0; u < SCAN_U; ++u) sum += c[u];
+    }
+    sPart[y][grp] = sum;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        // lane y < TH: the groups' prefixes in row y and the row's total, then
+        // the exclusive prefix over the rows
+        uint32_t tot = 0;
+        if (lane < TH) {
+#pragma unroll
+            for (int k = 0; k < SCAN_GROUPS; ++k) {
+                const uint32_t v = sPart[lane][k];
+                sPart[lane][k] = tot;
+                tot += v;
+            }
+        }
+        uint32_t x = tot;
+#pragma unroll
+        for (int d = 1; d < TH; d <<= 1) {
+            const uint32_t v = __shfl_up(x, d);
+            if (lane >= d) x += v;
+        }
+        if (lane < TH) sRowPre[lane] = x - tot;
+        if (lane == TH - 1) sRowPre[TH] = x;
+        __syncwarp();
+        const uint32_t total = __shfl(x, TH - 1);  // the band's leaders
+
+        // look-back: every lane of wave 0 takes part
         uint32_t pre = 0;
         if (ty == 0) {
-            band_publish(&st[band], BAND_PREFIX, total);
+            if (lane == 0) band_publish(&w.bandst[band], BAND_PREFIX, total);
         } else {
-            band_publish(&st[band], BAND_TOTAL, total);
-            // earlier bands of this image, nearest first, until one has its prefix
+            if (lane == 0) band_publish(&w.bandst[band], BAND_TOTAL, total);
+            uint32_t hi = band - 1;  // nearest band not yet added
+            uint32_t left = ty;      // earlier bands of the image not yet added: hi, hi-1, ...
             int budget = LOOKBACK_BUDGET;
-            for (uint32_t k = band - 1;; --k) {
-                uint64_t v;
-                while (((v = __hip_atomic_load(&st[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) &
-                        0xFFFFFFFFull) == 0 && --budget > 0)
+            while (true) {
+                // lane i looks at band hi - i, if that is still in the image
+                const bool in = (uint32_t)lane < left;
+                const uint64_t v = in ? __hip_atomic_load(&w.bandst[hi - (uint32_t)lane],
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                      : (uint64_t)BAND_PREFIX;  // before the image: prefix 0
+                const uint32_t state = (uint32_t)v;
+                const uint64_t pm = __ballot(state == BAND_PREFIX);
+                const uint64_t zm = __ballot(state == 0u);
+                const int near = pm ? (int)__builtin_ctzll(pm) : 63;  // last lane to add
+                if (zm & mask_le(near)) {  // a band up to there has not reported yet
+                    if (--budget <= 0) {   // never reported: flag it, do not wait
+                        if (lane == 0) set_err(w.err, ERR_LOOP);
+                        break;
+                    }
                     __builtin_amdgcn_s_sleep(1);
-                if (budget <= 0) {  // an earlier band never reported: flag it, do not wait
-                    set_err(w.err, ERR_LOOP);
-                    break;
+                    continue;
                 }
-                pre += (uint32_t)(v >> 32);
-                if ((uint32_t)v == BAND_PREFIX || k == band - ty) break;
+                uint32_t add = lane <= near ? (uint32_t)(v >> 32) : 0u;
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1) add += __shfl_xor(add, d);
+                pre += add;
+                if (pm) break;
+                hi -= 64u;  // no lane was past the image, so left >= 64
+                left -= 64u;
             }
-            band_publish(&st[band], BAND_PREFIX, pre + total);
+            if (lane == 0) band_publish(&w.bandst[band], BAND_PREFIX, pre + total);
         }
-        sPre = pre;
-        if (counts && ty == (uint32_t)g.nty - 1) counts[b] = (int32_t)(pre + total);
+        if (lane == 0) {
+            sPre = pre;
+            if (counts && ty == (uint32_t)g.nty - 1) counts[b] = (int32_t)(pre + total);
+        }
     }
     __syncthreads();
     if (!apply) return;
-    // leaders before each row of the band, then before this thread's tiles
-    uint32_t before = sPre;
+    // leaders before this thread's first segment, then along its tiles
+    uint32_t run = sPre + sRowPre[y] + sPart[y][grp];
+    for (uint32_t tx = tx0; tx < tx1; tx += SCAN_U) {
+        uint32_t c[SCAN_U];
+        bool uni[SCAN_U];
+        const size_t t = t0 + tx;
+        scan_counts(w, t, tx1 - tx, y, use_hdr, c, uni);
 #pragma unroll
-    for (int y = 0; y < TH; ++y) {
-        acc[y] += before;
-        before += tot[y];
-    }
-    for (uint32_t j = 0; j < G && tx0 + j < ntx; ++j) {
-        if (use_hdr && (w.hdr[t0 + tx0 + j].kind & KIND_UNIFORM)) {
-            TileHdr &h = w.hdr[t0 + tx0 + j];
-            h.pre = acc[0];  // leaders before the tile's first pixel
-            acc[0] += h.lead;
-            continue;
-        }
-        uint4 *p = (uint4 *)(w.seg + (t0 + tx0 + j) * TH);
-#pragma unroll
-        for (int q = 0; q < TH / 4; ++q) {
-            const uint4 v = p[q];
-            const uint4 o = make_uint4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
-            acc[4 * q] += v.x;
-            acc[4 * q + 1] += v.y;
-            acc[4 * q + 2] += v.z;
-            acc[4 * q + 3] += v.w;
-            p[q] = o;
+        for (int u = 0; u < SCAN_U; ++u) {
+            if (tx + (uint32_t)u >= tx1) break;
+            if (uni[u]) {
+                if (y == 0) w.hdr[t + u].pre = run;  // leaders before the tile's first pixel
+            } else {
+                w.seg[(t + u) * TH + (size_t)y] = run;
+            }
+            run += c[u];
         }
     }
 }
