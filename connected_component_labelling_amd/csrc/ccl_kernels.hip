@@ -1419,7 +1419,7 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
 // ------------------------------------------------------------------ scan
 // seg[] holds the leaders of each row segment (tile-major).  One workgroup per
 // tile row of tiles ("band"), in one pass.  Thread (y, g) owns tile row y of
-// a contiguous group g of the band's tiles (32 rows x 8 groups = 256 threads;
+// a contiguous group g of the band's tiles (32 rows x 32 groups = 1024 threads;
 // the 32 threads of a group read one tile's 32 counts, 128 contiguous bytes).
 // It sums its counts; the sums give, for each row, the leaders of the earlier
 // groups and of all earlier rows of the band; the leaders of all earlier
@@ -1428,7 +1428,8 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
 // inspects 64 earlier bands per step).  Then every segment gets its
 // exclusive prefix in reading order.
 
-constexpr int SCAN_GROUPS = BLOCK / TH;  // tile groups per band
+constexpr int SCAN_BLOCK = 1024;                // threads per band
+constexpr int SCAN_GROUPS = SCAN_BLOCK / TH;    // tile groups per band
 
 // Band status word: (value << 32) | state; state 1: value = the band's own
 // leaders, state 2: value = the leaders of the band and all earlier bands of
@@ -1472,7 +1473,7 @@ __device__ __forceinline__ void scan_counts(const Work &w, size_t t, uint32_t n,
 }
 
 // apply = 0 only counts.
-__global__ __launch_bounds__(BLOCK) void scan_kernel(Geom g, Work w, int32_t *counts, int apply,
+__global__ __launch_bounds__(SCAN_BLOCK) void scan_kernel(Geom g, Work w, int32_t *counts, int apply,
                                                      int use_hdr)
 {
     __shared__ uint32_t sPart[TH][SCAN_GROUPS + 1];  // per row: each group's sum, then its prefix
@@ -1925,7 +1926,7 @@ void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s)
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
                  hipStream_t s)
 {
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)g.nbands), dim3(BLOCK), 0, s, g, w, counts,
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)g.nbands), dim3(SCAN_BLOCK), 0, s, g, w, counts,
                        apply, use_hdr);
 }
 
