@@ -1014,8 +1014,12 @@ __device__ __forceinline__ uint32_t select_bit(const uint64_t (&u)[KMAX / 64], u
 // the one before it) costs LDS steps, not global round trips.
 constexpr int MB = 8;             // block side in tiles
 constexpr int BT = MB * MB;       // tiles per block
-constexpr int NODE_CAP = 3072;    // seam nodes of a block merged in LDS
-constexpr int REQ_CAP = 3072;     // seam requests of a block joined in LDS
+// LDS tables of a block (21 KB in all, so 7 blocks fit a CU).  On the sheet the
+// median block has 176 seam nodes and 5 % of blocks have more than 1536; those
+// join their requests with global unions instead.  Tables of 3072 (40 KB, 4
+// blocks per CU) made the merge 0.167 ms there, 1536 make it 0.153 ms.
+constexpr int NODE_CAP = 1536;    // seam nodes of a block merged in LDS
+constexpr int REQ_CAP = 1536;     // seam requests of a block joined in LDS
 static_assert(BT <= BLOCK, "one thread per tile of a block");
 
 // the workgroup's block: the tile number of its first tile, and how many of
