@@ -775,6 +775,10 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     }
     drain(true);
     lds_barrier();
+    // the join queues are free now: wave 0 leaves the halo column there for
+    // wave 1, which makes the left-edge seam requests
+    uint32_t *const s_hleft = s.Q[0];
+    if (wave == 0 && lane < TH) s_hleft[lane] = hleft;
 
     // ---- 3 Collapse; runs on an edge shared with another tile offer their
     //      edge position as the region's seam slot (the smallest wins)
@@ -827,14 +831,36 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         const uint32_t root = s.P[run] & PMASK;
         return 255u - (s.P[root] >> 16);
     };
+    // the last steps, spread over the waves: 3 the bottom row's seam slots, 2
+    // the right column's and the leader masks, 1 the left-edge requests, 0 the
+    // top-edge requests and the header
     if (has_bottom && wave == NWAVES - 1 && lane_ok) {
         const uint64_t mb = uniform64(s.Mask[TH - 1]);
         w.bslot[(size_t)t * TW + lane] = (uint8_t)seam_of(mbcnt_acc(mb >> 1, (uint32_t)((TH - 1) * 64)));
     }
-    if (has_right && wave == 2 && lane < vh)
-        w.rslot[t32 + lane] = (uint8_t)seam_of((uint32_t)(lane * 64) + popc64(s.Mask[lane]) - 1u);
+    if (wave == 2) {
+        if (has_right && lane < vh)
+            w.rslot[t32 + lane] = (uint8_t)seam_of((uint32_t)(lane * 64) + popc64(s.Mask[lane]) - 1u);
+        if (lane < TH) {  // rows past the image edge store 0
+            const uint64_t lead = s.Lead[lane];
+            w.leadmask[t32 + lane] = lead;
+            w.seg[t32 + lane] = popc64(lead);
+        }
+    }
+    if (wave == 1) {
+        uint32_t nleft = 0;
+        if (has_left) {
+            const bool valid = lane < vh;
+            const uint32_t me = valid ? seam_of((uint32_t)(lane * 64)) : 0u;
+            const uint32_t cur = valid ? s.ColC[lane] : 0u;
+            nleft = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, lane,
+                                        (1ull << vh) - 1ull, me, cur, lane < TH ? s_hleft[lane] : 0u,
+                                        IGN ? ~__ballot(valid && cur == ign) : ~0ull);
+        }
+        if (lane == 4) ((uint32_t *)&hdr)[4] = nleft;  // the header's word 4
+    }
     if (wave == 0) {
-        uint32_t ntop = 0, nleft = 0;
+        uint32_t ntop = 0;
         if (has_top) {
             const uint64_t m0 = uniform64(s.Mask[0]);
             const uint32_t me = seam_of(mbcnt_acc(m0 >> 1, 0u));  // region of the lane's run
@@ -842,16 +868,8 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
                                       c[0], m0, me, hrow, hm1, hp1,
                                       IGN ? ~uniform64(s.Ign[0]) : ~0ull);
         }
-        if (has_left) {
-            const bool valid = lane < vh;
-            const uint32_t me = valid ? seam_of((uint32_t)(lane * 64)) : 0u;
-            const uint32_t cur = valid ? s.ColC[lane] : 0u;
-            nleft = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, lane,
-                                        (1ull << vh) - 1ull, me, cur, hleft,
-                                        IGN ? ~__ballot(valid && cur == ign) : ~0ull);
-        }
-        // the header in one store (the one-colour fields stay 0); the first
-        // eight bytes also give the final write the bounds of its reads
+        // the header (the one-colour fields stay 0; word 4 comes from wave 1);
+        // the first eight bytes also give the final write the bounds of its reads
         const uint32_t nslots = s.Used[2] ? 128u + 64u - (uint32_t)__builtin_clzll(s.Used[2])
                               : s.Used[1] ? 64u + 64u - (uint32_t)__builtin_clzll(s.Used[1])
                               : s.Used[0] ? 64u - (uint32_t)__builtin_clzll(s.Used[0]) : 0u;
@@ -860,13 +878,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         v = write_lane(v, R, 1);
         v = write_lane(v, R, 2);
         v = write_lane(v, ntop, 3);
-        v = write_lane(v, nleft, 4);
-        if (lane < (int)(sizeof(TileHdr) / 4)) ((uint32_t *)&hdr)[lane] = v;
-    }
-    if (tid >= 64 && tid < 64 + TH) {  // rows past the image edge store 0
-        const uint64_t lead = s.Lead[tid - 64];
-        w.leadmask[t32 + tid - 64] = lead;
-        w.seg[t32 + tid - 64] = popc64(lead);
+        if (lane < (int)(sizeof(TileHdr) / 4) && lane != 4) ((uint32_t *)&hdr)[lane] = v;
     }
 }
 
