@@ -51,8 +51,10 @@ typedef enum {
     CCL_OK = 0,
     CCL_ERR_NULL = -1,          /* a required pointer is NULL                        */
     CCL_ERR_SHAPE = -2,         /* batch, height or width is negative                */
-    CCL_ERR_TOO_LARGE = -3,     /* height*width > 2^31-1, or the batch needs more
-                                   than 2^32 seam nodes (about 47 Gpx in all)        */
+    CCL_ERR_TOO_LARGE = -3,     /* height*width > 2^31-1, or the batch has more
+                                   than 2^24 tiles: each image is cut into 64 x 32
+                                   tiles, a partial one at the right or bottom edge
+                                   counting whole (2^24 full tiles: 34 Gpx)          */
     CCL_ERR_CONNECTIVITY = -4,  /* connectivity is not 4 or 8                        */
     CCL_ERR_DTYPE = -5,         /* dtype is not CCL_U8, CCL_RGB24 or CCL_U32         */
     CCL_ERR_WORKSPACE = -6,     /* workspace smaller than ccl_workspace_bytes()      */

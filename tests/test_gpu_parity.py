@@ -331,6 +331,34 @@ def test_workload_full_size(ccl, config):
     print(f"[gpu case] workload {config} regions per image: {counts[:4].tolist()}", flush=True)
 
 
+# ------------------------------------------------------------ maximum size
+
+def max_size_image(H: int, W: int) -> np.ndarray:
+    """Diagonal bands crossed by a coarse checker, with a vertical line every
+    4099 columns: regions that run through thousands of tiles, diagonal
+    contacts, at every tile position of a maximum-size image (built in row
+    chunks of 32-bit arithmetic)."""
+    img = np.empty((H, W), np.uint8)
+    x = np.arange(W, dtype=np.int32)[None, :]
+    for y0 in range(0, H, 2048):
+        y = np.arange(y0, min(H, y0 + 2048), dtype=np.int32)[:, None]
+        a = ((x * 3 + y * 5) // 211) & 1
+        b = ((x // 997) + (y // 613)) & 1
+        img[y0:y0 + y.shape[0]] = ((a ^ b) + 2 * (x % 4099 == 0)).astype(np.uint8)
+    return img
+
+
+def test_maximum_size_image(ccl):
+    """46340 x 46340 (2^31 - 87887 pixels, the largest square whose reading-order
+    indices fit int32): leaders, numbers and counts bit-exact with the oracle,
+    so no index of the path overflows at the limit."""
+    H = W = 46340
+    assert H * W <= 2**31 - 1
+    img = max_size_image(H, W)
+    counts = check_case(ccl, "maximum size 46340x46340", img, 8)
+    print(f"[gpu case] maximum size regions: {counts.tolist()}", flush=True)
+
+
 # ----------------------------------------------------- standalone number/count
 
 def test_number_and_count_standalone(ccl):
