@@ -327,7 +327,10 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v)
 
 // v with lane i < 16 replaced by the wave-uniform value x: one v_writelane
 // (the lane is an inline constant, as the scalar data already takes the one
-// scalar operand an instruction may read; i is a constant once inlined)
+// scalar operand an instruction may read; i is a constant once inlined).  The
+// compiler sees an opaque per-lane operation, so this is used only for values
+// built in straight-line code and stored at once (tile headers), never for
+// values kept across divergent code.
 static_assert(RPW <= 16 && sizeof(TileHdr) / 4 <= 16, "write_lane covers lanes 0..15");
 __device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t x, int i)
 {
@@ -699,6 +702,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         uint32_t ca = 0, mea = 0;
         uint64_t sta = 0;
         uint32_t mlo = 0, mhi = 0;  // lane i collects row i's run starts
+        uint32_t ilo = 0, ihi = 0;  // ... and its pixels of the ignored colour
         uint32_t nw = 0;            // runs in the wave's rows so far
         uint16_t *run = s.Run + wave * (RPW * TW);
 #pragma unroll
@@ -716,17 +720,16 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
                 run[nw + me - (uint32_t)(y * 64)] = (uint16_t)me;
             }
             nw += popc64(st_m);
+            // lane i keeps row i's masks.  A select, not write_lane: these
+            // values live through the joins' divergent loops, and gathered with
+            // the inline-asm v_writelane (whose other lanes the compiler does
+            // not know it keeps) they came out wrong in one instance of this
+            // pass on MI355X; the select costs about 0.013 ms on the sheet.
+            mlo = lane == i ? (uint32_t)st_m : mlo;
+            mhi = lane == i ? (uint32_t)(st_m >> 32) : mhi;
             if (IGN) {
-                // plain stores by lane 0 (gathering these masks into lanes with
-                // write_lane, as the other instance does, gave wrong masks in
-                // this instance on MI355X; the cause was not found)
-                if (lane == 0) {
-                    s.Mask[y] = st_m;
-                    s.Ign[y] = ig_m;
-                }
-            } else {
-                mlo = write_lane(mlo, (uint32_t)st_m, i);
-                mhi = write_lane(mhi, (uint32_t)(st_m >> 32), i);
+                ilo = lane == i ? (uint32_t)ig_m : ilo;
+                ihi = lane == i ? (uint32_t)(ig_m >> 32) : ihi;
             }
             if (i > 0) {
                 join_rows(cc, st_m, me, ca, sta, mea, ig_m);
@@ -736,8 +739,8 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             sta = st_m;
             mea = me;
         }
-        if (!IGN && lane < RPW) s.Mask[wave * RPW + lane] = ((uint64_t)mhi << 32) | mlo;  // 0 past the image edge
-        if (IGN && lane < RPW && lane >= nrows) s.Mask[wave * RPW + lane] = 0ull;
+        if (lane < RPW) s.Mask[wave * RPW + lane] = ((uint64_t)mhi << 32) | mlo;  // 0 past the image edge
+        if (IGN && lane < RPW) s.Ign[wave * RPW + lane] = ((uint64_t)ihi << 32) | ilo;
         if (lane == 0) {
 #pragma unroll
             for (int i = 0; i < RPW; ++i) s.ColC[wave * RPW + i] = c[i];  // (0 past the image edge)
