@@ -57,6 +57,9 @@ def _bind(lib):
     lib.oracle_number.restype = ctypes.c_int
     lib.oracle_count.argtypes = [i32p, i64, i64, i64, i32p]
     lib.oracle_count.restype = ctypes.c_int
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_region_stats.argtypes = [i32p, i64, i64, i64, i32p, i32p, i32p, i64p, i64p]
+    lib.oracle_region_stats.restype = ctypes.c_int
     return lib
 
 
@@ -170,3 +173,28 @@ def label_and_number(img, connectivity: int = 8, lib=None, ignore=None, rgb: boo
     leaders = label(img, connectivity, lib, ignore=ignore, rgb=rgb)
     labels, counts = number(leaders, lib)
     return leaders, labels, counts
+
+
+def region_stats(labels, counts, lib=None) -> dict:
+    """Per-region area, bounding box (min row, min col, max row, max col) and
+    sums of row / column indices of a numbered label image, regions of all
+    images concatenated (image b's region k at sum(counts[:b]) + k - 1)."""
+    lib = lib or load()
+    L = np.ascontiguousarray(np.asarray(labels, dtype=np.int32))
+    if L.ndim == 2:
+        L = L[None]
+    B, H, W = L.shape
+    c = np.ascontiguousarray(np.asarray(counts, dtype=np.int32).reshape(-1))
+    if c.size != B:
+        raise ValueError("one count per image")
+    n = int(c.sum())
+    area = np.empty(n, np.int32)
+    bbox = np.empty((n, 4), np.int32)
+    sy = np.empty(n, np.int64)
+    sx = np.empty(n, np.int64)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    rc = lib.oracle_region_stats(_ptr(L), B, H, W, _ptr(c), _ptr(area), _ptr(bbox),
+                                 sy.ctypes.data_as(i64p), sx.ctypes.data_as(i64p))
+    if rc != 0:
+        raise ValueError(f"oracle_region_stats failed with status {rc}")
+    return {"area": area, "bbox": bbox, "sum_y": sy, "sum_x": sx}

@@ -35,7 +35,12 @@
  *   "About Connected Components Labeling on GPU" (TorchCC blog), "The basic
  *     approach: Union-Find" and "Application in CCL": Find / Union / Compress,
  *     the raster two-pass scan over already-visited neighbours, 4- and
- *     8-connectivity.
+ *     8-connectivity; its introduction names the uses of a labelling, such as
+ *     a region's bounding box.
+ *   The tissue-scan segmentation article, sections 1.1 and 2.3: each region's
+ *     area and position are summed over its pixels once it is numbered.
+ *     oracle_region_stats computes, per region, its area, bounding box and the
+ *     sums of its pixels' row and column indices (the position is sum / area).
  *
  * The BFS labeller below is an independent second algorithm (graph traversal,
  * the alternative that page names in "The basic approach") used to pin the
@@ -48,7 +53,7 @@
  * all three bytes of an RGB pixel.  An RGB pixel's colour value, as an ignored
  * colour is named, is b0 | b1 << 8 | b2 << 16 with b0 its first byte.
  *
- * Building with -DORACLE_MUTANT=k plants a deliberate mistake (k = 1..11) so the
+ * Building with -DORACLE_MUTANT=k plants a deliberate mistake (k = 1..13) so the
  * pin tests can show that they catch it.  The default build plants nothing.
  */
 #include <stdint.h>
@@ -335,5 +340,64 @@ int oracle_bfs_label(const void *img, int dtype, int64_t B, int64_t H, int64_t W
         }
     }
     free(queue);
+    return ORACLE_OK;
+}
+
+/* Per-region statistics of a numbered label image (labels 1..counts[b] per
+ * image b, 0 for pixels of no region).  Region k of image b is entry
+ * i = off[b] + k - 1, off[b] = counts[0] + ... + counts[b-1]:
+ *   area[i]          number of its pixels
+ *   bbox[4i .. 4i+3] smallest row, smallest column, largest row, largest
+ *                    column of its pixels
+ *   sum_y[i], sum_x[i]  sums of its pixels' row and column indices
+ * Entries of regions without pixels keep area 0, bbox (INT32_MAX, INT32_MAX,
+ * -1, -1) and sums 0.  A label outside [0, counts[b]] is an error. */
+int oracle_region_stats(const int32_t *labels, int64_t B, int64_t H, int64_t W,
+                        const int32_t *counts, int32_t *area, int32_t *bbox,
+                        int64_t *sum_y, int64_t *sum_x)
+{
+    if (B < 0 || H < 0 || W < 0 || counts == NULL) return ORACLE_ERR_ARG;
+    int64_t total = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        if (counts[b] < 0) return ORACLE_ERR_ARG;
+        total += counts[b];
+    }
+    if (total > 0 && (area == NULL || bbox == NULL || sum_y == NULL || sum_x == NULL))
+        return ORACLE_ERR_ARG;
+    for (int64_t i = 0; i < total; ++i) {
+        area[i] = 0;
+        bbox[4 * i] = bbox[4 * i + 1] = 2147483647;
+        bbox[4 * i + 2] = bbox[4 * i + 3] = -1;
+        sum_y[i] = sum_x[i] = 0;
+    }
+    const int64_t n = H * W;
+    int64_t off = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t *L = labels + b * n;
+        for (int64_t r = 0; r < H; ++r) {
+            for (int64_t c = 0; c < W; ++c) {
+                const int32_t k = L[r * W + c];
+                if (k == 0) continue;
+                if (k < 0 || k > counts[b]) return ORACLE_ERR_ARG;
+                const int64_t i = off + k - 1;
+                area[i] += 1;
+                if (r < bbox[4 * i]) bbox[4 * i] = (int32_t)r;
+                if (c < bbox[4 * i + 1]) bbox[4 * i + 1] = (int32_t)c;
+#if ORACLE_MUTANT == 12
+                if (r >= bbox[4 * i + 2]) bbox[4 * i + 2] = (int32_t)r + 1;  /* mutant: exclusive bottom */
+#else
+                if (r > bbox[4 * i + 2]) bbox[4 * i + 2] = (int32_t)r;
+#endif
+                if (c > bbox[4 * i + 3]) bbox[4 * i + 3] = (int32_t)c;
+                sum_y[i] += r;
+#if ORACLE_MUTANT == 13
+                sum_x[i] += r;                        /* mutant: row summed as column */
+#else
+                sum_x[i] += c;
+#endif
+            }
+        }
+        off += counts[b];
+    }
     return ORACLE_OK;
 }

@@ -15,6 +15,9 @@ given disagrees with:
     are 1..n in reading order, 0 for background) value for value,
   * for RGB pictures stored as three bytes per pixel (same page, ch.08-09): a
     flood fill comparing the three bytes as a tuple,
+  * per-region statistics: the hand-derived areas, boxes and index sums of the
+    TorchCC example's components, and scipy's find_objects / sum_labels /
+    center_of_mass on random labellings,
   * invariants of the definition (leader = region minimum, equal-colour
     neighbours share a leader, numbers are 1..n in reading order).
 
@@ -374,6 +377,62 @@ def pin_rgb_vs_python_bfs(lib, n_images=240, seed=18):
         assert np.array_equal(L[b], py_bfs(rgb_tuples(imgs[b]), 8))
 
 
+def pin_stats_torchcc_4x4(lib):
+    """Statistics of the TorchCC example's three components (background
+    ignored), against values worked out by hand from the page's labelling."""
+    fx = fixtures.load("torchcc_4x4_binary.txt")
+    img = fx["input"].astype(np.uint8)
+    labels, counts = oracle.number(oracle.label(img, 8, lib=lib, ignore=0), lib=lib)
+    st = oracle.region_stats(labels, counts, lib=lib)
+    ints = lambda k: [int(v) for v in fx[k].split()]
+    assert st["area"].tolist() == ints("stats_area")
+    assert st["bbox"].reshape(-1).tolist() == ints("stats_bbox")
+    assert st["sum_y"].tolist() == ints("stats_sum_y")
+    assert st["sum_x"].tolist() == ints("stats_sum_x")
+
+
+def pin_stats_vs_scipy(lib, seed=19, n_images=80):
+    """Area, bounding box and index sums of every region against scipy's
+    find_objects (boxes), sum_labels over ones and over the row / column index
+    grids (areas and sums, exact in float64 at these sizes) and center_of_mass,
+    with and without an ignored colour; a batch is concatenated image by image."""
+    rng = np.random.default_rng(seed)
+    for k in range(n_images):
+        H, W = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        img = random_images(rng, 1, H, W, int(rng.integers(1, 5)), np.uint8)[0]
+        ign = int(img.reshape(-1)[0]) if k % 2 else None
+        labels, counts = oracle.number(oracle.label(img, 8 if k % 3 else 4, lib=lib, ignore=ign),
+                                       lib=lib)
+        n = int(counts[0])
+        st = oracle.region_stats(labels, counts, lib=lib)
+        idx = np.arange(1, n + 1)
+        yy, xx = np.mgrid[0:H, 0:W]
+        ones = np.ones((H, W))
+        assert np.array_equal(st["area"], ndi.sum_labels(ones, labels, idx).astype(np.int64))
+        assert np.array_equal(st["sum_y"], ndi.sum_labels(yy, labels, idx).astype(np.int64))
+        assert np.array_equal(st["sum_x"], ndi.sum_labels(xx, labels, idx).astype(np.int64))
+        boxes = ndi.find_objects(labels, max_label=n)
+        none = [2147483647, 2147483647, -1, -1]  # a number with no pixels
+        exp = np.array([none if b is None else [b[0].start, b[1].start, b[0].stop - 1, b[1].stop - 1]
+                        for b in boxes], dtype=np.int64).reshape(-1, 4)
+        assert np.array_equal(st["bbox"], exp), f"case {k}: boxes"
+        if n:
+            with np.errstate(invalid="ignore", divide="ignore"):  # (a mutant's empty region)
+                com = np.array(ndi.center_of_mass(ones, labels, idx)).reshape(-1, 2)
+                got = np.stack([st["sum_y"] / st["area"], st["sum_x"] / st["area"]], axis=1)
+            assert np.allclose(got, com, rtol=0, atol=1e-9)
+    imgs = random_images(rng, 3, 12, 17, 3, np.uint8)
+    labels, counts = oracle.number(oracle.label(imgs, 8, lib=lib), lib=lib)
+    st = oracle.region_stats(labels, counts, lib=lib)
+    off = 0
+    for b in range(3):
+        one = oracle.region_stats(labels[b], counts[b:b + 1], lib=lib)
+        n = int(counts[b])
+        for key in ("area", "bbox", "sum_y", "sum_x"):
+            assert np.array_equal(st[key][off:off + n], one[key])
+        off += n
+
+
 # ---------------------------------------------------------------------------
 # closed forms and special cases
 
@@ -454,4 +513,6 @@ ALL_PINS = [
     pin_ignore_scipy_binary,
     pin_ignore_leaves_other_regions,
     pin_rgb_vs_python_bfs,
+    pin_stats_torchcc_4x4,
+    pin_stats_vs_scipy,
 ]
