@@ -27,8 +27,8 @@ import torch
 
 from . import build as _build
 
-__all__ = ["label", "number", "count", "workspace_bytes", "Labeller", "error_word",
-           "CclError", "library_path"]
+__all__ = ["label", "number", "count", "region_stats", "workspace_bytes", "Labeller",
+           "error_word", "CclError", "library_path"]
 
 CCL_U8, CCL_RGB24, CCL_U32 = 1, 3, 4
 CCL_NUMBER, CCL_IGNORE = 1, 2
@@ -64,6 +64,8 @@ def _load():
     lib.ccl_number.restype = ctypes.c_int
     lib.ccl_count.argtypes = [vp, i64, i64, i64, vp, vp, sz, vp]
     lib.ccl_count.restype = ctypes.c_int
+    lib.ccl_region_stats.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.ccl_region_stats.restype = ctypes.c_int
     lib.ccl_status_string.argtypes = [ctypes.c_int]
     lib.ccl_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -192,6 +194,36 @@ def count(leaders: torch.Tensor, stream=None, workspace: torch.Tensor | None = N
     _check(_load().ccl_count(_ptr(x), B, H, W, _ptr(counts), _ptr(workspace), workspace.numel(),
                              ctypes.c_void_p(_stream_handle(stream))))
     return counts
+
+
+def region_stats(labels: torch.Tensor, counts: torch.Tensor, n_total: int | None = None,
+                 stream=None, workspace: torch.Tensor | None = None) -> dict:
+    """Per-region area, bounding box (min row, min col, max row, max col) and sums
+    of row / column indices of a numbered labelling (label(..., number=True)),
+    regions of all images concatenated: image b's region k is entry
+    sum(counts[:b]) + k - 1.  ``n_total`` (the sum of ``counts``) is read from
+    the device when not given."""
+    _require_device(labels, "labels")
+    if labels.dtype != torch.int32 or counts.dtype != torch.int32:
+        raise TypeError("labels and counts must be int32")
+    x, _ = _batch_view(labels)
+    B, H, W = x.shape
+    if counts.numel() != B or not counts.is_cuda:
+        raise ValueError("counts must be a device tensor with one entry per image")
+    if n_total is None:
+        n_total = int(counts.to(torch.int64).sum().item())
+    dev = labels.device
+    area = torch.empty(n_total, dtype=torch.int32, device=dev)
+    bbox = torch.empty((n_total, 4), dtype=torch.int32, device=dev)
+    sum_y = torch.empty(n_total, dtype=torch.int64, device=dev)
+    sum_x = torch.empty(n_total, dtype=torch.int64, device=dev)
+    if workspace is None:
+        workspace = _new_workspace(B, H, W, dev)
+    _check(_load().ccl_region_stats(_ptr(x), B, H, W, _ptr(counts.contiguous()), n_total,
+                                    _ptr(area), _ptr(bbox), _ptr(sum_y), _ptr(sum_x),
+                                    _ptr(workspace), workspace.numel(),
+                                    ctypes.c_void_p(_stream_handle(stream))))
+    return {"area": area, "bbox": bbox, "sum_y": sum_y, "sum_x": sum_x}
 
 
 class Labeller:

@@ -1895,6 +1895,158 @@ __global__ void zero_i32_kernel(int32_t *p, int64_t n)
         p[i] = 0;
 }
 
+// ------------------------------------------------------ region statistics
+// Per-region area, bounding box and sums of row and column indices of a
+// numbered labelling.  One workgroup per area of ST_ROWS x ST_COLS pixels of
+// one image: each wave takes 64-pixel row segments of the area, finds their
+// runs of one label with a ballot, and adds each run to its label's entry in
+// a hash table in LDS (local coordinates: every sum fits 32 bits).  Then each
+// entry is added to the region's global statistics with one set of atomics,
+// so a region that covers the whole picture takes one set per area, not one
+// per pixel or per run.  A run whose label finds no free entry (the table
+// holds ST_CAP labels) goes to the global statistics at once.
+
+constexpr int ST_COLS = 512, ST_ROWS = 256;
+constexpr int ST_CAP = 1024;                       // labels per area in LDS
+constexpr int ST_SEGS = ST_COLS / TW;              // row segments per area row
+static_assert((ST_CAP & (ST_CAP - 1)) == 0, "the hash table size is a power of two");
+
+struct StatsArgs {
+    const int32_t *labels;
+    const int32_t *counts;
+    const int64_t *off;        // [B] first entry of each image
+    int32_t *area;
+    int32_t *bbox;
+    unsigned long long *sum_y;
+    unsigned long long *sum_x;
+    int64_t B, H, W, HW;
+    int64_t n_total;           // entries of the outputs
+    uint32_t ay, ax;           // areas per image column / row
+};
+
+__device__ __forceinline__ void stats_global(const StatsArgs &a, int64_t i, uint32_t n, uint64_t sy,
+                                             uint64_t sx, int32_t y0, int32_t x0, int32_t y1,
+                                             int32_t x1)
+{
+    atomicAdd(&a.area[i], (int32_t)n);
+    atomicAdd(&a.sum_y[i], (unsigned long long)sy);
+    atomicAdd(&a.sum_x[i], (unsigned long long)sx);
+    atomicMin(&a.bbox[4 * i], y0);
+    atomicMin(&a.bbox[4 * i + 1], x0);
+    atomicMax(&a.bbox[4 * i + 2], y1);
+    atomicMax(&a.bbox[4 * i + 3], x1);
+}
+
+__global__ __launch_bounds__(BLOCK) void stats_kernel(StatsArgs a)
+{
+    __shared__ uint32_t sKey[ST_CAP];                    // label, 0: free
+    __shared__ unsigned long long sNY[ST_CAP];           // area | (sum of local rows << 32)
+    __shared__ uint32_t sSX[ST_CAP];                     // sum of local columns
+    __shared__ uint32_t sY0[ST_CAP], sX0[ST_CAP], sY1[ST_CAP], sX1[ST_CAP];
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t per_img = a.ay * a.ax;
+    const uint32_t b = blockIdx.x / per_img, rem = blockIdx.x - b * per_img;
+    const uint32_t by = rem / a.ax, bx = rem - by * a.ax;
+    const int32_t Y0 = (int32_t)(by * ST_ROWS), X0 = (int32_t)(bx * ST_COLS);
+    const int32_t W = (int32_t)a.W, H = (int32_t)a.H;
+    const int32_t nrows = min(ST_ROWS, H - Y0), ncols = min(ST_COLS, W - X0);
+    const int32_t nmax = a.counts[b];
+    const int64_t off = a.off[b] - 1;                    // entry of label k: off + k
+    const int32_t *img = a.labels + (int64_t)b * a.HW;
+    for (int i = threadIdx.x; i < ST_CAP; i += BLOCK) {
+        sKey[i] = 0u;
+        sNY[i] = 0ull;
+        sSX[i] = 0u;
+        sY0[i] = sX0[i] = 0xFFFFFFFFu;
+        sY1[i] = sX1[i] = 0u;
+    }
+    __syncthreads();
+    // row segments of the area, dealt to the waves
+    const int nseg = nrows * ST_SEGS;
+    for (int sg = wave; sg < nseg; sg += NWAVES) {
+        const int ly = sg / ST_SEGS, lx0 = (sg - ly * ST_SEGS) * TW;  // local row, first column
+        const int lx = lx0 + lane;
+        const bool in = lx < ncols;
+        const int32_t v = in ? img[(int64_t)(Y0 + ly) * W + X0 + lx] : 0;
+        // runs of one label in the segment: lane L starts one where the label
+        // differs from lane L-1's (lane 0 always, if it has a pixel)
+        const uint64_t valid = __ballot(in);
+        const uint64_t st = (__ballot(from_left_lane((uint32_t)v) != (uint32_t)v) | 1ull) & valid;
+        if (!lane_bit(st) || v <= 0 || v > nmax || off + v >= a.n_total) continue;
+        // the run ends before the next start (or the last valid lane)
+        const uint64_t after = st & ~mask_le(lane);
+        const int end = after ? (int)__builtin_ctzll(after) - 1 : 63 - (int)__builtin_clzll(valid);
+        const uint32_t len = (uint32_t)(end - lane + 1);
+        const uint32_t sxl = len * (uint32_t)lx + len * (len - 1u) / 2u;   // local columns
+        // the label's entry: open addressing from a multiplicative hash
+        uint32_t h = ((uint32_t)v * 2654435761u) >> (32 - 10);
+        static_assert(ST_CAP == 1024, "the hash takes 10 bits");
+        int e = -1;
+        for (int p = 0; p < ST_CAP; ++p, h = (h + 1u) & (ST_CAP - 1)) {
+            const uint32_t k = sKey[h];
+            if (k == (uint32_t)v) { e = (int)h; break; }
+            if (k == 0u) {
+                const uint32_t old = atomicCAS(&sKey[h], 0u, (uint32_t)v);
+                if (old == 0u || old == (uint32_t)v) { e = (int)h; break; }
+            }
+        }
+        if (e < 0) {  // the table is full: straight to the region's statistics
+            stats_global(a, off + v, len, (uint64_t)len * (uint64_t)(Y0 + ly),
+                         (uint64_t)sxl + (uint64_t)len * (uint64_t)X0, Y0 + ly, X0 + lx, Y0 + ly,
+                         X0 + end + lx0);
+            continue;
+        }
+        atomicAdd(&sNY[e], (unsigned long long)len | ((unsigned long long)(len * (uint32_t)ly) << 32));
+        atomicAdd(&sSX[e], sxl);
+        atomicMin(&sY0[e], (uint32_t)ly);
+        atomicMin(&sX0[e], (uint32_t)lx);
+        atomicMax(&sY1[e], (uint32_t)ly);
+        atomicMax(&sX1[e], (uint32_t)(lx0 + end));
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < ST_CAP; i += BLOCK) {
+        const uint32_t k = sKey[i];
+        if (k == 0u) continue;
+        const unsigned long long ny = sNY[i];
+        const uint32_t n = (uint32_t)ny, syl = (uint32_t)(ny >> 32);
+        stats_global(a, off + (int64_t)k, n, (uint64_t)syl + (uint64_t)n * (uint64_t)Y0,
+                     (uint64_t)sSX[i] + (uint64_t)n * (uint64_t)X0, Y0 + (int32_t)sY0[i],
+                     X0 + (int32_t)sX0[i], Y0 + (int32_t)sY1[i], X0 + (int32_t)sX1[i]);
+    }
+}
+
+// Entries of every region start empty (area 0, box (INT32_MAX, INT32_MAX, -1,
+// -1), sums 0); block 0 also writes the first entry of each image.
+__global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t n_total,
+                                                           int64_t *off)
+{
+    for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < n_total;
+         i += (int64_t)gridDim.x * BLOCK) {
+        a.area[i] = 0;
+        a.bbox[4 * i] = a.bbox[4 * i + 1] = 2147483647;
+        a.bbox[4 * i + 2] = a.bbox[4 * i + 3] = -1;
+        a.sum_y[i] = a.sum_x[i] = 0ull;
+    }
+    if (blockIdx.x != 0) return;
+    // exclusive prefix of the counts: thread j sums its chunk, a workgroup scan
+    // of the chunk sums, then each thread writes its chunk's prefixes
+    __shared__ uint32_t sWave[NWAVES];
+    const int64_t B = a.B;
+    const int64_t per = (B + BLOCK - 1) / BLOCK;
+    const int64_t j0 = (int64_t)threadIdx.x * per, j1 = min(B, j0 + per);
+    int64_t sum = 0;
+    for (int64_t j = j0; j < j1; ++j) sum += a.counts[j];
+    // (the counts of one batch add up to fewer than 2^32 regions: each needs a
+    // pixel and a batch has fewer than 2^24 tiles of 2048 pixels)
+    uint32_t total;
+    const uint32_t ex = block_exclusive_scan((uint32_t)sum, sWave, total);
+    int64_t run = ex;
+    for (int64_t j = j0; j < j1; ++j) {
+        off[j] = run;
+        run += a.counts[j];
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
 static inline unsigned grid_of(int64_t n, int64_t per)
@@ -1978,6 +2130,34 @@ void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(leader_assign_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, leaders,
                        labels, g, w);
+}
+
+void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geom &g,
+                         const Work &w, int64_t n_total, int32_t *area, int32_t *bbox,
+                         int64_t *sum_y, int64_t *sum_x, hipStream_t s)
+{
+    StatsArgs a;
+    a.labels = labels;
+    a.counts = counts;
+    a.off = (const int64_t *)w.bandst;
+    a.area = area;
+    a.bbox = bbox;
+    a.sum_y = (unsigned long long *)sum_y;
+    a.sum_x = (unsigned long long *)sum_x;
+    a.B = g.B;
+    a.H = g.H;
+    a.W = g.W;
+    a.HW = g.HW;
+    a.n_total = n_total;
+    a.ay = (uint32_t)((g.H + ST_ROWS - 1) / ST_ROWS);
+    a.ax = (uint32_t)((g.W + ST_COLS - 1) / ST_COLS);
+    int64_t iblocks = grid_of(n_total, BLOCK);
+    if (iblocks > 4096) iblocks = 4096;
+    if (iblocks < 1) iblocks = 1;
+    hipLaunchKernelGGL(stats_init_kernel, dim3((unsigned)iblocks), dim3(BLOCK), 0, s, a, n_total,
+                       (int64_t *)w.bandst);
+    const int64_t blocks = g.B * (int64_t)a.ay * (int64_t)a.ax;
+    hipLaunchKernelGGL(stats_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
 }
 
 void launch_zero_i32(int32_t *p, int64_t n, hipStream_t s)

@@ -156,6 +156,36 @@ int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t wi
 int ccl_count(const int32_t *leaders, int64_t batch, int64_t height, int64_t width,
               int32_t *counts, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Per-region statistics of a numbered labelling (as written by ccl_label with
+ * CCL_NUMBER, or by ccl_number): for each region, its area, its bounding box
+ * and the sums of its pixels' row and column indices, from which its position
+ * (centroid) is sum / area.  Computing such statistics over the regions is the
+ * step after labelling ("About Connected Components Labeling on GPU",
+ * introduction: bounding boxes; the tissue-scan segmentation article, section
+ * 1.1: area and position of each numbered region, section 2.3: sums over a
+ * region's pixels as a global reduction).
+ *   labels   device int32 [batch, height, width]: region numbers 1..counts[b]
+ *            in image b, 0 for a pixel of no region (an ignored colour).  Other
+ *            values are skipped.
+ *   counts   device int32 [batch]: regions per image (as ccl_label wrote them)
+ *   n_total  host: counts[0] + ... + counts[batch-1], the number of entries of
+ *            each output; entries past it are never written
+ *   Region k of image b is entry i = counts[0] + ... + counts[b-1] + k - 1 of
+ *   area     device int32 [n_total]: its pixels
+ *   bbox     device int32 [n_total, 4]: smallest row, smallest column, largest
+ *            row, largest column of its pixels (inclusive)
+ *   sum_y, sum_x  device int64 [n_total]: sums of its pixels' row / column
+ *            indices (exact)
+ * Every entry is written: a number with no pixel keeps area 0, box
+ * (INT32_MAX, INT32_MAX, -1, -1) and sums 0.  The workspace is the one of
+ * ccl_workspace_bytes(batch, height, width).
+ */
+int ccl_region_stats(const int32_t *labels, int64_t batch, int64_t height, int64_t width,
+                     const int32_t *counts, int64_t n_total, int32_t *area, int32_t *bbox,
+                     int64_t *sum_y, int64_t *sum_x, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
 /* Static text for a status code (never NULL). */
 const char *ccl_status_string(int status);
 

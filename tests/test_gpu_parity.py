@@ -331,6 +331,62 @@ def test_workload_full_size(ccl, config):
     print(f"[gpu case] workload {config} regions per image: {counts[:4].tolist()}", flush=True)
 
 
+# ------------------------------------------------------ region statistics
+
+def check_stats(ccl, name, img, conn=8, ignore=None, rgb=False):
+    """Per-region statistics on the GPU (of the GPU's own numbers, and of the
+    oracle's numbers uploaded) equal the oracle's, entry for entry."""
+    announce(f"stats {name}", img, conn, ignore)
+    exp_labels, exp_counts = oracle.number(oracle.label(img, conn, ignore=ignore, rgb=rgb))
+    exp = oracle.region_stats(exp_labels, exp_counts)
+    t = torch.from_numpy(np.ascontiguousarray(img.view(np.int32) if img.dtype == np.uint32 else img)).cuda()
+    labels, counts = ccl.label(t, conn, number=True, ignore=ignore, rgb=rgb)
+    got = ccl.region_stats(labels, counts)
+    up = torch.from_numpy(np.ascontiguousarray(exp_labels)).cuda()
+    got2 = ccl.region_stats(up, torch.from_numpy(np.ascontiguousarray(exp_counts)).cuda(),
+                            n_total=int(exp_counts.sum()))
+    torch.cuda.synchronize()
+    for key in ("area", "bbox", "sum_y", "sum_x"):
+        for g in (got, got2):
+            a = g[key].cpu().numpy()
+            if not np.array_equal(a, exp[key]):
+                bad = np.argwhere(a.reshape(len(a), -1) != exp[key].reshape(len(a), -1))
+                raise AssertionError(f"stats {name}: {key} differs at {len(bad)} entries, "
+                                     f"first {bad[:3].tolist()}")
+    return exp_counts
+
+
+@pytest.mark.parametrize("conn", [8, 4])
+def test_stats_ragged_random(ccl, conn):
+    """Shapes around the 512 x 256 areas of the statistics pass and the tiles."""
+    rng = np.random.default_rng(400 + conn)
+    for H, W in [(1, 1), (3, 700), (255, 513), (256, 512), (257, 511), (300, 1100), (70, 90)]:
+        img = rng.integers(0, 3, size=(H, W)).astype(np.uint8)
+        check_stats(ccl, f"random {H}x{W}", img, conn)
+        check_stats(ccl, f"random {H}x{W}", img, conn, ignore=0)
+
+
+def test_stats_structured_batch_and_overflow(ccl):
+    for name, img in structured_images().items():
+        check_stats(ccl, name, img, 8)
+    for name, img in mosaic_images().items():
+        check_stats(ccl, name, img, 8, ignore=7)
+    check_stats(ccl, "bernoulli batch 5x100x90", synth.bernoulli_batch(5, 100, 90, seed=9), 8)
+    # a 4-connected checkerboard: every pixel a region, 131072 labels in one
+    # 512 x 256 area, far past the LDS table
+    yy, xx = np.mgrid[0:300, 0:600]
+    check_stats(ccl, "checkerboard 300x600 (every pixel a region)", ((yy + xx) % 2).astype(np.uint8), 4)
+    rgb = synth.rgb24(synth.lines_image(256, 256, seed=1))
+    check_stats(ccl, "rgb drawing", rgb, 8, rgb=True)
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+def test_stats_workload_full_size(ccl, config):
+    img = synth.generate(config)
+    counts = check_stats(ccl, f"workload {config}: {synth.CONFIGS[config][0]}", img, 8)
+    print(f"[gpu case] stats workload {config}: {int(counts.sum())} regions", flush=True)
+
+
 # ------------------------------------------------------------ maximum size
 
 def max_size_image(H: int, W: int) -> np.ndarray:
