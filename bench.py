@@ -17,7 +17,9 @@ More legs are timed the same way and reported beside the headline value,
 never as it: "ignore_leg", the same call with the paper colour (the sheet's
 most common value) ignored (CCL_IGNORE, "Accountable AI starts at the pixel"
 ch.08 idea 4); "rgb24_leg", the same sheet stored as RGB bytes (3 B/px, read
-in place, same page ch.09), labelled whole and with the paper ignored.
+in place, same page ch.09), labelled whole and with the paper ignored;
+"stats_leg", the per-region statistics pass over the sheet's numbers (with
+HIP events around its two kernels; it reads 4 B/px of labels).
 """
 from __future__ import annotations
 
@@ -228,6 +230,42 @@ def extra_leg(lab, dev, npx, bpp, args, stream, hip, torch, ignore=None, rgb=Fal
     }
 
 
+def stats_leg(ccl, labels, counts, npx, steps, warmup, stream, hip, torch):
+    """Time ccl_region_stats over a numbered labelling (outputs and workspace
+    allocated once, before the timed calls)."""
+    import numpy as np
+    B, H, W = labels.shape
+    n_total = int(counts.to(torch.int64).sum().item())
+    dev = labels.device
+    ws = torch.zeros(ccl.workspace_bytes(B, H, W), dtype=torch.uint8, device=dev)
+    outs = [torch.empty(n_total, dtype=torch.int32, device=dev),
+            torch.empty((n_total, 4), dtype=torch.int32, device=dev),
+            torch.empty(n_total, dtype=torch.int64, device=dev),
+            torch.empty(n_total, dtype=torch.int64, device=dev)]
+    lib = ccl._load()
+    args = [ccl._ptr(labels), B, H, W, ccl._ptr(counts), n_total] + [ccl._ptr(o) for o in outs] + \
+           [ccl._ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream)]
+    for _ in range(warmup):
+        ccl._check(lib.ccl_region_stats(*args))
+    ev = hip.create(2 * steps)
+    torch.cuda.synchronize()
+    for k in range(steps):
+        hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k]), ctypes.c_void_p(stream.cuda_stream))
+        ccl._check(lib.ccl_region_stats(*args))
+        hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k + 1]), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms = float(np.median([hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]) for k in range(steps)]))
+    hip.destroy(ev)
+    return {
+        "regions": n_total,
+        "ms_per_call": round(ms, 4),
+        "value": round(npx / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gpixels/s",
+        "label_read_GBps": round(npx * 4 / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(npx * 4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
 def cpu_baseline(img_np, rows: int, ccl, torch):
     """Oracle (one thread) on the first `rows` rows of the sheet, and the GPU on
     the same band for a bit-exact check."""
@@ -321,8 +359,13 @@ def main():
 
     ignore_leg = None
     rgb24_leg = None
+    stats = None
     paper = None
     if not args.no_extra_legs:
+        hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        stats = stats_leg(ccl, lab.out, lab.counts, npx, args.steps, args.warmup, stream, hip,
+                          torch)
+        print(f"[bench] stats leg done ({args.steps} calls)", file=sys.stderr, flush=True)
         paper = most_common_colour(img_np)
         ignore_leg = extra_leg(lab, dev, npx, bpp, args, stream, hip, torch, ignore=paper)
         print(f"[bench] ignore leg done ({args.steps} steps)", file=sys.stderr, flush=True)
@@ -399,6 +442,7 @@ def main():
         "band_parity_bit_exact": exact,
         "ignore_leg": ignore_leg,
         "rgb24_leg": rgb24_leg,
+        "stats_leg": stats,
         "kernel_source": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

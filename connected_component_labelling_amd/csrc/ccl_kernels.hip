@@ -1898,17 +1898,30 @@ __global__ void zero_i32_kernel(int32_t *p, int64_t n)
 // ------------------------------------------------------ region statistics
 // Per-region area, bounding box and sums of row and column indices of a
 // numbered labelling.  One workgroup per area of ST_ROWS x ST_COLS pixels of
-// one image: each wave takes 64-pixel row segments of the area, finds their
-// runs of one label with a ballot, and adds each run to its label's entry in
-// a hash table in LDS (local coordinates: every sum fits 32 bits).  Then each
-// entry is added to the region's global statistics with one set of atomics,
-// so a region that covers the whole picture takes one set per area, not one
-// per pixel or per run.  A run whose label finds no free entry (the table
-// holds ST_CAP labels) goes to the global statistics at once.
+// one image, taken in chunks of ST_CHUNK rows: each wave takes 64-pixel row
+// segments, finds their runs of one label with a ballot, and adds each run to
+// its label's entry in a hash table in LDS (local coordinates: every sum fits
+// 32 bits).  A segment that is one run adds to a wave-uniform sum for its
+// label instead (paper, the inside of large regions: one table update per
+// change of label, not per segment).  Entries leave the table at the end of
+// the area, or after a chunk once the table is half full (anti-aliased glyph
+// rows put up to 20,000 labels in one area of the sheet):
+//   - a region that touches no side of the area shared with another area,
+//     not the last row taken so far, and that is not the continuation of an
+//     entry already written out (its first row is not the row right after the
+//     last clearing) is complete: its entry is stored with plain stores;
+//   - any other entry is added to the region's statistics with atomics, so a
+//     region that covers the whole picture takes one set per area.
+// A run whose label finds neither its entry nor a free slot within ST_PROBES
+// goes to the region's statistics at once, and from then on every entry of the
+// workgroup is added with atomics.
 
-constexpr int ST_COLS = 512, ST_ROWS = 256;
+constexpr int ST_COLS = 512, ST_ROWS = 256, ST_CHUNK = 8;
 constexpr int ST_CAP = 1024;                       // labels per area in LDS
+constexpr int ST_PROBES = 16;                      // slots a label tries before it gives up
+constexpr uint32_t ST_FLUSH_AT = ST_CAP / 2;       // entries that trigger a write-out
 constexpr int ST_SEGS = ST_COLS / TW;              // row segments per area row
+constexpr int ST_SPW = ST_CHUNK * ST_SEGS / NWAVES;  // segments of a chunk per wave
 static_assert((ST_CAP & (ST_CAP - 1)) == 0, "the hash table size is a power of two");
 
 struct StatsArgs {
@@ -1943,6 +1956,8 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(StatsArgs a)
     __shared__ unsigned long long sNY[ST_CAP];           // area | (sum of local rows << 32)
     __shared__ uint32_t sSX[ST_CAP];                     // sum of local columns
     __shared__ uint32_t sY0[ST_CAP], sX0[ST_CAP], sY1[ST_CAP], sX1[ST_CAP];
+    __shared__ uint32_t sUsed;                           // entries in use
+    __shared__ uint32_t sSpill;                          // some run went to the global statistics
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const uint32_t per_img = a.ay * a.ax;
     const uint32_t b = blockIdx.x / per_img, rem = blockIdx.x - b * per_img;
@@ -1953,66 +1968,150 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(StatsArgs a)
     const int32_t nmax = a.counts[b];
     const int64_t off = a.off[b] - 1;                    // entry of label k: off + k
     const int32_t *img = a.labels + (int64_t)b * a.HW;
-    for (int i = threadIdx.x; i < ST_CAP; i += BLOCK) {
-        sKey[i] = 0u;
-        sNY[i] = 0ull;
-        sSX[i] = 0u;
-        sY0[i] = sX0[i] = 0xFFFFFFFFu;
-        sY1[i] = sX1[i] = 0u;
-    }
+    const bool up = Y0 > 0, down = Y0 + nrows < H, left = X0 > 0, right = X0 + ncols < W;
+
+    auto clear = [&]() {
+        for (int i = threadIdx.x; i < ST_CAP; i += BLOCK) {
+            sKey[i] = 0u;
+            sNY[i] = 0ull;
+            sSX[i] = 0u;
+            sY0[i] = sX0[i] = 0xFFFFFFFFu;
+            sY1[i] = sX1[i] = 0u;
+        }
+        if (threadIdx.x == 0) sUsed = 0u;
+    };
+    clear();
+    if (threadIdx.x == 0) sSpill = 0u;
     __syncthreads();
-    // row segments of the area, dealt to the waves
-    const int nseg = nrows * ST_SEGS;
-    for (int sg = wave; sg < nseg; sg += NWAVES) {
-        const int ly = sg / ST_SEGS, lx0 = (sg - ly * ST_SEGS) * TW;  // local row, first column
-        const int lx = lx0 + lane;
-        const bool in = lx < ncols;
-        const int32_t v = in ? img[(int64_t)(Y0 + ly) * W + X0 + lx] : 0;
-        // runs of one label in the segment: lane L starts one where the label
-        // differs from lane L-1's (lane 0 always, if it has a pixel)
-        const uint64_t valid = __ballot(in);
-        const uint64_t st = (__ballot(from_left_lane((uint32_t)v) != (uint32_t)v) | 1ull) & valid;
-        if (!lane_bit(st) || v <= 0 || v > nmax || off + v >= a.n_total) continue;
-        // the run ends before the next start (or the last valid lane)
-        const uint64_t after = st & ~mask_le(lane);
-        const int end = after ? (int)__builtin_ctzll(after) - 1 : 63 - (int)__builtin_clzll(valid);
-        const uint32_t len = (uint32_t)(end - lane + 1);
-        const uint32_t sxl = len * (uint32_t)lx + len * (len - 1u) / 2u;   // local columns
-        // the label's entry: open addressing from a multiplicative hash
+
+    // one run's contribution (local coordinates) to its label's entry, or to
+    // the region's global statistics if the table has no room for the label
+    auto add = [&](int32_t v, uint32_t n, uint32_t syl, uint32_t sxl, uint32_t y0, uint32_t x0,
+                   uint32_t y1, uint32_t x1) {
         uint32_t h = ((uint32_t)v * 2654435761u) >> (32 - 10);
         static_assert(ST_CAP == 1024, "the hash takes 10 bits");
         int e = -1;
-        for (int p = 0; p < ST_CAP; ++p, h = (h + 1u) & (ST_CAP - 1)) {
+        for (int p = 0; p < ST_PROBES; ++p, h = (h + 1u) & (ST_CAP - 1)) {
             const uint32_t k = sKey[h];
             if (k == (uint32_t)v) { e = (int)h; break; }
             if (k == 0u) {
                 const uint32_t old = atomicCAS(&sKey[h], 0u, (uint32_t)v);
+                if (old == 0u) atomicAdd(&sUsed, 1u);
                 if (old == 0u || old == (uint32_t)v) { e = (int)h; break; }
             }
         }
-        if (e < 0) {  // the table is full: straight to the region's statistics
-            stats_global(a, off + v, len, (uint64_t)len * (uint64_t)(Y0 + ly),
-                         (uint64_t)sxl + (uint64_t)len * (uint64_t)X0, Y0 + ly, X0 + lx, Y0 + ly,
-                         X0 + end + lx0);
-            continue;
+        if (e < 0) {
+            sSpill = 1u;
+            stats_global(a, off + v, n, (uint64_t)syl + (uint64_t)n * (uint64_t)Y0,
+                         (uint64_t)sxl + (uint64_t)n * (uint64_t)X0, Y0 + (int32_t)y0,
+                         X0 + (int32_t)x0, Y0 + (int32_t)y1, X0 + (int32_t)x1);
+            return;
         }
-        atomicAdd(&sNY[e], (unsigned long long)len | ((unsigned long long)(len * (uint32_t)ly) << 32));
+        atomicAdd(&sNY[e], (unsigned long long)n | ((unsigned long long)syl << 32));
         atomicAdd(&sSX[e], sxl);
-        atomicMin(&sY0[e], (uint32_t)ly);
-        atomicMin(&sX0[e], (uint32_t)lx);
-        atomicMax(&sY1[e], (uint32_t)ly);
-        atomicMax(&sX1[e], (uint32_t)(lx0 + end));
+        atomicMin(&sY0[e], y0);
+        atomicMin(&sX0[e], x0);
+        atomicMax(&sY1[e], y1);
+        atomicMax(&sX1[e], x1);
+    };
+
+    // write the table out: rows 0..last are taken, the table was last cleared
+    // before row `cleared` (-1: never)
+    auto write_out = [&](int last, int cleared) {
+        const bool spill = sSpill != 0u;
+        for (int i = threadIdx.x; i < ST_CAP; i += BLOCK) {
+            const uint32_t k = sKey[i];
+            if (k == 0u) continue;
+            const unsigned long long ny = sNY[i];
+            const uint32_t n = (uint32_t)ny, syl = (uint32_t)(ny >> 32);
+            const uint32_t y0 = sY0[i], x0 = sX0[i], y1 = sY1[i], x1 = sX1[i];
+            const uint64_t sy = (uint64_t)syl + (uint64_t)n * (uint64_t)Y0;
+            const uint64_t sx = (uint64_t)sSX[i] + (uint64_t)n * (uint64_t)X0;
+            const int64_t e = off + (int64_t)k;
+            const bool open = (up && y0 == 0u) || (down && y1 == (uint32_t)(nrows - 1)) ||
+                              (left && x0 == 0u) || (right && x1 == (uint32_t)(ncols - 1)) ||
+                              (last < nrows - 1 && y1 == (uint32_t)last) ||
+                              (int)y0 == cleared;
+            if (open || spill) {
+                stats_global(a, e, n, sy, sx, Y0 + (int32_t)y0, X0 + (int32_t)x0,
+                             Y0 + (int32_t)y1, X0 + (int32_t)x1);
+            } else {
+                a.area[e] = (int32_t)n;
+                a.sum_y[e] = sy;
+                a.sum_x[e] = sx;
+                a.bbox[4 * e] = Y0 + (int32_t)y0;
+                a.bbox[4 * e + 1] = X0 + (int32_t)x0;
+                a.bbox[4 * e + 2] = Y0 + (int32_t)y1;
+                a.bbox[4 * e + 3] = X0 + (int32_t)x1;
+            }
+        }
+    };
+
+    int cleared = -1;
+    for (int r0 = 0; r0 < nrows; r0 += ST_CHUNK) {
+        const int r1 = min(nrows, r0 + ST_CHUNK);
+        // the wave's open sum for one-run segments (label cv, 0: none)
+        int32_t cv = 0;
+        uint32_t cn = 0, csy = 0, csx = 0, cy0 = 0, cx0 = 0, cy1 = 0, cx1 = 0;
+        // the wave's segments of the chunk: all their loads first, so that they
+        // are in flight together (one at a time, the pass ran at 1.6 TB/s)
+        int32_t vv[ST_SPW];
+#pragma unroll
+        for (int u = 0; u < ST_SPW; ++u) {
+            const int sg = r0 * ST_SEGS + wave + u * NWAVES;
+            const int ly = sg / ST_SEGS, lx = (sg - ly * ST_SEGS) * TW + lane;
+            vv[u] = (ly < r1 && lx < ncols) ? img[(int64_t)(Y0 + ly) * W + X0 + lx] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < ST_SPW; ++u) {
+            const int sg = r0 * ST_SEGS + wave + u * NWAVES;
+            const int ly = sg / ST_SEGS, lx0 = (sg - ly * ST_SEGS) * TW;  // local row, first column
+            const int lx = lx0 + lane;
+            const bool in = ly < r1 && lx < ncols;
+            const int32_t v = vv[u];
+            // runs of one label in the segment: lane L starts one where the
+            // label differs from lane L-1's (lane 0 always, if it has a pixel)
+            const uint64_t valid = __ballot(in);
+            const uint64_t st = (__ballot(from_left_lane((uint32_t)v) != (uint32_t)v) | 1ull) & valid;
+            if (st == 1ull) {  // one run: the whole segment (its valid part)
+                const int32_t v0 = __builtin_amdgcn_readfirstlane(v);
+                if (v0 <= 0 || v0 > nmax || off + v0 >= a.n_total) continue;
+                if (v0 != cv) {
+                    if (cv != 0 && lane == 0) add(cv, cn, csy, csx, cy0, cx0, cy1, cx1);
+                    cv = v0;
+                    cn = csy = csx = 0;
+                    cy0 = cx0 = 0xFFFFFFFFu;
+                    cy1 = cx1 = 0;
+                }
+                const uint32_t len = popc64(valid);
+                cn += len;
+                csy += len * (uint32_t)ly;
+                csx += len * (uint32_t)lx0 + len * (len - 1u) / 2u;
+                cy0 = min(cy0, (uint32_t)ly);
+                cx0 = min(cx0, (uint32_t)lx0);
+                cy1 = max(cy1, (uint32_t)ly);
+                cx1 = max(cx1, (uint32_t)lx0 + len - 1u);
+                continue;
+            }
+            if (!lane_bit(st) || v <= 0 || v > nmax || off + v >= a.n_total) continue;
+            // the run ends before the next start (or at the last valid lane)
+            const uint64_t after = st & ~mask_le(lane);
+            const int end = after ? (int)__builtin_ctzll(after) - 1 : 63 - (int)__builtin_clzll(valid);
+            const uint32_t len = (uint32_t)(end - lane + 1);
+            add(v, len, len * (uint32_t)ly, len * (uint32_t)lx + len * (len - 1u) / 2u,
+                (uint32_t)ly, (uint32_t)lx, (uint32_t)ly, (uint32_t)(lx0 + end));
+        }
+        if (cv != 0 && lane == 0) add(cv, cn, csy, csx, cy0, cx0, cy1, cx1);
+        __syncthreads();
+        if (r1 < nrows && sUsed > ST_FLUSH_AT) {  // the same for every thread
+            write_out(r1 - 1, cleared);
+            __syncthreads();
+            clear();
+            cleared = r1;
+            __syncthreads();
+        }
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < ST_CAP; i += BLOCK) {
-        const uint32_t k = sKey[i];
-        if (k == 0u) continue;
-        const unsigned long long ny = sNY[i];
-        const uint32_t n = (uint32_t)ny, syl = (uint32_t)(ny >> 32);
-        stats_global(a, off + (int64_t)k, n, (uint64_t)syl + (uint64_t)n * (uint64_t)Y0,
-                     (uint64_t)sSX[i] + (uint64_t)n * (uint64_t)X0, Y0 + (int32_t)sY0[i],
-                     X0 + (int32_t)sX0[i], Y0 + (int32_t)sY1[i], X0 + (int32_t)sX1[i]);
-    }
+    write_out(nrows - 1, cleared);
 }
 
 // Entries of every region start empty (area 0, box (INT32_MAX, INT32_MAX, -1,
