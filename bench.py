@@ -238,13 +238,10 @@ def stats_leg(ccl, labels, counts, npx, steps, warmup, stream, hip, torch):
     n_total = int(counts.to(torch.int64).sum().item())
     dev = labels.device
     ws = torch.zeros(ccl.workspace_bytes(B, H, W), dtype=torch.uint8, device=dev)
-    outs = [torch.empty(n_total, dtype=torch.int32, device=dev),
-            torch.empty((n_total, 4), dtype=torch.int32, device=dev),
-            torch.empty(n_total, dtype=torch.int64, device=dev),
-            torch.empty(n_total, dtype=torch.int64, device=dev)]
+    rec = torch.empty((n_total, 5), dtype=torch.int64, device=dev)  # 40-byte records
     lib = ccl._load()
-    args = [ccl._ptr(labels), B, H, W, ccl._ptr(counts), n_total] + [ccl._ptr(o) for o in outs] + \
-           [ccl._ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream)]
+    args = [ccl._ptr(labels), B, H, W, ccl._ptr(counts), n_total, ccl._ptr(rec),
+            ccl._ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream)]
     for _ in range(warmup):
         ccl._check(lib.ccl_region_stats(*args))
     ev = hip.create(2 * steps)

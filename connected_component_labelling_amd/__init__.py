@@ -64,7 +64,7 @@ def _load():
     lib.ccl_number.restype = ctypes.c_int
     lib.ccl_count.argtypes = [vp, i64, i64, i64, vp, vp, sz, vp]
     lib.ccl_count.restype = ctypes.c_int
-    lib.ccl_region_stats.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.ccl_region_stats.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, sz, vp]
     lib.ccl_region_stats.restype = ctypes.c_int
     lib.ccl_status_string.argtypes = [ctypes.c_int]
     lib.ccl_status_string.restype = ctypes.c_char_p
@@ -200,9 +200,10 @@ def region_stats(labels: torch.Tensor, counts: torch.Tensor, n_total: int | None
                  stream=None, workspace: torch.Tensor | None = None) -> dict:
     """Per-region area, bounding box (min row, min col, max row, max col) and sums
     of row / column indices of a numbered labelling (label(..., number=True)),
-    regions of all images concatenated: image b's region k is entry
+    regions of all images concatenated: image b's region k is record
     sum(counts[:b]) + k - 1.  ``n_total`` (the sum of ``counts``) is read from
-    the device when not given."""
+    the device when not given.  Returns views of one int64 [n, 5] tensor of
+    ccl_region records ("records"): "area", "bbox", "sum_y", "sum_x"."""
     _require_device(labels, "labels")
     if labels.dtype != torch.int32 or counts.dtype != torch.int32:
         raise TypeError("labels and counts must be int32")
@@ -213,17 +214,15 @@ def region_stats(labels: torch.Tensor, counts: torch.Tensor, n_total: int | None
     if n_total is None:
         n_total = int(counts.to(torch.int64).sum().item())
     dev = labels.device
-    area = torch.empty(n_total, dtype=torch.int32, device=dev)
-    bbox = torch.empty((n_total, 4), dtype=torch.int32, device=dev)
-    sum_y = torch.empty(n_total, dtype=torch.int64, device=dev)
-    sum_x = torch.empty(n_total, dtype=torch.int64, device=dev)
+    rec = torch.empty((n_total, 5), dtype=torch.int64, device=dev)  # 40-byte ccl_region records
     if workspace is None:
         workspace = _new_workspace(B, H, W, dev)
     _check(_load().ccl_region_stats(_ptr(x), B, H, W, _ptr(counts.contiguous()), n_total,
-                                    _ptr(area), _ptr(bbox), _ptr(sum_y), _ptr(sum_x),
-                                    _ptr(workspace), workspace.numel(),
+                                    _ptr(rec), _ptr(workspace), workspace.numel(),
                                     ctypes.c_void_p(_stream_handle(stream))))
-    return {"area": area, "bbox": bbox, "sum_y": sum_y, "sum_x": sum_x}
+    r32 = rec.view(torch.int32)
+    return {"records": rec, "area": r32[:, 4], "bbox": r32[:, 5:9], "sum_y": rec[:, 0],
+            "sum_x": rec[:, 1]}
 
 
 class Labeller:

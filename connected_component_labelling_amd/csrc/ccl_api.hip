@@ -237,25 +237,22 @@ int ccl_count(const int32_t *leaders, int64_t batch, int64_t height, int64_t wid
 }
 
 int ccl_region_stats(const int32_t *labels, int64_t batch, int64_t height, int64_t width,
-                     const int32_t *counts, int64_t n_total, int32_t *area, int32_t *bbox,
-                     int64_t *sum_y, int64_t *sum_x, void *workspace, size_t workspace_bytes,
-                     void *stream)
+                     const int32_t *counts, int64_t n_total, ccl_region *stats,
+                     void *workspace, size_t workspace_bytes, void *stream)
 {
     bool empty;
     int rc = check_shape(batch, height, width, &empty);
     if (rc != CCL_OK) return rc;
     if (n_total < 0) return CCL_ERR_SHAPE;
-    if (empty || n_total == 0) {
-        if (n_total > 0 && (!area || !bbox || !sum_y || !sum_x)) return CCL_ERR_NULL;
-        return CCL_OK;  // no pixel, or no region: nothing to write
-    }
-    if (!labels || !counts || !area || !bbox || !sum_y || !sum_x || !workspace) return CCL_ERR_NULL;
+    if (n_total > 0 && !stats) return CCL_ERR_NULL;
+    if (empty || n_total == 0) return CCL_OK;  // no pixel, or no region: nothing to write
+    if (!labels || !counts || !workspace) return CCL_ERR_NULL;
     Layout L;
     if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
     const Work w = bind_work(L, workspace);
-    launch_region_stats(labels, counts, L.g, w, n_total, area, bbox, sum_y, sum_x,
-                        (hipStream_t)stream);
+    static_assert(sizeof(ccl_region) == sizeof(RegionRec), "one record layout");
+    launch_region_stats(labels, counts, L.g, w, n_total, (RegionRec *)stats, (hipStream_t)stream);
     return finish_launches();
 }
 

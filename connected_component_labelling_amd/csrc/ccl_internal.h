@@ -153,11 +153,17 @@ void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, i
                          hipStream_t s);
 void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g, const Work &w,
                           hipStream_t s);
+// One region's statistics, laid out as ccl_region of the C ABI.
+struct RegionRec {
+    unsigned long long sum_y, sum_x;
+    int32_t area, y0, x0, y1, x1, pad;
+};
+static_assert(sizeof(RegionRec) == 40, "40-byte region records");
+
 // per-region statistics of a numbered labelling; the workspace's band-status
-// words hold the first entry of each image (B int64 fit in its B*nty words)
+// words hold the first record of each image (B int64 fit in its B*nty words)
 void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geom &g,
-                         const Work &w, int64_t n_total, int32_t *area, int32_t *bbox,
-                         int64_t *sum_y, int64_t *sum_x, hipStream_t s);
+                         const Work &w, int64_t n_total, RegionRec *recs, hipStream_t s);
 void launch_zero_i32(int32_t *p, int64_t n, hipStream_t s);
 
 }  // namespace ccl

@@ -1905,13 +1905,13 @@ __global__ void zero_i32_kernel(int32_t *p, int64_t n)
 // label instead (paper, the inside of large regions: one table update per
 // change of label, not per segment).  Entries leave the table at the end of
 // the area, or after a chunk once the table is half full (anti-aliased glyph
-// rows put up to 20,000 labels in one area of the sheet):
-//   - a region that touches no side of the area shared with another area,
-//     not the last row taken so far, and that is not the continuation of an
-//     entry already written out (its first row is not the row right after the
-//     last clearing) is complete: its entry is stored with plain stores;
-//   - any other entry is added to the region's statistics with atomics, so a
-//     region that covers the whole picture takes one set per area.
+// rows put up to 20,000 labels in one area of the sheet); then the entries of
+// regions that reach the last row taken so far stay (they may go on below)
+// and the others leave:
+//   - a region that touches no side of the area shared with another area is
+//     complete: its record is written with plain stores;
+//   - a region on a shared side is added to the region's record with atomics,
+//     so a region that covers the whole picture takes one set per area.
 // A run whose label finds neither its entry nor a free slot within ST_PROBES
 // goes to the region's statistics at once, and from then on every entry of the
 // workgroup is added with atomics.
@@ -1927,11 +1927,8 @@ static_assert((ST_CAP & (ST_CAP - 1)) == 0, "the hash table size is a power of t
 struct StatsArgs {
     const int32_t *labels;
     const int32_t *counts;
-    const int64_t *off;        // [B] first entry of each image
-    int32_t *area;
-    int32_t *bbox;
-    unsigned long long *sum_y;
-    unsigned long long *sum_x;
+    const int64_t *off;        // [B] first record of each image
+    RegionRec *rec;
     int64_t B, H, W, HW;
     int64_t n_total;           // entries of the outputs
     uint32_t ay, ax;           // areas per image column / row
@@ -1941,13 +1938,14 @@ __device__ __forceinline__ void stats_global(const StatsArgs &a, int64_t i, uint
                                              uint64_t sx, int32_t y0, int32_t x0, int32_t y1,
                                              int32_t x1)
 {
-    atomicAdd(&a.area[i], (int32_t)n);
-    atomicAdd(&a.sum_y[i], (unsigned long long)sy);
-    atomicAdd(&a.sum_x[i], (unsigned long long)sx);
-    atomicMin(&a.bbox[4 * i], y0);
-    atomicMin(&a.bbox[4 * i + 1], x0);
-    atomicMax(&a.bbox[4 * i + 2], y1);
-    atomicMax(&a.bbox[4 * i + 3], x1);
+    RegionRec &r = a.rec[i];
+    atomicAdd(&r.sum_y, (unsigned long long)sy);
+    atomicAdd(&r.sum_x, (unsigned long long)sx);
+    atomicAdd(&r.area, (int32_t)n);
+    atomicMin(&r.y0, y0);
+    atomicMin(&r.x0, x0);
+    atomicMax(&r.y1, y1);
+    atomicMax(&r.x1, x1);
 }
 
 __global__ __launch_bounds__(BLOCK) void stats_kernel(StatsArgs a)
@@ -2015,13 +2013,21 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(StatsArgs a)
         atomicMax(&sX1[e], x1);
     };
 
-    // write the table out: rows 0..last are taken, the table was last cleared
-    // before row `cleared` (-1: never)
-    auto write_out = [&](int last, int cleared) {
+    // write out the entries of regions that do not reach row `keep` (-1: all),
+    // returning in kept[] the slots of those that do
+    constexpr int SLOTS = ST_CAP / BLOCK;  // table slots per thread
+    auto write_out = [&](int keep, bool (&kept)[SLOTS]) {
         const bool spill = sSpill != 0u;
-        for (int i = threadIdx.x; i < ST_CAP; i += BLOCK) {
+#pragma unroll
+        for (int j = 0; j < SLOTS; ++j) {
+            const int i = threadIdx.x + j * BLOCK;
+            kept[j] = false;
             const uint32_t k = sKey[i];
             if (k == 0u) continue;
+            if ((int)sY1[i] == keep) {
+                kept[j] = true;
+                continue;
+            }
             const unsigned long long ny = sNY[i];
             const uint32_t n = (uint32_t)ny, syl = (uint32_t)(ny >> 32);
             const uint32_t y0 = sY0[i], x0 = sX0[i], y1 = sY1[i], x1 = sX1[i];
@@ -2029,25 +2035,22 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(StatsArgs a)
             const uint64_t sx = (uint64_t)sSX[i] + (uint64_t)n * (uint64_t)X0;
             const int64_t e = off + (int64_t)k;
             const bool open = (up && y0 == 0u) || (down && y1 == (uint32_t)(nrows - 1)) ||
-                              (left && x0 == 0u) || (right && x1 == (uint32_t)(ncols - 1)) ||
-                              (last < nrows - 1 && y1 == (uint32_t)last) ||
-                              (int)y0 == cleared;
+                              (left && x0 == 0u) || (right && x1 == (uint32_t)(ncols - 1));
             if (open || spill) {
                 stats_global(a, e, n, sy, sx, Y0 + (int32_t)y0, X0 + (int32_t)x0,
                              Y0 + (int32_t)y1, X0 + (int32_t)x1);
-            } else {
-                a.area[e] = (int32_t)n;
-                a.sum_y[e] = sy;
-                a.sum_x[e] = sx;
-                a.bbox[4 * e] = Y0 + (int32_t)y0;
-                a.bbox[4 * e + 1] = X0 + (int32_t)x0;
-                a.bbox[4 * e + 2] = Y0 + (int32_t)y1;
-                a.bbox[4 * e + 3] = X0 + (int32_t)x1;
+            } else {  // the whole record, five 8-byte stores
+                uint64_t *r = (uint64_t *)&a.rec[e];
+                r[0] = sy;
+                r[1] = sx;
+                r[2] = (uint64_t)n | ((uint64_t)(uint32_t)(Y0 + (int32_t)y0) << 32);
+                r[3] = (uint64_t)(uint32_t)(X0 + (int32_t)x0) | ((uint64_t)(uint32_t)(Y0 + (int32_t)y1) << 32);
+                r[4] = (uint64_t)(uint32_t)(X0 + (int32_t)x1);
             }
         }
     };
 
-    int cleared = -1;
+    bool kept[SLOTS];
     for (int r0 = 0; r0 < nrows; r0 += ST_CHUNK) {
         const int r1 = min(nrows, r0 + ST_CHUNK);
         // the wave's open sum for one-run segments (label cv, 0: none)
@@ -2104,14 +2107,33 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(StatsArgs a)
         if (cv != 0 && lane == 0) add(cv, cn, csy, csx, cy0, cx0, cy1, cx1);
         __syncthreads();
         if (r1 < nrows && sUsed > ST_FLUSH_AT) {  // the same for every thread
-            write_out(r1 - 1, cleared);
+            write_out(r1 - 1, kept);
+            // the entries that stay, out of the table and back into the cleared one
+            uint32_t kk[SLOTS], ksx[SLOTS], ky0[SLOTS], kx0[SLOTS], ky1[SLOTS], kx1[SLOTS];
+            unsigned long long kny[SLOTS];
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j) {
+                const int i = threadIdx.x + j * BLOCK;
+                kk[j] = kept[j] ? sKey[i] : 0u;
+                kny[j] = sNY[i];
+                ksx[j] = sSX[i];
+                ky0[j] = sY0[i];
+                kx0[j] = sX0[i];
+                ky1[j] = sY1[i];
+                kx1[j] = sX1[i];
+            }
             __syncthreads();
             clear();
-            cleared = r1;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j)
+                if (kk[j] != 0u)
+                    add((int32_t)kk[j], (uint32_t)kny[j], (uint32_t)(kny[j] >> 32), ksx[j], ky0[j],
+                        kx0[j], ky1[j], kx1[j]);
             __syncthreads();
         }
     }
-    write_out(nrows - 1, cleared);
+    write_out(-1, kept);
 }
 
 // Entries of every region start empty (area 0, box (INT32_MAX, INT32_MAX, -1,
@@ -2121,10 +2143,11 @@ __global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t 
 {
     for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < n_total;
          i += (int64_t)gridDim.x * BLOCK) {
-        a.area[i] = 0;
-        a.bbox[4 * i] = a.bbox[4 * i + 1] = 2147483647;
-        a.bbox[4 * i + 2] = a.bbox[4 * i + 3] = -1;
-        a.sum_y[i] = a.sum_x[i] = 0ull;
+        uint64_t *r = (uint64_t *)&a.rec[i];
+        r[0] = r[1] = 0ull;                                      // sums
+        r[2] = (uint64_t)2147483647u << 32;                      // area 0, y0 INT32_MAX
+        r[3] = 2147483647u | ((uint64_t)0xFFFFFFFFu << 32);      // x0 INT32_MAX, y1 -1
+        r[4] = 0xFFFFFFFFu;                                      // x1 -1, pad 0
     }
     if (blockIdx.x != 0) return;
     // exclusive prefix of the counts: thread j sums its chunk, a workgroup scan
@@ -2232,17 +2255,13 @@ void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g
 }
 
 void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geom &g,
-                         const Work &w, int64_t n_total, int32_t *area, int32_t *bbox,
-                         int64_t *sum_y, int64_t *sum_x, hipStream_t s)
+                         const Work &w, int64_t n_total, RegionRec *recs, hipStream_t s)
 {
     StatsArgs a;
     a.labels = labels;
     a.counts = counts;
     a.off = (const int64_t *)w.bandst;
-    a.area = area;
-    a.bbox = bbox;
-    a.sum_y = (unsigned long long *)sum_y;
-    a.sum_x = (unsigned long long *)sum_x;
+    a.rec = recs;
     a.B = g.B;
     a.H = g.H;
     a.W = g.W;

@@ -157,6 +157,17 @@ int ccl_count(const int32_t *leaders, int64_t batch, int64_t height, int64_t wid
               int32_t *counts, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Statistics of one region (40 bytes, 8-byte aligned): see ccl_region_stats.
+ */
+typedef struct {
+    int64_t sum_y, sum_x;    /* sums of its pixels' row / column indices (exact) */
+    int32_t area;            /* its pixels */
+    int32_t y0, x0, y1, x1;  /* bounding box: smallest row, smallest column,
+                                largest row, largest column (inclusive) */
+    int32_t pad;             /* 0 */
+} ccl_region;
+
+/*
  * Per-region statistics of a numbered labelling (as written by ccl_label with
  * CCL_NUMBER, or by ccl_number): for each region, its area, its bounding box
  * and the sums of its pixels' row and column indices, from which its position
@@ -169,22 +180,17 @@ int ccl_count(const int32_t *leaders, int64_t batch, int64_t height, int64_t wid
  *            in image b, 0 for a pixel of no region (an ignored colour).  Other
  *            values are skipped.
  *   counts   device int32 [batch]: regions per image (as ccl_label wrote them)
- *   n_total  host: counts[0] + ... + counts[batch-1], the number of entries of
- *            each output; entries past it are never written
- *   Region k of image b is entry i = counts[0] + ... + counts[b-1] + k - 1 of
- *   area     device int32 [n_total]: its pixels
- *   bbox     device int32 [n_total, 4]: smallest row, smallest column, largest
- *            row, largest column of its pixels (inclusive)
- *   sum_y, sum_x  device int64 [n_total]: sums of its pixels' row / column
- *            indices (exact)
- * Every entry is written: a number with no pixel keeps area 0, box
+ *   n_total  host: counts[0] + ... + counts[batch-1], the number of records;
+ *            records past it are never written
+ *   stats    device ccl_region [n_total], 8-byte aligned: region k of image b
+ *            is record counts[0] + ... + counts[b-1] + k - 1
+ * Every record is written: a number with no pixel keeps area 0, box
  * (INT32_MAX, INT32_MAX, -1, -1) and sums 0.  The workspace is the one of
  * ccl_workspace_bytes(batch, height, width).
  */
 int ccl_region_stats(const int32_t *labels, int64_t batch, int64_t height, int64_t width,
-                     const int32_t *counts, int64_t n_total, int32_t *area, int32_t *bbox,
-                     int64_t *sum_y, int64_t *sum_x, void *workspace, size_t workspace_bytes,
-                     void *stream);
+                     const int32_t *counts, int64_t n_total, ccl_region *stats,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static text for a status code (never NULL). */
 const char *ccl_status_string(int status);

@@ -101,18 +101,13 @@ def test_null_pointers(lib):
     assert lib.ccl_count(FAKE, 1, 8, 8, None, FAKE, 1 << 30, None) == -1
     assert lib.ccl_number(FAKE, 1, 8, 8, FAKE, None, FAKE, 16, None) == -6
     assert lib.ccl_count(FAKE, -1, 8, 8, FAKE, FAKE, 1 << 30, None) == -2
-    # region statistics: (labels, B, H, W, counts, n_total, area, bbox, sum_y, sum_x, ws, bytes, s)
-    assert lib.ccl_region_stats(None, 1, 8, 8, FAKE, 5, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
-                                None) == -1
-    assert lib.ccl_region_stats(FAKE, 1, 8, 8, FAKE, 5, FAKE, None, FAKE, FAKE, FAKE, 1 << 30,
-                                None) == -1
-    assert lib.ccl_region_stats(FAKE, 1, 8, 8, FAKE, -1, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
-                                None) == -2
-    assert lib.ccl_region_stats(FAKE, 1, 8, 8, FAKE, 5, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
-                                None) == -6
+    # region statistics: (labels, B, H, W, counts, n_total, records, ws, bytes, stream)
+    assert lib.ccl_region_stats(None, 1, 8, 8, FAKE, 5, FAKE, FAKE, 1 << 30, None) == -1
+    assert lib.ccl_region_stats(FAKE, 1, 8, 8, FAKE, 5, None, FAKE, 1 << 30, None) == -1
+    assert lib.ccl_region_stats(FAKE, 1, 8, 8, FAKE, -1, FAKE, FAKE, 1 << 30, None) == -2
+    assert lib.ccl_region_stats(FAKE, 1, 8, 8, FAKE, 5, FAKE, FAKE, 16, None) == -6
     # no region: nothing to write, no HIP call
-    assert lib.ccl_region_stats(FAKE, 1, 8, 8, FAKE, 0, None, None, None, None, None, 0,
-                                None) == 0
+    assert lib.ccl_region_stats(FAKE, 1, 8, 8, FAKE, 0, None, None, 0, None) == 0
 
 
 def test_empty_batches_are_noops(lib):
