@@ -298,8 +298,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5)
-    ap.add_argument("--cpu-rows", type=int, default=6000,
-                    help="rows of the sheet the CPU baseline labels (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=-1,
+                    help="rows of the sheet the CPU baseline labels (-1 = all, 0 = skip)")
     ap.add_argument("--no-extra-legs", action="store_true",
                     help="time the headline call only (no paper-ignored or RGB legs)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -396,12 +396,15 @@ def main():
 
     cpu = None
     exact = None
+    if args.cpu_rows < 0:
+        args.cpu_rows = H
     if args.cpu_rows > 0:
         print("[bench] CPU baseline (oracle) ...", file=sys.stderr, flush=True)
         del lab
         torch.cuda.empty_cache()
         cpu, exact = cpu_baseline(img_np, min(args.cpu_rows, H), ccl, torch)
         if ignore_leg is not None:
+            print("[bench] oracle with the paper ignored ...", file=sys.stderr, flush=True)
             ignore_leg["band_parity_bit_exact"] = band_parity_ignore(
                 img_np, min(args.cpu_rows, H), paper, ccl, torch)
 
