@@ -58,6 +58,11 @@ def _bind(lib):
     lib.oracle_count.argtypes = [i32p, i64, i64, i64, i32p]
     lib.oracle_count.restype = ctypes.c_int
     i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_label64.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_uint32, i64p]
+    lib.oracle_label64.restype = ctypes.c_int
+    lib.oracle_number64.argtypes = [i64p, i64, i64, i64, i64p, i64p]
+    lib.oracle_number64.restype = ctypes.c_int
     lib.oracle_region_stats.argtypes = [i32p, i64, i64, i64, i32p, i32p, i32p, i64p, i64p]
     lib.oracle_region_stats.restype = ctypes.c_int
     return lib
@@ -124,6 +129,41 @@ def label(img, connectivity: int = 8, lib=None, ignore=None, rgb: bool = False) 
         return _run_labeller("oracle_label", img, connectivity, lib or load(), rgb=rgb)
     return _run_labeller("oracle_label_ignore", img, connectivity, lib or load(),
                          ctypes.c_uint32(int(ignore) & 0xFFFFFFFF), rgb=rgb)
+
+
+def label64(img, connectivity: int = 8, lib=None, ignore=None, rgb: bool = False) -> np.ndarray:
+    """As ``label``, with int64 leaders: for images of any size, also beyond
+    2^31 pixels."""
+    lib = lib or load()
+    img, dtype, squeeze = _as_batch(img, rgb)
+    B, H, W = img.shape[:3]
+    out = np.empty((B, H, W), dtype=np.int64)
+    ign = ignore is not None
+    rc = lib.oracle_label64(img.ctypes.data_as(ctypes.c_void_p), dtype, B, H, W,
+                            int(connectivity), int(ign),
+                            ctypes.c_uint32(int(ignore) & 0xFFFFFFFF if ign else 0),
+                            out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    if rc != 0:
+        raise ValueError(f"oracle_label64 failed with status {rc}")
+    return out[0] if squeeze else out
+
+
+def number64(leaders, lib=None):
+    """As ``number``, on int64 leaders: (int64 labels, int64 counts)."""
+    lib = lib or load()
+    L = np.ascontiguousarray(np.asarray(leaders, dtype=np.int64))
+    squeeze = L.ndim == 2
+    if squeeze:
+        L = L[None]
+    B, H, W = L.shape
+    out = np.empty_like(L)
+    counts = np.empty(B, dtype=np.int64)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    rc = lib.oracle_number64(L.ctypes.data_as(i64p), B, H, W, out.ctypes.data_as(i64p),
+                             counts.ctypes.data_as(i64p))
+    if rc != 0:
+        raise ValueError(f"oracle_number64 failed with status {rc}")
+    return (out[0], counts) if squeeze else (out, counts)
 
 
 def connect(img, connectivity: int = 8, lib=None, rgb: bool = False) -> np.ndarray:

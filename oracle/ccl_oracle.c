@@ -37,6 +37,10 @@
  *     the raster two-pass scan over already-visited neighbours, 4- and
  *     8-connectivity; its introduction names the uses of a labelling, such as
  *     a region's bounding box.
+ *   same page, ch.11: images of more than 2^31 pixels; their leaders need
+ *     64-bit indices (oracle_label64, oracle_number64).  The union-find below
+ *     works on 64-bit parents for every entry point; the 32-bit ones narrow
+ *     the result.
  *   The tissue-scan segmentation article, sections 1.1 and 2.3: each region's
  *     area and position are summed over its pixels once it is numbered.
  *     oracle_region_stats computes, per region, its area, bounding box and the
@@ -53,7 +57,7 @@
  * all three bytes of an RGB pixel.  An RGB pixel's colour value, as an ignored
  * colour is named, is b0 | b1 << 8 | b2 << 16 with b0 its first byte.
  *
- * Building with -DORACLE_MUTANT=k plants a deliberate mistake (k = 1..13) so the
+ * Building with -DORACLE_MUTANT=k plants a deliberate mistake (k = 1..14) so the
  * pin tests can show that they catch it.  The default build plants nothing.
  */
 #include <stdint.h>
@@ -88,7 +92,7 @@ static inline uint32_t colour_at(const void *img, int dtype, int64_t i)
 
 /* Find: walk parent arrows to the pixel that points at itself, halving the
  * path on the way (each visited pixel is pointed at its grandparent). */
-static int32_t find_leader(int32_t *P, int32_t x)
+static int64_t find_leader(int64_t *P, int64_t x)
 {
     while (P[x] != x) {
         P[x] = P[P[x]];
@@ -98,10 +102,10 @@ static int32_t find_leader(int32_t *P, int32_t x)
 }
 
 /* Union: find both leaders and re-point the larger at the smaller. */
-static void join(int32_t *P, int32_t p, int32_t q)
+static void join(int64_t *P, int64_t p, int64_t q)
 {
-    int32_t a = find_leader(P, p);
-    int32_t b = find_leader(P, q);
+    int64_t a = find_leader(P, p);
+    int64_t b = find_leader(P, q);
     if (a == b)
         return;
 #if ORACLE_MUTANT == 3
@@ -119,14 +123,14 @@ static void join(int32_t *P, int32_t p, int32_t q)
  * ign != 0, pixels of colour `ignv` are marked -1 in Start and skipped by
  * Connect, as the pixel itself and as a neighbour. */
 static void start_connect(const void *img, int dtype, int64_t H, int64_t W,
-                          int conn, int ign, uint32_t ignv, int32_t *P)
+                          int conn, int ign, uint32_t ignv, int64_t *P)
 {
     const int64_t n = H * W;
     for (int64_t i = 0; i < n; ++i)                          /* Start */
 #if ORACLE_MUTANT == 10
-        P[i] = (int32_t)i;              /* mutant: the ignored colour is labelled */
+        P[i] = i;                       /* mutant: the ignored colour is labelled */
 #else
-        P[i] = (ign && colour_at(img, dtype, i) == ignv) ? -1 : (int32_t)i;
+        P[i] = (ign && colour_at(img, dtype, i) == ignv) ? -1 : i;
 #endif
 
     for (int64_t r = 0; r < H; ++r) {
@@ -166,7 +170,7 @@ static void start_connect(const void *img, int dtype, int64_t H, int64_t W,
                 const int64_t q = rr * W + cc;
 #endif
                 if (P[q] >= 0 && colour_at(img, dtype, q) == v)
-                    join(P, (int32_t)p, (int32_t)q);
+                    join(P, p, q);
             }
         }
     }
@@ -175,22 +179,35 @@ static void start_connect(const void *img, int dtype, int64_t H, int64_t W,
 /* Stage Collapse: every pixel points straight at its leader.  P[i] <= i holds
  * for every pixel, so an ascending pass sees each parent's leader first.
  * Ignored pixels (-1) stay -1. */
-static void collapse(int32_t *P, int64_t n)
+static void collapse(int64_t *P, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
         if (P[i] >= 0)
-            P[i] = (P[i] == i) ? (int32_t)i : P[P[i]];
+            P[i] = (P[i] == i) ? i : P[P[i]];
 }
 
 static int check_args(const void *img, int dtype, int64_t B, int64_t H,
-                      int64_t W, int conn, const void *out)
+                      int64_t W, int conn, const void *out, int64_t max_pixels)
 {
     if (B < 0 || H < 0 || W < 0) return ORACLE_ERR_ARG;
     if (dtype != 1 && dtype != 3 && dtype != 4) return ORACLE_ERR_ARG;
     if (conn != 4 && conn != 8) return ORACLE_ERR_ARG;
-    if (H * W > 2147483647LL) return ORACLE_ERR_ARG;
+    if (W > 0 && H > max_pixels / W) return ORACLE_ERR_ARG;
     if (B * H * W > 0 && (img == NULL || out == NULL)) return ORACLE_ERR_ARG;
     return ORACLE_OK;
+}
+
+/* Per-image scratch of 64-bit parents for the entry points with 32-bit
+ * results; the arithmetic is the same for both widths. */
+static int64_t *scratch64(int64_t n)
+{
+    return (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+}
+
+static void narrow(const int64_t *a, int64_t n, int32_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = (int32_t)a[i];
 }
 
 /* Parent array after the Connect stage (no Collapse) -- exposed so tests can
@@ -198,26 +215,35 @@ static int check_args(const void *img, int dtype, int64_t B, int64_t H,
 int oracle_connect(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
                    int conn, int32_t *parents)
 {
-    int rc = check_args(img, dtype, B, H, W, conn, parents);
+    int rc = check_args(img, dtype, B, H, W, conn, parents, 2147483647LL);
     if (rc) return rc;
     const int64_t n = H * W;
-    for (int64_t b = 0; b < B; ++b)
-        start_connect((const char *)img + b * n * dtype, dtype, H, W, conn, 0, 0u,
-                      parents + b * n);
+    int64_t *P = scratch64(n);
+    if (!P) return ORACLE_ERR_NOMEM;
+    for (int64_t b = 0; b < B; ++b) {
+        start_connect((const char *)img + b * n * dtype, dtype, H, W, conn, 0, 0u, P);
+        narrow(P, n, parents + b * n);
+    }
+    free(P);
     return ORACLE_OK;
 }
 
+/* Start, Connect and Collapse of each image into 64-bit leaders (leaders64),
+ * or through a scratch array into 32-bit ones (leaders32). */
 static int label_images(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
-                        int conn, int ign, uint32_t ignv, int32_t *leaders)
+                        int conn, int ign, uint32_t ignv, int32_t *leaders32,
+                        int64_t *leaders64)
 {
-    int rc = check_args(img, dtype, B, H, W, conn, leaders);
-    if (rc) return rc;
     const int64_t n = H * W;
+    int64_t *tmp = NULL;
+    if (leaders32 && !(tmp = scratch64(n))) return ORACLE_ERR_NOMEM;
     for (int64_t b = 0; b < B; ++b) {
-        int32_t *P = leaders + b * n;
+        int64_t *P = leaders32 ? tmp : leaders64 + b * n;
         start_connect((const char *)img + b * n * dtype, dtype, H, W, conn, ign, ignv, P);
         collapse(P, n);
+        if (leaders32) narrow(P, n, leaders32 + b * n);
     }
+    free(tmp);
     return ORACLE_OK;
 }
 
@@ -225,7 +251,9 @@ static int label_images(const void *img, int dtype, int64_t B, int64_t H, int64_
 int oracle_label(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
                  int conn, int32_t *leaders)
 {
-    return label_images(img, dtype, B, H, W, conn, 0, 0u, leaders);
+    int rc = check_args(img, dtype, B, H, W, conn, leaders, 2147483647LL);
+    if (rc) return rc;
+    return label_images(img, dtype, B, H, W, conn, 0, 0u, leaders, NULL);
 }
 
 /* Leaders with one colour ignored ("Accountable AI starts at the pixel",
@@ -236,43 +264,91 @@ int oracle_label(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
 int oracle_label_ignore(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
                         int conn, uint32_t ignore, int32_t *leaders)
 {
-    return label_images(img, dtype, B, H, W, conn, 1, ignore, leaders);
+    int rc = check_args(img, dtype, B, H, W, conn, leaders, 2147483647LL);
+    if (rc) return rc;
+    return label_images(img, dtype, B, H, W, conn, 1, ignore, leaders, NULL);
 }
 
-/* Stage Number: leaders become 1, 2, 3, ... in reading order and every pixel
- * takes its leader's number.  Requires a valid leader image (leader[p] <= p,
- * leader[leader[p]] == leader[p]): a leader comes no later than its pixels, so
- * its number is already written when a later pixel copies it.  A pixel whose
- * leader is negative (an ignored pixel) gets 0 and is not counted.  counts
- * may be NULL. */
+/* 64-bit leaders, for images of any size: a picture of more than 2^31 pixels
+ * has reading-order indices beyond int32 ("Accountable AI starts at the
+ * pixel", ch.11 "How we know it is right", lists such images as not yet run;
+ * ch.10 shows what a size wrapped to 32 bits does).  ign != 0 ignores colour
+ * `ignore`, as oracle_label_ignore does. */
+int oracle_label64(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
+                   int conn, int ign, uint32_t ignore, int64_t *leaders)
+{
+    int rc = check_args(img, dtype, B, H, W, conn, leaders, INT64_MAX / 8);
+    if (rc) return rc;
+#if ORACLE_MUTANT == 14
+    ign = 0;                                  /* mutant: the ignored colour dropped */
+#endif
+    return label_images(img, dtype, B, H, W, conn, ign != 0, ignore, NULL, leaders);
+}
+
+/* Stage Number for one image: leaders become 1, 2, 3, ... in reading order
+ * and every pixel takes its leader's number.  Requires a valid leader image
+ * (leader[p] <= p, leader[leader[p]] == leader[p]): a leader comes no later
+ * than its pixels, so its number is already written when a later pixel copies
+ * it.  A pixel whose leader is negative (an ignored pixel) gets 0 and is not
+ * counted.  Returns the count. */
+static int64_t number_image(const int64_t *L, int64_t n, int64_t *out)
+{
+    int64_t k = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (L[i] < 0) {
+#if ORACLE_MUTANT == 9
+            k += 1;                               /* mutant: ignored pixels counted */
+#endif
+            out[i] = 0;
+        } else if (L[i] == i) {
+#if ORACLE_MUTANT == 5
+            out[i] = k;                           /* mutant: numbers start at 0 */
+            k += 1;
+#else
+            k += 1;
+            out[i] = k;
+#endif
+        } else {
+            out[i] = out[L[i]];
+        }
+    }
+    return k;
+}
+
+/* Number, 32-bit leaders and labels (through 64-bit scratch); counts may be
+ * NULL. */
 int oracle_number(const int32_t *leaders, int64_t B, int64_t H, int64_t W,
                   int32_t *labels, int32_t *counts)
 {
     if (B < 0 || H < 0 || W < 0) return ORACLE_ERR_ARG;
     const int64_t n = H * W;
     if (B * n > 0 && (leaders == NULL || labels == NULL)) return ORACLE_ERR_ARG;
+    int64_t *L = scratch64(n), *out = scratch64(n);
+    if (!L || !out) {
+        free(L);
+        free(out);
+        return ORACLE_ERR_NOMEM;
+    }
     for (int64_t b = 0; b < B; ++b) {
-        const int32_t *L = leaders + b * n;
-        int32_t *out = labels + b * n;
-        int32_t k = 0;
-        for (int64_t i = 0; i < n; ++i) {
-            if (L[i] < 0) {
-#if ORACLE_MUTANT == 9
-                k += 1;                           /* mutant: ignored pixels counted */
-#endif
-                out[i] = 0;
-            } else if (L[i] == i) {
-#if ORACLE_MUTANT == 5
-                out[i] = k;                       /* mutant: numbers start at 0 */
-                k += 1;
-#else
-                k += 1;
-                out[i] = k;
-#endif
-            } else {
-                out[i] = out[L[i]];
-            }
-        }
+        for (int64_t i = 0; i < n; ++i) L[i] = leaders[b * n + i];
+        const int64_t k = number_image(L, n, out);
+        narrow(out, n, labels + b * n);
+        if (counts) counts[b] = (int32_t)k;
+    }
+    free(L);
+    free(out);
+    return ORACLE_OK;
+}
+
+/* Number, 64-bit leaders, labels and counts; counts may be NULL. */
+int oracle_number64(const int64_t *leaders, int64_t B, int64_t H, int64_t W,
+                    int64_t *labels, int64_t *counts)
+{
+    if (B < 0 || H < 0 || W < 0) return ORACLE_ERR_ARG;
+    const int64_t n = H * W;
+    if (B * n > 0 && (leaders == NULL || labels == NULL)) return ORACLE_ERR_ARG;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t k = number_image(leaders + b * n, n, labels + b * n);
         if (counts) counts[b] = k;
     }
     return ORACLE_OK;
@@ -302,7 +378,7 @@ int oracle_count(const int32_t *leaders, int64_t B, int64_t H, int64_t W,
 int oracle_bfs_label(const void *img, int dtype, int64_t B, int64_t H, int64_t W,
                      int conn, int32_t *leaders)
 {
-    int rc = check_args(img, dtype, B, H, W, conn, leaders);
+    int rc = check_args(img, dtype, B, H, W, conn, leaders, 2147483647LL);
     if (rc) return rc;
     const int64_t n = H * W;
     int32_t *queue = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));

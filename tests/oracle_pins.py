@@ -15,6 +15,8 @@ given disagrees with:
     are 1..n in reading order, 0 for background) value for value,
   * for RGB pictures stored as three bytes per pixel (same page, ch.08-09): a
     flood fill comparing the three bytes as a tuple,
+  * for the 64-bit entry points (images beyond 2^31 pixels): the flood fill
+    and the closed form of horizontal stripes,
   * per-region statistics: the hand-derived areas, boxes and index sums of the
     TorchCC example's components, and scipy's find_objects / sum_labels /
     center_of_mass on random labellings,
@@ -479,6 +481,62 @@ def pin_closed_forms(lib):
     assert c.tolist() == [0, 0]
 
 
+def pin_wide_vs_python_bfs(lib, n_images=160, seed=20):
+    """64-bit leaders and numbers (oracle_label64 / oracle_number64, the entry
+    points for images beyond 2^31 pixels) against the pure-Python flood fill,
+    with and without an ignored colour, in every pixel type; and the closed
+    form of horizontal stripes (row r of its own colour: leader r*W, number
+    r+1), whose leaders use every index width the image has."""
+    rng = np.random.default_rng(seed)
+    for k in range(n_images):
+        H, W = int(rng.integers(1, 24)), int(rng.integers(1, 24))
+        conn = 8 if k % 2 else 4
+        kind = k % 3
+        if kind == 2:
+            imgs = random_rgb(rng, 1, H, W, int(rng.integers(1, 5)))
+            T = rgb_tuples(imgs[0])
+            img, rgb = imgs[0], True
+        else:
+            img = random_images(rng, 1, H, W, int(rng.integers(1, 5)),
+                                np.uint8 if kind == 0 else np.uint32)[0]
+            T, rgb = img, False
+        L = oracle.label64(img, conn, lib=lib, rgb=rgb)
+        assert L.dtype == np.int64
+        assert np.array_equal(L, py_bfs(T, conn)), f"case {k}: {H}x{W} conn {conn}"
+        labels, counts = oracle.number64(L, lib=lib)
+        assert labels.dtype == np.int64 and counts.dtype == np.int64
+        check_numbering(L, labels, int(counts[0]))
+        r, c = int(rng.integers(0, H)), int(rng.integers(0, W))
+        ign = img[r, c]
+        ign_v = int(ign[0]) | int(ign[1]) << 8 | int(ign[2]) << 16 if rgb else int(ign)
+        L = oracle.label64(img, conn, lib=lib, ignore=ign_v, rgb=rgb)
+        E = py_bfs_ignore(T, conn, T[r, c])
+        assert np.array_equal(L, E), f"case {k}: ignore"
+        labels, counts = oracle.number64(L, lib=lib)
+        keep = L >= 0
+        assert np.all(labels[~keep] == 0)
+        uniq = np.unique(L[keep])
+        assert counts[0] == uniq.size
+        assert np.array_equal(labels[keep], np.searchsorted(uniq, L[keep]) + 1)
+    # a batch: indices per image, counts per image
+    imgs = random_images(rng, 4, 11, 13, 3)
+    L = oracle.label64(imgs, 8, lib=lib)
+    _, counts = oracle.number64(L, lib=lib)
+    for b in range(4):
+        E = py_bfs(imgs[b], 8)
+        assert np.array_equal(L[b], E)
+        assert counts[b] == np.unique(E).size
+    # horizontal stripes: rows alternate two colours, so no row touches a row
+    # of its colour (diagonals included); leader (r, c) = r*W, number r+1
+    for H, W in ((7, 5), (40, 3)):
+        img = np.repeat((np.arange(H) % 2).astype(np.uint8)[:, None], W, axis=1)
+        for conn in (8, 4):
+            L = oracle.label64(img, conn, lib=lib)
+            assert np.array_equal(L, np.repeat(np.arange(H, dtype=np.int64)[:, None] * W, W, 1))
+            labels, counts = oracle.number64(L, lib=lib)
+            assert counts[0] == H and np.array_equal(labels, L // W + 1)
+
+
 def pin_invariants_and_numbering(lib, seed=14, n_images=200):
     rng = np.random.default_rng(seed)
     for k in range(n_images):
@@ -515,4 +573,5 @@ ALL_PINS = [
     pin_rgb_vs_python_bfs,
     pin_stats_torchcc_4x4,
     pin_stats_vs_scipy,
+    pin_wide_vs_python_bfs,
 ]

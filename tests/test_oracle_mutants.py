@@ -19,6 +19,7 @@ MUTANTS = {
     11: "RGB pixels compared on two of their three bytes",
     12: "bounding boxes end one row late",
     13: "column sums take the row index",
+    14: "the 64-bit entry point drops the ignored colour",
 }
 
 
