@@ -11,6 +11,7 @@ functions raises -- there is no CPU fallback.
     out, counts = label(img, number=True, ignore=0xFFFFFF)  # white ignored: 0
     labels, counts = number(leaders)
     counts = count(leaders)
+    out, counts = label_large(img, number=True)             # int64, any size
 
 ``img`` is a CUDA (HIP) tensor of shape [H, W] or [B, H, W], dtype uint8, or
 uint32 / int32 (the 32 bits are compared as they are), or with ``rgb=True`` an
@@ -28,7 +29,7 @@ import torch
 from . import build as _build
 
 __all__ = ["label", "number", "count", "region_stats", "workspace_bytes", "Labeller",
-           "error_word", "CclError", "library_path"]
+           "error_word", "CclError", "library_path", "label_large", "large_workspace_bytes"]
 
 CCL_U8, CCL_RGB24, CCL_U32 = 1, 3, 4
 CCL_NUMBER, CCL_IGNORE = 1, 2
@@ -66,6 +67,11 @@ def _load():
     lib.ccl_count.restype = ctypes.c_int
     lib.ccl_region_stats.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, sz, vp]
     lib.ccl_region_stats.restype = ctypes.c_int
+    lib.ccl_large_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.ccl_large_workspace_bytes.restype = sz
+    lib.ccl_label_large.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_uint32, i64, vp, vp, vp, sz, vp]
+    lib.ccl_label_large.restype = ctypes.c_int
     lib.ccl_status_string.argtypes = [ctypes.c_int]
     lib.ccl_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -123,6 +129,19 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
 
 
+def _output(out, B, H, W, dtype, device, squeeze):
+    """(tensor the kernels write, tensor returned): a new [B, H, W] tensor
+    (returned as [H, W] for a single image), or the caller's ``out`` as given,
+    which must be contiguous, of ``dtype`` and hold B*H*W values."""
+    if out is None:
+        out = torch.empty((B, H, W), dtype=dtype, device=device)
+        return out, (out[0] if squeeze else out)
+    _require_device(out, "out")
+    if out.dtype != dtype or out.numel() != B * H * W:
+        raise ValueError(f"out must be a {dtype} tensor of {B * H * W} values")
+    return out, out
+
+
 def _new_workspace(B, H, W, device):
     n = workspace_bytes(B, H, W)
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
@@ -148,12 +167,12 @@ def label(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream
     pixel) or, with ``number=True``, numbers 1..n per image.  With ``ignore`` set,
     pixels of that colour belong to no region: -1 as leaders, 0 as numbers, never
     counted.  With ``rgb``, ``img`` is an RGB picture of three bytes per pixel.
-    Returns (out, counts)."""
+    ``out``, if given, is a contiguous int32 tensor of B*H*W values (any
+    shape), returned as it is.  Returns (out, counts)."""
     _require_device(img, "img")
     x, squeeze = _batch_view(img, rgb)
     B, H, W = x.shape[:3]
-    if out is None:
-        out = torch.empty((B, H, W), dtype=torch.int32, device=img.device)
+    out, ret = _output(out, B, H, W, torch.int32, img.device, squeeze)
     counts = torch.empty(B, dtype=torch.int32, device=img.device) if with_counts else None
     if workspace is None:
         workspace = _new_workspace(B, H, W, img.device)
@@ -161,7 +180,7 @@ def label(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream
     _check(_load().ccl_label(_ptr(x), _dtype_code(x, rgb), B, H, W, int(connectivity), flags, ign,
                              _ptr(out), _ptr(counts), _ptr(workspace), workspace.numel(),
                              ctypes.c_void_p(_stream_handle(stream))))
-    return (out[0] if squeeze else out), counts
+    return ret, counts
 
 
 def number(leaders: torch.Tensor, stream=None, inplace: bool = False,
@@ -223,6 +242,36 @@ def region_stats(labels: torch.Tensor, counts: torch.Tensor, n_total: int | None
     r32 = rec.view(torch.int32)
     return {"records": rec, "area": r32[:, 4], "bbox": r32[:, 5:9], "sum_y": rec[:, 0],
             "sum_x": rec[:, 1]}
+
+
+def large_workspace_bytes(batch: int, height: int, width: int, band_rows: int = 0) -> int:
+    return int(_load().ccl_large_workspace_bytes(batch, height, width, band_rows))
+
+
+def label_large(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream=None,
+                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                with_counts: bool = True, ignore: int | None = None, rgb: bool = False,
+                band_rows: int = 0):
+    """As ``label``, for images of any size (also beyond 2^31 pixels): int64
+    leaders or numbers and int64 counts.  The image is labelled in bands of
+    ``band_rows`` rows (0: automatic, about 2^30 pixels each; else a multiple
+    of 64), joined across the band seams; results do not depend on it.
+    Returns (out, counts)."""
+    _require_device(img, "img")
+    x, squeeze = _batch_view(img, rgb)
+    B, H, W = x.shape[:3]
+    out, ret = _output(out, B, H, W, torch.int64, img.device, squeeze)
+    counts = torch.empty(B, dtype=torch.int64, device=img.device) if with_counts else None
+    if workspace is None:
+        n = large_workspace_bytes(B, H, W, band_rows)
+        if n == 2**64 - 1:
+            _check(-10 if band_rows else -3)
+        workspace = torch.zeros(max(n, 1), dtype=torch.uint8, device=img.device)
+    flags, ign = _flags(number, ignore)
+    _check(_load().ccl_label_large(_ptr(x), _dtype_code(x, rgb), B, H, W, int(connectivity), flags,
+                                   ign, int(band_rows), _ptr(out), _ptr(counts), _ptr(workspace),
+                                   workspace.numel(), ctypes.c_void_p(_stream_handle(stream))))
+    return ret, counts
 
 
 class Labeller:

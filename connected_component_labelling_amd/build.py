@@ -7,7 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "ccl_kernels.hip"), os.path.join(HERE, "csrc", "ccl_api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("ccl_kernels.hip", "ccl_api.hip", "ccl_large.hip")]
 LIB_PATH = os.path.join(HERE, "libccl.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

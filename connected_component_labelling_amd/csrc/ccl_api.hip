@@ -269,6 +269,7 @@ const char *ccl_status_string(int status)
     case CCL_ERR_HIP: return "HIP rejected a kernel launch";
     case CCL_ERR_FLAGS: return "unknown flag bits";
     case CCL_ERR_IGNORE: return "ignored colour does not fit the dtype";
+    case CCL_ERR_BAND: return "band_rows must be a non-negative multiple of 64 with band_rows*width < 2^31";
     default: return "unknown status";
     }
 }

@@ -60,8 +60,10 @@ typedef enum {
     CCL_ERR_WORKSPACE = -6,     /* workspace smaller than ccl_workspace_bytes()      */
     CCL_ERR_HIP = -7,           /* HIP rejected a kernel launch                      */
     CCL_ERR_FLAGS = -8,         /* unknown bits in flags                             */
-    CCL_ERR_IGNORE = -9         /* CCL_IGNORE with a value wider than the pixel:
+    CCL_ERR_IGNORE = -9,        /* CCL_IGNORE with a value wider than the pixel:
                                    above 255 (CCL_U8) or 0xFFFFFF (CCL_RGB24)        */
+    CCL_ERR_BAND = -10          /* ccl_label_large: band_rows negative, not a
+                                   multiple of 64, or band_rows*width > 2^31-1       */
 } ccl_status;
 
 /* Colour element types; the value is the size of one pixel in bytes.
@@ -191,6 +193,42 @@ typedef struct {
 int ccl_region_stats(const int32_t *labels, int64_t batch, int64_t height, int64_t width,
                      const int32_t *counts, int64_t n_total, ccl_region *stats,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace ccl_label_large needs for a batch of this shape
+ * and band height (256-byte aligned; its first 4 bytes are the error word, as
+ * for ccl_workspace_bytes).  Pure host arithmetic.  Returns 0 for an empty
+ * batch and SIZE_MAX for a shape or band height ccl_label_large rejects.
+ * About 4 bytes per pixel of one image, plus the tile pipeline's workspace for
+ * one band and a few bytes per pixel of the band seams' rows.
+ */
+size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, int64_t band_rows);
+
+/*
+ * ccl_label for images of any size, beyond 2^31 pixels ("Accountable AI starts
+ * at the pixel", ch.11 "How we know it is right", names such images as not run;
+ * ch.10 shows a size wrapped to 32 bits): the same leaders, numbers and
+ * counts, as 64-bit values.
+ *   colours, dtype, connectivity, flags, ignore   as for ccl_label
+ *   band_rows  0: automatic (about 2^30 pixels per band); else the rows of each
+ *              band, a multiple of 64 with band_rows*width <= 2^31-1
+ *              (CCL_ERR_BAND otherwise).  Results do not depend on it.
+ *   out        device int64 [batch, height, width]: leaders (per-image reading-
+ *              order index, -1 for an ignored pixel) or, with CCL_NUMBER,
+ *              numbers 1..n (0 for an ignored pixel)
+ *   counts     device int64 [batch] or NULL: regions per image
+ *   workspace  device, at least ccl_large_workspace_bytes(batch, height, width,
+ *              band_rows)
+ * The image is cut into bands of band_rows rows; each band is labelled by the
+ * pipeline of ccl_label, then regions are joined across the band seams and the
+ * 64-bit results written.  Images of a batch are labelled one after another.
+ * CCL_ERR_TOO_LARGE: height*width*batch > 2^46, or a band of 64 rows is wider
+ * than 2^31-1 pixels.  Memory, streams and errors as for ccl_label.
+ */
+int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
+                    int connectivity, int flags, uint32_t ignore, int64_t band_rows,
+                    int64_t *out, int64_t *counts, void *workspace, size_t workspace_bytes,
+                    void *stream);
 
 /* Static text for a status code (never NULL). */
 const char *ccl_status_string(int status);

@@ -27,7 +27,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("ccl_label", "ccl_number", "ccl_count", "ccl_workspace_bytes",
-                     "ccl_status_string"):
+                     "ccl_status_string", "ccl_label_large", "ccl_large_workspace_bytes"):
         assert required in names
 
 
@@ -118,7 +118,46 @@ def test_empty_batches_are_noops(lib):
     assert lib.ccl_number(None, 2, 5, 0, None, None, None, 0, None) == 0
 
 
+def test_large_workspace_bytes(lib):
+    f = lib.ccl_large_workspace_bytes
+    assert f(0, 10, 10, 0) == 0
+    assert f(1, 10, 0, 0) == 0
+    assert f(-1, 10, 10, 0) == 2**64 - 1
+    assert f(1, 10, 10, 63) == 2**64 - 1           # band rows not a multiple of 64
+    assert f(1, 10, 10, -64) == 2**64 - 1
+    assert f(1, 2**20, 2**16, 2**16) == 2**64 - 1  # a band of 2^32 pixels
+    one = f(1, 300, 200, 0)                        # one band: the image itself
+    banded = f(1, 300, 200, 64)
+    assert 0 < banded < one                        # smaller tile workspace, small seam tables
+    assert one % 256 == 0 and banded % 256 == 0
+    # beyond 2^31 pixels: int32 leaders for the image plus the tile workspace of
+    # one band (about 2^30 pixels), a few bytes per pixel in all
+    big = f(1, 46400, 46400, 0)
+    assert 4 * 46400 * 46400 < big < 8 * 46400 * 46400
+    # a 64-row band wider than 2^31 - 1 pixels cannot be labelled
+    assert f(1, 64, 2**25 + 64, 0) == 2**64 - 1
+    # tall narrow images: bands stay within the tile limit
+    assert f(1, 2**31 + 64, 1, 0) < 2**64 - 1
+
+
+def test_label_large_validation(lib):
+    big = 1 << 40
+    L = lib.ccl_label_large
+    assert L(FAKE, 4, 1, 8, 8, 6, 0, 0, 0, FAKE, None, FAKE, big, None) == -4
+    assert L(FAKE, 2, 1, 8, 8, 8, 0, 0, 0, FAKE, None, FAKE, big, None) == -5
+    assert L(FAKE, 4, -1, 8, 8, 8, 0, 0, 0, FAKE, None, FAKE, big, None) == -2
+    assert L(FAKE, 4, 1, 8, 8, 8, 4, 0, 0, FAKE, None, FAKE, big, None) == -8
+    assert L(FAKE, 1, 1, 8, 8, 8, 2, 256, 0, FAKE, None, FAKE, big, None) == -9
+    assert L(FAKE, 4, 1, 8, 8, 8, 0, 0, 32, FAKE, None, FAKE, big, None) == -10
+    assert L(FAKE, 4, 1, 8, 8, 8, 0, 0, -64, FAKE, None, FAKE, big, None) == -10
+    assert L(FAKE, 4, 1, 8, 8, 8, 0, 0, 0, FAKE, None, FAKE, 16, None) == -6
+    assert L(None, 4, 1, 8, 8, 8, 0, 0, 0, FAKE, None, FAKE, big, None) == -1
+    assert L(FAKE, 4, 1, 8, 8, 8, 0, 0, 0, None, None, FAKE, big, None) == -1
+    assert L(FAKE, 4, 1, 2**24, 2**24, 8, 0, 0, 0, FAKE, None, FAKE, big, None) == -3
+    assert L(None, 4, 0, 8, 8, 8, 1, 0, 0, None, None, None, 0, None) == 0
+
+
 def test_status_strings(lib):
-    for s in range(-9, 1):
+    for s in range(-10, 1):
         assert lib.ccl_status_string(s).decode()
     assert lib.ccl_status_string(-99) == b"unknown status"
