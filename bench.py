@@ -19,7 +19,10 @@ most common value) ignored (CCL_IGNORE, "Accountable AI starts at the pixel"
 ch.08 idea 4); "rgb24_leg", the same sheet stored as RGB bytes (3 B/px, read
 in place, same page ch.09), labelled whole and with the paper ignored;
 "stats_leg", the per-region statistics pass over the sheet's numbers (with
-HIP events around its two kernels; it reads 4 B/px of labels).
+HIP events around its two kernels; it reads 4 B/px of labels); "large_leg",
+ccl_label_large (64-bit leaders and numbers, bands joined across their seams)
+numbering a 46400 x 46400 tissue picture of 2.15 G pixels, beyond the int32
+index range (same page, ch.11), with HIP events around each call.
 """
 from __future__ import annotations
 
@@ -292,6 +295,59 @@ def cpu_baseline(img_np, rows: int, ccl, torch):
     }, exact
 
 
+LARGE_HW = 46400
+
+
+def large_leg(ccl, steps, warmup, stream, hip, torch):
+    """Time ccl_label_large with numbers and counts on a 46400 x 46400 u8 tissue
+    picture (the tissue workload's recipe at 2.15 G pixels; output, counts and
+    workspace allocated once).  Algorithmic bytes: 1 B read + 8 B written per
+    pixel."""
+    import numpy as np
+
+    import synth
+    H = W = LARGE_HW
+    npx = H * W
+    print("[bench] large leg: generating the 46400x46400 tissue picture ...", file=sys.stderr,
+          flush=True)
+    img = synth.tissue_image(H, W, seed=11)
+    dev = torch.from_numpy(img).cuda()
+    del img
+    ws = torch.zeros(ccl.large_workspace_bytes(1, H, W, 0), dtype=torch.uint8, device="cuda")
+    out = torch.empty((H, W), dtype=torch.int64, device="cuda")
+    lib = ccl._load()
+    counts = torch.empty(1, dtype=torch.int64, device="cuda")
+    args = [ccl._ptr(dev), ccl.CCL_U8, 1, H, W, 8, ccl.CCL_NUMBER, 0, 0, ccl._ptr(out),
+            ccl._ptr(counts), ccl._ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream)]
+    for _ in range(max(warmup, 1)):
+        ccl._check(lib.ccl_label_large(*args))
+    ev = hip.create(2 * steps)
+    torch.cuda.synchronize()
+    for k in range(steps):
+        hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k]), ctypes.c_void_p(stream.cuda_stream))
+        ccl._check(lib.ccl_label_large(*args))
+        hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k + 1]), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms = float(np.median([hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]) for k in range(steps)]))
+    hip.destroy(ev)
+    regions = int(counts.item())
+    err = ccl.error_word(ws)
+    del dev, ws, out
+    torch.cuda.empty_cache()
+    gbs = npx * 9 / (ms * 1e-3) / 1e9
+    return {
+        "workload": "tissue-46400: the tissue recipe at 46400 x 46400 u8 (2.15 Gpx > 2^31), "
+                    "8-conn, int64 numbers, 3 bands of up to 23104 rows",
+        "value": round(npx / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gpixels/s",
+        "ms_per_call": round(ms, 4),
+        "path_algorithmic_GBps": round(gbs, 1),
+        "hbm_frac_path": round(gbs / HBM_PEAK_GBS, 4),
+        "regions": regions,
+        "error_word": err,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,6 +413,7 @@ def main():
     ignore_leg = None
     rgb24_leg = None
     stats = None
+    large = None
     paper = None
     if not args.no_extra_legs:
         hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -376,6 +433,8 @@ def main():
             }
             del rgb_dev
             print(f"[bench] rgb24 legs done ({args.steps} steps each)", file=sys.stderr, flush=True)
+        large = large_leg(ccl, args.steps, args.warmup, stream, hip, torch)
+        print(f"[bench] large leg done ({args.steps} calls)", file=sys.stderr, flush=True)
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
         src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
@@ -443,6 +502,7 @@ def main():
         "ignore_leg": ignore_leg,
         "rgb24_leg": rgb24_leg,
         "stats_leg": stats,
+        "large_leg": large,
         "kernel_source": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -83,8 +83,9 @@ __device__ __forceinline__ int32_t ld_parent(const int32_t *P, int64_t x)
     return __hip_atomic_load(P + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Step 2: every seam pixel tags its band leader's own entry with the largest
-// of the leader's seam nodes.  Ignored pixels (-1) take part in nothing.
+// Step 2: the seam pixels tag their band leader's own entry with the largest
+// of the leader's run-starting seam nodes.  Ignored pixels (-1) take part in
+// nothing.
 __global__ __launch_bounds__(LB) void tag_kernel(Bands g, int32_t *lead)
 {
     const int64_t node = (int64_t)blockIdx.x * LB + threadIdx.x;
@@ -94,6 +95,11 @@ __global__ __launch_bounds__(LB) void tag_kernel(Bands g, int32_t *lead)
     int32_t *L = lead + band * g.band_px;
     const int32_t l = L[local];
     if (l == -1) return;
+    // one atomic per run of one leader along the seam row: a pixel whose left
+    // neighbour on the row has its leader leaves the tag to that run's first
+    // pixel (the leader itself, if on the row, starts its run)
+    const int64_t col = node % g.W;
+    if (l >= 0 && col > 0 && L[local - 1] == l) return;
     // l < -1: this pixel is a leader another seam pixel has tagged already
     const int64_t target = l < 0 ? local : (int64_t)l;
     atomicMin(&L[target], (int32_t)(-2 - node));
@@ -166,16 +172,25 @@ __global__ __launch_bounds__(LB) void seam_union_kernel(Bands g, const uint8_t *
     if (i >= (g.nb - 1) * g.W) return;
     const int64_t s = i / g.W;
     const int64_t c = i - s * g.W;
-    const int32_t a = C[s * 2 * g.W + g.W + c];
+    const int32_t *Cu = C + s * 2 * g.W;  // band s's last row
+    const int32_t *Cl = Cu + g.W;         // band s+1's first row
+    const int32_t a = Cl[c];
     if (a < 0) return;
     const int64_t row1 = (s + 1) * g.hb;  // band s+1's first row
     const uint32_t v = seam_colour(img, dtype, row1 * g.W + c);
+    // Pairs of nodes equal to a pair of the column before are skipped (same
+    // nodes, so same colours: the same join): straight up when both nodes
+    // repeat, up-left when the lower node repeats (it is column c-1's straight
+    // pair), up-right when the upper node repeats (it is this column's).
     const int lo = conn == 8 ? -1 : 0, hi = conn == 8 ? 1 : 0;
     for (int d = lo; d <= hi; ++d) {
         const int64_t cc = c + d;
         if (cc < 0 || cc >= g.W) continue;
-        const int32_t b = C[s * 2 * g.W + cc];
+        const int32_t b = Cu[cc];
         if (b < 0) continue;
+        if (d == 0 && c > 0 && Cl[c - 1] == a && Cu[c - 1] == b) continue;
+        if (d < 0 && Cl[c - 1] == a) continue;
+        if (d > 0 && Cu[c] == b) continue;
         if (seam_colour(img, dtype, (row1 - 1) * g.W + cc) != v) continue;
         seam_unite(P, K, a, b, err);
     }
@@ -194,38 +209,81 @@ __global__ __launch_bounds__(LB) void seam_root_kernel(Bands g, const int32_t *C
     rootkey[node] = K[r];
 }
 
-// A pixel's 64-bit leader from its band-relative entry l (not -1).
-__device__ __forceinline__ int64_t global_leader(const int32_t *lead, const int64_t *rootkey,
-                                                 int64_t base, int32_t l)
+// Block of round `base` taken by workgroup bid: workgroups are dealt to the 8
+// XCDs round-robin, so XCD j gets the j-th contiguous eighth of the round's
+// blocks; the earlier rows that a pixel's leader lookups read were then mostly
+// streamed through the same XCD's L2.
+__device__ __forceinline__ int64_t xcd_block(int64_t base, int64_t nblk, uint32_t bid,
+                                             uint32_t grid)
 {
-    if (l <= -2) return rootkey[-2 - l];  // the pixel is a tagged seam leader
-    const int32_t t = lead[base + l];
-    return t <= -2 ? rootkey[-2 - t] : base + l;
+    const int64_t left = nblk - base;
+    const uint32_t n = left < grid ? (uint32_t)left : grid;
+    if (bid >= n) return -1;
+    const uint32_t q = n >> 3, r = n & 7u;
+    const uint32_t j = bid & 7u, i = bid >> 3;
+    if (n < 8) return base + bid;
+    return base + j * q + (j < r ? j : r) + i;
+}
+
+// The 16 consecutive words of one wave: their first pixel pw0 (wave-uniform)
+// and, per word, the first pixel of its band.  Bands hold a multiple of 64
+// pixels whenever there are several, so a word never straddles two; the band
+// of the first word takes one division and later words step band by band.
+struct WaveWords {
+    int64_t pw0;
+    int64_t base[WPW];
+};
+
+__device__ __forceinline__ void wave_words(const Bands &g, int64_t w0, WaveWords &ww)
+{
+    ww.pw0 = w0 * 64;
+    int64_t base = ww.pw0 / g.band_px * g.band_px;
+    int64_t next = base + g.band_px;
+#pragma unroll
+    for (int j = 0; j < WPW; ++j) {
+        const int64_t pw = ww.pw0 + 64 * j;
+        while (pw >= next) {
+            base = next;
+            next += g.band_px;
+        }
+        ww.base[j] = base;
+    }
 }
 
 // Step 4: leader bits, per-word prefixes inside each block, block counts.
+// Workgroup k takes block k (4096 pixels), wave v its words 16v..16v+15; every
+// lane's 16 loads are issued before the first is used.
 __global__ __launch_bounds__(LB) void flag_kernel(Bands g, const int32_t *lead,
                                                   const int64_t *rootkey, uint64_t *mask,
                                                   uint16_t *wordin, uint32_t *blkcnt)
 {
     __shared__ uint32_t wtot[LWAVES];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int64_t k = blockIdx.x; k < g.nblk; k += gridDim.x) {
-        uint32_t run = 0, mine = 0;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t round = 0; round < g.nblk; round += gridDim.x) {
+        const int64_t k = xcd_block(round, g.nblk, blockIdx.x, gridDim.x);
+        if (k < 0) break;
         const int64_t w0 = k * BLK_WORDS + wave * WPW;
+        WaveWords ww;
+        wave_words(g, w0, ww);
+        int32_t l[WPW];
+#pragma unroll
         for (int j = 0; j < WPW; ++j) {
-            const int64_t pw = (w0 + j) * 64;
-            if (pw >= g.HW) break;
-            const int64_t base = pw / g.band_px * g.band_px;
-            const int64_t px = pw + lane;
-            bool is_lead = false;
-            if (px < g.HW) {
-                const int32_t l = lead[px];
-                is_lead = l == (int32_t)(px - base) || (l <= -2 && rootkey[-2 - l] == px);
-            }
+            const int64_t px = ww.pw0 + 64 * j + lane;
+            l[j] = px < g.HW ? lead[px] : -1;
+        }
+        uint32_t run = 0, mine = 0;
+        uint64_t mymask = 0;  // lane j keeps word j's bits
+#pragma unroll
+        for (int j = 0; j < WPW; ++j) {
+            const int64_t px = ww.pw0 + 64 * j + lane;
+            const bool is_lead = l[j] == (int32_t)(px - ww.base[j]) ||
+                                 (l[j] <= -2 && rootkey[-2 - l[j]] == px);
             const uint64_t m = __ballot(is_lead);
-            if (lane == 0) mask[w0 + j] = m;
-            if (lane == j) mine = run;
+            if (lane == j) {
+                mine = run;
+                mymask = m;
+            }
             run += (uint32_t)__popcll(m);
         }
         if (lane == 0) wtot[wave] = run;
@@ -235,86 +293,169 @@ __global__ __launch_bounds__(LB) void flag_kernel(Bands g, const int32_t *lead,
             off += v < wave ? wtot[v] : 0u;
             tot += wtot[v];
         }
-        if (lane < WPW && (w0 + lane) * 64 < g.HW) wordin[w0 + lane] = (uint16_t)(off + mine);
+        if (lane < WPW && (w0 + lane) * 64 < g.HW) {
+            mask[w0 + lane] = mymask;
+            wordin[w0 + lane] = (uint16_t)(off + mine);
+        }
         if (threadIdx.x == 0) blkcnt[k] = tot;
         __syncthreads();
     }
 }
 
-// Step 4b: exclusive 64-bit prefix of the block counts (one workgroup of 1024
-// threads, 16 blocks per thread per round); blkpre[nblk] and *count = total.
+// Step 4b: exclusive 64-bit prefix of the block counts in two levels: chunks
+// of CHUNK blocks scanned by one workgroup each (prefix inside the chunk, and
+// the chunk's total), the chunk totals by one workgroup, then each block adds
+// its chunk's prefix.  blkpre[nblk] and *count = the image's total.
 constexpr int SCAN_T = 1024;
 constexpr int SCAN_PER = 16;
-__global__ __launch_bounds__(SCAN_T) void block_scan_kernel(const uint32_t *blkcnt, int64_t nblk,
-                                                            int64_t *blkpre, int64_t *count)
+constexpr int64_t CHUNK = (int64_t)SCAN_T * SCAN_PER;
+
+// Exclusive scan of n values (v loaded per thread, SCAN_PER consecutive each)
+// across one workgroup of SCAN_T threads; returns this thread's first prefix
+// and the total through `total`.
+__device__ __forceinline__ int64_t wg_exclusive(int64_t sum, int64_t *wsum, int64_t &total)
+{
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int64_t inc = sum;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int64_t woff = 0;
+    total = 0;
+    for (int v = 0; v < SCAN_T / 64; ++v) {
+        woff += v < wave ? wsum[v] : 0;
+        total += wsum[v];
+    }
+    __syncthreads();
+    return woff + inc - sum;
+}
+
+__global__ __launch_bounds__(SCAN_T) void chunk_scan_kernel(const uint32_t *blkcnt, int64_t nblk,
+                                                            int64_t *blkpre, int64_t *chunktot)
 {
     __shared__ int64_t wsum[SCAN_T / 64];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t i0 = blockIdx.x * CHUNK + (int64_t)threadIdx.x * SCAN_PER;
+    uint32_t v[SCAN_PER];
+    int64_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < SCAN_PER; ++j) {
+        v[j] = i0 + j < nblk ? blkcnt[i0 + j] : 0u;
+        sum += v[j];
+    }
+    int64_t total;
+    int64_t run = wg_exclusive(sum, wsum, total);
+#pragma unroll
+    for (int j = 0; j < SCAN_PER; ++j) {
+        if (i0 + j < nblk) blkpre[i0 + j] = run;
+        run += v[j];
+    }
+    if (threadIdx.x == 0) chunktot[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(SCAN_T) void chunk_total_scan_kernel(int64_t *chunktot,
+                                                                  int64_t nchunk, int64_t *total_out,
+                                                                  int64_t *count)
+{
+    __shared__ int64_t wsum[SCAN_T / 64];
     int64_t carry = 0;
-    for (int64_t base = 0; base < nblk; base += (int64_t)SCAN_T * SCAN_PER) {
-        const int64_t i0 = base + (int64_t)t * SCAN_PER;
-        uint32_t v[SCAN_PER];
+    for (int64_t base = 0; base < nchunk; base += CHUNK) {
+        const int64_t i0 = base + (int64_t)threadIdx.x * SCAN_PER;
+        int64_t v[SCAN_PER];
         int64_t sum = 0;
         for (int j = 0; j < SCAN_PER; ++j) {
-            v[j] = i0 + j < nblk ? blkcnt[i0 + j] : 0u;
+            v[j] = i0 + j < nchunk ? chunktot[i0 + j] : 0;
             sum += v[j];
         }
-        int64_t inc = sum;  // inclusive scan over the wave
-        for (int d = 1; d < 64; d <<= 1) {
-            const int64_t o = __shfl_up(inc, d, 64);
-            if (lane >= d) inc += o;
-        }
-        if (lane == 63) wsum[wave] = inc;
-        __syncthreads();
-        int64_t woff = 0, total = 0;
-        for (int v2 = 0; v2 < SCAN_T / 64; ++v2) {
-            woff += v2 < wave ? wsum[v2] : 0;
-            total += wsum[v2];
-        }
-        int64_t run = carry + woff + inc - sum;
+        int64_t total;
+        int64_t run = carry + wg_exclusive(sum, wsum, total);
         for (int j = 0; j < SCAN_PER; ++j) {
-            if (i0 + j < nblk) blkpre[i0 + j] = run;
+            if (i0 + j < nchunk) chunktot[i0 + j] = run;  // in place: now the chunk's prefix
             run += v[j];
         }
         carry += total;
-        __syncthreads();
     }
-    if (t == 0) {
-        blkpre[nblk] = carry;
+    if (threadIdx.x == 0) {
+        *total_out = carry;
         if (count) *count = carry;
     }
 }
 
+__global__ __launch_bounds__(LB) void chunk_add_kernel(int64_t *blkpre, int64_t nblk,
+                                                       const int64_t *chunkpre)
+{
+    const int64_t i = (int64_t)blockIdx.x * LB + threadIdx.x;
+    if (i < nblk) blkpre[i] += chunkpre[i / CHUNK];
+}
+
 // Step 5: each pixel's 64-bit leader (number = 0) or number 1..n (number = 1);
-// ignored pixels get -1 or 0.
+// ignored pixels get -1 or 0.  Same wave layout as the flag pass, in phases
+// over all 16 words of the wave, so that each phase's loads are in flight
+// together: the band-relative entries, the entries of their leaders, then the
+// leaders' mask words, word prefixes and block prefixes.  The pass is bound by
+// these dependent round trips, not by its registers: phases over groups of 4
+// words (7 waves per SIMD instead of 2) took twice as long.
+constexpr int FG = WPW;
 __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
                                                    const int64_t *rootkey, const uint64_t *mask,
                                                    const uint16_t *wordin, const int64_t *blkpre,
                                                    int number, int64_t *out)
 {
     const int lane = threadIdx.x & 63;
-    const int64_t stride = (int64_t)gridDim.x * LWAVES;
-    for (int64_t w = (int64_t)blockIdx.x * LWAVES + (threadIdx.x >> 6); w < g.nwords;
-         w += stride) {
-        const int64_t pw = w * 64;
-        const int64_t base = pw / g.band_px * g.band_px;
-        const int64_t px = pw + lane;
-        if (px >= g.HW) continue;
-        const int32_t l = lead[px];
-        int64_t v;
-        if (l == -1) {
-            v = number ? 0 : -1;
-        } else {
-            const int64_t G = global_leader(lead, rootkey, base, l);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t round = 0; round < g.nblk; round += gridDim.x) {
+        const int64_t k = xcd_block(round, g.nblk, blockIdx.x, gridDim.x);
+        if (k < 0) break;
+        const int64_t w0 = k * BLK_WORDS + wave * WPW;
+        WaveWords ww;
+        wave_words(g, w0, ww);
+#pragma unroll 1
+        for (int j0 = 0; j0 < WPW; j0 += FG) {
+            int32_t l[FG], t[FG];
+#pragma unroll
+            for (int j = 0; j < FG; ++j) {
+                const int64_t px = ww.pw0 + 64 * (j0 + j) + lane;
+                l[j] = px < g.HW ? lead[px] : -1;
+            }
+#pragma unroll
+            for (int j = 0; j < FG; ++j)  // the leader's own entry (a tag if a seam node)
+                t[j] = l[j] >= 0 ? lead[ww.base[j0 + j] + l[j]] : l[j];
+            int64_t G[FG];
+#pragma unroll
+            for (int j = 0; j < FG; ++j) {
+                const int32_t tag = l[j] <= -2 ? l[j] : t[j];
+                G[j] = ww.base[j0 + j] + (l[j] < 0 ? 0 : l[j]);
+                if (tag <= -2) G[j] = rootkey[-2 - tag];
+            }
             if (number) {
-                const int64_t wd = G >> 6;
-                const uint64_t below = mask[wd] & ((uint64_t(1) << (G & 63)) - 1);
-                v = 1 + blkpre[G >> BLK_SHIFT] + wordin[wd] + __popcll(below);
+                uint64_t m[FG];
+                uint32_t wi[FG];
+                int64_t bp[FG];
+#pragma unroll
+                for (int j = 0; j < FG; ++j) {
+                    const int64_t Gs = l[j] == -1 ? 0 : G[j];
+                    m[j] = mask[Gs >> 6];
+                    wi[j] = wordin[Gs >> 6];
+                    bp[j] = blkpre[Gs >> BLK_SHIFT];
+                }
+#pragma unroll
+                for (int j = 0; j < FG; ++j) {
+                    const int64_t px = ww.pw0 + 64 * (j0 + j) + lane;
+                    const uint64_t below = m[j] & ((uint64_t(1) << (G[j] & 63)) - 1);
+                    const int64_t v = l[j] == -1 ? 0 : 1 + bp[j] + wi[j] + __popcll(below);
+                    if (px < g.HW) __builtin_nontemporal_store(v, out + px);
+                }
             } else {
-                v = G;
+#pragma unroll
+                for (int j = 0; j < FG; ++j) {
+                    const int64_t px = ww.pw0 + 64 * (j0 + j) + lane;
+                    const int64_t v = l[j] == -1 ? -1 : G[j];
+                    if (px < g.HW) __builtin_nontemporal_store(v, out + px);
+                }
             }
         }
-        __builtin_nontemporal_store(v, out + px);
     }
 }
 
@@ -324,7 +465,7 @@ struct LargeLayout {
     Bands g;
     Layout band;      // tile-pipeline layout of the tallest band
     size_t off_lead, off_C, off_P, off_K, off_root, off_mask, off_wordin, off_blkcnt, off_blkpre,
-        total;
+        off_chunk, total;
 };
 
 // Fills `L` for one image of the batch; returns a ccl_status.
@@ -375,6 +516,7 @@ static int make_large_layout(int64_t H, int64_t W, int64_t band_rows, LargeLayou
     L->off_wordin = take((size_t)g.nwords * sizeof(uint16_t));
     L->off_blkcnt = take((size_t)g.nblk * sizeof(uint32_t));
     L->off_blkpre = take((size_t)(g.nblk + 1) * sizeof(int64_t));
+    L->off_chunk = take((size_t)((g.nblk + CHUNK - 1) / CHUNK) * sizeof(int64_t));
     L->total = off;
     return CCL_OK;
 }
@@ -452,6 +594,8 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
     uint16_t *wordin = (uint16_t *)(ws + L.off_wordin);
     uint32_t *blkcnt = (uint32_t *)(ws + L.off_blkcnt);
     int64_t *blkpre = (int64_t *)(ws + L.off_blkpre);
+    int64_t *chunk = (int64_t *)(ws + L.off_chunk);
+    const int64_t nchunk = (g.nblk + CHUNK - 1) / CHUNK;
     uint32_t *err = (uint32_t *)ws;  // the band workspace's error word
     const int number = (flags & CCL_NUMBER) != 0;
     const bool need_scan = number || counts != nullptr;
@@ -483,19 +627,21 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
                                err);
         }
         // 4. leader bits and their prefixes
+        const unsigned gblk = (unsigned)(g.nblk < (1 << 22) ? g.nblk : (1 << 22));
         if (need_scan) {
-            const unsigned gf = (unsigned)(g.nblk < (1 << 20) ? g.nblk : (1 << 20));
-            hipLaunchKernelGGL(flag_kernel, dim3(gf), dim3(LB), 0, s, g, lead, rootkey, mask,
+            hipLaunchKernelGGL(flag_kernel, dim3(gblk), dim3(LB), 0, s, g, lead, rootkey, mask,
                                wordin, blkcnt);
-            hipLaunchKernelGGL(block_scan_kernel, dim3(1), dim3(SCAN_T), 0, s, blkcnt, g.nblk,
-                               blkpre, counts ? counts + b : (int64_t *)nullptr);
+            hipLaunchKernelGGL(chunk_scan_kernel, dim3((unsigned)nchunk), dim3(SCAN_T), 0, s,
+                               blkcnt, g.nblk, blkpre, chunk);
+            hipLaunchKernelGGL(chunk_total_scan_kernel, dim3(1), dim3(SCAN_T), 0, s, chunk, nchunk,
+                               blkpre + g.nblk, counts ? counts + b : (int64_t *)nullptr);
+            if (nchunk > 1)
+                hipLaunchKernelGGL(chunk_add_kernel, dim3(grid_for(g.nblk, INT32_MAX)), dim3(LB),
+                                   0, s, blkpre, g.nblk, chunk);
         }
         // 5. 64-bit results
-        const int64_t waves = g.nwords;
-        const int64_t blocks = (waves + LWAVES - 1) / LWAVES;
-        hipLaunchKernelGGL(final_kernel, dim3((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))),
-                           dim3(LB), 0, s, g, lead, rootkey, mask, wordin, blkpre, number,
-                           out + b * g.HW);
+        hipLaunchKernelGGL(final_kernel, dim3(gblk), dim3(LB), 0, s, g, lead, rootkey, mask,
+                           wordin, blkpre, number, out + b * g.HW);
     }
     return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }
