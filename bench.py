@@ -22,7 +22,9 @@ in place, same page ch.09), labelled whole and with the paper ignored;
 HIP events around its two kernels; it reads 4 B/px of labels); "large_leg",
 ccl_label_large (64-bit leaders and numbers, bands joined across their seams)
 numbering a 46400 x 46400 tissue picture of 2.15 G pixels, beyond the int32
-index range (same page, ch.11), with HIP events around each call.
+index range (same page, ch.11), with HIP events around each call (alone with
+--large-only); "two_stream_leg", the headline call issued alternately on two
+streams with their own outputs and workspaces (wall clock over K steps).
 """
 from __future__ import annotations
 
@@ -233,6 +235,37 @@ def extra_leg(lab, dev, npx, bpp, args, stream, hip, torch, ignore=None, rgb=Fal
     }
 
 
+def two_stream_leg(ccl, lab, dev, npx, bpp, steps, warmup, torch):
+    """The labelled+numbered call issued alternately on two streams, each with
+    its own Labeller (output, counts, workspace), on the same sheet: K steps
+    by wall clock between two device synchronisations.  Consecutive calls are
+    independent, so one stream's latency-bound seam and scan kernels can run
+    beside the other's HBM-bound tile pass and final write."""
+    B, H, W = lab.B, lab.H, lab.W
+    labs = [lab, ccl.Labeller((B, H, W), device="cuda", connectivity=lab.connectivity)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    for k in range(max(warmup, 2)):
+        labs[k % 2](dev, number=True, stream=streams[k % 2])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        labs[k % 2](dev, number=True, stream=streams[k % 2])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    same = bool(torch.equal(labs[0].out, labs[1].out))
+    err = ccl.error_word(labs[1].workspace)
+    del labs[1]
+    return {
+        "streams": 2,
+        "value": round(npx / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gpixels/s",
+        "ms_per_step": round(ms, 4),
+        "hbm_frac_path": round(npx * (bpp + 4) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "outputs_identical": same,
+        "error_word": err,
+    }
+
+
 def stats_leg(ccl, labels, counts, npx, steps, warmup, stream, hip, torch):
     """Time ccl_region_stats over a numbered labelling (outputs and workspace
     allocated once, before the timed calls)."""
@@ -356,6 +389,8 @@ def main():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--cpu-rows", type=int, default=-1,
                     help="rows of the sheet the CPU baseline labels (-1 = all, 0 = skip)")
+    ap.add_argument("--large-only", action="store_true",
+                    help="time only ccl_label_large on the 2.15-Gpx tissue picture (for profiling)")
     ap.add_argument("--no-extra-legs", action="store_true",
                     help="time the headline call only (no paper-ignored or RGB legs)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -391,6 +426,11 @@ def main():
     import synth
 
     desc, (B, H, W), np_dtype, seed = synth.CONFIGS[args.config]
+    if args.large_only:
+        line = {"large_leg": large_leg(ccl, args.steps, args.warmup, torch.cuda.current_stream(),
+                                       HipEvents(), torch)}
+        print(json.dumps(line), flush=True)
+        return
     t0 = time.perf_counter()
     img_np = synth.generate(args.config)
     gen_s = time.perf_counter() - t0
@@ -414,6 +454,7 @@ def main():
     rgb24_leg = None
     stats = None
     large = None
+    two = None
     paper = None
     if not args.no_extra_legs:
         hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -433,6 +474,8 @@ def main():
             }
             del rgb_dev
             print(f"[bench] rgb24 legs done ({args.steps} steps each)", file=sys.stderr, flush=True)
+        two = two_stream_leg(ccl, lab, dev, npx, bpp, args.steps, args.warmup, torch)
+        print(f"[bench] two-stream leg done ({args.steps} steps)", file=sys.stderr, flush=True)
         large = large_leg(ccl, args.steps, args.warmup, stream, hip, torch)
         print(f"[bench] large leg done ({args.steps} calls)", file=sys.stderr, flush=True)
     if args.copy_calibration_mb > 0:
@@ -502,6 +545,7 @@ def main():
         "ignore_leg": ignore_leg,
         "rgb24_leg": rgb24_leg,
         "stats_leg": stats,
+        "two_stream_leg": two,
         "large_leg": large,
         "kernel_source": kernel_source_hash(),
     }
