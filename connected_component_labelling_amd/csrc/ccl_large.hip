@@ -20,6 +20,8 @@
 //   4. (numbers or counts) a pass flags each image's leaders in one bit per
 //      pixel, with per-word and per-block counts, and a scan turns the block
 //      counts into 64-bit prefixes (ch.08 idea 5 "Number without a giant list");
+//      for numbers, each leader's own entry then takes its number as a code
+//      relative to its band;
 //   5. a final pass writes each pixel's 64-bit leader or number.
 //
 // The seams between bands are the same seams a band per GPU would have: this
@@ -232,12 +234,14 @@ __device__ __forceinline__ int64_t xcd_block(int64_t base, int64_t nblk, uint32_
 struct WaveWords {
     int64_t pw0;
     int64_t base[WPW];
+    int64_t band[WPW];
 };
 
 __device__ __forceinline__ void wave_words(const Bands &g, int64_t w0, WaveWords &ww)
 {
     ww.pw0 = w0 * 64;
-    int64_t base = ww.pw0 / g.band_px * g.band_px;
+    int64_t band = ww.pw0 / g.band_px;
+    int64_t base = band * g.band_px;
     int64_t next = base + g.band_px;
 #pragma unroll
     for (int j = 0; j < WPW; ++j) {
@@ -245,8 +249,10 @@ __device__ __forceinline__ void wave_words(const Bands &g, int64_t w0, WaveWords
         while (pw >= next) {
             base = next;
             next += g.band_px;
+            ++band;
         }
         ww.base[j] = base;
+        ww.band[j] = band;
     }
 }
 
@@ -390,21 +396,80 @@ __global__ __launch_bounds__(LB) void chunk_add_kernel(int64_t *blkpre, int64_t 
     if (i < nblk) blkpre[i] += chunkpre[i / CHUNK];
 }
 
-// Step 5: each pixel's 64-bit leader (number = 0) or number 1..n (number = 1);
-// ignored pixels get -1 or 0.  Same wave layout as the flag pass, in phases
-// over all 16 words of the wave, so that each phase's loads are in flight
-// together: the band-relative entries, the entries of their leaders, then the
-// leaders' mask words, word prefixes and block prefixes.  The pass is bound by
-// these dependent round trips, not by its registers: phases over groups of 4
-// words (7 waves per SIMD instead of 2) took twice as long.
+// Leaders before pixel index G of the image (G's own bit excluded).
+__device__ __forceinline__ int64_t leaders_before(const uint64_t *mask, const uint16_t *wordin,
+                                                  const int64_t *blkpre, int64_t G)
+{
+    const uint64_t below = mask[G >> 6] & ((uint64_t(1) << (G & 63)) - 1);
+    return blkpre[G >> BLK_SHIFT] + wordin[G >> 6] + __popcll(below);
+}
+
+// Numbers through codes (when every code fits int32): leaders before each
+// band's first pixel; each seam node's root's number; then every global
+// leader's own entry becomes -(2 + nseam + r), r its rank among the global
+// leaders of its band, so that a pixel finds its number in its leader's
+// entry.  Merged seam leaders keep their tags and go through rootnum.
+__global__ __launch_bounds__(LB) void band_offset_kernel(Bands g, const uint64_t *mask,
+                                                         const uint16_t *wordin,
+                                                         const int64_t *blkpre, int64_t *bandoff)
+{
+    const int64_t b = (int64_t)blockIdx.x * LB + threadIdx.x;
+    if (b >= g.nb) return;
+    bandoff[b] = b == 0 ? 0 : leaders_before(mask, wordin, blkpre, b * g.band_px);
+}
+
+__global__ __launch_bounds__(LB) void root_number_kernel(Bands g, const int32_t *C,
+                                                         const int64_t *rootkey,
+                                                         const uint64_t *mask,
+                                                         const uint16_t *wordin,
+                                                         const int64_t *blkpre, int64_t *rootnum)
+{
+    const int64_t node = (int64_t)blockIdx.x * LB + threadIdx.x;
+    if (node >= g.nseam || C[node] != node) return;
+    rootnum[node] = 1 + leaders_before(mask, wordin, blkpre, rootkey[node]);
+}
+
+__global__ __launch_bounds__(LB) void leader_code_kernel(Bands g, const uint64_t *mask,
+                                                         const uint16_t *wordin,
+                                                         const int64_t *blkpre,
+                                                         const int64_t *bandoff, int32_t *lead)
+{
+    const int64_t stride = (int64_t)gridDim.x * LB;
+    for (int64_t w = (int64_t)blockIdx.x * LB + threadIdx.x; w < g.nwords; w += stride) {
+        uint64_t m = mask[w];
+        if (m == 0) continue;
+        const int64_t pw = w * 64;
+        // rank of the word's first leader among its band's global leaders
+        int64_t r = blkpre[w >> (BLK_SHIFT - 6)] + wordin[w] - bandoff[pw / g.band_px];
+        while (m) {
+            const int i = __builtin_ctzll(m);
+            m &= m - 1;
+            lead[pw + i] = (int32_t)(-2 - g.nseam - r);
+            ++r;
+        }
+    }
+}
+
+// Step 5: each pixel's 64-bit leader (OUT_LEADERS) or number 1..n
+// (OUT_NUMBERS); ignored pixels get -1 or 0.  Same wave layout as the flag
+// pass, in phases over all 16 words of the wave so that each phase's loads are
+// in flight together: the pixels' own entries, then their leaders' entries.  A
+// leader's entry holds what the pixel needs: a code (its number, through its
+// band's offset), a tag (a seam node: its root's key or number), or, for
+// leaders, its own index.  The pass is bound by these dependent round trips,
+// not by its registers (phases over groups of 4 words, with 7 waves per SIMD
+// instead of 2, took twice as long).
 constexpr int FG = WPW;
+enum { OUT_LEADERS = 0, OUT_NUMBERS = 1 };
+template <int MODE>
 __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
-                                                   const int64_t *rootkey, const uint64_t *mask,
-                                                   const uint16_t *wordin, const int64_t *blkpre,
-                                                   int number, int64_t *out)
+                                                   const int64_t *rootkey, const int64_t *rootnum,
+                                                   const int64_t *bandoff, int64_t *out,
+                                                   uint32_t *err)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t code0 = (int32_t)(-2 - g.nseam);  // codes are code0 - r
     for (int64_t round = 0; round < g.nblk; round += gridDim.x) {
         const int64_t k = xcd_block(round, g.nblk, blockIdx.x, gridDim.x);
         if (k < 0) break;
@@ -420,8 +485,28 @@ __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
                 l[j] = px < g.HW ? lead[px] : -1;
             }
 #pragma unroll
-            for (int j = 0; j < FG; ++j)  // the leader's own entry (a tag if a seam node)
+            for (int j = 0; j < FG; ++j)  // the leader's own entry (a tag or a code)
                 t[j] = l[j] >= 0 ? lead[ww.base[j0 + j] + l[j]] : l[j];
+            if constexpr (MODE == OUT_NUMBERS) {
+#pragma unroll
+                for (int j = 0; j < FG; ++j) {
+                    const int64_t px = ww.pw0 + 64 * (j0 + j) + lane;
+                    const int32_t e = t[j];
+                    int64_t v;
+                    if (e == -1) {
+                        v = 0;
+                    } else if (e <= code0) {
+                        v = bandoff[ww.band[j0 + j]] + (int64_t)(code0 - e) + 1;
+                    } else if (e <= -2) {
+                        v = rootnum[-2 - e];
+                    } else {
+                        v = 0;  // every band leader is coded or tagged by now
+                        atomicOr(err, ERR_LOOP);
+                    }
+                    if (px < g.HW) __builtin_nontemporal_store(v, out + px);
+                }
+                continue;
+            }
             int64_t G[FG];
 #pragma unroll
             for (int j = 0; j < FG; ++j) {
@@ -429,25 +514,7 @@ __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
                 G[j] = ww.base[j0 + j] + (l[j] < 0 ? 0 : l[j]);
                 if (tag <= -2) G[j] = rootkey[-2 - tag];
             }
-            if (number) {
-                uint64_t m[FG];
-                uint32_t wi[FG];
-                int64_t bp[FG];
-#pragma unroll
-                for (int j = 0; j < FG; ++j) {
-                    const int64_t Gs = l[j] == -1 ? 0 : G[j];
-                    m[j] = mask[Gs >> 6];
-                    wi[j] = wordin[Gs >> 6];
-                    bp[j] = blkpre[Gs >> BLK_SHIFT];
-                }
-#pragma unroll
-                for (int j = 0; j < FG; ++j) {
-                    const int64_t px = ww.pw0 + 64 * (j0 + j) + lane;
-                    const uint64_t below = m[j] & ((uint64_t(1) << (G[j] & 63)) - 1);
-                    const int64_t v = l[j] == -1 ? 0 : 1 + bp[j] + wi[j] + __popcll(below);
-                    if (px < g.HW) __builtin_nontemporal_store(v, out + px);
-                }
-            } else {
+            {
 #pragma unroll
                 for (int j = 0; j < FG; ++j) {
                     const int64_t px = ww.pw0 + 64 * (j0 + j) + lane;
@@ -464,8 +531,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct LargeLayout {
     Bands g;
     Layout band;      // tile-pipeline layout of the tallest band
-    size_t off_lead, off_C, off_P, off_K, off_root, off_mask, off_wordin, off_blkcnt, off_blkpre,
-        off_chunk, total;
+    size_t off_lead, off_C, off_P, off_K, off_root, off_rootnum, off_bandoff, off_mask, off_wordin,
+        off_blkcnt, off_blkpre, off_chunk, total;
 };
 
 // Fills `L` for one image of the batch; returns a ccl_status.
@@ -512,6 +579,8 @@ static int make_large_layout(int64_t H, int64_t W, int64_t band_rows, LargeLayou
     L->off_P = take(ns * sizeof(int32_t));
     L->off_K = take(ns * sizeof(int64_t));
     L->off_root = take(ns * sizeof(int64_t));
+    L->off_rootnum = take(ns * sizeof(int64_t));
+    L->off_bandoff = take((size_t)g.nb * sizeof(int64_t));
     L->off_mask = take((size_t)g.nwords * sizeof(uint64_t));
     L->off_wordin = take((size_t)g.nwords * sizeof(uint16_t));
     L->off_blkcnt = take((size_t)g.nblk * sizeof(uint32_t));
@@ -582,6 +651,10 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
     LargeLayout L;
     rc = make_large_layout(height, width, band_rows, &L);
     if (rc != CCL_OK) return rc;
+    // numbers pass through the leaders' int32 entries as -(2 + nseam + r), r a
+    // rank inside a band: every such code must fit
+    if ((flags & CCL_NUMBER) && L.g.nseam + L.g.band_px > (int64_t)INT32_MAX - 2)
+        return band_rows ? CCL_ERR_BAND : CCL_ERR_TOO_LARGE;
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
     const Bands &g = L.g;
     char *ws = (char *)workspace;
@@ -590,6 +663,8 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
     int32_t *P = (int32_t *)(ws + L.off_P);
     int64_t *K = (int64_t *)(ws + L.off_K);
     int64_t *rootkey = (int64_t *)(ws + L.off_root);
+    int64_t *rootnum = (int64_t *)(ws + L.off_rootnum);
+    int64_t *bandoff = (int64_t *)(ws + L.off_bandoff);
     uint64_t *mask = (uint64_t *)(ws + L.off_mask);
     uint16_t *wordin = (uint16_t *)(ws + L.off_wordin);
     uint32_t *blkcnt = (uint32_t *)(ws + L.off_blkcnt);
@@ -640,8 +715,21 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
                                    0, s, blkpre, g.nblk, chunk);
         }
         // 5. 64-bit results
-        hipLaunchKernelGGL(final_kernel, dim3(gblk), dim3(LB), 0, s, g, lead, rootkey, mask,
-                           wordin, blkpre, number, out + b * g.HW);
+        int64_t *o = out + b * g.HW;
+        if (!number) {
+            hipLaunchKernelGGL(final_kernel<OUT_LEADERS>, dim3(gblk), dim3(LB), 0, s, g, lead,
+                               rootkey, rootnum, bandoff, o, err);
+        } else {
+            hipLaunchKernelGGL(band_offset_kernel, dim3(grid_for(g.nb, INT32_MAX)), dim3(LB), 0, s,
+                               g, mask, wordin, blkpre, bandoff);
+            if (g.nb > 1)
+                hipLaunchKernelGGL(root_number_kernel, dim3(grid_for(g.nseam, INT32_MAX)), dim3(LB),
+                                   0, s, g, C, rootkey, mask, wordin, blkpre, rootnum);
+            hipLaunchKernelGGL(leader_code_kernel, dim3(grid_for(g.nwords, 1 << 20)), dim3(LB), 0,
+                               s, g, mask, wordin, blkpre, bandoff, lead);
+            hipLaunchKernelGGL(final_kernel<OUT_NUMBERS>, dim3(gblk), dim3(LB), 0, s, g,
+                               lead, rootkey, rootnum, bandoff, o, err);
+        }
     }
     return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }

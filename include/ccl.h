@@ -211,7 +211,8 @@ size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, i
  * counts, as 64-bit values.
  *   colours, dtype, connectivity, flags, ignore   as for ccl_label
  *   band_rows  0: automatic (about 2^30 pixels per band); else the rows of each
- *              band, a multiple of 64 with band_rows*width <= 2^31-1
+ *              band, a multiple of 64 with band_rows*width <= 2^31-1, and with
+ *              CCL_NUMBER also band_rows*width + 2*width*(bands-1) <= 2^31-3
  *              (CCL_ERR_BAND otherwise).  Results do not depend on it.
  *   out        device int64 [batch, height, width]: leaders (per-image reading-
  *              order index, -1 for an ignored pixel) or, with CCL_NUMBER,

@@ -155,6 +155,10 @@ def test_label_large_validation(lib):
     assert L(FAKE, 4, 1, 8, 8, 8, 0, 0, 0, None, None, FAKE, big, None) == -1
     assert L(FAKE, 4, 1, 2**24, 2**24, 8, 0, 0, 0, FAKE, None, FAKE, big, None) == -3
     assert L(None, 4, 0, 8, 8, 8, 1, 0, 0, None, None, None, 0, None) == 0
+    # numbers: a band of 2^31 - 64 pixels leaves no room for the seam codes
+    W = 2**25 - 1
+    assert L(FAKE, 1, 1, 128, W, 8, 1, 0, 64, FAKE, None, FAKE, big, None) == -10
+    assert L(FAKE, 1, 1, 128, W, 8, 0, 0, 64, FAKE, None, FAKE, 16, None) == -6
 
 
 def test_status_strings(lib):
