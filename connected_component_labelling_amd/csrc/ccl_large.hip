@@ -451,24 +451,45 @@ __global__ __launch_bounds__(LB) void leader_code_kernel(Bands g, const uint64_t
 }
 
 // Step 5: each pixel's 64-bit leader (OUT_LEADERS) or number 1..n
-// (OUT_NUMBERS); ignored pixels get -1 or 0.  Same wave layout as the flag
-// pass, in phases over all 16 words of the wave so that each phase's loads are
-// in flight together: the pixels' own entries, then their leaders' entries.  A
-// leader's entry holds what the pixel needs: a code (its number, through its
-// band's offset), a tag (a seam node: its root's key or number), or, for
-// leaders, its own index.  The pass is bound by these dependent round trips,
-// not by its registers (phases over groups of 4 words, with 7 waves per SIMD
-// instead of 2, took twice as long).
-constexpr int FG = WPW;
+// (OUT_NUMBERS); ignored pixels get -1 or 0.  A wave takes the same 16 words
+// as in the flag pass, as 4 groups of 256 pixels with 4 consecutive pixels per
+// lane (16-byte loads of the entries, 16-byte stores of the results), in
+// phases so that each phase's loads are in flight together: the pixels' own
+// entries, then their leaders' entries.  A leader's entry holds what the pixel
+// needs: a code (its number, through its band's offset), a tag (a seam node:
+// its root's key or number), or, for leaders, its own index.
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+typedef long long v2i64 __attribute__((ext_vector_type(2)));
+constexpr int FGRP = WPW / 4;  // groups of 256 pixels per wave
 enum { OUT_LEADERS = 0, OUT_NUMBERS = 1 };
+
+template <int MODE>
+__device__ __forceinline__ int64_t out_value(int32_t l, int32_t t, int64_t base, int64_t boff,
+                                             int32_t code0, const int64_t *rootkey,
+                                             const int64_t *rootnum, uint32_t *err)
+{
+    if (MODE == OUT_NUMBERS) {
+        if (t == -1) return 0;
+        if (t <= code0) return boff + (int64_t)(code0 - t) + 1;
+        if (t <= -2) return rootnum[-2 - t];
+        atomicOr(err, ERR_LOOP);  // every band leader is coded or tagged by now
+        return 0;
+    }
+    if (l == -1) return -1;
+    const int32_t tag = l <= -2 ? l : t;
+    if (tag <= -2) return rootkey[-2 - tag];
+    return base + l;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
                                                    const int64_t *rootkey, const int64_t *rootnum,
                                                    const int64_t *bandoff, int64_t *out,
-                                                   uint32_t *err)
+                                                   int out16, uint32_t *err)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = lane >> 4;  // the lane's word inside a group of 4
     const int32_t code0 = (int32_t)(-2 - g.nseam);  // codes are code0 - r
     for (int64_t round = 0; round < g.nblk; round += gridDim.x) {
         const int64_t k = xcd_block(round, g.nblk, blockIdx.x, gridDim.x);
@@ -476,51 +497,58 @@ __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
         const int64_t w0 = k * BLK_WORDS + wave * WPW;
         WaveWords ww;
         wave_words(g, w0, ww);
-#pragma unroll 1
-        for (int j0 = 0; j0 < WPW; j0 += FG) {
-            int32_t l[FG], t[FG];
+        int64_t base[FGRP], boff[FGRP];
 #pragma unroll
-            for (int j = 0; j < FG; ++j) {
-                const int64_t px = ww.pw0 + 64 * (j0 + j) + lane;
-                l[j] = px < g.HW ? lead[px] : -1;
+        for (int i = 0; i < FGRP; ++i) {
+            const int j = 4 * i;
+            base[i] = q == 0 ? ww.base[j] : q == 1 ? ww.base[j + 1] : q == 2 ? ww.base[j + 2]
+                                                                          : ww.base[j + 3];
+            if (MODE == OUT_NUMBERS) {
+                const int64_t b = q == 0 ? ww.band[j] : q == 1 ? ww.band[j + 1]
+                                        : q == 2 ? ww.band[j + 2] : ww.band[j + 3];
+                boff[i] = bandoff[b];
             }
+        }
+        int32_t l[FGRP][4], t[FGRP][4];
 #pragma unroll
-            for (int j = 0; j < FG; ++j)  // the leader's own entry (a tag or a code)
-                t[j] = l[j] >= 0 ? lead[ww.base[j0 + j] + l[j]] : l[j];
-            if constexpr (MODE == OUT_NUMBERS) {
+        for (int i = 0; i < FGRP; ++i) {
+            const int64_t px = ww.pw0 + 256 * i + 4 * lane;
+            if (px + 3 < g.HW) {
+                const v4i32 v = *(const v4i32 *)(lead + px);
+                l[i][0] = v.x;
+                l[i][1] = v.y;
+                l[i][2] = v.z;
+                l[i][3] = v.w;
+            } else {
 #pragma unroll
-                for (int j = 0; j < FG; ++j) {
-                    const int64_t px = ww.pw0 + 64 * (j0 + j) + lane;
-                    const int32_t e = t[j];
-                    int64_t v;
-                    if (e == -1) {
-                        v = 0;
-                    } else if (e <= code0) {
-                        v = bandoff[ww.band[j0 + j]] + (int64_t)(code0 - e) + 1;
-                    } else if (e <= -2) {
-                        v = rootnum[-2 - e];
-                    } else {
-                        v = 0;  // every band leader is coded or tagged by now
-                        atomicOr(err, ERR_LOOP);
-                    }
-                    if (px < g.HW) __builtin_nontemporal_store(v, out + px);
-                }
-                continue;
+                for (int e = 0; e < 4; ++e) l[i][e] = px + e < g.HW ? lead[px + e] : -1;
             }
-            int64_t G[FG];
+        }
 #pragma unroll
-            for (int j = 0; j < FG; ++j) {
-                const int32_t tag = l[j] <= -2 ? l[j] : t[j];
-                G[j] = ww.base[j0 + j] + (l[j] < 0 ? 0 : l[j]);
-                if (tag <= -2) G[j] = rootkey[-2 - tag];
-            }
-            {
+        for (int i = 0; i < FGRP; ++i)
 #pragma unroll
-                for (int j = 0; j < FG; ++j) {
-                    const int64_t px = ww.pw0 + 64 * (j0 + j) + lane;
-                    const int64_t v = l[j] == -1 ? -1 : G[j];
-                    if (px < g.HW) __builtin_nontemporal_store(v, out + px);
-                }
+            for (int e = 0; e < 4; ++e)
+                t[i][e] = l[i][e] >= 0 ? lead[base[i] + l[i][e]] : l[i][e];
+#pragma unroll
+        for (int i = 0; i < FGRP; ++i) {
+            const int64_t px = ww.pw0 + 256 * i + 4 * lane;
+            int64_t v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = out_value<MODE>(l[i][e], t[i][e], base[i], boff[i], code0, rootkey,
+                                       rootnum, err);
+            if (out16 && px + 3 < g.HW) {
+                v2i64 a, b;
+                a.x = v[0];
+                a.y = v[1];
+                b.x = v[2];
+                b.y = v[3];
+                __builtin_nontemporal_store(a, (v2i64 *)(out + px));
+                __builtin_nontemporal_store(b, (v2i64 *)(out + px + 2));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (px + e < g.HW) __builtin_nontemporal_store(v[e], out + px + e);
             }
         }
     }
@@ -716,9 +744,10 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
         }
         // 5. 64-bit results
         int64_t *o = out + b * g.HW;
+        const int o16 = ((uintptr_t)o & 15u) == 0;  // 16-byte stores where aligned
         if (!number) {
             hipLaunchKernelGGL(final_kernel<OUT_LEADERS>, dim3(gblk), dim3(LB), 0, s, g, lead,
-                               rootkey, rootnum, bandoff, o, err);
+                               rootkey, rootnum, bandoff, o, o16, err);
         } else {
             hipLaunchKernelGGL(band_offset_kernel, dim3(grid_for(g.nb, INT32_MAX)), dim3(LB), 0, s,
                                g, mask, wordin, blkpre, bandoff);
@@ -728,7 +757,7 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
             hipLaunchKernelGGL(leader_code_kernel, dim3(grid_for(g.nwords, 1 << 20)), dim3(LB), 0,
                                s, g, mask, wordin, blkpre, bandoff, lead);
             hipLaunchKernelGGL(final_kernel<OUT_NUMBERS>, dim3(gblk), dim3(LB), 0, s, g,
-                               lead, rootkey, rootnum, bandoff, o, err);
+                               lead, rootkey, rootnum, bandoff, o, o16, err);
         }
     }
     return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
