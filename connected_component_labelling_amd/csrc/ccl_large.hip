@@ -240,6 +240,14 @@ struct WaveWords {
 __device__ __forceinline__ void wave_words(const Bands &g, int64_t w0, WaveWords &ww)
 {
     ww.pw0 = w0 * 64;
+    if (g.nb == 1) {  // one band: the whole image
+#pragma unroll
+        for (int j = 0; j < WPW; ++j) {
+            ww.base[j] = 0;
+            ww.band[j] = 0;
+        }
+        return;
+    }
     int64_t band = ww.pw0 / g.band_px;
     int64_t base = band * g.band_px;
     int64_t next = base + g.band_px;

@@ -129,6 +129,11 @@ def test_large_batch(ccl):
     check_large(ccl, "batch 3x150x130", img, 8, band_rows=64)
     img = synth.bernoulli_batch(4, 300, 90, seed=9)
     check_large(ccl, "bernoulli batch 4x300x90", img, 8, band_rows=128)
+    # an odd number of pixels per image: every other image's int64 output
+    # starts 8 bytes off a 16-byte boundary (the 8-byte store path)
+    img = rng.integers(0, 3, size=(3, 133, 21)).astype(np.uint8)
+    check_large(ccl, "batch 3x133x21 (odd H*W)", img, 8, band_rows=64)
+    check_large(ccl, "batch 3x133x21 (odd H*W)", img, 4, band_rows=0)
 
 
 @pytest.mark.timeout(900)
