@@ -223,8 +223,10 @@ size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, i
  * The image is cut into bands of band_rows rows; each band is labelled by the
  * pipeline of ccl_label, then regions are joined across the band seams and the
  * 64-bit results written.  Images of a batch are labelled one after another.
- * CCL_ERR_TOO_LARGE: height*width*batch > 2^46, or a band of 64 rows is wider
- * than 2^31-1 pixels.  Memory, streams and errors as for ccl_label.
+ * CCL_ERR_TOO_LARGE: height*width*batch > 2^46, a band of 64 rows is wider
+ * than 2^31-1 pixels, or (CCL_NUMBER, automatic bands) a band's pixels plus
+ * 2*width per seam exceed 2^31-3 (numbers pass through int32 codes).  Memory,
+ * streams and errors as for ccl_label.
  */
 int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
                     int connectivity, int flags, uint32_t ignore, int64_t band_rows,
