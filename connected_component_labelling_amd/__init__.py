@@ -33,6 +33,7 @@ __all__ = ["label", "number", "count", "region_stats", "workspace_bytes", "Label
 
 CCL_U8, CCL_RGB24, CCL_U32 = 1, 3, 4
 CCL_NUMBER, CCL_IGNORE = 1, 2
+CCL_WS_ERR_LOOP = 1
 
 _lib = None
 
@@ -144,12 +145,26 @@ def _output(out, B, H, W, dtype, device, squeeze):
 
 def _new_workspace(B, H, W, device):
     n = workspace_bytes(B, H, W)
-    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+    if n == 2**64 - 1:
+        raise CclError("image or batch too large to index" if min(B, H, W) >= 0
+                       else "batch, height or width is negative")
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def error_word(workspace: torch.Tensor) -> int:
-    """The workspace's error word (nonzero only if a kernel hit a safety bound)."""
+    """The workspace's error word as the last call left it (each call clears it
+    first; nonzero only if a bounded loop of that call gave up).  Reading it
+    waits for the device."""
     return int(workspace[:4].view(torch.int32).item())
+
+
+def _check_word(workspace: torch.Tensor, stream):
+    """Wait for the call on ``stream`` and raise if it set the error word."""
+    (stream if stream is not None else torch.cuda.current_stream()).synchronize()
+    err = error_word(workspace)
+    if err != 0:
+        raise CclError(f"a bounded loop gave up (workspace error word 0x{err:x}): the labels "
+                       f"of this call are not valid")
 
 
 def _flags(number: bool, ignore) -> tuple[int, int]:
@@ -162,13 +177,16 @@ def _flags(number: bool, ignore) -> tuple[int, int]:
 
 def label(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream=None,
           workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
-          with_counts: bool = True, ignore: int | None = None, rgb: bool = False):
+          with_counts: bool = True, ignore: int | None = None, rgb: bool = False,
+          check: bool = False):
     """Label ``img``: leaders (per-image reading-order index of each region's first
     pixel) or, with ``number=True``, numbers 1..n per image.  With ``ignore`` set,
     pixels of that colour belong to no region: -1 as leaders, 0 as numbers, never
     counted.  With ``rgb``, ``img`` is an RGB picture of three bytes per pixel.
     ``out``, if given, is a contiguous int32 tensor of B*H*W values (any
-    shape), returned as it is.  Returns (out, counts)."""
+    shape), returned as it is.  With ``check``, waits for the call and raises
+    CclError if one of its bounded loops gave up (the default does not wait).
+    Returns (out, counts)."""
     _require_device(img, "img")
     x, squeeze = _batch_view(img, rgb)
     B, H, W = x.shape[:3]
@@ -180,6 +198,8 @@ def label(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream
     _check(_load().ccl_label(_ptr(x), _dtype_code(x, rgb), B, H, W, int(connectivity), flags, ign,
                              _ptr(out), _ptr(counts), _ptr(workspace), workspace.numel(),
                              ctypes.c_void_p(_stream_handle(stream))))
+    if check and B * H * W > 0:
+        _check_word(workspace, stream)
     return ret, counts
 
 
@@ -251,26 +271,36 @@ def large_workspace_bytes(batch: int, height: int, width: int, band_rows: int = 
 def label_large(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream=None,
                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
                 with_counts: bool = True, ignore: int | None = None, rgb: bool = False,
-                band_rows: int = 0):
+                band_rows: int = 0, check: bool = False):
     """As ``label``, for images of any size (also beyond 2^31 pixels): int64
     leaders or numbers and int64 counts.  The image is labelled in bands of
     ``band_rows`` rows (0: automatic, about 2^30 pixels each; else a multiple
     of 64), joined across the band seams; results do not depend on it.
-    Returns (out, counts)."""
+    ``check`` as for ``label``.  Returns (out, counts)."""
     _require_device(img, "img")
     x, squeeze = _batch_view(img, rgb)
     B, H, W = x.shape[:3]
     out, ret = _output(out, B, H, W, torch.int64, img.device, squeeze)
     counts = torch.empty(B, dtype=torch.int64, device=img.device) if with_counts else None
+    flags, ign = _flags(number, ignore)
+    lib = _load()
+
+    def call(ws, nbytes):
+        return lib.ccl_label_large(_ptr(x), _dtype_code(x, rgb), B, H, W, int(connectivity), flags,
+                                   ign, int(band_rows), _ptr(out), _ptr(counts), ws, nbytes,
+                                   ctypes.c_void_p(_stream_handle(stream)))
+
     if workspace is None:
         n = large_workspace_bytes(B, H, W, band_rows)
         if n == 2**64 - 1:
-            _check(-10 if band_rows else -3)
-        workspace = torch.zeros(max(n, 1), dtype=torch.uint8, device=img.device)
-    flags, ign = _flags(number, ignore)
-    _check(_load().ccl_label_large(_ptr(x), _dtype_code(x, rgb), B, H, W, int(connectivity), flags,
-                                   ign, int(band_rows), _ptr(out), _ptr(counts), _ptr(workspace),
-                                   workspace.numel(), ctypes.c_void_p(_stream_handle(stream))))
+            # the shape or band height is rejected: the call names why (its
+            # checks all run on the host before anything is enqueued)
+            _check(call(ctypes.c_void_p(256), 0))
+            _check(-3)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=img.device)
+    _check(call(_ptr(workspace), workspace.numel()))
+    if check and B * H * W > 0:
+        _check_word(workspace, stream)
     return ret, counts
 
 

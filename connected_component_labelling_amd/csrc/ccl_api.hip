@@ -103,19 +103,29 @@ static int finish_launches()
     return e == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }
 
+// Checks of ccl_label's arguments other than the buffers (host only).
+static int check_label_args(int dtype, int64_t B, int64_t H, int64_t W, int conn, int flags,
+                            uint32_t ignore, bool *empty)
+{
+    if (flags & ~(CCL_NUMBER | CCL_IGNORE)) return CCL_ERR_FLAGS;
+    int rc = check_shape(B, H, W, empty);
+    if (rc != CCL_OK) return rc;
+    if (dtype != CCL_U8 && dtype != CCL_RGB24 && dtype != CCL_U32) return CCL_ERR_DTYPE;
+    if (conn != 4 && conn != 8) return CCL_ERR_CONNECTIVITY;
+    if ((flags & CCL_IGNORE) && dtype != CCL_U32 && ignore >= (1u << (8 * dtype)))
+        return CCL_ERR_IGNORE;
+    return CCL_OK;
+}
+
 static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int64_t W, int conn,
                       int flags, uint32_t ignore, int32_t *out, int32_t *counts, void *workspace,
                       size_t workspace_bytes, void *stream, void **events, int n_events)
 {
-    if (flags & ~(CCL_NUMBER | CCL_IGNORE)) return CCL_ERR_FLAGS;
     bool empty;
-    int rc = check_shape(B, H, W, &empty);
+    int rc = check_label_args(dtype, B, H, W, conn, flags, ignore, &empty);
     if (rc != CCL_OK) return rc;
-    if (dtype != CCL_U8 && dtype != CCL_RGB24 && dtype != CCL_U32) return CCL_ERR_DTYPE;
-    if (conn != 4 && conn != 8) return CCL_ERR_CONNECTIVITY;
-    const int ign = (flags & CCL_IGNORE) != 0;
-    if (ign && dtype != CCL_U32 && ignore >= (1u << (8 * dtype))) return CCL_ERR_IGNORE;
     if (events != nullptr && n_events < 6) return CCL_ERR_NULL;
+    const int ign = (flags & CCL_IGNORE) != 0;
     hipStream_t s = (hipStream_t)stream;
     if (empty) {
         if (counts && B > 0) {
@@ -136,7 +146,7 @@ static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int6
         if (events) (void)hipEventRecord((hipEvent_t)events[i], s);
     };
     mark(0);
-    launch_tile(colours, dtype, conn, ign, ignore, L.g, w, s);
+    launch_tile(colours, dtype, conn, ign, ignore, L.g, w, 1, s);
     mark(1);
     launch_seam(L.g, w, conn, s);
     mark(2);
@@ -269,7 +279,9 @@ const char *ccl_status_string(int status)
     case CCL_ERR_HIP: return "HIP rejected a kernel launch";
     case CCL_ERR_FLAGS: return "unknown flag bits";
     case CCL_ERR_IGNORE: return "ignored colour does not fit the dtype";
-    case CCL_ERR_BAND: return "band_rows must be a non-negative multiple of 64 with band_rows*width < 2^31";
+    case CCL_ERR_BAND:
+        return "band_rows must be a non-negative multiple of 64 with band_rows*width < 2^31 "
+               "(with numbers also band_rows*width + 2*width*(bands-1) <= 2^31-3)";
     default: return "unknown status";
     }
 }

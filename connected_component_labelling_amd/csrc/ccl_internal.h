@@ -138,9 +138,10 @@ Work bind_work(const Layout &L, void *workspace);
 
 // Launchers (enqueue only).  dtype_bytes is 1, 3 (RGB) or 4, conn is 4 or 8.
 // ignore: pixels of colour ign take part in nothing (their regions are neither
-// labelled nor counted)
+// labelled nor counted).  clear_err: the tile pass clears the workspace's
+// error word first (the first kernel of a call).
 void launch_tile(const void *img, int dtype_bytes, int conn, int ignore, uint32_t ign,
-                 const Geom &g, const Work &w, hipStream_t s);
+                 const Geom &g, const Work &w, int clear_err, hipStream_t s);
 void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s);
 void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s);
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,

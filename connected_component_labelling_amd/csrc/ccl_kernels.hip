@@ -325,26 +325,12 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v)
            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
 }
 
-// v with lane i < 16 replaced by the wave-uniform value x: one v_writelane
-// (the lane is an inline constant, as the scalar data already takes the one
-// scalar operand an instruction may read; i is a constant once inlined).  The
-// compiler sees an opaque per-lane operation, so this is used only for values
-// built in straight-line code and stored at once (tile headers), never for
-// values kept across divergent code.
-static_assert(RPW <= 16 && sizeof(TileHdr) / 4 <= 16, "write_lane covers lanes 0..15");
+// v with lane i replaced by the wave-uniform value x: a plain select on the
+// lane id, which the compiler sees whole (other lanes keep their values).
+// Used for tile-header words built in straight-line code.
 __device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t x, int i)
 {
-    x = (uint32_t)__builtin_amdgcn_readfirstlane((int)x);  // into a scalar register
-#define CCL_WRITELANE(L) \
-    case L: asm("v_writelane_b32 %0, %1, " #L : "+v"(v) : "s"(x)); break;
-    switch (i) {
-        CCL_WRITELANE(0) CCL_WRITELANE(1) CCL_WRITELANE(2) CCL_WRITELANE(3)
-        CCL_WRITELANE(4) CCL_WRITELANE(5) CCL_WRITELANE(6) CCL_WRITELANE(7)
-        CCL_WRITELANE(8) CCL_WRITELANE(9) CCL_WRITELANE(10) CCL_WRITELANE(11)
-        CCL_WRITELANE(12) CCL_WRITELANE(13) CCL_WRITELANE(14) CCL_WRITELANE(15)
-    }
-#undef CCL_WRITELANE
-    return v;
+    return lane_id() == i ? x : v;
 }
 
 constexpr int QCAP = 256;  // join queue of one wave (a ring; at most 63 + 128 pending)
@@ -899,7 +885,8 @@ struct TileArgs {
     const T *img;
     Geom g;
     Work w;
-    uint32_t ign;  // the ignored colour (IGN instances only)
+    uint32_t ign;        // the ignored colour (IGN instances only)
+    uint32_t clear_err;  // workgroup 0 clears the error word (the call's first kernel)
 };
 
 template <typename T, int CONN, bool IGN>
@@ -912,6 +899,9 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void
     const Work &w = a.w;
     __shared__ TileLds<IGN> s;
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // no kernel of this call has run before this one, and the later ones set
+    // the word only after it has ended
+    if (blockIdx.x == 0 && threadIdx.x == 0 && a.clear_err) *w.err = 0u;
     const uint32_t t = remap_tile(blockIdx.x, gridDim.x);
     const TilePos tp = tile_pos(t, g);
     if (tp.vh == TH && tp.vw == TW)
@@ -1847,6 +1837,7 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
 __global__ __launch_bounds__(BLOCK) void leader_flag_kernel(const int32_t *leaders, Geom g,
                                                             Work w, int write_mask)
 {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *w.err = 0u;  // the call's first kernel
     clear_bands(g, w);
     const int lane = lane_id();
     const uint64_t nsegs = (uint64_t)g.ntiles * TH;
@@ -2139,8 +2130,9 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(StatsArgs a)
 // Entries of every region start empty (area 0, box (INT32_MAX, INT32_MAX, -1,
 // -1), sums 0); block 0 also writes the first entry of each image.
 __global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t n_total,
-                                                           int64_t *off)
+                                                           int64_t *off, uint32_t *err)
 {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0u;  // the call's first kernel
     for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < n_total;
          i += (int64_t)gridDim.x * BLOCK) {
         uint64_t *r = (uint64_t *)&a.rec[i];
@@ -2178,10 +2170,10 @@ static inline unsigned grid_of(int64_t n, int64_t per)
 
 template <typename T, int CONN>
 static void launch_tile_t(const void *img, int ignore, uint32_t ign, const Geom &g, const Work &w,
-                          hipStream_t s)
+                          int clear_err, hipStream_t s)
 {
     const dim3 grid((unsigned)g.ntiles), block(BLOCK);
-    const TileArgs<T> a{(const T *)img, g, w, ign};
+    const TileArgs<T> a{(const T *)img, g, w, ign, (uint32_t)(clear_err != 0)};
     if (ignore)
         hipLaunchKernelGGL((tile_label_kernel<T, CONN, true>), grid, block, 0, s, a);
     else
@@ -2189,17 +2181,18 @@ static void launch_tile_t(const void *img, int ignore, uint32_t ign, const Geom 
 }
 
 void launch_tile(const void *img, int dtype_bytes, int conn, int ignore, uint32_t ign,
-                 const Geom &g, const Work &w, hipStream_t s)
+                 const Geom &g, const Work &w, int clear_err, hipStream_t s)
 {
+    const int c = clear_err;
     if (dtype_bytes == 1) {
-        if (conn == 8) launch_tile_t<uint8_t, 8>(img, ignore, ign, g, w, s);
-        else launch_tile_t<uint8_t, 4>(img, ignore, ign, g, w, s);
+        if (conn == 8) launch_tile_t<uint8_t, 8>(img, ignore, ign, g, w, c, s);
+        else launch_tile_t<uint8_t, 4>(img, ignore, ign, g, w, c, s);
     } else if (dtype_bytes == 3) {
-        if (conn == 8) launch_tile_t<Rgb24, 8>(img, ignore, ign, g, w, s);
-        else launch_tile_t<Rgb24, 4>(img, ignore, ign, g, w, s);
+        if (conn == 8) launch_tile_t<Rgb24, 8>(img, ignore, ign, g, w, c, s);
+        else launch_tile_t<Rgb24, 4>(img, ignore, ign, g, w, c, s);
     } else {
-        if (conn == 8) launch_tile_t<uint32_t, 8>(img, ignore, ign, g, w, s);
-        else launch_tile_t<uint32_t, 4>(img, ignore, ign, g, w, s);
+        if (conn == 8) launch_tile_t<uint32_t, 8>(img, ignore, ign, g, w, c, s);
+        else launch_tile_t<uint32_t, 4>(img, ignore, ign, g, w, c, s);
     }
 }
 
@@ -2273,7 +2266,7 @@ void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geo
     if (iblocks > 4096) iblocks = 4096;
     if (iblocks < 1) iblocks = 1;
     hipLaunchKernelGGL(stats_init_kernel, dim3((unsigned)iblocks), dim3(BLOCK), 0, s, a, n_total,
-                       (int64_t *)w.bandst);
+                       (int64_t *)w.bandst, w.err);
     const int64_t blocks = g.B * (int64_t)a.ay * (int64_t)a.ax;
     hipLaunchKernelGGL(stats_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
 }

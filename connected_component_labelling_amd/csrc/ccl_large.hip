@@ -248,13 +248,16 @@ __device__ __forceinline__ void wave_words(const Bands &g, int64_t w0, WaveWords
         }
         return;
     }
+    // words past the image keep the last band (their values are never used,
+    // and every band index stays below nb)
     int64_t band = ww.pw0 / g.band_px;
+    if (band > g.nb - 1) band = g.nb - 1;
     int64_t base = band * g.band_px;
     int64_t next = base + g.band_px;
 #pragma unroll
     for (int j = 0; j < WPW; ++j) {
         const int64_t pw = ww.pw0 + 64 * j;
-        while (pw >= next) {
+        while (pw >= next && next < g.HW) {
             base = next;
             next += g.band_px;
             ++band;
@@ -583,13 +586,14 @@ static int make_large_layout(int64_t H, int64_t W, int64_t band_rows, LargeLayou
         if (hb > tile_rows) hb = tile_rows;
         hb = hb / 64 * 64;
         if (hb < 64) hb = 64;
-        if (hb * W > INT32_MAX) return CCL_ERR_TOO_LARGE;  // a 64-row band is too wide
     } else {
         if (band_rows < 0 || band_rows % 64 != 0) return CCL_ERR_BAND;
-        if (band_rows > INT32_MAX / W) return CCL_ERR_BAND;
         hb = band_rows;
     }
-    if (hb >= H) hb = H;  // one band: the whole image
+    // one band is the whole image (its height need not be a multiple of 64);
+    // the band's pixels must be indexable by the tile pipeline
+    if (hb >= H) hb = H;
+    if (hb > INT32_MAX / W) return band_rows ? CCL_ERR_BAND : CCL_ERR_TOO_LARGE;
     g.H = H;
     g.W = W;
     g.HW = H * W;
@@ -721,8 +725,9 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
             Layout Lb;
             if (!make_layout(1, rows, g.W, &Lb)) return CCL_ERR_TOO_LARGE;
             const Work w = bind_work(Lb, workspace);
+            // the first band's tile pass clears the error word for the whole call
             launch_tile(img + (size_t)(r0 * g.W) * px_bytes, dtype, connectivity, ign, ignore,
-                        Lb.g, w, s);
+                        Lb.g, w, b == 0 && k == 0, s);
             launch_seam(Lb.g, w, connectivity, s);
             launch_resolve(Lb.g, w, 0, s);
             launch_final(Lb.g, w, lead + r0 * g.W, 0, 0xFFFFFFFFu, s);

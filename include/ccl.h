@@ -63,7 +63,9 @@ typedef enum {
     CCL_ERR_IGNORE = -9,        /* CCL_IGNORE with a value wider than the pixel:
                                    above 255 (CCL_U8) or 0xFFFFFF (CCL_RGB24)        */
     CCL_ERR_BAND = -10          /* ccl_label_large: band_rows negative, not a
-                                   multiple of 64, or band_rows*width > 2^31-1       */
+                                   multiple of 64, or band_rows*width > 2^31-1, or
+                                   (CCL_NUMBER) band_rows*width + 2*width*(bands-1)
+                                   > 2^31-3: numbers pass through int32 codes        */
 } ccl_status;
 
 /* Colour element types; the value is the size of one pixel in bytes.
@@ -93,11 +95,21 @@ enum { CCL_NUMBER = 1, CCL_IGNORE = 2 };
  * Bytes of device workspace any call below needs for a batch of this shape.
  * Pure host arithmetic (no HIP call).  Returns 0 for an empty batch and
  * SIZE_MAX for a negative shape.  The workspace must be 256-byte aligned (any
- * HIP allocation is).  Its first 4 bytes are an error word that kernels set
- * to a nonzero value if an internal safety bound is ever hit; callers that
- * want to check it zero the workspace once after allocating it.
+ * HIP allocation is); its contents need no initialisation.
+ *
+ * Error word.  The workspace's first 4 bytes are an error word.  Every call
+ * that takes a workspace clears it in its first kernel, and sets bit 0
+ * (CCL_WS_ERR_LOOP) if a bounded loop gave up: the seam unions and walks
+ * (2^22 steps each), the numbering scan's wait for an earlier band (2^22
+ * polls) and, in ccl_label_large, a band-seam union (2^20 steps).  None of
+ * these bounds is reached by a correct run; a call that reaches one still
+ * returns CCL_OK (the return value only covers what the host can check before
+ * enqueueing), and its labels must then be taken as wrong.  Read the word
+ * after the stream has reached the end of the call (the Python binding's
+ * check=True does that and raises).
  */
 size_t ccl_workspace_bytes(int64_t batch, int64_t height, int64_t width);
+enum { CCL_WS_ERR_LOOP = 1 };
 
 /*
  * Label a batch of colour images: Start, Connect, Collapse and (with
@@ -151,7 +163,10 @@ int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t wi
 
 /*
  * Count the regions of a leader image: counts[b] = number of pixels p of image
- * b with leaders[p] == p.
+ * b with leaders[p] == p, i.e. the leaders, one per region ("Accountable AI
+ * starts at the pixel", ch.04 "Point at a leader": the pixel that points at
+ * itself leads its group; ch.10 "What we saw in NPP" compares labellers by
+ * this count of regions per image).
  *   leaders  device int32 [batch, height, width] (any int32 values)
  *   counts   device int32 [batch], required
  */

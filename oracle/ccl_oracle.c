@@ -37,7 +37,8 @@
  *     the raster two-pass scan over already-visited neighbours, 4- and
  *     8-connectivity; its introduction names the uses of a labelling, such as
  *     a region's bounding box.
- *   same page, ch.11: images of more than 2^31 pixels; their leaders need
+ *   "Accountable AI starts at the pixel", ch.11 "How we know it is right":
+ *     images of more than 2^31 pixels were not run; their leaders need
  *     64-bit indices (oracle_label64, oracle_number64).  The union-find below
  *     works on 64-bit parents for every entry point; the 32-bit ones narrow
  *     the result.

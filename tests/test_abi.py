@@ -138,6 +138,12 @@ def test_large_workspace_bytes(lib):
     assert f(1, 64, 2**25 + 64, 0) == 2**64 - 1
     # tall narrow images: bands stay within the tile limit
     assert f(1, 2**31 + 64, 1, 0) < 2**64 - 1
+    # short very wide images that ccl_label accepts: a single band is the whole
+    # image (fewer than 64 rows), not a 64-row band
+    for H, W in [(1, 2**26), (32, 40_000_000), (63, 2**31 // 64)]:
+        assert lib.ccl_workspace_bytes(1, H, W) < 2**64 - 1
+        assert f(1, H, W, 0) < 2**64 - 1, (H, W)
+        assert f(1, H, W, 64) < 2**64 - 1, (H, W)
 
 
 def test_label_large_validation(lib):

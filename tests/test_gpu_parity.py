@@ -479,6 +479,53 @@ def test_side_stream_and_reused_workspace(ccl):
         assert np.array_equal(o.cpu().numpy(), exp)
 
 
+def test_two_streams_at_once(ccl):
+    """Calls on two streams in flight together, each with its own workspace,
+    on different images (the spiral and the u8 batch, whose seam passes run
+    long), repeated so that they overlap; every result against the oracle."""
+    work = [synth.spiral_image(2048, 2048, seed=3), synth.bernoulli_batch(8, 512, 512, seed=2)]
+    exp = []
+    for im in work:
+        announce("two streams at once", im, 8)
+        exp.append(oracle.number(oracle.label(im, 8)))
+    devs = [to_device(im) for im in work]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    labs = [ccl.Labeller(tuple((im if im.ndim == 3 else im[None]).shape), device="cuda")
+            for im in work]
+    outs = [[], []]
+    torch.cuda.synchronize()
+    for _ in range(4):
+        for k in (0, 1):  # enqueue both before waiting on either
+            labs[k](devs[k], number=True, stream=streams[k])
+            with torch.cuda.stream(streams[k]):
+                outs[k].append((labs[k].out.clone(), labs[k].counts.clone()))
+    torch.cuda.synchronize()
+    for k in (0, 1):
+        assert ccl.error_word(labs[k].workspace) == 0
+        el, ec = exp[k]
+        for o, c in outs[k]:
+            assert np.array_equal(o.cpu().numpy().reshape(el.shape), el), f"stream {k}: labels"
+            assert np.array_equal(c.cpu().numpy(), ec), f"stream {k}: counts"
+
+
+def test_error_word_is_cleared_by_each_call(ccl):
+    """Each call clears the workspace's error word first: a workspace full of
+    ones still reads 0 after a good call, and check=True passes."""
+    img = synth.lines_image(300, 500, seed=8)
+    announce("error word cleared", img, 8)
+    ws = torch.full((ccl.workspace_bytes(1, 300, 500),), 0xFF, dtype=torch.uint8, device="cuda")
+    out, c = ccl.label(to_device(img), 8, number=True, workspace=ws, check=True)
+    assert ccl.error_word(ws) == 0
+    exp, ec = oracle.number(oracle.label(img, 8))
+    assert np.array_equal(out.cpu().numpy(), exp) and np.array_equal(c.cpu().numpy(), ec)
+    # ccl_number / ccl_count clear it too
+    leaders, _ = ccl.label(to_device(img), 8)
+    ws.fill_(0xFF)
+    ccl.number(leaders, workspace=ws)
+    torch.cuda.synchronize()
+    assert ccl.error_word(ws) == 0
+
+
 def test_empty_inputs(ccl):
     for shape in [(0, 5, 5), (2, 0, 7), (3, 4, 0)]:
         img = torch.zeros(shape, dtype=torch.uint8, device="cuda")
