@@ -12,6 +12,7 @@ functions raises -- there is no CPU fallback.
     labels, counts = number(leaders)
     counts = count(leaders)
     out, counts = label_large(img, number=True)             # int64, any size
+    out, counts = label_noalloc(img, number=True)           # no device allocation
 
 ``img`` is a CUDA (HIP) tensor of shape [H, W] or [B, H, W], dtype uint8, or
 uint32 / int32 (the 32 bits are compared as they are), or with ``rgb=True`` an
@@ -29,11 +30,13 @@ import torch
 from . import build as _build
 
 __all__ = ["label", "number", "count", "region_stats", "workspace_bytes", "Labeller",
-           "error_word", "CclError", "library_path", "label_large", "large_workspace_bytes"]
+           "error_word", "CclError", "library_path", "label_large", "large_workspace_bytes",
+           "label_noalloc", "SCRATCH_BYTES"]
 
 CCL_U8, CCL_RGB24, CCL_U32 = 1, 3, 4
 CCL_NUMBER, CCL_IGNORE = 1, 2
 CCL_WS_ERR_LOOP = 1
+SCRATCH_BYTES = 64 << 20   # CCL_SCRATCH_BYTES: the static workspace of ccl_label_noalloc
 
 _lib = None
 
@@ -73,6 +76,9 @@ def _load():
     lib.ccl_label_large.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_uint32, i64, vp, vp, vp, sz, vp]
     lib.ccl_label_large.restype = ctypes.c_int
+    lib.ccl_label_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_uint32, vp, vp, vp]
+    lib.ccl_label_noalloc.restype = ctypes.c_int
     lib.ccl_status_string.argtypes = [ctypes.c_int]
     lib.ccl_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -200,6 +206,31 @@ def label(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream
                              ctypes.c_void_p(_stream_handle(stream))))
     if check and B * H * W > 0:
         _check_word(workspace, stream)
+    return ret, counts
+
+
+def label_noalloc(img: torch.Tensor, connectivity: int = 8, number: bool = False, stream=None,
+                  out: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                  ignore: int | None = None, rgb: bool = False):
+    """``label`` through ccl_label_noalloc: no workspace, the library's static
+    per-GPU scratch array instead (batches up to SCRATCH_BYTES of workspace;
+    calls that overlap on one GPU race).  With ``out`` and ``counts`` given
+    (contiguous device int32 tensors of B*H*W and B values) nothing is
+    allocated.  Returns (out, counts)."""
+    _require_device(img, "img")
+    x, squeeze = _batch_view(img, rgb)
+    B, H, W = x.shape[:3]
+    out, ret = _output(out, B, H, W, torch.int32, img.device, squeeze)
+    if counts is None:
+        counts = torch.empty(B, dtype=torch.int32, device=img.device)
+    else:
+        _require_device(counts, "counts")
+        if counts.dtype != torch.int32 or counts.numel() != B:
+            raise ValueError(f"counts must be an int32 tensor of {B} values")
+    flags, ign = _flags(number, ignore)
+    _check(_load().ccl_label_noalloc(_ptr(x), _dtype_code(x, rgb), B, H, W, int(connectivity),
+                                     flags, ign, _ptr(out), _ptr(counts),
+                                     ctypes.c_void_p(_stream_handle(stream))))
     return ret, counts
 
 

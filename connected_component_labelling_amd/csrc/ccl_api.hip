@@ -5,6 +5,8 @@
 
 #include <limits.h>
 
+#include <mutex>
+
 namespace ccl {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -161,6 +163,30 @@ static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int6
     return finish_launches();
 }
 
+// ---- the workspace of ccl_label_noalloc: one static device array per GPU.
+// Host code never uses the array's name as an address (on the host it is only
+// a stand-in for the symbol): its device address is looked up once per device
+// with hipGetSymbolAddress, with that device current, and kept here.
+static __device__ __align__(256) unsigned char scratch[CCL_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 256;
+static void *g_scratch_ptr[MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+static int scratch_address(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return CCL_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return CCL_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return CCL_OK;
+}
+
 }  // namespace ccl
 
 using namespace ccl;
@@ -193,6 +219,28 @@ int ccl_label_profiled(const void *colours, int dtype, int64_t batch, int64_t he
     if (events == nullptr) return CCL_ERR_NULL;
     return label_impl(colours, dtype, batch, height, width, connectivity, flags, ignore, out,
                       counts, workspace, workspace_bytes, stream, events, n_events);
+}
+
+int ccl_label_noalloc(const void *colours, int dtype, int64_t batch, int64_t height,
+                      int64_t width, int connectivity, int flags, uint32_t ignore, int32_t *out,
+                      int32_t *counts, void *stream)
+{
+    // every check comes before any HIP call: a batch that does not fit is
+    // rejected without touching a device
+    bool empty;
+    int rc = check_label_args(dtype, batch, height, width, connectivity, flags, ignore, &empty);
+    if (rc != CCL_OK) return rc;
+    void *ws = nullptr;
+    if (!empty) {
+        if (!colours || !out) return CCL_ERR_NULL;
+        Layout L;
+        if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+        if (L.total > CCL_SCRATCH_BYTES) return CCL_ERR_SCRATCH;
+        rc = scratch_address(&ws);
+        if (rc != CCL_OK) return rc;
+    }
+    return label_impl(colours, dtype, batch, height, width, connectivity, flags, ignore, out,
+                      counts, ws, CCL_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
 int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t width,
@@ -282,6 +330,7 @@ const char *ccl_status_string(int status)
     case CCL_ERR_BAND:
         return "band_rows must be a non-negative multiple of 64 with band_rows*width < 2^31 "
                "(with numbers also band_rows*width + 2*width*(bands-1) <= 2^31-3)";
+    case CCL_ERR_SCRATCH: return "batch needs more workspace than the static scratch array holds";
     default: return "unknown status";
     }
 }

@@ -62,10 +62,13 @@ typedef enum {
     CCL_ERR_FLAGS = -8,         /* unknown bits in flags                             */
     CCL_ERR_IGNORE = -9,        /* CCL_IGNORE with a value wider than the pixel:
                                    above 255 (CCL_U8) or 0xFFFFFF (CCL_RGB24)        */
-    CCL_ERR_BAND = -10          /* ccl_label_large: band_rows negative, not a
+    CCL_ERR_BAND = -10,         /* ccl_label_large: band_rows negative, not a
                                    multiple of 64, or band_rows*width > 2^31-1, or
                                    (CCL_NUMBER) band_rows*width + 2*width*(bands-1)
                                    > 2^31-3: numbers pass through int32 codes        */
+    CCL_ERR_SCRATCH = -11       /* ccl_label_noalloc: the batch needs more workspace
+                                   than the static scratch array holds
+                                   (ccl_workspace_bytes() > CCL_SCRATCH_BYTES)       */
 } ccl_status;
 
 /* Colour element types; the value is the size of one pixel in bytes.
@@ -247,6 +250,31 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
                     int connectivity, int flags, uint32_t ignore, int64_t band_rows,
                     int64_t *out, int64_t *counts, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * ccl_label without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It calls no allocating routine; its workspace is a
+ * static device array of CCL_SCRATCH_BYTES (64 MiB) that each GPU the library
+ * runs on holds until the process ends (its address is looked up once per
+ * device, on the first call there).
+ *   arguments  as for ccl_label, less the workspace; the caller still passes
+ *              the input, `out` and `counts`
+ * CCL_ERR_SCRATCH: ccl_workspace_bytes(batch, height, width) exceeds
+ * CCL_SCRATCH_BYTES (about 17 Mpx of 64 x 32 tiles: a batch of 64 images of
+ * 512 x 512, or one 4096 x 4096 image, fits).  CCL_ERR_HIP: the array's
+ * address could not be looked up, or a launch failed.
+ * Every call on one GPU uses the same array, which keeps the last call's
+ * contents (each call clears what must start empty, its error word included):
+ * two calls on one GPU whose work overlaps in time, e.g. on two streams, race
+ * and give wrong results; serialise them (one stream, or events).  The error
+ * word of ccl_workspace_bytes is not reported by this entry point.
+ * Same results as ccl_label.
+ */
+#define CCL_SCRATCH_BYTES ((size_t)64 << 20)
+int ccl_label_noalloc(const void *colours, int dtype, int64_t batch, int64_t height,
+                      int64_t width, int connectivity, int flags, uint32_t ignore, int32_t *out,
+                      int32_t *counts, void *stream);
 
 /* Static text for a status code (never NULL). */
 const char *ccl_status_string(int status);

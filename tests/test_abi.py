@@ -27,7 +27,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("ccl_label", "ccl_number", "ccl_count", "ccl_workspace_bytes",
-                     "ccl_status_string", "ccl_label_large", "ccl_large_workspace_bytes"):
+                     "ccl_status_string", "ccl_label_large", "ccl_large_workspace_bytes",
+                     "ccl_label_noalloc"):
         assert required in names
 
 
@@ -167,7 +168,31 @@ def test_label_large_validation(lib):
     assert L(FAKE, 1, 1, 128, W, 8, 0, 0, 64, FAKE, None, FAKE, 16, None) == -6
 
 
+def test_noalloc_validation(lib):
+    """ccl_label_noalloc checks everything on the host before its first HIP
+    call (the scratch address lookup): these fail without a GPU."""
+    N = lib.ccl_label_noalloc
+    assert N(FAKE, 4, 1, 8, 8, 6, 0, 0, FAKE, None, None) == -4
+    assert N(FAKE, 2, 1, 8, 8, 8, 0, 0, FAKE, None, None) == -5
+    assert N(FAKE, 4, -1, 8, 8, 8, 0, 0, FAKE, None, None) == -2
+    assert N(FAKE, 4, 1, 8, 8, 8, 4, 0, FAKE, None, None) == -8
+    assert N(FAKE, 1, 1, 8, 8, 8, 2, 256, FAKE, None, None) == -9
+    assert N(None, 4, 1, 8, 8, 8, 0, 0, FAKE, None, None) == -1
+    assert N(FAKE, 4, 1, 8, 8, 8, 0, 0, None, None, None) == -1
+    assert N(FAKE, 4, 1, 65536, 65536, 8, 0, 0, FAKE, None, None) == -3
+    assert N(None, 4, 0, 8, 8, 8, 1, 0, None, None, None) == 0
+    # the static scratch: its size bound, and the shapes on either side of it
+    from connected_component_labelling_amd import SCRATCH_BYTES
+    assert SCRATCH_BYTES == 64 << 20
+    assert lib.ccl_workspace_bytes(64, 512, 512) <= SCRATCH_BYTES      # the u8 batch
+    assert lib.ccl_workspace_bytes(1, 4096, 4096) <= SCRATCH_BYTES     # the spiral
+    assert lib.ccl_workspace_bytes(1, 8192, 4096) > SCRATCH_BYTES
+    assert N(FAKE, 4, 1, 8192, 4096, 8, 1, 0, FAKE, None, None) == -11
+    assert N(FAKE, 1, 1, 24000, 33600, 8, 1, 0, FAKE, None, None) == -11
+    assert lib.ccl_status_string(-11)
+
+
 def test_status_strings(lib):
-    for s in range(-10, 1):
+    for s in range(-11, 1):
         assert lib.ccl_status_string(s).decode()
     assert lib.ccl_status_string(-99) == b"unknown status"
