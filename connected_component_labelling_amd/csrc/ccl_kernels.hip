@@ -335,13 +335,17 @@ __device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t x, int i)
 
 constexpr int QCAP = 256;  // join queue of one wave (a ring; at most 63 + 128 pending)
 
+// Run slots: wave w numbers the runs of its rows w*RPW*TW, w*RPW*TW + 1, ...
+// in reading order, so slot order is reading order across the whole tile and
+// the runs of one wave sit in consecutive LDS words.
+constexpr uint32_t WAVE_SLOTS = RPW * TW;  // slots of one wave (a run per pixel at most)
+
 template <bool IGN>
 struct TileLds {
     uint32_t P[TPX];               // parent of run slot; roots: + seam slot
-    uint16_t Run[TPX];             // run slots in reading order, wave w's rows from
-                                   // entry w*RPW*TW on
+    uint16_t RXY[TPX];             // tile row << 8 | start column of run slot
+    uint16_t RowBase[TH];          // slot of the first run of each tile row
     uint32_t WaveRuns[NWAVES];     // runs in each wave's rows
-    uint8_t RX[TPX];               // start column of run slot
     uint32_t Q[NWAVES][QCAP];      // queued joins: slot | other slot << 16
     uint64_t Mask[TH];             // run starts of each tile row
     uint64_t Lead[TH];             // start columns of the final roots of each row
@@ -640,11 +644,14 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     // Rows are handled as lane masks: a ballot per comparison, the logic on
     // the masks in scalar registers.  me / mea: run slot of the lane's pixel in
     // row y / in the row above (bit 0 of a row's start mask is always set, so
-    // the run of lane L is y*64 + the starts in lanes 1..L).
-    // queue the joins of row y (colours cc, run starts st_m) with the row above
-    // it (ca, sta_m)
+    // the run of lane L is the row's first slot + the starts in lanes 1..L).
+    // The joins of row y (colours cc, run starts st_m) with the row above it
+    // (ca, sta_m).  direct: row y was initialised just now and nothing refers
+    // to its runs yet, so the first join of each run is made at once by
+    // pointing the run at the parent of the run it joins (which puts it in
+    // that run's tree); only a run's further joins are queued as unions.
     auto join_rows = [&](uint32_t cc, uint64_t st_m, uint32_t me, uint32_t ca, uint64_t sta_m,
-                         uint32_t mea, uint64_t ig_m) {
+                         uint32_t mea, uint64_t ig_m, bool direct) {
         // lane shifts read other lanes, so they run with every lane active
         const uint32_t cl = from_left_lane(ca), cr = from_right_lane(ca);
         const uint64_t u0 = __ballot(ca == cc) & ok_m;
@@ -665,6 +672,23 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         // run of the row above at column lane-1 (if taken) or lane; at lane+1
         const uint32_t ab = mea - (lane_bit(lu) ? 1u : 0u);
         const uint32_t ar = mea + (lane_bit(sta_m >> 1) ? 1u : 0u);
+        if (direct) {
+            // each run's first lane with a join (a lane's rb join before its
+            // ra join): a 1 added at every run start carries through the
+            // run's lanes that make no join and stops at the first that makes
+            // one, or at the run's last lane (in E), which keeps the carry out
+            // of the next run
+            const uint64_t jm = ra | rb;
+            const uint64_t em = (st_m >> 1) | (1ull << 63);
+            const uint64_t first = (~(jm | em) + st_m) & jm;
+            if (lane_bit(first)) {
+                const uint32_t tgt = lane_bit(rb) ? ab : ar;
+                __hip_atomic_store(&s.P[me], lds_parent<false>(s.P, tgt), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+            ra &= ~(first & ~rb);
+            rb &= ~first;
+        }
         if (lane_bit(rb)) q[mbcnt_acc(rb, tail) & (QCAP - 1)] = me | (ab << 16);
         tail += popc64(rb);
         if (lane_bit(ra)) q[mbcnt_acc(ra, tail) & (QCAP - 1)] = me | (ar << 16);
@@ -684,48 +708,52 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     };
     const int nrows = vh - wave * RPW < 0 ? 0 : (vh - wave * RPW < RPW ? vh - wave * RPW : RPW);
     const uint32_t c0 = c[0];
+    const uint32_t wbase = (uint32_t)wave * WAVE_SLOTS;  // the wave's first slot
     {
         uint32_t ca = 0, mea = 0;
         uint64_t sta = 0;
         uint32_t mlo = 0, mhi = 0;  // lane i collects row i's run starts
         uint32_t ilo = 0, ihi = 0;  // ... and its pixels of the ignored colour
+        uint32_t rbase = 0;         // ... and its first slot
         uint32_t nw = 0;            // runs in the wave's rows so far
-        uint16_t *run = s.Run + wave * (RPW * TW);
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             if (i >= nrows) break;
             const int y = wave * RPW + i;
             const uint32_t cc = c[i];
             const uint64_t st_m = (__ballot(from_left_lane(cc) != cc) | 1ull) & ok_m;
-            const uint32_t me = mbcnt_acc(st_m >> 1, (uint32_t)(y * 64));
+            const uint32_t me = mbcnt_acc(st_m >> 1, wbase + nw);
             uint64_t ig_m = 0;
             if (IGN) ig_m = __ballot(cc == ign) & ok_m;
             if (lane_bit(st_m)) {
-                s.RX[me] = (uint8_t)lane;
+                s.RXY[me] = (uint16_t)((y << 8) | lane);
                 s.P[me] = me;
-                run[nw + me - (uint32_t)(y * 64)] = (uint16_t)me;
             }
-            nw += popc64(st_m);
-            // lane i keeps row i's masks.  A select, not write_lane: these
-            // values live through the joins' divergent loops, and gathered with
-            // the inline-asm v_writelane (whose other lanes the compiler does
-            // not know it keeps) they came out wrong in one instance of this
-            // pass on MI355X; the select costs about 0.013 ms on the sheet.
+            // lane i keeps row i's masks.  A select, not a v_writelane: these
+            // values live through the joins' divergent loops (gathered with an
+            // inline-asm v_writelane, whose other lanes the compiler does not
+            // know it keeps, they came out wrong in one instance of this pass
+            // on MI355X)
             mlo = lane == i ? (uint32_t)st_m : mlo;
             mhi = lane == i ? (uint32_t)(st_m >> 32) : mhi;
+            rbase = lane == i ? wbase + nw : rbase;
             if (IGN) {
                 ilo = lane == i ? (uint32_t)ig_m : ilo;
                 ihi = lane == i ? (uint32_t)(ig_m >> 32) : ihi;
             }
+            nw += popc64(st_m);
             if (i > 0) {
-                join_rows(cc, st_m, me, ca, sta, mea, ig_m);
+                join_rows(cc, st_m, me, ca, sta, mea, ig_m, true);
                 drain(false);
             }
             ca = cc;
             sta = st_m;
             mea = me;
         }
-        if (lane < RPW) s.Mask[wave * RPW + lane] = ((uint64_t)mhi << 32) | mlo;  // 0 past the image edge
+        if (lane < RPW) {  // rows past the image edge store 0
+            s.Mask[wave * RPW + lane] = ((uint64_t)mhi << 32) | mlo;
+            s.RowBase[wave * RPW + lane] = (uint16_t)rbase;
+        }
         if (IGN && lane < RPW) s.Ign[wave * RPW + lane] = ((uint64_t)ihi << 32) | ilo;
         if (lane == 0) {
 #pragma unroll
@@ -739,28 +767,29 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     lds_barrier();
     if (tid < TH) w.runmask[t32 + tid] = s.Mask[tid];
 
-    // runs of the tile; reading-order run r sits in wave w's part of Run when
-    // off[w] <= r < off[w+1] (the waves' rows follow each other)
+    // runs of the tile; reading-order run r is slot r - off[w] + w*WAVE_SLOTS
+    // of the wave w with off[w] <= r < off[w+1] (the waves' rows follow each
+    // other)
     const uint32_t n0 = __builtin_amdgcn_readfirstlane(s.WaveRuns[0]),
                    n1 = __builtin_amdgcn_readfirstlane(s.WaveRuns[1]),
                    n2 = __builtin_amdgcn_readfirstlane(s.WaveRuns[2]),
                    n3 = __builtin_amdgcn_readfirstlane(s.WaveRuns[3]);
     const uint32_t off1 = n0, off2 = off1 + n1, off3 = off2 + n2, R = off3 + n3;
     auto run_slot = [&](uint32_t r) -> uint32_t {
-        const uint32_t i = r >= off3 ? r + (3u * RPW * TW - off3)
-                         : r >= off2 ? r + (2u * RPW * TW - off2)
-                         : r >= off1 ? r + (1u * RPW * TW - off1) : r;
-        return s.Run[i];
+        return r >= off3 ? r + (3u * WAVE_SLOTS - off3)
+             : r >= off2 ? r + (2u * WAVE_SLOTS - off2)
+             : r >= off1 ? r + (1u * WAVE_SLOTS - off1) : r;
     };
 
-    // the wave's first row against the last row of the wave above; then every
-    // join still queued (fewer than 64 from the wave's rows, and these) is
-    // united
+    // the wave's first row against the last row of the wave above (unions:
+    // both rows' runs may already be joined to others); then every join still
+    // queued (fewer than 64 from the wave's rows, and these) is united
     if (wave > 0 && nrows > 0) {
         const int y = wave * RPW;
         const uint64_t mi = uniform64(s.Mask[y]), ma = uniform64(s.Mask[y - 1]);
-        join_rows(c0, mi, mbcnt_acc(mi >> 1, (uint32_t)(y * 64)), s.LastC[wave - 1][lane], ma,
-                  mbcnt_acc(ma >> 1, (uint32_t)((y - 1) * 64)), IGN ? uniform64(s.Ign[y]) : 0ull);
+        const uint32_t ba = __builtin_amdgcn_readfirstlane((uint32_t)s.RowBase[y - 1]);
+        join_rows(c0, mi, mbcnt_acc(mi >> 1, wbase), s.LastC[wave - 1][lane], ma,
+                  mbcnt_acc(ma >> 1, ba), IGN ? uniform64(s.Ign[y]) : 0ull, false);
     }
     drain(true);
     lds_barrier();
@@ -773,17 +802,18 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     //      edge position as the region's seam slot (the smallest wins)
     for (uint32_t r = tid; r < R; r += BLOCK) {
         const uint32_t slot = run_slot(r);
-        const int ry = (int)(slot >> 6), k = (int)(slot & 63u);
-        const int cnt = (int)popc64(s.Mask[ry]);
+        const uint32_t rxy = s.RXY[slot];
+        const int ry = (int)(rxy >> 8), col = (int)(rxy & 63u);
         const uint32_t root = lds_find<true>(s.P, slot);
         if (root != slot) atomicMin(&s.P[slot], root);
         // a run of the ignored colour joined nothing: it is its own root
-        if (IGN && ((s.Ign[ry] >> s.RX[slot]) & 1ull)) continue;
+        if (IGN && ((s.Ign[ry] >> col) & 1ull)) continue;
+        const uint64_t mrow = s.Mask[ry];
         uint32_t es = 255;
-        if (has_right && k == cnt - 1) es = 2 * TW + TH + ry;
-        if (has_left && k == 0) es = 2 * TW + ry;
-        if (has_bottom && ry == TH - 1) es = TW + k;
-        if (has_top && ry == 0) es = k;
+        if (has_right && ((mrow >> col) >> 1) == 0ull) es = 2 * TW + TH + ry;  // the row's last run
+        if (has_left && col == 0) es = 2 * TW + ry;
+        if (has_bottom && ry == TH - 1) es = TW + popc64(mrow & mask_lt(col));
+        if (has_top && ry == 0) es = popc64(mrow & mask_lt(col));
         if (es != 255) atomicMax(&s.P[root], ((255u - es) << 16) | root);
     }
     lds_barrier();
@@ -792,22 +822,26 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
     for (uint32_t r = tid; r < R; r += BLOCK) {
         const uint32_t slot = run_slot(r);
-        if (IGN && ((s.Ign[slot >> 6] >> s.RX[slot]) & 1ull)) {
-            rinfo[r] = (uint16_t)INFO_IGNORED;
-            continue;
+        if (IGN) {
+            const uint32_t sxy = s.RXY[slot];
+            if ((s.Ign[sxy >> 8] >> (sxy & 63u)) & 1ull) {
+                rinfo[r] = (uint16_t)INFO_IGNORED;
+                continue;
+            }
         }
         const uint32_t pv = s.P[slot];
         const uint32_t root = pv & PMASK;
         const uint32_t rv = root == slot ? pv : s.P[root];
         const uint32_t es = 255u - (rv >> 16);
-        const uint32_t rcol = s.RX[root];
-        rinfo[r] = (uint16_t)(es != 255u ? (INFO_BORDER | es) : ((root & ~63u) | rcol));
+        const uint32_t rxy = s.RXY[root];
+        const uint32_t rrow = rxy >> 8, rcol = rxy & 63u;
+        rinfo[r] = (uint16_t)(es != 255u ? (INFO_BORDER | es) : ((rrow << 6) | rcol));
         if (root == slot) {
             if (es == 255u) {
-                atomicOr((unsigned long long *)&s.Lead[slot >> 6], 1ull << rcol);
+                atomicOr((unsigned long long *)&s.Lead[rrow], 1ull << rcol);
             } else {
                 const uint32_t node = (t << 8) | es;
-                const uint32_t key = (y0 + (slot >> 6)) * W + x0 + rcol;
+                const uint32_t key = (y0 + rrow) * W + x0 + rcol;
                 w.gp[(size_t)t * KMAX + es] = ((uint64_t)key << 32) | node;
                 atomicOr((unsigned long long *)&s.Used[es >> 6], 1ull << (es & 63u));
             }
@@ -825,11 +859,12 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     // top-edge requests and the header
     if (has_bottom && wave == NWAVES - 1 && lane_ok) {
         const uint64_t mb = uniform64(s.Mask[TH - 1]);
-        w.bslot[(size_t)t * TW + lane] = (uint8_t)seam_of(mbcnt_acc(mb >> 1, (uint32_t)((TH - 1) * 64)));
+        const uint32_t bb = __builtin_amdgcn_readfirstlane((uint32_t)s.RowBase[TH - 1]);
+        w.bslot[(size_t)t * TW + lane] = (uint8_t)seam_of(mbcnt_acc(mb >> 1, bb));
     }
     if (wave == 2) {
         if (has_right && lane < vh)
-            w.rslot[t32 + lane] = (uint8_t)seam_of((uint32_t)(lane * 64) + popc64(s.Mask[lane]) - 1u);
+            w.rslot[t32 + lane] = (uint8_t)seam_of((uint32_t)s.RowBase[lane] + popc64(s.Mask[lane]) - 1u);
         if (lane < TH) {  // rows past the image edge store 0
             const uint64_t lead = s.Lead[lane];
             w.leadmask[t32 + lane] = lead;
@@ -840,7 +875,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         uint32_t nleft = 0;
         if (has_left) {
             const bool valid = lane < vh;
-            const uint32_t me = valid ? seam_of((uint32_t)(lane * 64)) : 0u;
+            const uint32_t me = valid ? seam_of((uint32_t)s.RowBase[lane]) : 0u;
             const uint32_t cur = valid ? s.ColC[lane] : 0u;
             nleft = left_requests<CONN>(w.req + (size_t)t * REQMAX + REQ_TOP, lane,
                                         (1ull << vh) - 1ull, me, cur, lane < TH ? s_hleft[lane] : 0u,
