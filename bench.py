@@ -212,6 +212,8 @@ def timed_steps(lab, dev, steps: int, stream, hip, torch, ignore=None, rgb=False
         step_ms.append(hip.elapsed_ms(ev[0], ev[5]))
     for ev in events:
         hip.destroy(ev)
+    timed_steps.last = {"median": round(float(np.median(step_ms)), 4),
+                        "min": round(min(step_ms), 4), "max": round(max(step_ms), 4)}
     return wall / steps * 1e3, stage_ms, float(np.median(step_ms))
 
 
@@ -299,6 +301,160 @@ def stats_leg(ccl, labels, counts, npx, steps, warmup, stream, hip, torch):
     }
 
 
+def host_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, the ones this process may
+    use, CPU model and memory."""
+    info = {"nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0))}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                info["ram_GiB"] = round(int(line.split()[1]) / 2**20, 1)
+                break
+    except OSError:
+        pass
+    return info
+
+
+class pinned_to_one_core:
+    """Runs the block on one CPU core (the first this process may use), as the
+    pages time the CPU library on one core; restores the affinity after."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        self.core = min(self.saved)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+        return False
+
+
+def per_config_leg(ccl, configs, steps, warmup, hip, torch):
+    """Workloads other than the headline one, each labelled and numbered at full
+    size: per-call HIP-event times (median, min, max), Gpixels/s and the
+    fraction of the HBM roofline of the path (colour read + 4 B label write per
+    pixel).  Returns the results and, per workload, the picture and the GPU's
+    numbers and counts for the CPU-baseline leg (cpu_baseline_per_config)."""
+    import numpy as np
+
+    import synth
+    out, stash = {}, {}
+    for cfg in configs:
+        desc, (B, H, W), np_dtype, seed = synth.CONFIGS[cfg]
+        img = synth.generate(cfg)
+        bpp = np.dtype(np_dtype).itemsize
+        npx = B * H * W
+        dev = torch.from_numpy(img.view(np.int32) if bpp == 4 else img).cuda()
+        lab = ccl.Labeller((B, H, W), device="cuda", connectivity=8)
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            lab(dev, number=True, stream=stream)
+        ev = hip.create(2 * steps)
+        sh = ctypes.c_void_p(stream.cuda_stream)
+        torch.cuda.synchronize()
+        for k in range(steps):
+            hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k]), sh)
+            lab(dev, number=True, stream=stream)
+            hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k + 1]), sh)
+        torch.cuda.synchronize()
+        ms = [hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]) for k in range(steps)]
+        hip.destroy(ev)
+        stash[cfg] = (img, lab.out.cpu().numpy(), lab.counts.cpu().numpy())
+        err = ccl.error_word(lab.workspace)
+        del lab, dev
+        torch.cuda.empty_cache()
+        med = float(np.median(ms))
+        out[str(cfg)] = {
+            "workload": desc,
+            "shape": [B, H, W],
+            "gpu_ms": {"median": round(med, 4), "min": round(min(ms), 4), "max": round(max(ms), 4),
+                       "calls": steps},
+            "value": round(npx / (med * 1e-3) / 1e9, 3),
+            "unit": "Gpixels/s",
+            "hbm_frac_path": round(npx * (bpp + 4) / (med * 1e-3) / 1e12 / 8.0, 4),
+            "regions": int(stash[cfg][2].sum()),
+            "error_word": err,
+        }
+        print(f"[bench] workload {cfg} done", file=sys.stderr, flush=True)
+    return out, stash
+
+
+def cpu_baseline_per_config(stash, per_config):
+    """CPU-baseline leg for the other workloads: the oracle on one pinned host
+    thread (median of a few calls; one call on the 400-Mpx tissue) and whether
+    the GPU's numbers and counts equal its own bit for bit.  Adds
+    oracle_ms, oracle_Gpixels_per_s and bit_exact to each workload's entry."""
+    import numpy as np
+
+    import oracle
+    lib = oracle.load()
+    reps = {1: 5, 2: 3, 3: 3, 4: 1}
+    for cfg, (img, got, got_counts) in stash.items():
+        times = []
+        with pinned_to_one_core() as pin:
+            for _ in range(reps.get(cfg, 1)):
+                t0 = time.perf_counter()
+                labels, counts = oracle.number(oracle.label(img, 8, lib=lib), lib=lib)
+                times.append(time.perf_counter() - t0)
+        med = float(np.median(times))
+        e = per_config[str(cfg)]
+        npx = int(np.prod(e["shape"]))
+        e["oracle_ms"] = round(med * 1e3, 2)
+        e["oracle_calls"] = len(times)
+        e["oracle_core"] = pin.core
+        e["oracle_Gpixels_per_s"] = round(npx / med / 1e9, 4)
+        e["bit_exact"] = bool(np.array_equal(got, labels.reshape(got.shape)) and
+                              np.array_equal(got_counts, counts))
+        print(f"[bench] oracle on workload {cfg} done", file=sys.stderr, flush=True)
+
+
+def two_call_leg(ccl, lab, dev, npx, bpp, steps, warmup, stream, hip, torch):
+    """The unfused pair: ccl_label writing leaders, then ccl_number numbering
+    them in place (its own scan), per step; HIP events around each pair."""
+    import numpy as np
+    B, H, W = lab.B, lab.H, lab.W
+    leaders = torch.empty((B, H, W), dtype=torch.int32, device="cuda")
+    counts = torch.empty(B, dtype=torch.int32, device="cuda")
+    lib = ccl._load()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    x = dev if dev.dim() == 3 else dev.unsqueeze(0)
+    dt = 4 if bpp == 4 else 1
+
+    def pair():
+        ccl._check(lib.ccl_label(ccl._ptr(x), dt, B, H, W, 8, 0, 0, ccl._ptr(leaders), None,
+                                 ccl._ptr(lab.workspace), lab.workspace.numel(), sh))
+        ccl._check(lib.ccl_number(ccl._ptr(leaders), B, H, W, ccl._ptr(leaders), ccl._ptr(counts),
+                                  ccl._ptr(lab.workspace), lab.workspace.numel(), sh))
+    for _ in range(warmup):
+        pair()
+    ev = hip.create(2 * steps)
+    torch.cuda.synchronize()
+    for k in range(steps):
+        hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k]), sh)
+        pair()
+        hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k + 1]), sh)
+    torch.cuda.synchronize()
+    ms = [hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]) for k in range(steps)]
+    hip.destroy(ev)
+    lab(dev, number=True, stream=stream)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(leaders, lab.out) and torch.equal(counts, lab.counts))
+    del leaders
+    med = float(np.median(ms))
+    return {
+        "value": round(npx / (med * 1e-3) / 1e9, 3),
+        "unit": "Gpixels/s",
+        "ms_per_pair": {"median": round(med, 4), "min": round(min(ms), 4), "max": round(max(ms), 4)},
+        "hbm_frac_path": round(npx * (bpp + 4) / (med * 1e-3) / 1e12 / 8.0, 4),
+        "same_as_fused": same,
+    }
+
+
 def cpu_baseline(img_np, rows: int, ccl, torch):
     """Oracle (one thread) on the first `rows` rows of the sheet, and the GPU on
     the same band for a bit-exact check."""
@@ -308,10 +464,11 @@ def cpu_baseline(img_np, rows: int, ccl, torch):
     band = np.ascontiguousarray(img_np[:, :rows, :])
     B, H, W = band.shape
     lib = oracle.load()
-    t0 = time.perf_counter()
-    leaders = oracle.label(band, 8, lib=lib)
-    labels, counts = oracle.number(leaders, lib=lib)
-    dt = time.perf_counter() - t0
+    with pinned_to_one_core() as pin:
+        t0 = time.perf_counter()
+        leaders = oracle.label(band, 8, lib=lib)
+        labels, counts = oracle.number(leaders, lib=lib)
+        dt = time.perf_counter() - t0
     dev = torch.from_numpy(band.view(np.int32)).cuda()
     got, gc = ccl.label(dev, 8, number=True)
     torch.cuda.synchronize()
@@ -324,8 +481,75 @@ def cpu_baseline(img_np, rows: int, ccl, torch):
         "cores": 1,
         "kind": "oracle",
         "sample": f"rows 0..{H - 1} of the sheet ({B * H * W / 1e6:.1f} Mpx, full width), "
-                  f"label + number, sequential C oracle on one host thread, {dt:.1f} s",
+                  f"label + number, sequential C oracle on one host thread pinned to core "
+                  f"{pin.core}, {dt:.1f} s",
+        "host": host_info(),
     }, exact
+
+
+def host_leg(ccl, img_np, steps, warmup, torch, band_rows=0):
+    """ccl_label_host (picture in page-locked host memory, labels back to
+    page-locked host memory, copies overlapped with the kernels band by band)
+    against the copies alone of the same bytes: all pixels in and then all
+    labels out on one stream ("serial"), and in and out at once on two streams
+    ("duplex").  Wall clock between device synchronisations, median of
+    `steps` calls."""
+    import numpy as np
+    B, H, W = img_np.shape
+    npx = B * H * W
+    host = torch.from_numpy(img_np.view(np.int32) if img_np.dtype == np.uint32 else img_np)
+    host = host.pin_memory()
+    lab = ccl.HostLabeller((B, H, W), dtype=host.dtype, device="cuda", band_rows=band_rows)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(warmup, 1)):
+        lab(host, number=True, stream=stream)
+    times = []
+    for _ in range(steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lab(host, number=True, stream=stream, wait=False)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    call_ms = float(np.median(times)) * 1e3
+    err = ccl.error_word(lab.workspace)
+    # the copies alone, same buffers
+    s_in, s_out = lab.copy_streams
+    serial, duplex = [], []
+    for _ in range(max(2, steps // 2)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        lab.dev_img.copy_(host.view(lab.dev_img.shape), non_blocking=True)
+        lab.out.copy_(lab.dev_out, non_blocking=True)
+        torch.cuda.synchronize()
+        serial.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s_in):
+            lab.dev_img.copy_(host.view(lab.dev_img.shape), non_blocking=True)
+        with torch.cuda.stream(s_out):
+            lab.out.copy_(lab.dev_out, non_blocking=True)
+        torch.cuda.synchronize()
+        duplex.append(time.perf_counter() - t0)
+    serial_ms = float(np.median(serial)) * 1e3
+    duplex_ms = float(np.median(duplex)) * 1e3
+    in_bytes = host.numel() * host.element_size()
+    out_bytes = npx * 4
+    hb = band_rows if band_rows else None
+    res = {
+        "value": round(npx / (call_ms * 1e-3) / 1e9, 3),
+        "unit": "Gpixels/s (copy-inclusive)",
+        "ms_per_call": round(call_ms, 3),
+        "copy_only_serial_ms": round(serial_ms, 3),
+        "copy_only_duplex_ms": round(duplex_ms, 3),
+        "call_over_serial_copies": round(call_ms / serial_ms, 4),
+        "call_over_duplex_copies": round(call_ms / duplex_ms, 4),
+        "pcie_GBps_serial": round((in_bytes + out_bytes) / (serial_ms * 1e-3) / 1e9, 1),
+        "band_rows": hb if hb else "automatic",
+        "error_word": err,
+    }
+    del lab, host
+    torch.cuda.empty_cache()
+    return res
 
 
 LARGE_HW = 46400
@@ -448,6 +672,7 @@ def main():
     print(f"[bench] warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     ms_per_step, stage_ms, event_ms = timed_steps(lab, dev, args.steps, stream, hip, torch)
+    event_stats = timed_steps.last
     counts = lab.counts.cpu().tolist()
 
     ignore_leg = None
@@ -455,7 +680,11 @@ def main():
     stats = None
     large = None
     two = None
+    host = None
     paper = None
+    two_call = None
+    per_config = None
+    stash = None
     if not args.no_extra_legs:
         hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         stats = stats_leg(ccl, lab.out, lab.counts, npx, args.steps, args.warmup, stream, hip,
@@ -474,10 +703,21 @@ def main():
             }
             del rgb_dev
             print(f"[bench] rgb24 legs done ({args.steps} steps each)", file=sys.stderr, flush=True)
+        hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        two_call = two_call_leg(ccl, lab, dev, npx, bpp, args.steps, args.warmup, stream, hip,
+                                torch)
+        print(f"[bench] two-call leg done ({args.steps} steps)", file=sys.stderr, flush=True)
         two = two_stream_leg(ccl, lab, dev, npx, bpp, args.steps, args.warmup, torch)
         print(f"[bench] two-stream leg done ({args.steps} steps)", file=sys.stderr, flush=True)
+        hsteps = max(3, min(args.steps, 7))
+        host = {"sheet": host_leg(ccl, img_np, hsteps, 1, torch),
+                "u8_batch_64x512x512": host_leg(ccl, synth.generate(2), hsteps, 1, torch)}
+        print(f"[bench] host leg done ({hsteps} calls each)", file=sys.stderr, flush=True)
         large = large_leg(ccl, args.steps, args.warmup, stream, hip, torch)
         print(f"[bench] large leg done ({args.steps} calls)", file=sys.stderr, flush=True)
+        others = [c for c in sorted(synth.CONFIGS) if c != args.config]
+        per_config, stash = per_config_leg(ccl, others, max(args.steps, 10), args.warmup, hip,
+                                           torch)
     if args.copy_calibration_mb > 0:
         n = args.copy_calibration_mb << 20
         src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
@@ -505,6 +745,9 @@ def main():
         del lab
         torch.cuda.empty_cache()
         cpu, exact = cpu_baseline(img_np, min(args.cpu_rows, H), ccl, torch)
+        if per_config is not None:
+            cpu_baseline_per_config(stash, per_config)
+            del stash
         if ignore_leg is not None:
             print("[bench] oracle with the paper ignored ...", file=sys.stderr, flush=True)
             ignore_leg["band_parity_bit_exact"] = band_parity_ignore(
@@ -538,6 +781,7 @@ def main():
         },
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
         "event_ms_per_step": round(event_ms, 4),
+        "event_ms_stats": event_stats,
         "regions": counts[:4],
         "error_word": err,
         "cpu_baseline": cpu,
@@ -545,8 +789,11 @@ def main():
         "ignore_leg": ignore_leg,
         "rgb24_leg": rgb24_leg,
         "stats_leg": stats,
+        "two_call_leg": two_call,
         "two_stream_leg": two,
+        "host_leg": host,
         "large_leg": large,
+        "per_config": per_config,
         "kernel_source": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

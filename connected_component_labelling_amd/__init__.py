@@ -13,6 +13,7 @@ functions raises -- there is no CPU fallback.
     counts = count(leaders)
     out, counts = label_large(img, number=True)             # int64, any size
     out, counts = label_noalloc(img, number=True)           # no device allocation
+    out, counts = label_host(pinned_img, number=True)       # host in, host out, copies overlapped
 
 ``img`` is a CUDA (HIP) tensor of shape [H, W] or [B, H, W], dtype uint8, or
 uint32 / int32 (the 32 bits are compared as they are), or with ``rgb=True`` an
@@ -31,7 +32,7 @@ from . import build as _build
 
 __all__ = ["label", "number", "count", "region_stats", "workspace_bytes", "Labeller",
            "error_word", "CclError", "library_path", "label_large", "large_workspace_bytes",
-           "label_noalloc", "SCRATCH_BYTES"]
+           "label_noalloc", "SCRATCH_BYTES", "label_host", "HostLabeller"]
 
 CCL_U8, CCL_RGB24, CCL_U32 = 1, 3, 4
 CCL_NUMBER, CCL_IGNORE = 1, 2
@@ -79,6 +80,9 @@ def _load():
     lib.ccl_label_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_uint32, vp, vp, vp]
     lib.ccl_label_noalloc.restype = ctypes.c_int
+    lib.ccl_label_host.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_uint32, vp, vp, vp, vp, vp, sz, i64, vp, vp, vp]
+    lib.ccl_label_host.restype = ctypes.c_int
     lib.ccl_status_string.argtypes = [ctypes.c_int]
     lib.ccl_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -367,3 +371,81 @@ class Labeller:
             arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e) for e in events])
             _check(lib.ccl_label_profiled(*args, arr, len(events)))
         return self.out, self.counts
+
+
+_copy_streams = {}
+
+
+def _copy_streams_for(device):
+    """Two streams (default priority) for the copies of label_host, made once
+    per device."""
+    idx = torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    if idx not in _copy_streams:
+        _copy_streams[idx] = (torch.cuda.Stream(device=idx), torch.cuda.Stream(device=idx))
+    return _copy_streams[idx]
+
+
+class HostLabeller:
+    """Labels pictures in page-locked host memory through ccl_label_host: the
+    picture goes in and the labels come out on two copy streams, band by band,
+    beside the kernels.  Holds the device copy of the picture, the device
+    labels, the page-locked host labels, the counts and the workspace for one
+    batch shape, so repeated calls allocate nothing."""
+
+    def __init__(self, shape, dtype=torch.uint8, rgb: bool = False, device="cuda",
+                 connectivity: int = 8, band_rows: int = 0):
+        """``shape`` is the label shape, [H, W] or [B, H, W]; ``dtype`` the colour
+        dtype (uint8, or uint32 / int32; with ``rgb``, three uint8 per pixel)."""
+        if len(shape) == 2:
+            shape = (1, *shape)
+        self.B, self.H, self.W = (int(v) for v in shape)
+        self.rgb = rgb
+        self.connectivity = connectivity
+        self.band_rows = int(band_rows)
+        pix = (self.B, self.H, self.W, 3) if rgb else (self.B, self.H, self.W)
+        self.dev_img = torch.empty(pix, dtype=torch.uint8 if rgb else dtype, device=device)
+        self.dev_out = torch.empty((self.B, self.H, self.W), dtype=torch.int32, device=device)
+        self.out = torch.empty((self.B, self.H, self.W), dtype=torch.int32, pin_memory=True)
+        self.counts = torch.empty(self.B, dtype=torch.int32, device=device)
+        self.workspace = _new_workspace(self.B, self.H, self.W, device)
+        self.copy_streams = _copy_streams_for(device)
+
+    def __call__(self, img: torch.Tensor, number: bool = True, stream=None,
+                 ignore: int | None = None, wait: bool = True):
+        """Label ``img`` (a page-locked CPU tensor of this labeller's shape and
+        dtype).  Returns (host labels, device counts); with ``wait`` the call
+        is complete on return, else once ``stream`` reaches its end."""
+        if img.is_cuda or not img.is_contiguous():
+            raise ValueError("img must be a contiguous host tensor")
+        if not img.is_pinned():
+            raise ValueError("img must be page-locked (pin_memory()) for the copies to overlap")
+        x, _ = _batch_view(img, self.rgb)
+        if tuple(x.shape) != tuple(self.dev_img.shape) or x.dtype != self.dev_img.dtype:
+            raise ValueError("image shape or dtype does not match the HostLabeller")
+        flags, ign = _flags(number, ignore)
+        s = stream if stream is not None else torch.cuda.current_stream()
+        h2d, d2h = self.copy_streams
+        _check(_load().ccl_label_host(
+            _ptr(x), _dtype_code(x, self.rgb), self.B, self.H, self.W, self.connectivity, flags,
+            ign, _ptr(self.out), _ptr(self.counts), _ptr(self.dev_img), _ptr(self.dev_out),
+            _ptr(self.workspace), self.workspace.numel(), self.band_rows,
+            ctypes.c_void_p(s.cuda_stream), ctypes.c_void_p(h2d.cuda_stream),
+            ctypes.c_void_p(d2h.cuda_stream)))
+        if wait:
+            s.synchronize()
+        return self.out, self.counts
+
+
+def label_host(img: torch.Tensor, connectivity: int = 8, number: bool = False,
+               ignore: int | None = None, rgb: bool = False, band_rows: int = 0,
+               device="cuda"):
+    """``label`` for a page-locked host picture, with the copies in and out
+    overlapped with the labelling band by band (ccl_label_host).  Returns
+    (host labels [B, H, W] or [H, W], device counts) once complete."""
+    x, squeeze = _batch_view(img, rgb)
+    lab = HostLabeller(tuple(x.shape[:3]), dtype=x.dtype, rgb=rgb, device=device,
+                       connectivity=connectivity, band_rows=band_rows)
+    out, counts = lab(img, number=number, ignore=ignore)
+    return (out[0] if squeeze else out), counts

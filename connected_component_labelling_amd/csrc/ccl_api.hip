@@ -6,6 +6,7 @@
 #include <limits.h>
 
 #include <mutex>
+#include <vector>
 
 namespace ccl {
 
@@ -243,6 +244,147 @@ int ccl_label_noalloc(const void *colours, int dtype, int64_t batch, int64_t hei
                       counts, ws, CCL_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
+int ccl_label_host(const void *host_colours, int dtype, int64_t batch, int64_t height,
+                   int64_t width, int connectivity, int flags, uint32_t ignore, int32_t *host_out,
+                   int32_t *counts, void *dev_colours, int32_t *dev_out, void *workspace,
+                   size_t workspace_bytes, int64_t band_rows, void *stream, void *h2d_stream,
+                   void *d2h_stream)
+{
+    bool empty;
+    int rc = check_label_args(dtype, batch, height, width, connectivity, flags, ignore, &empty);
+    if (rc != CCL_OK) return rc;
+    if (band_rows < 0 || band_rows % TH != 0) return CCL_ERR_BAND;
+    hipStream_t s = (hipStream_t)stream;
+    if (empty) {
+        if (counts && batch > 0) {
+            launch_zero_i32(counts, batch, s);
+            return finish_launches();
+        }
+        return CCL_OK;
+    }
+    if (!host_colours || !host_out || !dev_colours || !dev_out || !workspace) return CCL_ERR_NULL;
+    if (h2d_stream == nullptr || d2h_stream == nullptr || h2d_stream == stream ||
+        d2h_stream == stream || h2d_stream == d2h_stream)
+        return CCL_ERR_STREAM;
+    Layout L;
+    if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+    if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
+    hipStream_t sin = (hipStream_t)h2d_stream, sout = (hipStream_t)d2h_stream;
+    const int ign = (flags & CCL_IGNORE) != 0;
+    const int number = (flags & CCL_NUMBER) != 0;
+    const bool need_scan = number || counts != nullptr;
+    const size_t bpp = (size_t)dtype;  // bytes per pixel (CCL_U8 1, CCL_RGB24 3, CCL_U32 4)
+    const int64_t HW = height * width;
+
+    // Steps of the pipeline.  A large image is cut into bands of whole tile
+    // rows (band_rows, or automatically an eighth of it but at least 2^22
+    // pixels); small images are taken whole, in groups of at least 2^22
+    // pixels.  Each group (an image with its bands, or a group of images) is
+    // labelled as one batch; the steps of a group are its bands.
+    constexpr int64_t STEP_PX = int64_t(1) << 22;
+    int64_t brows = band_rows;
+    if (brows == 0) {
+        const int64_t eighth = (height + 8 * TH - 1) / (8 * TH) * TH;
+        const int64_t least = ((STEP_PX + width - 1) / width + TH - 1) / TH * TH;
+        brows = HW > 2 * STEP_PX ? (eighth > least ? eighth : least) : height;
+    }
+    if (brows > height) brows = (height + TH - 1) / TH * TH;
+    const int64_t nband = (height + brows - 1) / brows;
+    int64_t per_group = 1;  // images per group (bands of one image if there are several)
+    if (nband == 1) {
+        per_group = (STEP_PX + HW - 1) / HW;
+        if (per_group > batch) per_group = batch;
+    }
+    const int64_t ngroup = (batch + per_group - 1) / per_group;
+    const int64_t nstep = ngroup * nband;
+
+    std::vector<hipEvent_t> ev(2 * (size_t)nstep + 2, nullptr);
+    auto cleanup = [&]() {
+        for (hipEvent_t e : ev)
+            if (e) (void)hipEventDestroy(e);
+    };
+    for (hipEvent_t &e : ev)
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+            e = nullptr;
+            cleanup();
+            return CCL_ERR_HIP;
+        }
+    hipEvent_t *ein = ev.data(), *eout = ev.data() + nstep;
+    hipEvent_t estart = ev[2 * nstep], edone = ev[2 * nstep + 1];
+    bool ok = true;
+    auto chk = [&](hipError_t e) { ok = ok && e == hipSuccess; };
+    // pixels of step (group j, band k): first pixel and count (contiguous)
+    auto step_px = [&](int64_t j, int64_t k, int64_t &first, int64_t &n) {
+        const int64_t b0 = j * per_group, nb = batch - b0 < per_group ? batch - b0 : per_group;
+        const int64_t r0 = k * brows, r1 = r0 + brows < height ? r0 + brows : height;
+        first = b0 * HW + r0 * width;
+        n = nband == 1 ? nb * HW : (r1 - r0) * width;
+    };
+
+    // the copy streams start after everything already on the caller's stream
+    // (an earlier call may still read dev_colours or write dev_out there)
+    chk(hipEventRecord(estart, s));
+    chk(hipStreamWaitEvent(sin, estart, 0));
+    chk(hipStreamWaitEvent(sout, estart, 0));
+    // 1. every step's pixels in, in order, each followed by its event
+    for (int64_t j = 0; j < ngroup && ok; ++j)
+        for (int64_t k = 0; k < nband; ++k) {
+            int64_t first, n;
+            step_px(j, k, first, n);
+            chk(hipMemcpyAsync((char *)dev_colours + (size_t)first * bpp,
+                               (const char *)host_colours + (size_t)first * bpp, (size_t)n * bpp,
+                               hipMemcpyHostToDevice, sin));
+            chk(hipEventRecord(ein[j * nband + k], sin));
+        }
+    // 2. each group: its bands' tile passes, each once its pixels (and the
+    //    row above them, in the band before) are in; the seam merge, seam
+    //    roots, scan and resolve of the group; its bands' final writes, each
+    //    followed by the copy of its labels out
+    for (int64_t j = 0; j < ngroup && ok; ++j) {
+        const int64_t b0 = j * per_group, nb = batch - b0 < per_group ? batch - b0 : per_group;
+        Layout Lg;
+        make_layout(nb, height, width, &Lg);  // fits: it is part of the whole batch
+        const Geom &g = Lg.g;
+        const Work w = bind_work(Lg, workspace);
+        const char *img = (const char *)dev_colours + (size_t)(b0 * HW) * bpp;
+        int32_t *o = dev_out + b0 * HW;
+        const uint32_t band_tiles = (uint32_t)(brows / TH) * (uint32_t)g.ntx;
+        auto tiles_of = [&](int64_t k, uint32_t &t0, uint32_t &nt) {
+            t0 = nband == 1 ? 0u : (uint32_t)k * band_tiles;
+            nt = nband == 1 ? (uint32_t)g.ntiles
+                            : (t0 + band_tiles <= (uint32_t)g.ntiles ? band_tiles
+                                                                     : (uint32_t)g.ntiles - t0);
+        };
+        for (int64_t k = 0; k < nband; ++k) {
+            uint32_t t0, nt;
+            tiles_of(k, t0, nt);
+            chk(hipStreamWaitEvent(s, ein[j * nband + k], 0));
+            launch_tile(img, dtype, connectivity, ign, ignore, g, w, j == 0 && k == 0, s, t0, nt);
+        }
+        launch_seam(g, w, connectivity, s);
+        if (need_scan) launch_seam_roots(g, w, s);
+        if (need_scan) launch_scan(g, w, counts ? counts + b0 : nullptr, number, 1, s);
+        launch_resolve(g, w, number, s);
+        for (int64_t k = 0; k < nband; ++k) {
+            uint32_t t0, nt;
+            tiles_of(k, t0, nt);
+            launch_final(g, w, o, number, number ? 0u : 0xFFFFFFFFu, s, t0, nt);
+            chk(hipEventRecord(eout[j * nband + k], s));
+            chk(hipStreamWaitEvent(sout, eout[j * nband + k], 0));
+            int64_t first, n;
+            step_px(j, k, first, n);
+            chk(hipMemcpyAsync(host_out + first, dev_out + first, (size_t)n * sizeof(int32_t),
+                               hipMemcpyDeviceToHost, sout));
+        }
+    }
+    // 3. the call ends on the caller's stream once the last labels are out
+    chk(hipEventRecord(edone, sout));
+    chk(hipStreamWaitEvent(s, edone, 0));
+    cleanup();  // each event is released once the work it marks has run
+    if (!ok) return CCL_ERR_HIP;
+    return finish_launches();
+}
+
 int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t width,
                int32_t *labels, int32_t *counts, void *workspace, size_t workspace_bytes,
                void *stream)
@@ -331,6 +473,7 @@ const char *ccl_status_string(int status)
         return "band_rows must be a non-negative multiple of 64 with band_rows*width < 2^31 "
                "(with numbers also band_rows*width + 2*width*(bands-1) <= 2^31-3)";
     case CCL_ERR_SCRATCH: return "batch needs more workspace than the static scratch array holds";
+    case CCL_ERR_STREAM: return "the copy streams must be two streams other than the call's stream";
     default: return "unknown status";
     }
 }

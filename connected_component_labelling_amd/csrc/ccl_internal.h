@@ -140,8 +140,11 @@ Work bind_work(const Layout &L, void *workspace);
 // ignore: pixels of colour ign take part in nothing (their regions are neither
 // labelled nor counted).  clear_err: the tile pass clears the workspace's
 // error word first (the first kernel of a call).
+// t0, nt: the pass labels tiles t0 .. t0+nt-1 only (a band of whole tile rows
+// whose pixels, and the row above them, are in place); nt = 0: every tile
 void launch_tile(const void *img, int dtype_bytes, int conn, int ignore, uint32_t ign,
-                 const Geom &g, const Work &w, int clear_err, hipStream_t s);
+                 const Geom &g, const Work &w, int clear_err, hipStream_t s, uint32_t t0 = 0,
+                 uint32_t nt = 0);
 void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s);
 void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s);
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
@@ -149,7 +152,7 @@ void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int u
 void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s);
 // ignv: the value written for pixels of an ignored colour
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,
-                  hipStream_t s);
+                  hipStream_t s, uint32_t t0 = 0, uint32_t nt = 0);
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
                          hipStream_t s);
 void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g, const Work &w,

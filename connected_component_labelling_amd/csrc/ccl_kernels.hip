@@ -922,6 +922,7 @@ struct TileArgs {
     Work w;
     uint32_t ign;        // the ignored colour (IGN instances only)
     uint32_t clear_err;  // workgroup 0 clears the error word (the call's first kernel)
+    uint32_t t0;         // the first tile of the launch (workgroup v: tile t0 + remap(v))
 };
 
 template <typename T, int CONN, bool IGN>
@@ -937,7 +938,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void
     // no kernel of this call has run before this one, and the later ones set
     // the word only after it has ended
     if (blockIdx.x == 0 && threadIdx.x == 0 && a.clear_err) *w.err = 0u;
-    const uint32_t t = remap_tile(blockIdx.x, gridDim.x);
+    const uint32_t t = a.t0 + remap_tile(blockIdx.x, gridDim.x);
     const TilePos tp = tile_pos(t, g);
     if (tp.vh == TH && tp.vw == TW)
         label_tile<CONN, true, IGN>(g, w, s, t, tp, load_tile<T, true>(img, g, tp, wave, lane), a.ign);
@@ -1742,7 +1743,8 @@ __device__ __forceinline__ void write_rows_x4(int32_t *o0, int64_t W, int vh, in
 }
 
 __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int32_t *out,
-                                                            int number, uint32_t ignv)
+                                                            int number, uint32_t ignv,
+                                                            uint32_t t0, uint32_t t1)
 {
     __shared__ uint32_t sLab[NWAVES][DLAB];
     __shared__ uint32_t sNode[NWAVES][KMAX + 1];  // + IGN_SLOT: the ignored pixels' value
@@ -1750,8 +1752,8 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     __shared__ uint32_t sPre[NWAVES][TH];
 
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t t = remap_tile(blockIdx.x, gridDim.x) * NWAVES + wave;
-    if (t >= (uint32_t)g.ntiles) return;
+    const uint32_t t = t0 + remap_tile(blockIdx.x, gridDim.x) * NWAVES + wave;
+    if (t >= t1) return;  // tiles t0 .. t1-1
     const TilePos tp = tile_pos(t, g);
     const int64_t y0 = tp.y0, x0 = tp.x0, W = g.W;
     const size_t t32 = (size_t)t * TH;
@@ -2205,10 +2207,10 @@ static inline unsigned grid_of(int64_t n, int64_t per)
 
 template <typename T, int CONN>
 static void launch_tile_t(const void *img, int ignore, uint32_t ign, const Geom &g, const Work &w,
-                          int clear_err, hipStream_t s)
+                          int clear_err, hipStream_t s, uint32_t t0, uint32_t nt)
 {
-    const dim3 grid((unsigned)g.ntiles), block(BLOCK);
-    const TileArgs<T> a{(const T *)img, g, w, ign, (uint32_t)(clear_err != 0)};
+    const dim3 grid(nt), block(BLOCK);
+    const TileArgs<T> a{(const T *)img, g, w, ign, (uint32_t)(clear_err != 0), t0};
     if (ignore)
         hipLaunchKernelGGL((tile_label_kernel<T, CONN, true>), grid, block, 0, s, a);
     else
@@ -2216,18 +2218,20 @@ static void launch_tile_t(const void *img, int ignore, uint32_t ign, const Geom 
 }
 
 void launch_tile(const void *img, int dtype_bytes, int conn, int ignore, uint32_t ign,
-                 const Geom &g, const Work &w, int clear_err, hipStream_t s)
+                 const Geom &g, const Work &w, int clear_err, hipStream_t s, uint32_t t0,
+                 uint32_t nt)
 {
     const int c = clear_err;
+    if (nt == 0) nt = (uint32_t)g.ntiles;
     if (dtype_bytes == 1) {
-        if (conn == 8) launch_tile_t<uint8_t, 8>(img, ignore, ign, g, w, c, s);
-        else launch_tile_t<uint8_t, 4>(img, ignore, ign, g, w, c, s);
+        if (conn == 8) launch_tile_t<uint8_t, 8>(img, ignore, ign, g, w, c, s, t0, nt);
+        else launch_tile_t<uint8_t, 4>(img, ignore, ign, g, w, c, s, t0, nt);
     } else if (dtype_bytes == 3) {
-        if (conn == 8) launch_tile_t<Rgb24, 8>(img, ignore, ign, g, w, c, s);
-        else launch_tile_t<Rgb24, 4>(img, ignore, ign, g, w, c, s);
+        if (conn == 8) launch_tile_t<Rgb24, 8>(img, ignore, ign, g, w, c, s, t0, nt);
+        else launch_tile_t<Rgb24, 4>(img, ignore, ign, g, w, c, s, t0, nt);
     } else {
-        if (conn == 8) launch_tile_t<uint32_t, 8>(img, ignore, ign, g, w, c, s);
-        else launch_tile_t<uint32_t, 4>(img, ignore, ign, g, w, c, s);
+        if (conn == 8) launch_tile_t<uint32_t, 8>(img, ignore, ign, g, w, c, s, t0, nt);
+        else launch_tile_t<uint32_t, 4>(img, ignore, ign, g, w, c, s, t0, nt);
     }
 }
 
@@ -2258,10 +2262,11 @@ void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s)
 }
 
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,
-                  hipStream_t s)
+                  hipStream_t s, uint32_t t0, uint32_t nt)
 {
-    hipLaunchKernelGGL(final_write_kernel, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0, s, g,
-                       w, out, number, ignv);
+    if (nt == 0) nt = (uint32_t)g.ntiles;
+    hipLaunchKernelGGL(final_write_kernel, dim3(grid_of(nt, NWAVES)), dim3(BLOCK), 0, s, g, w,
+                       out, number, ignv, t0, t0 + nt);
 }
 
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,

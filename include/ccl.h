@@ -66,9 +66,11 @@ typedef enum {
                                    multiple of 64, or band_rows*width > 2^31-1, or
                                    (CCL_NUMBER) band_rows*width + 2*width*(bands-1)
                                    > 2^31-3: numbers pass through int32 codes        */
-    CCL_ERR_SCRATCH = -11       /* ccl_label_noalloc: the batch needs more workspace
+    CCL_ERR_SCRATCH = -11,      /* ccl_label_noalloc: the batch needs more workspace
                                    than the static scratch array holds
                                    (ccl_workspace_bytes() > CCL_SCRATCH_BYTES)       */
+    CCL_ERR_STREAM = -12        /* ccl_label_host: the two copy streams are NULL,
+                                   the same stream, or the call's own stream         */
 } ccl_status;
 
 /* Colour element types; the value is the size of one pixel in bytes.
@@ -211,6 +213,53 @@ typedef struct {
 int ccl_region_stats(const int32_t *labels, int64_t batch, int64_t height, int64_t width,
                      const int32_t *counts, int64_t n_total, ccl_region *stats,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ccl_label for a picture in host memory, with the copies overlapped with the
+ * labelling.  On a discrete GPU most of a call from host memory is the copy
+ * of the picture in and of the labels out ("Accountable AI starts at the
+ * pixel", ch.09 "Results", Fig. 20 "Where the time of one call goes"); here
+ * the copies run on two streams of their own beside the kernels, in steps:
+ *   - a large image is cut into bands of band_rows rows (automatic: an eighth
+ *     of the image, but at least 2^22 pixels, for images above 2^23 pixels);
+ *     smaller images are taken whole, in groups of at least 2^22 pixels;
+ *   - every step's pixels are copied in, in order, on h2d_stream, and each
+ *     band's tile pass starts as soon as its pixels are in (it reads the row
+ *     above it from the band before);
+ *   - the seam merge, seam roots, scan and resolve run once per image (or
+ *     group of images), after its last band: a region at the bottom of a
+ *     picture can change the labels at its top, so no label of an image
+ *     leaves before the whole image is in;
+ *   - each band's final write is followed by the copy of its labels out on
+ *     d2h_stream, while the next band is written;
+ *   - images are independent, so one group's pixels come in while the group
+ *     before is labelled and its labels go out (both PCIe directions at once).
+ * The call is complete, host_out included, when `stream` reaches its end.
+ *   host_colours  host, [batch, height, width] as for ccl_label; page-locked
+ *                 (hipHostMalloc, or torch's pin_memory()), else HIP copies
+ *                 through staging buffers and the copies do not overlap
+ *   host_out      host int32 [batch, height, width], page-locked: leaders or
+ *                 numbers as ccl_label writes them
+ *   counts        device int32 [batch] or NULL
+ *   dev_colours   device, batch*height*width pixels: where the picture is
+ *                 copied to (left holding it)
+ *   dev_out       device int32 [batch, height, width]: the labels on the
+ *                 device (left holding them)
+ *   workspace     device, at least ccl_workspace_bytes(batch, height, width)
+ *   band_rows     rows per band, a multiple of 32 (CCL_ERR_BAND otherwise); 0:
+ *                 automatic; height or more: whole images
+ *   stream, h2d_stream, d2h_stream  three distinct streams (CCL_ERR_STREAM
+ *                 otherwise); the copy streams first wait for the work already
+ *                 on `stream`, and `stream` ends by waiting for the last copy
+ * Results do not depend on band_rows.  CCL_ERR_HIP: an event could not be
+ * made, or a copy or launch was rejected (work enqueued before it stays
+ * enqueued).  Other errors as for ccl_label.
+ */
+int ccl_label_host(const void *host_colours, int dtype, int64_t batch, int64_t height,
+                   int64_t width, int connectivity, int flags, uint32_t ignore, int32_t *host_out,
+                   int32_t *counts, void *dev_colours, int32_t *dev_out, void *workspace,
+                   size_t workspace_bytes, int64_t band_rows, void *stream, void *h2d_stream,
+                   void *d2h_stream);
 
 /*
  * Bytes of device workspace ccl_label_large needs for a batch of this shape

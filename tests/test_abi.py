@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("ccl_label", "ccl_number", "ccl_count", "ccl_workspace_bytes",
                      "ccl_status_string", "ccl_label_large", "ccl_large_workspace_bytes",
-                     "ccl_label_noalloc"):
+                     "ccl_label_noalloc", "ccl_label_host"):
         assert required in names
 
 
@@ -192,7 +192,36 @@ def test_noalloc_validation(lib):
     assert lib.ccl_status_string(-11)
 
 
+def test_label_host_validation(lib):
+    """ccl_label_host rejects bad arguments on the host before any HIP call."""
+    Hh = lib.ccl_label_host
+    S1, S2, S3 = ctypes.c_void_p(0x10), ctypes.c_void_p(0x20), ctypes.c_void_p(0x30)
+
+    def call(dtype=4, B=1, H=64, W=64, conn=8, flags=1, ign=0, hin=FAKE, hout=FAKE, din=FAKE,
+             dout=FAKE, ws=FAKE, wsb=1 << 30, band=0, s=S1, s_in=S2, s_out=S3):
+        return Hh(hin, dtype, B, H, W, conn, flags, ign, hout, None, din, dout, ws, wsb, band,
+                  s, s_in, s_out)
+    assert call(conn=6) == -4
+    assert call(dtype=2) == -5
+    assert call(B=-1) == -2
+    assert call(flags=4) == -8
+    assert call(dtype=1, flags=2, ign=300) == -9
+    assert call(band=48) == -10                  # not a multiple of 32 rows
+    assert call(band=-32) == -10
+    assert call(hin=None) == -1
+    assert call(hout=None) == -1
+    assert call(din=None) == -1
+    assert call(dout=None) == -1
+    assert call(ws=None) == -1
+    assert call(s_in=None) == -12                # the copy streams: two, and not the call's
+    assert call(s_out=S1) == -12
+    assert call(s_in=S3) == -12
+    assert call(wsb=16) == -6                    # the batch's workspace is needed
+    assert call(B=4, wsb=lib.ccl_workspace_bytes(4, 64, 64) - 1) == -6
+    assert call(B=0, hin=None, hout=None, din=None, dout=None, ws=None) == 0
+
+
 def test_status_strings(lib):
-    for s in range(-11, 1):
+    for s in range(-12, 1):
         assert lib.ccl_status_string(s).decode()
     assert lib.ccl_status_string(-99) == b"unknown status"
