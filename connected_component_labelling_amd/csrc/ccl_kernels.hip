@@ -342,8 +342,10 @@ constexpr uint32_t WAVE_SLOTS = RPW * TW;  // slots of one wave (a run per pixel
 
 template <bool IGN>
 struct TileLds {
-    uint32_t P[TPX];               // parent of run slot; roots: + seam slot
-    uint16_t RXY[TPX];             // tile row << 8 | start column of run slot
+    // (each array has a tail of TW words past the run slots: lanes with
+    // nothing to store write there, so the row loop stores without branching)
+    uint32_t P[TPX + TW];          // parent of run slot; roots: + seam slot
+    uint16_t RXY[TPX + TW];        // tile row << 8 | start column of run slot
     uint16_t RowBase[TH];          // slot of the first run of each tile row
     uint32_t WaveRuns[NWAVES];     // runs in each wave's rows
     uint32_t Q[NWAVES][QCAP];      // queued joins: slot | other slot << 16
@@ -681,18 +683,22 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             const uint64_t jm = ra | rb;
             const uint64_t em = (st_m >> 1) | (1ull << 63);
             const uint64_t first = (~(jm | em) + st_m) & jm;
-            if (lane_bit(first)) {
-                const uint32_t tgt = lane_bit(rb) ? ab : ar;
-                __hip_atomic_store(&s.P[me], lds_parent<false>(s.P, tgt), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
+            // every lane reads and stores: a lane without a first join reads
+            // its own run's word and stores into the tail
+            const bool fl = lane_bit(first);
+            const uint32_t tgt = fl ? (lane_bit(rb) ? ab : ar) : me;
+            const uint32_t pv = lds_parent<false>(s.P, tgt);
+            __hip_atomic_store(&s.P[fl ? me : (uint32_t)(TPX + lane)], pv, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
             ra &= ~(first & ~rb);
             rb &= ~first;
         }
-        if (lane_bit(rb)) q[mbcnt_acc(rb, tail) & (QCAP - 1)] = me | (ab << 16);
-        tail += popc64(rb);
-        if (lane_bit(ra)) q[mbcnt_acc(ra, tail) & (QCAP - 1)] = me | (ar << 16);
-        tail += popc64(ra);
+        if ((rb | ra) != 0ull) {  // further joins (rare): queued as unions
+            if (lane_bit(rb)) q[mbcnt_acc(rb, tail) & (QCAP - 1)] = me | (ab << 16);
+            tail += popc64(rb);
+            if (lane_bit(ra)) q[mbcnt_acc(ra, tail) & (QCAP - 1)] = me | (ar << 16);
+            tail += popc64(ra);
+        }
     };
     // unite queued joins, 64 at a time while 64 wait (all: until none wait)
     auto drain = [&](bool all) {
@@ -725,10 +731,11 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             const uint32_t me = mbcnt_acc(st_m >> 1, wbase + nw);
             uint64_t ig_m = 0;
             if (IGN) ig_m = __ballot(cc == ign) & ok_m;
-            if (lane_bit(st_m)) {
-                s.RXY[me] = (uint16_t)((y << 8) | lane);
-                s.P[me] = me;
-            }
+            // the start lane of each run stores its row and column and its
+            // parent; the other lanes store into the arrays' tails
+            const uint32_t ws = lane_bit(st_m) ? me : (uint32_t)(TPX + lane);
+            s.RXY[ws] = (uint16_t)((y << 8) | lane);
+            s.P[ws] = me;
             // lane i keeps row i's masks.  A select, not a v_writelane: these
             // values live through the joins' divergent loops (gathered with an
             // inline-asm v_writelane, whose other lanes the compiler does not
@@ -798,27 +805,47 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     uint32_t *const s_hleft = s.Q[0];
     if (wave == 0 && lane < TH) s_hleft[lane] = hleft;
 
-    // ---- 3 Collapse; runs on an edge shared with another tile offer their
-    //      edge position as the region's seam slot (the smallest wins)
-    for (uint32_t r = tid; r < R; r += BLOCK) {
-        const uint32_t slot = run_slot(r);
-        const uint32_t rxy = s.RXY[slot];
-        const int ry = (int)(rxy >> 8), col = (int)(rxy & 63u);
-        const uint32_t root = lds_find<true>(s.P, slot);
-        if (root != slot) atomicMin(&s.P[slot], root);
-        // a run of the ignored colour joined nothing: it is its own root
-        if (IGN && ((s.Ign[ry] >> col) & 1ull)) continue;
-        const uint64_t mrow = s.Mask[ry];
-        uint32_t es = 255;
-        if (has_right && ((mrow >> col) >> 1) == 0ull) es = 2 * TW + TH + ry;  // the row's last run
-        if (has_left && col == 0) es = 2 * TW + ry;
-        if (has_bottom && ry == TH - 1) es = TW + popc64(mrow & mask_lt(col));
-        if (has_top && ry == 0) es = popc64(mrow & mask_lt(col));
-        if (es != 255) atomicMax(&s.P[root], ((255u - es) << 16) | root);
+    // ---- 3 Collapse, in two steps.  First the runs on an edge shared with
+    //      another tile offer their edge position as their region's seam slot
+    //      (the smallest wins): thread k < 64 takes the k-th run of the top
+    //      row, 64 + k of the bottom row, 128 + y the first run of row y and
+    //      160 + y its last run.
+    if (tid < KMAX) {
+        const int part = tid >> 5;  // 0, 1: top; 2, 3: bottom; 4: left; 5: right
+        uint32_t slot = 0, es = 255;
+        if (part < 2) {
+            const uint64_t m0 = s.Mask[0];
+            if (has_top && (uint32_t)tid < popc64(m0)) {
+                slot = (uint32_t)tid;  // row 0 starts at slot 0
+                es = (uint32_t)tid;
+            }
+        } else if (part < 4) {
+            const uint32_t k = (uint32_t)tid - TW;
+            if (has_bottom && k < popc64(s.Mask[TH - 1])) {
+                slot = s.RowBase[TH - 1] + k;
+                es = TW + k;
+            }
+        } else {
+            const int y = tid & (TH - 1);
+            if (y < vh && (part == 4 ? has_left : has_right)) {
+                slot = s.RowBase[y] + (part == 4 ? 0u : popc64(s.Mask[y]) - 1u);
+                es = (uint32_t)(2 * TW) + (part == 4 ? 0u : (uint32_t)TH) + (uint32_t)y;
+            }
+        }
+        if (IGN && es != 255) {  // a run of the ignored colour offers nothing
+            const uint32_t sxy = s.RXY[slot];
+            if ((s.Ign[sxy >> 8] >> (sxy & 63u)) & 1ull) es = 255;
+        }
+        if (es != 255) {
+            const uint32_t root = lds_find<true>(s.P, slot);
+            atomicMax(&s.P[root], ((255u - es) << 16) | root);
+        }
     }
     lds_barrier();
 
-    // ---- 4 Write: one thread per run; records in reading order
+    // ---- 4 Write: one thread per run; records in reading order.  Each run
+    //      finds its root (and points straight at it: the last steps read
+    //      one arrow per run)
     uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
     for (uint32_t r = tid; r < R; r += BLOCK) {
         const uint32_t slot = run_slot(r);
@@ -829,9 +856,10 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
                 continue;
             }
         }
-        const uint32_t pv = s.P[slot];
-        const uint32_t root = pv & PMASK;
-        const uint32_t rv = root == slot ? pv : s.P[root];
+        const uint32_t root = lds_find<true>(s.P, slot);
+        const uint32_t rv = s.P[root];
+        // (a root keeps its word, seam slot included: it stores into the tail)
+        atomicMin(&s.P[root == slot ? (uint32_t)(TPX + lane) : slot], root);
         const uint32_t es = 255u - (rv >> 16);
         const uint32_t rxy = s.RXY[root];
         const uint32_t rrow = rxy >> 8, rcol = rxy & 63u;
