@@ -19,7 +19,9 @@ most common value) ignored (CCL_IGNORE, "Accountable AI starts at the pixel"
 ch.08 idea 4); "rgb24_leg", the same sheet stored as RGB bytes (3 B/px, read
 in place, same page ch.09), labelled whole and with the paper ignored;
 "stats_leg", the per-region statistics pass over the sheet's numbers (with
-HIP events around its two kernels; it reads 4 B/px of labels); "large_leg",
+HIP events around its two kernels; it reads 4 B/px of labels);
+"label_stats_leg", ccl_label_stats (numbers and the same statistics in one
+call, from the run records), checked against the two calls; "large_leg",
 ccl_label_large (64-bit leaders and numbers, bands joined across their seams)
 numbering a 46400 x 46400 tissue picture of 2.15 G pixels, beyond the int32
 index range (same page, ch.11), with HIP events around each call (alone with
@@ -291,6 +293,7 @@ def stats_leg(ccl, labels, counts, npx, steps, warmup, stream, hip, torch):
     torch.cuda.synchronize()
     ms = float(np.median([hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]) for k in range(steps)]))
     hip.destroy(ev)
+    stats_leg.records = rec
     return {
         "regions": n_total,
         "ms_per_call": round(ms, 4),
@@ -298,6 +301,45 @@ def stats_leg(ccl, labels, counts, npx, steps, warmup, stream, hip, torch):
         "unit": "Gpixels/s",
         "label_read_GBps": round(npx * 4 / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(npx * 4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
+def label_stats_leg(ccl, dev, lab, n_total, npx, bpp, steps, warmup, stream, hip, torch,
+                    label_ms, stats_ms, stats_rec):
+    """Time ccl_label_stats (numbers, counts and per-region statistics in one
+    call) on the headline picture, with HIP events around each call; its
+    labels, counts and records must equal those of ccl_label followed by
+    ccl_region_stats."""
+    import numpy as np
+    B, H, W = lab.B, lab.H, lab.W
+    out = torch.empty((B, H, W), dtype=torch.int32, device=dev.device)
+    cnt = torch.empty(B, dtype=torch.int32, device=dev.device)
+    rec = torch.empty((max(n_total, 1), 5), dtype=torch.int64, device=dev.device)
+    ws = torch.zeros(ccl.workspace_bytes(B, H, W), dtype=torch.uint8, device=dev.device)
+    lib = ccl._load()
+    args = [ccl._ptr(dev), 4 if bpp == 4 else 1, B, H, W, 8, 1, 0, ccl._ptr(out), ccl._ptr(cnt),
+            ccl._ptr(rec), n_total, ccl._ptr(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream)]
+    for _ in range(warmup):
+        ccl._check(lib.ccl_label_stats(*args))
+    ev = hip.create(2 * steps)
+    torch.cuda.synchronize()
+    for k in range(steps):
+        hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k]), ctypes.c_void_p(stream.cuda_stream))
+        ccl._check(lib.ccl_label_stats(*args))
+        hip.lib.hipEventRecord(ctypes.c_void_p(ev[2 * k + 1]), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms = float(np.median([hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]) for k in range(steps)]))
+    hip.destroy(ev)
+    same = bool(torch.equal(out, lab.out) and torch.equal(cnt, lab.counts)
+                and torch.equal(rec[:n_total], stats_rec))
+    err = int(ws[:4].view(torch.int32).item())
+    return {
+        "ms_per_call": round(ms, 4),
+        "value": round(npx / (ms * 1e-3) / 1e9, 3),
+        "unit": "Gpixels/s labelled+numbered+statistics",
+        "label_then_region_stats_ms": round(label_ms + stats_ms, 4),
+        "same_as_label_then_region_stats": same,
+        "error_word": err,
     }
 
 
@@ -678,6 +720,7 @@ def main():
     ignore_leg = None
     rgb24_leg = None
     stats = None
+    label_stats = None
     large = None
     two = None
     host = None
@@ -690,6 +733,11 @@ def main():
         stats = stats_leg(ccl, lab.out, lab.counts, npx, args.steps, args.warmup, stream, hip,
                           torch)
         print(f"[bench] stats leg done ({args.steps} calls)", file=sys.stderr, flush=True)
+        label_stats = label_stats_leg(ccl, dev, lab, stats["regions"], npx, bpp, args.steps,
+                                      args.warmup, stream, hip, torch, ms_per_step,
+                                      stats["ms_per_call"], stats_leg.records)
+        stats_leg.records = None
+        print(f"[bench] label+stats leg done ({args.steps} calls)", file=sys.stderr, flush=True)
         paper = most_common_colour(img_np)
         ignore_leg = extra_leg(lab, dev, npx, bpp, args, stream, hip, torch, ignore=paper)
         print(f"[bench] ignore leg done ({args.steps} steps)", file=sys.stderr, flush=True)
@@ -789,6 +837,7 @@ def main():
         "ignore_leg": ignore_leg,
         "rgb24_leg": rgb24_leg,
         "stats_leg": stats,
+        "label_stats_leg": label_stats,
         "two_call_leg": two_call,
         "two_stream_leg": two,
         "host_leg": host,

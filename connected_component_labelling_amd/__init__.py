@@ -32,7 +32,7 @@ from . import build as _build
 
 __all__ = ["label", "number", "count", "region_stats", "workspace_bytes", "Labeller",
            "error_word", "CclError", "library_path", "label_large", "large_workspace_bytes",
-           "label_noalloc", "SCRATCH_BYTES", "label_host", "HostLabeller"]
+           "label_noalloc", "SCRATCH_BYTES", "label_host", "HostLabeller", "label_stats"]
 
 CCL_U8, CCL_RGB24, CCL_U32 = 1, 3, 4
 CCL_NUMBER, CCL_IGNORE = 1, 2
@@ -72,6 +72,9 @@ def _load():
     lib.ccl_count.restype = ctypes.c_int
     lib.ccl_region_stats.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp, sz, vp]
     lib.ccl_region_stats.restype = ctypes.c_int
+    lib.ccl_label_stats.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_uint32, vp, vp, vp, i64, vp, sz, vp]
+    lib.ccl_label_stats.restype = ctypes.c_int
     lib.ccl_large_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.ccl_large_workspace_bytes.restype = sz
     lib.ccl_label_large.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
@@ -294,9 +297,52 @@ def region_stats(labels: torch.Tensor, counts: torch.Tensor, n_total: int | None
     _check(_load().ccl_region_stats(_ptr(x), B, H, W, _ptr(counts.contiguous()), n_total,
                                     _ptr(rec), _ptr(workspace), workspace.numel(),
                                     ctypes.c_void_p(_stream_handle(stream))))
+    return _stats_views(rec)
+
+
+def _stats_views(rec: torch.Tensor) -> dict:
     r32 = rec.view(torch.int32)
     return {"records": rec, "area": r32[:, 4], "bbox": r32[:, 5:9], "sum_y": rec[:, 0],
             "sum_x": rec[:, 1]}
+
+
+def label_stats(img: torch.Tensor, max_regions: int, connectivity: int = 8, stream=None,
+                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                records: torch.Tensor | None = None, ignore: int | None = None,
+                rgb: bool = False, trim: bool = True, check: bool = False):
+    """``label(img, number=True)`` and ``region_stats`` in one call
+    (ccl_label_stats): the statistics come from the run records of the call,
+    not from a pass over the labels.  ``max_regions`` is the capacity of the
+    records (regions past it are not recorded; ``records``, if given, is a
+    contiguous int64 [>= max_regions, 5] tensor).  Returns (labels, counts,
+    stats) with ``stats`` as ``region_stats`` gives it; with ``trim`` (waits
+    for the device) its views are cut to the number of regions recorded.
+    ``check`` as for ``label``."""
+    _require_device(img, "img")
+    x, squeeze = _batch_view(img, rgb)
+    B, H, W = x.shape[:3]
+    out, ret = _output(out, B, H, W, torch.int32, img.device, squeeze)
+    counts = torch.empty(B, dtype=torch.int32, device=img.device)
+    cap = int(max_regions)
+    if records is None:
+        records = torch.empty((max(cap, 1), 5), dtype=torch.int64, device=img.device)
+    elif records.dtype != torch.int64 or records.dim() != 2 or records.shape[1] != 5 or \
+            records.shape[0] < cap or not records.is_contiguous():
+        raise ValueError("records must be a contiguous int64 [max_regions, 5] tensor")
+    if workspace is None:
+        workspace = _new_workspace(B, H, W, img.device)
+    flags, ign = _flags(True, ignore)
+    _check(_load().ccl_label_stats(_ptr(x), _dtype_code(x, rgb), B, H, W, int(connectivity), flags,
+                                   ign, _ptr(out), _ptr(counts), _ptr(records), cap,
+                                   _ptr(workspace), workspace.numel(),
+                                   ctypes.c_void_p(_stream_handle(stream))))
+    if check and B * H * W > 0:
+        _check_word(workspace, stream)
+    rec = records
+    if trim:
+        n = min(cap, int(counts.to(torch.int64).sum().item()))
+        rec = records[:n]
+    return ret, counts, _stats_views(rec)
 
 
 def large_workspace_bytes(batch: int, height: int, width: int, band_rows: int = 0) -> int:

@@ -385,6 +385,45 @@ int ccl_label_host(const void *host_colours, int dtype, int64_t batch, int64_t h
     return finish_launches();
 }
 
+int ccl_label_stats(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
+                    int connectivity, int flags, uint32_t ignore, int32_t *out, int32_t *counts,
+                    ccl_region *stats, int64_t stats_capacity, void *workspace,
+                    size_t workspace_bytes, void *stream)
+{
+    bool empty;
+    int rc = check_label_args(dtype, batch, height, width, connectivity, flags, ignore, &empty);
+    if (rc != CCL_OK) return rc;
+    if (!(flags & CCL_NUMBER)) return CCL_ERR_FLAGS;  // records are indexed by number
+    if (stats_capacity < 0) return CCL_ERR_SHAPE;
+    if (!counts || (stats_capacity > 0 && !stats)) return CCL_ERR_NULL;
+    hipStream_t s = (hipStream_t)stream;
+    if (empty) {
+        if (batch > 0) {
+            launch_zero_i32(counts, batch, s);
+            return finish_launches();
+        }
+        return CCL_OK;
+    }
+    if (!colours || !out || !workspace) return CCL_ERR_NULL;
+    Layout L;
+    if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+    if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
+    const Work w = bind_work(L, workspace);
+    const int ign = (flags & CCL_IGNORE) != 0;
+    static_assert(sizeof(ccl_region) == sizeof(RegionRec), "one record layout");
+    RegionRec *rec = (RegionRec *)stats;
+    launch_tile(colours, dtype, connectivity, ign, ignore, L.g, w, 1, s);
+    launch_seam(L.g, w, connectivity, s);
+    launch_seam_roots(L.g, w, s);
+    launch_scan(L.g, w, counts, 1, 1, s);
+    launch_label_stats(L.g, w, counts, rec, stats_capacity, 0, s);  // first record of each image
+    launch_resolve(L.g, w, 1, s, rec, stats_capacity);              // opens seam regions' records
+    launch_final(L.g, w, out, 1, 0u, s);
+    launch_label_stats(L.g, w, counts, rec, stats_capacity, 1, s);  // regions inside tiles; parts
+    launch_label_stats(L.g, w, counts, rec, stats_capacity, 2, s);  // parts into the records
+    return finish_launches();
+}
+
 int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t width,
                int32_t *labels, int32_t *counts, void *workspace, size_t workspace_bytes,
                void *stream)

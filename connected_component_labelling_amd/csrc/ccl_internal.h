@@ -149,7 +149,12 @@ void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s);
 void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s);
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
                  hipStream_t s);
-void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s);
+struct RegionRec;
+// rec: with numbers, each region that crosses a tile edge gets an empty record
+// (statistics of the labelling call; the band-status words hold the first
+// record of each image by then)
+void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s,
+                    RegionRec *rec = nullptr, int64_t cap = 0);
 // ignv: the value written for pixels of an ignored colour
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,
                   hipStream_t s, uint32_t t0 = 0, uint32_t nt = 0);
@@ -168,6 +173,11 @@ static_assert(sizeof(RegionRec) == 40, "40-byte region records");
 // words hold the first record of each image (B int64 fit in its B*nty words)
 void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geom &g,
                          const Work &w, int64_t n_total, RegionRec *recs, hipStream_t s);
+// statistics of the labelling call: stage 0 the first record of each image
+// (into the band-status words, after the scan), stage 1 the records pass
+// (after the final write), stage 2 the reduce pass
+void launch_label_stats(const Geom &g, const Work &w, const int32_t *counts, RegionRec *rec,
+                        int64_t cap, int stage, hipStream_t s);
 void launch_zero_i32(int32_t *p, int64_t n, hipStream_t s);
 
 }  // namespace ccl

@@ -1665,7 +1665,26 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_kernel(Geom g, Work w, int32_
 // workgroup's threads.  The records are only read here, so the walks may run
 // side by side; the values go to nval (a one-colour tile: its header).
 
-__global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int number)
+// Statistics outputs of the labelling call (rec == nullptr: none): records of
+// the image's regions, image b's region k at off[b] + k - 1, only the first
+// cap written.
+struct StatsOut {
+    RegionRec *rec;
+    int64_t cap;
+    const int64_t *off;  // [B] first record of each image
+};
+
+// an empty record: area 0, box (INT32_MAX, INT32_MAX, -1, -1), sums 0
+__device__ __forceinline__ void stats_empty(RegionRec *r)
+{
+    uint64_t *q = (uint64_t *)r;
+    q[0] = q[1] = 0ull;                                      // sums
+    q[2] = (uint64_t)2147483647u << 32;                      // area 0, y0 INT32_MAX
+    q[3] = 2147483647u | ((uint64_t)0xFFFFFFFFu << 32);      // x0 INT32_MAX, y1 -1
+    q[4] = 0xFFFFFFFFu;                                      // x1 -1, pad 0
+}
+
+__global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int number, StatsOut so)
 {
     __shared__ uint32_t sOff[SEAM_TILES + 1];
     __shared__ uint64_t sUsed[SEAM_TILES][KMAX / 64];
@@ -1700,7 +1719,7 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
         for (int word = 0; word < KMAX / 64; ++word) u[word] = sUsed[j][word];
         const uint32_t node = (t << 8) | (sUni[j] ? UNI_SLOT : select_bit(u, i - sOff[j]));
         uint64_t rrec;
-        g_root(w, node, rrec);
+        const uint32_t root = g_root(w, node, rrec);
         const uint32_t key = (uint32_t)(rrec >> 32);
         uint32_t val = key;
         if (number) {
@@ -1718,6 +1737,12 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
             w.hdr[t].value = val;  // a one-colour tile's only node
         else
             w.nval[(size_t)t * KMAX + (node & 0xFFu)] = val;
+        // statistics: each region that crosses a tile edge has one root
+        // node, which opens its record (the tiles' parts are added later)
+        if (so.rec != nullptr && root == node) {
+            const int64_t idx = so.off[fast_div(t, g.divTpi)] + (int64_t)val - 1;
+            if (idx < so.cap) stats_empty(&so.rec[idx]);
+        }
     }
 }
 
@@ -2226,6 +2251,352 @@ __global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t 
     }
 }
 
+// ------------------------------------ statistics in the labelling call
+// ccl_label_stats computes the records of ccl_region_stats inside the
+// labelling call, from the run records the final write expands (row masks and
+// per-run records: about 0.4 B/px), not from the labels.  Three steps:
+//   - resolve opens the record of every region that crosses a tile edge (its
+//     root seam node does, once);
+//   - stats_records_kernel, one wave per tile of several colours: a region
+//     inside the tile is complete there, its record is written whole; the
+//     part of a region on the tile's edges is packed into 64 bits in its seam
+//     node's record slot (free once resolve has run);
+//   - stats_reduce_kernel, one workgroup per block of 8x8 tiles: the parts of
+//     the block's seam nodes (and of its one-colour tiles, in closed form) are
+//     gathered per region in an LDS table and added to the records with
+//     global atomics, so a region covering the picture takes one set of
+//     atomics per block.
+
+// first record of each image: exclusive prefix of the per-image region counts
+__global__ __launch_bounds__(BLOCK) void image_offsets_kernel(const int32_t *counts, int64_t B,
+                                                             int64_t *off)
+{
+    __shared__ uint32_t sWave[NWAVES];
+    const int64_t per = (B + BLOCK - 1) / BLOCK;
+    const int64_t j0 = (int64_t)threadIdx.x * per, j1 = min(B, j0 + per);
+    int64_t sum = 0;
+    for (int64_t j = j0; j < j1; ++j) sum += counts[j];
+    // (a batch has fewer than 2^32 regions: each needs a pixel and a batch has
+    // fewer than 2^24 tiles of 2048 pixels)
+    uint32_t total;
+    int64_t run = block_exclusive_scan((uint32_t)sum, sWave, total);
+    for (int64_t j = j0; j < j1; ++j) {
+        off[j] = run;
+        run += counts[j];
+    }
+}
+
+constexpr int SR_CAP = 128;  // regions inside one tile gathered per pass over its rows
+
+struct SrLds {  // one wave's tables
+    // regions inside the tile, by their rank among the tile's inner roots
+    // (reading order) minus the pass's first rank
+    uint32_t ia[SR_CAP];    // area | sum of local rows << 11
+    uint32_t isx[SR_CAP];   // sum of local columns
+    uint32_t ix0[SR_CAP], ix1[SR_CAP], iy1[SR_CAP];
+    uint32_t ipos[SR_CAP];  // root run: row << 6 | column
+    // parts of regions on the tile's edges, by seam slot
+    uint32_t ba[KMAX], bsx[KMAX], by0[KMAX], bx0[KMAX], by1[KMAX], bx1[KMAX];
+    uint64_t ir[TH];        // inner roots' start columns in each row
+    uint32_t irpre[TH];     // inner roots in the rows before
+    uint64_t lead[TH];      // leaders of each row segment
+    uint32_t pre[TH];       // leaders of the image before each row segment
+    uint16_t info[DLAB];    // the tile's first run records
+};
+
+// a region's part in one tile, packed: area (11 bits: at most 2047 pixels in a
+// tile of several colours), sums of local rows (15: at most 31744) and local
+// columns (16: at most 64512), rows y0, y1 (5 each), columns x0, x1 (6 each)
+__device__ __forceinline__ uint64_t pack_part(uint32_t a, uint32_t sy, uint32_t sx, uint32_t y0,
+                                              uint32_t y1, uint32_t x0, uint32_t x1)
+{
+    return (uint64_t)a | ((uint64_t)sy << 11) | ((uint64_t)sx << 26) | ((uint64_t)y0 << 42) |
+           ((uint64_t)y1 << 47) | ((uint64_t)x0 << 52) | ((uint64_t)x1 << 58);
+}
+
+// a one-colour tile's whole record (its region lies in this tile alone)
+__device__ __forceinline__ void tile_record(RegionRec *r, const TilePos &tp)
+{
+    const int64_t vh = tp.vh, vw = tp.vw, y0 = tp.y0, x0 = tp.x0;
+    uint64_t *q = (uint64_t *)r;
+    q[0] = (uint64_t)(vw * (vh * y0 + vh * (vh - 1) / 2));
+    q[1] = (uint64_t)(vh * (vw * x0 + vw * (vw - 1) / 2));
+    q[2] = (uint64_t)(uint32_t)(vh * vw) | ((uint64_t)(uint32_t)y0 << 32);
+    q[3] = (uint64_t)(uint32_t)x0 | ((uint64_t)(uint32_t)(y0 + vh - 1) << 32);
+    q[4] = (uint64_t)(uint32_t)(x0 + vw - 1);
+}
+
+__global__ __launch_bounds__(BLOCK) void stats_records_kernel(Geom g, Work w, StatsOut so)
+{
+    __shared__ SrLds sl[NWAVES];
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t t = remap_tile(blockIdx.x, gridDim.x) * NWAVES + wave;
+    if (t >= (uint32_t)g.ntiles) return;
+    const TilePos tp = tile_pos(t, g);
+    const TileHdr &h = w.hdr[t];
+    const uint32_t kind = h.kind;
+    const int64_t off = so.off[tp.b];
+    if (kind & KIND_UNIFORM) {
+        // one colour: with an open edge its part is added by the reduce pass;
+        // with none the tile is the whole image and its region ends here
+        if (((kind >> 8) & 0xFFu) != 255u || (kind & KIND_IGNORED)) return;
+        const int64_t idx = off + (int64_t)h.pre;  // number 1 + pre, record number - 1
+        if (lane == 0 && idx < so.cap) tile_record(&so.rec[idx], tp);
+        return;
+    }
+    SrLds &L = sl[wave];
+    const int vh = tp.vh, vw = tp.vw;
+    const uint32_t R = h.value;  // runs
+    const size_t t32 = (size_t)t * TH;
+    const uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
+    // lane y: row y's run starts, leaders and leaders before it (for numbers)
+    const uint64_t mk = lane < TH ? w.runmask[t32 + lane] : 0ull;
+    const uint64_t ld = lane < TH ? w.leadmask[t32 + lane] : 0ull;
+    const uint32_t pr = lane < TH ? w.seg[t32 + lane] : 0u;
+    const uint32_t nl = R < DLAB ? R : DLAB;
+    for (uint32_t r = lane; r < nl; r += 64) L.info[r] = rinfo[r];
+    if (lane < TH) {
+        L.lead[lane] = ld;
+        L.pre[lane] = pr;
+    }
+    for (int i = lane; i < KMAX; i += 64) {
+        L.ba[i] = L.bsx[i] = L.by1[i] = L.bx1[i] = 0u;
+        L.by0[i] = L.bx0[i] = 0xFFFFFFFFu;
+    }
+    // runs before each row (lane y holds row y's)
+    const uint32_t cnt = popc64(mk);
+    uint32_t inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t v = __shfl_up(inc, d);
+        if (lane >= d) inc += v;
+    }
+    const uint32_t rex = inc - cnt;
+    const uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
+    __syncwarp();
+    auto info_of = [&](uint32_t r) -> uint32_t { return r < DLAB ? L.info[r] : rinfo[r]; };
+
+    // inner roots of each row: a start lane whose run record names itself
+    uint32_t ni = 0;  // inner roots so far
+    for (int y = 0; y < vh; ++y) {
+        const uint64_t m = ((uint64_t)__builtin_amdgcn_readlane(mhi, y) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane(mlo, y);
+        const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
+        bool root = false;
+        if (lane_bit(m)) {
+            const uint32_t info = info_of(rb + mbcnt(m));
+            root = !(info & INFO_BORDER) && info == (((uint32_t)y << 6) | (uint32_t)lane);
+        }
+        const uint64_t irm = __ballot(root);
+        if (lane == 0) {
+            L.ir[y] = irm;
+            L.irpre[y] = ni;
+        }
+        ni += popc64(irm);
+    }
+    __syncwarp();
+
+    // passes over the rows: pass p gathers the inner regions of rank
+    // [p*SR_CAP, (p+1)*SR_CAP), pass 0 also the edge regions' parts
+    for (uint32_t p0 = 0; p0 == 0 || p0 < ni; p0 += SR_CAP) {
+        const uint32_t nin = ni - p0 < (uint32_t)SR_CAP ? ni - p0 : (uint32_t)SR_CAP;
+        for (uint32_t i = lane; i < nin; i += 64) {
+            L.ia[i] = L.isx[i] = L.ix1[i] = L.iy1[i] = 0u;
+            L.ix0[i] = 0xFFFFFFFFu;
+        }
+        __syncwarp();
+        for (int y = 0; y < vh; ++y) {
+            const uint64_t m = ((uint64_t)__builtin_amdgcn_readlane(mhi, y) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane(mlo, y);
+            const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
+            if (!lane_bit(m)) continue;
+            const uint32_t info = info_of(rb + mbcnt(m));
+            if (info == INFO_IGNORED) continue;
+            // the run: row y, columns lane .. e
+            const uint64_t above = (m >> lane) >> 1;
+            const uint32_t e = above ? (uint32_t)lane + (uint32_t)__builtin_ctzll(above)
+                                     : (uint32_t)vw - 1u;
+            const uint32_t len = e - (uint32_t)lane + 1u;
+            const uint32_t ay = len | ((len * (uint32_t)y) << 11);
+            const uint32_t sx = len * (uint32_t)lane + len * (len - 1u) / 2u;
+            if (info & INFO_BORDER) {
+                if (p0 != 0) continue;
+                const uint32_t sl_ = info & 0xFFu;
+                atomicAdd(&L.ba[sl_], ay);
+                atomicAdd(&L.bsx[sl_], sx);
+                atomicMin(&L.by0[sl_], (uint32_t)y);
+                atomicMax(&L.by1[sl_], (uint32_t)y);
+                atomicMin(&L.bx0[sl_], (uint32_t)lane);
+                atomicMax(&L.bx1[sl_], e);
+            } else {
+                const uint32_t ry = info >> 6, rc = info & 63u;
+                const uint32_t rank = L.irpre[ry] + popc64(L.ir[ry] & mask_lt((int)rc));
+                if (rank < p0 || rank >= p0 + nin) continue;
+                const uint32_t k = rank - p0;
+                if (ry == (uint32_t)y && rc == (uint32_t)lane) L.ipos[k] = info;
+                atomicAdd(&L.ia[k], ay);
+                atomicAdd(&L.isx[k], sx);
+                atomicMin(&L.ix0[k], (uint32_t)lane);
+                atomicMax(&L.ix1[k], e);
+                atomicMax(&L.iy1[k], (uint32_t)y);
+            }
+        }
+        __syncwarp();
+        // the pass's inner regions are complete: their records, whole
+        for (uint32_t i = lane; i < nin; i += 64) {
+            const uint32_t pos = L.ipos[i];
+            const int ry = (int)(pos >> 6), rc = (int)(pos & 63u);
+            const uint32_t number = 1u + L.pre[ry] + popc64(L.lead[ry] & mask_lt(rc));
+            const int64_t idx = off + (int64_t)number - 1;
+            if (idx >= so.cap) continue;
+            const uint32_t a = L.ia[i] & 0x7FFu, sy = L.ia[i] >> 11;
+            uint64_t *q = (uint64_t *)&so.rec[idx];
+            q[0] = (uint64_t)sy + (uint64_t)a * tp.y0;
+            q[1] = (uint64_t)L.isx[i] + (uint64_t)a * tp.x0;
+            q[2] = (uint64_t)a | ((uint64_t)(tp.y0 + (uint32_t)ry) << 32);
+            q[3] = (uint64_t)(tp.x0 + L.ix0[i]) | ((uint64_t)(tp.y0 + L.iy1[i]) << 32);
+            q[4] = (uint64_t)(tp.x0 + L.ix1[i]);
+        }
+        __syncwarp();
+    }
+    // the parts of the edge regions, into their seam nodes' record slots
+    for (int i = lane; i < KMAX; i += 64) {
+        if (L.ba[i] == 0u) continue;
+        w.gp[(size_t)t * KMAX + i] = pack_part(L.ba[i] & 0x7FFu, L.ba[i] >> 11, L.bsx[i], L.by0[i],
+                                               L.by1[i], L.bx0[i], L.bx1[i]);
+    }
+}
+
+constexpr int RD_CAP = 1024;   // regions of a block gathered in LDS
+constexpr int RD_PROBES = 16;  // table slots a region tries before its part goes to the record
+
+__device__ __forceinline__ void stats_add_global(RegionRec &r, uint32_t a, uint64_t sy, uint64_t sx,
+                                                 int32_t y0, int32_t x0, int32_t y1, int32_t x1)
+{
+    atomicAdd(&r.sum_y, (unsigned long long)sy);
+    atomicAdd(&r.sum_x, (unsigned long long)sx);
+    atomicAdd(&r.area, (int32_t)a);
+    atomicMin(&r.y0, y0);
+    atomicMin(&r.x0, x0);
+    atomicMax(&r.y1, y1);
+    atomicMax(&r.x1, x1);
+}
+
+__global__ __launch_bounds__(BLOCK) void stats_reduce_kernel(Geom g, Work w, StatsOut so)
+{
+    __shared__ uint32_t sKey[RD_CAP];  // region number, 0: free
+    __shared__ unsigned long long sSY[RD_CAP], sSX[RD_CAP];
+    __shared__ uint32_t sA[RD_CAP], sY0[RD_CAP], sX0[RD_CAP], sY1[RD_CAP], sX1[RD_CAP];
+    __shared__ uint64_t sUsed[BT][KMAX / 64];
+    __shared__ uint32_t sOff[BT + 1];
+    __shared__ uint8_t sUni[BT];
+    __shared__ uint32_t sWave[NWAVES];
+    const int j = threadIdx.x;
+    const BlockBase bb = block_base(g);
+    const BlockTile me = block_tile(g, bb, j);
+    const int64_t off = so.off[fast_div(bb.t0, g.divTpi)];
+    for (int i = j; i < RD_CAP; i += BLOCK) {
+        sKey[i] = 0u;
+        sSY[i] = sSX[i] = 0ull;
+        sA[i] = sY1[i] = sX1[i] = 0u;
+        sY0[i] = sX0[i] = 0x7FFFFFFFu;
+    }
+    // the block's seam nodes: a one-colour tile's (if it has an open edge and
+    // is not of the ignored colour), or the used seam slots of a tile of
+    // several colours
+    uint32_t n = 0;
+    bool uni = false;
+    uint64_t u[KMAX / 64] = {0ull, 0ull, 0ull};
+    if (me.valid) {
+        const uint32_t kind = w.hdr[me.t].kind;
+        uni = (kind & KIND_UNIFORM) != 0;
+        if (uni) {
+            n = (((kind >> 8) & 0xFFu) != 255u && !(kind & KIND_IGNORED)) ? 1u : 0u;
+        } else {
+#pragma unroll
+            for (int word = 0; word < KMAX / 64; ++word) {
+                u[word] = w.hdr[me.t].used[word];
+                n += popc64(u[word]);
+            }
+        }
+    }
+    if (j < BT) {
+#pragma unroll
+        for (int word = 0; word < KMAX / 64; ++word) sUsed[j][word] = u[word];
+        sUni[j] = uni ? 1 : 0;
+    }
+    uint32_t total;
+    const uint32_t noff = block_exclusive_scan(n, sWave, total);
+    if (j <= BT) sOff[j] = noff;  // entry BT: the total
+    __syncthreads();
+    for (uint32_t i = j; i < total; i += BLOCK) {
+        const uint32_t jj = item_tile<BT>(sOff, i);
+        const BlockTile bt = block_tile(g, bb, (int)jj);
+        const TilePos tp = tile_pos(bt.t, g);
+        uint32_t number, a;
+        uint64_t sy, sx;
+        int32_t y0, x0, y1, x1;
+        if (sUni[jj]) {
+            number = w.hdr[bt.t].value;
+            const int64_t vh = tp.vh, vw = tp.vw;
+            a = (uint32_t)(vh * vw);
+            sy = (uint64_t)(vw * (vh * (int64_t)tp.y0 + vh * (vh - 1) / 2));
+            sx = (uint64_t)(vh * (vw * (int64_t)tp.x0 + vw * (vw - 1) / 2));
+            y0 = (int32_t)tp.y0;
+            x0 = (int32_t)tp.x0;
+            y1 = (int32_t)(tp.y0 + vh - 1);
+            x1 = (int32_t)(tp.x0 + vw - 1);
+        } else {
+            uint64_t uu[KMAX / 64];
+#pragma unroll
+            for (int word = 0; word < KMAX / 64; ++word) uu[word] = sUsed[jj][word];
+            const uint32_t slot = select_bit(uu, i - sOff[jj]);
+            number = w.nval[(size_t)bt.t * KMAX + slot];
+            const uint64_t pk = w.gp[(size_t)bt.t * KMAX + slot];
+            a = (uint32_t)(pk & 0x7FFu);
+            sy = ((pk >> 11) & 0x7FFFu) + (uint64_t)a * tp.y0;
+            sx = ((pk >> 26) & 0xFFFFu) + (uint64_t)a * tp.x0;
+            y0 = (int32_t)(tp.y0 + ((pk >> 42) & 31u));
+            y1 = (int32_t)(tp.y0 + ((pk >> 47) & 31u));
+            x0 = (int32_t)(tp.x0 + ((pk >> 52) & 63u));
+            x1 = (int32_t)(tp.x0 + ((pk >> 58) & 63u));
+        }
+        // the region's entry in the table, or its record if none is free
+        uint32_t hsh = (number * 2654435761u) >> (32 - 10);
+        static_assert(RD_CAP == 1024, "the hash takes 10 bits");
+        int e = -1;
+        for (int p = 0; p < RD_PROBES; ++p, hsh = (hsh + 1u) & (RD_CAP - 1)) {
+            const uint32_t k = sKey[hsh];
+            if (k == number) { e = (int)hsh; break; }
+            if (k == 0u) {
+                const uint32_t old = atomicCAS(&sKey[hsh], 0u, number);
+                if (old == 0u || old == number) { e = (int)hsh; break; }
+            }
+        }
+        if (e < 0) {
+            const int64_t idx = off + (int64_t)number - 1;
+            if (idx < so.cap) stats_add_global(so.rec[idx], a, sy, sx, y0, x0, y1, x1);
+            continue;
+        }
+        atomicAdd(&sSY[e], (unsigned long long)sy);
+        atomicAdd(&sSX[e], (unsigned long long)sx);
+        atomicAdd(&sA[e], a);
+        atomicMin(&sY0[e], (uint32_t)y0);
+        atomicMin(&sX0[e], (uint32_t)x0);
+        atomicMax(&sY1[e], (uint32_t)y1);
+        atomicMax(&sX1[e], (uint32_t)x1);
+    }
+    __syncthreads();
+    for (int i = j; i < RD_CAP; i += BLOCK) {
+        const uint32_t k = sKey[i];
+        if (k == 0u) continue;
+        const int64_t idx = off + (int64_t)k - 1;
+        if (idx >= so.cap) continue;
+        stats_add_global(so.rec[idx], sA[i], sSY[i], sSX[i], (int32_t)sY0[i], (int32_t)sX0[i],
+                         (int32_t)sY1[i], (int32_t)sX1[i]);
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
 static inline unsigned grid_of(int64_t n, int64_t per)
@@ -2283,10 +2654,12 @@ void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int u
                        apply, use_hdr);
 }
 
-void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s)
+void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s, RegionRec *rec,
+                    int64_t cap)
 {
+    const StatsOut so{rec, cap, (const int64_t *)w.bandst};
     hipLaunchKernelGGL(resolve_kernel, dim3(grid_of(g.ntiles, SEAM_TILES)), dim3(BLOCK), 0, s, g, w,
-                       number);
+                       number, so);
 }
 
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,
@@ -2337,6 +2710,22 @@ void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geo
                        (int64_t *)w.bandst, w.err);
     const int64_t blocks = g.B * (int64_t)a.ay * (int64_t)a.ax;
     hipLaunchKernelGGL(stats_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
+}
+
+void launch_label_stats(const Geom &g, const Work &w, const int32_t *counts, RegionRec *rec,
+                        int64_t cap, int stage, hipStream_t s)
+{
+    const StatsOut so{rec, cap, (const int64_t *)w.bandst};
+    if (stage == 0) {
+        hipLaunchKernelGGL(image_offsets_kernel, dim3(1), dim3(BLOCK), 0, s, counts, g.B,
+                           (int64_t *)w.bandst);
+    } else if (stage == 1) {
+        hipLaunchKernelGGL(stats_records_kernel, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0, s,
+                           g, w, so);
+    } else {
+        const int64_t blocks = g.B * ((g.nty + MB - 1) / MB) * ((g.ntx + MB - 1) / MB);
+        hipLaunchKernelGGL(stats_reduce_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, g, w, so);
+    }
 }
 
 void launch_zero_i32(int32_t *p, int64_t n, hipStream_t s)

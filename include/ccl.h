@@ -262,6 +262,36 @@ int ccl_label_host(const void *host_colours, int dtype, int64_t batch, int64_t h
                    void *d2h_stream);
 
 /*
+ * ccl_label with CCL_NUMBER that also computes the per-region statistics of
+ * ccl_region_stats (area, bounding box, sums of row and column indices), in
+ * the same call, from the run records the final write expands instead of
+ * from the labels ("About Connected Components Labeling on GPU",
+ * introduction: bounding boxes; the tissue-scan segmentation article, section
+ * 1.1: area and position of each numbered region, section 6.1: sums gathered
+ * per block before global atomics).  A region inside one 64 x 32 tile gets its
+ * record there whole; a region crossing tile edges has its record opened by
+ * its root seam node and its parts, gathered per block of 8 x 8 tiles, added
+ * with atomics.
+ *   flags           must contain CCL_NUMBER (CCL_ERR_FLAGS otherwise); may
+ *                   contain CCL_IGNORE
+ *   counts          device int32 [batch], required
+ *   stats           device ccl_region [stats_capacity], 8-byte aligned: region
+ *                   k of image b is record counts[0] + ... + counts[b-1] + k - 1
+ *   stats_capacity  records the caller has room for (>= 0); records past it
+ *                   are not written.  The number of records written is
+ *                   min(capacity, counts[0] + ... + counts[batch-1]); the sum
+ *                   of counts tells whether the capacity was enough.
+ * Every record below the capacity and the regions' total is written, each
+ * once, with the values ccl_region_stats gives for the same labels.  Other
+ * arguments, memory, streams and errors as for ccl_label; the workspace is
+ * the one of ccl_workspace_bytes(batch, height, width).
+ */
+int ccl_label_stats(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
+                    int connectivity, int flags, uint32_t ignore, int32_t *out, int32_t *counts,
+                    ccl_region *stats, int64_t stats_capacity, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace ccl_label_large needs for a batch of this shape
  * and band height (256-byte aligned; its first 4 bytes are the error word, as
  * for ccl_workspace_bytes).  Pure host arithmetic.  Returns 0 for an empty

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("ccl_label", "ccl_number", "ccl_count", "ccl_workspace_bytes",
                      "ccl_status_string", "ccl_label_large", "ccl_large_workspace_bytes",
-                     "ccl_label_noalloc", "ccl_label_host"):
+                     "ccl_label_noalloc", "ccl_label_host", "ccl_label_stats"):
         assert required in names
 
 
@@ -190,6 +190,29 @@ def test_noalloc_validation(lib):
     assert N(FAKE, 4, 1, 8192, 4096, 8, 1, 0, FAKE, None, None) == -11
     assert N(FAKE, 1, 1, 24000, 33600, 8, 1, 0, FAKE, None, None) == -11
     assert lib.ccl_status_string(-11)
+
+
+def test_label_stats_validation(lib):
+    """ccl_label_stats: numbers required, counts required, records required
+    when there is room for any, a capacity of at least 0; all checked on the
+    host before any HIP call."""
+    S = lib.ccl_label_stats
+    ws = 1 << 30
+    # (colours, dtype, B, H, W, conn, flags, ignore, out, counts, stats, cap, ws, bytes, stream)
+    assert S(FAKE, 4, 1, 8, 8, 8, 0, 0, FAKE, FAKE, FAKE, 5, FAKE, ws, None) == -8
+    assert S(FAKE, 4, 1, 8, 8, 8, 2, 0, FAKE, FAKE, FAKE, 5, FAKE, ws, None) == -8
+    assert S(FAKE, 4, 1, 8, 8, 8, 1, 0, FAKE, None, FAKE, 5, FAKE, ws, None) == -1
+    assert S(FAKE, 4, 1, 8, 8, 8, 1, 0, FAKE, FAKE, None, 5, FAKE, ws, None) == -1
+    assert S(FAKE, 4, 1, 8, 8, 8, 1, 0, FAKE, FAKE, FAKE, -1, FAKE, ws, None) == -2
+    assert S(None, 4, 1, 8, 8, 8, 1, 0, FAKE, FAKE, FAKE, 5, FAKE, ws, None) == -1
+    assert S(FAKE, 4, 1, 8, 8, 8, 1, 0, None, FAKE, FAKE, 5, FAKE, ws, None) == -1
+    assert S(FAKE, 4, 1, 8, 8, 8, 1, 0, FAKE, FAKE, FAKE, 5, None, ws, None) == -1
+    assert S(FAKE, 4, 1, 8, 8, 8, 1, 0, FAKE, FAKE, FAKE, 5, FAKE, 16, None) == -6
+    assert S(FAKE, 4, 1, 8, 8, 6, 1, 0, FAKE, FAKE, FAKE, 5, FAKE, ws, None) == -4
+    assert S(FAKE, 2, 1, 8, 8, 8, 1, 0, FAKE, FAKE, FAKE, 5, FAKE, ws, None) == -5
+    assert S(FAKE, 1, 1, 8, 8, 8, 3, 256, FAKE, FAKE, FAKE, 5, FAKE, ws, None) == -9
+    # an empty batch: nothing to write
+    assert S(None, 4, 0, 8, 8, 8, 1, 0, None, FAKE, None, 0, None, 0, None) == 0
 
 
 def test_label_host_validation(lib):

@@ -356,6 +356,79 @@ def check_stats(ccl, name, img, conn=8, ignore=None, rgb=False):
     return exp_counts
 
 
+def check_label_stats(ccl, name, img, conn=8, ignore=None, rgb=False, capacity=None):
+    """ccl_label_stats (labels, counts and statistics in one call) equal the
+    oracle's numbers and its statistics of them, entry for entry; with a
+    capacity below the region count, only the records below it are written."""
+    announce(f"label+stats {name}", img, conn, ignore)
+    exp_labels, exp_counts = oracle.number(oracle.label(img, conn, ignore=ignore, rgb=rgb))
+    exp = oracle.region_stats(exp_labels, exp_counts)
+    n = int(exp_counts.sum())
+    cap = n if capacity is None else capacity
+    t = torch.from_numpy(np.ascontiguousarray(img.view(np.int32) if img.dtype == np.uint32 else img)).cuda()
+    records = torch.full((max(n, cap, 1) + 3, 5), 0x5A5A5A5A, dtype=torch.int64, device="cuda")
+    labels, counts, st = ccl.label_stats(t, cap, conn, ignore=ignore, rgb=rgb, records=records,
+                                         trim=False, check=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(labels.cpu().numpy(), exp_labels), f"label+stats {name}: numbers differ"
+    assert np.array_equal(counts.cpu().numpy(), exp_counts), f"label+stats {name}: counts differ"
+    got = {k: v.cpu().numpy() for k, v in st.items()}
+    m = min(n, cap)
+    for key in ("area", "bbox", "sum_y", "sum_x"):
+        a = got[key][:m]
+        e = exp[key][:m]
+        if not np.array_equal(a, e):
+            bad = np.argwhere(a.reshape(m, -1) != e.reshape(m, -1))
+            raise AssertionError(f"label+stats {name}: {key} differs at {len(bad)} entries, "
+                                 f"first {bad[:3].tolist()}")
+    untouched = got["records"][m:]
+    assert np.all(untouched == 0x5A5A5A5A), f"label+stats {name}: records past {m} written"
+    return exp_counts
+
+
+def test_label_stats_ragged_structured_batch(ccl):
+    """Statistics in the labelling call: ragged shapes in every dtype and both
+    connectivities, with and without an ignored colour, structured pictures,
+    mosaics, a batch, RGB, and a 4-connected checkerboard (every pixel a region,
+    many regions per tile, more than one pass over a tile's rows)."""
+    rng = np.random.default_rng(700)
+    for H, W in [(1, 1), (3, 700), (33, 65), (64, 64), (100, 129), (255, 513), (70, 90)]:
+        for conn in (8, 4):
+            img = rng.integers(0, 3, size=(H, W)).astype(np.uint8)
+            check_label_stats(ccl, f"random u8 {H}x{W}", img, conn)
+            check_label_stats(ccl, f"random u8 {H}x{W}", img, conn, ignore=0)
+            col = rng.integers(0, 2**32, size=3, dtype=np.uint64).astype(np.uint32)
+            check_label_stats(ccl, f"random u32 {H}x{W}", col[rng.integers(0, 3, size=(H, W))],
+                              conn)
+    for name, img in structured_images().items():
+        check_label_stats(ccl, name, img, 8)
+    for name, img in mosaic_images().items():
+        check_label_stats(ccl, name, img, 8, ignore=7)
+    check_label_stats(ccl, "bernoulli batch 5x100x90", synth.bernoulli_batch(5, 100, 90, seed=9), 8)
+    check_label_stats(ccl, "bernoulli batch 7x64x64, 4-conn",
+                      synth.bernoulli_batch(7, 64, 64, seed=4), 4, ignore=1)
+    yy, xx = np.mgrid[0:300, 0:600]
+    check_label_stats(ccl, "checkerboard 300x600 (every pixel a region)",
+                      ((yy + xx) % 2).astype(np.uint8), 4)
+    check_label_stats(ccl, "rgb drawing", synth.rgb24(synth.lines_image(256, 256, seed=1)), 8,
+                      rgb=True)
+    check_label_stats(ccl, "a uniform 20x30 image (one tile, one region)",
+                      np.full((20, 30), 5, np.uint8), 8)
+
+
+def test_label_stats_capacity(ccl):
+    img = synth.lines_image(300, 400, seed=6)
+    n = int(oracle.number(oracle.label(img, 8))[1].sum())
+    for cap in (0, 1, n // 3, n - 1, n + 5):
+        check_label_stats(ccl, f"drawing, capacity {cap} of {n}", img, 8, capacity=cap)
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 5])
+def test_label_stats_workload_full_size(ccl, config):
+    img = synth.generate(config)
+    check_label_stats(ccl, f"workload {config}", img if img.shape[0] > 1 else img[0], 8)
+
+
 @pytest.mark.parametrize("conn", [8, 4])
 def test_stats_ragged_random(ccl, conn):
     """Shapes around the 512 x 256 areas of the statistics pass and the tiles."""
