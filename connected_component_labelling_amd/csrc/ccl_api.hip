@@ -416,11 +416,10 @@ int ccl_label_stats(const void *colours, int dtype, int64_t batch, int64_t heigh
     launch_seam(L.g, w, connectivity, s);
     launch_seam_roots(L.g, w, s);
     launch_scan(L.g, w, counts, 1, 1, s);
-    launch_label_stats(L.g, w, counts, rec, stats_capacity, 0, s);  // first record of each image
-    launch_resolve(L.g, w, 1, s, rec, stats_capacity);              // opens seam regions' records
-    launch_final(L.g, w, out, 1, 0u, s);
-    launch_label_stats(L.g, w, counts, rec, stats_capacity, 1, s);  // regions inside tiles; parts
-    launch_label_stats(L.g, w, counts, rec, stats_capacity, 2, s);  // parts into the records
+    launch_label_stats(L.g, w, counts, out, rec, stats_capacity, 0, s);  // first record per image
+    launch_resolve(L.g, w, 1, s, rec, stats_capacity);  // opens seam regions' records
+    launch_label_stats(L.g, w, counts, out, rec, stats_capacity, 1, s);  // numbers, records, parts
+    launch_label_stats(L.g, w, counts, out, rec, stats_capacity, 2, s);  // parts into the records
     return finish_launches();
 }
 

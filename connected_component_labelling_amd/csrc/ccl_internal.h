@@ -174,10 +174,10 @@ static_assert(sizeof(RegionRec) == 40, "40-byte region records");
 void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geom &g,
                          const Work &w, int64_t n_total, RegionRec *recs, hipStream_t s);
 // statistics of the labelling call: stage 0 the first record of each image
-// (into the band-status words, after the scan), stage 1 the records pass
-// (after the final write), stage 2 the reduce pass
-void launch_label_stats(const Geom &g, const Work &w, const int32_t *counts, RegionRec *rec,
-                        int64_t cap, int stage, hipStream_t s);
+// (into the band-status words, after the scan), stage 1 the final write with
+// statistics (numbers into out), stage 2 the reduce pass
+void launch_label_stats(const Geom &g, const Work &w, const int32_t *counts, int32_t *out,
+                        RegionRec *rec, int64_t cap, int stage, hipStream_t s);
 void launch_zero_i32(int32_t *p, int64_t n, hipStream_t s);
 
 }  // namespace ccl

@@ -189,6 +189,16 @@ __device__ __forceinline__ uint64_t *node_rec(const Work &w, uint32_t node)
     return slot == UNI_SLOT ? &w.hdr[t].rec : w.gp + (size_t)t * KMAX + slot;
 }
 
+// A seam node's region lies in its tile alone when no union ever touched the
+// node: it is still a root (its record names itself) and no other node has it
+// as root (bit 63 of a root's record, set by those nodes in the resolve pass
+// of the statistics; a key takes 31 bits).
+constexpr uint64_t REC_SHARED = 1ull << 63;
+__device__ __forceinline__ bool lone_node(uint64_t rec, uint32_t node)
+{
+    return (uint32_t)rec == node && !(rec & REC_SHARED);
+}
+
 __device__ __forceinline__ uint64_t g_load(const uint64_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1720,7 +1730,7 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
         const uint32_t node = (t << 8) | (sUni[j] ? UNI_SLOT : select_bit(u, i - sOff[j]));
         uint64_t rrec;
         const uint32_t root = g_root(w, node, rrec);
-        const uint32_t key = (uint32_t)(rrec >> 32);
+        const uint32_t key = (uint32_t)(rrec >> 32) & 0x7FFFFFFFu;  // (without REC_SHARED)
         uint32_t val = key;
         if (number) {
             uint32_t tl, row, col;
@@ -1737,12 +1747,296 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
             w.hdr[t].value = val;  // a one-colour tile's only node
         else
             w.nval[(size_t)t * KMAX + (node & 0xFFu)] = val;
-        // statistics: each region that crosses a tile edge has one root
-        // node, which opens its record (the tiles' parts are added later)
-        if (so.rec != nullptr && root == node) {
-            const int64_t idx = so.off[fast_div(t, g.divTpi)] + (int64_t)val - 1;
-            if (idx < so.cap) stats_empty(&so.rec[idx]);
+        // statistics: each region with a seam node has one root node, which
+        // opens its record (the tiles' parts are added later); the other nodes
+        // mark the root's record as shared.  Every such store writes the same
+        // value, and the walks of other nodes only read the root's id and key
+        // from it, so they may run side by side.
+        if (so.rec != nullptr) {
+            if (root == node) {
+                const int64_t idx = so.off[fast_div(t, g.divTpi)] + (int64_t)val - 1;
+                if ((uint64_t)idx < (uint64_t)so.cap) stats_empty(&so.rec[idx]);
+            } else if (!(rrec & REC_SHARED)) {
+                *node_rec(w, root) = rrec | REC_SHARED;
+            }
         }
+    }
+}
+
+// ------------------------------------------- statistics in the final write
+// With statistics (ccl_label_stats), the final write also gathers each
+// region's area, bounding box and sums of row and column indices from the
+// run records it expands (see the statistics section below for the steps).
+
+constexpr int SR_CAP = 128;  // regions inside one tile gathered per pass over its runs
+
+// a region's part in one tile, packed: area (11 bits: at most 2047 pixels in a
+// tile of several colours), sums of local rows (15: at most 31744) and local
+// columns (16: at most 64512), then rows y0, y1 (5 each), columns x0, x1 (6
+// each).  The three sums alone (the low 42 bits) add without carries between
+// them, so parts are gathered with one 64-bit add.
+__device__ __forceinline__ uint64_t pack_part(uint64_t sums, uint32_t rows, uint64_t cols)
+{
+    const uint32_t y0 = (uint32_t)__builtin_ctz(rows), y1 = 31u - (uint32_t)__builtin_clz(rows);
+    const uint32_t x0 = (uint32_t)__builtin_ctzll(cols), x1 = 63u - (uint32_t)__builtin_clzll(cols);
+    return sums | ((uint64_t)y0 << 42) | ((uint64_t)y1 << 47) | ((uint64_t)x0 << 52) |
+           ((uint64_t)x1 << 58);
+}
+
+// a one-colour tile's whole record (its region lies in this tile alone)
+__device__ __forceinline__ void tile_record(RegionRec *r, const TilePos &tp)
+{
+    const int64_t vh = tp.vh, vw = tp.vw, y0 = tp.y0, x0 = tp.x0;
+    uint64_t *q = (uint64_t *)r;
+    q[0] = (uint64_t)(vw * (vh * y0 + vh * (vh - 1) / 2));
+    q[1] = (uint64_t)(vh * (vw * x0 + vw * (vw - 1) / 2));
+    q[2] = (uint64_t)(uint32_t)(vh * vw) | ((uint64_t)(uint32_t)y0 << 32);
+    q[3] = (uint64_t)(uint32_t)x0 | ((uint64_t)(uint32_t)(y0 + vh - 1) << 32);
+    q[4] = (uint64_t)(uint32_t)(x0 + vw - 1);
+}
+
+// the whole record of a region that lies in one tile, from its packed part
+// (local sums and box) and the tile's position
+__device__ __forceinline__ void part_record(RegionRec *r, uint64_t pk, const TilePos &tp)
+{
+    const uint64_t a = pk & 0x7FFu;
+    uint64_t *q = (uint64_t *)r;
+    q[0] = ((pk >> 11) & 0x7FFFu) + a * tp.y0;
+    q[1] = ((pk >> 26) & 0xFFFFu) + a * tp.x0;
+    q[2] = a | ((uint64_t)(tp.y0 + (uint32_t)((pk >> 42) & 31u)) << 32);
+    q[3] = (uint64_t)(tp.x0 + (uint32_t)((pk >> 52) & 63u)) |
+           ((uint64_t)(tp.y0 + (uint32_t)((pk >> 47) & 31u)) << 32);
+    q[4] = (uint64_t)(tp.x0 + (uint32_t)(pk >> 58));
+}
+
+// the r-th set bit (from 0) of m, r < popcount(m): a binary search on
+// popcounts, without branches
+__device__ __forceinline__ uint32_t select_bit64_bs(uint64_t m, uint32_t r)
+{
+    const uint32_t lo = (uint32_t)m, c32 = (uint32_t)__builtin_popcount(lo);
+    const bool up = r >= c32;
+    uint32_t x = up ? (uint32_t)(m >> 32) : lo;
+    uint32_t pos = up ? 32u : 0u;
+    r -= up ? c32 : 0u;
+#pragma unroll
+    for (int half = 16; half >= 1; half >>= 1) {
+        const uint32_t c = (uint32_t)__builtin_popcount(x & ((1u << half) - 1u));
+        const bool hi = r >= c;
+        x = hi ? x >> half : x;
+        pos += hi ? (uint32_t)half : 0u;
+        r -= hi ? c : 0u;
+    }
+    return pos;
+}
+
+// run r of a tile: its row, first and last column.  rex_y (wave-uniform) is
+// the number of runs before row y; lane y of mlo / mhi / rexv holds row y's
+// run starts and run count before it.
+struct RunPos {
+    uint32_t y, x, e;
+};
+
+__device__ __forceinline__ RunPos run_pos(uint32_t r, const uint32_t (&rex)[TH], int vh, int vw,
+                                          uint32_t mlo, uint32_t mhi, uint32_t rexv)
+{
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int y = 1; y < TH; ++y) cnt += (y < vh && rex[y] <= r) ? 1u : 0u;
+    const int src = (int)cnt << 2;
+    const uint64_t m = ((uint64_t)(uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mhi) << 32) |
+                       (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)mlo);
+    const uint32_t k = r - (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)rexv);
+    const uint32_t x = select_bit64_bs(m, k);
+    const uint64_t above = (m >> x) >> 1;
+    const uint32_t e = above ? x + (uint32_t)__builtin_ctzll(above) : (uint32_t)vw - 1u;
+    return {cnt, x, e};
+}
+// one wave's statistics tables in the final write (they take the place of
+// its label staging once the tile's rows are written)
+struct FwTabs {
+    union {
+        // first pass: parts of the regions on the tile's edges, by seam slot
+        struct {
+            unsigned long long sum[KMAX], col[KMAX];
+            uint32_t row[KMAX];
+        } b;
+        // then the regions inside the tile, by rank among the tile's inner
+        // roots (reading order) minus the pass's first rank, and numbers
+        struct {
+            unsigned long long sum[SR_CAP], col[SR_CAP];
+            uint32_t row[SR_CAP], num[SR_CAP];
+        } in;
+    } u;
+    unsigned long long ir[TH];  // inner roots' start columns in each row
+    uint32_t irpre[TH];         // inner roots in the rows before
+};
+
+// one wave's LDS in the final write
+struct FwRows {  // while the rows are written: the labels of the first DLAB
+                 // runs, the seam nodes' values (+ IGN_SLOT: the ignored value)
+    uint32_t lab[DLAB];
+    uint32_t node[KMAX + 1];
+};
+template <bool STATS> struct FwWave {
+    union {
+        FwRows rows;
+        FwTabs tabs;  // then the statistics
+    } u;
+    uint64_t lead[TH];   // leaders of each row segment
+    uint32_t pre[TH];    // leaders of the image before each row segment
+    uint16_t pos[DLAB];  // start of each of the first DLAB runs: row << 6 | column
+};
+template <> struct FwWave<false> {
+    union {
+        FwRows rows;
+    } u;
+    uint64_t lead[TH];
+    uint32_t pre[TH];
+};
+
+// a run's packed sums (as a part): area, sum of rows, sum of columns
+__device__ __forceinline__ unsigned long long run_sums(uint32_t y, uint32_t x, uint32_t e)
+{
+    const uint32_t len = e - x + 1u;
+    return (unsigned long long)len | ((unsigned long long)(len * y) << 11) |
+           ((unsigned long long)(len * x + len * (len - 1u) / 2u) << 26);
+}
+// the columns x .. e of a row, as a mask
+__device__ __forceinline__ unsigned long long run_cols(uint32_t x, uint32_t e)
+{
+    return (~0ull >> (63u - e)) & (~0ull << x);
+}
+
+// The statistics of a tile of several colours, once its labels are written:
+// its run starts are in pos (the first DLAB runs), the words of its run
+// records in info[] (two per word, as the final write loads them), the values
+// and records of its seam nodes in nv[] and nrec[] (slot lane + 64k), the
+// leaders of its row segments in lead[] / pre[].
+//   First pass over the runs: each run of a region on the tile's edges adds
+//   to its seam slot's part, and the inner roots (runs whose record names
+//   themselves) are marked.  The parts then go to their seam nodes' record
+//   slots (free once resolve has run) for the reduce pass, or, for a region
+//   on the edges whose seam node no union touched, into its record, whole.
+//   Then one pass per SR_CAP regions inside the tile: their records, whole.
+__device__ __forceinline__ void fw_stats_mixed(const Geom &g, const Work &w, const StatsOut &so,
+                                               uint32_t t, const TilePos &tp, uint32_t R,
+                                               uint32_t mlo, uint32_t mhi, uint32_t rexv,
+                                               const uint32_t (&info)[DLAB / 128],
+                                               const uint32_t (&nv)[KMAX / 64],
+                                               const uint64_t (&nrec)[KMAX / 64],
+                                               const uint64_t *lead, const uint32_t *pre,
+                                               const uint16_t *pos, FwTabs &L, int lane)
+{
+    const int vh = tp.vh, vw = tp.vw;
+    const int64_t off = so.off[tp.b];
+    const uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
+    for (int i = lane; i < KMAX; i += 64) {
+        L.u.b.sum[i] = L.u.b.col[i] = 0ull;
+        L.u.b.row[i] = 0u;
+    }
+    if (lane < TH) L.ir[lane] = 0ull;
+    __syncwarp();
+    // run base + lane (base a multiple of 64; every lane takes part): its
+    // record, row, first and last column
+    auto run_at = [&](uint32_t base, uint32_t &rec, uint32_t &y, uint32_t &x, uint32_t &e) {
+        const uint32_t r = base + (uint32_t)lane;
+        const uint32_t rc = r < R ? r : R - 1u;
+        if (base < (uint32_t)DLAB) {
+            const uint32_t b = base >> 6;  // wave-uniform
+            const uint32_t word = b < 2 ? info[0] : b < 4 ? info[1] : b < 6 ? info[2] : info[3];
+            const int src = (int)((((b & 1u) << 5) + ((uint32_t)lane >> 1)) << 2);
+            const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)word);
+            rec = (lane & 1) ? v >> 16 : v & 0xFFFFu;
+            const uint32_t p = pos[rc];
+            y = p >> 6;
+            x = p & 63u;
+            const int sy = (int)(y << 2);
+            const uint64_t m = ((uint64_t)(uint32_t)__builtin_amdgcn_ds_bpermute(sy, (int)mhi) << 32) |
+                               (uint32_t)__builtin_amdgcn_ds_bpermute(sy, (int)mlo);
+            const uint64_t above = (m >> x) >> 1;
+            e = above ? x + (uint32_t)__builtin_ctzll(above) : (uint32_t)vw - 1u;
+        } else {
+            // past the staged runs: decode here
+            uint32_t rex[TH];
+#pragma unroll
+            for (int yy = 0; yy < TH; ++yy) rex[yy] = __builtin_amdgcn_readlane(rexv, yy);
+            const RunPos p = run_pos(rc, rex, vh, vw, mlo, mhi, rexv);
+            rec = rinfo[rc];
+            y = p.y;
+            x = p.x;
+            e = p.e;
+        }
+    };
+    static_assert(DLAB == 512, "four words of run records per lane");
+
+    for (uint32_t base = 0; base < R; base += 64) {
+        uint32_t rec, y, x, e;
+        run_at(base, rec, y, x, e);
+        if (base + (uint32_t)lane >= R || rec == INFO_IGNORED) continue;
+        if (rec & INFO_BORDER) {
+            const uint32_t sl_ = rec & 0xFFu;
+            atomicAdd(&L.u.b.sum[sl_], run_sums(y, x, e));
+            atomicOr(&L.u.b.row[sl_], 1u << y);
+            atomicOr(&L.u.b.col[sl_], run_cols(x, e));
+        } else if (rec == ((y << 6) | x)) {
+            atomicOr(&L.ir[y], 1ull << x);
+        }
+    }
+    __syncwarp();
+#pragma unroll
+    for (int k = 0; k < KMAX / 64; ++k) {
+        const int i = lane + 64 * k;
+        const unsigned long long sum = L.u.b.sum[i];
+        if (sum == 0ull) continue;
+        const uint64_t pk = pack_part(sum, L.u.b.row[i], L.u.b.col[i]);
+        uint64_t *slot = w.gp + (size_t)t * KMAX + i;
+        if (lone_node(nrec[k], (t << 8) | (uint32_t)i)) {
+            const int64_t idx = off + (int64_t)nv[k] - 1;
+            if ((uint64_t)idx < (uint64_t)so.cap) part_record(&so.rec[idx], pk, tp);
+            *slot = 0ull;  // nothing left for the reduce pass
+        } else {
+            *slot = pk;
+        }
+    }
+    // inner roots in the rows before each row
+    const uint32_t nr = lane < TH ? popc64(L.ir[lane]) : 0u;
+    uint32_t ninc = nr;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t v = __shfl_up(ninc, d);
+        if (lane >= d) ninc += v;
+    }
+    if (lane < TH) L.irpre[lane] = ninc - nr;
+    const uint32_t ni = __builtin_amdgcn_readlane(ninc, TH - 1);
+    __syncwarp();  // (the edge tables are free: the inner tables take their place)
+
+    for (uint32_t p0 = 0; p0 < ni; p0 += SR_CAP) {
+        const uint32_t nin = ni - p0 < (uint32_t)SR_CAP ? ni - p0 : (uint32_t)SR_CAP;
+        for (uint32_t i = lane; i < nin; i += 64) {
+            L.u.in.sum[i] = L.u.in.col[i] = 0ull;
+            L.u.in.row[i] = 0u;
+        }
+        __syncwarp();
+        for (uint32_t base = 0; base < R; base += 64) {
+            uint32_t rec, y, x, e;
+            run_at(base, rec, y, x, e);
+            if (base + (uint32_t)lane >= R || (rec & INFO_BORDER)) continue;  // (ignored too)
+            const uint32_t ry = rec >> 6, rc = rec & 63u;
+            const uint32_t rank = L.irpre[ry] + popc64(L.ir[ry] & mask_lt((int)rc));
+            if (rank < p0 || rank >= p0 + nin) continue;
+            const uint32_t k = rank - p0;
+            if (ry == y && rc == x) L.u.in.num[k] = 1u + pre[ry] + popc64(lead[ry] & mask_lt((int)rc));
+            atomicAdd(&L.u.in.sum[k], run_sums(y, x, e));
+            atomicOr(&L.u.in.row[k], 1u << y);
+            atomicOr(&L.u.in.col[k], run_cols(x, e));
+        }
+        __syncwarp();
+        for (uint32_t i = lane; i < nin; i += 64) {
+            const int64_t idx = off + (int64_t)L.u.in.num[i] - 1;
+            if ((uint64_t)idx < (uint64_t)so.cap)
+                part_record(&so.rec[idx], pack_part(L.u.in.sum[i], L.u.in.row[i], L.u.in.col[i]), tp);
+        }
+        __syncwarp();
     }
 }
 
@@ -1767,10 +2061,13 @@ __device__ __forceinline__ void store_label(int32_t *p, int32_t v)
 // labels of the tile's rows y = lane/16, +4, ...: lane covers columns
 // 4*(lane%16) .. +3.  rowmask/rowex: lane y holds row y's run starts and the
 // runs before row y.
+// With pos, the starts of the first DLAB runs (row << 6 | column) are written
+// there too.
 template <bool ALL_STAGED, typename L>
 __device__ __forceinline__ void write_rows_x4(int32_t *o0, int64_t W, int vh, int lane,
                                               uint32_t mlo, uint32_t mhi, uint32_t rex,
-                                              const uint32_t *lab, L run_label_slow)
+                                              const uint32_t *lab, L run_label_slow,
+                                              uint16_t *pos = nullptr)
 {
     const int c4 = 4 * (lane & 15);
     for (int yb = 0; yb < vh; yb += 4) {  // the same trip count for every lane
@@ -1782,6 +2079,13 @@ __device__ __forceinline__ void write_rows_x4(int32_t *o0, int64_t W, int vh, in
         const uint32_t bits = (uint32_t)(m >> c4) & 15u;
         const uint32_t r0 = rb + popc64(m & mask_le(c4)) - 1u;
         const uint32_t r1 = r0 + ((bits >> 1) & 1u), r2 = r1 + ((bits >> 2) & 1u), r3 = r2 + (bits >> 3);
+        if (pos != nullptr) {
+            const uint16_t p0 = (uint16_t)(((uint32_t)y << 6) | (uint32_t)c4);
+            if ((bits & 1u) && r0 < (uint32_t)DLAB) pos[r0] = p0;
+            if ((bits & 2u) && r1 < (uint32_t)DLAB) pos[r1] = (uint16_t)(p0 + 1);
+            if ((bits & 4u) && r2 < (uint32_t)DLAB) pos[r2] = (uint16_t)(p0 + 2);
+            if ((bits & 8u) && r3 < (uint32_t)DLAB) pos[r3] = (uint16_t)(p0 + 3);
+        }
         int4 v;
         if (ALL_STAGED) {
             v = make_int4((int)lab[r0], (int)lab[r1], (int)lab[r2], (int)lab[r3]);
@@ -1795,14 +2099,13 @@ __device__ __forceinline__ void write_rows_x4(int32_t *o0, int64_t W, int vh, in
     }
 }
 
+// STATS: also the statistics of ccl_label_stats (numbers only)
+template <bool STATS>
 __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int32_t *out,
                                                             int number, uint32_t ignv,
-                                                            uint32_t t0, uint32_t t1)
+                                                            uint32_t t0, uint32_t t1, StatsOut so)
 {
-    __shared__ uint32_t sLab[NWAVES][DLAB];
-    __shared__ uint32_t sNode[NWAVES][KMAX + 1];  // + IGN_SLOT: the ignored pixels' value
-    __shared__ uint64_t sLead[NWAVES][TH];
-    __shared__ uint32_t sPre[NWAVES][TH];
+    __shared__ FwWave<STATS> sW[NWAVES];
 
     const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t t = t0 + remap_tile(blockIdx.x, gridDim.x) * NWAVES + wave;
@@ -1831,15 +2134,25 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         } else if (lane_ok) {
             for (int y = 0; y < tp.vh; ++y) store_label(o0 + y * W + lane, (int32_t)v);
         }
+        if constexpr (STATS) {
+            // the record of a region that is this tile alone: the whole image,
+            // or a seam node no union touched
+            if (lane == 0 && !(uv.x & KIND_IGNORED) &&
+                (!seam || lone_node(h.rec, (t << 8) | UNI_SLOT))) {
+                const int64_t idx = so.off[tp.b] + (int64_t)v - 1;
+                if ((uint64_t)idx < (uint64_t)so.cap) tile_record(&so.rec[idx], tp);
+            }
+        }
         return;
     }
 
     const uint32_t R = uv.y;                 // a tile of several colours: its runs
     const uint32_t nslots = (uv.x >> 8) & 0xFFu;  // 1 + its highest seam slot in use
-    uint32_t *lab = sLab[wave];
-    uint32_t *nodev = sNode[wave];
-    uint64_t *lead = sLead[wave];
-    uint32_t *pre = sPre[wave];
+    FwWave<STATS> &lw = sW[wave];
+    uint32_t *lab = lw.u.rows.lab;
+    uint32_t *nodev = lw.u.rows.node;
+    uint64_t *lead = lw.lead;
+    uint32_t *pre = lw.pre;
     // every record of the tile is requested before any is used, so that their
     // latencies overlap
     const uint64_t mk = lane < TH ? w.runmask[t32 + lane] : 0ull;
@@ -1867,6 +2180,12 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
 #pragma unroll
     for (int j = 0; j < DLAB / 128; ++j)
         info[j] = __builtin_amdgcn_raw_buffer_load_b32(rr, ((uint32_t)lane + 64u * (uint32_t)j) * 4u, 0, 0);
+    uint64_t nrec[KMAX / 64];  // with statistics: the seam nodes' records
+#pragma unroll
+    for (int k = 0; k < KMAX / 64; ++k) {
+        const uint32_t i = (uint32_t)(lane + 64 * k);
+        nrec[k] = (STATS && i < nslots) ? w.gp[(size_t)t * KMAX + i] : 0ull;
+    }
     if (number && lane < TH) {
         lead[lane] = ld;
         pre[lane] = pr;
@@ -1901,21 +2220,31 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     const uint32_t rex = inc - cnt;
     const uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
     auto slow = [&](uint32_t run) -> uint32_t { return run_label(rinfo[run]); };
+    uint16_t *pos = nullptr;  // with statistics: the run starts
+    if constexpr (STATS) pos = lw.pos;
     if (x4) {
         if (R <= DLAB)
-            write_rows_x4<true>(o0, W, tp.vh, lane, mlo, mhi, rex, lab, slow);
+            write_rows_x4<true>(o0, W, tp.vh, lane, mlo, mhi, rex, lab, slow, pos);
         else
-            write_rows_x4<false>(o0, W, tp.vh, lane, mlo, mhi, rex, lab, slow);
-        return;
-    }
-    for (int y = 0; y < tp.vh; ++y) {
-        const uint64_t m = ((uint64_t)__builtin_amdgcn_readlane(mhi, y) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane(mlo, y);
-        const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
-        if (lane_ok) {
-            const uint32_t run = rb + mbcnt(m) + (uint32_t)((m >> lane) & 1ull) - 1u;
-            store_label(o0 + y * W + lane, (int32_t)(run < DLAB ? lab[run] : run_label(rinfo[run])));
+            write_rows_x4<false>(o0, W, tp.vh, lane, mlo, mhi, rex, lab, slow, pos);
+    } else {
+        for (int y = 0; y < tp.vh; ++y) {
+            const uint64_t m = ((uint64_t)__builtin_amdgcn_readlane(mhi, y) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane(mlo, y);
+            const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
+            if (lane_ok) {
+                const uint32_t start = (uint32_t)((m >> lane) & 1ull);
+                const uint32_t run = rb + mbcnt(m) + start - 1u;
+                store_label(o0 + y * W + lane, (int32_t)(run < DLAB ? lab[run] : run_label(rinfo[run])));
+                if (STATS && start && run < (uint32_t)DLAB)
+                    pos[run] = (uint16_t)(((uint32_t)y << 6) | (uint32_t)lane);
+            }
         }
+    }
+    if constexpr (STATS) {
+        __syncwarp();  // (the label staging is done with: the tables take its place)
+        fw_stats_mixed(g, w, so, t, tp, R, mlo, mhi, rex, info, nv, nrec, lead, pre, pos, lw.u.tabs,
+                       lane);
     }
 }
 
@@ -2254,18 +2583,19 @@ __global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t 
 // ------------------------------------ statistics in the labelling call
 // ccl_label_stats computes the records of ccl_region_stats inside the
 // labelling call, from the run records the final write expands (row masks and
-// per-run records: about 0.4 B/px), not from the labels.  Three steps:
-//   - resolve opens the record of every region that crosses a tile edge (its
-//     root seam node does, once);
-//   - stats_records_kernel, one wave per tile of several colours: a region
-//     inside the tile is complete there, its record is written whole; the
-//     part of a region on the tile's edges is packed into 64 bits in its seam
-//     node's record slot (free once resolve has run);
-//   - stats_reduce_kernel, one workgroup per block of 8x8 tiles: the parts of
-//     the block's seam nodes (and of its one-colour tiles, in closed form) are
-//     gathered per region in an LDS table and added to the records with
-//     global atomics, so a region covering the picture takes one set of
-//     atomics per block.
+// per-run records, already in hand there), not from the labels.  Three steps:
+//   - resolve opens the record of every region with a seam node (its root
+//     node does, once), and marks each root that other nodes reach;
+//   - the final write with statistics, per tile: a region inside a tile of
+//     several colours is complete there and gets its record whole, and so
+//     does a region on the tile's edges whose seam node no union touched (a
+//     one-colour tile too); the part of any other region is packed into 64
+//     bits in its seam node's record slot (free once resolve has run);
+//   - stats_reduce_kernel, one workgroup per group of 16 x 16 tiles: the
+//     parts of the group's seam nodes (and of its one-colour tiles, in closed
+//     form) are gathered per region in an LDS table and added to the records
+//     with global atomics, so a region covering the picture takes one set of
+//     atomics per group.
 
 // first record of each image: exclusive prefix of the per-image region counts
 __global__ __launch_bounds__(BLOCK) void image_offsets_kernel(const int32_t *counts, int64_t B,
@@ -2286,187 +2616,6 @@ __global__ __launch_bounds__(BLOCK) void image_offsets_kernel(const int32_t *cou
     }
 }
 
-constexpr int SR_CAP = 128;  // regions inside one tile gathered per pass over its rows
-
-struct SrLds {  // one wave's tables
-    // regions inside the tile, by their rank among the tile's inner roots
-    // (reading order) minus the pass's first rank
-    uint32_t ia[SR_CAP];    // area | sum of local rows << 11
-    uint32_t isx[SR_CAP];   // sum of local columns
-    uint32_t ix0[SR_CAP], ix1[SR_CAP], iy1[SR_CAP];
-    uint32_t ipos[SR_CAP];  // root run: row << 6 | column
-    // parts of regions on the tile's edges, by seam slot
-    uint32_t ba[KMAX], bsx[KMAX], by0[KMAX], bx0[KMAX], by1[KMAX], bx1[KMAX];
-    uint64_t ir[TH];        // inner roots' start columns in each row
-    uint32_t irpre[TH];     // inner roots in the rows before
-    uint64_t lead[TH];      // leaders of each row segment
-    uint32_t pre[TH];       // leaders of the image before each row segment
-    uint16_t info[DLAB];    // the tile's first run records
-};
-
-// a region's part in one tile, packed: area (11 bits: at most 2047 pixels in a
-// tile of several colours), sums of local rows (15: at most 31744) and local
-// columns (16: at most 64512), rows y0, y1 (5 each), columns x0, x1 (6 each)
-__device__ __forceinline__ uint64_t pack_part(uint32_t a, uint32_t sy, uint32_t sx, uint32_t y0,
-                                              uint32_t y1, uint32_t x0, uint32_t x1)
-{
-    return (uint64_t)a | ((uint64_t)sy << 11) | ((uint64_t)sx << 26) | ((uint64_t)y0 << 42) |
-           ((uint64_t)y1 << 47) | ((uint64_t)x0 << 52) | ((uint64_t)x1 << 58);
-}
-
-// a one-colour tile's whole record (its region lies in this tile alone)
-__device__ __forceinline__ void tile_record(RegionRec *r, const TilePos &tp)
-{
-    const int64_t vh = tp.vh, vw = tp.vw, y0 = tp.y0, x0 = tp.x0;
-    uint64_t *q = (uint64_t *)r;
-    q[0] = (uint64_t)(vw * (vh * y0 + vh * (vh - 1) / 2));
-    q[1] = (uint64_t)(vh * (vw * x0 + vw * (vw - 1) / 2));
-    q[2] = (uint64_t)(uint32_t)(vh * vw) | ((uint64_t)(uint32_t)y0 << 32);
-    q[3] = (uint64_t)(uint32_t)x0 | ((uint64_t)(uint32_t)(y0 + vh - 1) << 32);
-    q[4] = (uint64_t)(uint32_t)(x0 + vw - 1);
-}
-
-__global__ __launch_bounds__(BLOCK) void stats_records_kernel(Geom g, Work w, StatsOut so)
-{
-    __shared__ SrLds sl[NWAVES];
-    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t t = remap_tile(blockIdx.x, gridDim.x) * NWAVES + wave;
-    if (t >= (uint32_t)g.ntiles) return;
-    const TilePos tp = tile_pos(t, g);
-    const TileHdr &h = w.hdr[t];
-    const uint32_t kind = h.kind;
-    const int64_t off = so.off[tp.b];
-    if (kind & KIND_UNIFORM) {
-        // one colour: with an open edge its part is added by the reduce pass;
-        // with none the tile is the whole image and its region ends here
-        if (((kind >> 8) & 0xFFu) != 255u || (kind & KIND_IGNORED)) return;
-        const int64_t idx = off + (int64_t)h.pre;  // number 1 + pre, record number - 1
-        if (lane == 0 && idx < so.cap) tile_record(&so.rec[idx], tp);
-        return;
-    }
-    SrLds &L = sl[wave];
-    const int vh = tp.vh, vw = tp.vw;
-    const uint32_t R = h.value;  // runs
-    const size_t t32 = (size_t)t * TH;
-    const uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
-    // lane y: row y's run starts, leaders and leaders before it (for numbers)
-    const uint64_t mk = lane < TH ? w.runmask[t32 + lane] : 0ull;
-    const uint64_t ld = lane < TH ? w.leadmask[t32 + lane] : 0ull;
-    const uint32_t pr = lane < TH ? w.seg[t32 + lane] : 0u;
-    const uint32_t nl = R < DLAB ? R : DLAB;
-    for (uint32_t r = lane; r < nl; r += 64) L.info[r] = rinfo[r];
-    if (lane < TH) {
-        L.lead[lane] = ld;
-        L.pre[lane] = pr;
-    }
-    for (int i = lane; i < KMAX; i += 64) {
-        L.ba[i] = L.bsx[i] = L.by1[i] = L.bx1[i] = 0u;
-        L.by0[i] = L.bx0[i] = 0xFFFFFFFFu;
-    }
-    // runs before each row (lane y holds row y's)
-    const uint32_t cnt = popc64(mk);
-    uint32_t inc = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t v = __shfl_up(inc, d);
-        if (lane >= d) inc += v;
-    }
-    const uint32_t rex = inc - cnt;
-    const uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
-    __syncwarp();
-    auto info_of = [&](uint32_t r) -> uint32_t { return r < DLAB ? L.info[r] : rinfo[r]; };
-
-    // inner roots of each row: a start lane whose run record names itself
-    uint32_t ni = 0;  // inner roots so far
-    for (int y = 0; y < vh; ++y) {
-        const uint64_t m = ((uint64_t)__builtin_amdgcn_readlane(mhi, y) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane(mlo, y);
-        const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
-        bool root = false;
-        if (lane_bit(m)) {
-            const uint32_t info = info_of(rb + mbcnt(m));
-            root = !(info & INFO_BORDER) && info == (((uint32_t)y << 6) | (uint32_t)lane);
-        }
-        const uint64_t irm = __ballot(root);
-        if (lane == 0) {
-            L.ir[y] = irm;
-            L.irpre[y] = ni;
-        }
-        ni += popc64(irm);
-    }
-    __syncwarp();
-
-    // passes over the rows: pass p gathers the inner regions of rank
-    // [p*SR_CAP, (p+1)*SR_CAP), pass 0 also the edge regions' parts
-    for (uint32_t p0 = 0; p0 == 0 || p0 < ni; p0 += SR_CAP) {
-        const uint32_t nin = ni - p0 < (uint32_t)SR_CAP ? ni - p0 : (uint32_t)SR_CAP;
-        for (uint32_t i = lane; i < nin; i += 64) {
-            L.ia[i] = L.isx[i] = L.ix1[i] = L.iy1[i] = 0u;
-            L.ix0[i] = 0xFFFFFFFFu;
-        }
-        __syncwarp();
-        for (int y = 0; y < vh; ++y) {
-            const uint64_t m = ((uint64_t)__builtin_amdgcn_readlane(mhi, y) << 32) |
-                               (uint32_t)__builtin_amdgcn_readlane(mlo, y);
-            const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
-            if (!lane_bit(m)) continue;
-            const uint32_t info = info_of(rb + mbcnt(m));
-            if (info == INFO_IGNORED) continue;
-            // the run: row y, columns lane .. e
-            const uint64_t above = (m >> lane) >> 1;
-            const uint32_t e = above ? (uint32_t)lane + (uint32_t)__builtin_ctzll(above)
-                                     : (uint32_t)vw - 1u;
-            const uint32_t len = e - (uint32_t)lane + 1u;
-            const uint32_t ay = len | ((len * (uint32_t)y) << 11);
-            const uint32_t sx = len * (uint32_t)lane + len * (len - 1u) / 2u;
-            if (info & INFO_BORDER) {
-                if (p0 != 0) continue;
-                const uint32_t sl_ = info & 0xFFu;
-                atomicAdd(&L.ba[sl_], ay);
-                atomicAdd(&L.bsx[sl_], sx);
-                atomicMin(&L.by0[sl_], (uint32_t)y);
-                atomicMax(&L.by1[sl_], (uint32_t)y);
-                atomicMin(&L.bx0[sl_], (uint32_t)lane);
-                atomicMax(&L.bx1[sl_], e);
-            } else {
-                const uint32_t ry = info >> 6, rc = info & 63u;
-                const uint32_t rank = L.irpre[ry] + popc64(L.ir[ry] & mask_lt((int)rc));
-                if (rank < p0 || rank >= p0 + nin) continue;
-                const uint32_t k = rank - p0;
-                if (ry == (uint32_t)y && rc == (uint32_t)lane) L.ipos[k] = info;
-                atomicAdd(&L.ia[k], ay);
-                atomicAdd(&L.isx[k], sx);
-                atomicMin(&L.ix0[k], (uint32_t)lane);
-                atomicMax(&L.ix1[k], e);
-                atomicMax(&L.iy1[k], (uint32_t)y);
-            }
-        }
-        __syncwarp();
-        // the pass's inner regions are complete: their records, whole
-        for (uint32_t i = lane; i < nin; i += 64) {
-            const uint32_t pos = L.ipos[i];
-            const int ry = (int)(pos >> 6), rc = (int)(pos & 63u);
-            const uint32_t number = 1u + L.pre[ry] + popc64(L.lead[ry] & mask_lt(rc));
-            const int64_t idx = off + (int64_t)number - 1;
-            if (idx >= so.cap) continue;
-            const uint32_t a = L.ia[i] & 0x7FFu, sy = L.ia[i] >> 11;
-            uint64_t *q = (uint64_t *)&so.rec[idx];
-            q[0] = (uint64_t)sy + (uint64_t)a * tp.y0;
-            q[1] = (uint64_t)L.isx[i] + (uint64_t)a * tp.x0;
-            q[2] = (uint64_t)a | ((uint64_t)(tp.y0 + (uint32_t)ry) << 32);
-            q[3] = (uint64_t)(tp.x0 + L.ix0[i]) | ((uint64_t)(tp.y0 + L.iy1[i]) << 32);
-            q[4] = (uint64_t)(tp.x0 + L.ix1[i]);
-        }
-        __syncwarp();
-    }
-    // the parts of the edge regions, into their seam nodes' record slots
-    for (int i = lane; i < KMAX; i += 64) {
-        if (L.ba[i] == 0u) continue;
-        w.gp[(size_t)t * KMAX + i] = pack_part(L.ba[i] & 0x7FFu, L.ba[i] >> 11, L.bsx[i], L.by0[i],
-                                               L.by1[i], L.bx0[i], L.bx1[i]);
-    }
-}
-
 constexpr int RD_CAP = 1024;   // regions of a block gathered in LDS
 constexpr int RD_PROBES = 16;  // table slots a region tries before its part goes to the record
 
@@ -2482,19 +2631,38 @@ __device__ __forceinline__ void stats_add_global(RegionRec &r, uint32_t a, uint6
     atomicMax(&r.x1, x1);
 }
 
+// groups of 16 x 16 tiles, one tile per thread: a region spread over the
+// picture takes one set of global atomics per group
+constexpr int RG = 16;
+constexpr int RT = RG * RG;
+static_assert(RT == BLOCK, "one thread per tile of a group");
+
+__device__ __forceinline__ BlockTile group_tile(const Geom &g, uint32_t gb, int j)
+{
+    const uint32_t ngx = ((uint32_t)g.ntx + RG - 1) / RG, ngy = ((uint32_t)g.nty + RG - 1) / RG;
+    const uint32_t per = ngx * ngy;
+    const uint32_t b = gb / per, r = gb - b * per, gy = r / ngx, gx = r - gy * ngx;
+    BlockTile p;
+    p.ly = j / RG;
+    p.lx = j % RG;
+    const uint32_t ty = gy * RG + (uint32_t)p.ly, tx = gx * RG + (uint32_t)p.lx;
+    p.valid = ty < (uint32_t)g.nty && tx < (uint32_t)g.ntx;
+    p.t = b * (uint32_t)g.tpi + ty * (uint32_t)g.ntx + tx;
+    return p;
+}
+
 __global__ __launch_bounds__(BLOCK) void stats_reduce_kernel(Geom g, Work w, StatsOut so)
 {
     __shared__ uint32_t sKey[RD_CAP];  // region number, 0: free
     __shared__ unsigned long long sSY[RD_CAP], sSX[RD_CAP];
     __shared__ uint32_t sA[RD_CAP], sY0[RD_CAP], sX0[RD_CAP], sY1[RD_CAP], sX1[RD_CAP];
-    __shared__ uint64_t sUsed[BT][KMAX / 64];
-    __shared__ uint32_t sOff[BT + 1];
-    __shared__ uint8_t sUni[BT];
+    __shared__ uint64_t sUsed[RT][KMAX / 64];
+    __shared__ uint32_t sOff[RT];
+    __shared__ uint8_t sUni[RT];
     __shared__ uint32_t sWave[NWAVES];
     const int j = threadIdx.x;
-    const BlockBase bb = block_base(g);
-    const BlockTile me = block_tile(g, bb, j);
-    const int64_t off = so.off[fast_div(bb.t0, g.divTpi)];
+    const BlockTile me = group_tile(g, blockIdx.x, j);
+    const int64_t off = so.off[fast_div(group_tile(g, blockIdx.x, 0).t, g.divTpi)];
     for (int i = j; i < RD_CAP; i += BLOCK) {
         sKey[i] = 0u;
         sSY[i] = sSX[i] = 0ull;
@@ -2520,23 +2688,21 @@ __global__ __launch_bounds__(BLOCK) void stats_reduce_kernel(Geom g, Work w, Sta
             }
         }
     }
-    if (j < BT) {
 #pragma unroll
-        for (int word = 0; word < KMAX / 64; ++word) sUsed[j][word] = u[word];
-        sUni[j] = uni ? 1 : 0;
-    }
+    for (int word = 0; word < KMAX / 64; ++word) sUsed[j][word] = u[word];
+    sUni[j] = uni ? 1 : 0;
     uint32_t total;
-    const uint32_t noff = block_exclusive_scan(n, sWave, total);
-    if (j <= BT) sOff[j] = noff;  // entry BT: the total
+    sOff[j] = block_exclusive_scan(n, sWave, total);
     __syncthreads();
     for (uint32_t i = j; i < total; i += BLOCK) {
-        const uint32_t jj = item_tile<BT>(sOff, i);
-        const BlockTile bt = block_tile(g, bb, (int)jj);
+        const uint32_t jj = item_tile<RT>(sOff, i);
+        const BlockTile bt = group_tile(g, blockIdx.x, (int)jj);
         const TilePos tp = tile_pos(bt.t, g);
         uint32_t number, a;
         uint64_t sy, sx;
         int32_t y0, x0, y1, x1;
         if (sUni[jj]) {
+            if (lone_node(w.hdr[bt.t].rec, (bt.t << 8) | UNI_SLOT)) continue;  // done already
             number = w.hdr[bt.t].value;
             const int64_t vh = tp.vh, vw = tp.vw;
             a = (uint32_t)(vh * vw);
@@ -2554,6 +2720,7 @@ __global__ __launch_bounds__(BLOCK) void stats_reduce_kernel(Geom g, Work w, Sta
             number = w.nval[(size_t)bt.t * KMAX + slot];
             const uint64_t pk = w.gp[(size_t)bt.t * KMAX + slot];
             a = (uint32_t)(pk & 0x7FFu);
+            if (a == 0u) continue;  // a region on this tile's edges alone: done already
             sy = ((pk >> 11) & 0x7FFFu) + (uint64_t)a * tp.y0;
             sx = ((pk >> 26) & 0xFFFFu) + (uint64_t)a * tp.x0;
             y0 = (int32_t)(tp.y0 + ((pk >> 42) & 31u));
@@ -2575,7 +2742,7 @@ __global__ __launch_bounds__(BLOCK) void stats_reduce_kernel(Geom g, Work w, Sta
         }
         if (e < 0) {
             const int64_t idx = off + (int64_t)number - 1;
-            if (idx < so.cap) stats_add_global(so.rec[idx], a, sy, sx, y0, x0, y1, x1);
+            if ((uint64_t)idx < (uint64_t)so.cap) stats_add_global(so.rec[idx], a, sy, sx, y0, x0, y1, x1);
             continue;
         }
         atomicAdd(&sSY[e], (unsigned long long)sy);
@@ -2591,7 +2758,7 @@ __global__ __launch_bounds__(BLOCK) void stats_reduce_kernel(Geom g, Work w, Sta
         const uint32_t k = sKey[i];
         if (k == 0u) continue;
         const int64_t idx = off + (int64_t)k - 1;
-        if (idx >= so.cap) continue;
+        if ((uint64_t)idx >= (uint64_t)so.cap) continue;
         stats_add_global(so.rec[idx], sA[i], sSY[i], sSX[i], (int32_t)sY0[i], (int32_t)sX0[i],
                          (int32_t)sY1[i], (int32_t)sX1[i]);
     }
@@ -2666,8 +2833,9 @@ void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32
                   hipStream_t s, uint32_t t0, uint32_t nt)
 {
     if (nt == 0) nt = (uint32_t)g.ntiles;
-    hipLaunchKernelGGL(final_write_kernel, dim3(grid_of(nt, NWAVES)), dim3(BLOCK), 0, s, g, w,
-                       out, number, ignv, t0, t0 + nt);
+    const StatsOut none{nullptr, 0, nullptr};
+    hipLaunchKernelGGL(final_write_kernel<false>, dim3(grid_of(nt, NWAVES)), dim3(BLOCK), 0, s, g,
+                       w, out, number, ignv, t0, t0 + nt, none);
 }
 
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
@@ -2712,18 +2880,18 @@ void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geo
     hipLaunchKernelGGL(stats_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
 }
 
-void launch_label_stats(const Geom &g, const Work &w, const int32_t *counts, RegionRec *rec,
-                        int64_t cap, int stage, hipStream_t s)
+void launch_label_stats(const Geom &g, const Work &w, const int32_t *counts, int32_t *out,
+                        RegionRec *rec, int64_t cap, int stage, hipStream_t s)
 {
     const StatsOut so{rec, cap, (const int64_t *)w.bandst};
     if (stage == 0) {
         hipLaunchKernelGGL(image_offsets_kernel, dim3(1), dim3(BLOCK), 0, s, counts, g.B,
                            (int64_t *)w.bandst);
     } else if (stage == 1) {
-        hipLaunchKernelGGL(stats_records_kernel, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0, s,
-                           g, w, so);
+        hipLaunchKernelGGL(final_write_kernel<true>, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0,
+                           s, g, w, out, 1, 0u, 0u, (uint32_t)g.ntiles, so);
     } else {
-        const int64_t blocks = g.B * ((g.nty + MB - 1) / MB) * ((g.ntx + MB - 1) / MB);
+        const int64_t blocks = g.B * ((g.nty + RG - 1) / RG) * ((g.ntx + RG - 1) / RG);
         hipLaunchKernelGGL(stats_reduce_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, g, w, so);
     }
 }
