@@ -158,6 +158,30 @@ void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s,
 // ignv: the value written for pixels of an ignored colour
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,
                   hipStream_t s, uint32_t t0 = 0, uint32_t nt = 0);
+
+// Numbers of one band of a picture cut into bands, to the picture's numbers
+// (ccl_label_large): band-local number n (1..) is merged into a region led
+// elsewhere when bit n of M is set; with r the merged numbers below n, it then
+// takes MV[r], else it becomes G + n - r.
+struct Map64 {
+    const uint64_t *M;     // bit n: number n merged (this band's words)
+    const uint32_t *Mpre;  // merged numbers in the words before each word
+    const int64_t *MV;     // the picture's number of each merged number, by rank
+    const int64_t *G;      // [band]: numbers of the picture before the band's own
+    uint32_t band;
+    int merges;            // 0: one band, its numbers are the picture's
+};
+
+// a seam region's table slot to start probing at
+__device__ __forceinline__ uint32_t seam_hash(int64_t key, uint32_t mask)
+{
+    const uint64_t k = (uint64_t)key * 0x9E3779B97F4A7C15ull;
+    return (uint32_t)(k >> 40) & mask;
+}
+
+// the final write of one band with 64-bit numbers through the map (numbers
+// mode; ignored pixels 0)
+void launch_final64(const Geom &g, const Work &w, int64_t *out, const Map64 &m, hipStream_t s);
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
                          hipStream_t s);
 void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g, const Work &w,

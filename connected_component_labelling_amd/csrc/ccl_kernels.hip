@@ -2248,6 +2248,170 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     }
 }
 
+// ------------------------------------------------ 64-bit final write
+// The final write of one band of a picture cut into bands (ccl_label_large,
+// numbers): as above, the tile's runs are labelled once (their band-local
+// numbers, through Map64, to the picture's 64-bit numbers) and expanded into
+// rows; 8-byte labels, two per 16-byte store where rows are whole and aligned,
+// 32 lanes to a row so that each store instruction covers two whole rows (with
+// four pixels per lane, each instruction leaves every other 16 bytes of its
+// rows to the next, and the non-temporal stores ran at 1.9 TB/s instead of 4.8).
+
+__device__ __forceinline__ void store2_i64(int64_t *p, int64_t a, int64_t b)
+{
+    const int4v vv = {(int)(uint32_t)a, (int)(a >> 32), (int)(uint32_t)b, (int)(b >> 32)};
+    __builtin_nontemporal_store(vv, (int4v *)p);
+}
+
+__global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, int64_t *out, Map64 m)
+{
+    __shared__ int64_t sLab[NWAVES][DLAB];
+    __shared__ uint32_t sNode[NWAVES][KMAX + 1];
+    __shared__ uint64_t sLead[NWAVES][TH];
+    __shared__ uint32_t sPre[NWAVES][TH];
+
+    const int lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t t = remap_tile(blockIdx.x, gridDim.x) * NWAVES + wave;
+    if (t >= (uint32_t)g.ntiles) return;
+    const TilePos tp = tile_pos(t, g);
+    const int64_t y0 = tp.y0, x0 = tp.x0, W = g.W;
+    const size_t t32 = (size_t)t * TH;
+    const uint16_t *rinfo = w.runinfo + (size_t)t * TPX;
+    int64_t *o0 = out + (int64_t)tp.b * g.HW + y0 * W + x0;
+    const bool lane_ok = lane < tp.vw;
+    // 16-byte stores (two labels): whole tile rows whose starts are 16-byte aligned
+    const bool x4 = tp.vw == TW && (W & 1) == 0 && ((uintptr_t)out & 15u) == 0;
+    const int64_t G = m.merges ? m.G[m.band] : 0;
+    // band-local number n to the picture's number (0: an ignored pixel), in
+    // two steps so that many can be in flight: the mask and prefix words of n,
+    // then (merged numbers only) its entry
+    struct Pend {
+        uint64_t word;
+        uint32_t pre, n;
+    };
+    auto map_load = [&](uint32_t n) -> Pend {
+        Pend q{0ull, 0u, n};
+        if (n != 0u && m.merges) {
+            q.word = m.M[n >> 6];
+            q.pre = m.Mpre[n >> 6];
+        }
+        return q;
+    };
+    auto map_done = [&](const Pend &q) -> int64_t {
+        if (q.n == 0u || !m.merges) return (int64_t)q.n;
+        const uint32_t r = q.pre + popc64(q.word & mask_lt((int)(q.n & 63u)));
+        if ((q.word >> (q.n & 63u)) & 1ull) return m.MV[r];
+        return G + (int64_t)q.n - (int64_t)r;
+    };
+    auto map = [&](uint32_t n) -> int64_t { return map_done(map_load(n)); };
+    const TileHdr &h = w.hdr[t];
+    const uint2 uv = *(const uint2 *)&h;  // kind, value
+
+    if (uv.x & KIND_UNIFORM) {
+        const bool seam = tp.ty > 0 || tp.tx > 0 || y0 + TH < g.H || x0 + TW < W;
+        uint32_t v = uv.y;
+        if (!seam) v = 1u + h.pre;
+        if (uv.x & KIND_IGNORED) v = 0u;
+        const int64_t v64 = map(v);
+        if (x4) {
+            for (int y = lane >> 5; y < tp.vh; y += 2) store2_i64(o0 + y * W + 2 * (lane & 31), v64, v64);
+        } else if (lane_ok) {
+            for (int y = 0; y < tp.vh; ++y) __builtin_nontemporal_store(v64, o0 + y * W + lane);
+        }
+        return;
+    }
+
+    const uint32_t R = uv.y;
+    const uint32_t nslots = (uv.x >> 8) & 0xFFu;
+    int64_t *lab = sLab[wave];
+    uint32_t *nodev = sNode[wave];
+    uint64_t *lead = sLead[wave];
+    uint32_t *pre = sPre[wave];
+    const uint64_t mk = lane < TH ? w.runmask[t32 + lane] : 0ull;
+    const uint64_t ld = lane < TH ? w.leadmask[t32 + lane] : 0ull;
+    const uint32_t pr = lane < TH ? w.seg[t32 + lane] : 0u;
+    uint64_t used[KMAX / 64];
+#pragma unroll
+    for (int word = 0; word < KMAX / 64; ++word) used[word] = h.used[word];
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(w.nval + (size_t)t * KMAX), (short)0, (int)(nslots * 4u), 0x00020000);
+    uint32_t nv[KMAX / 64];
+#pragma unroll
+    for (int word = 0; word < KMAX / 64; ++word)
+        nv[word] = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(word * 64 + lane) * 4u, 0, 0);
+    const uint32_t nl = R < DLAB ? R : DLAB;
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)rinfo, (short)0, (int)((nl * 2u + 3u) & ~3u), 0x00020000);
+    uint32_t info[DLAB / 128];
+#pragma unroll
+    for (int j = 0; j < DLAB / 128; ++j)
+        info[j] = __builtin_amdgcn_raw_buffer_load_b32(rr, ((uint32_t)lane + 64u * (uint32_t)j) * 4u, 0, 0);
+    if (lane < TH) {
+        lead[lane] = ld;
+        pre[lane] = pr;
+    }
+#pragma unroll
+    for (int word = 0; word < KMAX / 64; ++word)
+        if ((used[word] >> lane) & 1ull) nodev[word * 64 + lane] = nv[word];
+    if (lane == 0) nodev[IGN_SLOT] = 0u;  // runs of an ignored colour
+    __syncwarp();
+    auto run_number = [&](uint32_t inf) -> uint32_t {
+        if (inf & INFO_BORDER) return nodev[inf & 0xFFu];
+        const uint32_t row = inf >> 6, col = inf & 63u;
+        return 1u + pre[row] + popc64(lead[row] & mask_lt((int)col));
+    };
+    Pend pq[DLAB / 64];  // the lane's staged runs, all requested before any is used
+#pragma unroll
+    for (int j = 0; j < DLAB / 128; ++j) {
+        const uint32_t r = 2u * ((uint32_t)lane + 64u * (uint32_t)j);
+        pq[2 * j] = map_load(r < nl ? run_number(info[j] & 0xFFFFu) : 0u);
+        pq[2 * j + 1] = map_load(r + 1u < nl ? run_number(info[j] >> 16) : 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < DLAB / 128; ++j) {
+        const uint32_t r = 2u * ((uint32_t)lane + 64u * (uint32_t)j);
+        if (r < nl) lab[r] = map_done(pq[2 * j]);
+        if (r + 1u < nl) lab[r + 1u] = map_done(pq[2 * j + 1]);
+    }
+    __syncwarp();
+
+    const uint32_t cnt = popc64(mk);
+    uint32_t inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t v = __shfl_up(inc, d);
+        if (lane >= d) inc += v;
+    }
+    const uint32_t rex = inc - cnt;
+    const uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
+    auto label_of = [&](uint32_t run) -> int64_t {
+        return run < (uint32_t)DLAB ? lab[run] : map(run_number(rinfo[run]));
+    };
+    if (x4) {
+        const int c2 = 2 * (lane & 31);
+        for (int yb = 0; yb < tp.vh; yb += 2) {  // the same trip count for every lane
+            const int y = yb + (lane >> 5);
+            const int ys = y < tp.vh ? y : tp.vh - 1;
+            const uint64_t mm = ((uint64_t)(uint32_t)__shfl((int)mhi, ys) << 32) | (uint32_t)__shfl((int)mlo, ys);
+            const uint32_t rb = (uint32_t)__shfl((int)rex, ys);
+            if (y >= tp.vh) continue;
+            const uint32_t r0 = rb + popc64(mm & mask_le(c2)) - 1u;
+            const uint32_t r1 = r0 + (uint32_t)((mm >> (c2 + 1)) & 1ull);
+            store2_i64(o0 + y * W + c2, label_of(r0), label_of(r1));
+        }
+        return;
+    }
+    for (int y = 0; y < tp.vh; ++y) {
+        const uint64_t mm = ((uint64_t)__builtin_amdgcn_readlane(mhi, y) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane(mlo, y);
+        const uint32_t rb = __builtin_amdgcn_readlane(rex, y);
+        if (lane_ok) {
+            const uint32_t run = rb + mbcnt(mm) + (uint32_t)((mm >> lane) & 1ull) - 1u;
+            __builtin_nontemporal_store(label_of(run), o0 + y * W + lane);
+        }
+    }
+}
+
 // ------------------------------------------------ standalone number/count
 // A leader image has no tiles of its own; its row segments use the same
 // tile-major layout so that the same scan numbers them.  One wave per row
@@ -2827,6 +2991,12 @@ void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s, Reg
     const StatsOut so{rec, cap, (const int64_t *)w.bandst};
     hipLaunchKernelGGL(resolve_kernel, dim3(grid_of(g.ntiles, SEAM_TILES)), dim3(BLOCK), 0, s, g, w,
                        number, so);
+}
+
+void launch_final64(const Geom &g, const Work &w, int64_t *out, const Map64 &m, hipStream_t s)
+{
+    hipLaunchKernelGGL(final_write64_kernel, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0, s, g,
+                       w, out, m);
 }
 
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,

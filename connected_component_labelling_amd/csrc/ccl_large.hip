@@ -4,7 +4,7 @@
 // "Accountable AI starts at the pixel" lists images of more than 2^31 pixels
 // as not run (ch.11 "How we know it is right"), and shows in ch.10 what a size
 // wrapped to 32 bits does.  Here such an image is cut into bands of whole tile
-// rows, each small enough for the 32-bit tile pipeline:
+// rows, each small enough for the 32-bit tile pipeline.  Leaders:
 //
 //   1. each band is labelled on its own (leaders relative to the band) into
 //      one int32 array over the whole image;
@@ -17,12 +17,14 @@
 //      indices; a join points the larger key at the smaller, as the tile
 //      pipeline does inside a band (same page, ch.04 "Point at a leader"), so
 //      each set's root is its region's first pixel;
-//   4. (numbers or counts) a pass flags each image's leaders in one bit per
-//      pixel, with per-word and per-block counts, and a scan turns the block
-//      counts into 64-bit prefixes (ch.08 idea 5 "Number without a giant list");
-//      for numbers, each leader's own entry then takes its number as a code
-//      relative to its band;
-//   5. a final pass writes each pixel's 64-bit leader or number.
+//   4. (counts) a pass flags each image's leaders in one bit per pixel, with
+//      per-word and per-block counts, and a scan turns the block counts into
+//      64-bit prefixes (ch.08 idea 5 "Number without a giant list");
+//   5. a final pass writes each pixel's 64-bit leader.
+//
+// Numbers take another route, with no 32-bit array over the picture (see
+// "numbers" below): the bands number themselves and their seam regions are
+// joined by (band, number).
 //
 // The seams between bands are the same seams a band per GPU would have: this
 // is the one-GPU form of labelling one picture across several GPUs.
@@ -407,118 +409,44 @@ __global__ __launch_bounds__(LB) void chunk_add_kernel(int64_t *blkpre, int64_t 
     if (i < nblk) blkpre[i] += chunkpre[i / CHUNK];
 }
 
-// Leaders before pixel index G of the image (G's own bit excluded).
-__device__ __forceinline__ int64_t leaders_before(const uint64_t *mask, const uint16_t *wordin,
-                                                  const int64_t *blkpre, int64_t G)
-{
-    const uint64_t below = mask[G >> 6] & ((uint64_t(1) << (G & 63)) - 1);
-    return blkpre[G >> BLK_SHIFT] + wordin[G >> 6] + __popcll(below);
-}
-
-// Numbers through codes (when every code fits int32): leaders before each
-// band's first pixel; each seam node's root's number; then every global
-// leader's own entry becomes -(2 + nseam + r), r its rank among the global
-// leaders of its band, so that a pixel finds its number in its leader's
-// entry.  Merged seam leaders keep their tags and go through rootnum.
-__global__ __launch_bounds__(LB) void band_offset_kernel(Bands g, const uint64_t *mask,
-                                                         const uint16_t *wordin,
-                                                         const int64_t *blkpre, int64_t *bandoff)
-{
-    const int64_t b = (int64_t)blockIdx.x * LB + threadIdx.x;
-    if (b >= g.nb) return;
-    bandoff[b] = b == 0 ? 0 : leaders_before(mask, wordin, blkpre, b * g.band_px);
-}
-
-__global__ __launch_bounds__(LB) void root_number_kernel(Bands g, const int32_t *C,
-                                                         const int64_t *rootkey,
-                                                         const uint64_t *mask,
-                                                         const uint16_t *wordin,
-                                                         const int64_t *blkpre, int64_t *rootnum)
-{
-    const int64_t node = (int64_t)blockIdx.x * LB + threadIdx.x;
-    if (node >= g.nseam || C[node] != node) return;
-    rootnum[node] = 1 + leaders_before(mask, wordin, blkpre, rootkey[node]);
-}
-
-__global__ __launch_bounds__(LB) void leader_code_kernel(Bands g, const uint64_t *mask,
-                                                         const uint16_t *wordin,
-                                                         const int64_t *blkpre,
-                                                         const int64_t *bandoff, int32_t *lead)
-{
-    const int64_t stride = (int64_t)gridDim.x * LB;
-    for (int64_t w = (int64_t)blockIdx.x * LB + threadIdx.x; w < g.nwords; w += stride) {
-        uint64_t m = mask[w];
-        if (m == 0) continue;
-        const int64_t pw = w * 64;
-        // rank of the word's first leader among its band's global leaders
-        int64_t r = blkpre[w >> (BLK_SHIFT - 6)] + wordin[w] - bandoff[pw / g.band_px];
-        while (m) {
-            const int i = __builtin_ctzll(m);
-            m &= m - 1;
-            lead[pw + i] = (int32_t)(-2 - g.nseam - r);
-            ++r;
-        }
-    }
-}
-
-// Step 5: each pixel's 64-bit leader (OUT_LEADERS) or number 1..n
-// (OUT_NUMBERS); ignored pixels get -1 or 0.  A wave takes the same 16 words
-// as in the flag pass, as 4 groups of 256 pixels with 4 consecutive pixels per
-// lane (16-byte loads of the entries, 16-byte stores of the results), in
-// phases so that each phase's loads are in flight together: the pixels' own
-// entries, then their leaders' entries.  A leader's entry holds what the pixel
-// needs: a code (its number, through its band's offset), a tag (a seam node:
-// its root's key or number), or, for leaders, its own index.
+// Step 5 (leaders): each pixel's 64-bit leader; ignored pixels get -1.  A
+// wave takes the same 16 words as in the flag pass, as 4 groups of 256 pixels
+// with 4 consecutive pixels per lane (16-byte loads of the entries, 16-byte
+// stores of the results), in phases so that each phase's loads are in flight
+// together: the pixels' own entries, then their leaders' entries.  A leader's
+// entry holds what the pixel needs: a tag (a seam node: its root's key) or its
+// own index.
 typedef int v4i32 __attribute__((ext_vector_type(4)));
 typedef long long v2i64 __attribute__((ext_vector_type(2)));
 constexpr int FGRP = WPW / 4;  // groups of 256 pixels per wave
-enum { OUT_LEADERS = 0, OUT_NUMBERS = 1 };
 
-template <int MODE>
-__device__ __forceinline__ int64_t out_value(int32_t l, int32_t t, int64_t base, int64_t boff,
-                                             int32_t code0, const int64_t *rootkey,
-                                             const int64_t *rootnum, uint32_t *err)
+__device__ __forceinline__ int64_t out_leader(int32_t l, int32_t t, int64_t base,
+                                              const int64_t *rootkey)
 {
-    if (MODE == OUT_NUMBERS) {
-        if (t == -1) return 0;
-        if (t <= code0) return boff + (int64_t)(code0 - t) + 1;
-        if (t <= -2) return rootnum[-2 - t];
-        atomicOr(err, ERR_LOOP);  // every band leader is coded or tagged by now
-        return 0;
-    }
     if (l == -1) return -1;
     const int32_t tag = l <= -2 ? l : t;
     if (tag <= -2) return rootkey[-2 - tag];
     return base + l;
 }
 
-template <int MODE>
 __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
-                                                   const int64_t *rootkey, const int64_t *rootnum,
-                                                   const int64_t *bandoff, int64_t *out,
-                                                   int out16, uint32_t *err)
+                                                   const int64_t *rootkey, int64_t *out, int out16)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q = lane >> 4;  // the lane's word inside a group of 4
-    const int32_t code0 = (int32_t)(-2 - g.nseam);  // codes are code0 - r
     for (int64_t round = 0; round < g.nblk; round += gridDim.x) {
         const int64_t k = xcd_block(round, g.nblk, blockIdx.x, gridDim.x);
         if (k < 0) break;
         const int64_t w0 = k * BLK_WORDS + wave * WPW;
         WaveWords ww;
         wave_words(g, w0, ww);
-        int64_t base[FGRP], boff[FGRP];
+        int64_t base[FGRP];
 #pragma unroll
         for (int i = 0; i < FGRP; ++i) {
             const int j = 4 * i;
             base[i] = q == 0 ? ww.base[j] : q == 1 ? ww.base[j + 1] : q == 2 ? ww.base[j + 2]
                                                                           : ww.base[j + 3];
-            if (MODE == OUT_NUMBERS) {
-                const int64_t b = q == 0 ? ww.band[j] : q == 1 ? ww.band[j + 1]
-                                        : q == 2 ? ww.band[j + 2] : ww.band[j + 3];
-                boff[i] = bandoff[b];
-            }
         }
         int32_t l[FGRP][4], t[FGRP][4];
 #pragma unroll
@@ -545,9 +473,7 @@ __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
             const int64_t px = ww.pw0 + 256 * i + 4 * lane;
             int64_t v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = out_value<MODE>(l[i][e], t[i][e], base[i], boff[i], code0, rootkey,
-                                       rootnum, err);
+            for (int e = 0; e < 4; ++e) v[e] = out_leader(l[i][e], t[i][e], base[i], rootkey);
             if (out16 && px + 3 < g.HW) {
                 v2i64 a, b;
                 a.x = v[0];
@@ -565,12 +491,263 @@ __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
     }
 }
 
+// ---------------------------------------------------------------- numbers
+// Numbers take another route, with no 32-bit intermediate over the picture:
+//   1. every band goes through the whole tile pipeline in number mode (its
+//      own numbers 1..n_b and count) and keeps its tile records;
+//   2. the band-local numbers of the rows either side of each seam are
+//      written out (the final write of those tile rows);
+//   3. each seam region (band, number) gets one entry of a hash table; its
+//      canonical node is its first seam pixel, equal-colour neighbours across
+//      the seams are joined over canonical nodes keyed by (band, number),
+//      which orders regions as their leaders do, so each set's root is its
+//      region's leading part;
+//   4. every other part is merged: bit n of its band's mask; each band's
+//      merged numbers are prefix-counted, the bands' own numbers give each
+//      band's first number G_b, each root's number is G_b + n - (merged
+//      numbers below n), and each merged number takes its root's, stored at
+//      its rank among its band's merged numbers;
+//   5. each band's final write maps its numbers through that (Map64) and
+//      writes the 64-bit labels straight from its tile records.
+
+// seam pixel `node`: its band and band-local number (from the seam rows)
+__device__ __forceinline__ void seam_number(const Bands &g, int64_t node, const int32_t *rows,
+                                            int64_t &band, uint32_t &n)
+{
+    const int64_t s = node / (2 * g.W);
+    const int64_t rem = node - s * 2 * g.W;
+    // seam s: TH rows of band s's last tile row, then TH rows of band s+1's first
+    const int32_t *top = rows + s * 2 * TH * g.W, *bot = top + TH * g.W;
+    if (rem < g.W) {
+        band = s;
+        n = (uint32_t)top[(TH - 1) * g.W + rem];
+    } else {
+        band = s + 1;
+        n = (uint32_t)bot[rem - g.W];
+    }
+}
+
+__global__ __launch_bounds__(LB) void nm_clear_kernel(int64_t *hkey, int32_t *hnode, int64_t cap)
+{
+    for (int64_t i = (int64_t)blockIdx.x * LB + threadIdx.x; i < cap; i += (int64_t)gridDim.x * LB) {
+        hkey[i] = -1;
+        hnode[i] = INT32_MAX;
+    }
+}
+
+// the words of each band's merge mask that its numbers use (bit n, n <= n_b)
+constexpr int MCB = 16;  // workgroups per band
+__global__ __launch_bounds__(LB) void nm_mclear_kernel(const int32_t *bandcnt, int64_t wpb,
+                                                       uint64_t *M)
+{
+    const int64_t k = blockIdx.x / MCB;
+    const int64_t nw = ((int64_t)bandcnt[k] >> 6) + 1;
+    for (int64_t i = (int64_t)(blockIdx.x % MCB) * LB + threadIdx.x; i < nw; i += (int64_t)MCB * LB)
+        M[k * wpb + i] = 0ull;
+}
+
+// the table slot of key (inserted if new); -1 if the table is full (it holds
+// twice the seam pixels, so it never is)
+__device__ int64_t nm_insert(int64_t *hkey, uint32_t hmask, int64_t key)
+{
+    uint32_t h = seam_hash(key, hmask);
+    for (uint32_t i = 0; i <= hmask; ++i, h = (h + 1u) & hmask) {
+        const int64_t k = hkey[h];
+        if (k == key) return h;
+        if (k == -1) {
+            const unsigned long long old = atomicCAS((unsigned long long *)&hkey[h],
+                                                     (unsigned long long)-1ll,
+                                                     (unsigned long long)key);
+            if ((int64_t)old == -1 || (int64_t)old == key) return h;
+        }
+    }
+    return -1;
+}
+
+// the first pixel of each stretch of one number along a seam row enters the
+// number into the table (the others find it there next), so that a region
+// along the whole row makes one entry, not one per pixel
+__global__ __launch_bounds__(LB) void nm_insert_kernel(Bands g, const int32_t *rows, int64_t *hkey,
+                                                       int32_t *hnode, uint32_t hmask, int32_t *S,
+                                                       uint32_t *err)
+{
+    const int64_t node = (int64_t)blockIdx.x * LB + threadIdx.x;
+    if (node >= g.nseam) return;
+    int64_t band;
+    uint32_t n;
+    seam_number(g, node, rows, band, n);
+    int32_t slot = -1;
+    if (n != 0u) {  // (0: an ignored pixel)
+        int64_t bl;
+        uint32_t nl = 0;
+        if (node % g.W != 0) seam_number(g, node - 1, rows, bl, nl);
+        if (nl == n) {
+            slot = -2;  // looked up next
+        } else {
+            const int64_t h = nm_insert(hkey, hmask, (band << 32) | n);
+            if (h < 0) {
+                atomicOr(err, ERR_LOOP);
+            } else {
+                slot = (int32_t)h;
+                atomicMin(&hnode[h], (int32_t)node);
+            }
+        }
+    }
+    S[node] = slot;
+}
+
+// canonical node of each seam pixel (its region's first seam pixel); those
+// take their region's key
+__global__ __launch_bounds__(LB) void nm_canon_kernel(Bands g, const int32_t *rows, int32_t *S,
+                                                      const int64_t *hkey, uint32_t hmask,
+                                                      const int32_t *hnode, int32_t *C, int32_t *P,
+                                                      int64_t *K, uint32_t *err)
+{
+    const int64_t node = (int64_t)blockIdx.x * LB + threadIdx.x;
+    if (node >= g.nseam) return;
+    P[node] = (int32_t)node;
+    int32_t slot = S[node];
+    if (slot == -2) {  // its stretch's first pixel entered the number
+        int64_t band;
+        uint32_t n;
+        seam_number(g, node, rows, band, n);
+        const int64_t key = (band << 32) | n;
+        uint32_t h = seam_hash(key, hmask);
+        slot = -1;
+        for (uint32_t i = 0; i <= hmask; ++i, h = (h + 1u) & hmask)
+            if (hkey[h] == key) {
+                slot = (int32_t)h;
+                break;
+            }
+        if (slot < 0) atomicOr(err, ERR_LOOP);
+        S[node] = slot;
+    }
+    if (slot < 0) {
+        C[node] = -1;
+        return;
+    }
+    const int32_t c = hnode[slot];
+    C[node] = c;
+    if (c == node) {
+        int64_t band;
+        uint32_t n;
+        seam_number(g, node, rows, band, n);
+        K[node] = (band << 32) | n;
+    }
+}
+
+// each canonical node's root; a part that is not its region's root is merged
+__global__ __launch_bounds__(LB) void nm_mark_kernel(Bands g, const int32_t *rows, const int32_t *C,
+                                                     int32_t *P, int32_t *R, int64_t wpb,
+                                                     uint64_t *M, uint32_t *err)
+{
+    const int64_t node = (int64_t)blockIdx.x * LB + threadIdx.x;
+    if (node >= g.nseam || C[node] != node) return;
+    int budget = SEAM_BUDGET;
+    const int32_t r = seam_find(P, (int32_t)node, budget);
+    if (budget <= 0) atomicOr(err, ERR_LOOP);
+    R[node] = r;
+    if (r != node) {
+        int64_t band;
+        uint32_t n;
+        seam_number(g, node, rows, band, n);
+        atomicOr((unsigned long long *)&M[band * wpb + (n >> 6)], 1ull << (n & 63u));
+    }
+}
+
+// per band (one workgroup each): merged numbers before each mask word, and in all
+constexpr int MS_T = 1024;
+__global__ __launch_bounds__(MS_T) void nm_mscan_kernel(const int32_t *bandcnt, int64_t wpb,
+                                                        const uint64_t *M, uint32_t *Mpre,
+                                                        int32_t *mcnt)
+{
+    __shared__ uint32_t sWave[MS_T / 64];
+    const int64_t k = blockIdx.x;
+    const int64_t nw = ((int64_t)bandcnt[k] >> 6) + 1;
+    const uint64_t *Mk = M + k * wpb;
+    uint32_t *Pk = Mpre + k * wpb;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t carry = 0;
+    for (int64_t base = 0; base < nw; base += MS_T) {
+        const int64_t i = base + threadIdx.x;
+        const uint32_t c = i < nw ? (uint32_t)__popcll(Mk[i]) : 0u;
+        uint32_t x = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) sWave[wave] = x;
+        __syncthreads();
+        uint32_t off = 0, tot = 0;
+        for (int j = 0; j < MS_T / 64; ++j) {
+            const uint32_t v = sWave[j];
+            off += j < wave ? v : 0u;
+            tot += v;
+        }
+        if (i < nw) Pk[i] = carry + off + x - c;
+        carry += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) mcnt[k] = (int32_t)carry;
+}
+
+// each band's first number (its regions that are not merged follow the
+// earlier bands'), and the picture's count
+__global__ void nm_gnum_kernel(const int32_t *bandcnt, const int32_t *mcnt, int64_t nb, int64_t *G,
+                               int64_t *count)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int64_t run = 0;
+    for (int64_t k = 0; k < nb; ++k) {
+        G[k] = run;
+        run += (int64_t)bandcnt[k] - mcnt[k];
+    }
+    if (count) *count = run;
+}
+
+// the number of each seam region: at its root, G + n - (merged numbers below
+// n); then the merged parts take their root's
+__global__ __launch_bounds__(LB) void nm_rootval_kernel(Bands g, const int32_t *rows,
+                                                        const int32_t *C, const int32_t *R,
+                                                        const int32_t *S, int64_t wpb,
+                                                        const uint64_t *M, const uint32_t *Mpre,
+                                                        const int64_t *G, int64_t *hval)
+{
+    const int64_t node = (int64_t)blockIdx.x * LB + threadIdx.x;
+    if (node >= g.nseam || C[node] != node || R[node] != node) return;
+    int64_t band;
+    uint32_t n;
+    seam_number(g, node, rows, band, n);
+    const int64_t wi = band * wpb + (n >> 6);
+    const uint64_t below = M[wi] & ((1ull << (n & 63u)) - 1ull);
+    hval[S[node]] = G[band] + (int64_t)n - (int64_t)(Mpre[wi] + (uint32_t)__popcll(below));
+}
+
+// each merged number's picture number, at its rank among its band's merged
+// numbers (a band has at most 2W: each has a seam pixel there)
+__global__ __launch_bounds__(LB) void nm_mergedval_kernel(Bands g, const int32_t *rows,
+                                                          const int32_t *C, const int32_t *R,
+                                                          const int32_t *S, int64_t wpb,
+                                                          const uint64_t *M, const uint32_t *Mpre,
+                                                          const int64_t *hval, int64_t *MV)
+{
+    const int64_t node = (int64_t)blockIdx.x * LB + threadIdx.x;
+    if (node >= g.nseam || C[node] != node || R[node] == node) return;
+    int64_t band;
+    uint32_t n;
+    seam_number(g, node, rows, band, n);
+    const int64_t wi = band * wpb + (n >> 6);
+    const uint32_t r = Mpre[wi] + (uint32_t)__popcll(M[wi] & ((1ull << (n & 63u)) - 1ull));
+    MV[band * 2 * g.W + r] = hval[S[R[node]]];
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct LargeLayout {
     Bands g;
     Layout band;      // tile-pipeline layout of the tallest band
-    size_t off_lead, off_C, off_P, off_K, off_root, off_rootnum, off_bandoff, off_mask, off_wordin,
+    size_t off_lead, off_C, off_P, off_K, off_root, off_mask, off_wordin,
         off_blkcnt, off_blkpre, off_chunk, total;
 };
 
@@ -619,8 +796,6 @@ static int make_large_layout(int64_t H, int64_t W, int64_t band_rows, LargeLayou
     L->off_P = take(ns * sizeof(int32_t));
     L->off_K = take(ns * sizeof(int64_t));
     L->off_root = take(ns * sizeof(int64_t));
-    L->off_rootnum = take(ns * sizeof(int64_t));
-    L->off_bandoff = take((size_t)g.nb * sizeof(int64_t));
     L->off_mask = take((size_t)g.nwords * sizeof(uint64_t));
     L->off_wordin = take((size_t)g.nwords * sizeof(uint16_t));
     L->off_blkcnt = take((size_t)g.nblk * sizeof(uint32_t));
@@ -628,6 +803,55 @@ static int make_large_layout(int64_t H, int64_t W, int64_t band_rows, LargeLayou
     L->off_chunk = take((size_t)((g.nblk + CHUNK - 1) / CHUNK) * sizeof(int64_t));
     L->total = off;
     return CCL_OK;
+}
+
+// Numbers: every band's tile workspace (bands keep their records until their
+// final write), the seam rows, the seam-region table and the merge masks.
+struct NumLayout {
+    Layout band;     // tile-pipeline layout of the tallest band
+    size_t band_ws;  // bytes of one full band's workspace (band k's starts at k * band_ws)
+    int64_t wpb;     // merge-mask words per band (bit n for numbers 0..band_px)
+    int64_t cap;     // seam-region table entries (a power of two)
+    size_t off_bands, off_bandcnt, off_mcnt, off_G, off_rows, off_S, off_C, off_P, off_R, off_K,
+        off_hkey, off_hnode, off_hval, off_M, off_Mpre, off_MV, total;
+};
+
+static void make_num_layout(const Bands &g, const Layout &band, NumLayout *N)
+{
+    N->band = band;
+    N->band_ws = align256(band.total);
+    N->wpb = g.band_px / 64 + 1;
+    int64_t cap = 1024;
+    while (cap < 2 * g.nseam) cap *= 2;
+    N->cap = cap;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const size_t nb = (size_t)g.nb, ns = (size_t)g.nseam;
+    // band 0's workspace comes first, so its error word is the workspace's;
+    // the last band may be shorter
+    Layout last;
+    make_layout(1, g.H - (g.nb - 1) * g.hb, g.W, &last);  // fits: no taller than a full band
+    N->off_bands = take((nb - 1) * N->band_ws + last.total);
+    N->off_bandcnt = take(nb * sizeof(int32_t));
+    N->off_mcnt = take(nb * sizeof(int32_t));
+    N->off_G = take(nb * sizeof(int64_t));
+    N->off_rows = take((nb - 1) * 2 * TH * (size_t)g.W * sizeof(int32_t));
+    N->off_S = take(ns * sizeof(int32_t));
+    N->off_C = take(ns * sizeof(int32_t));
+    N->off_P = take(ns * sizeof(int32_t));
+    N->off_R = take(ns * sizeof(int32_t));
+    N->off_K = take(ns * sizeof(int64_t));
+    N->off_hkey = take((size_t)cap * sizeof(int64_t));
+    N->off_hnode = take((size_t)cap * sizeof(int32_t));
+    N->off_hval = take((size_t)cap * sizeof(int64_t));
+    N->off_M = take(nb * (size_t)N->wpb * sizeof(uint64_t));
+    N->off_Mpre = take(nb * (size_t)N->wpb * sizeof(uint32_t));
+    N->off_MV = take(nb * 2 * (size_t)g.W * sizeof(int64_t));
+    N->total = off;
 }
 
 static unsigned grid_for(int64_t items, int64_t cap)
@@ -647,6 +871,107 @@ static int check_large_shape(int64_t B, int64_t H, int64_t W, bool *empty)
     return CCL_OK;
 }
 
+// ccl_label_large with CCL_NUMBER (see "numbers" above)
+static int label_large_numbers(const void *colours, int dtype, int64_t batch, int connectivity,
+                               int ign, uint32_t ignore, const Bands &g, const NumLayout &N,
+                               int64_t *out, int64_t *counts, char *ws, hipStream_t s)
+{
+    int32_t *bandcnt = (int32_t *)(ws + N.off_bandcnt);
+    int32_t *mcnt = (int32_t *)(ws + N.off_mcnt);
+    int64_t *G = (int64_t *)(ws + N.off_G);
+    int32_t *rows = (int32_t *)(ws + N.off_rows);
+    int32_t *S = (int32_t *)(ws + N.off_S);
+    int32_t *C = (int32_t *)(ws + N.off_C);
+    int32_t *P = (int32_t *)(ws + N.off_P);
+    int32_t *R = (int32_t *)(ws + N.off_R);
+    int64_t *K = (int64_t *)(ws + N.off_K);
+    int64_t *hkey = (int64_t *)(ws + N.off_hkey);
+    int32_t *hnode = (int32_t *)(ws + N.off_hnode);
+    int64_t *hval = (int64_t *)(ws + N.off_hval);
+    uint64_t *M = (uint64_t *)(ws + N.off_M);
+    uint32_t *Mpre = (uint32_t *)(ws + N.off_Mpre);
+    int64_t *MV = (int64_t *)(ws + N.off_MV);
+    uint32_t *err = (uint32_t *)ws;  // band 0's error word: the call's
+    const size_t px_bytes = (size_t)dtype;
+    const uint32_t hmask = (uint32_t)(N.cap - 1);
+    const unsigned gs = grid_for(g.nseam, INT32_MAX);
+
+    for (int64_t b = 0; b < batch; ++b) {
+        const uint8_t *img = (const uint8_t *)colours + (size_t)(b * g.HW) * px_bytes;
+        Layout Lb[2];  // the layouts of two bands at a time
+        auto band_work = [&](int64_t k, Layout &Lk) -> Work {
+            const int64_t r0 = k * g.hb;
+            const int64_t rowsk = g.H - r0 < g.hb ? g.H - r0 : g.hb;
+            make_layout(1, rowsk, g.W, &Lk);  // fits: no taller than the full band
+            Work w = bind_work(Lk, ws + N.off_bands + (size_t)k * N.band_ws);
+            w.err = err;  // every band reports into the call's error word
+            return w;
+        };
+        // 1. every band through the tile pipeline in number mode
+        for (int64_t k = 0; k < g.nb; ++k) {
+            const Work w = band_work(k, Lb[0]);
+            launch_tile(img + (size_t)(k * g.hb * g.W) * px_bytes, dtype, connectivity, ign,
+                        ignore, Lb[0].g, w, b == 0 && k == 0, s);
+            launch_seam(Lb[0].g, w, connectivity, s);
+            launch_seam_roots(Lb[0].g, w, s);
+            launch_scan(Lb[0].g, w, bandcnt + k, 1, 1, s);
+            launch_resolve(Lb[0].g, w, 1, s);
+        }
+        if (g.nb > 1) {
+            // 2. the band-local numbers of the tile rows either side of each
+            //    seam: band s's last (whole: bands hold a multiple of 64 rows)
+            //    and band s+1's first
+            for (int64_t sm = 0; sm + 1 < g.nb; ++sm) {
+                int32_t *top = rows + sm * 2 * TH * g.W, *bot = top + TH * g.W;
+                const Work wa = band_work(sm, Lb[0]);
+                const uint32_t lastrow = (uint32_t)(Lb[0].g.nty - 1) * (uint32_t)Lb[0].g.ntx;
+                launch_final(Lb[0].g, wa, top - (int64_t)(Lb[0].g.nty - 1) * TH * g.W, 1, 0u, s,
+                             lastrow, (uint32_t)Lb[0].g.ntx);
+                const Work wb = band_work(sm + 1, Lb[1]);
+                launch_final(Lb[1].g, wb, bot, 1, 0u, s, 0u, (uint32_t)Lb[1].g.ntx);
+            }
+            // 3. the seam regions and their joins
+            hipLaunchKernelGGL(nm_clear_kernel, dim3(grid_for(N.cap, 4096)), dim3(LB), 0, s, hkey,
+                               hnode, N.cap);
+            hipLaunchKernelGGL(nm_insert_kernel, dim3(gs), dim3(LB), 0, s, g, rows, hkey, hnode,
+                               hmask, S, err);
+            hipLaunchKernelGGL(nm_canon_kernel, dim3(gs), dim3(LB), 0, s, g, rows, S, hkey, hmask,
+                               hnode, C, P, K, err);
+            hipLaunchKernelGGL(seam_union_kernel, dim3(grid_for((g.nb - 1) * g.W, INT32_MAX)),
+                               dim3(LB), 0, s, g, img, dtype, connectivity, C, P, K, err);
+        }
+        // 4. merged parts, each band's first number, the seam regions' numbers
+        hipLaunchKernelGGL(nm_mclear_kernel, dim3((unsigned)(g.nb * MCB)), dim3(LB), 0, s, bandcnt,
+                           N.wpb, M);
+        if (g.nb > 1)
+            hipLaunchKernelGGL(nm_mark_kernel, dim3(gs), dim3(LB), 0, s, g, rows, C, P, R, N.wpb, M,
+                               err);
+        hipLaunchKernelGGL(nm_mscan_kernel, dim3((unsigned)g.nb), dim3(MS_T), 0, s, bandcnt, N.wpb,
+                           M, Mpre, mcnt);
+        hipLaunchKernelGGL(nm_gnum_kernel, dim3(1), dim3(64), 0, s, bandcnt, mcnt, g.nb, G,
+                           counts ? counts + b : (int64_t *)nullptr);
+        if (g.nb > 1) {
+            hipLaunchKernelGGL(nm_rootval_kernel, dim3(gs), dim3(LB), 0, s, g, rows, C, R, S, N.wpb,
+                               M, Mpre, G, hval);
+            hipLaunchKernelGGL(nm_mergedval_kernel, dim3(gs), dim3(LB), 0, s, g, rows, C, R, S,
+                               N.wpb, M, Mpre, hval, MV);
+        }
+        // 5. 64-bit numbers, band by band, from the bands' records
+        for (int64_t k = 0; k < g.nb; ++k) {
+            const Work w = band_work(k, Lb[0]);
+            Map64 m;
+            m.M = M + k * N.wpb;
+            m.Mpre = Mpre + k * N.wpb;
+            m.MV = MV + k * 2 * g.W;
+            m.G = G;
+            m.band = (uint32_t)k;
+            m.merges = g.nb > 1;
+            launch_final64(Lb[0].g, w, out + b * g.HW + k * g.band_px, m, s);
+        }
+    }
+    return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
+}
+
 }  // namespace large
 }  // namespace ccl
 
@@ -662,7 +987,9 @@ size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, i
     if (empty) return 0;
     LargeLayout L;
     if (make_large_layout(height, width, band_rows, &L) != CCL_OK) return SIZE_MAX;
-    return L.total;
+    NumLayout N;
+    make_num_layout(L.g, L.band, &N);
+    return L.total > N.total ? L.total : N.total;  // leaders or numbers
 }
 
 int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
@@ -691,11 +1018,12 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
     LargeLayout L;
     rc = make_large_layout(height, width, band_rows, &L);
     if (rc != CCL_OK) return rc;
-    // numbers pass through the leaders' int32 entries as -(2 + nseam + r), r a
-    // rank inside a band: every such code must fit
-    if ((flags & CCL_NUMBER) && L.g.nseam + L.g.band_px > (int64_t)INT32_MAX - 2)
-        return band_rows ? CCL_ERR_BAND : CCL_ERR_TOO_LARGE;
-    if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
+    NumLayout N;
+    make_num_layout(L.g, L.band, &N);
+    if (workspace_bytes < (L.total > N.total ? L.total : N.total)) return CCL_ERR_WORKSPACE;
+    if (flags & CCL_NUMBER)
+        return label_large_numbers(colours, dtype, batch, connectivity, ign, ignore, L.g, N, out,
+                                   counts, (char *)workspace, (hipStream_t)stream);
     const Bands &g = L.g;
     char *ws = (char *)workspace;
     int32_t *lead = (int32_t *)(ws + L.off_lead);
@@ -703,8 +1031,6 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
     int32_t *P = (int32_t *)(ws + L.off_P);
     int64_t *K = (int64_t *)(ws + L.off_K);
     int64_t *rootkey = (int64_t *)(ws + L.off_root);
-    int64_t *rootnum = (int64_t *)(ws + L.off_rootnum);
-    int64_t *bandoff = (int64_t *)(ws + L.off_bandoff);
     uint64_t *mask = (uint64_t *)(ws + L.off_mask);
     uint16_t *wordin = (uint16_t *)(ws + L.off_wordin);
     uint32_t *blkcnt = (uint32_t *)(ws + L.off_blkcnt);
@@ -712,8 +1038,7 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
     int64_t *chunk = (int64_t *)(ws + L.off_chunk);
     const int64_t nchunk = (g.nblk + CHUNK - 1) / CHUNK;
     uint32_t *err = (uint32_t *)ws;  // the band workspace's error word
-    const int number = (flags & CCL_NUMBER) != 0;
-    const bool need_scan = number || counts != nullptr;
+    const bool need_scan = counts != nullptr;  // (leaders here: numbers went above)
     const size_t px_bytes = (size_t)dtype;
 
     for (int64_t b = 0; b < batch; ++b) {
@@ -755,23 +1080,10 @@ int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t heigh
                 hipLaunchKernelGGL(chunk_add_kernel, dim3(grid_for(g.nblk, INT32_MAX)), dim3(LB),
                                    0, s, blkpre, g.nblk, chunk);
         }
-        // 5. 64-bit results
+        // 5. 64-bit leaders
         int64_t *o = out + b * g.HW;
         const int o16 = ((uintptr_t)o & 15u) == 0;  // 16-byte stores where aligned
-        if (!number) {
-            hipLaunchKernelGGL(final_kernel<OUT_LEADERS>, dim3(gblk), dim3(LB), 0, s, g, lead,
-                               rootkey, rootnum, bandoff, o, o16, err);
-        } else {
-            hipLaunchKernelGGL(band_offset_kernel, dim3(grid_for(g.nb, INT32_MAX)), dim3(LB), 0, s,
-                               g, mask, wordin, blkpre, bandoff);
-            if (g.nb > 1)
-                hipLaunchKernelGGL(root_number_kernel, dim3(grid_for(g.nseam, INT32_MAX)), dim3(LB),
-                                   0, s, g, C, rootkey, mask, wordin, blkpre, rootnum);
-            hipLaunchKernelGGL(leader_code_kernel, dim3(grid_for(g.nwords, 1 << 20)), dim3(LB), 0,
-                               s, g, mask, wordin, blkpre, bandoff, lead);
-            hipLaunchKernelGGL(final_kernel<OUT_NUMBERS>, dim3(gblk), dim3(LB), 0, s, g,
-                               lead, rootkey, rootnum, bandoff, o, o16, err);
-        }
+        hipLaunchKernelGGL(final_kernel, dim3(gblk), dim3(LB), 0, s, g, lead, rootkey, o, o16);
     }
     return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }

@@ -63,9 +63,7 @@ typedef enum {
     CCL_ERR_IGNORE = -9,        /* CCL_IGNORE with a value wider than the pixel:
                                    above 255 (CCL_U8) or 0xFFFFFF (CCL_RGB24)        */
     CCL_ERR_BAND = -10,         /* ccl_label_large: band_rows negative, not a
-                                   multiple of 64, or band_rows*width > 2^31-1, or
-                                   (CCL_NUMBER) band_rows*width + 2*width*(bands-1)
-                                   > 2^31-3: numbers pass through int32 codes        */
+                                   multiple of 64, or band_rows*width > 2^31-1     */
     CCL_ERR_SCRATCH = -11,      /* ccl_label_noalloc: the batch needs more workspace
                                    than the static scratch array holds
                                    (ccl_workspace_bytes() > CCL_SCRATCH_BYTES)       */
@@ -296,8 +294,10 @@ int ccl_label_stats(const void *colours, int dtype, int64_t batch, int64_t heigh
  * and band height (256-byte aligned; its first 4 bytes are the error word, as
  * for ccl_workspace_bytes).  Pure host arithmetic.  Returns 0 for an empty
  * batch and SIZE_MAX for a shape or band height ccl_label_large rejects.
- * About 4 bytes per pixel of one image, plus the tile pipeline's workspace for
- * one band and a few bytes per pixel of the band seams' rows.
+ * Enough for leaders (about 4 bytes per pixel of one image plus the tile
+ * pipeline's workspace for one band) and for numbers (the tile pipeline's
+ * workspace for every band, about 4 bytes per pixel, plus each seam's two
+ * tile rows of numbers and tables of a few bytes per seam pixel).
  */
 size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, int64_t band_rows);
 
@@ -308,8 +308,7 @@ size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, i
  * counts, as 64-bit values.
  *   colours, dtype, connectivity, flags, ignore   as for ccl_label
  *   band_rows  0: automatic (about 2^30 pixels per band); else the rows of each
- *              band, a multiple of 64 with band_rows*width <= 2^31-1, and with
- *              CCL_NUMBER also band_rows*width + 2*width*(bands-1) <= 2^31-3
+ *              band, a multiple of 64 with band_rows*width <= 2^31-1
  *              (CCL_ERR_BAND otherwise).  Results do not depend on it.
  *   out        device int64 [batch, height, width]: leaders (per-image reading-
  *              order index, -1 for an ignored pixel) or, with CCL_NUMBER,
@@ -319,11 +318,12 @@ size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, i
  *              band_rows)
  * The image is cut into bands of band_rows rows; each band is labelled by the
  * pipeline of ccl_label, then regions are joined across the band seams and the
- * 64-bit results written.  Images of a batch are labelled one after another.
- * CCL_ERR_TOO_LARGE: height*width*batch > 2^46, a band of 64 rows is wider
- * than 2^31-1 pixels, or (CCL_NUMBER, automatic bands) a band's pixels plus
- * 2*width per seam exceed 2^31-3 (numbers pass through int32 codes).  Memory,
- * streams and errors as for ccl_label.
+ * 64-bit results written.  With CCL_NUMBER each band numbers its own regions,
+ * the regions that continue across a seam are joined by (band, number), and
+ * each band's final write turns its numbers into the picture's as it writes
+ * them.  Images of a batch are labelled one after another.
+ * CCL_ERR_TOO_LARGE: height*width*batch > 2^46, or a band of 64 rows is wider
+ * than 2^31-1 pixels.  Memory, streams and errors as for ccl_label.
  */
 int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
                     int connectivity, int flags, uint32_t ignore, int64_t band_rows,

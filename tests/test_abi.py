@@ -129,10 +129,15 @@ def test_large_workspace_bytes(lib):
     assert f(1, 2**20, 2**16, 2**16) == 2**64 - 1  # a band of 2^32 pixels
     one = f(1, 300, 200, 0)                        # one band: the image itself
     banded = f(1, 300, 200, 64)
-    assert 0 < banded < one                        # smaller tile workspace, small seam tables
+    assert one > 0 and banded > 0
     assert one % 256 == 0 and banded % 256 == 0
+    # with numbers every band keeps its tile workspace (a few bytes per pixel)
+    # and each seam its two tile rows of numbers: at least the tile workspace
+    # of the whole image either way
+    assert banded >= lib.ccl_workspace_bytes(1, 300, 200) - 4096
     # beyond 2^31 pixels: int32 leaders for the image plus the tile workspace of
-    # one band (about 2^30 pixels), a few bytes per pixel in all
+    # one band (about 2^30 pixels) for leaders, the tile workspaces of all bands
+    # for numbers: a few bytes per pixel in all
     big = f(1, 46400, 46400, 0)
     assert 4 * 46400 * 46400 < big < 8 * 46400 * 46400
     # a 64-row band wider than 2^31 - 1 pixels cannot be labelled
@@ -162,10 +167,12 @@ def test_label_large_validation(lib):
     assert L(FAKE, 4, 1, 8, 8, 8, 0, 0, 0, None, None, FAKE, big, None) == -1
     assert L(FAKE, 4, 1, 2**24, 2**24, 8, 0, 0, 0, FAKE, None, FAKE, big, None) == -3
     assert L(None, 4, 0, 8, 8, 8, 1, 0, 0, None, None, None, 0, None) == 0
-    # numbers: a band of 2^31 - 64 pixels leaves no room for the seam codes
+    # bands of 2^31 - 64 pixels: numbers and leaders take them (numbers hold no
+    # 32-bit codes over the picture); the workspace is checked first
     W = 2**25 - 1
-    assert L(FAKE, 1, 1, 128, W, 8, 1, 0, 64, FAKE, None, FAKE, big, None) == -10
+    assert L(FAKE, 1, 1, 128, W, 8, 1, 0, 64, FAKE, None, FAKE, 16, None) == -6
     assert L(FAKE, 1, 1, 128, W, 8, 0, 0, 64, FAKE, None, FAKE, 16, None) == -6
+    assert lib.ccl_large_workspace_bytes(1, 128, W, 64) < 2**64 - 1
 
 
 def test_noalloc_validation(lib):
