@@ -410,15 +410,15 @@ __global__ __launch_bounds__(LB) void chunk_add_kernel(int64_t *blkpre, int64_t 
 }
 
 // Step 5 (leaders): each pixel's 64-bit leader; ignored pixels get -1.  A
-// wave takes the same 16 words as in the flag pass, as 4 groups of 256 pixels
-// with 4 consecutive pixels per lane (16-byte loads of the entries, 16-byte
-// stores of the results), in phases so that each phase's loads are in flight
-// together: the pixels' own entries, then their leaders' entries.  A leader's
-// entry holds what the pixel needs: a tag (a seam node: its root's key) or its
-// own index.
-typedef int v4i32 __attribute__((ext_vector_type(4)));
+// wave takes the same 16 words as in the flag pass, as 8 groups of 128 pixels
+// with 2 consecutive pixels per lane (8-byte loads of the entries, 16-byte
+// stores of the results: each store instruction covers 1 KB without gaps), in
+// phases so that each phase's loads are in flight together: the pixels' own
+// entries, then their leaders' entries.  A leader's entry holds what the pixel
+// needs: a tag (a seam node: its root's key) or its own index.
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef long long v2i64 __attribute__((ext_vector_type(2)));
-constexpr int FGRP = WPW / 4;  // groups of 256 pixels per wave
+constexpr int FGRP = WPW / 2;  // groups of 128 pixels per wave
 
 __device__ __forceinline__ int64_t out_leader(int32_t l, int32_t t, int64_t base,
                                               const int64_t *rootkey)
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int q = lane >> 4;  // the lane's word inside a group of 4
+    const int q = lane >> 5;  // the lane's word inside a group of 2
     for (int64_t round = 0; round < g.nblk; round += gridDim.x) {
         const int64_t k = xcd_block(round, g.nblk, blockIdx.x, gridDim.x);
         if (k < 0) break;
@@ -443,49 +443,38 @@ __global__ __launch_bounds__(LB) void final_kernel(Bands g, const int32_t *lead,
         wave_words(g, w0, ww);
         int64_t base[FGRP];
 #pragma unroll
-        for (int i = 0; i < FGRP; ++i) {
-            const int j = 4 * i;
-            base[i] = q == 0 ? ww.base[j] : q == 1 ? ww.base[j + 1] : q == 2 ? ww.base[j + 2]
-                                                                          : ww.base[j + 3];
-        }
-        int32_t l[FGRP][4], t[FGRP][4];
+        for (int i = 0; i < FGRP; ++i) base[i] = q == 0 ? ww.base[2 * i] : ww.base[2 * i + 1];
+        int32_t l[FGRP][2], t[FGRP][2];
 #pragma unroll
         for (int i = 0; i < FGRP; ++i) {
-            const int64_t px = ww.pw0 + 256 * i + 4 * lane;
-            if (px + 3 < g.HW) {
-                const v4i32 v = *(const v4i32 *)(lead + px);
+            const int64_t px = ww.pw0 + 128 * i + 2 * lane;
+            if (px + 1 < g.HW) {
+                const v2i32 v = *(const v2i32 *)(lead + px);
                 l[i][0] = v.x;
                 l[i][1] = v.y;
-                l[i][2] = v.z;
-                l[i][3] = v.w;
             } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) l[i][e] = px + e < g.HW ? lead[px + e] : -1;
+                l[i][0] = px < g.HW ? lead[px] : -1;
+                l[i][1] = -1;
             }
         }
 #pragma unroll
         for (int i = 0; i < FGRP; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 2; ++e)
                 t[i][e] = l[i][e] >= 0 ? lead[base[i] + l[i][e]] : l[i][e];
 #pragma unroll
         for (int i = 0; i < FGRP; ++i) {
-            const int64_t px = ww.pw0 + 256 * i + 4 * lane;
-            int64_t v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = out_leader(l[i][e], t[i][e], base[i], rootkey);
-            if (out16 && px + 3 < g.HW) {
-                v2i64 a, b;
-                a.x = v[0];
-                a.y = v[1];
-                b.x = v[2];
-                b.y = v[3];
+            const int64_t px = ww.pw0 + 128 * i + 2 * lane;
+            const int64_t v0 = out_leader(l[i][0], t[i][0], base[i], rootkey);
+            const int64_t v1 = out_leader(l[i][1], t[i][1], base[i], rootkey);
+            if (out16 && px + 1 < g.HW) {
+                v2i64 a;
+                a.x = v0;
+                a.y = v1;
                 __builtin_nontemporal_store(a, (v2i64 *)(out + px));
-                __builtin_nontemporal_store(b, (v2i64 *)(out + px + 2));
             } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (px + e < g.HW) __builtin_nontemporal_store(v[e], out + px + e);
+                if (px < g.HW) __builtin_nontemporal_store(v0, out + px);
+                if (px + 1 < g.HW) __builtin_nontemporal_store(v1, out + px + 1);
             }
         }
     }
