@@ -337,7 +337,8 @@ def label_stats_leg(ccl, dev, lab, n_total, npx, bpp, steps, warmup, stream, hip
         "ms_per_call": round(ms, 4),
         "value": round(npx / (ms * 1e-3) / 1e9, 3),
         "unit": "Gpixels/s labelled+numbered+statistics",
-        "label_then_region_stats_ms": round(label_ms + stats_ms, 4),
+        "label_then_region_stats_ms": (round(label_ms + stats_ms, 4)
+                                       if label_ms == label_ms else None),  # (nan: not timed)
         "same_as_label_then_region_stats": same,
         "error_word": err,
     }
@@ -657,6 +658,9 @@ def main():
                     help="rows of the sheet the CPU baseline labels (-1 = all, 0 = skip)")
     ap.add_argument("--large-only", action="store_true",
                     help="time only ccl_label_large on the 2.15-Gpx tissue picture (for profiling)")
+    ap.add_argument("--label-stats-only", action="store_true",
+                    help="time only ccl_label_stats on the headline picture (for profiling; "
+                         "one ccl_label and one ccl_region_stats call give its reference)")
     ap.add_argument("--no-extra-legs", action="store_true",
                     help="time the headline call only (no paper-ignored or RGB legs)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -707,6 +711,16 @@ def main():
     lab = ccl.Labeller((B, H, W), device="cuda", connectivity=8)
     stream = torch.cuda.current_stream()
     hip = HipEvents()
+
+    if args.label_stats_only:
+        lab(dev, number=True, stream=stream)
+        hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        ref = stats_leg(ccl, lab.out, lab.counts, npx, 1, 0, stream, hip, torch)
+        leg = label_stats_leg(ccl, dev, lab, ref["regions"], npx, bpp, args.steps, args.warmup,
+                              stream, hip, torch, float("nan"), ref["ms_per_call"],
+                              stats_leg.records)
+        print(json.dumps({"label_stats_leg": leg}), flush=True)
+        return
 
     for _ in range(args.warmup):
         lab(dev, number=True, stream=stream)
