@@ -216,8 +216,11 @@ __device__ __forceinline__ uint64_t g_min(uint64_t *p, uint64_t v)
 // stopped being a root; the atomic minimum that links it returns its true
 // record, and the union goes on from there (g_unite).  Once every union is
 // done, roots no longer change and the walk ends at the root.
-// PLAIN = false reads with agent-scope atomic loads instead.
-template <bool PLAIN = true>
+// PLAIN = false reads with agent-scope atomic loads instead.  HALVE = false
+// skips the halving on a walk's first step (a node two steps below its root
+// is left as it is): the walks once every union is done are mostly that short,
+// and only long chains gain from the atomics.
+template <bool PLAIN = true, bool HALVE = true>
 __device__ uint32_t g_find(const Work &w, uint32_t x, uint64_t &root_rec, int &budget)
 {
     auto load = [&](uint32_t i) -> uint64_t {
@@ -225,6 +228,7 @@ __device__ uint32_t g_find(const Work &w, uint32_t x, uint64_t &root_rec, int &b
         return PLAIN ? *r : g_load(r);
     };
     uint64_t rec = load(x);
+    bool halve = HALVE;
     while (budget-- > 0) {
         const uint32_t p = (uint32_t)rec;
         if (p == x) break;
@@ -234,7 +238,8 @@ __device__ uint32_t g_find(const Work &w, uint32_t x, uint64_t &root_rec, int &b
             rec = prec;
             break;
         }
-        g_min(node_rec(w, x), prec);  // path halving
+        if (halve) g_min(node_rec(w, x), prec);  // path halving
+        halve = true;
         x = (uint32_t)prec;
         rec = load(x);
     }
@@ -274,7 +279,7 @@ __device__ void g_unite(const Work &w, uint32_t a, uint32_t b)
 __device__ uint32_t g_root(const Work &w, uint32_t x, uint64_t &root_rec)
 {
     int budget = GLOBAL_BUDGET;
-    const uint32_t r = g_find<true>(w, x, root_rec, budget);
+    const uint32_t r = g_find<true, false>(w, x, root_rec, budget);
     if (budget <= 0) set_err(w.err, ERR_LOOP);
     return r;
 }
