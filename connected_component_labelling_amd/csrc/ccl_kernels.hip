@@ -1113,10 +1113,10 @@ struct BlockBase {
     int rows, cols;
 };
 
-__device__ __forceinline__ BlockBase block_base(const Geom &g)
+__device__ __forceinline__ BlockBase block_base(const Geom &g, uint32_t blk)
 {
     const uint32_t nbx = ((uint32_t)g.ntx + MB - 1) / MB, nby = ((uint32_t)g.nty + MB - 1) / MB;
-    const uint32_t per = nbx * nby, blk = blockIdx.x;
+    const uint32_t per = nbx * nby;
     const uint32_t b = blk / per, r = blk - b * per, by = r / nbx, bx = r - by * nbx;
     BlockBase bb;
     bb.t0 = b * (uint32_t)g.tpi + by * MB * (uint32_t)g.ntx + bx * MB;
@@ -1246,7 +1246,7 @@ __device__ __forceinline__ void l_unite(uint64_t *R, uint32_t a, uint32_t b)
     }
 }
 
-__global__ __launch_bounds__(BLOCK) void block_merge_kernel(Geom g, Work w, int conn)
+__global__ __launch_bounds__(BLOCK) void block_merge_kernel(Geom g, Work w, int conn, uint32_t slices)
 {
     __shared__ uint64_t sRec[NODE_CAP];      // node records: (key << 32) | parent
     __shared__ uint16_t sNode[NODE_CAP];     // node -> (local tile << 8) | seam slot
@@ -1257,7 +1257,10 @@ __global__ __launch_bounds__(BLOCK) void block_merge_kernel(Geom g, Work w, int 
     __shared__ uint32_t sKind[BT], sNtop[BT], sLeft[BT];
     __shared__ uint32_t sWave[NWAVES];
     const int j = threadIdx.x;
-    const BlockBase bb = block_base(g);
+    // workgroup (block, slice): a block that joins its requests with global
+    // unions deals them over its slices; one merged in LDS uses slice 0 alone
+    const uint32_t blk = blockIdx.x / slices, slice = blockIdx.x - blk * slices;
+    const BlockBase bb = block_base(g, blk);
     const BlockTile me = block_tile(g, bb, j);
     uint32_t nnodes = 0, nreq = 0, kind = 0;
     uint64_t u[KMAX / 64] = {0ull, 0ull, 0ull};
@@ -1295,6 +1298,7 @@ __global__ __launch_bounds__(BLOCK) void block_merge_kernel(Geom g, Work w, int 
     const uint32_t roff = block_exclusive_scan(nreq, sWave, total_req);
     const bool in_lds = total_nodes <= (uint32_t)NODE_CAP;  // the union-find fits in LDS
     const bool listed = total_req <= (uint32_t)REQ_CAP;     // so does the request list
+    if (in_lds && slice != 0) return;
     if (j <= BT) sOff[j] = roff;  // entry BT: the total
     if (in_lds && j < BT) {
         // each tile lists its nodes (slots in order)
@@ -1337,7 +1341,8 @@ __global__ __launch_bounds__(BLOCK) void block_merge_kernel(Geom g, Work w, int 
         __syncthreads();
     }
     // the requests whose two tiles lie in the block
-    for (uint32_t i = j; i < total_req; i += BLOCK) {
+    const uint32_t step = in_lds ? (uint32_t)BLOCK : slices * (uint32_t)BLOCK;
+    for (uint32_t i = (in_lds ? 0u : slice * (uint32_t)BLOCK) + (uint32_t)j; i < total_req; i += step) {
         uint32_t jj, r;
         if (listed) {
             const uint32_t e = sReq[i];
@@ -1375,14 +1380,16 @@ __global__ __launch_bounds__(BLOCK) void block_merge_kernel(Geom g, Work w, int 
 
 // The requests that cross a block border, from the tiles on the block's top
 // row and its left and right columns.
-__global__ __launch_bounds__(BLOCK) void border_merge_kernel(Geom g, Work w, int conn)
+__global__ __launch_bounds__(BLOCK) void border_merge_kernel(Geom g, Work w, int conn, uint32_t slices)
 {
     __shared__ uint64_t sTop[BT];
     __shared__ uint32_t sOff[BT + 1];
     __shared__ uint32_t sKind[BT], sNtop[BT], sLeft[BT];
     __shared__ uint32_t sWave[NWAVES];
     const int j = threadIdx.x;
-    const BlockBase bb = block_base(g);
+    // workgroup (block, slice): the slices of a block take its rounds in turn
+    const uint32_t blk = blockIdx.x / slices, slice = blockIdx.x - blk * slices;
+    const BlockBase bb = block_base(g, blk);
     const BlockTile me = block_tile(g, bb, j);
     const bool border = me.ly == 0 || me.lx == 0 || me.lx == MB - 1;
     uint32_t nreq = 0, kind = 0, ntop = 0, leftmask = 0;
@@ -1407,7 +1414,7 @@ __global__ __launch_bounds__(BLOCK) void border_merge_kernel(Geom g, Work w, int
     __syncthreads();
     const int lane = lane_id();
     const uint32_t rounds = (total + BLOCK - 1) / BLOCK;
-    for (uint32_t k = 0; k < rounds; ++k) {
+    for (uint32_t k = slice; k < rounds; k += slices) {
         const uint32_t i = k * BLOCK + (uint32_t)j;
         uint32_t a = 0xFFFFFFFFu, bn = 0xFFFFFFFFu;
         if (i < total) {
@@ -1429,13 +1436,13 @@ __global__ __launch_bounds__(BLOCK) void border_merge_kernel(Geom g, Work w, int
 }
 
 // ------------------------------------------------------------- seam roots
-// Seam nodes of SEAM_TILES consecutive tiles, dealt round-robin to the
+// Seam nodes of tpw (<= SEAM_TILES) consecutive tiles, dealt round-robin to the
 // workgroup's threads.  A node that is still a root after the merge leads a
 // region of the whole image: it joins its row segment's leader mask and count
 // (a one-colour tile's node sets the tile's leader bit).  This pass also
 // clears the band status words of the scan that follows.
 
-__global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
+__global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w, uint32_t tpw)
 {
     clear_bands(g, w);
     __shared__ uint32_t sOff[SEAM_TILES + 1];
@@ -1450,9 +1457,9 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
         sLead[i] = 0ull;
         sCnt[i] = 0u;
     }
-    const uint32_t t0 = blockIdx.x * SEAM_TILES;
+    const uint32_t t0 = blockIdx.x * tpw;  // tiles t0 .. t0+tpw-1 (tpw <= SEAM_TILES)
     const uint32_t tme = t0 + threadIdx.x;
-    const bool mine = threadIdx.x < SEAM_TILES && tme < (uint32_t)g.ntiles;
+    const bool mine = threadIdx.x < tpw && tme < (uint32_t)g.ntiles;
     uint32_t n = 0;
     bool uni = false;
     if (mine) {
@@ -1495,7 +1502,7 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w)
     }
     __syncthreads();
     // the tile pass wrote these words (its own leaders); add the seam leaders
-    for (int i = threadIdx.x; i < SEAM_TILES * TH; i += BLOCK) {
+    for (int i = threadIdx.x; i < (int)tpw * TH; i += BLOCK) {
         const uint32_t cnt = sCnt[i];
         if (cnt == 0) continue;
         const size_t sg = (size_t)t0 * TH + i;
@@ -1676,7 +1683,7 @@ __global__ __launch_bounds__(SCAN_BLOCK) void scan_kernel(Geom g, Work w, int32_
 // ---------------------------------------------------------------- resolve
 // After the scan, each seam node finds its leader (Collapse) and gets the value
 // its pixels will carry: the leader's index, or 1 + the leaders before it.
-// Nodes of SEAM_TILES consecutive tiles are dealt round-robin to the
+// Nodes of tpw (<= SEAM_TILES) consecutive tiles are dealt round-robin to the
 // workgroup's threads.  The records are only read here, so the walks may run
 // side by side; the values go to nval (a one-colour tile: its header).
 
@@ -1699,15 +1706,16 @@ __device__ __forceinline__ void stats_empty(RegionRec *r)
     q[4] = 0xFFFFFFFFu;                                      // x1 -1, pad 0
 }
 
-__global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int number, StatsOut so)
+__global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int number, StatsOut so,
+                                                       uint32_t tpw)
 {
     __shared__ uint32_t sOff[SEAM_TILES + 1];
     __shared__ uint64_t sUsed[SEAM_TILES][KMAX / 64];
     __shared__ uint8_t sUni[SEAM_TILES];
     __shared__ uint32_t sWave[NWAVES];
-    const uint32_t t0 = blockIdx.x * SEAM_TILES;
+    const uint32_t t0 = blockIdx.x * tpw;  // tiles t0 .. t0+tpw-1 (tpw <= SEAM_TILES)
     const uint32_t tme = t0 + threadIdx.x;
-    const bool mine = threadIdx.x < SEAM_TILES && tme < (uint32_t)g.ntiles;
+    const bool mine = threadIdx.x < tpw && tme < (uint32_t)g.ntiles;
     uint32_t n = 0;
     bool uni = false;
     if (mine) {
@@ -2973,14 +2981,27 @@ void launch_tile(const void *img, int dtype_bytes, int conn, int ignore, uint32_
 void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s)
 {
     const int64_t blocks = g.B * ((g.nty + MB - 1) / MB) * ((g.ntx + MB - 1) / MB);
-    hipLaunchKernelGGL(block_merge_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, g, w, conn);
-    hipLaunchKernelGGL(border_merge_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, g, w, conn);
+    // few blocks (small images, small batches): each block's global unions are
+    // dealt over up to 16 workgroups, so that about 2048 are in flight
+    const int64_t want = (2048 + blocks - 1) / blocks;
+    const uint32_t slices = (uint32_t)(want < 1 ? 1 : want > 16 ? 16 : want);
+    const dim3 grid((unsigned)(blocks * slices));
+    hipLaunchKernelGGL(block_merge_kernel, grid, dim3(BLOCK), 0, s, g, w, conn, slices);
+    hipLaunchKernelGGL(border_merge_kernel, grid, dim3(BLOCK), 0, s, g, w, conn, slices);
+}
+
+// tiles per workgroup of the roots and resolve passes: SEAM_TILES, or fewer
+// on small inputs, so that about 2048 workgroups walk their nodes at once
+static uint32_t seam_tiles_per_wg(const Geom &g)
+{
+    const int64_t k = g.ntiles / 2048;
+    return (uint32_t)(k < 1 ? 1 : k > SEAM_TILES ? SEAM_TILES : k);
 }
 
 void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s)
 {
-    hipLaunchKernelGGL(seam_roots_kernel, dim3(grid_of(g.ntiles, SEAM_TILES)), dim3(BLOCK), 0, s, g,
-                       w);
+    const uint32_t tpw = seam_tiles_per_wg(g);
+    hipLaunchKernelGGL(seam_roots_kernel, dim3(grid_of(g.ntiles, tpw)), dim3(BLOCK), 0, s, g, w, tpw);
 }
 
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
@@ -2994,8 +3015,9 @@ void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s, Reg
                     int64_t cap)
 {
     const StatsOut so{rec, cap, (const int64_t *)w.bandst};
-    hipLaunchKernelGGL(resolve_kernel, dim3(grid_of(g.ntiles, SEAM_TILES)), dim3(BLOCK), 0, s, g, w,
-                       number, so);
+    const uint32_t tpw = seam_tiles_per_wg(g);
+    hipLaunchKernelGGL(resolve_kernel, dim3(grid_of(g.ntiles, tpw)), dim3(BLOCK), 0, s, g, w, number,
+                       so, tpw);
 }
 
 void launch_final64(const Geom &g, const Work &w, int64_t *out, const Map64 &m, hipStream_t s)
