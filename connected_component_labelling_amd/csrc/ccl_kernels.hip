@@ -949,9 +949,13 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     }
 }
 
-// One workgroup per tile: workgroup v labels tile remap_tile(v), so that each
-// XCD works through one contiguous range of tiles.  Tiles wholly inside the
-// image are loaded without edge checks.
+// One workgroup per tile: workgroup v labels tile t0 + v, so that the
+// workgroups, dealt to the 8 XCDs in turn, spread every part of the picture
+// (and its tiles of several colours) over all of them, and the whole GPU reads
+// one stretch of the picture at a time.  (Contiguous tile ranges per XCD, as
+// the final write takes them, made this pass 5 % slower on a drawing whose
+// detail is unevenly spread.)  Tiles wholly inside the image are loaded
+// without edge checks.
 //
 // The arguments come as one struct, read through the kernel-argument segment
 // pointer at each use.  Arguments named as parameters are all loaded into scalar
@@ -965,7 +969,7 @@ struct TileArgs {
     Work w;
     uint32_t ign;        // the ignored colour (IGN instances only)
     uint32_t clear_err;  // workgroup 0 clears the error word (the call's first kernel)
-    uint32_t t0;         // the first tile of the launch (workgroup v: tile t0 + remap(v))
+    uint32_t t0;         // the first tile of the launch (workgroup v: tile t0 + v)
 };
 
 template <typename T, int CONN, bool IGN>
@@ -981,7 +985,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void
     // no kernel of this call has run before this one, and the later ones set
     // the word only after it has ended
     if (blockIdx.x == 0 && threadIdx.x == 0 && a.clear_err) *w.err = 0u;
-    const uint32_t t = a.t0 + remap_tile(blockIdx.x, gridDim.x);
+    const uint32_t t = a.t0 + blockIdx.x;
     const TilePos tp = tile_pos(t, g);
     if (tp.vh == TH && tp.vw == TW)
         label_tile<CONN, true, IGN>(g, w, s, t, tp, load_tile<T, true>(img, g, tp, wave, lane), a.ign);
