@@ -59,7 +59,9 @@ __device__ __forceinline__ uint32_t from_left_lane(uint32_t v)
 
 // Map workgroup ids to work items so that each XCD (workgroups are dealt to the
 // 8 XCDs round-robin) gets one contiguous range: neighbouring tiles then share
-// that XCD's L2.
+// that XCD's L2.  A bijection of 0..n-1.  Used where it measured faster: the
+// final write and the seam passes, not the tile pass.  Never for the scan,
+// whose bands wait for the bands before them and so must start in order.
 __device__ __forceinline__ uint32_t remap_tile(uint32_t bid, uint32_t n)
 {
     const uint32_t q = n >> 3, r = n & 7u;
@@ -1262,8 +1264,10 @@ __global__ __launch_bounds__(BLOCK) void block_merge_kernel(Geom g, Work w, int 
     __shared__ uint32_t sWave[NWAVES];
     const int j = threadIdx.x;
     // workgroup (block, slice): a block that joins its requests with global
-    // unions deals them over its slices; one merged in LDS uses slice 0 alone
-    const uint32_t blk = blockIdx.x / slices, slice = blockIdx.x - blk * slices;
+    // unions deals them over its slices; one merged in LDS uses slice 0 alone.
+    // Each XCD takes a contiguous range of blocks.
+    const uint32_t wg = remap_tile(blockIdx.x, gridDim.x);
+    const uint32_t blk = wg / slices, slice = wg - blk * slices;
     const BlockBase bb = block_base(g, blk);
     const BlockTile me = block_tile(g, bb, j);
     uint32_t nnodes = 0, nreq = 0, kind = 0;
@@ -1391,8 +1395,10 @@ __global__ __launch_bounds__(BLOCK) void border_merge_kernel(Geom g, Work w, int
     __shared__ uint32_t sKind[BT], sNtop[BT], sLeft[BT];
     __shared__ uint32_t sWave[NWAVES];
     const int j = threadIdx.x;
-    // workgroup (block, slice): the slices of a block take its rounds in turn
-    const uint32_t blk = blockIdx.x / slices, slice = blockIdx.x - blk * slices;
+    // workgroup (block, slice): the slices of a block take its rounds in turn;
+    // each XCD takes a contiguous range of blocks
+    const uint32_t wg = remap_tile(blockIdx.x, gridDim.x);
+    const uint32_t blk = wg / slices, slice = wg - blk * slices;
     const BlockBase bb = block_base(g, blk);
     const BlockTile me = block_tile(g, bb, j);
     const bool border = me.ly == 0 || me.lx == 0 || me.lx == MB - 1;
@@ -1461,7 +1467,8 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w, uint3
         sLead[i] = 0ull;
         sCnt[i] = 0u;
     }
-    const uint32_t t0 = blockIdx.x * tpw;  // tiles t0 .. t0+tpw-1 (tpw <= SEAM_TILES)
+    // tiles t0 .. t0+tpw-1 (tpw <= SEAM_TILES); each XCD takes a contiguous range
+    const uint32_t t0 = remap_tile(blockIdx.x, gridDim.x) * tpw;
     const uint32_t tme = t0 + threadIdx.x;
     const bool mine = threadIdx.x < tpw && tme < (uint32_t)g.ntiles;
     uint32_t n = 0;
@@ -1717,7 +1724,8 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
     __shared__ uint64_t sUsed[SEAM_TILES][KMAX / 64];
     __shared__ uint8_t sUni[SEAM_TILES];
     __shared__ uint32_t sWave[NWAVES];
-    const uint32_t t0 = blockIdx.x * tpw;  // tiles t0 .. t0+tpw-1 (tpw <= SEAM_TILES)
+    // tiles t0 .. t0+tpw-1 (tpw <= SEAM_TILES); each XCD takes a contiguous range
+    const uint32_t t0 = remap_tile(blockIdx.x, gridDim.x) * tpw;
     const uint32_t tme = t0 + threadIdx.x;
     const bool mine = threadIdx.x < tpw && tme < (uint32_t)g.ntiles;
     uint32_t n = 0;
