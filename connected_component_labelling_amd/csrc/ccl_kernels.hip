@@ -69,6 +69,20 @@ __device__ __forceinline__ uint32_t remap_tile(uint32_t bid, uint32_t n)
     return j * q + (j < r ? j : r) + i;
 }
 
+// The tile pass's order: runs of TILE_RUN consecutive tiles dealt to the 8 XCDs
+// in turn (workgroup ids reach the XCDs round-robin), so that the tiles of one
+// stretch of the picture are spread over every XCD while three tiles in four
+// find their left neighbour's pixels (their halo column) in their own L2.  A
+// bijection of 0..n-1: the last n mod 8*TILE_RUN ids map to themselves.
+constexpr uint32_t TILE_RUN = 4;
+__device__ __forceinline__ uint32_t tile_order(uint32_t bid, uint32_t n)
+{
+    constexpr uint32_t G = 8 * TILE_RUN;
+    if (bid >= n / G * G) return bid;
+    const uint32_t i = bid >> 3;
+    return i / TILE_RUN * G + (bid & 7u) * TILE_RUN + i % TILE_RUN;
+}
+
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f)
 {
     return (uint32_t)(((uint64_t)n * f.m) >> f.s);
@@ -951,13 +965,12 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     }
 }
 
-// One workgroup per tile: workgroup v labels tile t0 + v, so that the
-// workgroups, dealt to the 8 XCDs in turn, spread every part of the picture
-// (and its tiles of several colours) over all of them, and the whole GPU reads
-// one stretch of the picture at a time.  (Contiguous tile ranges per XCD, as
-// the final write takes them, made this pass 5 % slower on a drawing whose
-// detail is unevenly spread.)  Tiles wholly inside the image are loaded
-// without edge checks.
+// One workgroup per tile: workgroup v labels tile t0 + tile_order(v), so that
+// every stretch of the picture (and its tiles of several colours) is spread
+// over all the XCDs, and the whole GPU reads one stretch at a time.
+// (Contiguous tile ranges per XCD, as the final write takes them, made this
+// pass 5 % slower on a drawing whose detail is unevenly spread.)  Tiles wholly
+// inside the image are loaded without edge checks.
 //
 // The arguments come as one struct, read through the kernel-argument segment
 // pointer at each use.  Arguments named as parameters are all loaded into scalar
@@ -971,7 +984,7 @@ struct TileArgs {
     Work w;
     uint32_t ign;        // the ignored colour (IGN instances only)
     uint32_t clear_err;  // workgroup 0 clears the error word (the call's first kernel)
-    uint32_t t0;         // the first tile of the launch (workgroup v: tile t0 + v)
+    uint32_t t0;         // the first tile of the launch (workgroup v: tile t0 + tile_order(v))
 };
 
 template <typename T, int CONN, bool IGN>
@@ -987,7 +1000,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(8))) void
     // no kernel of this call has run before this one, and the later ones set
     // the word only after it has ended
     if (blockIdx.x == 0 && threadIdx.x == 0 && a.clear_err) *w.err = 0u;
-    const uint32_t t = a.t0 + blockIdx.x;
+    const uint32_t t = a.t0 + tile_order(blockIdx.x, gridDim.x);
     const TilePos tp = tile_pos(t, g);
     if (tp.vh == TH && tp.vw == TW)
         label_tile<CONN, true, IGN>(g, w, s, t, tp, load_tile<T, true>(img, g, tp, wave, lane), a.ign);
