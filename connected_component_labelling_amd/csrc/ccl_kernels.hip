@@ -714,13 +714,16 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             const uint64_t jm = ra | rb;
             const uint64_t em = (st_m >> 1) | (1ull << 63);
             const uint64_t first = (~(jm | em) + st_m) & jm;
-            // every lane reads and stores: a lane without a first join reads
-            // its own run's word and stores into the tail
-            const bool fl = lane_bit(first);
-            const uint32_t tgt = fl ? (lane_bit(rb) ? ab : ar) : me;
-            const uint32_t pv = lds_parent<false>(s.P, tgt);
-            __hip_atomic_store(&s.P[fl ? me : (uint32_t)(TPX + lane)], pv, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
+            // every lane reads the parent of the run above that its join (rb
+            // before ra) would take -- ab and ar are slots of the row above in
+            // every lane -- and stores it: a run's first join into the run's
+            // word, every other lane into the tail
+            const uint32_t pv = lds_parent<false>(s.P, lane_bit(rb) ? ab : ar);
+            __hip_atomic_store(&s.P[lane_bit(first) ? me : (uint32_t)(TPX + lane)], pv,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            // joins other than each run's first are left (a lane's ra join
+            // stays when its rb join came first); most rows have none
+            if (popc64(ra) + popc64(rb) == popc64(first)) return;
             ra &= ~(first & ~rb);
             rb &= ~first;
         }
