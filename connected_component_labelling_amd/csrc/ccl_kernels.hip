@@ -674,6 +674,19 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
     uint32_t head = 0, tail = 0;
     // lanes of the tile's columns
     const uint64_t ok_m = FULL || vw >= TW ? ~0ull : (1ull << vw) - 1ull;
+    // unite queued joins, 64 at a time while 64 wait (all: until none wait);
+    // join_rows calls it whenever it queues
+    auto drain = [&](bool all) {
+        while (tail - head >= 64u || (all && tail != head)) {
+            const uint32_t n = tail - head;
+            __syncwarp();
+            if ((uint32_t)lane < n) {
+                const uint32_t e = q[(head + (uint32_t)lane) & (QCAP - 1)];
+                lds_unite(s.P, e & 0xFFFFu, e >> 16);
+            }
+            head += n < 64u ? n : 64u;
+        }
+    };
     // Rows are handled as lane masks: a ballot per comparison, the logic on
     // the masks in scalar registers.  me / mea: run slot of the lane's pixel in
     // row y / in the row above (bit 0 of a row's start mask is always set, so
@@ -723,28 +736,18 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             // joins other than each run's first are left (a lane's ra join
             // stays when its rb join came first); most rows have none
-            if (popc64(ra) + popc64(rb) == popc64(first)) return;
+            if (popc64(ra) + popc64(rb) == popc64(first)) return false;
             ra &= ~(first & ~rb);
             rb &= ~first;
         }
-        if ((rb | ra) != 0ull) {  // further joins (rare): queued as unions
-            if (lane_bit(rb)) q[mbcnt_acc(rb, tail) & (QCAP - 1)] = me | (ab << 16);
-            tail += popc64(rb);
-            if (lane_bit(ra)) q[mbcnt_acc(ra, tail) & (QCAP - 1)] = me | (ar << 16);
-            tail += popc64(ra);
-        }
-    };
-    // unite queued joins, 64 at a time while 64 wait (all: until none wait)
-    auto drain = [&](bool all) {
-        while (tail - head >= 64u || (all && tail != head)) {
-            const uint32_t n = tail - head;
-            __syncwarp();
-            if ((uint32_t)lane < n) {
-                const uint32_t e = q[(head + (uint32_t)lane) & (QCAP - 1)];
-                lds_unite(s.P, e & 0xFFFFu, e >> 16);
-            }
-            head += n < 64u ? n : 64u;
-        }
+        if ((rb | ra) == 0ull) return false;
+        // further joins (rare): queued as unions
+        if (lane_bit(rb)) q[mbcnt_acc(rb, tail) & (QCAP - 1)] = me | (ab << 16);
+        tail += popc64(rb);
+        if (lane_bit(ra)) q[mbcnt_acc(ra, tail) & (QCAP - 1)] = me | (ar << 16);
+        tail += popc64(ra);
+        drain(false);
+        return true;
     };
     const int nrows = vh - wave * RPW < 0 ? 0 : (vh - wave * RPW < RPW ? vh - wave * RPW : RPW);
     const uint32_t c0 = c[0];
@@ -755,14 +758,14 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         uint32_t mlo = 0, mhi = 0;  // lane i collects row i's run starts
         uint32_t ilo = 0, ihi = 0;  // ... and its pixels of the ignored colour
         uint32_t rbase = 0;         // ... and its first slot
-        uint32_t nw = 0;            // runs in the wave's rows so far
+        uint32_t base = wbase;      // the slot of the row's first run
 #pragma unroll
         for (int i = 0; i < RPW; ++i) {
             if (i >= nrows) break;
             const int y = wave * RPW + i;
             const uint32_t cc = c[i];
             const uint64_t st_m = (__ballot(from_left_lane(cc) != cc) | 1ull) & ok_m;
-            const uint32_t me = mbcnt_acc(st_m >> 1, wbase + nw);
+            const uint32_t me = mbcnt_acc(st_m >> 1, base);
             uint64_t ig_m = 0;
             if (IGN) ig_m = __ballot(cc == ign) & ok_m;
             // the start lane of each run stores its row and column and its
@@ -777,16 +780,13 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             // on MI355X)
             mlo = lane == i ? (uint32_t)st_m : mlo;
             mhi = lane == i ? (uint32_t)(st_m >> 32) : mhi;
-            rbase = lane == i ? wbase + nw : rbase;
+            rbase = lane == i ? base : rbase;
             if (IGN) {
                 ilo = lane == i ? (uint32_t)ig_m : ilo;
                 ihi = lane == i ? (uint32_t)(ig_m >> 32) : ihi;
             }
-            nw += popc64(st_m);
-            if (i > 0) {
-                join_rows(cc, st_m, me, ca, sta, mea, ig_m, true);
-                drain(false);
-            }
+            base += popc64(st_m);
+            if (i > 0) join_rows(cc, st_m, me, ca, sta, mea, ig_m, true);
             ca = cc;
             sta = st_m;
             mea = me;
@@ -801,7 +801,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
             for (int i = 0; i < RPW; ++i) s.ColC[wave * RPW + i] = c[i];  // (0 past the image edge)
         }
         if (wave < NWAVES - 1) s.LastC[wave][lane] = ca;  // this wave's last row
-        if (lane == 0) s.WaveRuns[wave] = nw;
+        if (lane == 0) s.WaveRuns[wave] = base - wbase;
     }
     if (tid < KMAX / 64) s.Used[tid] = 0;
     if (tid < TH) s.Lead[tid] = 0;
