@@ -816,10 +816,15 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
                    n2 = __builtin_amdgcn_readfirstlane(s.WaveRuns[2]),
                    n3 = __builtin_amdgcn_readfirstlane(s.WaveRuns[3]);
     const uint32_t off1 = n0, off2 = off1 + n1, off3 = off2 + n2, R = off3 + n3;
+    // (three independent selects of wave-uniform offsets, not a chain of
+    // branches)
+    const uint32_t adj1 = 1u * WAVE_SLOTS - off1, adj2 = 2u * WAVE_SLOTS - off2,
+                   adj3 = 3u * WAVE_SLOTS - off3;
     auto run_slot = [&](uint32_t r) -> uint32_t {
-        return r >= off3 ? r + (3u * WAVE_SLOTS - off3)
-             : r >= off2 ? r + (2u * WAVE_SLOTS - off2)
-             : r >= off1 ? r + (1u * WAVE_SLOTS - off1) : r;
+        uint32_t adj = r >= off1 ? adj1 : 0u;
+        adj = r >= off2 ? adj2 : adj;
+        adj = r >= off3 ? adj3 : adj;
+        return r + adj;
     };
 
     // the wave's first row against the last row of the wave above (unions:
