@@ -1534,12 +1534,15 @@ __global__ __launch_bounds__(BLOCK) void seam_roots_kernel(Geom g, Work w, uint3
     }
     __syncthreads();
     // the tile pass wrote these words (its own leaders); add the seam leaders
+    // (each segment is this workgroup's alone: the atomics only spare the
+    // workgroup a read before each write)
     for (int i = threadIdx.x; i < (int)tpw * TH; i += BLOCK) {
         const uint32_t cnt = sCnt[i];
         if (cnt == 0) continue;
         const size_t sg = (size_t)t0 * TH + i;
-        w.leadmask[sg] |= sLead[i];
-        w.seg[sg] += cnt;
+        __hip_atomic_fetch_or((unsigned long long *)&w.leadmask[sg], (unsigned long long)sLead[i],
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&w.seg[sg], cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
