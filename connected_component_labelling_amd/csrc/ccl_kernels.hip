@@ -921,13 +921,26 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
         const uint32_t root = s.P[run] & PMASK;
         return 255u - (s.P[root] >> 16);
     };
-    // the last steps, spread over the waves: 3 the bottom row's seam slots, 2
-    // the right column's and the leader masks, 1 the left-edge requests, 0 the
-    // top-edge requests and the header
-    if (has_bottom && wave == NWAVES - 1 && lane_ok) {
-        const uint64_t mb = uniform64(s.Mask[TH - 1]);
-        const uint32_t bb = __builtin_amdgcn_readfirstlane((uint32_t)s.RowBase[TH - 1]);
-        w.bslot[(size_t)t * TW + lane] = (uint8_t)seam_of(mbcnt_acc(mb >> 1, bb));
+    // the last steps, spread over the waves: 3 the bottom row's seam slots and
+    // the header, 2 the right column's slots and the leader masks, 1 the
+    // left-edge requests, 0 the top-edge requests
+    if (wave == NWAVES - 1) {
+        if (has_bottom && lane_ok) {
+            const uint64_t mb = uniform64(s.Mask[TH - 1]);
+            const uint32_t bb = __builtin_amdgcn_readfirstlane((uint32_t)s.RowBase[TH - 1]);
+            w.bslot[(size_t)t * TW + lane] = (uint8_t)seam_of(mbcnt_acc(mb >> 1, bb));
+        }
+        // the header but its words 3 and 4 (the requests' counts, from waves 0
+        // and 1; the one-colour fields stay 0); the first eight bytes also give
+        // the final write the bounds of its reads
+        const uint32_t nslots = s.Used[2] ? 128u + 64u - (uint32_t)__builtin_clzll(s.Used[2])
+                              : s.Used[1] ? 64u + 64u - (uint32_t)__builtin_clzll(s.Used[1])
+                              : s.Used[0] ? 64u - (uint32_t)__builtin_clzll(s.Used[0]) : 0u;
+        uint32_t v = lane >= 6 && lane < 12 ? ((const uint32_t *)s.Used)[lane - 6] : 0u;
+        v = write_lane(v, nslots << 8, 0);
+        v = write_lane(v, R, 1);
+        v = write_lane(v, R, 2);
+        if (lane < (int)(sizeof(TileHdr) / 4) && lane != 3 && lane != 4) ((uint32_t *)&hdr)[lane] = v;
     }
     if (wave == 2) {
         if (has_right && lane < vh)
@@ -959,17 +972,7 @@ __device__ __forceinline__ void label_tile(const Geom &g, const Work &w, TileLds
                                       c[0], m0, me, hrow, hm1, hp1,
                                       IGN ? ~uniform64(s.Ign[0]) : ~0ull);
         }
-        // the header (the one-colour fields stay 0; word 4 comes from wave 1);
-        // the first eight bytes also give the final write the bounds of its reads
-        const uint32_t nslots = s.Used[2] ? 128u + 64u - (uint32_t)__builtin_clzll(s.Used[2])
-                              : s.Used[1] ? 64u + 64u - (uint32_t)__builtin_clzll(s.Used[1])
-                              : s.Used[0] ? 64u - (uint32_t)__builtin_clzll(s.Used[0]) : 0u;
-        uint32_t v = lane >= 6 && lane < 12 ? ((const uint32_t *)s.Used)[lane - 6] : 0u;
-        v = write_lane(v, nslots << 8, 0);
-        v = write_lane(v, R, 1);
-        v = write_lane(v, R, 2);
-        v = write_lane(v, ntop, 3);
-        if (lane < (int)(sizeof(TileHdr) / 4) && lane != 4) ((uint32_t *)&hdr)[lane] = v;
+        if (lane == 3) ((uint32_t *)&hdr)[3] = ntop;  // the header's word 3
     }
 }
 
