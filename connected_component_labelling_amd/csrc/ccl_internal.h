@@ -150,24 +150,31 @@ void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s);
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
                  hipStream_t s);
 struct RegionRec;
-// rec: with numbers, each region that crosses a tile edge gets an empty record
-// (statistics of the labelling call; the band-status words hold the first
-// record of each image by then)
+// number: 0 leaders, 1 numbers, 2 numbers and each seam node's record pointed
+// at its root (whose key is the region's leader).  rec: with numbers, each
+// region that crosses a tile edge gets an empty record (statistics of the
+// labelling call; the band-status words hold the first record of each image by
+// then)
 void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s,
                     RegionRec *rec = nullptr, int64_t cap = 0);
-// ignv: the value written for pixels of an ignored colour
+// number: 0 leaders, 1 numbers, 2 leaders of a workspace numbered with
+// resolve's number == 2.  ignv: the value written for pixels of an ignored
+// colour
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,
                   hipStream_t s, uint32_t t0 = 0, uint32_t nt = 0);
 
 // Numbers of one band of a picture cut into bands, to the picture's numbers
 // (ccl_label_large): band-local number n (1..) is merged into a region led
 // elsewhere when bit n of M is set; with r the merged numbers below n, it then
-// takes MV[r], else it becomes G + n - r.
+// takes MV[r], else it becomes G + n - r.  For leaders, MV holds the picture's
+// leader of each merged number, and an unmerged region's leader is base + its
+// band-local leader.
 struct Map64 {
     const uint64_t *M;     // bit n: number n merged (this band's words)
     const uint32_t *Mpre;  // merged numbers in the words before each word
-    const int64_t *MV;     // the picture's number of each merged number, by rank
+    const int64_t *MV;     // the picture's number (or leader) of each merged number, by rank
     const int64_t *G;      // [band]: numbers of the picture before the band's own
+    int64_t base;          // the picture index of the band's first pixel (leaders)
     uint32_t band;
     int merges;            // 0: one band, its numbers are the picture's
 };
@@ -179,9 +186,11 @@ __device__ __forceinline__ uint32_t seam_hash(int64_t key, uint32_t mask)
     return (uint32_t)(k >> 40) & mask;
 }
 
-// the final write of one band with 64-bit numbers through the map (numbers
-// mode; ignored pixels 0)
-void launch_final64(const Geom &g, const Work &w, int64_t *out, const Map64 &m, hipStream_t s);
+// the final write of one band with 64-bit numbers through the map (ignored
+// pixels 0), or with leaders (lead: the band's workspace was numbered with
+// keys, number == 2 in resolve; ignored pixels -1)
+void launch_final64(const Geom &g, const Work &w, int64_t *out, const Map64 &m, int lead,
+                    hipStream_t s);
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
                          hipStream_t s);
 void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g, const Work &w,

@@ -1799,6 +1799,9 @@ __global__ __launch_bounds__(BLOCK) void resolve_kernel(Geom g, Work w, int numb
             w.hdr[t].value = val;  // a one-colour tile's only node
         else
             w.nval[(size_t)t * KMAX + (node & 0xFFu)] = val;
+        // number == 2: the node's record also takes its root's (the key of the
+        // region's leader), for leaders written from a numbered labelling
+        if (number == 2 && root != node) g_min(node_rec(w, node), rrec);
         // statistics: each region with a seam node has one root node, which
         // opens its record (the tiles' parts are added later); the other nodes
         // mark the root's record as shared.  Every such store writes the same
@@ -2178,7 +2181,8 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
         // node's, unless the tile is the whole image)
         const bool seam = tp.ty > 0 || tp.tx > 0 || y0 + TH < g.H || x0 + TW < W;
         uint32_t v = uv.y;
-        if (!seam) v = number ? 1u + h.pre : (uint32_t)(y0 * W + x0);
+        if (!seam) v = number == 1 ? 1u + h.pre : (uint32_t)(y0 * W + x0);
+        else if (number == 2) v = (uint32_t)(h.rec >> 32) & 0x7FFFFFFFu;  // its root's key
         if (uv.x & KIND_IGNORED) v = ignv;
         if (x4) {
             const int4 v4 = make_int4((int)v, (int)v, (int)v, (int)v);
@@ -2208,8 +2212,8 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     // every record of the tile is requested before any is used, so that their
     // latencies overlap
     const uint64_t mk = lane < TH ? w.runmask[t32 + lane] : 0ull;
-    const uint64_t ld = (number && lane < TH) ? w.leadmask[t32 + lane] : 0ull;
-    const uint32_t pr = (number && lane < TH) ? w.seg[t32 + lane] : 0u;
+    const uint64_t ld = (number == 1 && lane < TH) ? w.leadmask[t32 + lane] : 0ull;
+    const uint32_t pr = (number == 1 && lane < TH) ? w.seg[t32 + lane] : 0u;
     uint64_t used[KMAX / 64];
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word) used[word] = h.used[word];
@@ -2222,6 +2226,13 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word)
         nv[word] = __builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)(word * 64 + lane) * 4u, 0, 0);
+    if (number == 2) {  // leaders: each seam node's value is its root's key
+#pragma unroll
+        for (int word = 0; word < KMAX / 64; ++word) {
+            const uint32_t i = (uint32_t)(word * 64 + lane);
+            nv[word] = i < nslots ? (uint32_t)(w.gp[(size_t)t * KMAX + i] >> 32) & 0x7FFFFFFFu : 0u;
+        }
+    }
     const uint32_t nl = R < DLAB ? R : DLAB;
     // two 16-bit records per dword: lane l of load j holds runs 2(l + 64j) and
     // 2(l + 64j) + 1 (the bound is rounded up to whole dwords; a run past nl is
@@ -2250,7 +2261,7 @@ __global__ __launch_bounds__(BLOCK) void final_write_kernel(Geom g, Work w, int3
     auto run_label = [&](uint32_t info) -> uint32_t {
         if (info & INFO_BORDER) return nodev[info & 0xFFu];
         const uint32_t row = info >> 6, col = info & 63u;
-        if (number) return 1u + pre[row] + popc64(lead[row] & mask_lt((int)col));
+        if (number == 1) return 1u + pre[row] + popc64(lead[row] & mask_lt((int)col));
         return (uint32_t)((y0 + row) * W + x0 + col);
     };
 #pragma unroll
@@ -2315,10 +2326,12 @@ __device__ __forceinline__ void store2_i64(int64_t *p, int64_t a, int64_t b)
     __builtin_nontemporal_store(vv, (int4v *)p);
 }
 
+template <bool LEAD>
 __global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, int64_t *out, Map64 m)
 {
     __shared__ int64_t sLab[NWAVES][DLAB];
     __shared__ uint32_t sNode[NWAVES][KMAX + 1];
+    __shared__ uint32_t sKey[LEAD ? NWAVES : 1][KMAX + 1];  // leaders: each seam node's root key
     __shared__ uint64_t sLead[NWAVES][TH];
     __shared__ uint32_t sPre[NWAVES][TH];
 
@@ -2337,12 +2350,14 @@ __global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, in
     // band-local number n to the picture's number (0: an ignored pixel), in
     // two steps so that many can be in flight: the mask and prefix words of n,
     // then (merged numbers only) its entry
+    // (leaders: the band-local leader key travels with n; an ignored pixel,
+    // n = 0, is -1)
     struct Pend {
         uint64_t word;
-        uint32_t pre, n;
+        uint32_t pre, n, key;
     };
-    auto map_load = [&](uint32_t n) -> Pend {
-        Pend q{0ull, 0u, n};
+    auto map_load = [&](uint32_t n, uint32_t key) -> Pend {
+        Pend q{0ull, 0u, n, key};
         if (n != 0u && m.merges) {
             q.word = m.M[n >> 6];
             q.pre = m.Mpre[n >> 6];
@@ -2350,12 +2365,13 @@ __global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, in
         return q;
     };
     auto map_done = [&](const Pend &q) -> int64_t {
-        if (q.n == 0u || !m.merges) return (int64_t)q.n;
+        if (q.n == 0u) return LEAD ? -1 : 0;
+        if (!m.merges) return LEAD ? (int64_t)q.key : (int64_t)q.n;
         const uint32_t r = q.pre + popc64(q.word & mask_lt((int)(q.n & 63u)));
         if ((q.word >> (q.n & 63u)) & 1ull) return m.MV[r];
-        return G + (int64_t)q.n - (int64_t)r;
+        return LEAD ? m.base + (int64_t)q.key : G + (int64_t)q.n - (int64_t)r;
     };
-    auto map = [&](uint32_t n) -> int64_t { return map_done(map_load(n)); };
+    auto map = [&](uint32_t n, uint32_t key) -> int64_t { return map_done(map_load(n, key)); };
     const TileHdr &h = w.hdr[t];
     const uint2 uv = *(const uint2 *)&h;  // kind, value
 
@@ -2364,7 +2380,9 @@ __global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, in
         uint32_t v = uv.y;
         if (!seam) v = 1u + h.pre;
         if (uv.x & KIND_IGNORED) v = 0u;
-        const int64_t v64 = map(v);
+        // (leaders: its root's key, or its first pixel if the tile is the band)
+        const uint32_t key = seam ? (uint32_t)(h.rec >> 32) & 0x7FFFFFFFu : (uint32_t)(y0 * W + x0);
+        const int64_t v64 = map(v, key);
         if (x4) {
             for (int y = lane >> 5; y < tp.vh; y += 2) store2_i64(o0 + y * W + 2 * (lane & 31), v64, v64);
         } else if (lane_ok) {
@@ -2402,9 +2420,21 @@ __global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, in
         lead[lane] = ld;
         pre[lane] = pr;
     }
+    uint32_t nk[KMAX / 64] = {0u, 0u, 0u};
+    if constexpr (LEAD) {
+#pragma unroll
+        for (int word = 0; word < KMAX / 64; ++word) {
+            const uint32_t i = (uint32_t)(word * 64 + lane);
+            nk[word] = i < nslots ? (uint32_t)(w.gp[(size_t)t * KMAX + i] >> 32) & 0x7FFFFFFFu : 0u;
+        }
+    }
+    uint32_t *nodek = sKey[LEAD ? wave : 0];
 #pragma unroll
     for (int word = 0; word < KMAX / 64; ++word)
-        if ((used[word] >> lane) & 1ull) nodev[word * 64 + lane] = nv[word];
+        if ((used[word] >> lane) & 1ull) {
+            nodev[word * 64 + lane] = nv[word];
+            if (LEAD) nodek[word * 64 + lane] = nk[word];
+        }
     if (lane == 0) nodev[IGN_SLOT] = 0u;  // runs of an ignored colour
     __syncwarp();
     auto run_number = [&](uint32_t inf) -> uint32_t {
@@ -2412,12 +2442,21 @@ __global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, in
         const uint32_t row = inf >> 6, col = inf & 63u;
         return 1u + pre[row] + popc64(lead[row] & mask_lt((int)col));
     };
+    // leaders: the band-local key of the run's leader (a run of an ignored
+    // colour has none, and its number 0 decides)
+    auto run_key = [&](uint32_t inf) -> uint32_t {
+        if (!LEAD) return 0u;
+        if (inf & INFO_BORDER) return (inf & 0xFFu) < IGN_SLOT ? nodek[inf & 0xFFu] : 0u;
+        const uint32_t row = inf >> 6, col = inf & 63u;
+        return (uint32_t)((y0 + row) * W + x0 + col);
+    };
     Pend pq[DLAB / 64];  // the lane's staged runs, all requested before any is used
 #pragma unroll
     for (int j = 0; j < DLAB / 128; ++j) {
         const uint32_t r = 2u * ((uint32_t)lane + 64u * (uint32_t)j);
-        pq[2 * j] = map_load(r < nl ? run_number(info[j] & 0xFFFFu) : 0u);
-        pq[2 * j + 1] = map_load(r + 1u < nl ? run_number(info[j] >> 16) : 0u);
+        const uint32_t i0 = info[j] & 0xFFFFu, i1 = info[j] >> 16;
+        pq[2 * j] = map_load(r < nl ? run_number(i0) : 0u, run_key(i0));
+        pq[2 * j + 1] = map_load(r + 1u < nl ? run_number(i1) : 0u, run_key(i1));
     }
 #pragma unroll
     for (int j = 0; j < DLAB / 128; ++j) {
@@ -2437,7 +2476,9 @@ __global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, in
     const uint32_t rex = inc - cnt;
     const uint32_t mlo = (uint32_t)mk, mhi = (uint32_t)(mk >> 32);
     auto label_of = [&](uint32_t run) -> int64_t {
-        return run < (uint32_t)DLAB ? lab[run] : map(run_number(rinfo[run]));
+        if (run < (uint32_t)DLAB) return lab[run];
+        const uint32_t inf = rinfo[run];
+        return map(run_number(inf), run_key(inf));
     };
     if (x4) {
         const int c2 = 2 * (lane & 31);
@@ -3059,10 +3100,15 @@ void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s, Reg
                        so, tpw);
 }
 
-void launch_final64(const Geom &g, const Work &w, int64_t *out, const Map64 &m, hipStream_t s)
+void launch_final64(const Geom &g, const Work &w, int64_t *out, const Map64 &m, int lead,
+                    hipStream_t s)
 {
-    hipLaunchKernelGGL(final_write64_kernel, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0, s, g,
-                       w, out, m);
+    if (lead)
+        hipLaunchKernelGGL(final_write64_kernel<true>, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK),
+                           0, s, g, w, out, m);
+    else
+        hipLaunchKernelGGL(final_write64_kernel<false>, dim3(grid_of(g.ntiles, NWAVES)),
+                           dim3(BLOCK), 0, s, g, w, out, m);
 }
 
 void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32_t ignv,

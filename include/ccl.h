@@ -294,10 +294,9 @@ int ccl_label_stats(const void *colours, int dtype, int64_t batch, int64_t heigh
  * and band height (256-byte aligned; its first 4 bytes are the error word, as
  * for ccl_workspace_bytes).  Pure host arithmetic.  Returns 0 for an empty
  * batch and SIZE_MAX for a shape or band height ccl_label_large rejects.
- * Enough for leaders (about 4 bytes per pixel of one image plus the tile
- * pipeline's workspace for one band) and for numbers (the tile pipeline's
- * workspace for every band, about 4 bytes per pixel, plus each seam's two
- * tile rows of numbers and tables of a few bytes per seam pixel).
+ * The same for leaders and numbers: the tile pipeline's workspace for every
+ * band of one image (about 4 bytes per pixel), each seam's two tile rows of
+ * numbers and of leaders, and tables of a few bytes per seam pixel.
  */
 size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, int64_t band_rows);
 
@@ -316,12 +315,11 @@ size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, i
  *   counts     device int64 [batch] or NULL: regions per image
  *   workspace  device, at least ccl_large_workspace_bytes(batch, height, width,
  *              band_rows)
- * The image is cut into bands of band_rows rows; each band is labelled by the
- * pipeline of ccl_label, then regions are joined across the band seams and the
- * 64-bit results written.  With CCL_NUMBER each band numbers its own regions,
- * the regions that continue across a seam are joined by (band, number), and
- * each band's final write turns its numbers into the picture's as it writes
- * them.  Images of a batch are labelled one after another.
+ * The image is cut into bands of band_rows rows; each band numbers its own
+ * regions with the pipeline of ccl_label, the regions that continue across a
+ * seam are joined by (band, number), and each band's final write turns its
+ * numbers, or its leaders, into the picture's as it writes them (no 32-bit
+ * array over the picture).  Images of a batch are labelled one after another.
  * CCL_ERR_TOO_LARGE: height*width*batch > 2^46, or a band of 64 rows is wider
  * than 2^31-1 pixels.  Memory, streams and errors as for ccl_label.
  */
