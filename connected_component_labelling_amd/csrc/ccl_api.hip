@@ -508,7 +508,8 @@ const char *ccl_status_string(int status)
     case CCL_ERR_FLAGS: return "unknown flag bits";
     case CCL_ERR_IGNORE: return "ignored colour does not fit the dtype";
     case CCL_ERR_BAND:
-        return "band_rows must be a non-negative multiple of 64 with band_rows*width < 2^31";
+        return "band_rows must be a non-negative multiple of 64 (ccl_label_large, with "
+               "band_rows*width < 2^31) or of 32 (ccl_label_host)";
     case CCL_ERR_SCRATCH: return "batch needs more workspace than the static scratch array holds";
     case CCL_ERR_STREAM: return "the copy streams must be two streams other than the call's stream";
     default: return "unknown status";

@@ -63,7 +63,9 @@ typedef enum {
     CCL_ERR_IGNORE = -9,        /* CCL_IGNORE with a value wider than the pixel:
                                    above 255 (CCL_U8) or 0xFFFFFF (CCL_RGB24)        */
     CCL_ERR_BAND = -10,         /* ccl_label_large: band_rows negative, not a
-                                   multiple of 64, or band_rows*width > 2^31-1     */
+                                   multiple of 64, or band_rows*width > 2^31-1;
+                                   ccl_label_host: band_rows negative or not a
+                                   multiple of 32                                    */
     CCL_ERR_SCRATCH = -11,      /* ccl_label_noalloc: the batch needs more workspace
                                    than the static scratch array holds
                                    (ccl_workspace_bytes() > CCL_SCRATCH_BYTES)       */
@@ -320,8 +322,10 @@ size_t ccl_large_workspace_bytes(int64_t batch, int64_t height, int64_t width, i
  * seam are joined by (band, number), and each band's final write turns its
  * numbers, or its leaders, into the picture's as it writes them (no 32-bit
  * array over the picture).  Images of a batch are labelled one after another.
- * CCL_ERR_TOO_LARGE: height*width*batch > 2^46, or a band of 64 rows is wider
- * than 2^31-1 pixels.  Memory, streams and errors as for ccl_label.
+ * CCL_ERR_TOO_LARGE: height*width*batch > 2^46, a band of 64 rows is wider
+ * than 2^31-1 pixels, or the seams hold more than 2^31-3 pixels (2*width per
+ * seam: seam pixels have int32 ids).  Memory, streams and errors as for
+ * ccl_label.
  */
 int ccl_label_large(const void *colours, int dtype, int64_t batch, int64_t height, int64_t width,
                     int connectivity, int flags, uint32_t ignore, int64_t band_rows,
