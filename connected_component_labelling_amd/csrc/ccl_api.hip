@@ -100,6 +100,17 @@ static int check_shape(int64_t B, int64_t H, int64_t W, bool *empty)
     return CCL_OK;
 }
 
+// Images per pass: a batch with more tiles than seam node ids can name
+// (MAX_TILES) is labelled in passes of whole images, one after another on the
+// stream, all in one workspace sized for one pass.  0: one image alone has too
+// many tiles.
+static int64_t images_per_pass(int64_t B, int64_t H, int64_t W)
+{
+    const int64_t tpi = ((W + TW - 1) / TW) * ((H + TH - 1) / TH);
+    const int64_t per = MAX_TILES / tpi;
+    return per < B ? per : B;
+}
+
 static int finish_launches()
 {
     const hipError_t e = hipGetLastError();
@@ -138,29 +149,41 @@ static int label_impl(const void *colours, int dtype, int64_t B, int64_t H, int6
         return CCL_OK;
     }
     if (!colours || !out || !workspace) return CCL_ERR_NULL;
+    const int64_t per = images_per_pass(B, H, W);
     Layout L;
-    if (!make_layout(B, H, W, &L)) return CCL_ERR_TOO_LARGE;
+    if (per < 1 || !make_layout(per, H, W, &L)) return CCL_ERR_TOO_LARGE;
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
-    const Work w = bind_work(L, workspace);
     const int number = (flags & CCL_NUMBER) != 0;
     const bool need_scan = number || counts != nullptr;
+    const int64_t HW = H * W;
 
+    // (with several passes the events are recorded again by each: they time
+    // the last pass)
     auto mark = [&](int i) {
         if (events) (void)hipEventRecord((hipEvent_t)events[i], s);
     };
-    mark(0);
-    launch_tile(colours, dtype, conn, ign, ignore, L.g, w, 1, s);
-    mark(1);
-    launch_seam(L.g, w, conn, s);
-    mark(2);
-    if (need_scan) launch_seam_roots(L.g, w, s);
-    mark(3);
-    if (need_scan) launch_scan(L.g, w, counts, number, 1, s);
-    launch_resolve(L.g, w, number, s);
-    mark(4);
-    // ignored pixels: number 0, or leader -1 (label 0 in the leader + 1 form)
-    launch_final(L.g, w, out, number, number ? 0u : 0xFFFFFFFFu, s);
-    mark(5);
+    for (int64_t b0 = 0; b0 < B; b0 += per) {
+        Layout Lp = L;
+        if (B - b0 < per) make_layout(B - b0, H, W, &Lp);  // fits: fewer images
+        const Work w = bind_work(Lp, workspace);
+        const void *cp = (const char *)colours + (size_t)(b0 * HW) * (size_t)dtype;
+        int32_t *op = out + b0 * HW;
+        int32_t *np = counts ? counts + b0 : nullptr;
+        mark(0);
+        // the first pass's tile pass clears the error word for the whole call
+        launch_tile(cp, dtype, conn, ign, ignore, Lp.g, w, b0 == 0, s);
+        mark(1);
+        launch_seam(Lp.g, w, conn, s);
+        mark(2);
+        if (need_scan) launch_seam_roots(Lp.g, w, s);
+        mark(3);
+        if (need_scan) launch_scan(Lp.g, w, np, number, 1, s);
+        launch_resolve(Lp.g, w, number, s);
+        mark(4);
+        // ignored pixels: number 0, or leader -1 (label 0 in the leader + 1 form)
+        launch_final(Lp.g, w, op, number, number ? 0u : 0xFFFFFFFFu, s);
+        mark(5);
+    }
     return finish_launches();
 }
 
@@ -199,8 +222,10 @@ size_t ccl_workspace_bytes(int64_t batch, int64_t height, int64_t width)
     bool empty;
     if (check_shape(batch, height, width, &empty) != CCL_OK) return SIZE_MAX;
     if (empty) return 0;
+    // one pass of images (the whole batch unless it has 2^24 tiles or more)
+    const int64_t per = images_per_pass(batch, height, width);
     Layout L;
-    if (!make_layout(batch, height, width, &L)) return SIZE_MAX;
+    if (per < 1 || !make_layout(per, height, width, &L)) return SIZE_MAX;
     return L.total;
 }
 
@@ -234,8 +259,9 @@ int ccl_label_noalloc(const void *colours, int dtype, int64_t batch, int64_t hei
     void *ws = nullptr;
     if (!empty) {
         if (!colours || !out) return CCL_ERR_NULL;
+        const int64_t per = images_per_pass(batch, height, width);
         Layout L;
-        if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+        if (per < 1 || !make_layout(per, height, width, &L)) return CCL_ERR_TOO_LARGE;
         if (L.total > CCL_SCRATCH_BYTES) return CCL_ERR_SCRATCH;
         rc = scratch_address(&ws);
         if (rc != CCL_OK) return rc;
@@ -439,13 +465,19 @@ int ccl_number(const int32_t *leaders, int64_t batch, int64_t height, int64_t wi
         return CCL_OK;
     }
     if (!leaders || !labels || !workspace) return CCL_ERR_NULL;
+    const int64_t per = images_per_pass(batch, height, width);
     Layout L;
-    if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+    if (per < 1 || !make_layout(per, height, width, &L)) return CCL_ERR_TOO_LARGE;
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
-    const Work w = bind_work(L, workspace);
-    launch_leader_flags(leaders, L.g, w, 1, s);
-    launch_scan(L.g, w, counts, 1, 0, s);
-    launch_leader_assign(leaders, labels, L.g, w, s);
+    const int64_t HW = height * width;
+    for (int64_t b0 = 0; b0 < batch; b0 += per) {  // passes of whole images
+        Layout Lp = L;
+        if (batch - b0 < per) make_layout(batch - b0, height, width, &Lp);  // fits
+        const Work w = bind_work(Lp, workspace);
+        launch_leader_flags(leaders + b0 * HW, Lp.g, w, 1, b0 == 0, s);
+        launch_scan(Lp.g, w, counts ? counts + b0 : nullptr, 1, 0, s);
+        launch_leader_assign(leaders + b0 * HW, labels + b0 * HW, Lp.g, w, s);
+    }
     return finish_launches();
 }
 
@@ -465,12 +497,18 @@ int ccl_count(const int32_t *leaders, int64_t batch, int64_t height, int64_t wid
         return CCL_OK;
     }
     if (!leaders || !workspace) return CCL_ERR_NULL;
+    const int64_t per = images_per_pass(batch, height, width);
     Layout L;
-    if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+    if (per < 1 || !make_layout(per, height, width, &L)) return CCL_ERR_TOO_LARGE;
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
-    const Work w = bind_work(L, workspace);
-    launch_leader_flags(leaders, L.g, w, 0, s);
-    launch_scan(L.g, w, counts, 0, 0, s);
+    const int64_t HW = height * width;
+    for (int64_t b0 = 0; b0 < batch; b0 += per) {  // passes of whole images
+        Layout Lp = L;
+        if (batch - b0 < per) make_layout(batch - b0, height, width, &Lp);  // fits
+        const Work w = bind_work(Lp, workspace);
+        launch_leader_flags(leaders + b0 * HW, Lp.g, w, 0, b0 == 0, s);
+        launch_scan(Lp.g, w, counts + b0, 0, 0, s);
+    }
     return finish_launches();
 }
 

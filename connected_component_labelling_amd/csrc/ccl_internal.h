@@ -32,7 +32,9 @@ static_assert(KMAX <= 255, "seam slots are stored in one byte");
 // tile of several colours, whose records are gp[tile*KMAX + slot]; a one-colour
 // tile has one node, slot UNI_SLOT, whose record sits in its header.
 constexpr uint32_t UNI_SLOT = 255;
-constexpr int64_t MAX_TILES = int64_t(1) << 24;  // node ids are 32-bit
+// tiles of one pass of the pipeline: node ids (tile << 8 | slot) are 32-bit,
+// and a launch of one 256-thread workgroup per tile stays below 2^32 threads
+constexpr int64_t MAX_TILES = (int64_t(1) << 24) - 1;
 static_assert(TH == 32 && TW == 64, "row masks are one wave64 ballot, tile rows are lanes");
 
 // Bit layout of a per-run record (16 bits) written by the tile pass.
@@ -192,7 +194,7 @@ __device__ __forceinline__ uint32_t seam_hash(int64_t key, uint32_t mask)
 void launch_final64(const Geom &g, const Work &w, int64_t *out, const Map64 &m, int lead,
                     hipStream_t s);
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
-                         hipStream_t s);
+                         int clear_err, hipStream_t s);
 void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g, const Work &w,
                           hipStream_t s);
 // One region's statistics, laid out as ccl_region of the C ABI.

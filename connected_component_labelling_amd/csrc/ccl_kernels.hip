@@ -1607,12 +1607,12 @@ __device__ __forceinline__ void scan_counts(const Work &w, size_t t, uint32_t n,
 
 // apply = 0 only counts.
 __global__ __launch_bounds__(SCAN_BLOCK) void scan_kernel(Geom g, Work w, int32_t *counts, int apply,
-                                                     int use_hdr)
+                                                     int use_hdr, uint32_t band0)
 {
     __shared__ uint32_t sPart[TH][SCAN_GROUPS + 1];  // per row: each group's sum, then its prefix
     __shared__ uint32_t sRowPre[TH + 1];             // leaders of the earlier rows; [TH]: the band's
     __shared__ uint32_t sPre;                        // leaders of the earlier bands of the image
-    const uint32_t band = blockIdx.x;  // b * nty + ty
+    const uint32_t band = band0 + blockIdx.x;  // b * nty + ty
     const uint32_t b = fast_div(band, g.divNty), ty = band - b * (uint32_t)g.nty;
     const size_t t0 = (size_t)b * g.tpi + (size_t)ty * g.ntx;
     const uint32_t ntx = (uint32_t)g.ntx;
@@ -2511,9 +2511,10 @@ __global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, in
 // segment: a ballot of "leaders[p] == p".
 
 __global__ __launch_bounds__(BLOCK) void leader_flag_kernel(const int32_t *leaders, Geom g,
-                                                            Work w, int write_mask)
+                                                            Work w, int write_mask, int clear_err)
 {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *w.err = 0u;  // the call's first kernel
+    // the call's first kernel (of its first pass of images) clears the error word
+    if (clear_err && blockIdx.x == 0 && threadIdx.x == 0) *w.err = 0u;
     clear_bands(g, w);
     const int lane = lane_id();
     const uint64_t nsegs = (uint64_t)g.ntiles * TH;
@@ -2827,7 +2828,7 @@ __global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t 
     int64_t sum = 0;
     for (int64_t j = j0; j < j1; ++j) sum += a.counts[j];
     // (the counts of one batch add up to fewer than 2^32 regions: each needs a
-    // pixel and a batch has fewer than 2^24 tiles of 2048 pixels)
+    // pixel and a pass has fewer than 2^24 tiles of 2048 pixels)
     uint32_t total;
     const uint32_t ex = block_exclusive_scan((uint32_t)sum, sWave, total);
     int64_t run = ex;
@@ -2864,7 +2865,7 @@ __global__ __launch_bounds__(BLOCK) void image_offsets_kernel(const int32_t *cou
     int64_t sum = 0;
     for (int64_t j = j0; j < j1; ++j) sum += counts[j];
     // (a batch has fewer than 2^32 regions: each needs a pixel and a batch has
-    // fewer than 2^24 tiles of 2048 pixels)
+    // fewer than 2^24 tiles of 2048 pixels in a pass)
     uint32_t total;
     int64_t run = block_exclusive_scan((uint32_t)sum, sWave, total);
     for (int64_t j = j0; j < j1; ++j) {
@@ -3087,8 +3088,14 @@ void launch_seam_roots(const Geom &g, const Work &w, hipStream_t s)
 void launch_scan(const Geom &g, const Work &w, int32_t *counts, int apply, int use_hdr,
                  hipStream_t s)
 {
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)g.nbands), dim3(SCAN_BLOCK), 0, s, g, w, counts,
-                       apply, use_hdr);
+    // launches of at most 2^21 bands (a launch stays below 2^32 threads); a
+    // band's look-back finds the bands of earlier launches finished
+    constexpr int64_t PER_LAUNCH = int64_t(1) << 21;
+    for (int64_t b0 = 0; b0 < g.nbands; b0 += PER_LAUNCH) {
+        const int64_t n = g.nbands - b0 < PER_LAUNCH ? g.nbands - b0 : PER_LAUNCH;
+        hipLaunchKernelGGL(scan_kernel, dim3((unsigned)n), dim3(SCAN_BLOCK), 0, s, g, w, counts,
+                           apply, use_hdr, (uint32_t)b0);
+    }
 }
 
 void launch_resolve(const Geom &g, const Work &w, int number, hipStream_t s, RegionRec *rec,
@@ -3121,12 +3128,12 @@ void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32
 }
 
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
-                         hipStream_t s)
+                         int clear_err, hipStream_t s)
 {
     int64_t blocks = grid_of(g.ntiles * TH, NWAVES);
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(leader_flag_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, leaders, g,
-                       w, write_mask);
+                       w, write_mask, clear_err);
 }
 
 void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g, const Work &w,

@@ -51,10 +51,15 @@ typedef enum {
     CCL_OK = 0,
     CCL_ERR_NULL = -1,          /* a required pointer is NULL                        */
     CCL_ERR_SHAPE = -2,         /* batch, height or width is negative                */
-    CCL_ERR_TOO_LARGE = -3,     /* height*width > 2^31-1, or the batch has more
-                                   than 2^24 tiles: each image is cut into 64 x 32
+    CCL_ERR_TOO_LARGE = -3,     /* height*width > 2^31-1, or one image has 2^24
+                                   tiles or more: each image is cut into 64 x 32
                                    tiles, a partial one at the right or bottom edge
-                                   counting whole (2^24 full tiles: 34 Gpx)          */
+                                   counting whole (2^24 full tiles: 34 Gpx).  A
+                                   batch of more tiles is labelled in passes of
+                                   whole images by ccl_label, ccl_label_noalloc,
+                                   ccl_number and ccl_count; ccl_label_stats,
+                                   ccl_region_stats and ccl_label_host take fewer
+                                   than 2^24 tiles in all                            */
     CCL_ERR_CONNECTIVITY = -4,  /* connectivity is not 4 or 8                        */
     CCL_ERR_DTYPE = -5,         /* dtype is not CCL_U8, CCL_RGB24 or CCL_U32         */
     CCL_ERR_WORKSPACE = -6,     /* workspace smaller than ccl_workspace_bytes()      */
@@ -99,8 +104,12 @@ enum { CCL_NUMBER = 1, CCL_IGNORE = 2 };
 /*
  * Bytes of device workspace any call below needs for a batch of this shape.
  * Pure host arithmetic (no HIP call).  Returns 0 for an empty batch and
- * SIZE_MAX for a negative shape.  The workspace must be 256-byte aligned (any
- * HIP allocation is); its contents need no initialisation.
+ * SIZE_MAX for a negative shape or an image too large.  A batch of 2^24
+ * tiles or more (see CCL_ERR_TOO_LARGE) is labelled in passes of as many whole
+ * images as fit in 2^24 - 1 tiles, one after another on the stream in the same
+ * workspace, so the size is that of one such pass.  The workspace must be
+ * 256-byte aligned (any HIP allocation is); its contents need no
+ * initialisation.
  *
  * Error word.  The workspace's first 4 bytes are an error word.  Every call
  * that takes a workspace clears it in its first kernel, and sets bit 0
@@ -142,7 +151,9 @@ int ccl_label(const void *colours, int dtype, int64_t batch, int64_t height, int
  * and `events[i]` after stage i, for the stages tile labelling, seam merge,
  * seam collapse, numbering scan and final write (n_events >= 6; the scan
  * event is recorded even when no scan runs).  `events` is a host array of
- * hipEvent_t created by the caller.  Same results as ccl_label.
+ * hipEvent_t created by the caller.  Same results as ccl_label.  A batch
+ * labelled in several passes records the events again in each: they time the
+ * last pass.
  */
 int ccl_label_profiled(const void *colours, int dtype, int64_t batch, int64_t height,
                        int64_t width, int connectivity, int flags, uint32_t ignore,

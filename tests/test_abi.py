@@ -61,10 +61,15 @@ def test_workspace_bytes(lib):
     assert 0 < big < 8 * 24000 * 33600
     # per-image indices must fit in int32
     assert lib.ccl_workspace_bytes(1, 65536, 65536) == 2**64 - 1
-    # at most 2^24 tiles of 64 x 32 in the batch (a one-row image of 2^30 + 64
-    # pixels has 2^24 + 1 tiles; the largest square image is far below that)
-    assert lib.ccl_workspace_bytes(1, 1, 2**30 + 64) == 2**64 - 1
-    assert lib.ccl_workspace_bytes(1, 1, 2**30) < 2**64 - 1
+    # fewer than 2^24 tiles of 64 x 32 in one image (a one-row image of 2^30
+    # pixels has 2^24 tiles; the largest square image is far below that)
+    assert lib.ccl_workspace_bytes(1, 1, 2**30) == 2**64 - 1
+    assert lib.ccl_workspace_bytes(1, 1, 2**30 - 64) < 2**64 - 1
+    # a batch of more tiles runs in passes of whole images: one pass's workspace
+    one = lib.ccl_workspace_bytes(2**24 - 1, 2, 2)
+    assert lib.ccl_workspace_bytes(2**24, 2, 2) == one
+    assert lib.ccl_workspace_bytes(3 * 2**24, 2, 2) == one
+    assert lib.ccl_workspace_bytes(2**23, 64, 128) == lib.ccl_workspace_bytes(2**23 - 1, 64, 128)
     assert lib.ccl_workspace_bytes(1, 46340, 46340) < 2**64 - 1
 
 
