@@ -431,21 +431,31 @@ int ccl_label_stats(const void *colours, int dtype, int64_t batch, int64_t heigh
         return CCL_OK;
     }
     if (!colours || !out || !workspace) return CCL_ERR_NULL;
+    const int64_t per = images_per_pass(batch, height, width);
     Layout L;
-    if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+    if (per < 1 || !make_layout(per, height, width, &L)) return CCL_ERR_TOO_LARGE;
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
-    const Work w = bind_work(L, workspace);
     const int ign = (flags & CCL_IGNORE) != 0;
     static_assert(sizeof(ccl_region) == sizeof(RegionRec), "one record layout");
     RegionRec *rec = (RegionRec *)stats;
-    launch_tile(colours, dtype, connectivity, ign, ignore, L.g, w, 1, s);
-    launch_seam(L.g, w, connectivity, s);
-    launch_seam_roots(L.g, w, s);
-    launch_scan(L.g, w, counts, 1, 1, s);
-    launch_label_stats(L.g, w, counts, out, rec, stats_capacity, 0, s);  // first record per image
-    launch_resolve(L.g, w, 1, s, rec, stats_capacity);  // opens seam regions' records
-    launch_label_stats(L.g, w, counts, out, rec, stats_capacity, 1, s);  // numbers, records, parts
-    launch_label_stats(L.g, w, counts, out, rec, stats_capacity, 2, s);  // parts into the records
+    const int64_t HW = height * width;
+    for (int64_t b0 = 0; b0 < batch; b0 += per) {  // passes of whole images
+        Layout Lp = L;
+        if (batch - b0 < per) make_layout(batch - b0, height, width, &Lp);  // fits
+        const Work w = bind_work(Lp, workspace);
+        const void *cp = (const char *)colours + (size_t)(b0 * HW) * (size_t)dtype;
+        int32_t *op = out + b0 * HW, *np = counts + b0;
+        const int first = b0 == 0;
+        launch_tile(cp, dtype, connectivity, ign, ignore, Lp.g, w, first, s);
+        launch_seam(Lp.g, w, connectivity, s);
+        launch_seam_roots(Lp.g, w, s);
+        launch_scan(Lp.g, w, np, 1, 1, s);
+        // the first record of each image (after the earlier passes' regions)
+        launch_label_stats(Lp.g, w, np, op, rec, stats_capacity, 0, first, s);
+        launch_resolve(Lp.g, w, 1, s, rec, stats_capacity);  // opens seam regions' records
+        launch_label_stats(Lp.g, w, np, op, rec, stats_capacity, 1, first, s);  // numbers, parts
+        launch_label_stats(Lp.g, w, np, op, rec, stats_capacity, 2, first, s);  // parts in
+    }
     return finish_launches();
 }
 
@@ -523,12 +533,19 @@ int ccl_region_stats(const int32_t *labels, int64_t batch, int64_t height, int64
     if (n_total > 0 && !stats) return CCL_ERR_NULL;
     if (empty || n_total == 0) return CCL_OK;  // no pixel, or no region: nothing to write
     if (!labels || !counts || !workspace) return CCL_ERR_NULL;
+    const int64_t per = images_per_pass(batch, height, width);
     Layout L;
-    if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+    if (per < 1 || !make_layout(per, height, width, &L)) return CCL_ERR_TOO_LARGE;
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
-    const Work w = bind_work(L, workspace);
     static_assert(sizeof(ccl_region) == sizeof(RegionRec), "one record layout");
-    launch_region_stats(labels, counts, L.g, w, n_total, (RegionRec *)stats, (hipStream_t)stream);
+    const int64_t HW = height * width;
+    for (int64_t b0 = 0; b0 < batch; b0 += per) {  // passes of whole images
+        Layout Lp = L;
+        if (batch - b0 < per) make_layout(batch - b0, height, width, &Lp);  // fits
+        const Work w = bind_work(Lp, workspace);
+        launch_region_stats(labels + b0 * HW, counts + b0, Lp.g, w, n_total, (RegionRec *)stats,
+                            b0 == 0, (hipStream_t)stream);
+    }
     return finish_launches();
 }
 

@@ -204,15 +204,19 @@ struct RegionRec {
 };
 static_assert(sizeof(RegionRec) == 40, "40-byte region records");
 
-// per-region statistics of a numbered labelling; the workspace's band-status
-// words hold the first record of each image (B int64 fit in its B*nty words)
+// per-region statistics of a numbered labelling, one pass of images (first:
+// the batch's first pass, which sets all n_total records empty); the
+// workspace's band-status words hold the first record of each image of the
+// pass (B int64 fit in its B*nty words), counted on from the earlier passes'
 void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geom &g,
-                         const Work &w, int64_t n_total, RegionRec *recs, hipStream_t s);
+                         const Work &w, int64_t n_total, RegionRec *recs, int first,
+                         hipStream_t s);
 // statistics of the labelling call: stage 0 the first record of each image
-// (into the band-status words, after the scan), stage 1 the final write with
-// statistics (numbers into out), stage 2 the reduce pass
+// (into the band-status words, after the scan; first: the batch's first pass
+// of images), stage 1 the final write with statistics (numbers into out),
+// stage 2 the reduce pass
 void launch_label_stats(const Geom &g, const Work &w, const int32_t *counts, int32_t *out,
-                        RegionRec *rec, int64_t cap, int stage, hipStream_t s);
+                        RegionRec *rec, int64_t cap, int stage, int first, hipStream_t s);
 void launch_zero_i32(int32_t *p, int64_t n, hipStream_t s);
 
 }  // namespace ccl

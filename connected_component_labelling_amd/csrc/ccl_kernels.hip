@@ -2806,11 +2806,16 @@ __global__ __launch_bounds__(BLOCK) void stats_kernel(StatsArgs a)
 
 // Entries of every region start empty (area 0, box (INT32_MAX, INT32_MAX, -1,
 // -1), sums 0); block 0 also writes the first entry of each image.
-__global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t n_total,
-                                                           int64_t *off, uint32_t *err)
+// Records of the first n_init regions set empty, and the first record of each
+// image of the pass: after *carry records (the regions of the batch's earlier
+// passes; 0 for the first pass), and *carry advanced past this pass's.
+__global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t n_init,
+                                                           int64_t *off, uint32_t *err,
+                                                           int64_t *carry, int first)
 {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0u;  // the call's first kernel
-    for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < n_total;
+    // the call's first kernel (of its first pass of images)
+    if (first && blockIdx.x == 0 && threadIdx.x == 0) *err = 0u;
+    for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < n_init;
          i += (int64_t)gridDim.x * BLOCK) {
         uint64_t *r = (uint64_t *)&a.rec[i];
         r[0] = r[1] = 0ull;                                      // sums
@@ -2822,20 +2827,22 @@ __global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t 
     // exclusive prefix of the counts: thread j sums its chunk, a workgroup scan
     // of the chunk sums, then each thread writes its chunk's prefixes
     __shared__ uint32_t sWave[NWAVES];
+    const int64_t base = first ? 0 : *carry;  // (read before the scan's barriers)
     const int64_t B = a.B;
     const int64_t per = (B + BLOCK - 1) / BLOCK;
     const int64_t j0 = (int64_t)threadIdx.x * per, j1 = min(B, j0 + per);
     int64_t sum = 0;
     for (int64_t j = j0; j < j1; ++j) sum += a.counts[j];
-    // (the counts of one batch add up to fewer than 2^32 regions: each needs a
+    // (the counts of one pass add up to fewer than 2^32 regions: each needs a
     // pixel and a pass has fewer than 2^24 tiles of 2048 pixels)
     uint32_t total;
     const uint32_t ex = block_exclusive_scan((uint32_t)sum, sWave, total);
-    int64_t run = ex;
+    int64_t run = base + ex;
     for (int64_t j = j0; j < j1; ++j) {
         off[j] = run;
         run += a.counts[j];
     }
+    if (threadIdx.x == 0) *carry = base + total;
 }
 
 // ------------------------------------ statistics in the labelling call
@@ -2856,10 +2863,15 @@ __global__ __launch_bounds__(BLOCK) void stats_init_kernel(StatsArgs a, int64_t 
 //     atomics per group.
 
 // first record of each image: exclusive prefix of the per-image region counts
+// the first record of each image of the pass (after *carry records of the
+// batch's earlier passes; 0 for the first), and *carry advanced past this
+// pass's regions
 __global__ __launch_bounds__(BLOCK) void image_offsets_kernel(const int32_t *counts, int64_t B,
-                                                             int64_t *off)
+                                                             int64_t *off, int64_t *carry,
+                                                             int first)
 {
     __shared__ uint32_t sWave[NWAVES];
+    const int64_t base = first ? 0 : *carry;  // (read before the scan's barriers)
     const int64_t per = (B + BLOCK - 1) / BLOCK;
     const int64_t j0 = (int64_t)threadIdx.x * per, j1 = min(B, j0 + per);
     int64_t sum = 0;
@@ -2867,11 +2879,12 @@ __global__ __launch_bounds__(BLOCK) void image_offsets_kernel(const int32_t *cou
     // (a batch has fewer than 2^32 regions: each needs a pixel and a batch has
     // fewer than 2^24 tiles of 2048 pixels in a pass)
     uint32_t total;
-    int64_t run = block_exclusive_scan((uint32_t)sum, sWave, total);
+    int64_t run = base + block_exclusive_scan((uint32_t)sum, sWave, total);
     for (int64_t j = j0; j < j1; ++j) {
         off[j] = run;
         run += counts[j];
     }
+    if (threadIdx.x == 0) *carry = base + total;
 }
 
 constexpr int RD_CAP = 1024;   // regions of a block gathered in LDS
@@ -3145,8 +3158,13 @@ void launch_leader_assign(const int32_t *leaders, int32_t *labels, const Geom &g
                        labels, g, w);
 }
 
+// the regions counted by the batch's passes so far, carried from pass to pass
+// in the workspace's first 256 bytes (after the error word), which every
+// pass's layout shares
+static int64_t *pass_carry(const Work &w) { return (int64_t *)((char *)w.err + 8); }
+
 void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geom &g,
-                         const Work &w, int64_t n_total, RegionRec *recs, hipStream_t s)
+                         const Work &w, int64_t n_total, RegionRec *recs, int first, hipStream_t s)
 {
     StatsArgs a;
     a.labels = labels;
@@ -3160,22 +3178,24 @@ void launch_region_stats(const int32_t *labels, const int32_t *counts, const Geo
     a.n_total = n_total;
     a.ay = (uint32_t)((g.H + ST_ROWS - 1) / ST_ROWS);
     a.ax = (uint32_t)((g.W + ST_COLS - 1) / ST_COLS);
-    int64_t iblocks = grid_of(n_total, BLOCK);
+    // the first pass sets every record empty
+    const int64_t n_init = first ? n_total : 0;
+    int64_t iblocks = grid_of(n_init, BLOCK);
     if (iblocks > 4096) iblocks = 4096;
     if (iblocks < 1) iblocks = 1;
-    hipLaunchKernelGGL(stats_init_kernel, dim3((unsigned)iblocks), dim3(BLOCK), 0, s, a, n_total,
-                       (int64_t *)w.bandst, w.err);
+    hipLaunchKernelGGL(stats_init_kernel, dim3((unsigned)iblocks), dim3(BLOCK), 0, s, a, n_init,
+                       (int64_t *)w.bandst, w.err, pass_carry(w), first);
     const int64_t blocks = g.B * (int64_t)a.ay * (int64_t)a.ax;
     hipLaunchKernelGGL(stats_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, a);
 }
 
 void launch_label_stats(const Geom &g, const Work &w, const int32_t *counts, int32_t *out,
-                        RegionRec *rec, int64_t cap, int stage, hipStream_t s)
+                        RegionRec *rec, int64_t cap, int stage, int first, hipStream_t s)
 {
     const StatsOut so{rec, cap, (const int64_t *)w.bandst};
     if (stage == 0) {
         hipLaunchKernelGGL(image_offsets_kernel, dim3(1), dim3(BLOCK), 0, s, counts, g.B,
-                           (int64_t *)w.bandst);
+                           (int64_t *)w.bandst, pass_carry(w), first);
     } else if (stage == 1) {
         hipLaunchKernelGGL(final_write_kernel<true>, dim3(grid_of(g.ntiles, NWAVES)), dim3(BLOCK), 0,
                            s, g, w, out, 1, 0u, 0u, (uint32_t)g.ntiles, so);

@@ -56,10 +56,8 @@ typedef enum {
                                    tiles, a partial one at the right or bottom edge
                                    counting whole (2^24 full tiles: 34 Gpx).  A
                                    batch of more tiles is labelled in passes of
-                                   whole images by ccl_label, ccl_label_noalloc,
-                                   ccl_number and ccl_count; ccl_label_stats,
-                                   ccl_region_stats and ccl_label_host take fewer
-                                   than 2^24 tiles in all                            */
+                                   whole images by every call but ccl_label_host,
+                                   which takes fewer than 2^24 tiles in all          */
     CCL_ERR_CONNECTIVITY = -4,  /* connectivity is not 4 or 8                        */
     CCL_ERR_DTYPE = -5,         /* dtype is not CCL_U8, CCL_RGB24 or CCL_U32         */
     CCL_ERR_WORKSPACE = -6,     /* workspace smaller than ccl_workspace_bytes()      */

@@ -1,10 +1,11 @@
 """GPU parity of a batch with more tiles than one pass of the pipeline takes
 (2^24 - 1: seam node ids are 32-bit, and a launch of one 256-thread workgroup
-per tile stays below 2^32 threads): ccl_label, ccl_number and ccl_count take
-it in passes of whole images, one after another in one workspace sized for a
+per tile stays below 2^32 threads): ccl_label, ccl_number, ccl_count,
+ccl_label_stats and ccl_region_stats take it in passes of whole images, one after another in one workspace sized for a
 pass.  2^24 + 3 pictures of 2 x 2 pixels (one tile each): the first pass holds
 2^24 - 1 images, the second the last four.  Its 2^24 + 3 tile rows also take
-the numbering scan over several launches.
+the numbering scan over several launches; the statistics calls carry the
+regions of the first pass into the records of the second.
 
 Expected values: the oracle on images from both passes, and for every image a
 closed form that holds for any 2 x 2 picture with 8 neighbours (every two of
@@ -39,6 +40,39 @@ def closed_form_2x2(c: np.ndarray):
     numbers = np.take_along_axis(upto, leaders, axis=1)
     counts = is_leader.sum(axis=1, dtype=np.int32)
     return leaders, numbers, counts
+
+
+def closed_form_stats_2x2(numbers: np.ndarray, counts: np.ndarray):
+    """Records (area, y0, x0, y1, x1, sum_y, sum_x) of every region of 2 x 2
+    pictures, regions of all images concatenated: pixel p sits at row p // 2,
+    column p % 2."""
+    B = numbers.shape[0]
+    off = np.zeros(B, np.int64)
+    np.cumsum(counts[:-1], out=off[1:])
+    n = int(counts.sum(dtype=np.int64))
+    rec = np.zeros((n, 7), np.int64)
+    ys = np.array([0, 0, 1, 1], np.int64)
+    xs = np.array([0, 1, 0, 1], np.int64)
+    big = np.int64(1 << 40)
+    for k in range(1, 5):
+        m = numbers == k
+        has = m.any(axis=1)
+        idx = off[has] + (k - 1)
+        mk = m[has]
+        rec[idx, 0] = mk.sum(axis=1)
+        rec[idx, 1] = np.where(mk, ys, big).min(axis=1)
+        rec[idx, 2] = np.where(mk, xs, big).min(axis=1)
+        rec[idx, 3] = np.where(mk, ys, -1).max(axis=1)
+        rec[idx, 4] = np.where(mk, xs, -1).max(axis=1)
+        rec[idx, 5] = (mk * ys).sum(axis=1)
+        rec[idx, 6] = (mk * xs).sum(axis=1)
+    return off, rec
+
+
+def gpu_records(stats) -> np.ndarray:
+    bbox = stats["bbox"].cpu().numpy().astype(np.int64)
+    return np.column_stack([stats["area"].cpu().numpy().astype(np.int64), bbox,
+                            stats["sum_y"].cpu().numpy(), stats["sum_x"].cpu().numpy()])
 
 
 @pytest.mark.timeout(600)
@@ -76,5 +110,27 @@ def test_batch_beyond_tile_limit(ccl):
     assert np.array_equal(numbered.cpu().numpy().reshape(B, 4), exp_numbers)
     for cnt in (c0, c1, c2, c3):
         assert np.array_equal(cnt.cpu().numpy(), exp_counts)
-    del t, ws, leaders, labels, numbered
+    del leaders, numbered
+
+    # statistics: the records of the second pass's images follow those of
+    # the first pass, in both statistics calls
+    off, exp_rec = closed_form_stats_2x2(exp_numbers, exp_counts)
+    n_total = exp_rec.shape[0]
+    for sl in (slice(0, 2000), slice(TILES - 1000, B)):  # the closed form against the oracle
+        o = oracle.region_stats(exp_numbers[sl].reshape(-1, 2, 2), exp_counts[sl])
+        lo = int(off[sl.start])
+        hi = lo + int(exp_counts[sl].sum(dtype=np.int64))
+        orec = np.column_stack([o["area"], o["bbox"], o["sum_y"], o["sum_x"]]).astype(np.int64)
+        assert np.array_equal(orec, exp_rec[lo:hi])
+    print(f"[gpu case] batch passes: region_stats and label_stats, {n_total} records", flush=True)
+    st = ccl.region_stats(labels, c1, n_total=n_total, workspace=ws)
+    torch.cuda.synchronize()
+    assert ccl.error_word(ws) == 0
+    assert np.array_equal(gpu_records(st), exp_rec)
+    del st
+    labels2, c4, st2 = ccl.label_stats(t, n_total, 8, workspace=ws, check=True)
+    assert np.array_equal(c4.cpu().numpy(), exp_counts)
+    assert np.array_equal(labels2.cpu().numpy().reshape(B, 4), exp_numbers)
+    assert np.array_equal(gpu_records(st2), exp_rec)
+    del t, ws, labels, labels2, st2
     torch.cuda.empty_cache()
