@@ -292,8 +292,12 @@ int ccl_label_host(const void *host_colours, int dtype, int64_t batch, int64_t h
     if (h2d_stream == nullptr || d2h_stream == nullptr || h2d_stream == stream ||
         d2h_stream == stream || h2d_stream == d2h_stream)
         return CCL_ERR_STREAM;
+    // the workspace of one pass of images, as for ccl_label: every group of
+    // images below is labelled in it in turn, and a group never has more
+    // tiles than a pass (a group of several images has fewer than 2^23)
+    const int64_t per = images_per_pass(batch, height, width);
     Layout L;
-    if (!make_layout(batch, height, width, &L)) return CCL_ERR_TOO_LARGE;
+    if (per < 1 || !make_layout(per, height, width, &L)) return CCL_ERR_TOO_LARGE;
     if (workspace_bytes < L.total) return CCL_ERR_WORKSPACE;
     hipStream_t sin = (hipStream_t)h2d_stream, sout = (hipStream_t)d2h_stream;
     const int ign = (flags & CCL_IGNORE) != 0;
@@ -369,7 +373,7 @@ int ccl_label_host(const void *host_colours, int dtype, int64_t batch, int64_t h
     for (int64_t j = 0; j < ngroup && ok; ++j) {
         const int64_t b0 = j * per_group, nb = batch - b0 < per_group ? batch - b0 : per_group;
         Layout Lg;
-        make_layout(nb, height, width, &Lg);  // fits: it is part of the whole batch
+        make_layout(nb, height, width, &Lg);  // fits: no more tiles than a pass
         const Geom &g = Lg.g;
         const Work w = bind_work(Lg, workspace);
         const char *img = (const char *)dev_colours + (size_t)(b0 * HW) * bpp;

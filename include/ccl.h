@@ -56,8 +56,8 @@ typedef enum {
                                    tiles, a partial one at the right or bottom edge
                                    counting whole (2^24 full tiles: 34 Gpx).  A
                                    batch of more tiles is labelled in passes of
-                                   whole images by every call but ccl_label_host,
-                                   which takes fewer than 2^24 tiles in all          */
+                                   whole images (ccl_label_host: in its groups of
+                                   images, in the same workspace)                    */
     CCL_ERR_CONNECTIVITY = -4,  /* connectivity is not 4 or 8                        */
     CCL_ERR_DTYPE = -5,         /* dtype is not CCL_U8, CCL_RGB24 or CCL_U32         */
     CCL_ERR_WORKSPACE = -6,     /* workspace smaller than ccl_workspace_bytes()      */

@@ -1,7 +1,8 @@
 """GPU parity of a batch with more tiles than one pass of the pipeline takes
 (2^24 - 1: seam node ids are 32-bit, and a launch of one 256-thread workgroup
 per tile stays below 2^32 threads): ccl_label, ccl_number, ccl_count,
-ccl_label_stats and ccl_region_stats take it in passes of whole images, one after another in one workspace sized for a
+ccl_label_stats and ccl_region_stats take it in passes of whole images
+(ccl_label_host in its groups of images), one after another in one workspace sized for a
 pass.  2^24 + 3 pictures of 2 x 2 pixels (one tile each): the first pass holds
 2^24 - 1 images, the second the last four.  Its 2^24 + 3 tile rows also take
 the numbering scan over several launches; the statistics calls carry the
@@ -133,4 +134,13 @@ def test_batch_beyond_tile_limit(ccl):
     assert np.array_equal(labels2.cpu().numpy().reshape(B, 4), exp_numbers)
     assert np.array_equal(gpu_records(st2), exp_rec)
     del t, ws, labels, labels2, st2
+    torch.cuda.empty_cache()
+
+    # from page-locked host memory, in groups of images in one pass's workspace
+    print("[gpu case] batch passes: label_host", flush=True)
+    host = torch.from_numpy(img).pin_memory()
+    hl, hc = ccl.label_host(host, 8, number=True)
+    assert np.array_equal(hl.numpy().reshape(B, 4), exp_numbers)
+    assert np.array_equal(hc.cpu().numpy(), exp_counts)
+    del host, hl, hc
     torch.cuda.empty_cache()
