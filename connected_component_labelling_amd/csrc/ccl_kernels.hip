@@ -2510,6 +2510,12 @@ __global__ __launch_bounds__(BLOCK) void final_write64_kernel(Geom g, Work w, in
 // tile-major layout so that the same scan numbers them.  One wave per row
 // segment: a ballot of "leaders[p] == p".
 
+// Each wave takes LF_U consecutive row segments of one tile at a time (the
+// segment count per tile, 32, is a multiple of LF_U), all their loads issued
+// before the first ballot.
+constexpr int LF_U = 8;
+static_assert(TH % LF_U == 0, "a wave's segments lie in one tile");
+
 __global__ __launch_bounds__(BLOCK) void leader_flag_kernel(const int32_t *leaders, Geom g,
                                                             Work w, int write_mask, int clear_err)
 {
@@ -2519,21 +2525,44 @@ __global__ __launch_bounds__(BLOCK) void leader_flag_kernel(const int32_t *leade
     const int lane = lane_id();
     const uint64_t nsegs = (uint64_t)g.ntiles * TH;
     const uint64_t nw = (uint64_t)gridDim.x * NWAVES;
-    for (uint64_t sgi = (uint64_t)blockIdx.x * NWAVES + (threadIdx.x >> 6); sgi < nsegs; sgi += nw) {
-        const uint32_t t = (uint32_t)(sgi / TH), y = (uint32_t)(sgi % TH);
+    for (uint64_t sg0 = ((uint64_t)blockIdx.x * NWAVES + (threadIdx.x >> 6)) * LF_U; sg0 < nsegs;
+         sg0 += nw * LF_U) {
+        const uint32_t t = (uint32_t)(sg0 / TH), y0 = (uint32_t)(sg0 % TH);
         const TilePos tp = tile_pos(t, g);
-        bool root = false;
-        if ((int)y < tp.vh && lane < tp.vw) {
-            const int64_t Y = tp.y0 + y, X = tp.x0 + lane;
-            root = (int64_t)leaders[(int64_t)tp.b * g.HW + Y * g.W + X] == Y * g.W + X;
+        const int64_t X = tp.x0 + lane;
+        const int32_t *base = leaders + (int64_t)tp.b * g.HW;
+        int32_t v[LF_U];
+#pragma unroll
+        for (int u = 0; u < LF_U; ++u) {
+            const int64_t Y = tp.y0 + y0 + u;
+            v[u] = ((int)(y0 + u) < tp.vh && lane < tp.vw) ? base[Y * g.W + X] : -1;
         }
-        const uint64_t m = __ballot(root);
-        if (lane == 0) {
-            w.seg[sgi] = popc64(m);
-            if (write_mask) w.leadmask[sgi] = m;
+        uint32_t cnt = 0;
+        uint64_t mask = 0;  // lane u keeps segment u's
+#pragma unroll
+        for (int u = 0; u < LF_U; ++u) {
+            const int64_t Y = tp.y0 + y0 + u;
+            const uint64_t m = __ballot(v[u] >= 0 && (int64_t)v[u] == Y * g.W + X);
+            cnt = lane == u ? popc64(m) : cnt;
+            mask = lane == u ? m : mask;
+        }
+        if (lane < LF_U) {
+            w.seg[sg0 + lane] = cnt;
+            if (write_mask) w.leadmask[sg0 + lane] = mask;
         }
     }
 }
+
+// One workgroup per image row at a time; each thread takes LA_U pixels of the
+// row BLOCK apart, all their leaders' loads, then all their segment words'
+// loads, issued before the first is used.  Where a wave's 64 pixels share one
+// leader (the inside of a large region: on a drawing, most of the paper), the
+// number is computed once, from segment words read through the scalar cache:
+// every such wave of a region reads the same two words, which as vector loads
+// all queue at one L2 channel.
+constexpr int LA_U = 4;
+typedef __attribute__((address_space(4))) const uint32_t const_u32;
+typedef __attribute__((address_space(4))) const uint64_t const_u64;
 
 __global__ __launch_bounds__(BLOCK) void leader_assign_kernel(const int32_t *leaders,
                                                               int32_t *labels, Geom g, Work w)
@@ -2541,17 +2570,57 @@ __global__ __launch_bounds__(BLOCK) void leader_assign_kernel(const int32_t *lea
     const int64_t nrows = g.B * g.H;
     for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
         const uint32_t b = (uint32_t)(row / g.H);
-        for (int64_t x = threadIdx.x; x < g.W; x += BLOCK) {
-            const int64_t i = row * g.W + x;
-            const int32_t v = leaders[i];
-            int32_t out = 0;
-            if (v >= 0 && (int64_t)v < g.HW) {
-                uint32_t tl, r, c;
-                pixel_tile((uint32_t)v, b, g, tl, r, c);
-                const size_t sg = (size_t)tl * TH + r;
-                out = (int32_t)(1u + w.seg[sg] + popc64(w.leadmask[sg] & mask_lt((int)c)));
+        for (int64_t x0 = threadIdx.x; x0 < g.W; x0 += (int64_t)BLOCK * LA_U) {
+            int32_t v[LA_U];
+#pragma unroll
+            for (int u = 0; u < LA_U; ++u) {
+                const int64_t x = x0 + (int64_t)u * BLOCK;
+                v[u] = x < g.W ? leaders[row * g.W + x] : -1;
             }
-            labels[i] = out;
+            uint32_t sg[LA_U], col[LA_U];
+            uint64_t lm[LA_U];
+            bool ok[LA_U];
+            int32_t one[LA_U];  // the wave's label where all its pixels share a leader
+            uint64_t uni = 0;   // bit u: they do
+#pragma unroll
+            for (int u = 0; u < LA_U; ++u) {
+                // a value outside the image (an ignored pixel's -1) is never
+                // dereferenced and gets 0
+                const int32_t v0 = __builtin_amdgcn_readfirstlane(v[u]);
+                one[u] = 0;
+                sg[u] = 0u;
+                lm[u] = 0ull;
+                col[u] = 0u;
+                ok[u] = false;
+                if (__ballot(v[u] != v0) == 0ull) {
+                    uni |= 1ull << u;
+                    if (v0 >= 0 && (int64_t)v0 < g.HW) {
+                        uint32_t tl, r, c;
+                        pixel_tile((uint32_t)v0, b, g, tl, r, c);
+                        const size_t si = (size_t)tl * TH + r;
+                        const uint32_t sgs = ((const const_u32 *)w.seg)[si];
+                        const uint64_t lms = ((const const_u64 *)w.leadmask)[si];
+                        one[u] = (int32_t)(1u + sgs + popc64(lms & mask_lt((int)c)));
+                    }
+                } else {
+                    ok[u] = v[u] >= 0 && (int64_t)v[u] < g.HW;
+                    uint32_t tl = 0, r = 0, c = 0;
+                    if (ok[u]) pixel_tile((uint32_t)v[u], b, g, tl, r, c);
+                    const size_t si = (size_t)tl * TH + r;
+                    sg[u] = ok[u] ? w.seg[si] : 0u;
+                    lm[u] = ok[u] ? w.leadmask[si] : 0ull;
+                    col[u] = c;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < LA_U; ++u) {
+                const int64_t x = x0 + (int64_t)u * BLOCK;
+                if (x < g.W)
+                    labels[row * g.W + x] =
+                        ((uni >> u) & 1ull) ? one[u]
+                        : ok[u] ? (int32_t)(1u + sg[u] + popc64(lm[u] & mask_lt((int)col[u])))
+                                : 0;
+            }
         }
     }
 }
@@ -3143,7 +3212,7 @@ void launch_final(const Geom &g, const Work &w, int32_t *out, int number, uint32
 void launch_leader_flags(const int32_t *leaders, const Geom &g, const Work &w, int write_mask,
                          int clear_err, hipStream_t s)
 {
-    int64_t blocks = grid_of(g.ntiles * TH, NWAVES);
+    int64_t blocks = grid_of(g.ntiles * (TH / LF_U), NWAVES);
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(leader_flag_kernel, dim3((unsigned)blocks), dim3(BLOCK), 0, s, leaders, g,
                        w, write_mask, clear_err);
