@@ -171,8 +171,9 @@ def test_label_large_validation(lib):
     assert L(FAKE, 4, 1, 8, 8, 8, 0, 0, 0, None, None, FAKE, big, None) == -1
     assert L(FAKE, 4, 1, 2**24, 2**24, 8, 0, 0, 0, FAKE, None, FAKE, big, None) == -3
     assert L(None, 4, 0, 8, 8, 8, 1, 0, 0, None, None, None, 0, None) == 0
-    # bands of 2^31 - 64 pixels: numbers and leaders take them (numbers hold no
-    # 32-bit codes over the picture); the workspace is checked first
+    # bands of 2^31 - 64 pixels: numbers and leaders take them (both go through
+    # the bands' own numbering, with no 32-bit array over the picture); the
+    # workspace is checked first
     W = 2**25 - 1
     assert L(FAKE, 1, 1, 128, W, 8, 1, 0, 64, FAKE, None, FAKE, 16, None) == -6
     assert L(FAKE, 1, 1, 128, W, 8, 0, 0, 64, FAKE, None, FAKE, 16, None) == -6
