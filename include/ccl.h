@@ -28,7 +28,12 @@
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Calls only enqueue work on it and never synchronise; results are
- * ready when the stream reaches that point.
+ * ready when the stream reaches that point.  ccl_label, ccl_label_noalloc,
+ * ccl_label_stats, ccl_number, ccl_count and ccl_region_stats enqueue kernel
+ * launches only (no memory-set or copy: what must start empty is cleared by
+ * the kernels), so they can be recorded into a HIP graph and replayed
+ * (ccl_label_noalloc needs one call on the device before capture, which looks
+ * up its scratch array).
  *
  * Errors.  Each call returns a ccl_status.  Arguments are checked on the host
  * before anything is enqueued; on a validation error nothing is enqueued and
