@@ -3150,7 +3150,9 @@ void launch_seam(const Geom &g, const Work &w, int conn, hipStream_t s)
     const uint32_t slices = (uint32_t)(want < 1 ? 1 : want > 16 ? 16 : want);
     const dim3 grid((unsigned)(blocks * slices));
     hipLaunchKernelGGL(block_merge_kernel, grid, dim3(BLOCK), 0, s, g, w, conn, slices);
-    hipLaunchKernelGGL(border_merge_kernel, grid, dim3(BLOCK), 0, s, g, w, conn, slices);
+    // images of one block each (at most 8 x 8 tiles) have no block borders
+    if (g.ntx > MB || g.nty > MB)
+        hipLaunchKernelGGL(border_merge_kernel, grid, dim3(BLOCK), 0, s, g, w, conn, slices);
 }
 
 // tiles per workgroup of the roots and resolve passes: SEAM_TILES, or fewer
