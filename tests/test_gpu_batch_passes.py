@@ -2,8 +2,9 @@
 (2^24 - 1: seam node ids are 32-bit, and a launch of one 256-thread workgroup
 per tile stays below 2^32 threads): ccl_label, ccl_number, ccl_count,
 ccl_label_stats and ccl_region_stats take it in passes of whole images
-(ccl_label_host in its groups of images), one after another in one workspace sized for a
-pass.  2^24 + 3 pictures of 2 x 2 pixels (one tile each): the first pass holds
+(ccl_label_host in its groups of images), one after another in one
+workspace sized for a pass.  2^24 + 3 pictures of 2 x 2 pixels (one tile
+each): the first pass holds
 2^24 - 1 images, the second the last four.  Its 2^24 + 3 tile rows also take
 the numbering scan over several launches; the statistics calls carry the
 regions of the first pass into the records of the second.
